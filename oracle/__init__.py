@@ -1,0 +1,245 @@
+"""fp64 CPU oracle for the chunked gated delta rule forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Nothing here is part of the product: only the tests,
+the smoke check and the CPU-baseline leg of the benchmark import this package.
+It shares no code with the HIP library and never loads it.
+
+Three functions mirror the three library entry points:
+
+* ``token_recurrence`` -- the plain definition (C, fp64, one token at a time),
+  the reference for ``gdn_forward``.  See ``gdn_oracle.c`` for the recurrence.
+* ``chunk_prepare`` -- the per-chunk WY factors (gate cumsum, the strictly lower
+  decayed Gram matrix, its unit-triangular inverse, then w and u), the
+  reference for ``gdn_prepare``.  Steps follow the TileOPs "Reuse P as beta
+  tiles in gated deltanet fused prepare" page (the A_g build, the inverse held
+  in S_shared, then w = A_g^-1 k_beta and u = A_g^-1 v_beta), with the gate
+  factor folded into w as the chunk algebra requires (see ``chunk_prepare``).
+* ``chunk_scan`` -- the serial inter-chunk scan given w, u and the cumsum, the
+  reference for ``gdn_scan``.  Steps follow the per-chunk algebra in the
+  docstring of the kernel_fun KDA re-scan page (bwd_scan.py, KdaB1ScanKernel):
+  v' = u - w h, then h <- exp(gd) h + kg^T v', plus the output read-out.
+
+All three work on numpy arrays in the library's layouts: q, k, w [B,T,H,K];
+v, u, o [B,T,H,V]; beta [B,T,H]; g, gcum [B,T,H] (one gate per head) or
+[B,T,H,K] (one gate per key dimension); h0, hT [B,H,K,V] with
+hT[b,h,i,j] = S_T[j,i].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+_lock = threading.Lock()
+
+
+def build(force: bool = True) -> str:
+    """Compile gdn_oracle.c into liboracle.so with gcc (host only)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-shared", "-fPIC",
+             "-o", tmp, _SRC, "-lpthread", "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH) or (
+                    os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB_PATH)
+            f = lib.gdn_oracle_f64
+            i64, vp = ctypes.c_int64, ctypes.c_void_p
+            f.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
+                          vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, ctypes.c_int]
+            f.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _f32(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def token_recurrence(q, k, v, beta, g, h0=None, heads=None, nthreads=None,
+                     want_o=True, want_hT=True):
+    """Token-by-token fp64 recurrence.
+
+    Inputs are anything numpy can view as float32 holding the exact values the
+    GPU sees (bf16 widens exactly).  ``heads`` optionally selects flat head
+    indices b*H + h.  Returns ``(o, hT)`` as float64 arrays: with ``heads`` None
+    they are [B,T,H,V] and [B,H,K,V]; otherwise head-major [n,T,V], [n,K,V].
+    """
+    q, k, v, beta, g = map(_f32, (q, k, v, beta, g))
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if k.shape != (B, T, H, K) or v.shape != (B, T, H, V):
+        raise ValueError("q/k/v shapes disagree")
+    if beta.shape != (B, T, H):
+        raise ValueError("beta must be [B,T,H]")
+    if g.shape == (B, T, H):
+        per_key = 0
+    elif g.shape == (B, T, H, K):
+        per_key = 1
+    else:
+        raise ValueError("g must be [B,T,H] or [B,T,H,K]")
+    h0c = None if h0 is None else _f32(h0)
+    if h0c is not None and h0c.shape != (B, H, K, V):
+        raise ValueError("h0 must be [B,H,K,V]")
+    if heads is None:
+        sel, n = None, B * H
+    else:
+        sel = np.ascontiguousarray(np.asarray(heads, dtype=np.int64))
+        n = sel.size
+    o = np.empty((n, T, V), np.float64) if want_o else None
+    hT = np.empty((n, K, V), np.float64) if want_hT else None
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    ptr = lambda a: None if a is None else a.ctypes.data
+    rc = _load().gdn_oracle_f64(
+        B, T, H, K, V, per_key, ptr(q), ptr(k), ptr(v), ptr(beta), ptr(g),
+        ptr(h0c), n, ptr(sel), ptr(o), ptr(hT), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("gdn_oracle_f64 failed with code %d" % rc)
+    if heads is None:
+        if o is not None:
+            o = o.reshape(B, H, T, V).transpose(0, 2, 1, 3)
+        if hT is not None:
+            hT = hT.reshape(B, H, K, V)
+    return o, hT
+
+
+# --------------------------------------------------------------------------
+# Chunk form.  Per (batch, head) and per chunk of C tokens (the last chunk may
+# be shorter).  Notation: gamma = chunk-local inclusive cumsum of g.
+# --------------------------------------------------------------------------
+
+def _chunks(T, C):
+    for s in range(0, T, C):
+        yield s, min(s + C, T)
+
+
+def chunk_prepare(k, v, beta, g, chunk):
+    """WY factors per chunk, fp64.  Returns ``(gcum, w, u)``.
+
+    Follows the prepare kernel of the TileOPs gated deltanet page:
+      1. gamma: the chunk-local cumulative sum of the log gate (inclusive of
+         the current token; the KDA re-scan page stages the same cumsum, g2).
+      2. A_g: strictly lower triangular, A[r,s] = beta_r * sum_d k[r,d] k[s,d]
+         exp(gamma[r,d] - gamma[s,d]) for s < r (scalar gate: one exponent).
+      3. The inverse of (I + A_g), unit lower triangular (the page's
+         S_shared; it gets there by a Neumann series, here by an exact solve).
+      4. k_beta = k * beta, v_beta = v * beta; w = inv @ (k_beta * exp(gamma)),
+         u = inv @ v_beta.
+    The exp(gamma) factor on k_beta is the reading under which the scan's
+    v' = u - w h is taken against the chunk-start state, which the KDA page
+    states ("kg carries the v~ scaling so v' stores un-decayed"); without it
+    the chunk form disagrees with the token recurrence.
+    """
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    beta = np.asarray(beta, np.float64)
+    g = np.asarray(g, np.float64)
+    B, T, H, K = k.shape
+    per_key = g.ndim == 4
+    gcum = np.zeros_like(g)
+    w = np.zeros(k.shape, np.float64)
+    u = np.zeros(v.shape, np.float64)
+    for b in range(B):
+        for h in range(H):
+            for s, e in _chunks(T, chunk):
+                n = e - s
+                kc = k[b, s:e, h]                       # [n,K]
+                vc = v[b, s:e, h]                       # [n,V]
+                bc = beta[b, s:e, h]                    # [n]
+                gc = g[b, s:e, h]                       # [n] or [n,K]
+                gam = np.cumsum(gc, axis=0)
+                gcum[b, s:e, h] = gam
+                if per_key:
+                    # A[r,s] = beta_r sum_d k_rd k_sd exp(gam_rd - gam_sd)
+                    dec = np.exp(gam[:, None, :] - gam[None, :, :])   # [n,n,K]
+                    G = np.einsum("rd,sd,rsd->rs", kc, kc, dec)
+                    ke = kc * np.exp(gam)
+                else:
+                    G = (kc @ kc.T) * np.exp(gam[:, None] - gam[None, :])
+                    ke = kc * np.exp(gam)[:, None]
+                A = np.tril(bc[:, None] * G, -1)
+                Tm = np.linalg.inv(np.eye(n) + A)
+                w[b, s:e, h] = Tm @ (ke * bc[:, None])
+                u[b, s:e, h] = Tm @ (vc * bc[:, None])
+    return gcum, w, u
+
+
+def chunk_scan(q, k, w, u, gcum, chunk, h0=None):
+    """Serial scan over chunks, fp64.  Returns ``(o, hT)``.
+
+    Per chunk with start state h (K x V), following the re-scan page's
+    per-chunk algebra (there with h checkpoints and dq, which are not part of
+    the forward output):
+      v' = u - w h                         (the page's "v' = u - WH")
+      o  = (q * exp(gamma)) h + tril_incl((q k^T) * decay) v'
+      h  <- exp(gamma_last) * h + (k * exp(gamma_last - gamma))^T v'
+    where decay[r,s] = exp(gamma_r - gamma_s) (per key dimension for KDA) and
+    the causal mask keeps s <= r (o_t is read from the updated state).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    w = np.asarray(w, np.float64)
+    u = np.asarray(u, np.float64)
+    gcum = np.asarray(gcum, np.float64)
+    B, T, H, K = q.shape
+    V = u.shape[-1]
+    per_key = gcum.ndim == 4
+    o = np.zeros((B, T, H, V), np.float64)
+    hT = np.zeros((B, H, K, V), np.float64)
+    for b in range(B):
+        for hh in range(H):
+            S = (np.zeros((K, V)) if h0 is None
+                 else np.array(h0[b, hh], np.float64))
+            for s, e in _chunks(T, chunk):
+                qc, kc = q[b, s:e, hh], k[b, s:e, hh]
+                wc, uc = w[b, s:e, hh], u[b, s:e, hh]
+                gam = gcum[b, s:e, hh]
+                vp = uc - wc @ S
+                if per_key:
+                    dec = np.exp(gam[:, None, :] - gam[None, :, :])
+                    P = np.einsum("rd,sd,rsd->rs", qc, kc, dec)
+                    qd = qc * np.exp(gam)
+                    kg = kc * np.exp(gam[-1][None, :] - gam)
+                    last = np.exp(gam[-1])[:, None]
+                else:
+                    P = (qc @ kc.T) * np.exp(gam[:, None] - gam[None, :])
+                    qd = qc * np.exp(gam)[:, None]
+                    kg = kc * np.exp(gam[-1] - gam)[:, None]
+                    last = np.exp(gam[-1])
+                o[b, s:e, hh] = qd @ S + np.tril(P) @ vp
+                S = last * S + kg.T @ vp
+            hT[b, hh] = S
+    return o, hT
+
+
+def chunk_forward(q, k, v, beta, g, chunk, h0=None):
+    """chunk_prepare followed by chunk_scan."""
+    gcum, w, u = chunk_prepare(k, v, beta, g, chunk)
+    return chunk_scan(q, k, w, u, gcum, chunk, h0)
+
+
+def rel_err(x, ref):
+    """max |x - ref| / rms(ref), the parity measure used throughout."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    if rms == 0.0:
+        return float(np.max(np.abs(x - ref))) if ref.size else 0.0
+    return float(np.max(np.abs(x - ref)) / rms)
