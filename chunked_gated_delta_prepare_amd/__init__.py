@@ -1,0 +1,250 @@
+"""chunked_gated_delta_prepare_amd -- Python binding for libgdn.
+
+Forward pass of the chunked gated delta rule (Gated DeltaNet with one gate
+per head, Kimi-Delta-Attention with one gate per key dimension) on AMD
+MI355X.  Every step runs in the HIP kernels of ``libgdn.so``; this module only
+checks tensors, allocates outputs with torch and passes raw pointers and the
+current HIP stream through the C ABI declared in ``include/libgdn.h``.
+
+Entry points (same names as the C ABI):
+    prepare(k, v, beta, g, chunk)                 -> (w, u, gcum)
+    scan(q, k, w, u, gcum, chunk, h0=None)        -> (o, hT)
+    forward(q, k, v, beta, g, chunk, h0=None)     -> (o, hT)
+Layouts: q, k [B,T,H,K]; v [B,T,H,V]; beta [B,T,H]; g [B,T,H] or [B,T,H,K];
+h0/hT [B,H,K,V] fp32.  q, k, v are bf16 or fp32 (same dtype); o is the io
+dtype unless ``o_dtype`` says otherwise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = ["prepare", "scan", "forward", "workspace_bytes", "load_library",
+           "GdnError", "LIB_PATH", "STATUS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+GDN_GATE_HEAD, GDN_GATE_KEY = 0, 1
+STATUS = {
+    0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE",
+    3: "GDN_ERR_UNSUPPORTED", 4: "GDN_ERR_ALIGNMENT", 5: "GDN_ERR_LDS_BUDGET",
+    6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP",
+}
+EXPORTS = ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_workspace_bytes",
+           "gdn_status_str", "gdn_abi_version"]
+ABI_VERSION = 1
+
+
+class GdnError(RuntimeError):
+    def __init__(self, call, status, message):
+        super().__init__("%s failed: %s" % (call, message))
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("V", ctypes.c_int64), ("chunk", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("o_dtype", ctypes.c_int32),
+                ("gate", ctypes.c_int32)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library(path: str | None = None):
+    """Load libgdn.so (built in-tree by build.py).  Raises if it is missing:
+    there is no fallback implementation."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(
+                "libgdn.so not found at %s; build it with "
+                "`python -m chunked_gated_delta_prepare_amd.build`" % p)
+        lib = ctypes.CDLL(p)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        pp = ctypes.POINTER(Problem)
+        lib.gdn_prepare.argtypes = [pp] + [vp] * 8
+        lib.gdn_scan.argtypes = [pp] + [vp] * 9
+        lib.gdn_forward.argtypes = [pp] + [vp] * 9 + [sz, vp]
+        for f in (lib.gdn_prepare, lib.gdn_scan, lib.gdn_forward):
+            f.restype = ctypes.c_int
+        lib.gdn_workspace_bytes.argtypes = [pp]
+        lib.gdn_workspace_bytes.restype = sz
+        lib.gdn_status_str.argtypes = [ctypes.c_int]
+        lib.gdn_status_str.restype = ctypes.c_char_p
+        lib.gdn_abi_version.argtypes = []
+        lib.gdn_abi_version.restype = ctypes.c_int
+        if lib.gdn_abi_version() != ABI_VERSION:
+            raise RuntimeError("libgdn ABI %d, binding expects %d"
+                               % (lib.gdn_abi_version(), ABI_VERSION))
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt):
+    torch = _torch()
+    if dt == torch.float32:
+        return GDN_F32
+    if dt == torch.bfloat16:
+        return GDN_BF16
+    raise TypeError("unsupported dtype %s (bf16 or fp32)" % dt)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype=None, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device (HIP) tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _check(call, rc):
+    if rc != 0:
+        lib = load_library()
+        raise GdnError(call, rc, lib.gdn_status_str(rc).decode())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _problem(q_or_k, v, chunk, gate_per_key, o_dtype):
+    B, T, H, K = q_or_k.shape
+    V = v.shape[-1] if v is not None else K
+    io = _dtype_code(q_or_k.dtype)
+    return Problem(B, T, H, K, V, int(chunk), io, _dtype_code(o_dtype),
+                   GDN_GATE_KEY if gate_per_key else GDN_GATE_HEAD)
+
+
+def _gate_kind(g, B, T, H, K):
+    if tuple(g.shape) == (B, T, H):
+        return False
+    if tuple(g.shape) == (B, T, H, K):
+        return True
+    raise ValueError("g must be [B,T,H] or [B,T,H,K], got %s" % (tuple(g.shape),))
+
+
+def workspace_bytes(B, T, H, K, V, chunk, io_dtype, gate_per_key=False, o_dtype=None):
+    io = _dtype_code(io_dtype)
+    od = _dtype_code(o_dtype or io_dtype)
+    pr = Problem(B, T, H, K, V, chunk, io, od, GDN_GATE_KEY if gate_per_key else GDN_GATE_HEAD)
+    return int(load_library().gdn_workspace_bytes(ctypes.byref(pr)))
+
+
+def prepare(k, v, beta, g, chunk, *, w=None, u=None, gcum=None, stream=None):
+    """WY factors per chunk: returns (w [B,T,H,K], u [B,T,H,V], gcum) fp32."""
+    torch = _torch()
+    lib = load_library()
+    B, T, H, K = k.shape
+    V = v.shape[-1]
+    per_key = _gate_kind(g, B, T, H, K)
+    _need(k, "k")
+    _need(v, "v", k.dtype, (B, T, H, V))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    _need(g, "g", torch.float32)
+    dev = k.device
+    if w is None:
+        w = torch.empty(B, T, H, K, device=dev, dtype=torch.float32)
+    if u is None:
+        u = torch.empty(B, T, H, V, device=dev, dtype=torch.float32)
+    if gcum is None:
+        gcum = torch.empty_like(g)
+    _need(w, "w", torch.float32, (B, T, H, K))
+    _need(u, "u", torch.float32, (B, T, H, V))
+    _need(gcum, "gcum", torch.float32, tuple(g.shape))
+    pr = _problem(k, v, chunk, per_key, k.dtype)
+    rc = lib.gdn_prepare(ctypes.byref(pr), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                         _ptr(w), _ptr(u), _ptr(gcum), _stream(stream))
+    _check("gdn_prepare", rc)
+    return w, u, gcum
+
+
+def scan(q, k, w, u, gcum, chunk, h0=None, *, o_dtype=None, o=None, hT=None,
+         output_final_state=True, stream=None):
+    """Inter-chunk scan from WY factors: returns (o, hT or None)."""
+    torch = _torch()
+    lib = load_library()
+    B, T, H, K = q.shape
+    V = u.shape[-1]
+    per_key = _gate_kind(gcum, B, T, H, K)
+    _need(q, "q")
+    _need(k, "k", q.dtype, (B, T, H, K))
+    _need(w, "w", torch.float32, (B, T, H, K))
+    _need(u, "u", torch.float32, (B, T, H, V))
+    _need(gcum, "gcum", torch.float32)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (B, H, K, V))
+    od = o_dtype or q.dtype
+    if o is None:
+        o = torch.empty(B, T, H, V, device=q.device, dtype=od)
+    _need(o, "o", od, (B, T, H, V))
+    if hT is None and output_final_state:
+        hT = torch.empty(B, H, K, V, device=q.device, dtype=torch.float32)
+    if hT is not None:
+        _need(hT, "hT", torch.float32, (B, H, K, V))
+    pr = _problem(q, u, chunk, per_key, od)
+    rc = lib.gdn_scan(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(w), _ptr(u), _ptr(gcum),
+                      _ptr(h0), _ptr(o), _ptr(hT), _stream(stream))
+    _check("gdn_scan", rc)
+    return o, hT
+
+
+def forward(q, k, v, beta, g, chunk, h0=None, *, o_dtype=None, o=None, hT=None,
+            output_final_state=True, workspace=None, stream=None):
+    """Whole forward pass: returns (o [B,T,H,V], hT [B,H,K,V] fp32 or None)."""
+    torch = _torch()
+    lib = load_library()
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    per_key = _gate_kind(g, B, T, H, K)
+    _need(q, "q")
+    _need(k, "k", q.dtype, (B, T, H, K))
+    _need(v, "v", q.dtype, (B, T, H, V))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    _need(g, "g", torch.float32)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (B, H, K, V))
+    od = o_dtype or q.dtype
+    if o is None:
+        o = torch.empty(B, T, H, V, device=q.device, dtype=od)
+    _need(o, "o", od, (B, T, H, V))
+    if hT is None and output_final_state:
+        hT = torch.empty(B, H, K, V, device=q.device, dtype=torch.float32)
+    if hT is not None:
+        _need(hT, "hT", torch.float32, (B, H, K, V))
+    pr = _problem(q, v, chunk, per_key, od)
+    need = int(lib.gdn_workspace_bytes(ctypes.byref(pr)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.gdn_forward(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                         _ptr(h0), _ptr(o), _ptr(hT), _ptr(workspace),
+                         ctypes.c_size_t(ws_bytes), _stream(stream))
+    _check("gdn_forward", rc)
+    return o, hT

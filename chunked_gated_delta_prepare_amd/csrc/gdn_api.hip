@@ -1,0 +1,242 @@
+// libgdn C ABI: argument validation, launch planning and dispatch onto the
+// kernel template instances.  Everything here runs on the host, enqueues on
+// the caller's stream and returns; nothing allocates or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/libgdn.h"
+#include "gdn_prepare.h"
+#include "gdn_scan.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kBV = 64;            // V tile per scan workgroup
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+gdn_status check_problem(const gdn_problem *pr) {
+    if (!pr) return GDN_ERR_NULL_ARG;
+    if (pr->B < 1 || pr->H < 1 || pr->K < 1 || pr->V < 1 || pr->T < 0 || pr->chunk < 1)
+        return GDN_ERR_BAD_SHAPE;
+    if (pr->io_dtype != GDN_F32 && pr->io_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (pr->o_dtype != GDN_F32 && pr->o_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (pr->io_dtype == GDN_F32 && pr->o_dtype != GDN_F32) return GDN_ERR_UNSUPPORTED;
+    if (pr->gate != GDN_GATE_HEAD && pr->gate != GDN_GATE_KEY) return GDN_ERR_UNSUPPORTED;
+    if (pr->K != 64 && pr->K != 128) return GDN_ERR_UNSUPPORTED;
+    if (pr->V != 64 && pr->V != 128) return GDN_ERR_UNSUPPORTED;
+    if (pr->chunk != 32 && pr->chunk != 64) return GDN_ERR_UNSUPPORTED;
+    // index arithmetic inside the kernels: token rows and grid sizes in int
+    const int64_t rows = pr->B * pr->T * pr->H;
+    if (pr->T > (1 << 30) || rows > ((int64_t)1 << 31) / 8 || pr->B * pr->H > (1 << 24))
+        return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+gdn_status check_ptrs(std::initializer_list<const void *> required,
+                      std::initializer_list<const void *> optional) {
+    for (const void *p : required)
+        if (!p) return GDN_ERR_NULL_ARG;
+    for (const void *p : required)
+        if (!aligned16(p)) return GDN_ERR_ALIGNMENT;
+    for (const void *p : optional)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGNMENT;
+    return GDN_OK;
+}
+
+gdn_status launch(const void *fn, int grid, void *params, size_t psize, hipStream_t s) {
+    (void)psize;
+    if (grid <= 0) return GDN_OK;
+    void *args[] = {params};
+    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// prepare
+// ---------------------------------------------------------------------------
+template <int C, int K, typename IO, bool KG>
+gdn_status run_prepare(PrepParams &pp, int grid, hipStream_t s) {
+    if constexpr (PrepLayout<C, K, IO, KG>::kBytes > kLdsBytesMax) {
+        return GDN_ERR_LDS_BUDGET;
+    } else {
+        return launch((const void *)&prepare_kernel<C, K, IO, KG>, grid, &pp, sizeof(pp), s);
+    }
+}
+
+template <int C, int K, typename IO>
+gdn_status prepare_gate(const gdn_problem *pr, PrepParams &pp, int grid, hipStream_t s) {
+    return pr->gate == GDN_GATE_KEY ? run_prepare<C, K, IO, true>(pp, grid, s)
+                                    : run_prepare<C, K, IO, false>(pp, grid, s);
+}
+
+template <int C, typename IO>
+gdn_status prepare_k(const gdn_problem *pr, PrepParams &pp, int grid, hipStream_t s) {
+    return pr->K == 64 ? prepare_gate<C, 64, IO>(pr, pp, grid, s)
+                       : prepare_gate<C, 128, IO>(pr, pp, grid, s);
+}
+
+template <typename IO>
+gdn_status prepare_c(const gdn_problem *pr, PrepParams &pp, int grid, hipStream_t s) {
+    return pr->chunk == 32 ? prepare_k<32, IO>(pr, pp, grid, s)
+                           : prepare_k<64, IO>(pr, pp, grid, s);
+}
+
+gdn_status enqueue_prepare(const gdn_problem *pr, const void *k, const void *v,
+                           const float *beta, const float *g, float *w, float *u,
+                           float *gcum, hipStream_t s) {
+    PrepParams pp;
+    pp.k = k; pp.v = v; pp.beta = beta; pp.g = g;
+    pp.w = w; pp.u = u; pp.gcum = gcum;
+    pp.B = (int)pr->B; pp.T = (int)pr->T; pp.H = (int)pr->H; pp.V = (int)pr->V;
+    pp.nt = (int)((pr->T + pr->chunk - 1) / pr->chunk);
+    const int grid = (int)(pr->B * pr->H) * pp.nt;
+    return pr->io_dtype == GDN_F32 ? prepare_c<float>(pr, pp, grid, s)
+                                   : prepare_c<bf16_t>(pr, pp, grid, s);
+}
+
+// ---------------------------------------------------------------------------
+// scan
+// ---------------------------------------------------------------------------
+template <int C, int K, typename IO, typename OT, bool KG>
+gdn_status run_scan(ScanParams &sp, int grid, hipStream_t s) {
+    if constexpr (ScanLayout<C, K, kBV, IO, KG>::kBytes > kLdsBytesMax) {
+        return GDN_ERR_LDS_BUDGET;
+    } else {
+        return launch((const void *)&scan_kernel<C, K, kBV, IO, OT, KG>, grid, &sp, sizeof(sp), s);
+    }
+}
+
+template <int C, int K, typename IO, typename OT>
+gdn_status scan_gate(const gdn_problem *pr, ScanParams &sp, int grid, hipStream_t s) {
+    return pr->gate == GDN_GATE_KEY ? run_scan<C, K, IO, OT, true>(sp, grid, s)
+                                    : run_scan<C, K, IO, OT, false>(sp, grid, s);
+}
+
+template <int C, int K>
+gdn_status scan_dt(const gdn_problem *pr, ScanParams &sp, int grid, hipStream_t s) {
+    if (pr->io_dtype == GDN_F32) return scan_gate<C, K, float, float>(pr, sp, grid, s);
+    if (pr->o_dtype == GDN_F32) return scan_gate<C, K, bf16_t, float>(pr, sp, grid, s);
+    return scan_gate<C, K, bf16_t, bf16_t>(pr, sp, grid, s);
+}
+
+template <int C>
+gdn_status scan_k(const gdn_problem *pr, ScanParams &sp, int grid, hipStream_t s) {
+    return pr->K == 64 ? scan_dt<C, 64>(pr, sp, grid, s) : scan_dt<C, 128>(pr, sp, grid, s);
+}
+
+gdn_status enqueue_scan(const gdn_problem *pr, const void *q, const void *k,
+                        const float *w, const float *u, const float *gcum,
+                        const float *h0, void *o, float *hT, hipStream_t s) {
+    ScanParams sp;
+    sp.q = q; sp.k = k; sp.w = w; sp.u = u; sp.gcum = gcum; sp.h0 = h0;
+    sp.o = o; sp.hT = hT;
+    sp.B = (int)pr->B; sp.T = (int)pr->T; sp.H = (int)pr->H; sp.V = (int)pr->V;
+    sp.nvt = (int)(pr->V / kBV);
+    const int pairs = (int)(pr->B * pr->H);
+    sp.swizzle = (pairs % 8 == 0) ? 1 : 0;
+    if (const char *e = std::getenv("GDN_NO_SWIZZLE")) sp.swizzle = (*e == '1') ? 0 : sp.swizzle;
+    const int grid = pairs * sp.nvt;
+    return pr->chunk == 32 ? scan_k<32>(pr, sp, grid, s) : scan_k<64>(pr, sp, grid, s);
+}
+
+size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsPlan { size_t w, u, g, total; };
+
+WsPlan workspace_plan(const gdn_problem *pr) {
+    const size_t rows = (size_t)(pr->B * pr->T * pr->H);
+    WsPlan p;
+    p.w = round_up(rows * (size_t)pr->K * 4);
+    p.u = round_up(rows * (size_t)pr->V * 4);
+    p.g = round_up(rows * (size_t)(pr->gate == GDN_GATE_KEY ? pr->K : 1) * 4);
+    p.total = p.w + p.u + p.g;
+    return p;
+}
+
+}  // namespace
+}  // namespace gdn
+
+using namespace gdn;
+
+extern "C" {
+
+gdn_status gdn_prepare(const gdn_problem *problem, const void *k, const void *v,
+                       const float *beta, const float *g, float *w, float *u,
+                       float *gcum, void *stream) {
+    gdn_status st = check_problem(problem);
+    if (st != GDN_OK) return st;
+    if (problem->T == 0) return GDN_OK;
+    st = check_ptrs({k, v, beta, g, w, u, gcum}, {});
+    if (st != GDN_OK) return st;
+    return enqueue_prepare(problem, k, v, beta, g, w, u, gcum, (hipStream_t)stream);
+}
+
+gdn_status gdn_scan(const gdn_problem *problem, const void *q, const void *k,
+                    const float *w, const float *u, const float *gcum,
+                    const float *h0, void *o, float *hT, void *stream) {
+    gdn_status st = check_problem(problem);
+    if (st != GDN_OK) return st;
+    if (problem->T == 0) {
+        st = check_ptrs({}, {h0, hT});
+        if (st != GDN_OK) return st;
+    } else {
+        st = check_ptrs({q, k, w, u, gcum, o}, {h0, hT});
+        if (st != GDN_OK) return st;
+    }
+    if (problem->T == 0 && !hT) return GDN_OK;
+    return enqueue_scan(problem, q, k, w, u, gcum, h0, o, hT, (hipStream_t)stream);
+}
+
+size_t gdn_workspace_bytes(const gdn_problem *problem) {
+    if (check_problem(problem) != GDN_OK) return 0;
+    return workspace_plan(problem).total;
+}
+
+gdn_status gdn_forward(const gdn_problem *problem, const void *q, const void *k,
+                       const void *v, const float *beta, const float *g,
+                       const float *h0, void *o, float *hT, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    gdn_status st = check_problem(problem);
+    if (st != GDN_OK) return st;
+    if (problem->T == 0) {
+        st = check_ptrs({}, {h0, hT});
+        if (st != GDN_OK) return st;
+        if (!hT) return GDN_OK;
+        return enqueue_scan(problem, nullptr, nullptr, nullptr, nullptr, nullptr, h0,
+                            nullptr, hT, (hipStream_t)stream);
+    }
+    st = check_ptrs({q, k, v, beta, g, o}, {h0, hT});
+    if (st != GDN_OK) return st;
+    const WsPlan wp = workspace_plan(problem);
+    if (wp.total > 0) {
+        if (!workspace || workspace_bytes < wp.total) return GDN_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return GDN_ERR_ALIGNMENT;
+    }
+    char *ws = (char *)workspace;
+    float *w = (float *)ws, *u = (float *)(ws + wp.w), *gc = (float *)(ws + wp.w + wp.u);
+    hipStream_t s = (hipStream_t)stream;
+    st = enqueue_prepare(problem, k, v, beta, g, w, u, gc, s);
+    if (st != GDN_OK) return st;
+    return enqueue_scan(problem, q, k, w, u, gc, h0, o, hT, s);
+}
+
+const char *gdn_status_str(gdn_status status) {
+    switch (status) {
+        case GDN_OK: return "GDN_OK";
+        case GDN_ERR_NULL_ARG: return "GDN_ERR_NULL_ARG: a required pointer is NULL";
+        case GDN_ERR_BAD_SHAPE: return "GDN_ERR_BAD_SHAPE: invalid problem size";
+        case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: shape or dtype not implemented";
+        case GDN_ERR_ALIGNMENT: return "GDN_ERR_ALIGNMENT: pointer not 16-byte aligned";
+        case GDN_ERR_LDS_BUDGET: return "GDN_ERR_LDS_BUDGET: kernel LDS need exceeds 160 KiB";
+        case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
+        case GDN_ERR_HIP: return "GDN_ERR_HIP: HIP runtime call failed";
+    }
+    return "unknown gdn_status";
+}
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,155 @@
+/*
+ * libgdn -- forward pass of the chunked gated delta rule on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method: per (batch, head) a state S_t (V x K) follows
+ *     S_t = S_{t-1} Diag(a_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t,            a_t = exp(g_t),
+ * with one log-gate g_t per (token, head) for Gated DeltaNet, or one per
+ * (token, head, key dimension) for Kimi-Delta-Attention (KDA), in which case
+ * Diag(a_t) scales the key index of S.  The sequence is cut into chunks of C
+ * tokens; a chunk's tokens are folded into WY factors (w, u) by a unit lower
+ * triangular inverse, and a serial scan carries the state across chunks.
+ *   - gdn_prepare follows the TileOPs gated deltanet "fused prepare" kernel
+ *     (page "Reuse P as beta tiles in gated deltanet fused prepare": A_g, its
+ *     inverse, then w = A_g^-1 k_beta and u = A_g^-1 v_beta).
+ *   - gdn_scan follows the per-chunk algebra of the kernel_fun KDA forward
+ *     re-scan (bwd_scan.py, KdaB1ScanKernel docstring: v' = u - w h,
+ *     h <- exp(gd) h + kg^T v'), plus the output read-out.
+ *   - gdn_forward is the two fused: q, k, v, beta, g (and h0) in, o and the
+ *     final state out.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layouts are dense and row-major (the innermost index is contiguous):
+ *     q, k, w     [B, T, H, K]       v, u, o   [B, T, H, V]
+ *     beta        [B, T, H]          g, gcum   [B, T, H]  (GDN_GATE_HEAD)
+ *                                              [B, T, H, K] (GDN_GATE_KEY)
+ *     h0, hT      [B, H, K, V]  with hT[b,h,i,j] = S_T[j,i]  (fp32)
+ * q, k, v use the problem's io dtype; o uses its o dtype; beta, g, gcum, w,
+ * u, h0 and hT are always fp32.  g is the natural-log gate (g <= 0 for a
+ * decaying state); gcum is its chunk-local inclusive cumulative sum.
+ *
+ * Numerics: state, accumulation and the triangular inverse are fp32.  With
+ * bf16 io, matrix-core operands are fp16 (raw bf16 inputs convert exactly for
+ * magnitudes in [2^-14, 65504]; derived operands are rounded once); with
+ * fp32 io they are fp32.  Inputs and the state must keep |x| < 65504 with
+ * bf16 io.  For the per-key gate, the chunk-local gate sums are referenced to
+ * the middle of the chunk, so |gcum[r] - gcum[mid]| must stay below ~11 for
+ * full accuracy with bf16 io.
+ *
+ * Ownership and execution: the caller allocates every buffer (device
+ * memory) and owns it; the library never allocates, frees or synchronises.
+ * Every call only enqueues work on `stream` (a hipStream_t; NULL is the
+ * default stream) and returns.  Argument, shape, alignment and resource
+ * errors are reported before anything is enqueued; a failed launch returns
+ * GDN_ERR_HIP; faults during execution surface at the caller's next
+ * synchronisation.  No C++ exception crosses this interface.
+ *
+ * Requirements: all pointers 16-byte aligned; K, V in {64, 128}; chunk in
+ * {32, 64}; B, H >= 1; T >= 0 (any T: a short last chunk is exact).  Shapes
+ * outside this set return GDN_ERR_UNSUPPORTED; there is no fallback path.
+ * o must not alias any input; hT may alias h0 only in gdn_forward/gdn_scan
+ * (each state tile is read completely before it is written).
+ *
+ * Thread safety: stateless; calls from several host threads are safe.
+ */
+#ifndef LIBGDN_H
+#define LIBGDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_NULL_ARG = 1,      /* a required pointer is NULL */
+    GDN_ERR_BAD_SHAPE = 2,     /* negative or zero size where >= 1 is needed */
+    GDN_ERR_UNSUPPORTED = 3,   /* valid but not implemented (K, V, chunk, dtype) */
+    GDN_ERR_ALIGNMENT = 4,     /* a pointer is not 16-byte aligned */
+    GDN_ERR_LDS_BUDGET = 5,    /* the kernel's LDS need exceeds 160 KiB per CU */
+    GDN_ERR_WORKSPACE = 6,     /* workspace missing or smaller than required */
+    GDN_ERR_HIP = 7            /* a HIP runtime call failed (see hipGetLastError) */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef enum gdn_gate {
+    GDN_GATE_HEAD = 0,         /* Gated DeltaNet: g [B,T,H] */
+    GDN_GATE_KEY = 1           /* KDA: g [B,T,H,K] */
+} gdn_gate;
+
+typedef struct gdn_problem {
+    int64_t B, T, H, K, V;     /* batch, tokens, heads, key dim, value dim */
+    int32_t chunk;             /* chunk size C: 32 or 64 */
+    int32_t io_dtype;          /* gdn_dtype of q, k, v */
+    int32_t o_dtype;           /* gdn_dtype of o */
+    int32_t gate;              /* gdn_gate */
+} gdn_problem;
+
+/*
+ * gdn_prepare -- per-chunk WY factors (fully parallel over chunks).
+ * For each (b, h) and chunk of C tokens (r, s index the chunk's rows):
+ *   gcum[r] = sum_{j<=r} g[j]                      (chunk-local, inclusive)
+ *   A[r,s]  = beta_r sum_d k[r,d] k[s,d] exp(gcum[r,d]-gcum[s,d]),  s < r
+ *   Tm      = (I + A)^-1                           (unit lower triangular)
+ *   w       = Tm diag(beta) (exp(gcum) * k)        (row r of k scaled by
+ *                                                   beta_r exp(gcum[r]))
+ *   u       = Tm diag(beta) v
+ * (TileOPs "Reuse P as beta tiles in gated deltanet fused prepare": A_g,
+ * S_shared = its inverse, w/u from k_beta/v_beta; the exp(gcum) factor on w
+ * is what makes the scan's v' = u - w h use the chunk-start state.)
+ * Inputs k [B,T,H,K], v [B,T,H,V] in io dtype; beta, g fp32.
+ * Outputs w [B,T,H,K], u [B,T,H,V], gcum (g's shape), all fp32, written in
+ * full.  problem->o_dtype is ignored.
+ */
+gdn_status gdn_prepare(const gdn_problem *problem, const void *k, const void *v,
+                       const float *beta, const float *g, float *w, float *u,
+                       float *gcum, void *stream);
+
+/*
+ * gdn_scan -- the serial inter-chunk scan, given gdn_prepare's outputs.
+ * For each (b, h), starting from h = h0[b,h] (K x V; zero if h0 is NULL),
+ * per chunk (kernel_fun KDA re-scan, per-chunk algebra of KdaB1ScanKernel):
+ *   v'  = u - w h
+ *   o   = (q * exp(gcum)) h + tril_incl((q k^T) * decay) v'
+ *            decay[r,s] = exp(gcum[r] - gcum[s])  (per key dim for KDA)
+ *   h  <- exp(gcum_last) * h + (k * exp(gcum_last - gcum))^T v'
+ * and finally hT[b,h] = h.  Inputs q, k in io dtype; w, u, gcum, h0 fp32.
+ * o [B,T,H,V] in o dtype; hT may be NULL (not written) or alias h0.
+ */
+gdn_status gdn_scan(const gdn_problem *problem, const void *q, const void *k,
+                    const float *w, const float *u, const float *gcum,
+                    const float *h0, void *o, float *hT, void *stream);
+
+/*
+ * gdn_forward -- the whole forward pass: o and the final state from q, k, v,
+ * beta, g and an optional h0 (NULL = zero state).  Results equal
+ * gdn_prepare followed by gdn_scan up to rounding.  `workspace` must hold
+ * gdn_workspace_bytes(problem) bytes (it may be NULL when that is 0); its
+ * contents on entry do not matter.  hT may be NULL or alias h0.
+ */
+gdn_status gdn_forward(const gdn_problem *problem, const void *q, const void *k,
+                       const void *v, const float *beta, const float *g,
+                       const float *h0, void *o, float *hT, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* Workspace gdn_forward needs for this problem (0 if none); 0 on bad args. */
+size_t gdn_workspace_bytes(const gdn_problem *problem);
+
+/* Static, human-readable name of a status code. */
+const char *gdn_status_str(gdn_status status);
+
+/* GDN_ABI_VERSION of the library that was loaded. */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBGDN_H */

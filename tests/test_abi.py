@@ -1,0 +1,134 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+include/libgdn.h declares, and rejects bad arguments before enqueuing any
+GPU work (every call below returns during validation, so none needs a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libgdn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import chunked_gated_delta_prepare_amd as gdn
+    if not os.path.exists(gdn.LIB_PATH):
+        from chunked_gated_delta_prepare_amd import build
+        build.build()
+    return gdn.load_library()
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import chunked_gated_delta_prepare_amd as m
+    return m
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*[A-Za-z_][\w \*]*?\b(gdn_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == sorted(
+        ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_workspace_bytes",
+         "gdn_status_str", "gdn_abi_version"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_binding_exports_match_header(gdn):
+    assert sorted(gdn.EXPORTS) == _declared_functions()
+
+
+def test_abi_version_and_status_strings(lib, gdn):
+    assert lib.gdn_abi_version() == gdn.ABI_VERSION
+    for code, name in gdn.STATUS.items():
+        assert lib.gdn_status_str(code).decode().startswith(name)
+    assert b"unknown" in lib.gdn_status_str(99)
+
+
+def test_header_enums_match_binding(gdn):
+    src = open(HEADER).read()
+    for code, name in gdn.STATUS.items():
+        assert re.search(r"\b%s = %d\b" % (name, code), src), name
+    assert re.search(r"GDN_F32 = 0", src) and re.search(r"GDN_BF16 = 1", src)
+    assert re.search(r"GDN_GATE_HEAD = 0", src) and re.search(r"GDN_GATE_KEY = 1", src)
+    assert re.search(r"#define GDN_ABI_VERSION %d\b" % gdn.ABI_VERSION, src)
+
+
+def _problem(gdn, B=1, T=64, H=1, K=64, V=64, chunk=64, io=1, o=1, gate=0):
+    return gdn.Problem(B, T, H, K, V, chunk, io, o, gate)
+
+
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def _fwd(lib, pr, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, h0=None, o=FAKE,
+         hT=None, ws=FAKE, ws_bytes=1 << 40):
+    return lib.gdn_forward(ctypes.byref(pr), q, k, v, beta, g, h0, o, hT, ws,
+                           ctypes.c_size_t(ws_bytes), None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("K", 96, 3), ("V", 32, 3), ("chunk", 16, 3), ("chunk", 128, 3),
+    ("io_dtype", 7, 3), ("o_dtype", 5, 3), ("gate", 2, 3),
+    ("B", 0, 2), ("H", 0, 2), ("T", -1, 2), ("K", 0, 2), ("chunk", 0, 2),
+])
+def test_bad_problem_rejected(lib, gdn, field, value, status):
+    pr = _problem(gdn)
+    setattr(pr, field, value)
+    assert _fwd(lib, pr) == status
+    assert lib.gdn_workspace_bytes(ctypes.byref(pr)) == 0
+
+
+def test_fp32_io_with_bf16_output_rejected(lib, gdn):
+    assert _fwd(lib, _problem(gdn, io=0, o=1)) == 3
+
+
+def test_null_problem_and_pointers(lib, gdn):
+    assert lib.gdn_forward(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                           FAKE, ctypes.c_size_t(1 << 40), None) == 1
+    pr = _problem(gdn)
+    for name in ("q", "k", "v", "beta", "g", "o"):
+        assert _fwd(lib, pr, **{name: None}) == 1, name
+    assert lib.gdn_prepare(ctypes.byref(pr), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                           None) == 1
+    assert lib.gdn_scan(ctypes.byref(pr), FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
+                        None, None) == 1
+
+
+def test_alignment_rejected(lib, gdn):
+    pr = _problem(gdn)
+    assert _fwd(lib, pr, q=MISALIGNED) == 4
+    assert _fwd(lib, pr, h0=MISALIGNED) == 4
+    assert _fwd(lib, pr, hT=MISALIGNED) == 4
+
+
+def test_workspace_checked(lib, gdn):
+    pr = _problem(gdn, B=2, T=100, H=3, K=64, V=128, gate=1)
+    need = lib.gdn_workspace_bytes(ctypes.byref(pr))
+    rows = 2 * 100 * 3
+    r = lambda x: (x + 255) // 256 * 256
+    assert need == r(rows * 64 * 4) + r(rows * 128 * 4) + r(rows * 64 * 4)
+    if need:
+        assert _fwd(lib, pr, ws_bytes=need - 1) == 6
+        assert _fwd(lib, pr, ws=None) == 6
+
+
+def test_lds_budget_reported_before_launch(lib, gdn):
+    # fp32 operands at K = 128 with 64-token chunks need more than 160 KiB of
+    # LDS in the scan: reported as a status, never attempted.
+    pr = _problem(gdn, B=1, T=0, H=1, K=128, V=128, chunk=64, io=0, o=0)
+    pr.T = 64
+    st = lib.gdn_scan(ctypes.byref(pr), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                      None, None)
+    assert st == 5
