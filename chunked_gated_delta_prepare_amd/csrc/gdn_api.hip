@@ -3,10 +3,12 @@
 // the caller's stream and returns; nothing allocates or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 
 #include "../../include/libgdn.h"
+#include "gdn_forward.h"
 #include "gdn_prepare.h"
 #include "gdn_scan.h"
 
@@ -32,6 +34,7 @@ gdn_status check_problem(const gdn_problem *pr) {
     const int64_t rows = pr->B * pr->T * pr->H;
     if (pr->T > (1 << 30) || rows > ((int64_t)1 << 31) / 8 || pr->B * pr->H > (1 << 24))
         return GDN_ERR_UNSUPPORTED;
+
     return GDN_OK;
 }
 
@@ -142,18 +145,61 @@ gdn_status enqueue_scan(const gdn_problem *pr, const void *q, const void *k,
     return pr->chunk == 32 ? scan_k<32>(pr, sp, grid, s) : scan_k<64>(pr, sp, grid, s);
 }
 
-size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
+// ---------------------------------------------------------------------------
+// forward (fused)
+// ---------------------------------------------------------------------------
+template <int C, int K, typename IO, typename OT, bool KG>
+gdn_status run_forward(FwdParams &fp, int grid, hipStream_t s) {
+    if constexpr (FwdLayout<C, K, IO, KG>::kBytes > kLdsBytesMax) {
+        return GDN_ERR_LDS_BUDGET;
+    } else {
+        return launch((const void *)&forward_kernel<C, K, IO, OT, KG>, grid, &fp, sizeof(fp), s);
+    }
+}
 
-struct WsPlan { size_t w, u, g, total; };
+template <int C, int K, typename IO, typename OT>
+gdn_status forward_gate(const gdn_problem *pr, FwdParams &fp, int grid, hipStream_t s) {
+    return pr->gate == GDN_GATE_KEY ? run_forward<C, K, IO, OT, true>(fp, grid, s)
+                                    : run_forward<C, K, IO, OT, false>(fp, grid, s);
+}
 
-WsPlan workspace_plan(const gdn_problem *pr) {
-    const size_t rows = (size_t)(pr->B * pr->T * pr->H);
-    WsPlan p;
-    p.w = round_up(rows * (size_t)pr->K * 4);
-    p.u = round_up(rows * (size_t)pr->V * 4);
-    p.g = round_up(rows * (size_t)(pr->gate == GDN_GATE_KEY ? pr->K : 1) * 4);
-    p.total = p.w + p.u + p.g;
-    return p;
+template <int C, int K>
+gdn_status forward_dt(const gdn_problem *pr, FwdParams &fp, int grid, hipStream_t s) {
+    if (pr->io_dtype == GDN_F32) return forward_gate<C, K, float, float>(pr, fp, grid, s);
+    if (pr->o_dtype == GDN_F32) return forward_gate<C, K, bf16_t, float>(pr, fp, grid, s);
+    return forward_gate<C, K, bf16_t, bf16_t>(pr, fp, grid, s);
+}
+
+template <int C>
+gdn_status forward_k(const gdn_problem *pr, FwdParams &fp, int grid, hipStream_t s) {
+    return pr->K == 64 ? forward_dt<C, 64>(pr, fp, grid, s) : forward_dt<C, 128>(pr, fp, grid, s);
+}
+
+// The fused kernel addresses one (batch, head) stream of each tensor with
+// 32-bit byte offsets from that stream's first token.
+bool fits_32bit_streams(const gdn_problem *pr) {
+    const int64_t sio = pr->io_dtype == GDN_F32 ? 4 : 2, so = pr->o_dtype == GDN_F32 ? 4 : 2;
+    const int64_t th = pr->T * pr->H;
+    const int64_t gdim = pr->gate == GDN_GATE_KEY ? pr->K : 1;
+    const int64_t worst = std::max({th * pr->K * sio, th * pr->V * sio, th * pr->V * so,
+                                    th * gdim * 4});
+    return worst < ((int64_t)1 << 32);
+}
+
+gdn_status enqueue_forward(const gdn_problem *pr, const void *q, const void *k,
+                           const void *v, const float *beta, const float *g,
+                           const float *h0, void *o, float *hT, hipStream_t s) {
+    if (!fits_32bit_streams(pr)) return GDN_ERR_UNSUPPORTED;
+    FwdParams fp;
+    fp.q = q; fp.k = k; fp.v = v; fp.beta = beta; fp.g = g; fp.h0 = h0;
+    fp.o = o; fp.hT = hT;
+    fp.B = (int)pr->B; fp.T = (int)pr->T; fp.H = (int)pr->H; fp.V = (int)pr->V;
+    fp.nvt = (int)(pr->V / 64);
+    const int pairs = (int)(pr->B * pr->H);
+    fp.swizzle = (pairs % 8 == 0) ? 1 : 0;
+    if (const char *e = std::getenv("GDN_NO_SWIZZLE")) fp.swizzle = (*e == '1') ? 0 : fp.swizzle;
+    const int grid = pairs * fp.nvt;
+    return pr->chunk == 32 ? forward_k<32>(pr, fp, grid, s) : forward_k<64>(pr, fp, grid, s);
 }
 
 }  // namespace
@@ -191,36 +237,27 @@ gdn_status gdn_scan(const gdn_problem *problem, const void *q, const void *k,
 }
 
 size_t gdn_workspace_bytes(const gdn_problem *problem) {
-    if (check_problem(problem) != GDN_OK) return 0;
-    return workspace_plan(problem).total;
+    (void)problem;
+    return 0;        // the fused kernel keeps every intermediate on chip
 }
 
 gdn_status gdn_forward(const gdn_problem *problem, const void *q, const void *k,
                        const void *v, const float *beta, const float *g,
                        const float *h0, void *o, float *hT, void *workspace,
                        size_t workspace_bytes, void *stream) {
+    (void)workspace;
+    (void)workspace_bytes;
     gdn_status st = check_problem(problem);
     if (st != GDN_OK) return st;
     if (problem->T == 0) {
         st = check_ptrs({}, {h0, hT});
         if (st != GDN_OK) return st;
         if (!hT) return GDN_OK;
-        return enqueue_scan(problem, nullptr, nullptr, nullptr, nullptr, nullptr, h0,
-                            nullptr, hT, (hipStream_t)stream);
+    } else {
+        st = check_ptrs({q, k, v, beta, g, o}, {h0, hT});
+        if (st != GDN_OK) return st;
     }
-    st = check_ptrs({q, k, v, beta, g, o}, {h0, hT});
-    if (st != GDN_OK) return st;
-    const WsPlan wp = workspace_plan(problem);
-    if (wp.total > 0) {
-        if (!workspace || workspace_bytes < wp.total) return GDN_ERR_WORKSPACE;
-        if (!aligned16(workspace)) return GDN_ERR_ALIGNMENT;
-    }
-    char *ws = (char *)workspace;
-    float *w = (float *)ws, *u = (float *)(ws + wp.w), *gc = (float *)(ws + wp.w + wp.u);
-    hipStream_t s = (hipStream_t)stream;
-    st = enqueue_prepare(problem, k, v, beta, g, w, u, gc, s);
-    if (st != GDN_OK) return st;
-    return enqueue_scan(problem, q, k, w, u, gc, h0, o, hT, s);
+    return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, (hipStream_t)stream);
 }
 
 const char *gdn_status_str(gdn_status status) {

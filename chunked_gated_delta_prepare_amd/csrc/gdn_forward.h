@@ -1,0 +1,594 @@
+// gdn_forward kernel: prepare and scan fused, one pass over q, k, v.
+//
+// One workgroup per (batch, head, 64-wide V tile), serial over chunks.  Per
+// chunk of C tokens with chunk-start state h (K x 64 slice, fp32 registers):
+//   gcum  chunk-local inclusive cumsum of g
+//   A     strictly lower beta * (k k^T * decay)           (Gram on the MFMA)
+//   Tm    (I + A)^-1                                        (blockwise, fp32)
+//   X     k h                     R' = v - e^gcum * X       (GDN)
+//   v'    Tm diag(beta) R'        (= u - w h of the WY form, without forming
+//                                   w or u: the KDA re-scan page's v')
+//   o     e^gcum * (q h) + P v'   P = tril_incl(q k^T * decay)
+//   h    <- e^gl h + (k * e^(gl - gcum))^T v'             (gl = last gcum)
+// For the per-key gate (KDA) every exponent is per key dimension; the decays
+// move into the operands around a reference row gm in the middle of the
+// chunk: q e^(g-gm), k e^(g-gm), k e^(gm-g), and h scaled by e^gm.
+//
+// Work split.  The state update is the serial chain; each wave owns 16 of the
+// tile's 64 value columns (its slice of h, v', o), so the chain is wave-local
+// and needs no barrier.  The chunk's shared operands (q, k, P, Tm) are built
+// cooperatively in phases separated by workgroup barriers:
+//   phase 0  registers -> LDS operands; gate cumsum and row factors; the next
+//            chunk's loads are issued
+//   phase 1  Gram tiles; diagonal 16x16 inverses and the first sub-diagonal
+//            merge by the wave that computed their Gram tiles
+//   phase 2  the remaining merges of the inverse (C = 64)
+//   phase 3  the wave-local chain
+// All HBM traffic is buffer loads/stores; a stream's byte range ends at token
+// T, so the rows of a short last chunk read as zero (an identity step: g = 0,
+// beta = 0, k = 0) and their outputs are dropped by the hardware.
+#pragma once
+
+#include "gdn_buffer.h"
+#include "gdn_chunk_io.h"
+#include "gdn_inverse.h"
+#include "gdn_scan.h"
+
+namespace gdn {
+
+struct FwdParams {
+    const void *q, *k, *v;
+    const float *beta, *g, *h0;
+    void *o;
+    float *hT;
+    int B, T, H, V;
+    int nvt;        // V / 64
+    int swizzle;
+};
+
+template <int C, int K, typename IO, bool KEYGATE>
+struct FwdLayout {
+    typedef typename OpOf<IO>::type OpT;
+    static constexpr int NB = C / 16;
+    static constexpr int LDK = K + Mma<OpT>::kPad;
+    static constexpr int LDC = C + Mma<OpT>::kPad;
+    static constexpr int LDA = C + 4;
+    static constexpr int E = sizeof(OpT);
+    static constexpr int kQ = 0;                                   // [C][LDK]
+    static constexpr int kK = kQ + C * LDK * E;                    // [C][LDK]
+    static constexpr int kKi = kK + C * LDK * E;                   // KDA: [C][LDK]
+    static constexpr int kTmb = kKi + (KEYGATE ? C * LDK * E : 0);  // [C][LDC] Tm diag(beta)
+    static constexpr int kP = kTmb + C * LDC * E;                  // [C][LDC]
+    static constexpr int kHT = kP + C * LDC * E;                   // 4 x [16][LDK]
+    // bf16 io: the v tile, raw bf16 [C][64 + 8]; fp32 io reads v from HBM
+    static constexpr bool kVinLds = sizeof(IO) == 2;
+    static constexpr int LDV = 64 + 8;
+    static constexpr int kVs = kHT + 4 * 16 * LDK * E;
+    static constexpr int kScr = kVs + (kVinLds ? C * LDV * 2 : 0);
+    // scratch: fp32 A and Tm of the inverse; after the inverse the per-wave
+    // R'/v' slabs (4 x [16][LDC]); for KDA the fp32 gcum rows [C][K] in phase 0
+    static constexpr int kA = kScr;
+    static constexpr int kTm = kA + C * LDA * 4;
+    static constexpr int kRD = kScr;
+    static constexpr int kGst = kScr;
+    static constexpr int kScrBytes0 = 2 * C * LDA * 4;
+    static constexpr int kScrBytes = (KEYGATE && C * K * 4 > kScrBytes0) ? C * K * 4 : kScrBytes0;
+    static_assert(4 * 16 * LDC * E <= kScrBytes0, "v' slabs must fit in the scratch");
+    // per-row / per-key fp32 factors
+    static constexpr int kRow = kScr + kScrBytes;
+    static constexpr int NSEG = kThreads / K;                      // KDA cumsum segments
+    static constexpr int kRowN = KEYGATE ? (C + 5 * K + NSEG * K) : (5 * C + NB * C + 4);
+    static constexpr int kBytes = kRow + kRowN * 4;
+};
+
+// Diagonal 16x16 inverses T_bb = (I + A_bb)^-1 for the blocks in [b0, b0+nb)
+// by one wave: lane (blk = l/16, column j = l%16) runs forward substitution
+// down its column (each row of A_bb is a broadcast read).  Writes T_bb to Tm.
+template <int LDA>
+__device__ __forceinline__ void diag_inverse(const float *A, float *Tm, int b0, int nb) {
+    const int l = lane_id(), blk = l >> 4, j = l & 15;
+    if (blk < nb) {
+        const int bb = b0 + blk;
+        const float *Ab = A + 16 * bb * LDA + 16 * bb;
+        float t[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float row[16];
+#pragma unroll
+            for (int kk = 0; kk < 16; kk += 4) {
+                if (kk < i) {
+                    const float4v a4 = *(const float4v *)(Ab + i * LDA + kk);
+                    row[kk] = a4[0]; row[kk + 1] = a4[1]; row[kk + 2] = a4[2]; row[kk + 3] = a4[3];
+                }
+            }
+            float s0 = (i == j) ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < i; kk += 2) {
+                s0 -= row[kk] * t[kk];
+                if (kk + 1 < i) s1 -= row[kk + 1] * t[kk + 1];
+            }
+            t[i] = s0 + s1;
+        }
+        float *Tb = Tm + 16 * bb * LDA + 16 * bb;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Tb[i * LDA + j] = t[i];
+    }
+}
+
+// Tm_ij = -T_ii * sum_{k=j}^{i-1} A_ik Tm_kj for one 16x16 block, one wave;
+// the result goes to Tm (fp32) and, scaled by beta of its columns, to Tmb.
+template <int LDA, int LDC, typename OpT>
+__device__ __forceinline__ void merge_block(const float *A, float *Tm, OpT *Tmb,
+                                            const float *bet, int i, int j) {
+    float4v x = {0, 0, 0, 0};
+    for (int k = j; k < i; ++k)
+        mm16_f32(x, A + 16 * i * LDA + 16 * k, LDA, Tm + 16 * k * LDA + 16 * j, LDA);
+    x = -x;
+    float4v y = {0, 0, 0, 0};
+    mm16_f32_regB(y, Tm + 16 * i * LDA + 16 * i, LDA, x);
+    const int col = 16 * j + acc_col();
+    const float bc = bet[col];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = 16 * i + acc_row(r);
+        Tm[row * LDA + col] = y[r];
+        Tmb[row * LDC + col] = Mma<OpT>::cvt(y[r] * bc);
+    }
+}
+
+// Copy a diagonal block of Tm into Tmb scaled by beta of its columns.  (The
+// blocks above the diagonal, which the chain's rounded-up k range also reads,
+// stay zero from the clear at kernel start.)
+template <int LDA, int LDC, typename OpT>
+__device__ __forceinline__ void emit_diag(const float *Tm, OpT *Tmb, const float *bet, int b) {
+    const int l = lane_id();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int idx = l + 64 * e, row = 16 * b + (idx >> 4), col = 16 * b + (idx & 15);
+        Tmb[row * LDC + col] = Mma<OpT>::cvt(Tm[row * LDA + col] * bet[col]);
+    }
+}
+
+// Four consecutive operand values of one row, one vector store.
+__device__ __forceinline__ void store_row4(_Float16 *dst, const float4v &a) {
+    half4 h;
+    h[0] = (_Float16)a[0]; h[1] = (_Float16)a[1]; h[2] = (_Float16)a[2]; h[3] = (_Float16)a[3];
+    *(half4 *)dst = h;
+}
+__device__ __forceinline__ void store_row4(float *dst, const float4v &a) { *(float4v *)dst = a; }
+
+template <int C, int K, typename IO, typename OT, bool KEYGATE>
+__global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
+    typedef FwdLayout<C, K, IO, KEYGATE> L;
+    typedef typename L::OpT OpT;
+    typedef Mma<OpT> M;
+    constexpr int LDK = L::LDK, LDC = L::LDC, LDA = L::LDA;
+    constexpr int NB = C / 16, NKB = K / 16;
+    constexpr int SIO = sizeof(IO), SO = sizeof(OT);
+    static_assert(L::kBytes <= kLdsBytesMax, "LDS budget");
+    static_assert(NB == 2 || NB == 4, "chunk 32 or 64");
+
+    __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
+    OpT *Qs = (OpT *)(smem + L::kQ);      // GDN q; KDA q e^(g - gm)
+    OpT *Ks = (OpT *)(smem + L::kK);      // GDN k; KDA k e^(g - gm)
+    OpT *Ki = KEYGATE ? (OpT *)(smem + L::kKi) : Ks;   // KDA k e^(gm - g)
+    OpT *Tmb = (OpT *)(smem + L::kTmb);
+    OpT *Ps = (OpT *)(smem + L::kP);
+    uint16_t *Vs = (uint16_t *)(smem + L::kVs);
+    float *Af = (float *)(smem + L::kA);
+    float *Tmf = (float *)(smem + L::kTm);
+    float *Gst = (float *)(smem + L::kGst);
+    float *rowf = (float *)(smem + L::kRow);
+    // GDN row factors
+    float *eg = rowf + C, *egl = rowf + 2 * C, *bet = rowf + 3 * C;
+    float *einv = rowf + 4 * C, *efac = rowf + 5 * C, *misc = rowf + 5 * C + NB * C;
+    // KDA key factors (beta takes the first C slots)
+    float *kbet = rowf, *gmv = rowf + C, *fsv = rowf + C + K, *flv = rowf + C + 2 * K;
+    float *fmv = rowf + C + 3 * K, *glv = rowf + C + 4 * K, *segt = rowf + C + 5 * K;
+    float *betp = KEYGATE ? kbet : bet;
+
+    const int wv = wave_id(), l = lane_id(), tid = threadIdx.x;
+    const int g4 = 4 * (l >> 4);                 // first accumulator row of this lane
+    OpT *HTw = (OpT *)(smem + L::kHT) + wv * 16 * LDK;     // this wave's h^T slice
+    OpT *RDw = (OpT *)(smem + L::kRD) + wv * 16 * LDC;     // this wave's R'/v' slab
+
+    int pair, vt;
+    map_block(blockIdx.x, p.nvt, p.swizzle, pair, vt);
+    const int b = pair / p.H, h = pair - b * p.H;
+    const int T = p.T, H = p.H, V = p.V;
+    const int vcol = vt * 64 + 16 * wv + acc_col();          // this lane's value column
+    const int nt = (T + C - 1) / C;
+
+    // ---- buffer descriptors: each covers this (b, h) stream up to token T
+    const int64_t row0 = (int64_t)b * T * H + h;
+    const uint32_t rsK = (uint32_t)(H * K), rsV = (uint32_t)(H * V);
+    const uint32_t rsG = KEYGATE ? rsK : (uint32_t)H;
+    const rsrc_t rq_ = make_rsrc((const IO *)p.q + row0 * K, (uint32_t)T * rsK * SIO);
+    const rsrc_t rk_ = make_rsrc((const IO *)p.k + row0 * K, (uint32_t)T * rsK * SIO);
+    const rsrc_t rv_ = make_rsrc((const IO *)p.v + row0 * V, (uint32_t)T * rsV * SIO);
+    const rsrc_t ro_ = make_rsrc((OT *)p.o + row0 * V, (uint32_t)T * rsV * SO);
+    const rsrc_t rg_ = make_rsrc(p.g + row0 * (KEYGATE ? K : 1), (uint32_t)T * rsG * 4);
+    const rsrc_t rb_ = make_rsrc(p.beta + row0, (uint32_t)T * (uint32_t)H * 4);
+
+    // per-thread constant offsets
+    constexpr int NVEC = C * K / 8 / kThreads;               // q/k vectors per thread
+    uint32_t qk_off[NVEC];
+#pragma unroll
+    for (int j = 0; j < NVEC; ++j) {
+        const int i = tid + kThreads * j, row = i / (K / 8), col = 8 * (i % (K / 8));
+        qk_off[j] = ((uint32_t)row * rsK + col) * SIO;
+    }
+    const uint32_t v_off = ((uint32_t)g4 * rsV + vcol) * SIO;
+    constexpr int NVV = L::kVinLds ? C * 64 / 8 / kThreads : 1;   // v vectors per thread
+    uint32_t vv_off[NVV];
+#pragma unroll
+    for (int j = 0; j < NVV; ++j) {
+        const int i = tid + kThreads * j, row = i / 8, col = 8 * (i % 8);
+        vv_off[j] = ((uint32_t)row * rsV + vt * 64 + col) * SIO;
+    }
+    const uint32_t o_off = ((uint32_t)g4 * rsV + vcol) * SO;
+    constexpr int NR = KEYGATE ? C * K / kThreads : 1;        // KDA gate rows per thread
+    const int kseg = KEYGATE ? tid / K : 0, kcol = KEYGATE ? tid % K : 0;
+    const uint32_t g_off = KEYGATE ? ((uint32_t)(kseg * NR) * rsG + kcol) * 4
+                                   : (uint32_t)l * rsG * 4;
+
+    // ---- state: hacc[i][r] = h[16 i + 4 (l/16) + r][vcol]
+    float4v hacc[NKB];
+    if (p.h0) {
+#pragma unroll
+        for (int i = 0; i < NKB; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                hacc[i][r] = p.h0[((int64_t)pair * K + 16 * i + g4 + r) * V + vcol];
+    } else {
+#pragma unroll
+        for (int i = 0; i < NKB; ++i) hacc[i] = float4v{0, 0, 0, 0};
+    }
+    // the operand tiles above the diagonal are read but stay zero
+    for (int i = tid; i < C * LDC; i += kThreads) {
+        Tmb[i] = (OpT)0.f;
+        Ps[i] = (OpT)0.f;
+    }
+
+    // ---- prefetch registers
+    Raw8B<IO> rq[NVEC], rk[NVEC];
+    Raw8B<IO> rvv[NVV];                // bf16 io: v rows
+    float vreg[L::kVinLds ? 1 : NB][4]; // fp32 io: v in accumulator layout
+    float g_own[NR];
+    float b_own = 0.f;
+    auto load_chunk = [&](int c) {
+        const uint32_t t0 = (uint32_t)(c * C);
+#pragma unroll
+        for (int j = 0; j < NVEC; ++j) {
+            rq[j].load(rq_, qk_off[j], t0 * rsK * SIO);
+            rk[j].load(rk_, qk_off[j], t0 * rsK * SIO);
+        }
+        if constexpr (L::kVinLds) {
+#pragma unroll
+            for (int j = 0; j < NVV; ++j) rvv[j].load(rv_, vv_off[j], t0 * rsV * SIO);
+        } else {
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    vreg[cb][r] = BufElem<IO>::load(rv_, v_off, (t0 + 16 * cb + r) * rsV * SIO);
+        }
+        if constexpr (KEYGATE) {
+#pragma unroll
+            for (int i = 0; i < NR; ++i)
+                g_own[i] = __uint_as_float(bload32(rg_, g_off, (t0 + i) * rsG * 4));
+        } else {
+            g_own[0] = __uint_as_float(bload32(rg_, g_off, t0 * rsG * 4));
+        }
+        b_own = __uint_as_float(bload32(rb_, (uint32_t)l * (uint32_t)H * 4, t0 * (uint32_t)H * 4));
+    };
+    if (nt > 0) load_chunk(0);
+
+    for (int c = 0; c < nt; ++c) {
+        const uint32_t t0 = (uint32_t)(c * C);
+
+        // ================= phase 0: operands into LDS =======================
+        float vcur[NB][4];
+        if constexpr (L::kVinLds) {
+#pragma unroll
+            for (int j = 0; j < NVV; ++j) {
+                const int i = tid + kThreads * j, row = i / 8, col = 8 * (i % 8);
+                *(u32x4 *)(Vs + row * L::LDV + col) = rvv[j].v;
+            }
+        } else {
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vcur[cb][r] = vreg[cb][r];
+        }
+        if (wv == 1 && l < C) betp[l] = b_own;
+        if constexpr (!KEYGATE) {
+#pragma unroll
+            for (int j = 0; j < NVEC; ++j) {
+                const int i = tid + kThreads * j, row = i / (K / 8), col = 8 * (i % (K / 8));
+                put_raw8(Qs + row * LDK + col, rq[j]);
+                put_raw8(Ks + row * LDK + col, rk[j]);
+            }
+            if (wv == 0) {
+                // inclusive scan of the gate down the chunk, then row factors
+                float x = l < C ? g_own[0] : 0.f;
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const float y = __shfl_up(x, d);
+                    if (l >= d) x += y;
+                }
+                const float gl = __shfl(x, C - 1);
+                const float gref = __shfl(x, l & ~15);      // gcum at the start of l's block
+                float ef[NB];
+#pragma unroll
+                for (int J = 0; J < NB; ++J) ef[J] = __shfl(x, 16 * J);
+                if (l < C) {
+                    eg[l] = fast_exp(x);
+                    egl[l] = fast_exp(gl - x);
+                    einv[l] = fast_exp(gref - x);
+#pragma unroll
+                    for (int J = 0; J < NB; ++J) efac[J * C + l] = fast_exp(x - ef[J]);
+                }
+                if (l == 0) misc[0] = fast_exp(gl);
+            }
+            if (c + 1 < nt) load_chunk(c + 1);
+            __syncthreads();
+        } else {
+            // gcum down each key column: thread (seg, kd) holds NR rows
+            float run = 0.f;
+#pragma unroll
+            for (int i = 0; i < NR; ++i) { run += g_own[i]; g_own[i] = run; }
+            segt[kseg * K + kcol] = run;
+            __syncthreads();
+            float off = 0.f;
+#pragma unroll
+            for (int sgi = 0; sgi < L::NSEG; ++sgi)
+                if (sgi < kseg) off += segt[sgi * K + kcol];
+            constexpr int MROW = C / 2 - 1;
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                const int row = kseg * NR + i;
+                const float gg = g_own[i] + off;
+                Gst[row * K + kcol] = gg;
+                if (row == MROW) gmv[kcol] = gg;
+                if (row == C - 1) glv[kcol] = gg;
+            }
+            __syncthreads();
+            if (tid < K) {
+                const float gm = gmv[tid], gl = glv[tid];
+                fsv[tid] = fast_exp(gm);
+                flv[tid] = fast_exp(gl);
+                fmv[tid] = fast_exp(gl - gm);
+            }
+#pragma unroll
+            for (int j = 0; j < NVEC; ++j) {
+                const int i = tid + kThreads * j, row = i / (K / 8), col = 8 * (i % (K / 8));
+                float xq[8], xk[8], a[8], bq[8], bk[8];
+                unpack_raw8(rq[j], xq);
+                unpack_raw8(rk[j], xk);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float d = Gst[row * K + col + e] - gmv[col + e];
+                    const float up = fast_exp(d), dn = fast_exp(-d);
+                    a[e] = xq[e] * up;
+                    bq[e] = xk[e] * up;
+                    bk[e] = xk[e] * dn;
+                }
+                put8(Qs + row * LDK + col, a);
+                put8(Ks + row * LDK + col, bq);
+                put8(Ki + row * LDK + col, bk);
+            }
+            if (c + 1 < nt) load_chunk(c + 1);
+            __syncthreads();
+        }
+
+        // ================= phase 1: Gram, diagonal inverses, first merges ===
+        // Tile (I, J) is computed transposed (rows s of block J against rows
+        // r of block I), so lane (l/16, j) ends up with row r = 16 I + j and
+        // four consecutive columns s = 16 J + 4 (l/16) + e: one vector store.
+        {
+            auto gram_tile = [&](int I, int J, bool isA) {
+                float4v acc = {0, 0, 0, 0};
+                mma_tile<OpT, K>(acc, Ki + 16 * J * LDK, LDK, (isA ? Ks : Qs) + 16 * I * LDK, LDK);
+                const int r = 16 * I + acc_col(), s0 = 16 * J + g4;
+                float4v fac = {1.f, 1.f, 1.f, 1.f};
+                if constexpr (!KEYGATE) {
+                    const float fr = efac[J * C + r];
+                    const float4v fi = *(const float4v *)(einv + s0);
+                    fac = fi * fr;
+                }
+                if (isA) {
+                    const float br = betp[r];
+                    float4v a;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) a[e] = (s0 + e < r) ? acc[e] * fac[e] * br : 0.f;
+                    *(float4v *)(Af + r * LDA + s0) = a;
+                } else {
+                    float4v a;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) a[e] = (s0 + e <= r) ? acc[e] * fac[e] : 0.f;
+                    store_row4(Ps + r * LDC + s0, a);
+                }
+            };
+            const int pb = 2 * wv;          // diagonal pair (pb, pb+1) for waves 0 .. NB/2-1
+            if (wv < NB / 2) {
+                gram_tile(pb, pb, true);
+                gram_tile(pb + 1, pb + 1, true);
+                gram_tile(pb + 1, pb, true);
+                diag_inverse<LDA>(Af, Tmf, pb, 2);
+                emit_diag<LDA, LDC, OpT>(Tmf, Tmb, betp, pb);
+                emit_diag<LDA, LDC, OpT>(Tmf, Tmb, betp, pb + 1);
+                merge_block<LDA, LDC, OpT>(Af, Tmf, Tmb, betp, pb + 1, pb);
+            }
+            // the other tiles, round robin over the waves that hold no pair
+            constexpr int NA_REST = (NB == 4) ? 4 : 0;    // A (2,0) (2,1) (3,0) (3,1)
+            constexpr int NP = NB * (NB + 1) / 2;
+            constexpr int NREST = NA_REST + NP;
+            constexpr int W0 = NB / 2, NW = kWaves - NB / 2;
+#pragma unroll
+            for (int t = 0; t < NREST; ++t) {
+                if (W0 + t % NW != wv) continue;
+                if (t < NA_REST) {
+                    gram_tile(2 + t / 2, t % 2, true);
+                } else {
+                    const int idx = t - NA_REST;
+                    int I = 0;
+                    while ((I + 1) * (I + 2) / 2 <= idx) ++I;
+                    gram_tile(I, idx - I * (I + 1) / 2, false);
+                }
+            }
+        }
+        __syncthreads();
+
+        // ================= phase 2: remaining merges (C = 64) ================
+        if constexpr (NB == 4) {
+            //   X = A_[23][01] T_[01];  Tm_[23][01] = -T_[23] X
+            const int i = 2 + (wv >> 1), j = wv & 1;
+            float4v x0 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
+            for (int k = j; k < 2; ++k)
+                mm16_f32(x0, Af + 32 * LDA + 16 * k, LDA, Tmf + 16 * k * LDA + 16 * j, LDA);
+            if (i == 3)
+                for (int k = j; k < 2; ++k)
+                    mm16_f32(x1, Af + 48 * LDA + 16 * k, LDA, Tmf + 16 * k * LDA + 16 * j, LDA);
+            x0 = -x0;
+            x1 = -x1;
+            float4v y = {0, 0, 0, 0};
+            if (i == 2) {
+                mm16_f32_regB(y, Tmf + 32 * LDA + 32, LDA, x0);            // T22 X2j
+            } else {
+                mm16_f32_regB(y, Tmf + 48 * LDA + 32, LDA, x0);            // T32 X2j
+                mm16_f32_regB(y, Tmf + 48 * LDA + 48, LDA, x1);            // T33 X3j
+            }
+            const int col = 16 * j + acc_col();
+            const float bc = betp[col];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Tmb[(16 * i + g4 + r) * LDC + col] = M::cvt(y[r] * bc);
+            __syncthreads();
+        }
+
+        // ================= phase 3: the wave-local chain =====================
+        {
+            float4v eg4[NB], egl4[NB];
+            float el = 1.f;
+            if constexpr (!KEYGATE) {
+#pragma unroll
+                for (int cb = 0; cb < NB; ++cb) {
+                    eg4[cb] = *(const float4v *)(eg + 16 * cb + g4);
+                    egl4[cb] = *(const float4v *)(egl + 16 * cb + g4);
+                }
+                el = misc[0];
+            }
+            // h^T slice (KDA: key rows scaled by e^gm, the reference of q, k)
+#pragma unroll
+            for (int i = 0; i < NKB; ++i) {
+                float4v hv = hacc[i];
+                if constexpr (KEYGATE) hv = hv * *(const float4v *)(fsv + 16 * i + g4);
+                store_T(HTw + 16 * i, LDK, hv);
+            }
+            // X = k h, Y = q h for this wave's 16 columns
+            typename M::frag hf[K / 32];
+#pragma unroll
+            for (int s = 0; s < K / 32; ++s) hf[s] = M::load(frag_ptr(HTw, LDK, 32 * s));
+            float4v xa[NB], ya[NB];
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) {
+                xa[cb] = float4v{0, 0, 0, 0};
+                ya[cb] = float4v{0, 0, 0, 0};
+#pragma unroll
+                for (int s = 0; s < K / 32; ++s) {
+                    const typename M::frag ak = M::load(frag_ptr(Ks + 16 * cb * LDK, LDK, 32 * s));
+                    const typename M::frag aq = M::load(frag_ptr(Qs + 16 * cb * LDK, LDK, 32 * s));
+                    M::mma(xa[cb], ak, hf[s]);
+                    M::mma(ya[cb], aq, hf[s]);
+                }
+            }
+            // R' = v - e^gcum X  (KDA: the decay is inside X already)
+            if constexpr (L::kVinLds) {
+                // v[16 cb + 4 (l/16) + e][this lane's column] for e = 0..3
+#pragma unroll
+                for (int cb = 0; cb < NB; ++cb) {
+                    const u32x2 w = read_T4(Vs + 16 * cb * L::LDV, L::LDV, 16 * wv);
+                    vcur[cb][0] = __uint_as_float(w[0] << 16);
+                    vcur[cb][1] = __uint_as_float(w[0] & 0xffff0000u);
+                    vcur[cb][2] = __uint_as_float(w[1] << 16);
+                    vcur[cb][3] = __uint_as_float(w[1] & 0xffff0000u);
+                }
+            }
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) {
+                const float4v vv = {vcur[cb][0], vcur[cb][1], vcur[cb][2], vcur[cb][3]};
+                float4v rr;
+                if constexpr (KEYGATE) rr = vv - xa[cb];
+                else rr = vv - eg4[cb] * xa[cb];
+                store_T(RDw + 16 * cb, LDC, rr);
+            }
+            // v' = Tm diag(beta) R'
+            typename M::frag rf[C / 32];
+#pragma unroll
+            for (int s = 0; s < C / 32; ++s) rf[s] = M::load(frag_ptr(RDw, LDC, 32 * s));
+            float4v da[NB];
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) {
+                da[cb] = float4v{0, 0, 0, 0};
+#pragma unroll
+                for (int s = 0; s < C / 32; ++s)
+                    if (32 * s < 16 * (cb + 1))
+                        M::mma(da[cb], M::load(frag_ptr(Tmb + 16 * cb * LDC, LDC, 32 * s)), rf[s]);
+            }
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) store_T(RDw + 16 * cb, LDC, da[cb]);
+            // o = e^gcum Y + P v'
+            typename M::frag df[C / 32];
+#pragma unroll
+            for (int s = 0; s < C / 32; ++s) df[s] = M::load(frag_ptr(RDw, LDC, 32 * s));
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) {
+                float4v oa = {0, 0, 0, 0};
+#pragma unroll
+                for (int s = 0; s < C / 32; ++s)
+                    if (32 * s < 16 * (cb + 1))
+                        M::mma(oa, M::load(frag_ptr(Ps + 16 * cb * LDC, LDC, 32 * s)), df[s]);
+                if constexpr (KEYGATE) oa = oa + ya[cb];
+                else oa = oa + eg4[cb] * ya[cb];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    BufElem<OT>::store(oa[r], ro_, o_off, (t0 + 16 * cb + r) * rsV * SO);
+            }
+            // h <- e^gl h + kg^T v'
+            if constexpr (!KEYGATE) {
+#pragma unroll
+                for (int cb = 0; cb < NB; ++cb) store_T(RDw + 16 * cb, LDC, da[cb] * egl4[cb]);
+#pragma unroll
+                for (int s = 0; s < C / 32; ++s) df[s] = M::load(frag_ptr(RDw, LDC, 32 * s));
+#pragma unroll
+                for (int i = 0; i < NKB; ++i) {
+                    hacc[i] = hacc[i] * el;
+#pragma unroll
+                    for (int s = 0; s < C / 32; ++s) M::mma(hacc[i], frag_T(Ks, LDK, 16 * i, 32 * s), df[s]);
+                }
+            } else {
+                // h = e^gl h + e^(gl - gm) (k e^(gm - g))^T v'
+#pragma unroll
+                for (int i = 0; i < NKB; ++i) {
+                    float4v acc = {0, 0, 0, 0};
+#pragma unroll
+                    for (int s = 0; s < C / 32; ++s) M::mma(acc, frag_T(Ki, LDK, 16 * i, 32 * s), df[s]);
+                    const float4v fl = *(const float4v *)(flv + 16 * i + g4);
+                    const float4v fm = *(const float4v *)(fmv + 16 * i + g4);
+                    hacc[i] = fl * hacc[i] + fm * acc;
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    if (p.hT) {
+#pragma unroll
+        for (int i = 0; i < NKB; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                p.hT[((int64_t)pair * K + 16 * i + g4 + r) * V + vcol] = hacc[i][r];
+    }
+}
+
+}  // namespace gdn

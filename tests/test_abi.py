@@ -113,15 +113,11 @@ def test_alignment_rejected(lib, gdn):
     assert _fwd(lib, pr, hT=MISALIGNED) == 4
 
 
-def test_workspace_checked(lib, gdn):
-    pr = _problem(gdn, B=2, T=100, H=3, K=64, V=128, gate=1)
-    need = lib.gdn_workspace_bytes(ctypes.byref(pr))
-    rows = 2 * 100 * 3
-    r = lambda x: (x + 255) // 256 * 256
-    assert need == r(rows * 64 * 4) + r(rows * 128 * 4) + r(rows * 64 * 4)
-    if need:
-        assert _fwd(lib, pr, ws_bytes=need - 1) == 6
-        assert _fwd(lib, pr, ws=None) == 6
+def test_forward_needs_no_workspace(lib, gdn):
+    # the fused forward keeps every intermediate on chip
+    for gate in (0, 1):
+        pr = _problem(gdn, B=2, T=100, H=3, K=64, V=128, gate=gate)
+        assert lib.gdn_workspace_bytes(ctypes.byref(pr)) == 0
 
 
 def test_lds_budget_reported_before_launch(lib, gdn):
