@@ -126,6 +126,17 @@ __device__ __forceinline__ Mma<float>::frag frag_T(const float *S, int ld, int m
     return f;
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt in [3:0] and [15:14], expcnt in
+// [6:4], lgkmcnt in [11:8]).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitVm0 = waitcnt_vm(0);
+constexpr int kWaitLgkm0 = (15) | (3 << 14) | (7 << 4);   // lgkmcnt(0), vmcnt/expcnt max
+
+// Raw staged vector (16 bytes) back from LDS.
+__device__ __forceinline__ void stage_get(Raw8B<bf16_t> &r, const uint16_t *p) {
+    r.v = *(const u32x4 *)p;
+}
+
 // Accumulator-layout read of a row-major 16-bit matrix S (pitch ld): lane
 // (g = l/16, j = l%16) gets S[4g + e][m0 + j] for e = 0..3 (one
 // ds_read_b64_tr_b16; lane L of each 16-lane group fetches row 4g + L/4,
@@ -136,6 +147,67 @@ __device__ __forceinline__ u32x2 read_T4(const uint16_t *S, int ld, int m0) {
     typedef __fp16 v4fp16 __attribute__((vector_size(8)));
     typedef __attribute__((address_space(3))) v4fp16 lds_v4fp16;
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_v4fp16 *)p));
+}
+
+// ---------------------------------------------------------------------------
+// Register-chained products.  The accumulator of a 16x16 tile C gives lane
+// (q = l/16, j = l%16) the rows 4q .. 4q+3 of column j.  Two such tiles that
+// cover rows 0..15 and 16..31 of a 32-wide k step therefore hand lane group q
+// eight distinct k values, {4q + e} and {16 + 4q + e} (e = 0..3), and column
+// j: exactly a B fragment, if the A fragment uses the same "split" k slots.
+// Products chained this way keep their intermediate in registers.
+// ---------------------------------------------------------------------------
+
+// B fragment from the accumulators of the k rows [k0, k0+16) and [k0+16, k0+32).
+__device__ __forceinline__ half8 fragB_acc(const float4v &lo, const float4v &hi, _Float16) {
+    half8 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        h[e] = (_Float16)lo[e];
+        h[4 + e] = (_Float16)hi[e];
+    }
+    return h;
+}
+__device__ __forceinline__ Mma<float>::frag fragB_acc(const float4v &lo, const float4v &hi, float) {
+    Mma<float>::frag f;
+    f.lo = lo;
+    f.hi = hi;
+    return f;
+}
+
+// A fragment with split k slots from a row-major S[m][k] (pitch ld): lane
+// (q, i) reads S[m0 + i][k0 + 4q .. +3] and S[m0 + i][k0 + 16 + 4q .. +3].
+__device__ __forceinline__ half8 fragA_split(const _Float16 *S, int ld, int m0, int k0) {
+    const int l = lane_id();
+    const _Float16 *p = S + (m0 + (l & 15)) * ld + k0 + 4 * (l >> 4);
+    const half4 a = *(const half4 *)p, b = *(const half4 *)(p + 16);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ Mma<float>::frag fragA_split(const float *S, int ld, int m0, int k0) {
+    const int l = lane_id();
+    const float *p = S + (m0 + (l & 15)) * ld + k0 + 4 * (l >> 4);
+    Mma<float>::frag f;
+    f.lo = *(const float4v *)p;
+    f.hi = *(const float4v *)(p + 16);
+    return f;
+}
+
+// A fragment with split k slots from the transpose of a row-major S[k][m]:
+// lane (q, i) gets S[k0 + 4q + e][m0 + i] and S[k0 + 16 + 4q + e][m0 + i].
+__device__ __forceinline__ half8 fragAT_split(const _Float16 *S, int ld, int m0, int k0) {
+    const half4 a = __builtin_bit_cast(half4, read_T4((const uint16_t *)(S + k0 * ld), ld, m0));
+    const half4 b = __builtin_bit_cast(half4, read_T4((const uint16_t *)(S + (k0 + 16) * ld), ld, m0));
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ Mma<float>::frag fragAT_split(const float *S, int ld, int m0, int k0) {
+    const int l = lane_id(), q = l >> 4, m = m0 + (l & 15);
+    Mma<float>::frag f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f.lo[e] = S[(k0 + 4 * q + e) * ld + m];
+        f.hi[e] = S[(k0 + 16 + 4 * q + e) * ld + m];
+    }
+    return f;
 }
 
 // Store an accumulator tile transposed, dst[n][m] (m contiguous), with one

@@ -59,21 +59,24 @@ struct FwdLayout {
     static constexpr int kKi = kK + C * LDK * E;                   // KDA: [C][LDK]
     static constexpr int kTmb = kKi + (KEYGATE ? C * LDK * E : 0);  // [C][LDC] Tm diag(beta)
     static constexpr int kP = kTmb + C * LDC * E;                  // [C][LDC]
-    static constexpr int kHT = kP + C * LDC * E;                   // 4 x [16][LDK]
-    // bf16 io: the v tile, raw bf16 [C][64 + 8]; fp32 io reads v from HBM
-    static constexpr bool kVinLds = sizeof(IO) == 2;
-    static constexpr int LDV = 64 + 8;
-    static constexpr int kVs = kHT + 4 * 16 * LDK * E;
-    static constexpr int kScr = kVs + (kVinLds ? C * LDV * 2 : 0);
-    // scratch: fp32 A and Tm of the inverse; after the inverse the per-wave
-    // R'/v' slabs (4 x [16][LDC]); for KDA the fp32 gcum rows [C][K] in phase 0
+    // bf16 io: chunk data is prefetched from HBM straight into LDS: raw q, k
+    // in per-thread vector order (each thread later converts the vectors its
+    // own lanes fetched), and the v tile row-major [C][64], double buffered
+    // because the chain of one chunk reads it while the next one lands.
+    // fp32 io prefetches into registers instead.
+    static constexpr bool kStage = sizeof(IO) == 2;
+    static constexpr int LDV = 64;
+    static constexpr int kSq = kP + C * LDC * E;
+    static constexpr int kSk = kSq + (kStage ? C * K * 2 : 0);
+    static constexpr int kVs = kSk + (kStage ? C * K * 2 : 0);
+    static constexpr int kScr = kVs + (kStage ? 2 * C * LDV * 2 : 0);
+    // scratch: fp32 A and Tm of the inverse; for KDA the fp32 gcum rows
+    // [C][K] in phase 0, before the Gram needs the space
     static constexpr int kA = kScr;
     static constexpr int kTm = kA + C * LDA * 4;
-    static constexpr int kRD = kScr;
     static constexpr int kGst = kScr;
     static constexpr int kScrBytes0 = 2 * C * LDA * 4;
     static constexpr int kScrBytes = (KEYGATE && C * K * 4 > kScrBytes0) ? C * K * 4 : kScrBytes0;
-    static_assert(4 * 16 * LDC * E <= kScrBytes0, "v' slabs must fit in the scratch");
     // per-row / per-key fp32 factors
     static constexpr int kRow = kScr + kScrBytes;
     static constexpr int NSEG = kThreads / K;                      // KDA cumsum segments
@@ -174,6 +177,8 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
     OpT *Ki = KEYGATE ? (OpT *)(smem + L::kKi) : Ks;   // KDA k e^(gm - g)
     OpT *Tmb = (OpT *)(smem + L::kTmb);
     OpT *Ps = (OpT *)(smem + L::kP);
+    uint16_t *Sq = (uint16_t *)(smem + L::kSq);
+    uint16_t *Sk = (uint16_t *)(smem + L::kSk);
     uint16_t *Vs = (uint16_t *)(smem + L::kVs);
     float *Af = (float *)(smem + L::kA);
     float *Tmf = (float *)(smem + L::kTm);
@@ -189,8 +194,6 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
 
     const int wv = wave_id(), l = lane_id(), tid = threadIdx.x;
     const int g4 = 4 * (l >> 4);                 // first accumulator row of this lane
-    OpT *HTw = (OpT *)(smem + L::kHT) + wv * 16 * LDK;     // this wave's h^T slice
-    OpT *RDw = (OpT *)(smem + L::kRD) + wv * 16 * LDC;     // this wave's R'/v' slab
 
     int pair, vt;
     map_block(blockIdx.x, p.nvt, p.swizzle, pair, vt);
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
         qk_off[j] = ((uint32_t)row * rsK + col) * SIO;
     }
     const uint32_t v_off = ((uint32_t)g4 * rsV + vcol) * SIO;
-    constexpr int NVV = L::kVinLds ? C * 64 / 8 / kThreads : 1;   // v vectors per thread
+    constexpr int NVV = L::kStage ? C * 64 / 8 / kThreads : 1;   // v vectors per thread
     uint32_t vv_off[NVV];
 #pragma unroll
     for (int j = 0; j < NVV; ++j) {
@@ -251,28 +254,15 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
     }
 
     // ---- prefetch registers
-    Raw8B<IO> rq[NVEC], rk[NVEC];
-    Raw8B<IO> rvv[NVV];                // bf16 io: v rows
-    float vreg[L::kVinLds ? 1 : NB][4]; // fp32 io: v in accumulator layout
+    constexpr int NRQ = L::kStage ? 1 : NVEC;
+    Raw8B<IO> rq[NRQ], rk[NRQ];         // fp32 io: q, k rows
+    float vreg[L::kStage ? 1 : NB][4];  // fp32 io: v in accumulator layout
     float g_own[NR];
     float b_own = 0.f;
+    // (the gate and beta loads go first: the staged loads are then the last
+    // memory operations of a chunk before its outputs are stored)
     auto load_chunk = [&](int c) {
         const uint32_t t0 = (uint32_t)(c * C);
-#pragma unroll
-        for (int j = 0; j < NVEC; ++j) {
-            rq[j].load(rq_, qk_off[j], t0 * rsK * SIO);
-            rk[j].load(rk_, qk_off[j], t0 * rsK * SIO);
-        }
-        if constexpr (L::kVinLds) {
-#pragma unroll
-            for (int j = 0; j < NVV; ++j) rvv[j].load(rv_, vv_off[j], t0 * rsV * SIO);
-        } else {
-#pragma unroll
-            for (int cb = 0; cb < NB; ++cb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    vreg[cb][r] = BufElem<IO>::load(rv_, v_off, (t0 + 16 * cb + r) * rsV * SIO);
-        }
         if constexpr (KEYGATE) {
 #pragma unroll
             for (int i = 0; i < NR; ++i)
@@ -281,6 +271,38 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
             g_own[0] = __uint_as_float(bload32(rg_, g_off, t0 * rsG * 4));
         }
         b_own = __uint_as_float(bload32(rb_, (uint32_t)l * (uint32_t)H * 4, t0 * (uint32_t)H * 4));
+        if constexpr (L::kStage) {
+#if defined(__HIP_DEVICE_COMPILE__)
+            // (device pass only: seen by the host pass, this builtin makes it
+            // drop the kernel's launch stub without a diagnostic)
+            // LDS destination of lane l: base + 16 l, base uniform per wave
+            typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+            for (int j = 0; j < NVEC; ++j) {
+                const int blk = (j * kThreads + wv * 64) * 8;     // in 16-bit elements
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rq_, (lds_void *)(Sq + blk), 16,
+                                                         qk_off[j], t0 * rsK * SIO, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk_, (lds_void *)(Sk + blk), 16,
+                                                         qk_off[j], t0 * rsK * SIO, 0, 0);
+            }
+            uint16_t *vdst = Vs + (c & 1) * C * L::LDV;
+#pragma unroll
+            for (int j = 0; j < NVV; ++j)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv_, (lds_void *)(vdst + (j * kThreads + wv * 64) * 8),
+                                                         16, vv_off[j], t0 * rsV * SIO, 0, 0);
+#endif
+        } else {
+#pragma unroll
+            for (int j = 0; j < NVEC; ++j) {
+                rq[j].load(rq_, qk_off[j], t0 * rsK * SIO);
+                rk[j].load(rk_, qk_off[j], t0 * rsK * SIO);
+            }
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    vreg[cb][r] = BufElem<IO>::load(rv_, v_off, (t0 + 16 * cb + r) * rsV * SIO);
+        }
     };
     if (nt > 0) load_chunk(0);
 
@@ -289,12 +311,11 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
 
         // ================= phase 0: operands into LDS =======================
         float vcur[NB][4];
-        if constexpr (L::kVinLds) {
-#pragma unroll
-            for (int j = 0; j < NVV; ++j) {
-                const int i = tid + kThreads * j, row = i / 8, col = 8 * (i % 8);
-                *(u32x4 *)(Vs + row * L::LDV + col) = rvv[j].v;
-            }
+        if constexpr (L::kStage) {
+            // this chunk's staged loads were issued a chunk ago; only the
+            // previous chunk's output stores may still be in flight after them
+            if (c == 0) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(NB * 4));
         } else {
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb)
@@ -306,8 +327,16 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
 #pragma unroll
             for (int j = 0; j < NVEC; ++j) {
                 const int i = tid + kThreads * j, row = i / (K / 8), col = 8 * (i % (K / 8));
-                put_raw8(Qs + row * LDK + col, rq[j]);
-                put_raw8(Ks + row * LDK + col, rk[j]);
+                if constexpr (L::kStage) {
+                    Raw8B<IO> xq, xk;
+                    stage_get(xq, Sq + i * 8);
+                    stage_get(xk, Sk + i * 8);
+                    put_raw8(Qs + row * LDK + col, xq);
+                    put_raw8(Ks + row * LDK + col, xk);
+                } else {
+                    put_raw8(Qs + row * LDK + col, rq[j]);
+                    put_raw8(Ks + row * LDK + col, rk[j]);
+                }
             }
             if (wv == 0) {
                 // inclusive scan of the gate down the chunk, then row factors
@@ -331,7 +360,8 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
                 }
                 if (l == 0) misc[0] = fast_exp(gl);
             }
-            if (c + 1 < nt) load_chunk(c + 1);
+            if constexpr (!L::kStage)
+                if (c + 1 < nt) load_chunk(c + 1);
             __syncthreads();
         } else {
             // gcum down each key column: thread (seg, kd) holds NR rows
@@ -364,8 +394,16 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
             for (int j = 0; j < NVEC; ++j) {
                 const int i = tid + kThreads * j, row = i / (K / 8), col = 8 * (i % (K / 8));
                 float xq[8], xk[8], a[8], bq[8], bk[8];
-                unpack_raw8(rq[j], xq);
-                unpack_raw8(rk[j], xk);
+                if constexpr (L::kStage) {
+                    Raw8B<IO> sq, sk;
+                    stage_get(sq, Sq + i * 8);
+                    stage_get(sk, Sk + i * 8);
+                    unpack_raw8(sq, xq);
+                    unpack_raw8(sk, xk);
+                } else {
+                    unpack_raw8(rq[j], xq);
+                    unpack_raw8(rk[j], xk);
+                }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float d = Gst[row * K + col + e] - gmv[col + e];
@@ -378,11 +416,17 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
                 put8(Ks + row * LDK + col, bq);
                 put8(Ki + row * LDK + col, bk);
             }
-            if (c + 1 < nt) load_chunk(c + 1);
+            if constexpr (!L::kStage)
+                if (c + 1 < nt) load_chunk(c + 1);
             __syncthreads();
         }
 
         // ================= phase 1: Gram, diagonal inverses, first merges ===
+        // Staged prefetch of the next chunk: issued here, after the barrier
+        // that retires this chunk's staging reads, so that a whole phase of
+        // work separates it from the next barrier (which waits for it).
+        if constexpr (L::kStage)
+            if (c + 1 < nt) load_chunk(c + 1);
         // Tile (I, J) is computed transposed (rows s of block J against rows
         // r of block I), so lane (l/16, j) ends up with row r = 16 I + j and
         // four consecutive columns s = 16 J + 4 (l/16) + e: one vector store.
@@ -467,6 +511,9 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
         }
 
         // ================= phase 3: the wave-local chain =====================
+        // Every intermediate (h, R', v') stays in registers: the accumulator
+        // of one product is the B fragment of the next (see fragB_acc), the
+        // shared operands come from LDS with matching split k slots.
         {
             float4v eg4[NB], egl4[NB];
             float el = 1.f;
@@ -478,17 +525,19 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
                 }
                 el = misc[0];
             }
-            // h^T slice (KDA: key rows scaled by e^gm, the reference of q, k)
-#pragma unroll
-            for (int i = 0; i < NKB; ++i) {
-                float4v hv = hacc[i];
-                if constexpr (KEYGATE) hv = hv * *(const float4v *)(fsv + 16 * i + g4);
-                store_T(HTw + 16 * i, LDK, hv);
-            }
-            // X = k h, Y = q h for this wave's 16 columns
+            // h as B fragments over the key dimension (KDA: rows scaled by
+            // e^gm, the reference of the q and k operands)
             typename M::frag hf[K / 32];
 #pragma unroll
-            for (int s = 0; s < K / 32; ++s) hf[s] = M::load(frag_ptr(HTw, LDK, 32 * s));
+            for (int s = 0; s < K / 32; ++s) {
+                float4v lo = hacc[2 * s], hi = hacc[2 * s + 1];
+                if constexpr (KEYGATE) {
+                    lo = lo * *(const float4v *)(fsv + 32 * s + g4);
+                    hi = hi * *(const float4v *)(fsv + 32 * s + 16 + g4);
+                }
+                hf[s] = fragB_acc(lo, hi, OpT{});
+            }
+            // X = k h, Y = q h for this wave's 16 columns
             float4v xa[NB], ya[NB];
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb) {
@@ -496,36 +545,33 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
                 ya[cb] = float4v{0, 0, 0, 0};
 #pragma unroll
                 for (int s = 0; s < K / 32; ++s) {
-                    const typename M::frag ak = M::load(frag_ptr(Ks + 16 * cb * LDK, LDK, 32 * s));
-                    const typename M::frag aq = M::load(frag_ptr(Qs + 16 * cb * LDK, LDK, 32 * s));
-                    M::mma(xa[cb], ak, hf[s]);
-                    M::mma(ya[cb], aq, hf[s]);
+                    M::mma(xa[cb], fragA_split(Ks, LDK, 16 * cb, 32 * s), hf[s]);
+                    M::mma(ya[cb], fragA_split(Qs, LDK, 16 * cb, 32 * s), hf[s]);
                 }
             }
             // R' = v - e^gcum X  (KDA: the decay is inside X already)
-            if constexpr (L::kVinLds) {
+            if constexpr (L::kStage) {
                 // v[16 cb + 4 (l/16) + e][this lane's column] for e = 0..3
 #pragma unroll
                 for (int cb = 0; cb < NB; ++cb) {
-                    const u32x2 w = read_T4(Vs + 16 * cb * L::LDV, L::LDV, 16 * wv);
+                    const u32x2 w = read_T4(Vs + (c & 1) * C * L::LDV + 16 * cb * L::LDV, L::LDV, 16 * wv);
                     vcur[cb][0] = __uint_as_float(w[0] << 16);
                     vcur[cb][1] = __uint_as_float(w[0] & 0xffff0000u);
                     vcur[cb][2] = __uint_as_float(w[1] << 16);
                     vcur[cb][3] = __uint_as_float(w[1] & 0xffff0000u);
                 }
             }
+            float4v rr[NB];
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb) {
                 const float4v vv = {vcur[cb][0], vcur[cb][1], vcur[cb][2], vcur[cb][3]};
-                float4v rr;
-                if constexpr (KEYGATE) rr = vv - xa[cb];
-                else rr = vv - eg4[cb] * xa[cb];
-                store_T(RDw + 16 * cb, LDC, rr);
+                if constexpr (KEYGATE) rr[cb] = vv - xa[cb];
+                else rr[cb] = vv - eg4[cb] * xa[cb];
             }
-            // v' = Tm diag(beta) R'
+            // v' = Tm diag(beta) R'   (lower triangular: k steps up to the diagonal)
             typename M::frag rf[C / 32];
 #pragma unroll
-            for (int s = 0; s < C / 32; ++s) rf[s] = M::load(frag_ptr(RDw, LDC, 32 * s));
+            for (int s = 0; s < C / 32; ++s) rf[s] = fragB_acc(rr[2 * s], rr[2 * s + 1], OpT{});
             float4v da[NB];
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb) {
@@ -533,21 +579,19 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
 #pragma unroll
                 for (int s = 0; s < C / 32; ++s)
                     if (32 * s < 16 * (cb + 1))
-                        M::mma(da[cb], M::load(frag_ptr(Tmb + 16 * cb * LDC, LDC, 32 * s)), rf[s]);
+                        M::mma(da[cb], fragA_split(Tmb, LDC, 16 * cb, 32 * s), rf[s]);
             }
-#pragma unroll
-            for (int cb = 0; cb < NB; ++cb) store_T(RDw + 16 * cb, LDC, da[cb]);
             // o = e^gcum Y + P v'
             typename M::frag df[C / 32];
 #pragma unroll
-            for (int s = 0; s < C / 32; ++s) df[s] = M::load(frag_ptr(RDw, LDC, 32 * s));
+            for (int s = 0; s < C / 32; ++s) df[s] = fragB_acc(da[2 * s], da[2 * s + 1], OpT{});
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb) {
                 float4v oa = {0, 0, 0, 0};
 #pragma unroll
                 for (int s = 0; s < C / 32; ++s)
                     if (32 * s < 16 * (cb + 1))
-                        M::mma(oa, M::load(frag_ptr(Ps + 16 * cb * LDC, LDC, 32 * s)), df[s]);
+                        M::mma(oa, fragA_split(Ps, LDC, 16 * cb, 32 * s), df[s]);
                 if constexpr (KEYGATE) oa = oa + ya[cb];
                 else oa = oa + eg4[cb] * ya[cb];
 #pragma unroll
@@ -557,14 +601,14 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
             // h <- e^gl h + kg^T v'
             if constexpr (!KEYGATE) {
 #pragma unroll
-                for (int cb = 0; cb < NB; ++cb) store_T(RDw + 16 * cb, LDC, da[cb] * egl4[cb]);
-#pragma unroll
-                for (int s = 0; s < C / 32; ++s) df[s] = M::load(frag_ptr(RDw, LDC, 32 * s));
+                for (int s = 0; s < C / 32; ++s)
+                    df[s] = fragB_acc(da[2 * s] * egl4[2 * s], da[2 * s + 1] * egl4[2 * s + 1], OpT{});
 #pragma unroll
                 for (int i = 0; i < NKB; ++i) {
                     hacc[i] = hacc[i] * el;
 #pragma unroll
-                    for (int s = 0; s < C / 32; ++s) M::mma(hacc[i], frag_T(Ks, LDK, 16 * i, 32 * s), df[s]);
+                    for (int s = 0; s < C / 32; ++s)
+                        M::mma(hacc[i], fragAT_split(Ks, LDK, 16 * i, 32 * s), df[s]);
                 }
             } else {
                 // h = e^gl h + e^(gl - gm) (k e^(gm - g))^T v'
@@ -572,7 +616,8 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
                 for (int i = 0; i < NKB; ++i) {
                     float4v acc = {0, 0, 0, 0};
 #pragma unroll
-                    for (int s = 0; s < C / 32; ++s) M::mma(acc, frag_T(Ki, LDK, 16 * i, 32 * s), df[s]);
+                    for (int s = 0; s < C / 32; ++s)
+                        M::mma(acc, fragAT_split(Ki, LDK, 16 * i, 32 * s), df[s]);
                     const float4v fl = *(const float4v *)(flv + 16 * i + g4);
                     const float4v fm = *(const float4v *)(fmv + 16 * i + g4);
                     hacc[i] = fl * hacc[i] + fm * acc;
