@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--o-dtype", default=None, choices=[None, "bf16", "fp32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of known size (counter scale)")
@@ -65,19 +65,41 @@ def forward_flops(w):
     return 2.0 * mac * w.B * w.T * w.H
 
 
-def scan_bytes(w, o_dtype):
-    """gdn_scan kernel: reads q, k (io), w, u, gcum (fp32), h0; writes o, hT."""
-    B, T, H, K, V = w.B, w.T, w.H, w.K, w.V
-    per_tok = (io_bytes(w.io) * 2 * K + 4 * K + 4 * V + 4 * (K if w.gate == "key" else 1)
-               + io_bytes(o_dtype) * V)
-    return B * T * H * per_tok + 4 * K * V * B * H * (2 if w.h0 else 1)
+def kernel_name(w, o_dtype):
+    """Template instance of the fused kernel that gdn_forward launches."""
+    io = {"bf16": "bf16_t", "fp32": "float"}
+    return "forward_kernel<%d, %d, %s, %s, %s>" % (w.chunk, w.K, io[w.io], io[o_dtype],
+                                                   "true" if w.gate == "key" else "false")
 
 
-def prepare_bytes(w):
-    """gdn_prepare kernel: reads k, v (io), beta, g; writes w, u, gcum (fp32)."""
-    B, T, H, K, V = w.B, w.T, w.H, w.K, w.V
-    g = 4 * (K if w.gate == "key" else 1)
-    return B * T * H * (io_bytes(w.io) * (K + V) + 4 + g + 4 * K + 4 * V + g)
+def source_digest():
+    """sha256 over the HIP sources and the public header: a traffic figure
+    measured on other sources no longer describes this kernel."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "chunked_gated_delta_prepare_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)
+                   if f.endswith((".h", ".hip")))
+    for p in files + [os.path.join(ROOT, "include", "libgdn.h")]:
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(w, o_dtype):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this kernel and workload (FETCH_SIZE and WRITE_SIZE, each scaled by what
+    the counter reads for a plain copy of known size), or None when there is
+    none or it was taken on different sources."""
+    path = os.path.join(ROOT, "profiles", "forward_kernel.%s.%s.traffic.json" % (w.name, o_dtype))
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != source_digest():
+        return None
+    return rec.get("traffic_bytes_per_launch")
 
 
 def main():
@@ -88,7 +110,6 @@ def main():
               % args.gpus, file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import chunked_gated_delta_prepare_amd as gdn
@@ -115,10 +136,12 @@ def main():
     tdt = {"bf16": torch.bfloat16, "fp32": torch.float32}[o_dtype]
     o = torch.empty(w.B, w.T, w.H, w.V, device=dev, dtype=tdt)
     hT = torch.empty(w.B, w.H, w.K, w.V, device=dev, dtype=torch.float32)
+    # the fused forward needs no workspace (gdn_workspace_bytes is 0); a
+    # nonzero size would be allocated here, outside the timed region
     ws_bytes = gdn.workspace_bytes(w.B, w.T, w.H, w.K, w.V, w.chunk,
                                    {"bf16": torch.bfloat16, "fp32": torch.float32}[w.io],
                                    w.gate == "key", tdt)
-    ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+    ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8) if ws_bytes else None
 
     def step():
         gdn.forward(d["q"], d["k"], d["v"], d["beta"], d["g"], w.chunk, d["h0"],
@@ -146,46 +169,29 @@ def main():
     print("bench: %d steps, %.4f ms/step (wall %.4f ms/step)"
           % (args.steps, ms_step, wall * 1e3 / args.steps), file=sys.stderr, flush=True)
 
-    # ---- per-kernel durations with events on the same stream: the forward
-    # runs gdn_prepare then gdn_scan; time each entry point alone
-    wbuf = torch.empty(w.B, w.T, w.H, w.K, device=dev, dtype=torch.float32)
-    ubuf = torch.empty(w.B, w.T, w.H, w.V, device=dev, dtype=torch.float32)
-    gbuf = torch.empty_like(d["g"])
-    gdn.prepare(d["k"], d["v"], d["beta"], d["g"], w.chunk, w=wbuf, u=ubuf, gcum=gbuf)
-    torch.cuda.synchronize()
-
-    def timed(fn, n):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # ---- the dominant (and only) kernel: gdn_forward is one launch of the
+    # fused forward kernel.  Each launch is bracketed by its own events on
+    # the stream the library launches on, and the durations averaged.
+    n_k = max(5, args.steps)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_k)]
+    for a, b in evs:
         a.record(stream)
-        for _ in range(n):
-            fn()
+        step()
         b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / n
-
-    n_k = max(5, args.steps // 2)
-    ms_prep = timed(lambda: gdn.prepare(d["k"], d["v"], d["beta"], d["g"], w.chunk,
-                                        w=wbuf, u=ubuf, gcum=gbuf), n_k)
-    ms_scan = timed(lambda: gdn.scan(d["q"], d["k"], wbuf, ubuf, gbuf, w.chunk, d["h0"],
-                                     o_dtype=tdt, o=o, hT=hT), n_k)
-    kernels = {
-        "prepare_kernel": {"ms": ms_prep, "bytes": prepare_bytes(w)},
-        "scan_kernel": {"ms": ms_scan, "bytes": scan_bytes(w, o_dtype)},
-    }
-    dom_name = max(kernels, key=lambda k: kernels[k]["ms"])
-    dom = kernels[dom_name]
-    achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
-    roofline = {"kernel": dom_name, "bound": "hbm", "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None, "ms_per_launch": round(dom["ms"], 5),
-                "algorithmic_bytes_per_launch": dom["bytes"]}
-
+    torch.cuda.synchronize()
+    ms_launch = sum(a.elapsed_time(b) for a, b in evs) / n_k
     fbytes, fflops = forward_bytes(w, o_dtype), forward_flops(w)
-    forward_frac = {
-        "hbm": round(fbytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "mfma_bf16": round(fflops / (ms_step * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
-        "algorithmic_bytes": fbytes, "algorithmic_flops": fflops,
-    }
+    achieved = fbytes / (ms_launch * 1e-3) / 1e9
+    mfma_peak = MFMA_PEAK_TFLOPS["f16" if w.io == "bf16" else "f32"]
+    roofline = {"kernel": kernel_name(w, o_dtype), "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(w, o_dtype),
+                "ms_per_launch": round(ms_launch, 5),
+                "algorithmic_bytes_per_launch": fbytes,
+                "algorithmic_flops_per_launch": fflops,
+                "mfma_frac": round(fflops / (ms_launch * 1e-3) / 1e12 / mfma_peak, 4),
+                "mfma_peak_tflops": mfma_peak}
 
     # ---- the oracle on the host's cores, on a bounded sample of the workload
     cpu = None
@@ -201,17 +207,16 @@ def main():
                    "chunk": w.chunk, "io": w.io, "o_dtype": o_dtype, "gate": w.gate,
                    "h0": w.h0, "parallelism": "single-gpu"},
         "roofline": roofline,
-        "forward_roofline_frac": forward_frac,
-        "kernels_ms": {k: round(v["ms"], 5) for k, v in kernels.items()},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
 
 def cpu_baseline(w, inp, target_s):
-    """Time the fp64 oracle on whole heads of the same workload, growing the
-    sample until it takes about target_s seconds (or covers every head)."""
-    import numpy as np
+    """Time the fp64 oracle on whole (batch, head) sequences of the same
+    workload: grow the sample until one pass takes a quarter of target_s (or
+    covers every sequence), then repeat that pass until about target_s of
+    wall time has been spent, and report the mean rate."""
     import oracle
 
     nthreads = min(os.cpu_count() or 1, 16)
@@ -221,23 +226,29 @@ def cpu_baseline(w, inp, target_s):
     beta, g = inp["beta"].numpy(), inp["g"].numpy()
     h0 = None if inp["h0"] is None else inp["h0"].numpy()
     pairs = w.B * w.H
-    n = min(pairs, nthreads)
-    spent = 0.0
-    while True:
-        heads = list(range(n))
+
+    def run(n):
         t0 = time.perf_counter()
-        oracle.token_recurrence(q, k, v, beta, g, h0, heads=heads, nthreads=nthreads,
+        oracle.token_recurrence(q, k, v, beta, g, h0, heads=list(range(n)), nthreads=nthreads,
                                 want_hT=False)
-        spent = time.perf_counter() - t0
+        return time.perf_counter() - t0
+
+    n = min(pairs, nthreads)
+    while True:
+        spent = run(n)
         if spent >= target_s / 4 or n >= pairs:
             break
         n = min(pairs, max(n + 1, int(n * min(8.0, target_s / max(spent, 1e-3)))))
-    token_heads_per_s = n * w.T / spent
+    times = [spent]
+    while sum(times) < target_s and len(times) < 100:
+        times.append(run(n))
+    token_heads_per_s = n * w.T * len(times) / sum(times)
     return {"value": round(token_heads_per_s / w.H, 1), "unit": "tokens/s",
             "cores": min(nthreads, n), "kind": "oracle",
-            "sample": "%d of %d (batch, head) sequences of %d tokens, fp64 token recurrence "
-                      "in C; tokens/s = token-heads/s / H" % (n, pairs, w.T),
-            "seconds": round(spent, 3)}
+            "sample": "%d of %d (batch, head) sequences of %d tokens, %d passes; fp64 token "
+                      "recurrence in C, one thread per sequence; tokens/s = token-heads/s / H"
+                      % (n, pairs, w.T, len(times)),
+            "seconds": round(sum(times), 3)}
 
 
 if __name__ == "__main__":
