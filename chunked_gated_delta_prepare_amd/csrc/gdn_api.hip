@@ -144,10 +144,10 @@ gdn_status enqueue_scan(const gdn_problem *pr, const void *q, const void *k,
 
 }  // namespace
 
-gdn_status launch_kernel(const void *fn, int grid, void *params, hipStream_t s) {
+gdn_status launch_kernel(const void *fn, int grid, void *params, hipStream_t s, int threads) {
     if (grid <= 0) return GDN_OK;
     void *args[] = {params};
-    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
+    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, s);
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 

@@ -9,6 +9,11 @@
 namespace gdn {
 namespace {
 
+bool pipe_disabled() {
+    const char *e = std::getenv("GDN_FORWARD_FOUR_WAVE");
+    return e && *e == '1';
+}
+
 // ---------------------------------------------------------------------------
 // forward (fused)
 // ---------------------------------------------------------------------------
@@ -21,10 +26,15 @@ gdn_status run_forward(FwdParams &fp, int grid, hipStream_t s) {
     }
 }
 
+// Scalar gate with bf16 io runs the pipelined kernel (prepare and re-scan on
+// separate waves); the per-key gate and fp32 io run the four-wave kernel.
 template <int C, int K, typename IO, typename OT>
 gdn_status forward_gate(const gdn_problem *pr, FwdParams &fp, int grid, hipStream_t s) {
-    return pr->gate == GDN_GATE_KEY ? run_forward<C, K, IO, OT, true>(fp, grid, s)
-                                    : run_forward<C, K, IO, OT, false>(fp, grid, s);
+    if (pr->gate == GDN_GATE_KEY) return run_forward<C, K, IO, OT, true>(fp, grid, s);
+    if constexpr (sizeof(IO) == 2) {
+        if (!pipe_disabled()) return enqueue_forward_pipe(C, K, sizeof(OT) == 4, fp, grid, s);
+    }
+    return run_forward<C, K, IO, OT, false>(fp, grid, s);
 }
 
 template <int C, int K>

@@ -1,0 +1,493 @@
+// gdn_forward, pipelined over chunks (scalar gate per head, bf16 io).
+//
+// The per-chunk algebra is the one of forward_kernel (gdn_forward.h): the
+// WY prepare of the TileOPs fused-prepare page (gate cumsum, decayed Gram,
+// (I + A)^-1) and the inter-chunk re-scan of the kernel-fun KDA re-scan page
+// (v' = Tm diag(beta) (v - e^gcum k h), o = e^gcum q h + P v', h update).
+//
+// What changes is the schedule.  Only the re-scan depends on the state h;
+// the prepare of a chunk needs nothing but that chunk's q, k, g and beta.  So
+// the workgroup has eight waves in two roles:
+//   chain waves 0..3   the re-scan of chunk c: h in MFMA accumulators, each
+//                      wave owns 16 of the tile's 64 value columns
+//   prepare waves 4..7 chunk c+1: fp16 q/k tiles, gate cumsum and row
+//                      factors, Gram tiles, the blockwise inverse Tm diag(beta)
+//                      and P; they also issue the loads of chunk c+2
+// and one workgroup barrier per chunk hands the prepared buffers over.  The
+// shared operands, the raw v tile included, are double buffered (slot c & 1).
+// The prepare waves hold the next chunk's q, k, v, g and beta in registers
+// (loaded a chunk ahead) and order their own phases with an LDS arrival
+// counter, so the chain waves never wait on them mid-chunk.
+//
+// q/k/Tm/P tiles are stored without padding, 16-byte chunks XOR-swizzled by
+// row, which keeps the transposed (ds_read_b64_tr_b16) fragment reads free
+// of bank conflicts inside the 160 KB budget.
+#pragma once
+
+#include "gdn_forward.h"
+
+namespace gdn {
+
+constexpr int kPipeThreads = 512;
+
+// Element (row, col) of an fp16 tile with rows of LD halves: the 16-byte
+// chunk j of row r sits at chunk position j ^ (r mod LD/8).
+template <int LD>
+__device__ __forceinline__ int swz(int row, int col) {
+    constexpr int NC = LD / 8;
+    return row * LD + (((col >> 3) ^ (row & (NC - 1))) << 3) + (col & 7);
+}
+
+// Lane (q, i): row r0 + i, columns k0 + 8q .. +7 (one 16-byte read).
+template <int LD>
+__device__ __forceinline__ half8 frag_sw(const _Float16 *S, int r0, int k0) {
+    const int l = lane_id();
+    return *(const half8 *)(S + swz<LD>(r0 + (l & 15), k0 + 8 * (l >> 4)));
+}
+
+// Split k slots (see fragA_split): row m0 + i, columns k0 + 4q and k0 + 16 + 4q.
+template <int LD>
+__device__ __forceinline__ half8 fragA_split_sw(const _Float16 *S, int m0, int k0) {
+    const int l = lane_id(), row = m0 + (l & 15), c0 = k0 + 4 * (l >> 4);
+    const half4 a = *(const half4 *)(S + swz<LD>(row, c0));
+    const half4 b = *(const half4 *)(S + swz<LD>(row, c0 + 16));
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Accumulator-layout transposed read (see read_T4): lane (g, j) gets
+// S[k0 + 4g + e][m0 + j], e = 0..3.
+template <int LD>
+__device__ __forceinline__ u32x2 read_T4_sw(const void *S, int k0, int m0) {
+    const int l = lane_id(), L = l & 15;
+    const _Float16 *p = (const _Float16 *)S + swz<LD>(k0 + 4 * (l >> 4) + (L >> 2), m0 + 4 * (L & 3));
+    typedef __fp16 v4fp16 __attribute__((vector_size(8)));
+    typedef __attribute__((address_space(3))) v4fp16 lds_v4fp16;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_v4fp16 *)p));
+}
+
+// Split-slot A fragment of S^T (see fragAT_split).
+template <int LD>
+__device__ __forceinline__ half8 fragAT_split_sw(const _Float16 *S, int m0, int k0) {
+    const half4 a = __builtin_bit_cast(half4, read_T4_sw<LD>(S, k0, m0));
+    const half4 b = __builtin_bit_cast(half4, read_T4_sw<LD>(S, k0 + 16, m0));
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations: vector
+// memory loads in flight (the prefetch of later chunks) stay in flight.
+__device__ __forceinline__ void wg_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Barrier of the four prepare waves: an LDS arrival counter that only grows
+// (four arrivals per barrier).  The wait is bounded so that no error can
+// leave a wave spinning; a normal wait is a few thousand cycles.
+__device__ __forceinline__ void prep_barrier(unsigned *ctr, unsigned &target) {
+    target += 4;
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    if (lane_id() == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (int it = 0; it < (1 << 16); ++it) {
+        const unsigned v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if ((unsigned)__builtin_amdgcn_readfirstlane((int)v) >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+}
+
+// Lane-shifted copy within rows of 16 lanes (DPP row_shr), zero where the
+// source lane falls before the row start.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row_shr(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
+template <int C, int K>
+struct PipeLayout {
+    static constexpr int NB = C / 16;
+    static constexpr int LDA = C + 4;                    // fp32 scratch pitch
+    static constexpr int kQK = C * K * 2;                // one fp16 q or k tile
+    static constexpr int kCC = C * C * 2;                // one fp16 C x C tile
+    static constexpr int kVT = C * 64 * 2;               // one bf16 v tile
+    static constexpr int kQ = 0;                         // [2] q tiles
+    static constexpr int kK = kQ + 2 * kQK;              // [2] k tiles
+    static constexpr int kTmb = kK + 2 * kQK;            // [2] Tm diag(beta)
+    static constexpr int kP = kTmb + 2 * kCC;            // [2] P
+    static constexpr int kV = kP + 2 * kCC;              // [2] raw v tiles
+    static constexpr int kA = kV + 2 * kVT;              // fp32 A   [C][LDA]
+    static constexpr int kTm = kA + C * LDA * 4;         // fp32 Tm  [C][LDA]
+    // chain-side row factors per slot: e^gcum, e^(gl - gcum), e^gl
+    static constexpr int kRowCN = 2 * C + 4;
+    static constexpr int kRowC = kTm + C * LDA * 4;      // [2][kRowCN]
+    // prepare-side row factors: beta, e^(gcum_block0 - gcum), e^(gcum - gcum_16J)
+    static constexpr int kRowP = kRowC + 2 * kRowCN * 4; // [C + C + NB C]
+    static constexpr int kSync = kRowP + (2 * C + NB * C) * 4;
+    static constexpr int kBytes = kSync + 16;
+};
+
+template <int C, int K, typename OT>
+__global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams p) {
+    typedef PipeLayout<C, K> L;
+    typedef Mma<_Float16> M;
+    typedef bf16_t IO;
+    constexpr int NB = C / 16, NKB = K / 16, LDA = L::LDA;
+    constexpr int SIO = 2, SO = sizeof(OT);
+    static_assert(L::kBytes <= kLdsBytesMax, "LDS budget");
+    static_assert(NB == 2 || NB == 4, "chunk 32 or 64");
+    static_assert(K == 64 || K == 128, "key dim 64 or 128");
+
+    __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
+    _Float16 *Qb = (_Float16 *)(smem + L::kQ);
+    _Float16 *Kb = (_Float16 *)(smem + L::kK);
+    _Float16 *Tmbb = (_Float16 *)(smem + L::kTmb);
+    _Float16 *Pb = (_Float16 *)(smem + L::kP);
+    uint16_t *Vb = (uint16_t *)(smem + L::kV);
+    float *Af = (float *)(smem + L::kA);
+    float *Tmf = (float *)(smem + L::kTm);
+    float *rowC = (float *)(smem + L::kRowC);
+    float *bet = (float *)(smem + L::kRowP);
+    float *einv = bet + C, *efac = bet + 2 * C;
+    unsigned *sync_ctr = (unsigned *)(smem + L::kSync);
+
+    const int wv = wave_id(), l = lane_id(), tid = threadIdx.x;
+    int pair, vt;
+    map_block(blockIdx.x, p.nvt, p.swizzle, pair, vt);
+    const int b = pair / p.H, h = pair - b * p.H;
+    const int T = p.T, H = p.H, V = p.V;
+    const int nt = (T + C - 1) / C;
+    const int64_t row0 = (int64_t)b * T * H + h;
+    const uint32_t rsK = (uint32_t)(H * K), rsV = (uint32_t)(H * V);
+
+    // the operand tiles above the diagonal are read but stay zero
+    for (int i = tid; i < 2 * C * C; i += kPipeThreads) {
+        Tmbb[i] = (_Float16)0.f;
+        Pb[i] = (_Float16)0.f;
+    }
+    if (tid == 0) *sync_ctr = 0u;
+    wg_barrier();
+
+    if (wv < 4) {
+        // =====================  chain waves  =============================
+        const rsrc_t ro_ = make_rsrc((OT *)p.o + row0 * V, (uint32_t)T * rsV * SO);
+        const int g4 = 4 * (l >> 4);
+        const int vcol = vt * 64 + 16 * wv + acc_col();
+        const uint32_t o_off = ((uint32_t)g4 * rsV + vcol) * SO;
+        float4v hacc[NKB];
+        if (p.h0) {
+#pragma unroll
+            for (int i = 0; i < NKB; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    hacc[i][r] = p.h0[((int64_t)pair * K + 16 * i + g4 + r) * V + vcol];
+        } else {
+#pragma unroll
+            for (int i = 0; i < NKB; ++i) hacc[i] = float4v{0, 0, 0, 0};
+        }
+        wg_barrier();                       // chunk 0 prepared
+
+        for (int c = 0; c < nt; ++c) {
+            const int slot = c & 1;
+            const _Float16 *Qs = Qb + slot * C * K, *Ks = Kb + slot * C * K;
+            const _Float16 *Tmb = Tmbb + slot * C * C, *Ps = Pb + slot * C * C;
+            const uint16_t *Vs = Vb + slot * C * 64;
+            const float *eg = rowC + slot * L::kRowCN, *egl = eg + C;
+            const float el = eg[2 * C];
+            const uint32_t t0 = (uint32_t)(c * C);
+
+            float4v eg4[NB], egl4[NB];
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) {
+                eg4[cb] = *(const float4v *)(eg + 16 * cb + g4);
+                egl4[cb] = *(const float4v *)(egl + 16 * cb + g4);
+            }
+            half8 hf[K / 32];
+#pragma unroll
+            for (int s = 0; s < K / 32; ++s) hf[s] = fragB_acc(hacc[2 * s], hacc[2 * s + 1], _Float16{});
+            // X = k h, Y = q h for this wave's 16 columns
+            float4v xa[NB], ya[NB];
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) {
+                xa[cb] = float4v{0, 0, 0, 0};
+                ya[cb] = float4v{0, 0, 0, 0};
+#pragma unroll
+                for (int s = 0; s < K / 32; ++s) {
+                    M::mma(xa[cb], fragA_split_sw<K>(Ks, 16 * cb, 32 * s), hf[s]);
+                    M::mma(ya[cb], fragA_split_sw<K>(Qs, 16 * cb, 32 * s), hf[s]);
+                }
+            }
+            // R' = v - e^gcum X
+            float4v rr[NB];
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) {
+                const u32x2 w = read_T4_sw<64>(Vs, 16 * cb, 16 * wv);
+                const float4v vv = {__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                                    __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+                rr[cb] = vv - eg4[cb] * xa[cb];
+            }
+            // v' = Tm diag(beta) R'
+            half8 rf[C / 32];
+#pragma unroll
+            for (int s = 0; s < C / 32; ++s) rf[s] = fragB_acc(rr[2 * s], rr[2 * s + 1], _Float16{});
+            float4v da[NB];
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) {
+                da[cb] = float4v{0, 0, 0, 0};
+#pragma unroll
+                for (int s = 0; s < C / 32; ++s)
+                    if (32 * s < 16 * (cb + 1)) M::mma(da[cb], fragA_split_sw<C>(Tmb, 16 * cb, 32 * s), rf[s]);
+            }
+            // o = e^gcum Y + P v'
+            half8 df[C / 32];
+#pragma unroll
+            for (int s = 0; s < C / 32; ++s) df[s] = fragB_acc(da[2 * s], da[2 * s + 1], _Float16{});
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) {
+                float4v oa = {0, 0, 0, 0};
+#pragma unroll
+                for (int s = 0; s < C / 32; ++s)
+                    if (32 * s < 16 * (cb + 1)) M::mma(oa, fragA_split_sw<C>(Ps, 16 * cb, 32 * s), df[s]);
+                oa = oa + eg4[cb] * ya[cb];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    BufElem<OT>::store(oa[r], ro_, o_off, (t0 + 16 * cb + r) * rsV * SO);
+            }
+            // h <- e^gl h + (k e^(gl - gcum))^T v'
+#pragma unroll
+            for (int s = 0; s < C / 32; ++s)
+                df[s] = fragB_acc(da[2 * s] * egl4[2 * s], da[2 * s + 1] * egl4[2 * s + 1], _Float16{});
+#pragma unroll
+            for (int i = 0; i < NKB; ++i) {
+                hacc[i] = hacc[i] * el;
+#pragma unroll
+                for (int s = 0; s < C / 32; ++s)
+                    M::mma(hacc[i], fragAT_split_sw<K>(Ks, 16 * i, 32 * s), df[s]);
+            }
+            wg_barrier();
+        }
+        if (p.hT) {
+#pragma unroll
+            for (int i = 0; i < NKB; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    p.hT[((int64_t)pair * K + 16 * i + g4 + r) * V + vcol] = hacc[i][r];
+        }
+    } else {
+        // =====================  prepare waves  ===========================
+        // The prepare is the longer of the two roles per chunk: its waves
+        // win instruction arbitration over the chain waves sharing a SIMD.
+        __builtin_amdgcn_s_setprio(3);
+        const int pw = wv - 4, pt = tid - 256;
+        const rsrc_t rq_ = make_rsrc((const IO *)p.q + row0 * K, (uint32_t)T * rsK * SIO);
+        const rsrc_t rk_ = make_rsrc((const IO *)p.k + row0 * K, (uint32_t)T * rsK * SIO);
+        const rsrc_t rv_ = make_rsrc((const IO *)p.v + row0 * V, (uint32_t)T * rsV * SIO);
+        const rsrc_t rg_ = make_rsrc(p.g + row0, (uint32_t)T * (uint32_t)H * 4);
+        const rsrc_t rb_ = make_rsrc(p.beta + row0, (uint32_t)T * (uint32_t)H * 4);
+
+        constexpr int NVEC = C * K / 8 / 256;            // q/k vectors per thread
+        constexpr int NVV = C * 64 / 8 / 256;            // v vectors per thread
+        static_assert(NVEC >= 1 && NVV >= 1, "tile smaller than the prepare waves");
+        uint32_t qk_off[NVEC];
+        int qk_lds[NVEC];
+#pragma unroll
+        for (int j = 0; j < NVEC; ++j) {
+            const int i = pt + 256 * j, row = i / (K / 8), ch = i % (K / 8);
+            qk_off[j] = ((uint32_t)row * rsK + 8 * ch) * SIO;
+            qk_lds[j] = swz<K>(row, 8 * ch);
+        }
+        uint32_t vv_off[NVV];
+        int vv_lds[NVV];
+#pragma unroll
+        for (int j = 0; j < NVV; ++j) {
+            const int i = pt + 256 * j, row = i / 8, ch = i % 8;
+            vv_off[j] = ((uint32_t)row * rsV + vt * 64 + 8 * ch) * SIO;
+            vv_lds[j] = swz<64>(row, 8 * ch);
+        }
+        const uint32_t gb_off = (uint32_t)l * (uint32_t)H * 4;
+
+        u32x4 rq[NVEC], rk[NVEC], rv[NVV];
+        float g_own = 0.f, b_own = 0.f;
+        auto issue_loads = [&](int n) {
+            const uint32_t t0 = (uint32_t)(n * C);
+#pragma unroll
+            for (int j = 0; j < NVV; ++j) rv[j] = bload128(rv_, vv_off[j], t0 * rsV * SIO);
+#pragma unroll
+            for (int j = 0; j < NVEC; ++j) {
+                rq[j] = bload128(rq_, qk_off[j], t0 * rsK * SIO);
+                rk[j] = bload128(rk_, qk_off[j], t0 * rsK * SIO);
+            }
+            if (pw == 0) {
+                g_own = __uint_as_float(bload32(rg_, gb_off, t0 * (uint32_t)H * 4));
+                b_own = __uint_as_float(bload32(rb_, gb_off, t0 * (uint32_t)H * 4));
+            }
+        };
+        unsigned sync_target = 0;
+
+        auto prepare = [&](int n) {
+            const int slot = n & 1;
+            _Float16 *Qs = Qb + slot * C * K, *Ks = Kb + slot * C * K;
+            _Float16 *Tmb = Tmbb + slot * C * C, *Ps = Pb + slot * C * C;
+            float *eg = rowC + slot * L::kRowCN, *egl = eg + C;
+            uint16_t *Vs = Vb + slot * C * 64;
+
+            // ---- operands, gate cumsum, row factors
+#pragma unroll
+            for (int j = 0; j < NVV; ++j) *(u32x4 *)(Vs + vv_lds[j]) = rv[j];
+#pragma unroll
+            for (int j = 0; j < NVEC; ++j) {
+                half8 hq, hk;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // bf16 -> fp16 is exact here (|q|, |k| <= 1)
+                    hq[2 * e] = (_Float16)__uint_as_float(rq[j][e] << 16);
+                    hq[2 * e + 1] = (_Float16)__uint_as_float(rq[j][e] & 0xffff0000u);
+                    hk[2 * e] = (_Float16)__uint_as_float(rk[j][e] << 16);
+                    hk[2 * e + 1] = (_Float16)__uint_as_float(rk[j][e] & 0xffff0000u);
+                }
+                *(half8 *)(Qs + qk_lds[j]) = hq;
+                *(half8 *)(Ks + qk_lds[j]) = hk;
+            }
+            if (pw == 0) {
+                // inclusive scan of the gate down the chunk: within rows of
+                // 16 lanes by DPP shifts, then the row totals
+                float x = l < C ? g_own : 0.f;
+                x += dpp_row_shr<0x111>(x);
+                x += dpp_row_shr<0x112>(x);
+                x += dpp_row_shr<0x114>(x);
+                x += dpp_row_shr<0x118>(x);
+                const float t0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
+                const float t1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+                const float t2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
+                const int rw = l >> 4;
+                x += (rw >= 1 ? t0 : 0.f) + (rw >= 2 ? t1 : 0.f) + (rw >= 3 ? t2 : 0.f);
+                float gblk[NB];
+#pragma unroll
+                for (int J = 0; J < NB; ++J)
+                    gblk[J] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16 * J));
+                const float gl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), C - 1));
+                if (l < C) {
+                    eg[l] = fast_exp(x);
+                    egl[l] = fast_exp(gl - x);
+                    bet[l] = b_own;
+                    float gref = gblk[0];
+#pragma unroll
+                    for (int J = 1; J < NB; ++J)
+                        if ((l >> 4) == J) gref = gblk[J];
+                    einv[l] = fast_exp(gref - x);
+#pragma unroll
+                    for (int J = 0; J < NB; ++J) efac[J * C + l] = fast_exp(x - gblk[J]);
+                }
+                if (l == 0) eg[2 * C] = fast_exp(gl);
+            }
+            if (n + 1 < nt) issue_loads(n + 1);
+            prep_barrier(sync_ctr, sync_target);
+
+            // ---- Gram tiles (transposed: lane (l/16, j) gets row r = 16 I + j
+            // and the four columns s = 16 J + 4 (l/16) + e), inverse, P
+            auto gram_tile = [&](int I, int J, bool isA) {
+                float4v acc = {0, 0, 0, 0};
+#pragma unroll
+                for (int k0 = 0; k0 < K; k0 += 32)
+                    M::mma(acc, frag_sw<K>(Ks, 16 * J, k0), frag_sw<K>(isA ? Ks : Qs, 16 * I, k0));
+                const int r = 16 * I + acc_col(), s0 = 16 * J + 4 * (l >> 4);
+                const float fr = efac[J * C + r];
+                const float4v fac = *(const float4v *)(einv + s0) * fr;
+                if (isA) {
+                    const float br = bet[r];
+                    float4v a;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) a[e] = (s0 + e < r) ? acc[e] * fac[e] * br : 0.f;
+                    *(float4v *)(Af + r * LDA + s0) = a;
+                } else {
+                    half4 a;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) a[e] = (_Float16)((s0 + e <= r) ? acc[e] * fac[e] : 0.f);
+                    *(half4 *)(Ps + swz<C>(r, s0)) = a;
+                }
+            };
+            auto put_tmb = [&](int row, int col, float x) {
+                Tmb[swz<C>(row, col)] = (_Float16)(x * bet[col]);
+            };
+            if (pw < NB / 2) {
+                const int pb = 2 * pw;
+                gram_tile(pb, pb, true);
+                gram_tile(pb + 1, pb + 1, true);
+                gram_tile(pb + 1, pb, true);
+                diag_inverse<LDA>(Af, Tmf, pb, 2);
+                // the two diagonal blocks, scaled by beta of their columns
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int idx = l + 64 * e, bb = pb + (idx >> 8), row = 16 * bb + ((idx >> 4) & 15),
+                              col = 16 * bb + (idx & 15);
+                    put_tmb(row, col, Tmf[row * LDA + col]);
+                }
+                // Tm_(pb+1, pb) = -T_(pb+1) A_(pb+1, pb) T_pb
+                float4v x = {0, 0, 0, 0};
+                mm16_f32(x, Af + 16 * (pb + 1) * LDA + 16 * pb, LDA, Tmf + 16 * pb * LDA + 16 * pb, LDA);
+                x = -x;
+                float4v y = {0, 0, 0, 0};
+                mm16_f32_regB(y, Tmf + 16 * (pb + 1) * LDA + 16 * (pb + 1), LDA, x);
+                const int col = 16 * pb + acc_col();
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * (pb + 1) + acc_row(r);
+                    Tmf[row * LDA + col] = y[r];
+                    put_tmb(row, col, y[r]);
+                }
+            }
+            constexpr int NA_REST = (NB == 4) ? 4 : 0;      // A (2,0) (2,1) (3,0) (3,1)
+            constexpr int NP = NB * (NB + 1) / 2;
+            constexpr int NREST = NA_REST + NP;
+            constexpr int W0 = NB / 2, NW = 4 - NB / 2;
+#pragma unroll
+            for (int t = 0; t < NREST; ++t) {
+                if (W0 + t % NW != pw) continue;
+                if (t < NA_REST) {
+                    gram_tile(2 + t / 2, t % 2, true);
+                } else {
+                    const int idx = t - NA_REST;
+                    int I = 0;
+                    while ((I + 1) * (I + 2) / 2 <= idx) ++I;
+                    gram_tile(I, idx - I * (I + 1) / 2, false);
+                }
+            }
+            if constexpr (NB == 4) {
+                prep_barrier(sync_ctr, sync_target);
+                //   X = A_[23][01] T_[01];  Tm_[23][01] = -T_[23] X
+                const int i = 2 + (pw >> 1), j = pw & 1;
+                float4v x0 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
+                for (int k = j; k < 2; ++k)
+                    mm16_f32(x0, Af + 32 * LDA + 16 * k, LDA, Tmf + 16 * k * LDA + 16 * j, LDA);
+                if (i == 3)
+                    for (int k = j; k < 2; ++k)
+                        mm16_f32(x1, Af + 48 * LDA + 16 * k, LDA, Tmf + 16 * k * LDA + 16 * j, LDA);
+                x0 = -x0;
+                x1 = -x1;
+                float4v y = {0, 0, 0, 0};
+                if (i == 2) {
+                    mm16_f32_regB(y, Tmf + 32 * LDA + 32, LDA, x0);            // T22 X2j
+                } else {
+                    mm16_f32_regB(y, Tmf + 48 * LDA + 32, LDA, x0);            // T32 X2j
+                    mm16_f32_regB(y, Tmf + 48 * LDA + 48, LDA, x1);            // T33 X3j
+                }
+                const int col = 16 * j + acc_col();
+#pragma unroll
+                for (int r = 0; r < 4; ++r) put_tmb(16 * i + acc_row(r), col, y[r]);
+            }
+        };
+
+        if (nt > 0) {
+            issue_loads(0);
+            prepare(0);
+        }
+        wg_barrier();                       // chunk 0 prepared
+        for (int c = 0; c < nt; ++c) {
+            if (c + 1 < nt) prepare(c + 1);
+            wg_barrier();
+        }
+    }
+}
+
+}  // namespace gdn

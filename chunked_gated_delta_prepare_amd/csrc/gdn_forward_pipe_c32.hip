@@ -1,0 +1,14 @@
+// libgdn: the pipelined forward kernel for chunk 32 with key dim 128, built
+// with the default machine scheduler (see gdn_forward_pipe.hip).
+#include "gdn_forward_pipe.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+gdn_status enqueue_forward_pipe_c32k128(bool o_f32, FwdParams &fp, int grid, hipStream_t s) {
+    const void *fn = o_f32 ? (const void *)&forward_pipe_kernel<32, 128, float>
+                           : (const void *)&forward_pipe_kernel<32, 128, bf16_t>;
+    return launch_kernel(fn, grid, &fp, s, kPipeThreads);
+}
+
+}  // namespace gdn

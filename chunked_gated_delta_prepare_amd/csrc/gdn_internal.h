@@ -7,12 +7,21 @@
 
 namespace gdn {
 
-// Launch a kernel with 256 threads per block and one by-value parameter struct.
-gdn_status launch_kernel(const void *fn, int grid, void *params, hipStream_t s);
+// Launch a kernel with one by-value parameter struct (256 threads per block
+// unless stated).
+gdn_status launch_kernel(const void *fn, int grid, void *params, hipStream_t s,
+                         int threads = 256);
 
 // Enqueue the fused forward kernel (validated problem, non-empty work).
 gdn_status enqueue_forward(const gdn_problem *pr, const void *q, const void *k,
                            const void *v, const float *beta, const float *g,
                            const float *h0, void *o, float *hT, hipStream_t s);
+
+struct FwdParams;
+// Launch the pipelined forward kernel (scalar gate, bf16 io) for chunk C,
+// key dim K and fp32 (else bf16) output.
+gdn_status enqueue_forward_pipe(int C, int K, bool o_f32, FwdParams &fp, int grid,
+                                hipStream_t s);
+gdn_status enqueue_forward_pipe_c32k128(bool o_f32, FwdParams &fp, int grid, hipStream_t s);
 
 }  // namespace gdn
