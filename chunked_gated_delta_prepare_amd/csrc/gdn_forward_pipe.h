@@ -38,20 +38,26 @@ __device__ __forceinline__ int swz(int row, int col) {
     return row * LD + (((col >> 3) ^ (row & (NC - 1))) << 3) + (col & 7);
 }
 
-// Lane (q, i): row r0 + i, columns k0 + 8q .. +7 (one 16-byte read).
+// Operand tiles keep their columns permuted within each 32-column group:
+// the 4-column group a (columns 4a .. 4a+3) sits at slot 2a for a < 4 and
+// at slot 2(a-4)+1 otherwise.  Lane group q's split k slots {4q .. 4q+3} and
+// {16+4q .. 16+4q+3} (see fragA_split) are then the one 16-byte chunk at
+// slots 2q, 2q+1, so every A fragment is a single aligned read.  Any
+// product over the permuted columns pairs equal positions on both sides, so
+// Gram tiles read the permuted tiles as they are.
+__device__ __forceinline__ int pcol(int col) {
+    const int a = (col >> 2) & 7;
+    const int slot = a < 4 ? 2 * a : 2 * a - 7;
+    return (col & ~31) | (slot << 2) | (col & 3);
+}
+
+// Lane (q, i): row r0 + i, stored columns k0 + 8q .. +7 (one 16-byte read).
+// On a permuted tile this is the split-slot A fragment of logical columns
+// k0 .. k0+31.
 template <int LD>
 __device__ __forceinline__ half8 frag_sw(const _Float16 *S, int r0, int k0) {
     const int l = lane_id();
     return *(const half8 *)(S + swz<LD>(r0 + (l & 15), k0 + 8 * (l >> 4)));
-}
-
-// Split k slots (see fragA_split): row m0 + i, columns k0 + 4q and k0 + 16 + 4q.
-template <int LD>
-__device__ __forceinline__ half8 fragA_split_sw(const _Float16 *S, int m0, int k0) {
-    const int l = lane_id(), row = m0 + (l & 15), c0 = k0 + 4 * (l >> 4);
-    const half4 a = *(const half4 *)(S + swz<LD>(row, c0));
-    const half4 b = *(const half4 *)(S + swz<LD>(row, c0 + 16));
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // Accumulator-layout transposed read (see read_T4): lane (g, j) gets
@@ -65,11 +71,21 @@ __device__ __forceinline__ u32x2 read_T4_sw(const void *S, int k0, int m0) {
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_v4fp16 *)p));
 }
 
-// Split-slot A fragment of S^T (see fragAT_split).
+// Split-slot A fragment of S^T (see fragAT_split) for a column-permuted S:
+// lane (g, L) fetches logical columns m0 + 4 (L % 4) .. +3, which are stored
+// contiguously at pcol(m0 + 4 (L % 4)).
 template <int LD>
-__device__ __forceinline__ half8 fragAT_split_sw(const _Float16 *S, int m0, int k0) {
-    const half4 a = __builtin_bit_cast(half4, read_T4_sw<LD>(S, k0, m0));
-    const half4 b = __builtin_bit_cast(half4, read_T4_sw<LD>(S, k0 + 16, m0));
+__device__ __forceinline__ half4 read_T4_p(const _Float16 *S, int k0, int m0) {
+    const int l = lane_id(), L = l & 15;
+    const _Float16 *p = S + swz<LD>(k0 + 4 * (l >> 4) + (L >> 2), pcol(m0 + 4 * (L & 3)));
+    typedef __fp16 v4fp16 __attribute__((vector_size(8)));
+    typedef __attribute__((address_space(3))) v4fp16 lds_v4fp16;
+    return __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_v4fp16 *)p));
+}
+template <int LD>
+__device__ __forceinline__ half8 fragAT_split_p(const _Float16 *S, int m0, int k0) {
+    const half4 a = read_T4_p<LD>(S, k0, m0);
+    const half4 b = read_T4_p<LD>(S, k0 + 16, m0);
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -103,6 +119,29 @@ __device__ __forceinline__ void prep_barrier(unsigned *ctr, unsigned &target) {
 template <int CTRL>
 __device__ __forceinline__ float dpp_row_shr(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
+// Four consecutive output values of one token: one 8-byte (bf16) or 16-byte
+// (fp32) buffer store.
+__device__ __forceinline__ void store4(const float4v &x, rsrc_t r, uint32_t voff, uint32_t soff) {
+    const uint32_t lo = (uint32_t)f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, r, voff, soff, 0);
+}
+template <typename OT>
+__device__ __forceinline__ void store4(const float4v &x, rsrc_t r, uint32_t voff, uint32_t soff);
+template <>
+__device__ __forceinline__ void store4<bf16_t>(const float4v &x, rsrc_t r, uint32_t voff, uint32_t soff) {
+    store4(x, r, voff, soff);
+}
+// (two 8-byte stores, not one 16-byte store: for vector-memory stores of
+// more than 8 bytes the compiler does not hold back a following write of the
+// data registers, and lanes then store the overwritten value)
+template <>
+__device__ __forceinline__ void store4<float>(const float4v &x, rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4 u = __builtin_bit_cast(u32x4, x);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{u[0], u[1]}, r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{u[2], u[3]}, r, voff + 8, soff, 0);
 }
 
 template <int C, int K>
@@ -174,7 +213,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
         const rsrc_t ro_ = make_rsrc((OT *)p.o + row0 * V, (uint32_t)T * rsV * SO);
         const int g4 = 4 * (l >> 4);
         const int vcol = vt * 64 + 16 * wv + acc_col();
-        const uint32_t o_off = ((uint32_t)g4 * rsV + vcol) * SO;
+        // o^T tiles: token (l % 16) of a 16-token block, columns 4 (l / 16) .. +3
+        const uint32_t o_off = ((uint32_t)(l & 15) * rsV + vt * 64 + 16 * wv + g4) * SO;
         float4v hacc[NKB];
         if (p.h0) {
 #pragma unroll
@@ -207,6 +247,9 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
 #pragma unroll
             for (int s = 0; s < K / 32; ++s) hf[s] = fragB_acc(hacc[2 * s], hacc[2 * s + 1], _Float16{});
             // X = k h, Y = q h for this wave's 16 columns
+            // (Y is formed transposed, Y^T = h^T q^T: the same fragments with
+            // the operands swapped, so a lane ends up with four consecutive
+            // value columns of one token)
             float4v xa[NB], ya[NB];
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb) {
@@ -214,8 +257,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                 ya[cb] = float4v{0, 0, 0, 0};
 #pragma unroll
                 for (int s = 0; s < K / 32; ++s) {
-                    M::mma(xa[cb], fragA_split_sw<K>(Ks, 16 * cb, 32 * s), hf[s]);
-                    M::mma(ya[cb], fragA_split_sw<K>(Qs, 16 * cb, 32 * s), hf[s]);
+                    M::mma(xa[cb], frag_sw<K>(Ks, 16 * cb, 32 * s), hf[s]);
+                    M::mma(ya[cb], hf[s], frag_sw<K>(Qs, 16 * cb, 32 * s));
                 }
             }
             // R' = v - e^gcum X
@@ -237,22 +280,20 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                 da[cb] = float4v{0, 0, 0, 0};
 #pragma unroll
                 for (int s = 0; s < C / 32; ++s)
-                    if (32 * s < 16 * (cb + 1)) M::mma(da[cb], fragA_split_sw<C>(Tmb, 16 * cb, 32 * s), rf[s]);
+                    if (32 * s < 16 * (cb + 1)) M::mma(da[cb], frag_sw<C>(Tmb, 16 * cb, 32 * s), rf[s]);
             }
-            // o = e^gcum Y + P v'
+            // o^T = v'^T P^T + Y^T diag(e^gcum): lane (g, j) holds token
+            // 16 cb + j, value columns 4g .. 4g+3 of this wave's 16
             half8 df[C / 32];
 #pragma unroll
             for (int s = 0; s < C / 32; ++s) df[s] = fragB_acc(da[2 * s], da[2 * s + 1], _Float16{});
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb) {
-                float4v oa = {0, 0, 0, 0};
+                float4v oa = eg[16 * cb + (l & 15)] * ya[cb];
 #pragma unroll
                 for (int s = 0; s < C / 32; ++s)
-                    if (32 * s < 16 * (cb + 1)) M::mma(oa, fragA_split_sw<C>(Ps, 16 * cb, 32 * s), df[s]);
-                oa = oa + eg4[cb] * ya[cb];
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    BufElem<OT>::store(oa[r], ro_, o_off, (t0 + 16 * cb + r) * rsV * SO);
+                    if (32 * s < 16 * (cb + 1)) M::mma(oa, df[s], frag_sw<C>(Ps, 16 * cb, 32 * s));
+                store4<OT>(oa, ro_, o_off, (t0 + 16 * cb) * rsV * SO);
             }
             // h <- e^gl h + (k e^(gl - gcum))^T v'
 #pragma unroll
@@ -263,7 +304,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                 hacc[i] = hacc[i] * el;
 #pragma unroll
                 for (int s = 0; s < C / 32; ++s)
-                    M::mma(hacc[i], fragAT_split_sw<K>(Ks, 16 * i, 32 * s), df[s]);
+                    M::mma(hacc[i], fragAT_split_p<K>(Ks, 16 * i, 32 * s), df[s]);
             }
             wg_barrier();
         }
@@ -290,12 +331,13 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
         constexpr int NVV = C * 64 / 8 / 256;            // v vectors per thread
         static_assert(NVEC >= 1 && NVV >= 1, "tile smaller than the prepare waves");
         uint32_t qk_off[NVEC];
-        int qk_lds[NVEC];
+        int qk_lds[NVEC][2];        // stored positions of the two 4-column halves
 #pragma unroll
         for (int j = 0; j < NVEC; ++j) {
             const int i = pt + 256 * j, row = i / (K / 8), ch = i % (K / 8);
             qk_off[j] = ((uint32_t)row * rsK + 8 * ch) * SIO;
-            qk_lds[j] = swz<K>(row, 8 * ch);
+            qk_lds[j][0] = swz<K>(row, pcol(8 * ch));
+            qk_lds[j][1] = swz<K>(row, pcol(8 * ch + 4));
         }
         uint32_t vv_off[NVV];
         int vv_lds[NVV];
@@ -346,8 +388,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                     hk[2 * e] = (_Float16)__uint_as_float(rk[j][e] << 16);
                     hk[2 * e + 1] = (_Float16)__uint_as_float(rk[j][e] & 0xffff0000u);
                 }
-                *(half8 *)(Qs + qk_lds[j]) = hq;
-                *(half8 *)(Ks + qk_lds[j]) = hk;
+                *(half4 *)(Qs + qk_lds[j][0]) = __builtin_shufflevector(hq, hq, 0, 1, 2, 3);
+                *(half4 *)(Qs + qk_lds[j][1]) = __builtin_shufflevector(hq, hq, 4, 5, 6, 7);
+                *(half4 *)(Ks + qk_lds[j][0]) = __builtin_shufflevector(hk, hk, 0, 1, 2, 3);
+                *(half4 *)(Ks + qk_lds[j][1]) = __builtin_shufflevector(hk, hk, 4, 5, 6, 7);
             }
             if (pw == 0) {
                 // inclusive scan of the gate down the chunk: within rows of
@@ -404,11 +448,11 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                     half4 a;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) a[e] = (_Float16)((s0 + e <= r) ? acc[e] * fac[e] : 0.f);
-                    *(half4 *)(Ps + swz<C>(r, s0)) = a;
+                    *(half4 *)(Ps + swz<C>(r, pcol(s0))) = a;
                 }
             };
             auto put_tmb = [&](int row, int col, float x) {
-                Tmb[swz<C>(row, col)] = (_Float16)(x * bet[col]);
+                Tmb[swz<C>(row, pcol(col))] = (_Float16)(x * bet[col]);
             };
             if (pw < NB / 2) {
                 const int pb = 2 * pw;

@@ -1,0 +1,71 @@
+"""Host-only checks of the gfx950 code objects inside libgdn.so (built here
+from this repository's sources): every kernel the dispatch can launch is
+present, and no vector-memory store writes more than 8 bytes per lane.
+
+The second rule guards against a miscompile seen with this toolchain: after
+a 12- or 16-byte buffer/global store, the compiler may let the next vector
+instruction overwrite the store's data registers before the store has read
+them, and some lanes then store the new value.  The kernels only use stores
+of at most 8 bytes, and this test keeps it that way."""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+LLVM = "/opt/rocm/llvm/bin"
+TARGET = "hipv4-amdgcn-amd-amdhsa--gfx950"
+MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
+
+
+def _tool(name):
+    path = os.path.join(LLVM, name)
+    if not os.path.exists(path):
+        pytest.skip("%s not available" % path)
+    return path
+
+
+@pytest.fixture(scope="module")
+def disassembly(tmp_path_factory):
+    import chunked_gated_delta_prepare_amd as gdn
+    if not os.path.exists(gdn.LIB_PATH):
+        from chunked_gated_delta_prepare_amd import build
+        build.build()
+    objcopy, bundler, objdump = (_tool("llvm-objcopy"), _tool("clang-offload-bundler"),
+                                 _tool("llvm-objdump"))
+    d = tmp_path_factory.mktemp("co")
+    fat = d / "fatbin.bin"
+    subprocess.run([objcopy, "--dump-section", ".hip_fatbin=%s" % fat, gdn.LIB_PATH], check=True)
+    data = fat.read_bytes()
+    # one offload bundle per translation unit, concatenated in the section
+    starts = [m.start() for m in re.finditer(re.escape(MAGIC), data)]
+    assert starts, "no offload bundle in libgdn.so"
+    text = []
+    for n, s in enumerate(starts):
+        e = starts[n + 1] if n + 1 < len(starts) else len(data)
+        b = d / ("b%d.bin" % n)
+        b.write_bytes(data[s:e])
+        co = d / ("co%d.o" % n)
+        subprocess.run([bundler, "--unbundle", "--type=o", "--targets=" + TARGET,
+                        "--input=%s" % b, "--output=%s" % co], check=True)
+        text.append(subprocess.run([objdump, "-d", str(co)], capture_output=True, text=True,
+                                   check=True).stdout)
+    yield "\n".join(text)
+    shutil.rmtree(d, ignore_errors=True)
+
+
+def test_no_vector_memory_store_wider_than_8_bytes(disassembly):
+    wide = re.findall(r"\b((?:buffer|global|flat)_store_(?:dwordx3|dwordx4|b96|b128))\b",
+                      disassembly)
+    assert not wide, "wide vector-memory stores in libgdn: %s" % sorted(set(wide))
+
+
+def test_every_dispatched_kernel_is_present(disassembly):
+    names = set(re.findall(r"^[0-9a-f]+ <(_ZN3gdn\w+)>:", disassembly, flags=re.M))
+    demangled = " ".join(names)
+    for kernel in ("forward_pipe_kernelILi64ELi128ENS_6bf16_t", "forward_pipe_kernelILi64ELi128Ef",
+                   "forward_pipe_kernelILi32ELi64ENS_6bf16_t", "forward_pipe_kernelILi32ELi128ENS_6bf16_t",
+                   "forward_kernelILi64ELi128ENS_6bf16_tES1_Lb1", "forward_kernelILi64ELi64EffLb0",
+                   "prepare_kernel", "scan_kernel"):
+        assert kernel in demangled, kernel
