@@ -3,7 +3,10 @@
 // The per-chunk algebra is the one of forward_kernel (gdn_forward.h): the
 // WY prepare of the TileOPs fused-prepare page (gate cumsum, decayed Gram,
 // (I + A)^-1) and the inter-chunk re-scan of the kernel-fun KDA re-scan page
-// (v' = Tm diag(beta) (v - e^gcum k h), o = e^gcum q h + P v', h update).
+// (v' = (I + A)^-1 diag(beta) (v - e^gcum k h), o = e^gcum q h + P v', h
+// update).  (I + A)^-1 is never formed whole: the prepare provides the
+// inverted 16 x 16 diagonal blocks and the blocks -T_bb A_bj, and the chain
+// finishes the triangular solve by blocks of 16 tokens.
 //
 // What changes is the schedule.  Only the re-scan depends on the state h;
 // the prepare of a chunk needs nothing but that chunk's q, k, g and beta.  So
@@ -11,8 +14,9 @@
 //   chain waves 0..3   the re-scan of chunk c: h in MFMA accumulators, each
 //                      wave owns 16 of the tile's 64 value columns
 //   prepare waves 4..7 chunk c+1: fp16 q/k tiles, gate cumsum and row
-//                      factors, Gram tiles, the blockwise inverse Tm diag(beta)
-//                      and P; they also issue the loads of chunk c+2
+//                      factors, Gram tiles, the inverted diagonal blocks and
+//                      the solve blocks, P; they also issue the loads of
+//                      chunk c+2
 // and one workgroup barrier per chunk hands the prepared buffers over.  The
 // shared operands, the raw v tile included, are double buffered (slot c & 1).
 // The prepare waves hold the next chunk's q, k, v, g and beta in registers
@@ -153,7 +157,7 @@ struct PipeLayout {
     static constexpr int kVT = C * 64 * 2;               // one bf16 v tile
     static constexpr int kQ = 0;                         // [2] q tiles
     static constexpr int kK = kQ + 2 * kQK;              // [2] k tiles
-    static constexpr int kTmb = kK + 2 * kQK;            // [2] Tm diag(beta)
+    static constexpr int kTmb = kK + 2 * kQK;            // [2] solve blocks (Tb, Mn)
     static constexpr int kP = kTmb + 2 * kCC;            // [2] P
     static constexpr int kV = kP + 2 * kCC;              // [2] raw v tiles
     static constexpr int kA = kV + 2 * kVT;              // fp32 A   [C][LDA]
@@ -270,17 +274,24 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                                     __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
                 rr[cb] = vv - eg4[cb] * xa[cb];
             }
-            // v' = Tm diag(beta) R'
-            half8 rf[C / 32];
-#pragma unroll
-            for (int s = 0; s < C / 32; ++s) rf[s] = fragB_acc(rr[2 * s], rr[2 * s + 1], _Float16{});
+            // v' solves (I + A) v' = diag(beta) R' by blocks of 16 tokens:
+            //   v'_b = Tb_bb R'_b + sum_{j<b} Mn_bj v'_j,
+            //   Tb_bb = (I + A_bb)^-1 diag(beta_b),  Mn_bj = -(I + A_bb)^-1 A_bj.
+            // Row block b of the C x C operand tile holds [Mn_b0 .. | Tb_bb | 0],
+            // so each step is a 32-wide k step over a [v' ; R'] fragment pair.
             float4v da[NB];
-#pragma unroll
-            for (int cb = 0; cb < NB; ++cb) {
-                da[cb] = float4v{0, 0, 0, 0};
-#pragma unroll
-                for (int s = 0; s < C / 32; ++s)
-                    if (32 * s < 16 * (cb + 1)) M::mma(da[cb], frag_sw<C>(Tmb, 16 * cb, 32 * s), rf[s]);
+            da[0] = float4v{0, 0, 0, 0};
+            M::mma(da[0], frag_sw<C>(Tmb, 0, 0), fragB_acc(rr[0], rr[1], _Float16{}));
+            da[1] = float4v{0, 0, 0, 0};
+            M::mma(da[1], frag_sw<C>(Tmb, 16, 0), fragB_acc(da[0], rr[1], _Float16{}));
+            if constexpr (NB == 4) {
+                da[2] = float4v{0, 0, 0, 0};
+                da[3] = float4v{0, 0, 0, 0};
+                M::mma(da[2], frag_sw<C>(Tmb, 32, 32), fragB_acc(rr[2], rr[3], _Float16{}));
+                const half8 d01 = fragB_acc(da[0], da[1], _Float16{});
+                M::mma(da[2], frag_sw<C>(Tmb, 32, 0), d01);
+                M::mma(da[3], frag_sw<C>(Tmb, 48, 0), d01);
+                M::mma(da[3], frag_sw<C>(Tmb, 48, 32), fragB_acc(da[2], rr[3], _Float16{}));
             }
             // o^T = v'^T P^T + Y^T diag(e^gcum): lane (g, j) holds token
             // 16 cb + j, value columns 4g .. 4g+3 of this wave's 16
@@ -452,7 +463,14 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                 }
             };
             auto put_tmb = [&](int row, int col, float x) {
-                Tmb[swz<C>(row, pcol(col))] = (_Float16)(x * bet[col]);
+                Tmb[swz<C>(row, pcol(col))] = (_Float16)x;
+            };
+            // Mn_ij = -T_ii A_ij for one 16 x 16 block, one wave
+            auto put_mn = [&](int i, int j) {
+                float4v x = {0, 0, 0, 0};
+                mm16_f32(x, Tmf + 16 * i * LDA + 16 * i, LDA, Af + 16 * i * LDA + 16 * j, LDA);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) put_tmb(16 * i + acc_row(r), 16 * j + acc_col(), -x[r]);
             };
             if (pw < NB / 2) {
                 const int pb = 2 * pw;
@@ -460,26 +478,14 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                 gram_tile(pb + 1, pb + 1, true);
                 gram_tile(pb + 1, pb, true);
                 diag_inverse<LDA>(Af, Tmf, pb, 2);
-                // the two diagonal blocks, scaled by beta of their columns
+                // Tb of the two diagonal blocks: T scaled by beta of its columns
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int idx = l + 64 * e, bb = pb + (idx >> 8), row = 16 * bb + ((idx >> 4) & 15),
                               col = 16 * bb + (idx & 15);
-                    put_tmb(row, col, Tmf[row * LDA + col]);
+                    put_tmb(row, col, Tmf[row * LDA + col] * bet[col]);
                 }
-                // Tm_(pb+1, pb) = -T_(pb+1) A_(pb+1, pb) T_pb
-                float4v x = {0, 0, 0, 0};
-                mm16_f32(x, Af + 16 * (pb + 1) * LDA + 16 * pb, LDA, Tmf + 16 * pb * LDA + 16 * pb, LDA);
-                x = -x;
-                float4v y = {0, 0, 0, 0};
-                mm16_f32_regB(y, Tmf + 16 * (pb + 1) * LDA + 16 * (pb + 1), LDA, x);
-                const int col = 16 * pb + acc_col();
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * (pb + 1) + acc_row(r);
-                    Tmf[row * LDA + col] = y[r];
-                    put_tmb(row, col, y[r]);
-                }
+                put_mn(pb + 1, pb);
             }
             constexpr int NA_REST = (NB == 4) ? 4 : 0;      // A (2,0) (2,1) (3,0) (3,1)
             constexpr int NP = NB * (NB + 1) / 2;
@@ -498,27 +504,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                 }
             }
             if constexpr (NB == 4) {
+                // Mn_20, Mn_21, Mn_30, Mn_31: T_22 and T_33 come from wave 1,
+                // the A blocks from waves 2 and 3
                 prep_barrier(sync_ctr, sync_target);
-                //   X = A_[23][01] T_[01];  Tm_[23][01] = -T_[23] X
-                const int i = 2 + (pw >> 1), j = pw & 1;
-                float4v x0 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
-                for (int k = j; k < 2; ++k)
-                    mm16_f32(x0, Af + 32 * LDA + 16 * k, LDA, Tmf + 16 * k * LDA + 16 * j, LDA);
-                if (i == 3)
-                    for (int k = j; k < 2; ++k)
-                        mm16_f32(x1, Af + 48 * LDA + 16 * k, LDA, Tmf + 16 * k * LDA + 16 * j, LDA);
-                x0 = -x0;
-                x1 = -x1;
-                float4v y = {0, 0, 0, 0};
-                if (i == 2) {
-                    mm16_f32_regB(y, Tmf + 32 * LDA + 32, LDA, x0);            // T22 X2j
-                } else {
-                    mm16_f32_regB(y, Tmf + 48 * LDA + 32, LDA, x0);            // T32 X2j
-                    mm16_f32_regB(y, Tmf + 48 * LDA + 48, LDA, x1);            // T33 X3j
-                }
-                const int col = 16 * j + acc_col();
-#pragma unroll
-                for (int r = 0; r < 4; ++r) put_tmb(16 * i + acc_row(r), col, y[r]);
+                put_mn(2 + (pw >> 1), pw & 1);
             }
         };
 
