@@ -441,11 +441,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
 
             // ---- Gram tiles (transposed: lane (l/16, j) gets row r = 16 I + j
             // and the four columns s = 16 J + 4 (l/16) + e), inverse, P
-            auto gram_tile = [&](int I, int J, bool isA) {
-                float4v acc = {0, 0, 0, 0};
-#pragma unroll
-                for (int k0 = 0; k0 < K; k0 += 32)
-                    M::mma(acc, frag_sw<K>(Ks, 16 * J, k0), frag_sw<K>(isA ? Ks : Qs, 16 * I, k0));
+            auto gram_store = [&](int I, int J, bool isA, const float4v &acc) {
                 const int r = 16 * I + acc_col(), s0 = 16 * J + 4 * (l >> 4);
                 const float fr = efac[J * C + r];
                 const float4v fac = *(const float4v *)(einv + s0) * fr;
@@ -462,45 +458,107 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                     *(half4 *)(Ps + swz<C>(r, pcol(s0))) = a;
                 }
             };
-            auto put_tmb = [&](int row, int col, float x) {
-                Tmb[swz<C>(row, pcol(col))] = (_Float16)x;
-            };
-            // Mn_ij = -T_ii A_ij for one 16 x 16 block, one wave
-            auto put_mn = [&](int i, int j) {
-                float4v x = {0, 0, 0, 0};
-                mm16_f32(x, Tmf + 16 * i * LDA + 16 * i, LDA, Af + 16 * i * LDA + 16 * j, LDA);
+            // Two tiles at once: every fragment load first, then the two
+            // accumulations interleaved (tile (I, J) reads k rows of block J
+            // as the A operand, rows of block I as the B operand).
+            auto gram_two = [&](int I0, int J0, bool a0, int I1, int J1, bool a1, bool two) {
+                half8 fa0[K / 32], fb0[K / 32], fa1[K / 32], fb1[K / 32];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) put_tmb(16 * i + acc_row(r), 16 * j + acc_col(), -x[r]);
+                for (int k = 0; k < K / 32; ++k) {
+                    fa0[k] = frag_sw<K>(Ks, 16 * J0, 32 * k);
+                    fb0[k] = frag_sw<K>(a0 ? Ks : Qs, 16 * I0, 32 * k);
+                    if (two) {
+                        fa1[k] = frag_sw<K>(Ks, 16 * J1, 32 * k);
+                        fb1[k] = frag_sw<K>(a1 ? Ks : Qs, 16 * I1, 32 * k);
+                    }
+                }
+                float4v acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+#pragma unroll
+                for (int k = 0; k < K / 32; ++k) {
+                    M::mma(acc0, fa0[k], fb0[k]);
+                    if (two) M::mma(acc1, fa1[k], fb1[k]);
+                }
+                gram_store(I0, J0, a0, acc0);
+                if (two) gram_store(I1, J1, a1, acc1);
+            };
+            // Mn_ij = -T_ii A_ij for one 16 x 16 block, one wave, formed as
+            // (A_ij^T T_ii^T) so that lane (g, n) ends with row n of the block,
+            // columns 4g .. 4g+3: one 8-byte store.
+            auto put_mn = [&](int i, int j) {
+                const int g = l >> 4, n = l & 15;
+                const float4v tb = *(const float4v *)(Tmf + (16 * i + n) * LDA + 16 * i + 4 * g);
+                float4v x = {0, 0, 0, 0};
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    x = __builtin_amdgcn_mfma_f32_16x16x4f32(Af[(16 * i + 4 * g + s) * LDA + 16 * j + n], tb[s],
+                                                             x, 0, 0, 0);
+                half4 h;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h[e] = (_Float16)(-x[e]);
+                *(half4 *)(Tmb + swz<C>(16 * i + n, pcol(16 * j + 4 * g))) = h;
             };
             if (pw < NB / 2) {
+                // the diagonal pair (pb, pb+1): A_pb,pb, A_pb+1,pb+1, A_pb+1,pb
                 const int pb = 2 * pw;
-                gram_tile(pb, pb, true);
-                gram_tile(pb + 1, pb + 1, true);
-                gram_tile(pb + 1, pb, true);
-                diag_inverse<LDA>(Af, Tmf, pb, 2);
-                // Tb of the two diagonal blocks: T scaled by beta of its columns
+                half8 f0[K / 32], f1[K / 32];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int idx = l + 64 * e, bb = pb + (idx >> 8), row = 16 * bb + ((idx >> 4) & 15),
-                              col = 16 * bb + (idx & 15);
-                    put_tmb(row, col, Tmf[row * LDA + col] * bet[col]);
+                for (int k = 0; k < K / 32; ++k) {
+                    f0[k] = frag_sw<K>(Ks, 16 * pb, 32 * k);
+                    f1[k] = frag_sw<K>(Ks, 16 * (pb + 1), 32 * k);
+                }
+                float4v a00 = {0, 0, 0, 0}, a11 = {0, 0, 0, 0}, a10 = {0, 0, 0, 0};
+#pragma unroll
+                for (int k = 0; k < K / 32; ++k) {
+                    M::mma(a00, f0[k], f0[k]);
+                    M::mma(a11, f1[k], f1[k]);
+                    M::mma(a10, f0[k], f1[k]);
+                }
+                gram_store(pb, pb, true, a00);
+                gram_store(pb + 1, pb + 1, true, a11);
+                gram_store(pb + 1, pb, true, a10);
+                diag_inverse<LDA>(Af, Tmf, pb, 2);
+                // Tb of the two diagonal blocks, T scaled by beta of its columns:
+                // 2 blocks x 16 rows x 4 column quads, two per lane
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int item = l + 64 * e, bb = pb + (item >> 6), row = 16 * bb + ((item & 63) >> 2),
+                              c4 = 16 * bb + 4 * (item & 3);
+                    const float4v t = *(const float4v *)(Tmf + row * LDA + c4) * *(const float4v *)(bet + c4);
+                    half4 h;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) h[q] = (_Float16)t[q];
+                    *(half4 *)(Tmb + swz<C>(row, pcol(c4))) = h;
                 }
                 put_mn(pb + 1, pb);
             }
+            // the other tiles, round robin over the waves that hold no pair,
+            // two at a time
             constexpr int NA_REST = (NB == 4) ? 4 : 0;      // A (2,0) (2,1) (3,0) (3,1)
             constexpr int NP = NB * (NB + 1) / 2;
             constexpr int NREST = NA_REST + NP;
             constexpr int W0 = NB / 2, NW = 4 - NB / 2;
+            // (tile coordinates are compile-time: t runs over an unrolled loop)
+            auto tile_I = [](int t) {
+                if (t < NA_REST) return 2 + t / 2;
+                int I = 0;
+                while ((I + 1) * (I + 2) / 2 <= t - NA_REST) ++I;
+                return I;
+            };
+            auto tile_J = [&](int t) {
+                if (t < NA_REST) return t % 2;
+                const int I = tile_I(t);
+                return t - NA_REST - I * (I + 1) / 2;
+            };
 #pragma unroll
-            for (int t = 0; t < NREST; ++t) {
-                if (W0 + t % NW != pw) continue;
-                if (t < NA_REST) {
-                    gram_tile(2 + t / 2, t % 2, true);
-                } else {
-                    const int idx = t - NA_REST;
-                    int I = 0;
-                    while ((I + 1) * (I + 2) / 2 <= idx) ++I;
-                    gram_tile(I, idx - I * (I + 1) / 2, false);
+            for (int t = 0; t < NREST; t += 2 * NW) {
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    const int t0 = t + w, t1 = t0 + NW;
+                    if (t0 >= NREST || W0 + w != pw) continue;
+                    if (t1 < NREST)
+                        gram_two(tile_I(t0), tile_J(t0), t0 < NA_REST, tile_I(t1), tile_J(t1), t1 < NA_REST, true);
+                    else
+                        gram_two(tile_I(t0), tile_J(t0), t0 < NA_REST, 0, 0, false, false);
                 }
             }
             if constexpr (NB == 4) {
