@@ -13,10 +13,11 @@
 // the workgroup has eight waves in two roles:
 //   chain waves 0..3   the re-scan of chunk c: h in MFMA accumulators, each
 //                      wave owns 16 of the tile's 64 value columns
-//   prepare waves 4..7 chunk c+1: fp16 q/k tiles, gate cumsum and row
-//                      factors, Gram tiles, the inverted diagonal blocks and
-//                      the solve blocks, P; they also issue the loads of
-//                      chunk c+2
+//   prepare waves 4..7 chunk c+1: fp16 q/k tiles, Gram tiles, the inverted
+//                      diagonal blocks and the solve blocks, P; they also
+//                      issue the loads of chunk c+2
+// Chain wave 0 also computes chunk c+1's gate cumsum and row factors at the
+// start of chunk c and signals the prepare waves through an LDS counter.
 // and one workgroup barrier per chunk hands the prepared buffers over.  The
 // shared operands, the raw v tile included, are double buffered (slot c & 1).
 // The prepare waves hold the next chunk's q, k, v, g and beta in registers
@@ -148,6 +149,64 @@ __device__ __forceinline__ void store4<float>(const float4v &x, rsrc_t r, uint32
     __builtin_amdgcn_raw_buffer_store_b64(u32x2{u[2], u[3]}, r, voff + 8, soff, 0);
 }
 
+// Inclusive scan of a chunk's scalar gate (lane l holds g of row l) and
+// the row factors the chunk needs, written by one wave: e^gcum, e^(gl-gcum),
+// e^gl for the chain; beta, e^(gcum_block - gcum), e^(gcum - gcum_16J) for
+// the Gram tiles.  (Within rows of 16 lanes by DPP shifts, then the row
+// totals.)
+template <int C>
+__device__ __forceinline__ void gate_factors(float g_own, float b_own, float *eg, float *bet) {
+    constexpr int NB = C / 16;
+    float *egl = eg + C, *einv = bet + C, *efac = bet + 2 * C;
+    const int l = lane_id();
+    float x = l < C ? g_own : 0.f;
+    x += dpp_row_shr<0x111>(x);
+    x += dpp_row_shr<0x112>(x);
+    x += dpp_row_shr<0x114>(x);
+    x += dpp_row_shr<0x118>(x);
+    const float t0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
+    const float t1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+    const float t2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
+    const int rw = l >> 4;
+    x += (rw >= 1 ? t0 : 0.f) + (rw >= 2 ? t1 : 0.f) + (rw >= 3 ? t2 : 0.f);
+    float gblk[NB];
+#pragma unroll
+    for (int J = 0; J < NB; ++J) gblk[J] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16 * J));
+    const float gl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), C - 1));
+    if (l < C) {
+        eg[l] = fast_exp(x);
+        egl[l] = fast_exp(gl - x);
+        bet[l] = b_own;
+        float gref = gblk[0];
+#pragma unroll
+        for (int J = 1; J < NB; ++J)
+            if ((l >> 4) == J) gref = gblk[J];
+        einv[l] = fast_exp(gref - x);
+#pragma unroll
+        for (int J = 0; J < NB; ++J) efac[J * C + l] = fast_exp(x - gblk[J]);
+    }
+    if (l == 0) eg[2 * C] = fast_exp(gl);
+}
+
+// Wait until an LDS counter reaches target (bounded, like prep_barrier).
+__device__ __forceinline__ void wait_counter(const unsigned *ctr, unsigned target) {
+    asm volatile("" ::: "memory");
+    for (int it = 0; it < (1 << 16); ++it) {
+        const unsigned v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if ((unsigned)__builtin_amdgcn_readfirstlane((int)v) >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+}
+
+// Count one arrival on an LDS counter once this wave's LDS writes are done.
+__device__ __forceinline__ void signal_counter(unsigned *ctr) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    if (lane_id() == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    asm volatile("" ::: "memory");
+}
+
 template <int C, int K>
 struct PipeLayout {
     static constexpr int NB = C / 16;
@@ -209,7 +268,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
         Tmbb[i] = (_Float16)0.f;
         Pb[i] = (_Float16)0.f;
     }
-    if (tid == 0) *sync_ctr = 0u;
+    if (tid == 0) {
+        sync_ctr[0] = 0u;                   // prepare waves' barrier
+        sync_ctr[1] = 0u;                   // chunks whose row factors are written
+    }
     wg_barrier();
 
     if (wv < 4) {
@@ -230,6 +292,24 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
 #pragma unroll
             for (int i = 0; i < NKB; ++i) hacc[i] = float4v{0, 0, 0, 0};
         }
+        // Chain wave 0 also scans the gate: chunk c+1's row factors at the
+        // start of chunk c (the prepare waves are converting operands
+        // meanwhile), from gate and beta loaded a chunk earlier.
+        const rsrc_t rg_ = make_rsrc(p.g + row0, (uint32_t)T * (uint32_t)H * 4);
+        const rsrc_t rb_ = make_rsrc(p.beta + row0, (uint32_t)T * (uint32_t)H * 4);
+        const uint32_t gb_off = (uint32_t)l * (uint32_t)H * 4;
+        float g_nx = 0.f, b_nx = 0.f;
+        auto gload = [&](int n) {
+            const uint32_t so = (uint32_t)(n * C) * (uint32_t)H * 4;
+            g_nx = __uint_as_float(bload32(rg_, gb_off, so));
+            b_nx = __uint_as_float(bload32(rb_, gb_off, so));
+        };
+        if (wv == 0 && nt > 0) {
+            gload(0);
+            gate_factors<C>(g_nx, b_nx, rowC, bet);
+            signal_counter(sync_ctr + 1);
+            if (nt > 1) gload(1);
+        }
         wg_barrier();                       // chunk 0 prepared
 
         for (int c = 0; c < nt; ++c) {
@@ -238,8 +318,13 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
             const _Float16 *Tmb = Tmbb + slot * C * C, *Ps = Pb + slot * C * C;
             const uint16_t *Vs = Vb + slot * C * 64;
             const float *eg = rowC + slot * L::kRowCN, *egl = eg + C;
-            const float el = eg[2 * C];
             const uint32_t t0 = (uint32_t)(c * C);
+            if (wv == 0 && c + 1 < nt) {
+                gate_factors<C>(g_nx, b_nx, rowC + (slot ^ 1) * L::kRowCN, bet);
+                signal_counter(sync_ctr + 1);
+                if (c + 2 < nt) gload(c + 2);
+            }
+            const float el = eg[2 * C];
 
             float4v eg4[NB], egl4[NB];
 #pragma unroll
@@ -335,8 +420,6 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
         const rsrc_t rq_ = make_rsrc((const IO *)p.q + row0 * K, (uint32_t)T * rsK * SIO);
         const rsrc_t rk_ = make_rsrc((const IO *)p.k + row0 * K, (uint32_t)T * rsK * SIO);
         const rsrc_t rv_ = make_rsrc((const IO *)p.v + row0 * V, (uint32_t)T * rsV * SIO);
-        const rsrc_t rg_ = make_rsrc(p.g + row0, (uint32_t)T * (uint32_t)H * 4);
-        const rsrc_t rb_ = make_rsrc(p.beta + row0, (uint32_t)T * (uint32_t)H * 4);
 
         constexpr int NVEC = C * K / 8 / 256;            // q/k vectors per thread
         constexpr int NVV = C * 64 / 8 / 256;            // v vectors per thread
@@ -358,10 +441,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
             vv_off[j] = ((uint32_t)row * rsV + vt * 64 + 8 * ch) * SIO;
             vv_lds[j] = swz<64>(row, 8 * ch);
         }
-        const uint32_t gb_off = (uint32_t)l * (uint32_t)H * 4;
 
         u32x4 rq[NVEC], rk[NVEC], rv[NVV];
-        float g_own = 0.f, b_own = 0.f;
         auto issue_loads = [&](int n) {
             const uint32_t t0 = (uint32_t)(n * C);
 #pragma unroll
@@ -371,10 +452,6 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                 rq[j] = bload128(rq_, qk_off[j], t0 * rsK * SIO);
                 rk[j] = bload128(rk_, qk_off[j], t0 * rsK * SIO);
             }
-            if (pw == 0) {
-                g_own = __uint_as_float(bload32(rg_, gb_off, t0 * (uint32_t)H * 4));
-                b_own = __uint_as_float(bload32(rb_, gb_off, t0 * (uint32_t)H * 4));
-            }
         };
         unsigned sync_target = 0;
 
@@ -382,10 +459,9 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
             const int slot = n & 1;
             _Float16 *Qs = Qb + slot * C * K, *Ks = Kb + slot * C * K;
             _Float16 *Tmb = Tmbb + slot * C * C, *Ps = Pb + slot * C * C;
-            float *eg = rowC + slot * L::kRowCN, *egl = eg + C;
             uint16_t *Vs = Vb + slot * C * 64;
 
-            // ---- operands, gate cumsum, row factors
+            // ---- operands (the row factors come from chain wave 0)
 #pragma unroll
             for (int j = 0; j < NVV; ++j) *(u32x4 *)(Vs + vv_lds[j]) = rv[j];
 #pragma unroll
@@ -404,39 +480,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                 *(half4 *)(Ks + qk_lds[j][0]) = __builtin_shufflevector(hk, hk, 0, 1, 2, 3);
                 *(half4 *)(Ks + qk_lds[j][1]) = __builtin_shufflevector(hk, hk, 4, 5, 6, 7);
             }
-            if (pw == 0) {
-                // inclusive scan of the gate down the chunk: within rows of
-                // 16 lanes by DPP shifts, then the row totals
-                float x = l < C ? g_own : 0.f;
-                x += dpp_row_shr<0x111>(x);
-                x += dpp_row_shr<0x112>(x);
-                x += dpp_row_shr<0x114>(x);
-                x += dpp_row_shr<0x118>(x);
-                const float t0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
-                const float t1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
-                const float t2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
-                const int rw = l >> 4;
-                x += (rw >= 1 ? t0 : 0.f) + (rw >= 2 ? t1 : 0.f) + (rw >= 3 ? t2 : 0.f);
-                float gblk[NB];
-#pragma unroll
-                for (int J = 0; J < NB; ++J)
-                    gblk[J] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16 * J));
-                const float gl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), C - 1));
-                if (l < C) {
-                    eg[l] = fast_exp(x);
-                    egl[l] = fast_exp(gl - x);
-                    bet[l] = b_own;
-                    float gref = gblk[0];
-#pragma unroll
-                    for (int J = 1; J < NB; ++J)
-                        if ((l >> 4) == J) gref = gblk[J];
-                    einv[l] = fast_exp(gref - x);
-#pragma unroll
-                    for (int J = 0; J < NB; ++J) efac[J * C + l] = fast_exp(x - gblk[J]);
-                }
-                if (l == 0) eg[2 * C] = fast_exp(gl);
-            }
             if (n + 1 < nt) issue_loads(n + 1);
+            wait_counter(sync_ctr + 1, (unsigned)(n + 1));     // chunk n's row factors
             prep_barrier(sync_ctr, sync_target);
 
             // ---- Gram tiles (transposed: lane (l/16, j) gets row r = 16 I + j
