@@ -66,8 +66,11 @@ def forward_flops(w):
 
 
 def kernel_name(w, o_dtype):
-    """Template instance of the fused kernel that gdn_forward launches."""
+    """Template instance of the kernel that gdn_forward launches: the
+    pipelined kernel for a scalar gate with bf16 io, else the four-wave one."""
     io = {"bf16": "bf16_t", "fp32": "float"}
+    if w.gate == "head" and w.io == "bf16":
+        return "forward_pipe_kernel<%d, %d, %s>" % (w.chunk, w.K, io[o_dtype])
     return "forward_kernel<%d, %d, %s, %s, %s>" % (w.chunk, w.K, io[w.io], io[o_dtype],
                                                    "true" if w.gate == "key" else "false")
 
@@ -92,7 +95,8 @@ def measured_traffic(w, o_dtype):
     this kernel and workload (FETCH_SIZE and WRITE_SIZE, each scaled by what
     the counter reads for a plain copy of known size), or None when there is
     none or it was taken on different sources."""
-    path = os.path.join(ROOT, "profiles", "forward_kernel.%s.%s.traffic.json" % (w.name, o_dtype))
+    short = kernel_name(w, o_dtype).split("<")[0]
+    path = os.path.join(ROOT, "profiles", "%s.%s.%s.traffic.json" % (short, w.name, o_dtype))
     if not os.path.exists(path):
         return None
     with open(path) as f:
