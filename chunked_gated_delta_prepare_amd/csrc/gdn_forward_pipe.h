@@ -207,6 +207,65 @@ __device__ __forceinline__ void signal_counter(unsigned *ctr) {
     asm volatile("" ::: "memory");
 }
 
+// Diagonal 16 x 16 inverses T_bb = (I + A_bb)^-1, bb = b0 and b0 + 1, by
+// one wave on the matrix cores.  The inverse is built by doubling the block
+// size s = 1, 2, 4, 8: with B the block-diagonal inverse at size s and L the
+// (2,1) blocks of size s inside each 2s-block of A, the inverse at size 2s is
+// B - B L B (the inverse of a 2 x 2 block lower-triangular matrix).  Every
+// factor is bounded (|A| < 1 entrywise, the partial inverses are O(1)), so
+// fp16 operands with fp32 accumulation keep T within a few fp16 roundings of
+// the exact inverse, the precision at which the chain uses it anyway.
+//
+// Two layouts of a 16 x 16 matrix M in lane (g, n) = (l / 16, l % 16):
+//   col layout  M[4g + r][n], r = 0..3: the MFMA B operand and its result
+//   row layout  M[n][4g + r]:           the MFMA A operand
+// X Y takes X in row and Y in col layout; Y^T X^T takes the same registers
+// with the roles swapped and returns X Y in row layout.
+// Result t[j]: row n of T_(b0+j), columns 4g .. 4g+3, fp32.
+template <int LDA>
+__device__ __forceinline__ void diag_inverse_mfma(const float *Af, int b0, float4v (&t)[2]) {
+    const int l = lane_id(), g = l >> 4, n = l & 15;
+    float4v ra[2], Bc[2], Br[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const float *Ab = Af + 16 * (b0 + j) * (LDA + 1);
+        ra[j] = *(const float4v *)(Ab + n * LDA + 4 * g);               // A[n][4g + r]
+        // s = 1: B = I minus the subdiagonal entries A[i][i-1] at odd rows i
+        const float sub1 = Ab[(4 * g + 1) * LDA + 4 * g], sub3 = Ab[(4 * g + 3) * LDA + 4 * g + 2];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 4 * g + r;
+            const float ca = (r & 1) && n == i - 1 ? (r == 1 ? sub1 : sub3) : 0.f;   // A[i][i-1]
+            const float rb = (n & 1) && i == n - 1 ? ra[j][r] : 0.f;                 // A[n][n-1]
+            Bc[j][r] = (i == n ? 1.f : 0.f) - ca;
+            Br[j][r] = (i == n ? 1.f : 0.f) - rb;
+        }
+    }
+#pragma unroll
+    for (int s = 2; s <= 8; s *= 2) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            half4 Lr, Bch, Brh;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 4 * g + r;
+                const bool inL = (n / (2 * s)) == (i / (2 * s)) && (n & s) && !(i & s);
+                Lr[r] = (_Float16)(inL ? ra[j][r] : 0.f);
+                Bch[r] = (_Float16)Bc[j][r];
+                Brh[r] = (_Float16)Br[j][r];
+            }
+            const float4v x = __builtin_amdgcn_mfma_f32_16x16x16f16(Lr, Bch, float4v{0, 0, 0, 0}, 0, 0, 0);
+            half4 xn;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) xn[r] = (_Float16)(-x[r]);
+            if (s < 8) Bc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(Brh, xn, Bc[j], 0, 0, 0);
+            Br[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(xn, Brh, Br[j], 0, 0, 0);
+        }
+    }
+    t[0] = Br[0];
+    t[1] = Br[1];
+}
+
 template <int C, int K>
 struct PipeLayout {
     static constexpr int NB = C / 16;
@@ -529,9 +588,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
             // Mn_ij = -T_ii A_ij for one 16 x 16 block, one wave, formed as
             // (A_ij^T T_ii^T) so that lane (g, n) ends with row n of the block,
             // columns 4g .. 4g+3: one 8-byte store.
-            auto put_mn = [&](int i, int j) {
+            auto put_mn_t = [&](int i, int j, const float4v &tb) {
                 const int g = l >> 4, n = l & 15;
-                const float4v tb = *(const float4v *)(Tmf + (16 * i + n) * LDA + 16 * i + 4 * g);
                 float4v x = {0, 0, 0, 0};
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
@@ -541,6 +599,9 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
 #pragma unroll
                 for (int e = 0; e < 4; ++e) h[e] = (_Float16)(-x[e]);
                 *(half4 *)(Tmb + swz<C>(16 * i + n, pcol(16 * j + 4 * g))) = h;
+            };
+            auto put_mn = [&](int i, int j) {
+                put_mn_t(i, j, *(const float4v *)(Tmf + (16 * i + (l & 15)) * LDA + 16 * i + 4 * (l >> 4)));
             };
             if (pw < NB / 2) {
                 // the diagonal pair (pb, pb+1): A_pb,pb, A_pb+1,pb+1, A_pb+1,pb
@@ -561,20 +622,21 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                 gram_store(pb, pb, true, a00);
                 gram_store(pb + 1, pb + 1, true, a11);
                 gram_store(pb + 1, pb, true, a10);
-                diag_inverse<LDA>(Af, Tmf, pb, 2);
-                // Tb of the two diagonal blocks, T scaled by beta of its columns:
-                // 2 blocks x 16 rows x 4 column quads, two per lane
+                float4v tr[2];
+                diag_inverse_mfma<LDA>(Af, pb, tr);
+                // T of the two diagonal blocks to Tmf (fp32, read by the other
+                // waves' solve blocks) and Tb = T scaled by beta of its columns
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    const int item = l + 64 * e, bb = pb + (item >> 6), row = 16 * bb + ((item & 63) >> 2),
-                              c4 = 16 * bb + 4 * (item & 3);
-                    const float4v t = *(const float4v *)(Tmf + row * LDA + c4) * *(const float4v *)(bet + c4);
+                    const int row = 16 * (pb + e) + (l & 15), c4 = 16 * (pb + e) + 4 * (l >> 4);
+                    *(float4v *)(Tmf + row * LDA + c4) = tr[e];
+                    const float4v t = tr[e] * *(const float4v *)(bet + c4);
                     half4 h;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) h[q] = (_Float16)t[q];
                     *(half4 *)(Tmb + swz<C>(row, pcol(c4))) = h;
                 }
-                put_mn(pb + 1, pb);
+                put_mn_t(pb + 1, pb, tr[1]);
             }
             // the other tiles, round robin over the waves that hold no pair,
             // two at a time
