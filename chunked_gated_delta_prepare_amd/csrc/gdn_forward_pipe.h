@@ -119,6 +119,30 @@ __device__ __forceinline__ void prep_barrier(unsigned *ctr, unsigned &target) {
     asm volatile("" ::: "memory");
 }
 
+// The arrival half of prep_barrier, for a wave that has other work to issue
+// before it waits (wait_two below).
+__device__ __forceinline__ void prep_arrive(unsigned *ctr, unsigned &target) {
+    target += 4;
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    if (lane_id() == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    asm volatile("" ::: "memory");
+}
+
+// Wait until ctr[0] >= t0 and ctr[1] >= t1, both read by one 8-byte LDS load
+// per poll (bounded, like prep_barrier).
+__device__ __forceinline__ void wait_two(const unsigned *ctr, unsigned t0, unsigned t1) {
+    asm volatile("" ::: "memory");
+    for (int it = 0; it < (1 << 16); ++it) {
+        const uint64_t v = __hip_atomic_load((const uint64_t *)ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const unsigned a = (unsigned)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+        const unsigned b = (unsigned)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+        if (a >= t0 && b >= t1) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+}
+
 // Lane-shifted copy within rows of 16 lanes (DPP row_shr), zero where the
 // source lane falls before the row start.
 template <int CTRL>
@@ -287,6 +311,7 @@ struct PipeLayout {
     static constexpr int kRowP = kRowC + 2 * kRowCN * 4; // [C + C + NB C]
     static constexpr int kSync = kRowP + (2 * C + NB * C) * 4;
     static constexpr int kBytes = kSync + 16;
+    static_assert(kSync % 8 == 0, "the two sync counters are read as one 8-byte word");
 };
 
 template <int C, int K, typename OT>
@@ -369,6 +394,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
             signal_counter(sync_ctr + 1);
             if (nt > 1) gload(1);
         }
+        asm volatile("" : "+v"(g_nx), "+v"(b_nx));     // (see the o stores below)
         wg_barrier();                       // chunk 0 prepared
 
         for (int c = 0; c < nt; ++c) {
@@ -461,6 +487,11 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                 for (int s = 0; s < C / 32; ++s)
                     M::mma(hacc[i], fragAT_split_p<K>(Ks, 16 * i, 32 * s), df[s]);
             }
+            // (chain wave 0 has the gate and beta of chunk c + 2 in flight:
+            // they are taken into registers here, where the wait counts the
+            // o stores issued since, so the next chunk's factor scan does not
+            // wait for those stores)
+            asm volatile("" : "+v"(g_nx), "+v"(b_nx));
             wg_barrier();
         }
         if (p.hT) {
@@ -539,9 +570,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                 *(half4 *)(Ks + qk_lds[j][0]) = __builtin_shufflevector(hk, hk, 0, 1, 2, 3);
                 *(half4 *)(Ks + qk_lds[j][1]) = __builtin_shufflevector(hk, hk, 4, 5, 6, 7);
             }
+            prep_arrive(sync_ctr, sync_target);
             if (n + 1 < nt) issue_loads(n + 1);
-            wait_counter(sync_ctr + 1, (unsigned)(n + 1));     // chunk n's row factors
-            prep_barrier(sync_ctr, sync_target);
+            // every prepare wave's q/k rows and chunk n's row factors are in
+            wait_two(sync_ctr, sync_target, (unsigned)(n + 1));
 
             // ---- Gram tiles (transposed: lane (l/16, j) gets row r = 16 I + j
             // and the four columns s = 16 J + 4 (l/16) + e), inverse, P
