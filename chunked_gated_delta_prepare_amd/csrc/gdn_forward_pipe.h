@@ -231,36 +231,37 @@ __device__ __forceinline__ void signal_counter(unsigned *ctr) {
     asm volatile("" ::: "memory");
 }
 
-// Diagonal 16 x 16 inverses T_bb = (I + A_bb)^-1, bb = b0 and b0 + 1, by
-// one wave on the matrix cores.  The inverse is built by doubling the block
-// size s = 1, 2, 4, 8: with B the block-diagonal inverse at size s and L the
-// (2,1) blocks of size s inside each 2s-block of A, the inverse at size 2s is
-// B - B L B (the inverse of a 2 x 2 block lower-triangular matrix).  Every
-// factor is bounded (|A| < 1 entrywise, the partial inverses are O(1)), so
-// fp16 operands with fp32 accumulation keep T within a few fp16 roundings of
-// the exact inverse, the precision at which the chain uses it anyway.
+// Diagonal 16 x 16 inverses T = (I + A)^-1 of two blocks by one wave, on the
+// matrix cores.  The inverse is built by doubling the block size s = 1, 2, 4,
+// 8: with B the block-diagonal inverse at size s and L the (2,1) blocks of
+// size s inside each 2s-block of A, the inverse at size 2s is B - B L B (the
+// inverse of a 2 x 2 block lower-triangular matrix).  Every factor is bounded
+// (|A| < 1 entrywise, the partial inverses are O(1)), so fp16 operands with
+// fp32 accumulation keep T within a few fp16 roundings of the exact inverse,
+// the precision at which the chain uses it anyway.
 //
 // Two layouts of a 16 x 16 matrix M in lane (g, n) = (l / 16, l % 16):
 //   col layout  M[4g + r][n], r = 0..3: the MFMA B operand and its result
 //   row layout  M[n][4g + r]:           the MFMA A operand
 // X Y takes X in row and Y in col layout; Y^T X^T takes the same registers
 // with the roles swapped and returns X Y in row layout.
-// Result t[j]: row n of T_(b0+j), columns 4g .. 4g+3, fp32.
-template <int LDA>
-__device__ __forceinline__ void diag_inverse_mfma(const float *Af, int b0, float4v (&t)[2]) {
+// In: a[j], block j of A (strictly lower) in row layout.  Out: t[j], T of
+// block j in row layout (row n, columns 4g .. 4g+3), fp32.
+__device__ __forceinline__ void diag_inverse_mfma(const float4v (&a)[2], float4v (&t)[2]) {
     const int l = lane_id(), g = l >> 4, n = l & 15;
-    float4v ra[2], Bc[2], Br[2];
+    float4v Bc[2], Br[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const float *Ab = Af + 16 * (b0 + j) * (LDA + 1);
-        ra[j] = *(const float4v *)(Ab + n * LDA + 4 * g);               // A[n][4g + r]
-        // s = 1: B = I minus the subdiagonal entries A[i][i-1] at odd rows i
-        const float sub1 = Ab[(4 * g + 1) * LDA + 4 * g], sub3 = Ab[(4 * g + 3) * LDA + 4 * g + 2];
+        // s = 1: B = I minus the subdiagonal entries A[i][i-1] at odd rows i.
+        // In col layout lane (g, 4g) needs A[4g+1][4g] and lane (g, 4g+2)
+        // needs A[4g+3][4g+2]: row-layout entries of the next lane.
+        const float sub1 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a[j][0]), 0x101, 0xf, 0xf, true));
+        const float sub3 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a[j][2]), 0x101, 0xf, 0xf, true));
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = 4 * g + r;
             const float ca = (r & 1) && n == i - 1 ? (r == 1 ? sub1 : sub3) : 0.f;   // A[i][i-1]
-            const float rb = (n & 1) && i == n - 1 ? ra[j][r] : 0.f;                 // A[n][n-1]
+            const float rb = (n & 1) && i == n - 1 ? a[j][r] : 0.f;                  // A[n][n-1]
             Bc[j][r] = (i == n ? 1.f : 0.f) - ca;
             Br[j][r] = (i == n ? 1.f : 0.f) - rb;
         }
@@ -274,7 +275,7 @@ __device__ __forceinline__ void diag_inverse_mfma(const float *Af, int b0, float
             for (int r = 0; r < 4; ++r) {
                 const int i = 4 * g + r;
                 const bool inL = (n / (2 * s)) == (i / (2 * s)) && (n & s) && !(i & s);
-                Lr[r] = (_Float16)(inL ? ra[j][r] : 0.f);
+                Lr[r] = (_Float16)(inL ? a[j][r] : 0.f);
                 Bch[r] = (_Float16)Bc[j][r];
                 Brh[r] = (_Float16)Br[j][r];
             }
@@ -290,10 +291,35 @@ __device__ __forceinline__ void diag_inverse_mfma(const float *Af, int b0, float
     t[1] = Br[1];
 }
 
+// A 16 x 16 block of A in col layout as an MFMA operand of k = 32: its fp16
+// high parts (k = 8g .. 8g+3) and low parts (k = 8g+4 .. 8g+7), so that one
+// product with an fp16 right operand keeps A to about 22 bits.
+__device__ __forceinline__ half8 split_hi_lo(const float4v &x) {
+    half8 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        h[e] = (_Float16)x[e];
+        h[4 + e] = (_Float16)(x[e] - (float)h[e]);
+    }
+    return h;
+}
+
+// The solve block Mn = -T_ii A_ij, in row layout (lane (g, n): row n, columns
+// 4g .. 4g+3), from A_ij split by split_hi_lo and T_ii in row layout, fp16:
+// (A_ij^T T_ii^T) with T_ii^T's rows repeated for the low parts.
+__device__ __forceinline__ half4 solve_block(const half8 &a_split, const half4 &t) {
+    const half8 tt = __builtin_shufflevector(t, t, 0, 1, 2, 3, 0, 1, 2, 3);
+    const float4v x = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_split, tt, float4v{0, 0, 0, 0}, 0, 0, 0);
+    half4 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = (_Float16)(-x[e]);
+    return h;
+}
+
 template <int C, int K>
 struct PipeLayout {
     static constexpr int NB = C / 16;
-    static constexpr int LDA = C + 4;                    // fp32 scratch pitch
+    static constexpr int NASP = NB == 4 ? 4 : 0;         // A blocks (2,0) (2,1) (3,0) (3,1)
     static constexpr int kQK = C * K * 2;                // one fp16 q or k tile
     static constexpr int kCC = C * C * 2;                // one fp16 C x C tile
     static constexpr int kVT = C * 64 * 2;               // one bf16 v tile
@@ -302,11 +328,13 @@ struct PipeLayout {
     static constexpr int kTmb = kK + 2 * kQK;            // [2] solve blocks (Tb, Mn)
     static constexpr int kP = kTmb + 2 * kCC;            // [2] P
     static constexpr int kV = kP + 2 * kCC;              // [2] raw v tiles
-    static constexpr int kA = kV + 2 * kVT;              // fp32 A   [C][LDA]
-    static constexpr int kTm = kA + C * LDA * 4;         // fp32 Tm  [C][LDA]
+    // A blocks of the later solve blocks, split fp16, one half8 per lane
+    static constexpr int kAsp = kV + 2 * kVT;            // [NASP][64][8]
+    // the diagonal inverses T_bb in row layout, fp16, one half4 per lane
+    static constexpr int kTr = kAsp + NASP * 1024;       // [NB][64][4]
     // chain-side row factors per slot: e^gcum, e^(gl - gcum), e^gl
     static constexpr int kRowCN = 2 * C + 4;
-    static constexpr int kRowC = kTm + C * LDA * 4;      // [2][kRowCN]
+    static constexpr int kRowC = kTr + NB * 512;         // [2][kRowCN]
     // prepare-side row factors: beta, e^(gcum_block0 - gcum), e^(gcum - gcum_16J)
     static constexpr int kRowP = kRowC + 2 * kRowCN * 4; // [C + C + NB C]
     static constexpr int kSync = kRowP + (2 * C + NB * C) * 4;
@@ -319,7 +347,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
     typedef PipeLayout<C, K> L;
     typedef Mma<_Float16> M;
     typedef bf16_t IO;
-    constexpr int NB = C / 16, NKB = K / 16, LDA = L::LDA;
+    constexpr int NB = C / 16, NKB = K / 16;
     constexpr int SIO = 2, SO = sizeof(OT);
     static_assert(L::kBytes <= kLdsBytesMax, "LDS budget");
     static_assert(NB == 2 || NB == 4, "chunk 32 or 64");
@@ -331,8 +359,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
     _Float16 *Tmbb = (_Float16 *)(smem + L::kTmb);
     _Float16 *Pb = (_Float16 *)(smem + L::kP);
     uint16_t *Vb = (uint16_t *)(smem + L::kV);
-    float *Af = (float *)(smem + L::kA);
-    float *Tmf = (float *)(smem + L::kTm);
+    _Float16 *Asp = (_Float16 *)(smem + L::kAsp);
+    _Float16 *Tr = (_Float16 *)(smem + L::kTr);
     float *rowC = (float *)(smem + L::kRowC);
     float *bet = (float *)(smem + L::kRowP);
     float *einv = bet + C, *efac = bet + 2 * C;
@@ -575,29 +603,40 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
             // every prepare wave's q/k rows and chunk n's row factors are in
             wait_two(sync_ctr, sync_target, (unsigned)(n + 1));
 
-            // ---- Gram tiles (transposed: lane (l/16, j) gets row r = 16 I + j
-            // and the four columns s = 16 J + 4 (l/16) + e), inverse, P
-            auto gram_store = [&](int I, int J, bool isA, const float4v &acc) {
-                const int r = 16 * I + acc_col(), s0 = 16 * J + 4 * (l >> 4);
-                const float fr = efac[J * C + r];
-                const float4v fac = *(const float4v *)(einv + s0) * fr;
-                if (isA) {
-                    const float br = bet[r];
-                    float4v a;
+            // ---- Gram tiles.  Tile (I, J) of a P or A block, with its decay
+            // e^(gcum_r - gcum_s) = efac[J][r] einv[s] (and beta_r for A), in
+            // row layout (lane (g, n): row 16 I + n, columns 16 J + 4g + e)
+            // or col layout (rows 16 I + 4g + e, column 16 J + n).
+            auto fac_row = [&](int I, int J, bool isA, const float4v &acc) {
+                const int r = 16 * I + (l & 15), s0 = 16 * J + 4 * (l >> 4);
+                const float fr = efac[J * C + r] * (isA ? bet[r] : 1.f);
+                const float4v fs = *(const float4v *)(einv + s0);
+                float4v a;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) a[e] = (s0 + e < r) ? acc[e] * fac[e] * br : 0.f;
-                    *(float4v *)(Af + r * LDA + s0) = a;
-                } else {
-                    half4 a;
+                for (int e = 0; e < 4; ++e) a[e] = (isA ? s0 + e < r : s0 + e <= r) ? acc[e] * fs[e] * fr : 0.f;
+                return a;
+            };
+            auto fac_col = [&](int I, int J, const float4v &acc) {      // A blocks only
+                const int r0 = 16 * I + 4 * (l >> 4), s = 16 * J + (l & 15);
+                const float4v fr = *(const float4v *)(efac + J * C + r0) * *(const float4v *)(bet + r0);
+                const float fs = einv[s];
+                float4v a;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) a[e] = (_Float16)((s0 + e <= r) ? acc[e] * fac[e] : 0.f);
-                    *(half4 *)(Ps + swz<C>(r, pcol(s0))) = a;
-                }
+                for (int e = 0; e < 4; ++e) a[e] = s < r0 + e ? acc[e] * fs * fr[e] : 0.f;
+                return a;
+            };
+            auto put_p = [&](int I, int J, const float4v &acc) {
+                const float4v a = fac_row(I, J, false, acc);
+                half4 h;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h[e] = (_Float16)a[e];
+                *(half4 *)(Ps + swz<C>(16 * I + (l & 15), pcol(16 * J + 4 * (l >> 4)))) = h;
             };
             // Two tiles at once: every fragment load first, then the two
-            // accumulations interleaved (tile (I, J) reads k rows of block J
-            // as the A operand, rows of block I as the B operand).
-            auto gram_two = [&](int I0, int J0, bool a0, int I1, int J1, bool a1, bool two) {
+            // accumulations interleaved.  mma(x, frag of rows X, frag of rows
+            // Y) forms X Y^T in col layout: P tiles (rows of block J first)
+            // come out in row layout, A tiles (block I first) in col layout.
+            auto gram_two = [&](int I0, int J0, bool a0, int I1, int J1, bool a1, bool two, int sl0, int sl1) {
                 half8 fa0[K / 32], fb0[K / 32], fa1[K / 32], fb1[K / 32];
 #pragma unroll
                 for (int k = 0; k < K / 32; ++k) {
@@ -611,100 +650,105 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                 float4v acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
 #pragma unroll
                 for (int k = 0; k < K / 32; ++k) {
-                    M::mma(acc0, fa0[k], fb0[k]);
-                    if (two) M::mma(acc1, fa1[k], fb1[k]);
+                    if (a0) M::mma(acc0, fb0[k], fa0[k]); else M::mma(acc0, fa0[k], fb0[k]);
+                    if (two) {
+                        if (a1) M::mma(acc1, fb1[k], fa1[k]); else M::mma(acc1, fa1[k], fb1[k]);
+                    }
                 }
-                gram_store(I0, J0, a0, acc0);
-                if (two) gram_store(I1, J1, a1, acc1);
+                auto put = [&](int I, int J, bool isA, int sl, const float4v &acc) {
+                    if (isA)
+                        *(half8 *)(Asp + sl * 512 + 8 * l) = split_hi_lo(fac_col(I, J, acc));
+                    else
+                        put_p(I, J, acc);
+                };
+                put(I0, J0, a0, sl0, acc0);
+                if (two) put(I1, J1, a1, sl1, acc1);
             };
-            // Mn_ij = -T_ii A_ij for one 16 x 16 block, one wave, formed as
-            // (A_ij^T T_ii^T) so that lane (g, n) ends with row n of the block,
-            // columns 4g .. 4g+3: one 8-byte store.
-            auto put_mn_t = [&](int i, int j, const float4v &tb) {
-                const int g = l >> 4, n = l & 15;
-                float4v x = {0, 0, 0, 0};
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    x = __builtin_amdgcn_mfma_f32_16x16x4f32(Af[(16 * i + 4 * g + s) * LDA + 16 * j + n], tb[s],
-                                                             x, 0, 0, 0);
-                half4 h;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) h[e] = (_Float16)(-x[e]);
-                *(half4 *)(Tmb + swz<C>(16 * i + n, pcol(16 * j + 4 * g))) = h;
-            };
-            auto put_mn = [&](int i, int j) {
-                put_mn_t(i, j, *(const float4v *)(Tmf + (16 * i + (l & 15)) * LDA + 16 * i + 4 * (l >> 4)));
+            auto put_mn = [&](int i, int j, const half8 &a_split, const half4 &t) {
+                *(half4 *)(Tmb + swz<C>(16 * i + (l & 15), pcol(16 * j + 4 * (l >> 4)))) = solve_block(a_split, t);
             };
             if (pw < NB / 2) {
-                // the diagonal pair (pb, pb+1): A_pb,pb, A_pb+1,pb+1, A_pb+1,pb
+                // the diagonal pair (pb, pb+1): A_pb,pb, A_pb+1,pb+1 (row
+                // layout, for the inverse) and A_pb+1,pb (col layout, for its
+                // solve block), kept in registers
                 const int pb = 2 * pw;
-                half8 f0[K / 32], f1[K / 32];
+                half8 f0[K / 32], f1[K / 32], q0[K / 32], q1[K / 32];
 #pragma unroll
                 for (int k = 0; k < K / 32; ++k) {
                     f0[k] = frag_sw<K>(Ks, 16 * pb, 32 * k);
                     f1[k] = frag_sw<K>(Ks, 16 * (pb + 1), 32 * k);
+                }
+                if constexpr (NB == 4) {
+#pragma unroll
+                    for (int k = 0; k < K / 32; ++k) {
+                        q0[k] = frag_sw<K>(Qs, 16 * pb, 32 * k);
+                        q1[k] = frag_sw<K>(Qs, 16 * (pb + 1), 32 * k);
+                    }
                 }
                 float4v a00 = {0, 0, 0, 0}, a11 = {0, 0, 0, 0}, a10 = {0, 0, 0, 0};
 #pragma unroll
                 for (int k = 0; k < K / 32; ++k) {
                     M::mma(a00, f0[k], f0[k]);
                     M::mma(a11, f1[k], f1[k]);
-                    M::mma(a10, f0[k], f1[k]);
+                    M::mma(a10, f1[k], f0[k]);
                 }
-                gram_store(pb, pb, true, a00);
-                gram_store(pb + 1, pb + 1, true, a11);
-                gram_store(pb + 1, pb, true, a10);
+                const float4v ad[2] = {fac_row(pb, pb, true, a00), fac_row(pb + 1, pb + 1, true, a11)};
+                const half8 a10s = split_hi_lo(fac_col(pb + 1, pb, a10));
                 float4v tr[2];
-                diag_inverse_mfma<LDA>(Af, pb, tr);
-                // T of the two diagonal blocks to Tmf (fp32, read by the other
-                // waves' solve blocks) and Tb = T scaled by beta of its columns
+                diag_inverse_mfma(ad, tr);
+                if constexpr (NB == 4) {
+                    // the P tiles of the same 2 x 2 block (their MFMAs fill
+                    // the gaps of the inverse's dependent chain)
+                    float4v p00 = {0, 0, 0, 0}, p10 = {0, 0, 0, 0}, p11 = {0, 0, 0, 0};
+#pragma unroll
+                    for (int k = 0; k < K / 32; ++k) {
+                        M::mma(p00, f0[k], q0[k]);
+                        M::mma(p10, f0[k], q1[k]);
+                        M::mma(p11, f1[k], q1[k]);
+                    }
+                    put_p(pb, pb, p00);
+                    put_p(pb + 1, pb, p10);
+                    put_p(pb + 1, pb + 1, p11);
+                }
+                // Tb = T scaled by beta of its columns, and T itself (fp16, row
+                // layout) for the other waves' solve blocks
+                half4 t16[2];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const int row = 16 * (pb + e) + (l & 15), c4 = 16 * (pb + e) + 4 * (l >> 4);
-                    *(float4v *)(Tmf + row * LDA + c4) = tr[e];
                     const float4v t = tr[e] * *(const float4v *)(bet + c4);
                     half4 h;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) h[q] = (_Float16)t[q];
+                    for (int q = 0; q < 4; ++q) {
+                        h[q] = (_Float16)t[q];
+                        t16[e][q] = (_Float16)tr[e][q];
+                    }
                     *(half4 *)(Tmb + swz<C>(row, pcol(c4))) = h;
+                    *(half4 *)(Tr + (pb + e) * 256 + 4 * l) = t16[e];
                 }
-                put_mn_t(pb + 1, pb, tr[1]);
+                put_mn(pb + 1, pb, a10s, t16[1]);
             }
-            // the other tiles, round robin over the waves that hold no pair,
-            // two at a time
-            constexpr int NA_REST = (NB == 4) ? 4 : 0;      // A (2,0) (2,1) (3,0) (3,1)
-            constexpr int NP = NB * (NB + 1) / 2;
-            constexpr int NREST = NA_REST + NP;
-            constexpr int W0 = NB / 2, NW = 4 - NB / 2;
-            // (tile coordinates are compile-time: t runs over an unrolled loop)
-            auto tile_I = [](int t) {
-                if (t < NA_REST) return 2 + t / 2;
-                int I = 0;
-                while ((I + 1) * (I + 2) / 2 <= t - NA_REST) ++I;
-                return I;
-            };
-            auto tile_J = [&](int t) {
-                if (t < NA_REST) return t % 2;
-                const int I = tile_I(t);
-                return t - NA_REST - I * (I + 1) / 2;
-            };
-#pragma unroll
-            for (int t = 0; t < NREST; t += 2 * NW) {
-#pragma unroll
-                for (int w = 0; w < NW; ++w) {
-                    const int t0 = t + w, t1 = t0 + NW;
-                    if (t0 >= NREST || W0 + w != pw) continue;
-                    if (t1 < NREST)
-                        gram_two(tile_I(t0), tile_J(t0), t0 < NA_REST, tile_I(t1), tile_J(t1), t1 < NA_REST, true);
-                    else
-                        gram_two(tile_I(t0), tile_J(t0), t0 < NA_REST, 0, 0, false, false);
+            if constexpr (NB == 4) {
+                // prepare wave 2 + J: the A and P tiles (2, J) and (3, J), with
+                // the A tiles in slots 2 (I - 2) + J
+                if (pw >= 2) {
+                    const int J = pw - 2;
+                    gram_two(2, J, true, 3, J, true, true, J, 2 + J);
+                    gram_two(2, J, false, 3, J, false, true, 0, 0);
+                }
+            } else {
+                // prepare waves 1..3: one P tile each
+                if (pw >= 1) {
+                    const int t = pw - 1, I = t == 0 ? 0 : 1, J = t == 2 ? 1 : 0;
+                    gram_two(I, J, false, 0, 0, false, false, 0, 0);
                 }
             }
             if constexpr (NB == 4) {
-                // Mn_20, Mn_21, Mn_30, Mn_31: T_22 and T_33 come from wave 1,
-                // the A blocks from waves 2 and 3
+                // Mn_20, Mn_21, Mn_30, Mn_31 (prepare wave pw takes A block pw):
+                // T_22 and T_33 come from wave 1, the A blocks from waves 2, 3
                 prep_barrier(sync_ctr, sync_target);
-                put_mn(2 + (pw >> 1), pw & 1);
+                const int i = 2 + (pw >> 1);
+                put_mn(i, pw & 1, *(const half8 *)(Asp + pw * 512 + 8 * l), *(const half4 *)(Tr + i * 256 + 4 * l));
             }
         };
 
