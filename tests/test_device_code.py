@@ -1,6 +1,11 @@
 """Host-only checks of the gfx950 code objects inside libgdn.so (built here
 from this repository's sources): every kernel the dispatch can launch is
-present, and no vector-memory store writes more than 8 bytes per lane.
+present, no kernel uses scratch memory, and no vector-memory store writes
+more than 8 bytes per lane.
+
+Scratch: a register array indexed with a run-time value is moved to
+per-lane scratch memory, which silently costs a large factor in speed; the
+kernels index their register arrays with constants only.
 
 The second rule guards against a miscompile seen with this toolchain: after
 a 12- or 16-byte buffer/global store, the compiler may let the next vector
@@ -32,8 +37,8 @@ def disassembly(tmp_path_factory):
     if not os.path.exists(gdn.LIB_PATH):
         from chunked_gated_delta_prepare_amd import build
         build.build()
-    objcopy, bundler, objdump = (_tool("llvm-objcopy"), _tool("clang-offload-bundler"),
-                                 _tool("llvm-objdump"))
+    objcopy, bundler, objdump, readelf = (_tool("llvm-objcopy"), _tool("clang-offload-bundler"),
+                                          _tool("llvm-objdump"), _tool("llvm-readelf"))
     d = tmp_path_factory.mktemp("co")
     fat = d / "fatbin.bin"
     subprocess.run([objcopy, "--dump-section", ".hip_fatbin=%s" % fat, gdn.LIB_PATH], check=True)
@@ -41,7 +46,7 @@ def disassembly(tmp_path_factory):
     # one offload bundle per translation unit, concatenated in the section
     starts = [m.start() for m in re.finditer(re.escape(MAGIC), data)]
     assert starts, "no offload bundle in libgdn.so"
-    text = []
+    text, notes = [], []
     for n, s in enumerate(starts):
         e = starts[n + 1] if n + 1 < len(starts) else len(data)
         b = d / ("b%d.bin" % n)
@@ -51,21 +56,32 @@ def disassembly(tmp_path_factory):
                         "--input=%s" % b, "--output=%s" % co], check=True)
         text.append(subprocess.run([objdump, "-d", str(co)], capture_output=True, text=True,
                                    check=True).stdout)
-    yield "\n".join(text)
+        notes.append(subprocess.run([readelf, "--notes", str(co)], capture_output=True, text=True,
+                                    check=True).stdout)
+    yield "\n".join(text), "\n".join(notes)
     shutil.rmtree(d, ignore_errors=True)
 
 
 def test_no_vector_memory_store_wider_than_8_bytes(disassembly):
     wide = re.findall(r"\b((?:buffer|global|flat)_store_(?:dwordx3|dwordx4|b96|b128))\b",
-                      disassembly)
+                      disassembly[0])
     assert not wide, "wide vector-memory stores in libgdn: %s" % sorted(set(wide))
 
 
 def test_every_dispatched_kernel_is_present(disassembly):
-    names = set(re.findall(r"^[0-9a-f]+ <(_ZN3gdn\w+)>:", disassembly, flags=re.M))
+    names = set(re.findall(r"^[0-9a-f]+ <(_ZN3gdn\w+)>:", disassembly[0], flags=re.M))
     demangled = " ".join(names)
     for kernel in ("forward_pipe_kernelILi64ELi128ENS_6bf16_t", "forward_pipe_kernelILi64ELi128Ef",
                    "forward_pipe_kernelILi32ELi64ENS_6bf16_t", "forward_pipe_kernelILi32ELi128ENS_6bf16_t",
                    "forward_kernelILi64ELi128ENS_6bf16_tES1_Lb1", "forward_kernelILi64ELi64EffLb0",
                    "prepare_kernel", "scan_kernel"):
         assert kernel in demangled, kernel
+
+
+def test_no_kernel_uses_scratch(disassembly):
+    meta = disassembly[1]
+    names = re.findall(r"^\s+\.name:\s+(_ZN3gdn\S+)", meta, flags=re.M)
+    sizes = [int(s) for s in re.findall(r"\.private_segment_fixed_size:\s+(\d+)", meta)]
+    assert names and len(names) == len(sizes), "kernel metadata not parsed"
+    bad = [(n, s) for n, s in zip(names, sizes) if s]
+    assert not bad, "kernels with scratch: %s" % bad
