@@ -25,8 +25,9 @@
 // counter, so the chain waves never wait on them mid-chunk.
 //
 // q/k/Tm/P tiles are stored without padding, 16-byte chunks XOR-swizzled by
-// row, which keeps the transposed (ds_read_b64_tr_b16) fragment reads free
-// of bank conflicts inside the 160 KB budget.
+// row (see swz), which keeps the fragment reads free of bank conflicts and
+// the transposed (ds_read_b64_tr_b16) reads at their minimum inside the
+// 160 KB budget.
 #pragma once
 
 #include "gdn_forward.h"
@@ -36,10 +37,22 @@ namespace gdn {
 constexpr int kPipeThreads = 512;
 
 // Element (row, col) of an fp16 tile with rows of LD halves: the 16-byte
-// chunk j of row r sits at chunk position j ^ (r mod LD/8).
+// chunk j of row r sits at chunk position j ^ s(r).  For 64- and 32-half
+// rows s(r) = r mod LD/8.  The 128-half q/k tiles are read two ways, as
+// 16-byte row fragments (16 rows, one chunk each) and by transposed 8-byte
+// reads (four rows, the same half of four chunks each); s is then the
+// GF(2)-linear map of r mod 16 with s(1) = 14, s(2) = 1, s(4) = 11,
+// s(8) = 8, picked by measurement among the maps that keep the fragment
+// reads free of bank conflicts: it leaves the transposed reads at the
+// two-way minimum that the permuted columns allow (the plain map r mod 16
+// costs four-way).
 template <int LD>
 __device__ __forceinline__ int swz(int row, int col) {
     constexpr int NC = LD / 8;
+    if constexpr (NC == 16) {
+        const int s = ((row & 1) ? 14 : 0) ^ ((row & 2) ? 1 : 0) ^ ((row & 4) ? 11 : 0) ^ ((row & 8) ? 8 : 0);
+        return row * LD + (((col >> 3) ^ s) << 3) + (col & 7);
+    }
     return row * LD + (((col >> 3) ^ (row & (NC - 1))) << 3) + (col & 7);
 }
 
