@@ -459,7 +459,21 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
                 gram_tile(pb, pb, true);
                 gram_tile(pb + 1, pb + 1, true);
                 gram_tile(pb + 1, pb, true);
-                diag_inverse<LDA>(Af, Tmf, pb, 2);
+                if constexpr (sizeof(OpT) == 2) {
+                    // fp16 operands: the two diagonal inverses on the matrix
+                    // cores (block doubling), into Tm's fp32 rows
+                    const int n = l & 15;
+                    float4v ad[2], tr[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e)
+                        ad[e] = *(const float4v *)(Af + (16 * (pb + e) + n) * LDA + 16 * (pb + e) + g4);
+                    diag_inverse_mfma(ad, tr);
+#pragma unroll
+                    for (int e = 0; e < 2; ++e)
+                        *(float4v *)(Tmf + (16 * (pb + e) + n) * LDA + 16 * (pb + e) + g4) = tr[e];
+                } else {
+                    diag_inverse<LDA>(Af, Tmf, pb, 2);
+                }
                 emit_diag<LDA, LDC, OpT>(Tmf, Tmb, betp, pb);
                 emit_diag<LDA, LDC, OpT>(Tmf, Tmb, betp, pb + 1);
                 merge_block<LDA, LDC, OpT>(Af, Tmf, Tmb, betp, pb + 1, pb);
