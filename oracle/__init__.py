@@ -4,10 +4,12 @@ TEST INFRASTRUCTURE ONLY.  Nothing here is part of the product: only the tests,
 the smoke check and the CPU-baseline leg of the benchmark import this package.
 It shares no code with the HIP library and never loads it.
 
-Three functions mirror the three library entry points:
+These functions mirror the library entry points:
 
 * ``token_recurrence`` -- the plain definition (C, fp64, one token at a time),
   the reference for ``gdn_forward``.  See ``gdn_oracle.c`` for the recurrence.
+  ``token_states`` also records the per-chunk start states and the per-token
+  state deltas, the reference for ``gdn_forward_states``.
 * ``chunk_prepare`` -- the per-chunk WY factors (gate cumsum, the strictly lower
   decayed Gram matrix, its unit-triangular inverse, then w and u), the
   reference for ``gdn_prepare``.  Steps follow the TileOPs "Reuse P as beta
@@ -59,10 +61,11 @@ def _load():
                     os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
                 build(force=True)
             lib = ctypes.CDLL(_LIB_PATH)
-            f = lib.gdn_oracle_f64
             i64, vp = ctypes.c_int64, ctypes.c_void_p
+            f = lib.gdn_oracle_states_f64
             f.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
-                          vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, ctypes.c_int]
+                          vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, i64, vp, vp,
+                          ctypes.c_int]
             f.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -72,15 +75,7 @@ def _f32(x):
     return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
 
 
-def token_recurrence(q, k, v, beta, g, h0=None, heads=None, nthreads=None,
-                     want_o=True, want_hT=True):
-    """Token-by-token fp64 recurrence.
-
-    Inputs are anything numpy can view as float32 holding the exact values the
-    GPU sees (bf16 widens exactly).  ``heads`` optionally selects flat head
-    indices b*H + h.  Returns ``(o, hT)`` as float64 arrays: with ``heads`` None
-    they are [B,T,H,V] and [B,H,K,V]; otherwise head-major [n,T,V], [n,K,V].
-    """
+def _recurrence(q, k, v, beta, g, h0, heads, nthreads, want_o, want_hT, chunk):
     q, k, v, beta, g = map(_f32, (q, k, v, beta, g))
     B, T, H, K = q.shape
     V = v.shape[-1]
@@ -104,20 +99,58 @@ def token_recurrence(q, k, v, beta, g, h0=None, heads=None, nthreads=None,
         n = sel.size
     o = np.empty((n, T, V), np.float64) if want_o else None
     hT = np.empty((n, K, V), np.float64) if want_hT else None
+    hck = vnew = None
+    if chunk is not None:
+        if chunk < 1:
+            raise ValueError("chunk must be >= 1")
+        hck = np.empty((n, (T + chunk - 1) // chunk, K, V), np.float64)
+        vnew = np.empty((n, T, V), np.float64)
     if nthreads is None:
         nthreads = os.cpu_count() or 1
     ptr = lambda a: None if a is None else a.ctypes.data
-    rc = _load().gdn_oracle_f64(
+    rc = _load().gdn_oracle_states_f64(
         B, T, H, K, V, per_key, ptr(q), ptr(k), ptr(v), ptr(beta), ptr(g),
-        ptr(h0c), n, ptr(sel), ptr(o), ptr(hT), int(nthreads))
+        ptr(h0c), n, ptr(sel), ptr(o), ptr(hT), int(chunk or 0), ptr(hck),
+        ptr(vnew), int(nthreads))
     if rc != 0:
-        raise RuntimeError("gdn_oracle_f64 failed with code %d" % rc)
+        raise RuntimeError("gdn_oracle_states_f64 failed with code %d" % rc)
     if heads is None:
         if o is not None:
             o = o.reshape(B, H, T, V).transpose(0, 2, 1, 3)
         if hT is not None:
             hT = hT.reshape(B, H, K, V)
+        if hck is not None:
+            hck = hck.reshape(B, H, -1, K, V).transpose(0, 2, 1, 3, 4)
+            vnew = vnew.reshape(B, H, T, V).transpose(0, 2, 1, 3)
+    return o, hT, hck, vnew
+
+
+def token_recurrence(q, k, v, beta, g, h0=None, heads=None, nthreads=None,
+                     want_o=True, want_hT=True):
+    """Token-by-token fp64 recurrence.
+
+    Inputs are anything numpy can view as float32 holding the exact values the
+    GPU sees (bf16 widens exactly).  ``heads`` optionally selects flat head
+    indices b*H + h.  Returns ``(o, hT)`` as float64 arrays: with ``heads`` None
+    they are [B,T,H,V] and [B,H,K,V]; otherwise head-major [n,T,V], [n,K,V].
+    """
+    o, hT, _, _ = _recurrence(q, k, v, beta, g, h0, heads, nthreads, want_o, want_hT, None)
     return o, hT
+
+
+def token_states(q, k, v, beta, g, chunk, h0=None, heads=None, nthreads=None):
+    """The token recurrence with the states a backward pass re-reads.
+
+    Returns ``(o, hT, hck, vnew)``: o and hT as ``token_recurrence``; ``hck``
+    the state h (K x V) at the start of every chunk of ``chunk`` tokens,
+    before that chunk's first token is applied, [B,NT,H,K,V] with
+    NT = ceil(T / chunk) (the KDA re-scan page's h checkpoints); ``vnew`` the
+    delta beta_t (v_t - (decayed state)^T k_t) that token t writes into the
+    state, [B,T,H,V] (the page's v_new, v' = u - w h of the chunk form).
+    With ``heads`` the outputs are head-major: [n,T,V], [n,K,V], [n,NT,K,V],
+    [n,T,V].
+    """
+    return _recurrence(q, k, v, beta, g, h0, heads, nthreads, True, True, int(chunk))
 
 
 # --------------------------------------------------------------------------
@@ -181,8 +214,10 @@ def chunk_prepare(k, v, beta, g, chunk):
     return gcum, w, u
 
 
-def chunk_scan(q, k, w, u, gcum, chunk, h0=None):
-    """Serial scan over chunks, fp64.  Returns ``(o, hT)``.
+def chunk_scan(q, k, w, u, gcum, chunk, h0=None, states=False):
+    """Serial scan over chunks, fp64.  Returns ``(o, hT)``, and with
+    ``states`` also the chunk-start states [B,NT,H,K,V] and v' [B,T,H,V]:
+    ``(o, hT, hck, vnew)``.
 
     Per chunk with start state h (K x V), following the re-scan page's
     per-chunk algebra (there with h checkpoints and dq, which are not part of
@@ -203,6 +238,9 @@ def chunk_scan(q, k, w, u, gcum, chunk, h0=None):
     per_key = gcum.ndim == 4
     o = np.zeros((B, T, H, V), np.float64)
     hT = np.zeros((B, H, K, V), np.float64)
+    NT = (T + chunk - 1) // chunk
+    hck = np.zeros((B, NT, H, K, V), np.float64) if states else None
+    vnew = np.zeros((B, T, H, V), np.float64) if states else None
     for b in range(B):
         for hh in range(H):
             S = (np.zeros((K, V)) if h0 is None
@@ -212,6 +250,9 @@ def chunk_scan(q, k, w, u, gcum, chunk, h0=None):
                 wc, uc = w[b, s:e, hh], u[b, s:e, hh]
                 gam = gcum[b, s:e, hh]
                 vp = uc - wc @ S
+                if states:
+                    hck[b, s // chunk, hh] = S
+                    vnew[b, s:e, hh] = vp
                 if per_key:
                     dec = np.exp(gam[:, None, :] - gam[None, :, :])
                     P = np.einsum("rd,sd,rsd->rs", qc, kc, dec)
@@ -226,13 +267,15 @@ def chunk_scan(q, k, w, u, gcum, chunk, h0=None):
                 o[b, s:e, hh] = qd @ S + np.tril(P) @ vp
                 S = last * S + kg.T @ vp
             hT[b, hh] = S
+    if states:
+        return o, hT, hck, vnew
     return o, hT
 
 
-def chunk_forward(q, k, v, beta, g, chunk, h0=None):
+def chunk_forward(q, k, v, beta, g, chunk, h0=None, states=False):
     """chunk_prepare followed by chunk_scan."""
     gcum, w, u = chunk_prepare(k, v, beta, g, chunk)
-    return chunk_scan(q, k, w, u, gcum, chunk, h0)
+    return chunk_scan(q, k, w, u, gcum, chunk, h0, states)
 
 
 def rel_err(x, ref):

@@ -36,6 +36,14 @@
  * g [B,T,H] (scalar gate) or [B,T,H,K] (per-key gate); h0 [B,H,K,V] or NULL.
  * Outputs are head-major for the selected heads: o [n][T][V], hT [n][K][V],
  * where head n is sel[n] = b*H + h (or every head in order when sel == NULL).
+ *
+ * Saved states (gdn_oracle_states_f64), what a backward pass re-reads (the
+ * KDA re-scan page's h checkpoints and v_new):
+ *   hck  [n][NT][K][V]  h at the start of each chunk of C tokens, before the
+ *                       chunk's first token is applied (NT = ceil(T / C))
+ *   vnew [n][T][V]      the delta written into the state at token t,
+ *                       beta_t * e_t with e the prediction error above: the
+ *                       state update is h <- Diag(a_t) h + k_t vnew_t^T
  */
 #include <math.h>
 #include <pthread.h>
@@ -51,6 +59,9 @@ typedef struct {
     const int64_t *sel;        /* NULL: all B*H heads */
     double *o;                 /* [n_sel][T][V], may be NULL */
     double *hT;                /* [n_sel][K][V], may be NULL */
+    int64_t chunk;             /* C of the checkpoints (>= 1 when hck is set) */
+    double *hck;               /* [n_sel][NT][K][V], may be NULL */
+    double *vnew;              /* [n_sel][T][V], may be NULL */
 } oracle_job;
 
 /* One (batch, head) pair, token by token. */
@@ -67,8 +78,11 @@ static void run_head(const oracle_job *J, int64_t n, double *h, double *kk,
         memset(h, 0, sizeof(double) * (size_t)(K * V));
     }
 
+    const int64_t NT = J->hck ? (T + J->chunk - 1) / J->chunk : 0;
     for (int64_t t = 0; t < T; ++t) {
         const int64_t row = (b * T + t) * H + hd;      /* token-head index */
+        if (J->hck && t % J->chunk == 0)
+            memcpy(J->hck + (n * NT + t / J->chunk) * K * V, h, sizeof(double) * (size_t)(K * V));
         const float *qt = J->q + row * K;
         const float *kt = J->k + row * K;
         const float *vt = J->v + row * V;
@@ -94,6 +108,10 @@ static void run_head(const oracle_job *J, int64_t n, double *h, double *kk,
                 hr[j] *= ad;
                 e[j] -= hr[j] * kd;
             }
+        }
+        if (J->vnew) {
+            double *vn = J->vnew + (n * T + t) * V;
+            for (int64_t j = 0; j < V; ++j) vn[j] = bt * e[j];
         }
         /* S = S' + beta e k^T;  o = S q. */
         double *ot = J->o ? J->o + (n * T + t) * V : NULL;
@@ -137,21 +155,23 @@ static void *worker(void *p) {
 }
 
 /*
- * Entry point.  Returns 0 on success, nonzero on a bad argument or an
+ * Entry points.  Return 0 on success, nonzero on a bad argument or an
  * allocation failure.  nthreads <= 0 means one thread.
  */
-int gdn_oracle_f64(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
-                   int gate_per_key, const float *q, const float *k,
-                   const float *v, const float *beta, const float *g,
-                   const float *h0, int64_t n_sel, const int64_t *sel,
-                   double *o, double *hT, int nthreads) {
+int gdn_oracle_states_f64(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                          int gate_per_key, const float *q, const float *k,
+                          const float *v, const float *beta, const float *g,
+                          const float *h0, int64_t n_sel, const int64_t *sel,
+                          double *o, double *hT, int64_t chunk, double *hck,
+                          double *vnew, int nthreads) {
     if (B < 1 || T < 0 || H < 1 || K < 1 || V < 1) return 1;
     if (!q || !k || !v || !beta || !g) return 1;
+    if (hck && chunk < 1) return 1;
     if (!sel) n_sel = B * H;
     for (int64_t n = 0; sel && n < n_sel; ++n)
         if (sel[n] < 0 || sel[n] >= B * H) return 1;
     oracle_job J = {B, T, H, K, V, gate_per_key, q, k, v, beta, g, h0,
-                    n_sel, sel, o, hT};
+                    n_sel, sel, o, hT, chunk, hck, vnew};
     if (nthreads < 1) nthreads = 1;
     if (nthreads > n_sel) nthreads = (int)(n_sel > 0 ? n_sel : 1);
     pthread_t *tid = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
@@ -170,4 +190,13 @@ int gdn_oracle_f64(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
     }
     free(tid); free(args);
     return err;
+}
+
+int gdn_oracle_f64(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                   int gate_per_key, const float *q, const float *k,
+                   const float *v, const float *beta, const float *g,
+                   const float *h0, int64_t n_sel, const int64_t *sel,
+                   double *o, double *hT, int nthreads) {
+    return gdn_oracle_states_f64(B, T, H, K, V, gate_per_key, q, k, v, beta, g, h0,
+                                 n_sel, sel, o, hT, 0, NULL, NULL, nthreads);
 }

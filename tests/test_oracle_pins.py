@@ -355,6 +355,150 @@ def test_rel_err_definition(oracle_mod):
 
 
 # ---------------------------------------------------------------------------
+# Saved states: the chunk-start state h_c and the per-token delta v_new that a
+# backward pass re-reads (the KDA re-scan page's h checkpoints and v_new).
+# ---------------------------------------------------------------------------
+
+def brute_force_states(q, k, v, beta, a, S0):
+    """Every state S_t (V x K) of the unrolled product form, t = -1 .. T-1."""
+    T, K, V = len(q), len(q[0]), len(v[0])
+    A = [_transition(a[t], beta[t], k[t]) for t in range(T)]
+    states = [S0]
+    for t in range(T):
+        P = [[Fraction(int(i == j)) for j in range(K)] for i in range(K)]
+        for j in range(t + 1):
+            P = _matmul(P, A[j])
+        S_t = _matmul(S0, P)
+        for s in range(t + 1):
+            R = [[Fraction(int(i == j)) for j in range(K)] for i in range(K)]
+            for j in range(s + 1, t + 1):
+                R = _matmul(R, A[j])
+            outer = [[beta[s] * v[s][i] * k[s][j] for j in range(K)]
+                     for i in range(V)]
+            contrib = _matmul(outer, R)
+            S_t = [[S_t[i][j] + contrib[i][j] for j in range(K)] for i in range(V)]
+        states.append(S_t)
+    return states
+
+
+@pytest.mark.parametrize("per_key", [False, True])
+def test_states_exact_bruteforce(oracle_mod, per_key, T=5, K=3, V=2, chunk=2):
+    """h_c is S^T just before token c*C; v_new_t is what token t adds to the
+    decayed state along k_t: S_t = S_{t-1} Diag(a_t) + v_new_t k_t^T, which
+    expands the product form to v_new_t = b_t (v_t - S_{t-1} Diag(a_t) k_t).
+    Both from exact rational states of the unrolled product (T = 5 leaves a
+    ragged last chunk)."""
+    rng = np.random.default_rng(300 + (1 if per_key else 0))
+    q, k, v, beta, g, h0 = _small_case(rng, T, K, V, per_key)
+    o, hT, hck, vnew = oracle_mod.token_states(q, k, v, beta, g, chunk, h0, nthreads=1)
+    assert hck.shape == (1, (T + chunk - 1) // chunk, 1, K, V)
+    assert vnew.shape == (1, T, 1, V)
+    if per_key:
+        a = [[Fraction(math.exp(float(g[0, t, 0, d]))) for d in range(K)]
+             for t in range(T)]
+    else:
+        a = [[Fraction(math.exp(float(g[0, t, 0])))] * K for t in range(T)]
+    S0 = [[Fraction(float(h0[0, 0, i, j])) for i in range(K)] for j in range(V)]
+    kf, vf = _to_frac(k[0, :, 0]), _to_frac(v[0, :, 0])
+    bf = [Fraction(float(b)) for b in beta[0, :, 0]]
+    states = brute_force_states(_to_frac(q[0, :, 0]), kf, vf, bf, a, S0)
+    for c in range(hck.shape[1]):
+        S = states[c * chunk]                       # S_{c C - 1}
+        ex = np.array([[float(S[j][i]) for j in range(V)] for i in range(K)])
+        np.testing.assert_allclose(hck[0, c, 0], ex, rtol=1e-12, atol=1e-13)
+    for t in range(T):
+        S = states[t]                               # S_{t-1}
+        pred = [sum((S[i][d] * a[t][d] * kf[t][d] for d in range(K)), Fraction(0))
+                for i in range(V)]
+        ex = np.array([float(bf[t] * (vf[t][i] - pred[i])) for i in range(V)])
+        np.testing.assert_allclose(vnew[0, t, 0], ex, rtol=1e-12, atol=1e-13)
+    # o and hT are those of the plain recurrence
+    o2, h2 = oracle_mod.token_recurrence(q, k, v, beta, g, h0, nthreads=1)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(hT, h2)
+
+
+@pytest.mark.parametrize("per_key", [False, True])
+def test_state_deltas_rebuild_the_next_checkpoint(oracle_mod, per_key):
+    """Unrolling S_t = S_{t-1} Diag(a_t) + v_new_t k_t^T over a chunk:
+    h_{c+1} = Diag(prod a) h_c + sum_t Diag(prod_{j>t} a_j) k_t v_new_t^T,
+    and the same sum over the last chunk gives hT."""
+    rng = np.random.default_rng(301)
+    T, K, V, C = 23, 6, 4, 8
+    q, k, v, beta, g, h0 = _small_case(rng, T, K, V, per_key)
+    _, hT, hck, vnew = oracle_mod.token_states(q, k, v, beta, g, C, h0, nthreads=1)
+    gg = g[0, :, 0].astype(np.float64)
+    if not per_key:
+        gg = gg[:, None] * np.ones((1, K))
+    kk = k[0, :, 0].astype(np.float64)
+    NT = hck.shape[1]
+    for c in range(NT):
+        s, e = c * C, min(c * C + C, T)
+        h = np.exp(gg[s:e].sum(0))[:, None] * hck[0, c, 0]
+        for t in range(s, e):
+            h += np.outer(np.exp(gg[t + 1:e].sum(0)) * kk[t], vnew[0, t, 0])
+        nxt = hck[0, c + 1, 0] if c + 1 < NT else hT[0, 0]
+        np.testing.assert_allclose(h, nxt, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("per_key", [False, True])
+def test_states_beta_zero(oracle_mod, per_key):
+    """beta = 0: nothing is written (v_new = 0) and h_c is h0 decayed by the
+    gates of the first c*C tokens."""
+    rng = np.random.default_rng(302)
+    T, K, V, C = 13, 4, 3, 4
+    q, k, v, beta, g, h0 = _small_case(rng, T, K, V, per_key)
+    beta[:] = 0
+    _, _, hck, vnew = oracle_mod.token_states(q, k, v, beta, g, C, h0, nthreads=1)
+    assert np.all(vnew == 0)
+    G = np.concatenate([np.zeros((1,) + g.shape[3:]),
+                        np.cumsum(g[0, :, 0].astype(np.float64), axis=0)])
+    for c in range(hck.shape[1]):
+        d = np.exp(G[c * C])
+        d = d if per_key else d * np.ones(K)
+        np.testing.assert_allclose(hck[0, c, 0], d[:, None] * h0[0, 0], rtol=1e-12)
+
+
+@pytest.mark.parametrize("per_key", [False, True])
+@pytest.mark.parametrize("chunk,T", [(16, 64), (32, 70), (64, 1)])
+def test_chunk_form_states_equal_token_states(oracle_mod, per_key, chunk, T):
+    """v' = u - w h of the chunk form is the token recurrence's v_new, and
+    the chunk scan's chunk-start states are its checkpoints."""
+    rng = np.random.default_rng(303 + T + chunk)
+    B, H, K, V = 1, 2, 12, 8
+    q = rng.standard_normal((B, T, H, K)).astype(np.float32)
+    k = rng.standard_normal((B, T, H, K)).astype(np.float32)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, V)).astype(np.float32)
+    beta = rng.random((B, T, H)).astype(np.float32)
+    gs = (B, T, H, K) if per_key else (B, T, H)
+    g = (-0.3 * rng.random(gs)).astype(np.float32)
+    h0 = rng.standard_normal((B, H, K, V)).astype(np.float32)
+    _, _, hck, vnew = oracle_mod.token_states(q, k, v, beta, g, chunk, h0)
+    _, _, hck2, vnew2 = oracle_mod.chunk_forward(q, k, v, beta, g, chunk, h0, states=True)
+    np.testing.assert_allclose(hck2, hck, atol=1e-10)
+    np.testing.assert_allclose(vnew2, vnew, atol=1e-10)
+
+
+def test_states_head_selection(oracle_mod):
+    rng = np.random.default_rng(304)
+    B, T, H, K, V, C = 2, 9, 3, 4, 5, 4
+    q = rng.standard_normal((B, T, H, K)).astype(np.float32)
+    k = (0.5 * rng.standard_normal((B, T, H, K))).astype(np.float32)
+    v = rng.standard_normal((B, T, H, V)).astype(np.float32)
+    beta = rng.random((B, T, H)).astype(np.float32)
+    g = (-rng.random((B, T, H))).astype(np.float32)
+    h0 = rng.standard_normal((B, H, K, V)).astype(np.float32)
+    _, _, hck, vnew = oracle_mod.token_states(q, k, v, beta, g, C, h0, nthreads=3)
+    sel = [5, 0]
+    _, _, hs, vs = oracle_mod.token_states(q, k, v, beta, g, C, h0, heads=sel)
+    for n, bh in enumerate(sel):
+        b, h = divmod(bh, H)
+        np.testing.assert_array_equal(hs[n], hck[b, :, h])
+        np.testing.assert_array_equal(vs[n], vnew[b, :, h])
+
+
+# ---------------------------------------------------------------------------
 # Planted mistakes: each slip below, made in a copy of the C oracle, must be
 # caught by the pins above (run on small inputs).
 # ---------------------------------------------------------------------------
@@ -372,6 +516,8 @@ _MUTANTS = {
     "drop_beta": ("const double bk = bt * kk[d]", "const double bk = kk[d]"),
     "gate_not_exponentiated": ("a[d] = exp((double)gt[d]);", "a[d] = 1.0 + (double)gt[d];"),
     "per_key_gate_on_value_index": ("hr[j] *= ad;", "hr[j] *= a[j % K];"),
+    "state_delta_without_beta": ("vn[j] = bt * e[j];", "vn[j] = e[j];"),
+    "checkpoint_one_token_late": ("t % J->chunk == 0", "t % J->chunk == 1 % J->chunk"),
 }
 
 
@@ -383,6 +529,7 @@ def _pins_pass(mod):
         lambda: test_orthonormal_keys_reduce_to_linear_attention(mod),
         lambda: [test_unit_key_query_equal_reads_back_value(mod, pk)
                  for pk in (False, True)],
+        lambda: [test_states_exact_bruteforce(mod, pk) for pk in (False, True)],
     ]
     for c in checks:
         try:
