@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--o-dtype", default=None, choices=[None, "bf16", "fp32"])
+    ap.add_argument("--states", action="store_true",
+                    help="time gdn_forward_states (also saves chunk-start states and v')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
@@ -51,12 +53,17 @@ def io_bytes(dt):
     return {"bf16": 2, "fp32": 4}[dt]
 
 
-def forward_bytes(w, o_dtype):
+def forward_bytes(w, o_dtype, states=False):
     B, T, H, K, V = w.B, w.T, w.H, w.K, w.V
     per_tok = (io_bytes(w.io) * 2 * K + io_bytes(w.io) * V + io_bytes(o_dtype) * V
                + 4 + 4 * (K if w.gate == "key" else 1))
     state = 4 * K * V * B * H * (2 if w.h0 else 1)
-    return B * T * H * per_tok + state
+    saved = 0
+    if states:
+        # chunk-start states [B,NT,H,K,V] and v' [B,T,H,V], in the o dtype
+        nt = (T + w.chunk - 1) // w.chunk
+        saved = io_bytes(o_dtype) * (B * nt * H * K * V + B * T * H * V)
+    return B * T * H * per_tok + state + saved
 
 
 def forward_flops(w):
@@ -65,14 +72,16 @@ def forward_flops(w):
     return 2.0 * mac * w.B * w.T * w.H
 
 
-def kernel_name(w, o_dtype):
-    """Template instance of the kernel that gdn_forward launches: the
-    pipelined kernel for a scalar gate with bf16 io, else the four-wave one."""
+def kernel_name(w, o_dtype, states=False):
+    """Template instance of the kernel that gdn_forward (or, with states,
+    gdn_forward_states) launches: the pipelined kernel for a scalar gate with
+    bf16 io, else the four-wave one."""
     io = {"bf16": "bf16_t", "fp32": "float"}
+    st = ", true" if states else ""
     if w.gate == "head" and w.io == "bf16":
-        return "forward_pipe_kernel<%d, %d, %s>" % (w.chunk, w.K, io[o_dtype])
-    return "forward_kernel<%d, %d, %s, %s, %s>" % (w.chunk, w.K, io[w.io], io[o_dtype],
-                                                   "true" if w.gate == "key" else "false")
+        return "forward_pipe_kernel<%d, %d, %s%s>" % (w.chunk, w.K, io[o_dtype], st)
+    return "forward_kernel<%d, %d, %s, %s, %s%s>" % (w.chunk, w.K, io[w.io], io[o_dtype],
+                                                     "true" if w.gate == "key" else "false", st)
 
 
 def source_digest():
@@ -90,13 +99,14 @@ def source_digest():
     return h.hexdigest()
 
 
-def measured_traffic(w, o_dtype):
+def measured_traffic(w, o_dtype, states=False):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
     this kernel and workload (FETCH_SIZE and WRITE_SIZE, each scaled by what
     the counter reads for a plain copy of known size), or None when there is
     none or it was taken on different sources."""
     short = kernel_name(w, o_dtype).split("<")[0]
-    path = os.path.join(ROOT, "profiles", "%s.%s.%s.traffic.json" % (short, w.name, o_dtype))
+    path = os.path.join(ROOT, "profiles", "%s.%s.%s%s.traffic.json"
+                        % (short, w.name, o_dtype, ".states" if states else ""))
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -147,9 +157,18 @@ def main():
                                    w.gate == "key", tdt)
     ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8) if ws_bytes else None
 
-    def step():
-        gdn.forward(d["q"], d["k"], d["v"], d["beta"], d["g"], w.chunk, d["h0"],
-                    o_dtype=tdt, o=o, hT=hT, workspace=ws)
+    if args.states:
+        nt = (w.T + w.chunk - 1) // w.chunk
+        hck = torch.empty(w.B, nt, w.H, w.K, w.V, device=dev, dtype=tdt)
+        vnew = torch.empty(w.B, w.T, w.H, w.V, device=dev, dtype=tdt)
+
+        def step():
+            gdn.forward_states(d["q"], d["k"], d["v"], d["beta"], d["g"], w.chunk, d["h0"],
+                               o_dtype=tdt, o=o, hT=hT, hck=hck, vnew=vnew)
+    else:
+        def step():
+            gdn.forward(d["q"], d["k"], d["v"], d["beta"], d["g"], w.chunk, d["h0"],
+                        o_dtype=tdt, o=o, hT=hT, workspace=ws)
 
     print("bench: workload %s warmup %d" % (w.name, args.warmup), file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -185,12 +204,13 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     ms_launch = sum(a.elapsed_time(b) for a, b in evs) / n_k
-    fbytes, fflops = forward_bytes(w, o_dtype), forward_flops(w)
+    fbytes, fflops = forward_bytes(w, o_dtype, args.states), forward_flops(w)
     achieved = fbytes / (ms_launch * 1e-3) / 1e9
     mfma_peak = MFMA_PEAK_TFLOPS["f16" if w.io == "bf16" else "f32"]
-    roofline = {"kernel": kernel_name(w, o_dtype), "bound": "hbm", "achieved": round(achieved, 1),
+    roofline = {"kernel": kernel_name(w, o_dtype, args.states), "bound": "hbm",
+                "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(w, o_dtype),
+                "traffic": measured_traffic(w, o_dtype, args.states),
                 "ms_per_launch": round(ms_launch, 5),
                 "algorithmic_bytes_per_launch": fbytes,
                 "algorithmic_flops_per_launch": fflops,
@@ -209,7 +229,7 @@ def main():
         "dtype": "f16" if w.io == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "K": w.K, "V": w.V,
                    "chunk": w.chunk, "io": w.io, "o_dtype": o_dtype, "gate": w.gate,
-                   "h0": w.h0, "parallelism": "single-gpu"},
+                   "h0": w.h0, "states": bool(args.states), "parallelism": "single-gpu"},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -10,6 +10,8 @@ Entry points (same names as the C ABI):
     prepare(k, v, beta, g, chunk)                 -> (w, u, gcum)
     scan(q, k, w, u, gcum, chunk, h0=None)        -> (o, hT)
     forward(q, k, v, beta, g, chunk, h0=None)     -> (o, hT)
+    forward_states(q, k, v, beta, g, chunk, h0=None)
+                                                  -> (o, hT, hck, vnew)
 Layouts: q, k [B,T,H,K]; v [B,T,H,V]; beta [B,T,H]; g [B,T,H] or [B,T,H,K];
 h0/hT [B,H,K,V] fp32.  q, k, v are bf16 or fp32 (same dtype); o is the io
 dtype unless ``o_dtype`` says otherwise.
@@ -20,7 +22,7 @@ import ctypes
 import os
 import threading
 
-__all__ = ["prepare", "scan", "forward", "workspace_bytes", "load_library",
+__all__ = ["prepare", "scan", "forward", "forward_states", "workspace_bytes", "load_library",
            "GdnError", "LIB_PATH", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,9 +35,9 @@ STATUS = {
     3: "GDN_ERR_UNSUPPORTED", 4: "GDN_ERR_ALIGNMENT", 5: "GDN_ERR_LDS_BUDGET",
     6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP",
 }
-EXPORTS = ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_workspace_bytes",
-           "gdn_status_str", "gdn_abi_version"]
-ABI_VERSION = 1
+EXPORTS = ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_forward_states",
+           "gdn_workspace_bytes", "gdn_status_str", "gdn_abi_version"]
+ABI_VERSION = 2
 
 
 class GdnError(RuntimeError):
@@ -73,7 +75,8 @@ def load_library(path: str | None = None):
         lib.gdn_prepare.argtypes = [pp] + [vp] * 8
         lib.gdn_scan.argtypes = [pp] + [vp] * 9
         lib.gdn_forward.argtypes = [pp] + [vp] * 9 + [sz, vp]
-        for f in (lib.gdn_prepare, lib.gdn_scan, lib.gdn_forward):
+        lib.gdn_forward_states.argtypes = [pp] + [vp] * 11
+        for f in (lib.gdn_prepare, lib.gdn_scan, lib.gdn_forward, lib.gdn_forward_states):
             f.restype = ctypes.c_int
         lib.gdn_workspace_bytes.argtypes = [pp]
         lib.gdn_workspace_bytes.restype = sz
@@ -248,3 +251,47 @@ def forward(q, k, v, beta, g, chunk, h0=None, *, o_dtype=None, o=None, hT=None,
                          ctypes.c_size_t(ws_bytes), _stream(stream))
     _check("gdn_forward", rc)
     return o, hT
+
+
+def forward_states(q, k, v, beta, g, chunk, h0=None, *, o_dtype=None, o=None, hT=None,
+                   hck=None, vnew=None, output_final_state=True, stream=None):
+    """Forward pass that also saves the chunk-start states and the per-token
+    deltas: returns (o, hT or None, hck [B,NT,H,K,V], vnew [B,T,H,V]), with
+    hck and vnew in the o dtype and NT = ceil(T / chunk)."""
+    torch = _torch()
+    lib = load_library()
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    per_key = _gate_kind(g, B, T, H, K)
+    _need(q, "q")
+    _need(k, "k", q.dtype, (B, T, H, K))
+    _need(v, "v", q.dtype, (B, T, H, V))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    _need(g, "g", torch.float32)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (B, H, K, V))
+    od = o_dtype or q.dtype
+    nt = (T + int(chunk) - 1) // int(chunk) if chunk > 0 else 0
+    if o is None:
+        o = torch.empty(B, T, H, V, device=q.device, dtype=od)
+    if hck is None:
+        hck = torch.empty(B, nt, H, K, V, device=q.device, dtype=od)
+    if vnew is None:
+        vnew = torch.empty(B, T, H, V, device=q.device, dtype=od)
+    _need(o, "o", od, (B, T, H, V))
+    _need(hck, "hck", od, (B, nt, H, K, V))
+    _need(vnew, "vnew", od, (B, T, H, V))
+    if hT is None and output_final_state:
+        hT = torch.empty(B, H, K, V, device=q.device, dtype=torch.float32)
+    if hT is not None:
+        _need(hT, "hT", torch.float32, (B, H, K, V))
+    pr = _problem(q, v, chunk, per_key, od)
+    if T == 0:
+        rc = lib.gdn_forward_states(ctypes.byref(pr), None, None, None, None, None,
+                                    _ptr(h0), None, _ptr(hT), None, None, _stream(stream))
+    else:
+        rc = lib.gdn_forward_states(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                    _ptr(g), _ptr(h0), _ptr(o), _ptr(hT), _ptr(hck),
+                                    _ptr(vnew), _stream(stream))
+    _check("gdn_forward_states", rc)
+    return o, hT, hck, vnew

@@ -38,8 +38,10 @@ UNITS = {
     # so fragment loads must run ahead of the matrix instructions using them
     "gdn_forward.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
     "gdn_forward_pipe.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
-    # (the ILP scheduler crashes the compiler on this instance)
+    # (the ILP scheduler crashes the compiler on these instances)
     "gdn_forward_pipe_c32.hip": [],
+    "gdn_forward_states.hip": [],
+    "gdn_forward_states_c64.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
 }
 
 

@@ -205,7 +205,27 @@ gdn_status gdn_forward(const gdn_problem *problem, const void *q, const void *k,
         st = check_ptrs({q, k, v, beta, g, o}, {h0, hT});
         if (st != GDN_OK) return st;
     }
-    return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, (hipStream_t)stream);
+    return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, nullptr, nullptr,
+                           (hipStream_t)stream);
+}
+
+gdn_status gdn_forward_states(const gdn_problem *problem, const void *q, const void *k,
+                              const void *v, const float *beta, const float *g,
+                              const float *h0, void *o, float *hT, void *hck, void *vnew,
+                              void *stream) {
+    gdn_status st = check_problem(problem);
+    if (st != GDN_OK) return st;
+    if (problem->T == 0) {
+        // no chunk, so no checkpoint and no token: only hT = h0 (or zero)
+        st = check_ptrs({}, {h0, hT, hck, vnew});
+        if (st != GDN_OK) return st;
+        if (!hT) return GDN_OK;
+        return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, nullptr, nullptr,
+                               (hipStream_t)stream);
+    }
+    st = check_ptrs({q, k, v, beta, g, o, hck, vnew}, {h0, hT});
+    if (st != GDN_OK) return st;
+    return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, hck, vnew, (hipStream_t)stream);
 }
 
 const char *gdn_status_str(gdn_status status) {

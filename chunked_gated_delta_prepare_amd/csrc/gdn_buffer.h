@@ -54,6 +54,34 @@ template <> struct BufElem<bf16_t> {
     }
 };
 
+// Store one 16 x 16 accumulator tile x of a row-major matrix (lane (g, j)
+// holds rows 4g .. 4g+3 of column j) as runs of two columns: lanes j and
+// j ^ 1 swap halves (DPP quad_perm [1,0,3,2]), so that the even lane holds
+// rows 4g, 4g+1 and the odd lane rows 4g+2, 4g+3 of columns j & ~1 and
+// j | 1, and each lane issues two stores of two elements (4 bytes bf16,
+// 8 bytes fp32) instead of four of one.  voff is the byte offset of this
+// lane's (row 4g + 2 (j & 1), column j & ~1); row_bytes the row pitch;
+// soff the uniform offset of the tile's row 0.
+template <typename OT>
+__device__ __forceinline__ void store_acc_pairs(const float4v &x, rsrc_t r, uint32_t voff,
+                                                uint32_t row_bytes, uint32_t soff) {
+    const bool odd = lane_id() & 1;
+    const float s0 = odd ? x[0] : x[2], s1 = odd ? x[1] : x[3];
+    const float r0 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s0), 0xB1, 0xf, 0xf, false));
+    const float r1 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s1), 0xB1, 0xf, 0xf, false));
+    const float a0 = odd ? r0 : x[0], b0 = odd ? x[2] : r0;     // row 2 odd + 0
+    const float a1 = odd ? r1 : x[1], b1 = odd ? x[3] : r1;     // row 2 odd + 1
+    if constexpr (sizeof(OT) == 2) {
+        bstore32((uint32_t)f32_to_bf16_bits(a0) | ((uint32_t)f32_to_bf16_bits(b0) << 16), r, voff, soff);
+        bstore32((uint32_t)f32_to_bf16_bits(a1) | ((uint32_t)f32_to_bf16_bits(b1) << 16), r, voff,
+                 soff + row_bytes);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(a0), __float_as_uint(b0)}, r, voff, soff, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(a1), __float_as_uint(b1)}, r, voff,
+                                              soff + row_bytes, 0);
+    }
+}
+
 // Eight raw io elements (16 bytes of bf16, 32 bytes of fp32).
 template <typename IO> struct Raw8B;
 template <> struct Raw8B<bf16_t> {

@@ -41,6 +41,10 @@ struct FwdParams {
     const float *beta, *g, *h0;
     void *o;
     float *hT;
+    // saved states (o dtype; both NULL unless the states instance runs):
+    // hck [B, NT, H, K, V] the state at each chunk start, vnew [B, T, H, V]
+    // the delta v' each token writes into the state
+    void *hck, *vnew;
     int B, T, H, V;
     int nvt;        // V / 64
     int swizzle;
@@ -160,7 +164,7 @@ __device__ __forceinline__ void store_row4(_Float16 *dst, const float4v &a) {
 }
 __device__ __forceinline__ void store_row4(float *dst, const float4v &a) { *(float4v *)dst = a; }
 
-template <int C, int K, typename IO, typename OT, bool KEYGATE>
+template <int C, int K, typename IO, typename OT, bool KEYGATE, bool ST = false>
 __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
     typedef FwdLayout<C, K, IO, KEYGATE> L;
     typedef typename L::OpT OpT;
@@ -230,6 +234,11 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
         vv_off[j] = ((uint32_t)row * rsV + vt * 64 + col) * SIO;
     }
     const uint32_t o_off = ((uint32_t)g4 * rsV + vcol) * SO;
+    const rsrc_t rvn_ = make_rsrc(ST ? (OT *)p.vnew + row0 * V : nullptr, ST ? (uint32_t)T * rsV * SO : 0u);
+    // saved states leave the accumulators as column pairs (store_acc_pairs)
+    const uint32_t prow = (uint32_t)(g4 + 2 * (l & 1));
+    const uint32_t vn_off = (prow * rsV + (vcol & ~1)) * SO;
+    const uint32_t hck_off = (prow * V + (vcol & ~1)) * SO;
     constexpr int NR = KEYGATE ? C * K / kThreads : 1;        // KDA gate rows per thread
     const int kseg = KEYGATE ? tid / K : 0, kcol = KEYGATE ? tid % K : 0;
     const uint32_t g_off = KEYGATE ? ((uint32_t)(kseg * NR) * rsG + kcol) * 4
@@ -529,6 +538,13 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
         // of one product is the B fragment of the next (see fragB_acc), the
         // shared operands come from LDS with matching split k slots.
         {
+            if constexpr (ST) {
+                // the state at the start of this chunk: hck[b, c, h, row, vcol]
+                const rsrc_t rh = make_rsrc((OT *)p.hck + (((int64_t)b * nt + c) * H + h) * K * V,
+                                            (uint32_t)(K * V * SO));
+#pragma unroll
+                for (int i = 0; i < NKB; ++i) store_acc_pairs<OT>(hacc[i], rh, hck_off, V * SO, 16 * i * V * SO);
+            }
             float4v eg4[NB], egl4[NB];
             float el = 1.f;
             if constexpr (!KEYGATE) {
@@ -594,6 +610,12 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
                 for (int s = 0; s < C / 32; ++s)
                     if (32 * s < 16 * (cb + 1))
                         M::mma(da[cb], fragA_split(Tmb, LDC, 16 * cb, 32 * s), rf[s]);
+            }
+            if constexpr (ST) {
+                // v' of this chunk's tokens (dropped past token T by the range)
+#pragma unroll
+                for (int cb = 0; cb < NB; ++cb)
+                    store_acc_pairs<OT>(da[cb], rvn_, vn_off, rsV * SO, (t0 + 16 * cb) * rsV * SO);
             }
             // o = e^gcum Y + P v'
             typename M::frag df[C / 32];

@@ -295,7 +295,7 @@ struct PipeLayout {
     static_assert(kSync % 8 == 0, "the two sync counters are read as one 8-byte word");
 };
 
-template <int C, int K, typename OT>
+template <int C, int K, typename OT, bool ST = false>
 __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams p) {
     typedef PipeLayout<C, K> L;
     typedef Mma<_Float16> M;
@@ -346,6 +346,14 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
         const int vcol = vt * 64 + 16 * wv + acc_col();
         // o^T tiles: token (l % 16) of a 16-token block, columns 4 (l / 16) .. +3
         const uint32_t o_off = ((uint32_t)(l & 15) * rsV + vt * 64 + 16 * wv + g4) * SO;
+        // saved states: v' and h leave the accumulators as column pairs
+        // (store_acc_pairs): this lane's first row 4 (l / 16) + 2 (l & 1)
+        // of a 16-row block (tokens for v', key rows for h), columns
+        // vcol & ~1 and vcol | 1
+        const rsrc_t rvn_ = make_rsrc(ST ? (OT *)p.vnew + row0 * V : nullptr, ST ? (uint32_t)T * rsV * SO : 0u);
+        const uint32_t prow = (uint32_t)(g4 + 2 * (l & 1));
+        const uint32_t vn_off = (prow * rsV + (vcol & ~1)) * SO;
+        const uint32_t hck_off = (prow * V + (vcol & ~1)) * SO;
         float4v hacc[NKB];
         if (p.h0) {
 #pragma unroll
@@ -456,6 +464,19 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                 for (int s = 0; s < C / 32; ++s)
                     if (32 * s < 16 * (cb + 1)) M::mma(oa, df[s], frag_sw<C>(Ps, 16 * cb, 32 * s));
                 store4<OT>(oa, ro_, o_off, (t0 + 16 * cb) * rsV * SO);
+            }
+            if constexpr (ST) {
+                // v' of this chunk's tokens (dropped past token T by the range)
+#pragma unroll
+                for (int cb = 0; cb < NB; ++cb)
+                    store_acc_pairs<OT>(da[cb], rvn_, vn_off, rsV * SO, (t0 + 16 * cb) * rsV * SO);
+                // the state at the start of this chunk, hck[b, c, h, row, vcol]:
+                // issued late in the chunk, after the prepare waves' loads of
+                // the chunk after next, which would otherwise queue behind it
+                const rsrc_t rh = make_rsrc((OT *)p.hck + (((int64_t)b * nt + c) * H + h) * K * V,
+                                            (uint32_t)(K * V * SO));
+#pragma unroll
+                for (int i = 0; i < NKB; ++i) store_acc_pairs<OT>(hacc[i], rh, hck_off, V * SO, 16 * i * V * SO);
             }
             // h <- e^gl h + (k e^(gl - gcum))^T v'
 #pragma unroll

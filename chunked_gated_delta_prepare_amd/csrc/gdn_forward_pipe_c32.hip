@@ -1,5 +1,6 @@
-// libgdn: the pipelined forward kernel for chunk 32 with key dim 128, built
-// with the default machine scheduler (see gdn_forward_pipe.hip).
+// libgdn: the pipelined forward kernel instances that the ILP machine
+// scheduler crashes the compiler on (chunk 32 with key dim 128, and chunk 32
+// saving states), built with the default scheduler (see gdn_forward_pipe.hip).
 #include "gdn_forward_pipe.h"
 #include "gdn_internal.h"
 
@@ -8,6 +9,18 @@ namespace gdn {
 gdn_status enqueue_forward_pipe_c32k128(bool o_f32, FwdParams &fp, int grid, hipStream_t s) {
     const void *fn = o_f32 ? (const void *)&forward_pipe_kernel<32, 128, float>
                            : (const void *)&forward_pipe_kernel<32, 128, bf16_t>;
+    return launch_kernel(fn, grid, &fp, s, kPipeThreads);
+}
+
+gdn_status enqueue_forward_pipe_c32_states(int K, bool o_f32, FwdParams &fp, int grid,
+                                           hipStream_t s) {
+    const void *fn;
+    if (K == 64)
+        fn = o_f32 ? (const void *)&forward_pipe_kernel<32, 64, float, true>
+                   : (const void *)&forward_pipe_kernel<32, 64, bf16_t, true>;
+    else
+        fn = o_f32 ? (const void *)&forward_pipe_kernel<32, 128, float, true>
+                   : (const void *)&forward_pipe_kernel<32, 128, bf16_t, true>;
     return launch_kernel(fn, grid, &fp, s, kPipeThreads);
 }
 

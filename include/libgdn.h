@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -138,6 +138,29 @@ gdn_status gdn_forward(const gdn_problem *problem, const void *q, const void *k,
                        const void *v, const float *beta, const float *g,
                        const float *h0, void *o, float *hT, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_forward_states -- gdn_forward that also saves what a backward pass
+ * re-reads: the state at the start of every chunk and the delta each token
+ * writes into the state (kernel_fun KDA re-scan page, bwd_scan.py: the h
+ * checkpoints [B,NT,HV,K,V] and v_new [B,T,HV,V] of its host wrapper
+ * chunk_gated_delta_rule_fwd_h and of KdaB1ScanKernel's per-chunk algebra).
+ *   hck  [B, NT, H, K, V], NT = ceil(T / chunk): hck[b,c,h] is h (the K x V
+ *        state, h = S^T) before token c*chunk is applied; hck[b,0,h] = h0
+ *        (or zero).
+ *   vnew [B, T, H, V]: the chunk form's v' = u - w h, which equals
+ *        beta_t (v_t - S' k_t) with S' the state after token t's decay, so
+ *        that h_t = Diag(a_t) h_{t-1} + k_t vnew_t^T.
+ * Both are written in full, in the problem's o dtype (bf16 rounds to
+ * nearest even).  o, hT and every other argument are as in gdn_forward;
+ * hck and vnew must be non-NULL and 16-byte aligned when T > 0 (with T = 0
+ * nothing is written to them and they may be NULL).  hck, vnew and o must
+ * not alias each other or any input.  Needs no workspace.
+ */
+gdn_status gdn_forward_states(const gdn_problem *problem, const void *q, const void *k,
+                              const void *v, const float *beta, const float *g,
+                              const float *h0, void *o, float *hT, void *hck, void *vnew,
+                              void *stream);
 
 /* Workspace gdn_forward needs for this problem (0 if none); 0 on bad args. */
 size_t gdn_workspace_bytes(const gdn_problem *problem);

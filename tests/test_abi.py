@@ -35,8 +35,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     assert _declared_functions() == sorted(
-        ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_workspace_bytes",
-         "gdn_status_str", "gdn_abi_version"])
+        ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_forward_states",
+         "gdn_workspace_bytes", "gdn_status_str", "gdn_abi_version"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -128,3 +128,28 @@ def test_lds_budget_reported_before_launch(lib, gdn):
     st = lib.gdn_scan(ctypes.byref(pr), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
                       None, None)
     assert st == 5
+
+
+def _fwd_states(lib, pr, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, h0=None, o=FAKE,
+                hT=None, hck=FAKE, vnew=FAKE):
+    return lib.gdn_forward_states(ctypes.byref(pr), q, k, v, beta, g, h0, o, hT, hck,
+                                  vnew, None)
+
+
+def test_forward_states_validates_before_launch(lib, gdn):
+    pr = _problem(gdn)
+    for name in ("q", "k", "v", "beta", "g", "o", "hck", "vnew"):
+        assert _fwd_states(lib, pr, **{name: None}) == 1, name
+    for name in ("q", "o", "hck", "vnew", "h0", "hT"):
+        assert _fwd_states(lib, pr, **{name: MISALIGNED}) == 4, name
+    bad = _problem(gdn, K=96)
+    assert _fwd_states(lib, bad) == 3
+    assert lib.gdn_forward_states(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                                  FAKE, FAKE, None) == 1
+
+
+def test_forward_states_empty_sequence_needs_no_buffers(lib, gdn):
+    # T = 0 with no final state requested: nothing to write, nothing enqueued
+    pr = _problem(gdn, T=0)
+    assert _fwd_states(lib, pr, q=None, k=None, v=None, beta=None, g=None, o=None,
+                       hck=None, vnew=None) == 0
