@@ -12,6 +12,8 @@ Entry points (same names as the C ABI):
     forward(q, k, v, beta, g, chunk, h0=None)     -> (o, hT)
     forward_states(q, k, v, beta, g, chunk, h0=None)
                                                   -> (o, hT, hck, vnew)
+    forward_varlen(q, k, v, beta, g, cu_seqlens, chunk, h0=None)
+                                                  -> (o, hT [N,H,K,V])
 Layouts: q, k [B,T,H,K]; v [B,T,H,V]; beta [B,T,H]; g [B,T,H] or [B,T,H,K];
 h0/hT [B,H,K,V] fp32.  q, k, v are bf16 or fp32 (same dtype); o is the io
 dtype unless ``o_dtype`` says otherwise.
@@ -22,7 +24,8 @@ import ctypes
 import os
 import threading
 
-__all__ = ["prepare", "scan", "forward", "forward_states", "workspace_bytes", "load_library",
+__all__ = ["prepare", "scan", "forward", "forward_states", "forward_varlen", "workspace_bytes",
+           "load_library",
            "GdnError", "LIB_PATH", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,8 +39,8 @@ STATUS = {
     6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP",
 }
 EXPORTS = ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_forward_states",
-           "gdn_workspace_bytes", "gdn_status_str", "gdn_abi_version"]
-ABI_VERSION = 2
+           "gdn_forward_varlen", "gdn_workspace_bytes", "gdn_status_str", "gdn_abi_version"]
+ABI_VERSION = 3
 
 
 class GdnError(RuntimeError):
@@ -76,7 +79,9 @@ def load_library(path: str | None = None):
         lib.gdn_scan.argtypes = [pp] + [vp] * 9
         lib.gdn_forward.argtypes = [pp] + [vp] * 9 + [sz, vp]
         lib.gdn_forward_states.argtypes = [pp] + [vp] * 11
-        for f in (lib.gdn_prepare, lib.gdn_scan, lib.gdn_forward, lib.gdn_forward_states):
+        lib.gdn_forward_varlen.argtypes = [pp, vp, ctypes.c_int64] + [vp] * 9
+        for f in (lib.gdn_prepare, lib.gdn_scan, lib.gdn_forward, lib.gdn_forward_states,
+                  lib.gdn_forward_varlen):
             f.restype = ctypes.c_int
         lib.gdn_workspace_bytes.argtypes = [pp]
         lib.gdn_workspace_bytes.restype = sz
@@ -295,3 +300,43 @@ def forward_states(q, k, v, beta, g, chunk, h0=None, *, o_dtype=None, o=None, hT
                                     _ptr(vnew), _stream(stream))
     _check("gdn_forward_states", rc)
     return o, hT, hck, vnew
+
+
+def forward_varlen(q, k, v, beta, g, cu_seqlens, chunk, h0=None, *, o_dtype=None, o=None,
+                   hT=None, output_final_state=True, stream=None):
+    """Forward pass over packed sequences: q, k [1,T,H,K], v [1,T,H,V], beta
+    [1,T,H], g [1,T,H] or [1,T,H,K]; cu_seqlens an int32 device tensor of
+    N + 1 token offsets; h0 [N,H,K,V] fp32 or None.  Returns (o [1,T,H,V],
+    hT [N,H,K,V] or None)."""
+    torch = _torch()
+    lib = load_library()
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if B != 1:
+        raise ValueError("packed sequences use a batch of 1, got %d" % B)
+    per_key = _gate_kind(g, B, T, H, K)
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must hold N + 1 >= 2 offsets")
+    N = cu_seqlens.numel() - 1
+    _need(q, "q")
+    _need(k, "k", q.dtype, (B, T, H, K))
+    _need(v, "v", q.dtype, (B, T, H, V))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    _need(g, "g", torch.float32)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (N, H, K, V))
+    od = o_dtype or q.dtype
+    if o is None:
+        o = torch.empty(B, T, H, V, device=q.device, dtype=od)
+    _need(o, "o", od, (B, T, H, V))
+    if hT is None and output_final_state:
+        hT = torch.empty(N, H, K, V, device=q.device, dtype=torch.float32)
+    if hT is not None:
+        _need(hT, "hT", torch.float32, (N, H, K, V))
+    pr = _problem(q, v, chunk, per_key, od)
+    rc = lib.gdn_forward_varlen(ctypes.byref(pr), _ptr(cu_seqlens), ctypes.c_int64(N),
+                                _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0),
+                                _ptr(o), _ptr(hT), _stream(stream))
+    _check("gdn_forward_varlen", rc)
+    return o, hT

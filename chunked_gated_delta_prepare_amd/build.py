@@ -42,6 +42,8 @@ UNITS = {
     "gdn_forward_pipe_c32.hip": [],
     "gdn_forward_states.hip": [],
     "gdn_forward_states_c64.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "gdn_forward_varlen.hip": [],
+    "gdn_forward_varlen_c64.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
 }
 
 

@@ -205,7 +205,7 @@ gdn_status gdn_forward(const gdn_problem *problem, const void *q, const void *k,
         st = check_ptrs({q, k, v, beta, g, o}, {h0, hT});
         if (st != GDN_OK) return st;
     }
-    return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, nullptr, nullptr,
+    return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, nullptr, nullptr, nullptr, 0,
                            (hipStream_t)stream);
 }
 
@@ -220,12 +220,35 @@ gdn_status gdn_forward_states(const gdn_problem *problem, const void *q, const v
         st = check_ptrs({}, {h0, hT, hck, vnew});
         if (st != GDN_OK) return st;
         if (!hT) return GDN_OK;
-        return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, nullptr, nullptr,
-                               (hipStream_t)stream);
+        return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, nullptr, nullptr, nullptr,
+                               0, (hipStream_t)stream);
     }
     st = check_ptrs({q, k, v, beta, g, o, hck, vnew}, {h0, hT});
     if (st != GDN_OK) return st;
-    return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, hck, vnew, (hipStream_t)stream);
+    return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, hck, vnew, nullptr, 0,
+                           (hipStream_t)stream);
+}
+
+gdn_status gdn_forward_varlen(const gdn_problem *problem, const int32_t *cu_seqlens,
+                              int64_t n_seqs, const void *q, const void *k, const void *v,
+                              const float *beta, const float *g, const float *h0, void *o,
+                              float *hT, void *stream) {
+    gdn_status st = check_problem(problem);
+    if (st != GDN_OK) return st;
+    if (problem->B != 1 || n_seqs < 1 || n_seqs * problem->H > (1 << 24)) return GDN_ERR_BAD_SHAPE;
+    if (!cu_seqlens) return GDN_ERR_NULL_ARG;
+    if (((uintptr_t)cu_seqlens & 3u) != 0) return GDN_ERR_ALIGNMENT;
+    if (problem->T == 0) {
+        // every sequence is empty: hT = h0 (or zero) per sequence
+        st = check_ptrs({}, {h0, hT});
+        if (st != GDN_OK) return st;
+        if (!hT) return GDN_OK;
+    } else {
+        st = check_ptrs({q, k, v, beta, g, o}, {h0, hT});
+        if (st != GDN_OK) return st;
+    }
+    return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, nullptr, nullptr, cu_seqlens,
+                           n_seqs, (hipStream_t)stream);
 }
 
 const char *gdn_status_str(gdn_status status) {

@@ -45,10 +45,35 @@ struct FwdParams {
     // hck [B, NT, H, K, V] the state at each chunk start, vnew [B, T, H, V]
     // the delta v' each token writes into the state
     void *hck, *vnew;
+    // packed sequences: NULL, or B + 1 token offsets (int32) into a
+    // [1, T, H, .] layout, sequence b being tokens [cu[b], cu[b+1])
+    const int *cu;
     int B, T, H, V;
     int nvt;        // V / 64
     int swizzle;
 };
+
+// The tokens of stream b: batch row b, [0, T) of a [B, T, H, .] layout, or
+// with VL (cu set) the packed sequence b, tokens [cu[b], cu[b+1]) of a
+// [1, T, H, .] layout, the offsets clamped to [0, T] so that no value of cu
+// can reach outside the tensors.  row0 is the stream's first (token, head)
+// row for head h.
+struct StreamRange {
+    int T;
+    int64_t row0;
+};
+template <bool VL>
+__device__ __forceinline__ StreamRange stream_range(const FwdParams &p, int b, int h) {
+    if constexpr (VL) {
+        const int c0 = __builtin_amdgcn_readfirstlane(p.cu[b]);
+        const int c1 = __builtin_amdgcn_readfirstlane(p.cu[b + 1]);
+        const int bos = min(max(c0, 0), p.T);
+        const int eos = min(max(c1, bos), p.T);
+        return StreamRange{eos - bos, (int64_t)bos * p.H + h};
+    } else {
+        return StreamRange{p.T, (int64_t)b * p.T * p.H + h};
+    }
+}
 
 template <int C, int K, typename IO, bool KEYGATE>
 struct FwdLayout {
@@ -164,7 +189,7 @@ __device__ __forceinline__ void store_row4(_Float16 *dst, const float4v &a) {
 }
 __device__ __forceinline__ void store_row4(float *dst, const float4v &a) { *(float4v *)dst = a; }
 
-template <int C, int K, typename IO, typename OT, bool KEYGATE, bool ST = false>
+template <int C, int K, typename IO, typename OT, bool KEYGATE, bool ST = false, bool VL = false>
 __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
     typedef FwdLayout<C, K, IO, KEYGATE> L;
     typedef typename L::OpT OpT;
@@ -202,12 +227,13 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
     int pair, vt;
     map_block(blockIdx.x, p.nvt, p.swizzle, pair, vt);
     const int b = pair / p.H, h = pair - b * p.H;
-    const int T = p.T, H = p.H, V = p.V;
+    const StreamRange sr = stream_range<VL>(p, b, h);
+    const int T = sr.T, H = p.H, V = p.V;
     const int vcol = vt * 64 + 16 * wv + acc_col();          // this lane's value column
     const int nt = (T + C - 1) / C;
 
     // ---- buffer descriptors: each covers this (b, h) stream up to token T
-    const int64_t row0 = (int64_t)b * T * H + h;
+    const int64_t row0 = sr.row0;
     const uint32_t rsK = (uint32_t)(H * K), rsV = (uint32_t)(H * V);
     const uint32_t rsG = KEYGATE ? rsK : (uint32_t)H;
     const rsrc_t rq_ = make_rsrc((const IO *)p.q + row0 * K, (uint32_t)T * rsK * SIO);

@@ -22,18 +22,21 @@ static bool fits_32bit_streams(const gdn_problem *pr) {
 gdn_status enqueue_forward(const gdn_problem *pr, const void *q, const void *k,
                            const void *v, const float *beta, const float *g,
                            const float *h0, void *o, float *hT, void *hck, void *vnew,
-                           hipStream_t s) {
+                           const int32_t *cu, int64_t n_seqs, hipStream_t s) {
     if (!fits_32bit_streams(pr)) return GDN_ERR_UNSUPPORTED;
     FwdParams fp;
     fp.q = q; fp.k = k; fp.v = v; fp.beta = beta; fp.g = g; fp.h0 = h0;
-    fp.o = o; fp.hT = hT; fp.hck = hck; fp.vnew = vnew;
-    fp.B = (int)pr->B; fp.T = (int)pr->T; fp.H = (int)pr->H; fp.V = (int)pr->V;
+    fp.o = o; fp.hT = hT; fp.hck = hck; fp.vnew = vnew; fp.cu = cu;
+    // packed sequences: one stream per sequence over the [1, T, H, .] tensors
+    const int64_t streams = cu ? n_seqs : pr->B;
+    fp.B = (int)streams; fp.T = (int)pr->T; fp.H = (int)pr->H; fp.V = (int)pr->V;
     fp.nvt = (int)(pr->V / 64);
-    const int pairs = (int)(pr->B * pr->H);
+    const int pairs = (int)(streams * pr->H);
     fp.swizzle = (pairs % 8 == 0) ? 1 : 0;
     if (const char *e = std::getenv("GDN_NO_SWIZZLE")) fp.swizzle = (*e == '1') ? 0 : fp.swizzle;
     const int grid = pairs * fp.nvt;
     if (hck) return enqueue_forward_states(pr, fp, grid, s);
+    if (cu) return enqueue_forward_varlen(pr, fp, grid, s);
     return pr->chunk == 32 ? forward_k<32, false>(pr, fp, grid, s)
                            : forward_k<64, false>(pr, fp, grid, s);
 }

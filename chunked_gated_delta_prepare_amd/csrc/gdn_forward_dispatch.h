@@ -1,6 +1,7 @@
 // libgdn: dispatch of a validated forward problem onto the kernel template
-// instances, for the plain forward (ST = false) and for the forward that also
-// saves states (ST = true); each is instantiated in its own translation unit.
+// instances, for the plain forward (ST = false), the forward that also saves
+// states (ST = true) and the one over packed sequences (VL = true); each is
+// instantiated in its own translation units.
 #pragma once
 
 #include <cstdlib>
@@ -16,37 +17,37 @@ inline bool pipe_disabled() {
     return e && *e == '1';
 }
 
-template <int C, int K, typename IO, typename OT, bool KG, bool ST>
+template <int C, int K, typename IO, typename OT, bool KG, bool ST, bool VL>
 gdn_status run_forward(FwdParams &fp, int grid, hipStream_t s) {
     if constexpr (FwdLayout<C, K, IO, KG>::kBytes > kLdsBytesMax) {
         return GDN_ERR_LDS_BUDGET;
     } else {
-        return launch_kernel((const void *)&forward_kernel<C, K, IO, OT, KG, ST>, grid, &fp, s);
+        return launch_kernel((const void *)&forward_kernel<C, K, IO, OT, KG, ST, VL>, grid, &fp, s);
     }
 }
 
 // Scalar gate with bf16 io runs the pipelined kernel (prepare and re-scan on
 // separate waves); the per-key gate and fp32 io run the four-wave kernel.
-template <int C, int K, typename IO, typename OT, bool ST>
+template <int C, int K, typename IO, typename OT, bool ST, bool VL>
 gdn_status forward_gate(const gdn_problem *pr, FwdParams &fp, int grid, hipStream_t s) {
-    if (pr->gate == GDN_GATE_KEY) return run_forward<C, K, IO, OT, true, ST>(fp, grid, s);
+    if (pr->gate == GDN_GATE_KEY) return run_forward<C, K, IO, OT, true, ST, VL>(fp, grid, s);
     if constexpr (sizeof(IO) == 2) {
         if (!pipe_disabled()) return enqueue_forward_pipe(C, K, sizeof(OT) == 4, fp, grid, s);
     }
-    return run_forward<C, K, IO, OT, false, ST>(fp, grid, s);
+    return run_forward<C, K, IO, OT, false, ST, VL>(fp, grid, s);
 }
 
-template <int C, int K, bool ST>
+template <int C, int K, bool ST, bool VL>
 gdn_status forward_dt(const gdn_problem *pr, FwdParams &fp, int grid, hipStream_t s) {
-    if (pr->io_dtype == GDN_F32) return forward_gate<C, K, float, float, ST>(pr, fp, grid, s);
-    if (pr->o_dtype == GDN_F32) return forward_gate<C, K, bf16_t, float, ST>(pr, fp, grid, s);
-    return forward_gate<C, K, bf16_t, bf16_t, ST>(pr, fp, grid, s);
+    if (pr->io_dtype == GDN_F32) return forward_gate<C, K, float, float, ST, VL>(pr, fp, grid, s);
+    if (pr->o_dtype == GDN_F32) return forward_gate<C, K, bf16_t, float, ST, VL>(pr, fp, grid, s);
+    return forward_gate<C, K, bf16_t, bf16_t, ST, VL>(pr, fp, grid, s);
 }
 
-template <int C, bool ST>
+template <int C, bool ST, bool VL = false>
 gdn_status forward_k(const gdn_problem *pr, FwdParams &fp, int grid, hipStream_t s) {
-    return pr->K == 64 ? forward_dt<C, 64, ST>(pr, fp, grid, s)
-                       : forward_dt<C, 128, ST>(pr, fp, grid, s);
+    return pr->K == 64 ? forward_dt<C, 64, ST, VL>(pr, fp, grid, s)
+                       : forward_dt<C, 128, ST, VL>(pr, fp, grid, s);
 }
 
 }  // namespace

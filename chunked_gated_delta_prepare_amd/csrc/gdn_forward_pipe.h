@@ -295,7 +295,7 @@ struct PipeLayout {
     static_assert(kSync % 8 == 0, "the two sync counters are read as one 8-byte word");
 };
 
-template <int C, int K, typename OT, bool ST = false>
+template <int C, int K, typename OT, bool ST = false, bool VL = false>
 __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams p) {
     typedef PipeLayout<C, K> L;
     typedef Mma<_Float16> M;
@@ -323,9 +323,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
     int pair, vt;
     map_block(blockIdx.x, p.nvt, p.swizzle, pair, vt);
     const int b = pair / p.H, h = pair - b * p.H;
-    const int T = p.T, H = p.H, V = p.V;
+    const StreamRange sr = stream_range<VL>(p, b, h);
+    const int T = sr.T, H = p.H, V = p.V;
     const int nt = (T + C - 1) / C;
-    const int64_t row0 = (int64_t)b * T * H + h;
+    const int64_t row0 = sr.row0;
     const uint32_t rsK = (uint32_t)(H * K), rsV = (uint32_t)(H * V);
 
     // the operand tiles above the diagonal are read but stay zero

@@ -14,17 +14,26 @@ gdn_status launch_kernel(const void *fn, int grid, void *params, hipStream_t s,
 
 // Enqueue the fused forward kernel (validated problem, non-empty work).
 // hck and vnew are both NULL, or both set for the instance that also saves
-// the chunk-start states and the per-token deltas.
+// the chunk-start states and the per-token deltas.  cu (n_seqs + 1 device
+// int32 offsets) selects packed sequences over a B = 1 problem, or is NULL.
 gdn_status enqueue_forward(const gdn_problem *pr, const void *q, const void *k,
                            const void *v, const float *beta, const float *g,
                            const float *h0, void *o, float *hT, void *hck, void *vnew,
-                           hipStream_t s);
+                           const int32_t *cu, int64_t n_seqs, hipStream_t s);
 
 struct FwdParams;
 // Dispatch a forward problem whose FwdParams carry hck and vnew.
 gdn_status enqueue_forward_states(const gdn_problem *pr, FwdParams &fp, int grid, hipStream_t s);
 gdn_status enqueue_forward_states_c64(const gdn_problem *pr, FwdParams &fp, int grid,
                                       hipStream_t s);
+// Dispatch a forward problem whose FwdParams carry packed-sequence offsets.
+gdn_status enqueue_forward_varlen(const gdn_problem *pr, FwdParams &fp, int grid, hipStream_t s);
+gdn_status enqueue_forward_varlen_c64(const gdn_problem *pr, FwdParams &fp, int grid,
+                                      hipStream_t s);
+gdn_status enqueue_forward_pipe_varlen_c32(int K, bool o_f32, FwdParams &fp, int grid,
+                                           hipStream_t s);
+gdn_status enqueue_forward_pipe_varlen_c64(int K, bool o_f32, FwdParams &fp, int grid,
+                                           hipStream_t s);
 // Launch the pipelined forward kernel (scalar gate, bf16 io) for chunk C,
 // key dim K and fp32 (else bf16) output.
 gdn_status enqueue_forward_pipe(int C, int K, bool o_f32, FwdParams &fp, int grid,

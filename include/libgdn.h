@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -161,6 +161,29 @@ gdn_status gdn_forward_states(const gdn_problem *problem, const void *q, const v
                               const void *v, const float *beta, const float *g,
                               const float *h0, void *o, float *hT, void *hck, void *vnew,
                               void *stream);
+
+/*
+ * gdn_forward_varlen -- gdn_forward over packed sequences of different
+ * lengths (the kernel_fun re-scan page's host wrapper takes only T a
+ * multiple of 64 and falls back otherwise; here any lengths run in the one
+ * kernel, each sequence from its own initial state).
+ *   problem->B must be 1 and problem->T is the total token count; q, k, v,
+ *   beta, g, o use the [1, T, H, .] layouts of gdn_forward.
+ *   cu_seqlens: n_seqs + 1 int32 token offsets in device memory (4-byte
+ *   aligned), cu_seqlens[0] = 0, nondecreasing, cu_seqlens[n_seqs] = T;
+ *   sequence n is tokens [cu_seqlens[n], cu_seqlens[n+1]).  The kernel
+ *   clamps each offset into [0, T] (a malformed list gives wrong results,
+ *   never an access outside the tensors); it must hold n_seqs + 1 entries.
+ *   h0, hT: [n_seqs, H, K, V] fp32, the initial and final state of each
+ *   sequence; h0 NULL means zero states, hT NULL means not written.
+ * The state never crosses from one sequence into the next; results equal
+ * separate gdn_forward calls per sequence.  Returns GDN_ERR_BAD_SHAPE if
+ * problem->B != 1 or n_seqs < 1.  Needs no workspace.
+ */
+gdn_status gdn_forward_varlen(const gdn_problem *problem, const int32_t *cu_seqlens,
+                              int64_t n_seqs, const void *q, const void *k, const void *v,
+                              const float *beta, const float *g, const float *h0, void *o,
+                              float *hT, void *stream);
 
 /* Workspace gdn_forward needs for this problem (0 if none); 0 on bad args. */
 size_t gdn_workspace_bytes(const gdn_problem *problem);

@@ -36,7 +36,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     assert _declared_functions() == sorted(
         ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_forward_states",
-         "gdn_workspace_bytes", "gdn_status_str", "gdn_abi_version"])
+         "gdn_forward_varlen", "gdn_workspace_bytes", "gdn_status_str", "gdn_abi_version"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -153,3 +153,25 @@ def test_forward_states_empty_sequence_needs_no_buffers(lib, gdn):
     pr = _problem(gdn, T=0)
     assert _fwd_states(lib, pr, q=None, k=None, v=None, beta=None, g=None, o=None,
                        hck=None, vnew=None) == 0
+
+
+def _fwd_varlen(lib, pr, cu=FAKE, n=2, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, h0=None,
+                o=FAKE, hT=None):
+    return lib.gdn_forward_varlen(ctypes.byref(pr), cu, ctypes.c_int64(n), q, k, v, beta, g,
+                                  h0, o, hT, None)
+
+
+def test_forward_varlen_validates_before_launch(lib, gdn):
+    pr = _problem(gdn, B=1, T=200)
+    assert _fwd_varlen(lib, pr, cu=None) == 1
+    assert _fwd_varlen(lib, pr, cu=ctypes.c_void_p(0x10002)) == 4
+    assert _fwd_varlen(lib, _problem(gdn, B=2, T=200)) == 2     # packed means B = 1
+    assert _fwd_varlen(lib, pr, n=0) == 2
+    assert _fwd_varlen(lib, pr, n=(1 << 24) + 1) == 2
+    for name in ("q", "k", "v", "beta", "g", "o"):
+        assert _fwd_varlen(lib, pr, **{name: None}) == 1, name
+    assert _fwd_varlen(lib, pr, h0=MISALIGNED) == 4
+    assert _fwd_varlen(lib, _problem(gdn, B=1, T=200, K=96)) == 3
+    # no tokens and no final state: nothing to do
+    assert _fwd_varlen(lib, _problem(gdn, B=1, T=0), q=None, k=None, v=None, beta=None,
+                       g=None, o=None) == 0
