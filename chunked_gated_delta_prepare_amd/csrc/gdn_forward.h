@@ -4,7 +4,8 @@
 // chunk of C tokens with chunk-start state h (K x 64 slice, fp32 registers):
 //   gcum  chunk-local inclusive cumsum of g
 //   A     strictly lower beta * (k k^T * decay)           (Gram on the MFMA)
-//   Tm    (I + A)^-1                                        (blockwise, fp32)
+//   Tm    (I + A)^-1: the 16 x 16 diagonal blocks inverted, the rest
+//         applied by blocks in the chain (see solve_block)
 //   X     k h                     R' = v - e^gcum * X       (GDN)
 //   v'    Tm diag(beta) R'        (= u - w h of the WY form, without forming
 //                                   w or u: the KDA re-scan page's v')
@@ -20,14 +21,17 @@
 // cooperatively in phases separated by workgroup barriers:
 //   phase 0  registers -> LDS operands; gate cumsum and row factors; the next
 //            chunk's loads are issued
-//   phase 1  Gram tiles; diagonal 16x16 inverses and the first sub-diagonal
-//            merge by the wave that computed their Gram tiles
-//   phase 2  the remaining merges of the inverse (C = 64)
-//   phase 3  the wave-local chain
+//   phase 1  Gram tiles; diagonal 16x16 inverses T_bb and the first solve
+//            block by the wave that computed their Gram tiles
+//   phase 2  the remaining solve blocks (C = 64)
+//   phase 3  the wave-local chain, which finishes the triangular solve by
+//            blocks of 16 tokens (see solve_block)
 // All HBM traffic is buffer loads/stores; a stream's byte range ends at token
 // T, so the rows of a short last chunk read as zero (an identity step: g = 0,
 // beta = 0, k = 0) and their outputs are dropped by the hardware.
 #pragma once
+
+#include <type_traits>
 
 #include "gdn_buffer.h"
 #include "gdn_chunk_io.h"
@@ -86,7 +90,7 @@ struct FwdLayout {
     static constexpr int kQ = 0;                                   // [C][LDK]
     static constexpr int kK = kQ + C * LDK * E;                    // [C][LDK]
     static constexpr int kKi = kK + C * LDK * E;                   // KDA: [C][LDK]
-    static constexpr int kTmb = kKi + (KEYGATE ? C * LDK * E : 0);  // [C][LDC] Tm diag(beta)
+    static constexpr int kTmb = kKi + (KEYGATE ? C * LDK * E : 0);  // [C][LDC] solve blocks
     static constexpr int kP = kTmb + C * LDC * E;                  // [C][LDC]
     // bf16 io: chunk data is prefetched from HBM straight into LDS: raw q, k
     // in per-thread vector order (each thread later converts the vectors its
@@ -108,7 +112,8 @@ struct FwdLayout {
     static constexpr int kScrBytes = (KEYGATE && C * K * 4 > kScrBytes0) ? C * K * 4 : kScrBytes0;
     // per-row / per-key fp32 factors
     static constexpr int kRow = kScr + kScrBytes;
-    static constexpr int NSEG = kThreads / K;                      // KDA cumsum segments
+    // KDA cumsum segments: a thread holds 4 key columns of C / NSEG rows
+    static constexpr int NSEG = kThreads * 4 / K;
     static constexpr int kRowN = KEYGATE ? (C + 5 * K + NSEG * K) : (5 * C + NB * C + 4);
     static constexpr int kBytes = kRow + kRowN * 4;
 };
@@ -147,25 +152,24 @@ __device__ __forceinline__ void diag_inverse(const float *A, float *Tm, int b0, 
     }
 }
 
-// Tm_ij = -T_ii * sum_{k=j}^{i-1} A_ik Tm_kj for one 16x16 block, one wave;
-// the result goes to Tm (fp32) and, scaled by beta of its columns, to Tmb.
+// (I + A)^-1 is never formed whole: the chain solves (I + A) v' = diag(beta) R'
+// by blocks of 16 tokens,
+//     v'_b = Tb_bb R'_b + sum_{j<b} Mn_bj v'_j,
+//     Tb_bb = T_bb diag(beta_b),  Mn_bj = -T_bb A_bj,  T_bb = (I + A_bb)^-1,
+// with row block b of the C x C operand tile Tmb holding [Mn_b0 .. | Tb_bb | 0]
+// (the TileOPs fused-prepare page's A_g inverse, applied by blocks).  This
+// writes Mn_ij (one 16 x 16 product, one wave) into Tmb.
 template <int LDA, int LDC, typename OpT>
-__device__ __forceinline__ void merge_block(const float *A, float *Tm, OpT *Tmb,
-                                            const float *bet, int i, int j) {
-    float4v x = {0, 0, 0, 0};
-    for (int k = j; k < i; ++k)
-        mm16_f32(x, A + 16 * i * LDA + 16 * k, LDA, Tm + 16 * k * LDA + 16 * j, LDA);
-    x = -x;
-    float4v y = {0, 0, 0, 0};
-    mm16_f32_regB(y, Tm + 16 * i * LDA + 16 * i, LDA, x);
-    const int col = 16 * j + acc_col();
-    const float bc = bet[col];
+__device__ __forceinline__ void solve_block(const float *A, const float *Tm, OpT *Tmb,
+                                            int i, int j) {
+    const int l = lane_id(), g4 = 4 * (l >> 4), col = l & 15;
+    float4v a;                      // A_ij in accumulator layout
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int row = 16 * i + acc_row(r);
-        Tm[row * LDA + col] = y[r];
-        Tmb[row * LDC + col] = Mma<OpT>::cvt(y[r] * bc);
-    }
+    for (int r = 0; r < 4; ++r) a[r] = A[(16 * i + g4 + r) * LDA + 16 * j + col];
+    float4v y = {0, 0, 0, 0};
+    mm16_f32_regB(y, Tm + 16 * i * LDA + 16 * i, LDA, a);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Tmb[(16 * i + g4 + r) * LDC + 16 * j + col] = Mma<OpT>::cvt(-y[r]);
 }
 
 // Copy a diagonal block of Tm into Tmb scaled by beta of its columns.  (The
@@ -265,8 +269,12 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
     const uint32_t prow = (uint32_t)(g4 + 2 * (l & 1));
     const uint32_t vn_off = (prow * rsV + (vcol & ~1)) * SO;
     const uint32_t hck_off = (prow * V + (vcol & ~1)) * SO;
-    constexpr int NR = KEYGATE ? C * K / kThreads : 1;        // KDA gate rows per thread
-    const int kseg = KEYGATE ? tid / K : 0, kcol = KEYGATE ? tid % K : 0;
+    // KDA gate: thread (kseg, cg) holds rows kseg NR .. +NR-1 of the four key
+    // columns 4 cg .. 4 cg + 3, one 16-byte load per row (one load per lane
+    // per row would take four times the vector-memory instructions, and the
+    // waves stall at issue while the loads of a chunk queue up)
+    constexpr int NR = KEYGATE ? C * K / (4 * kThreads) : 1;
+    const int kseg = KEYGATE ? tid / (K / 4) : 0, kcol = KEYGATE ? 4 * (tid % (K / 4)) : 0;
     const uint32_t g_off = KEYGATE ? ((uint32_t)(kseg * NR) * rsG + kcol) * 4
                                    : (uint32_t)l * rsG * 4;
 
@@ -292,7 +300,8 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
     constexpr int NRQ = L::kStage ? 1 : NVEC;
     Raw8B<IO> rq[NRQ], rk[NRQ];         // fp32 io: q, k rows
     float vreg[L::kStage ? 1 : NB][4];  // fp32 io: v in accumulator layout
-    float g_own[NR];
+    float g_own[KEYGATE ? 1 : NR];
+    float4v gk4[KEYGATE ? NR : 1];      // KDA: gates of four key columns per row
     float b_own = 0.f;
     // (the gate and beta loads go first: the staged loads are then the last
     // memory operations of a chunk before its outputs are stored)
@@ -301,7 +310,7 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
         if constexpr (KEYGATE) {
 #pragma unroll
             for (int i = 0; i < NR; ++i)
-                g_own[i] = __uint_as_float(bload32(rg_, g_off, (t0 + i) * rsG * 4));
+                gk4[i] = __builtin_bit_cast(float4v, bload128(rg_, g_off, (t0 + i) * rsG * 4));
         } else {
             g_own[0] = __uint_as_float(bload32(rg_, g_off, t0 * rsG * 4));
         }
@@ -399,24 +408,25 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
                 if (c + 1 < nt) load_chunk(c + 1);
             __syncthreads();
         } else {
-            // gcum down each key column: thread (seg, kd) holds NR rows
-            float run = 0.f;
+            // gcum down each key column: thread (seg, cg) holds NR rows of
+            // four columns; segment totals are added in segment order
+            float4v run = {0, 0, 0, 0};
 #pragma unroll
-            for (int i = 0; i < NR; ++i) { run += g_own[i]; g_own[i] = run; }
-            segt[kseg * K + kcol] = run;
+            for (int i = 0; i < NR; ++i) { run += gk4[i]; gk4[i] = run; }
+            *(float4v *)(segt + kseg * K + kcol) = run;
             __syncthreads();
-            float off = 0.f;
+            float4v off = {0, 0, 0, 0};
 #pragma unroll
             for (int sgi = 0; sgi < L::NSEG; ++sgi)
-                if (sgi < kseg) off += segt[sgi * K + kcol];
+                if (sgi < kseg) off += *(const float4v *)(segt + sgi * K + kcol);
             constexpr int MROW = C / 2 - 1;
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
                 const int row = kseg * NR + i;
-                const float gg = g_own[i] + off;
-                Gst[row * K + kcol] = gg;
-                if (row == MROW) gmv[kcol] = gg;
-                if (row == C - 1) glv[kcol] = gg;
+                const float4v gg = gk4[i] + off;
+                *(float4v *)(Gst + row * K + kcol) = gg;
+                if (row == MROW) *(float4v *)(gmv + kcol) = gg;
+                if (row == C - 1) *(float4v *)(glv + kcol) = gg;
             }
             __syncthreads();
             if (tid < K) {
@@ -456,7 +466,7 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
             __syncthreads();
         }
 
-        // ================= phase 1: Gram, diagonal inverses, first merges ===
+        // ================= phase 1: Gram, diagonal inverses, first solve block
         // Staged prefetch of the next chunk: issued here, after the barrier
         // that retires this chunk's staging reads, so that a whole phase of
         // work separates it from the next barrier (which waits for it).
@@ -466,9 +476,7 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
         // r of block I), so lane (l/16, j) ends up with row r = 16 I + j and
         // four consecutive columns s = 16 J + 4 (l/16) + e: one vector store.
         {
-            auto gram_tile = [&](int I, int J, bool isA) {
-                float4v acc = {0, 0, 0, 0};
-                mma_tile<OpT, K>(acc, Ki + 16 * J * LDK, LDK, (isA ? Ks : Qs) + 16 * I * LDK, LDK);
+            auto gram_put = [&](int I, int J, bool isA, const float4v &acc) {
                 const int r = 16 * I + acc_col(), s0 = 16 * J + g4;
                 float4v fac = {1.f, 1.f, 1.f, 1.f};
                 if constexpr (!KEYGATE) {
@@ -489,11 +497,43 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
                     store_row4(Ps + r * LDC + s0, a);
                 }
             };
+            // Several tiles at once (a wave-uniform list): every fragment
+            // load first, then the accumulations interleaved, so that one
+            // wave per SIMD keeps the matrix pipe busy instead of waiting out
+            // each tile's load and dependent accumulate latency in turn.
+            auto gram_batch = [&](auto n_c, const int *tI, const int *tJ, const bool *tA) {
+                constexpr int N = decltype(n_c)::value;
+                typename M::frag fa[N][K / 32], fb[N][K / 32];
+#pragma unroll
+                for (int u = 0; u < N; ++u)
+#pragma unroll
+                    for (int k = 0; k < K / 32; ++k) {
+                        fa[u][k] = M::load(frag_ptr(Ki + 16 * tJ[u] * LDK, LDK, 32 * k));
+                        fb[u][k] = M::load(frag_ptr((tA[u] ? Ks : Qs) + 16 * tI[u] * LDK, LDK, 32 * k));
+                    }
+                float4v acc[N];
+#pragma unroll
+                for (int u = 0; u < N; ++u) acc[u] = float4v{0, 0, 0, 0};
+#pragma unroll
+                for (int k = 0; k < K / 32; ++k)
+#pragma unroll
+                    for (int u = 0; u < N; ++u) M::mma(acc[u], fa[u][k], fb[u][k]);
+#pragma unroll
+                for (int u = 0; u < N; ++u) gram_put(tI[u], tJ[u], tA[u], acc[u]);
+            };
+            // tiles per batch: fp32 fragments are twice the registers
+            constexpr int BATCH = sizeof(OpT) == 2 ? 4 : 1;
             const int pb = 2 * wv;          // diagonal pair (pb, pb+1) for waves 0 .. NB/2-1
             if (wv < NB / 2) {
-                gram_tile(pb, pb, true);
-                gram_tile(pb + 1, pb + 1, true);
-                gram_tile(pb + 1, pb, true);
+                const int tI[3] = {pb, pb + 1, pb + 1}, tJ[3] = {pb, pb + 1, pb};
+                const bool tA[3] = {true, true, true};
+                if constexpr (BATCH >= 3) {
+                    gram_batch(std::integral_constant<int, 3>{}, tI, tJ, tA);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 3; ++u)
+                        gram_batch(std::integral_constant<int, 1>{}, tI + u, tJ + u, tA + u);
+                }
                 if constexpr (sizeof(OpT) == 2) {
                     // fp16 operands: the two diagonal inverses on the matrix
                     // cores (block doubling), into Tm's fp32 rows
@@ -511,51 +551,50 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
                 }
                 emit_diag<LDA, LDC, OpT>(Tmf, Tmb, betp, pb);
                 emit_diag<LDA, LDC, OpT>(Tmf, Tmb, betp, pb + 1);
-                merge_block<LDA, LDC, OpT>(Af, Tmf, Tmb, betp, pb + 1, pb);
+                solve_block<LDA, LDC, OpT>(Af, Tmf, Tmb, pb + 1, pb);
             }
             // the other tiles, round robin over the waves that hold no pair
             constexpr int NA_REST = (NB == 4) ? 4 : 0;    // A (2,0) (2,1) (3,0) (3,1)
             constexpr int NP = NB * (NB + 1) / 2;
             constexpr int NREST = NA_REST + NP;
             constexpr int W0 = NB / 2, NW = kWaves - NB / 2;
+            constexpr int PER = NREST / NW;               // tiles t = (wv - W0) + NW u
+            static_assert(NREST % NW == 0, "the other tiles split evenly over their waves");
+            if (wv >= W0) {
+                int tI[PER], tJ[PER];
+                bool tA[PER];
 #pragma unroll
-            for (int t = 0; t < NREST; ++t) {
-                if (W0 + t % NW != wv) continue;
-                if (t < NA_REST) {
-                    gram_tile(2 + t / 2, t % 2, true);
-                } else {
-                    const int idx = t - NA_REST;
-                    int I = 0;
-                    while ((I + 1) * (I + 2) / 2 <= idx) ++I;
-                    gram_tile(I, idx - I * (I + 1) / 2, false);
+                for (int u = 0; u < PER; ++u) {
+                    const int t = (wv - W0) + NW * u;
+                    if (t < NA_REST) {
+                        tI[u] = 2 + t / 2; tJ[u] = t % 2; tA[u] = true;
+                    } else {
+                        const int idx = t - NA_REST;
+                        int I = 0;
+                        while ((I + 1) * (I + 2) / 2 <= idx) ++I;
+                        tI[u] = I; tJ[u] = idx - I * (I + 1) / 2; tA[u] = false;
+                    }
+                }
+#pragma unroll
+                for (int u0 = 0; u0 < PER; u0 += BATCH) {
+                    if constexpr (PER % BATCH == 0) {
+                        gram_batch(std::integral_constant<int, BATCH>{}, tI + u0, tJ + u0, tA + u0);
+                    } else {
+                        if (u0 + BATCH <= PER)
+                            gram_batch(std::integral_constant<int, BATCH>{}, tI + u0, tJ + u0, tA + u0);
+                        else
+                            gram_batch(std::integral_constant<int, PER % BATCH>{}, tI + u0, tJ + u0, tA + u0);
+                    }
                 }
             }
         }
         __syncthreads();
 
-        // ================= phase 2: remaining merges (C = 64) ================
+        // ================= phase 2: remaining solve blocks (C = 64) ==========
         if constexpr (NB == 4) {
-            //   X = A_[23][01] T_[01];  Tm_[23][01] = -T_[23] X
-            const int i = 2 + (wv >> 1), j = wv & 1;
-            float4v x0 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
-            for (int k = j; k < 2; ++k)
-                mm16_f32(x0, Af + 32 * LDA + 16 * k, LDA, Tmf + 16 * k * LDA + 16 * j, LDA);
-            if (i == 3)
-                for (int k = j; k < 2; ++k)
-                    mm16_f32(x1, Af + 48 * LDA + 16 * k, LDA, Tmf + 16 * k * LDA + 16 * j, LDA);
-            x0 = -x0;
-            x1 = -x1;
-            float4v y = {0, 0, 0, 0};
-            if (i == 2) {
-                mm16_f32_regB(y, Tmf + 32 * LDA + 32, LDA, x0);            // T22 X2j
-            } else {
-                mm16_f32_regB(y, Tmf + 48 * LDA + 32, LDA, x0);            // T32 X2j
-                mm16_f32_regB(y, Tmf + 48 * LDA + 48, LDA, x1);            // T33 X3j
-            }
-            const int col = 16 * j + acc_col();
-            const float bc = betp[col];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Tmb[(16 * i + g4 + r) * LDC + col] = M::cvt(y[r] * bc);
+            // Mn_20, Mn_21, Mn_30, Mn_31: T_22 and T_33 from the pair waves,
+            // the A blocks from the tile waves
+            solve_block<LDA, LDC, OpT>(Af, Tmf, Tmb, 2 + (wv >> 1), wv & 1);
             __syncthreads();
         }
 
@@ -624,18 +663,22 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
                 if constexpr (KEYGATE) rr[cb] = vv - xa[cb];
                 else rr[cb] = vv - eg4[cb] * xa[cb];
             }
-            // v' = Tm diag(beta) R'   (lower triangular: k steps up to the diagonal)
-            typename M::frag rf[C / 32];
-#pragma unroll
-            for (int s = 0; s < C / 32; ++s) rf[s] = fragB_acc(rr[2 * s], rr[2 * s + 1], OpT{});
+            // v' solves (I + A) v' = diag(beta) R' by blocks of 16 tokens
+            // (see solve_block): row block b of Tmb is [Mn_b0 .. | Tb_bb | 0],
+            // so each step is a 32-wide k step over a [v' ; R'] fragment pair
             float4v da[NB];
-#pragma unroll
-            for (int cb = 0; cb < NB; ++cb) {
-                da[cb] = float4v{0, 0, 0, 0};
-#pragma unroll
-                for (int s = 0; s < C / 32; ++s)
-                    if (32 * s < 16 * (cb + 1))
-                        M::mma(da[cb], fragA_split(Tmb, LDC, 16 * cb, 32 * s), rf[s]);
+            da[0] = float4v{0, 0, 0, 0};
+            M::mma(da[0], fragA_split(Tmb, LDC, 0, 0), fragB_acc(rr[0], rr[1], OpT{}));
+            da[1] = float4v{0, 0, 0, 0};
+            M::mma(da[1], fragA_split(Tmb, LDC, 16, 0), fragB_acc(da[0], rr[1], OpT{}));
+            if constexpr (NB == 4) {
+                da[2] = float4v{0, 0, 0, 0};
+                da[3] = float4v{0, 0, 0, 0};
+                M::mma(da[2], fragA_split(Tmb, LDC, 32, 32), fragB_acc(rr[2], rr[3], OpT{}));
+                const typename M::frag d01 = fragB_acc(da[0], da[1], OpT{});
+                M::mma(da[2], fragA_split(Tmb, LDC, 32, 0), d01);
+                M::mma(da[3], fragA_split(Tmb, LDC, 48, 0), d01);
+                M::mma(da[3], fragA_split(Tmb, LDC, 48, 32), fragB_acc(da[2], rr[3], OpT{}));
             }
             if constexpr (ST) {
                 // v' of this chunk's tokens (dropped past token T by the range)
