@@ -305,16 +305,28 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
     float b_own = 0.f;
     // (the gate and beta loads go first: the staged loads are then the last
     // memory operations of a chunk before its outputs are stored)
-    auto load_chunk = [&](int c) {
+    // The loads of a chunk come in parts (kLd*), so that the staged path can
+    // spread them over the previous chunk: the CU's memory pipeline takes
+    // about a cycle per 64 bytes, and a wave that issues more loads than it
+    // queues stalls at issue until they drain.
+    enum { kLdG = 1, kLdQ = 2, kLdK = 4, kLdV = 8, kLdAll = 15 };
+    auto load_gate_rows = [&](int c, int i0, int n) {      // KDA gate rows i0 .. i0+n-1
         const uint32_t t0 = (uint32_t)(c * C);
-        if constexpr (KEYGATE) {
 #pragma unroll
-            for (int i = 0; i < NR; ++i)
-                gk4[i] = __builtin_bit_cast(float4v, bload128(rg_, g_off, (t0 + i) * rsG * 4));
-        } else {
-            g_own[0] = __uint_as_float(bload32(rg_, g_off, t0 * rsG * 4));
-        }
+        for (int i = i0; i < i0 + n; ++i)
+            gk4[i] = __builtin_bit_cast(float4v, bload128(rg_, g_off, (t0 + i) * rsG * 4));
+    };
+    auto load_beta = [&](int c) {
+        const uint32_t t0 = (uint32_t)(c * C);
         b_own = __uint_as_float(bload32(rb_, (uint32_t)l * (uint32_t)H * 4, t0 * (uint32_t)H * 4));
+    };
+    auto load_chunk = [&](int c, int parts) {
+        const uint32_t t0 = (uint32_t)(c * C);
+        if (parts & kLdG) {
+            if constexpr (KEYGATE) load_gate_rows(c, 0, NR);
+            else g_own[0] = __uint_as_float(bload32(rg_, g_off, t0 * rsG * 4));
+            load_beta(c);
+        }
         if constexpr (L::kStage) {
 #if defined(__HIP_DEVICE_COMPILE__)
             // (device pass only: seen by the host pass, this builtin makes it
@@ -324,16 +336,20 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
 #pragma unroll
             for (int j = 0; j < NVEC; ++j) {
                 const int blk = (j * kThreads + wv * 64) * 8;     // in 16-bit elements
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rq_, (lds_void *)(Sq + blk), 16,
-                                                         qk_off[j], t0 * rsK * SIO, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk_, (lds_void *)(Sk + blk), 16,
-                                                         qk_off[j], t0 * rsK * SIO, 0, 0);
+                if (parts & kLdQ)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq_, (lds_void *)(Sq + blk), 16,
+                                                             qk_off[j], t0 * rsK * SIO, 0, 0);
+                if (parts & kLdK)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk_, (lds_void *)(Sk + blk), 16,
+                                                             qk_off[j], t0 * rsK * SIO, 0, 0);
             }
             uint16_t *vdst = Vs + (c & 1) * C * L::LDV;
+            if (parts & kLdV) {
 #pragma unroll
-            for (int j = 0; j < NVV; ++j)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv_, (lds_void *)(vdst + (j * kThreads + wv * 64) * 8),
-                                                         16, vv_off[j], t0 * rsV * SIO, 0, 0);
+                for (int j = 0; j < NVV; ++j)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv_, (lds_void *)(vdst + (j * kThreads + wv * 64) * 8),
+                                                             16, vv_off[j], t0 * rsV * SIO, 0, 0);
+            }
 #endif
         } else {
 #pragma unroll
@@ -348,7 +364,16 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
                     vreg[cb][r] = BufElem<IO>::load(rv_, v_off, (t0 + 16 * cb + r) * rsV * SIO);
         }
     };
-    if (nt > 0) load_chunk(0);
+    if (nt > 0) load_chunk(0, kLdAll);
+    // staged path: the parts of chunk c+1 issued during chunk c
+    //   KDA gate rows and beta   phase 0, two rows per operand vector, once
+    //                            the gate scan of chunk c is done with them
+    //   (scalar gate and beta)   phase 1
+    //   q                        phase 1        k   phase 2 (C = 64) or 3
+    //   v                        phase 3
+    constexpr int kLdP1 = kLdQ | (KEYGATE ? 0 : kLdG);
+    constexpr int kLdP2 = NB == 4 ? kLdK : 0;
+    constexpr int kLdP3 = kLdV | (NB == 4 ? 0 : kLdK);
 
     for (int c = 0; c < nt; ++c) {
         const uint32_t t0 = (uint32_t)(c * C);
@@ -405,7 +430,7 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
                 if (l == 0) misc[0] = fast_exp(gl);
             }
             if constexpr (!L::kStage)
-                if (c + 1 < nt) load_chunk(c + 1);
+                if (c + 1 < nt) load_chunk(c + 1, kLdAll);
             __syncthreads();
         } else {
             // gcum down each key column: thread (seg, cg) holds NR rows of
@@ -460,9 +485,18 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
                 put8(Qs + row * LDK + col, a);
                 put8(Ks + row * LDK + col, bq);
                 put8(Ki + row * LDK + col, bk);
+                if constexpr (L::kStage) {
+                    // the next chunk's gate rows (NR = 2 NVEC), spread over
+                    // the loop; this chunk's are in Gst by now
+                    static_assert(NR == 2 * NVEC, "two gate rows per operand vector");
+                    if (c + 1 < nt) {
+                        load_gate_rows(c + 1, 2 * j, 2);
+                        if (j == 0) load_beta(c + 1);
+                    }
+                }
             }
             if constexpr (!L::kStage)
-                if (c + 1 < nt) load_chunk(c + 1);
+                if (c + 1 < nt) load_chunk(c + 1, kLdAll);
             __syncthreads();
         }
 
@@ -471,7 +505,7 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
         // that retires this chunk's staging reads, so that a whole phase of
         // work separates it from the next barrier (which waits for it).
         if constexpr (L::kStage)
-            if (c + 1 < nt) load_chunk(c + 1);
+            if (c + 1 < nt) load_chunk(c + 1, kLdP1);
         // Tile (I, J) is computed transposed (rows s of block J against rows
         // r of block I), so lane (l/16, j) ends up with row r = 16 I + j and
         // four consecutive columns s = 16 J + 4 (l/16) + e: one vector store.
@@ -591,6 +625,8 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
         __syncthreads();
 
         // ================= phase 2: remaining solve blocks (C = 64) ==========
+        if constexpr (L::kStage && kLdP2 != 0)
+            if (c + 1 < nt) load_chunk(c + 1, kLdP2);
         if constexpr (NB == 4) {
             // Mn_20, Mn_21, Mn_30, Mn_31: T_22 and T_33 from the pair waves,
             // the A blocks from the tile waves
@@ -599,6 +635,8 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
         }
 
         // ================= phase 3: the wave-local chain =====================
+        if constexpr (L::kStage)
+            if (c + 1 < nt) load_chunk(c + 1, kLdP3);
         // Every intermediate (h, R', v') stays in registers: the accumulator
         // of one product is the B fragment of the next (see fragB_acc), the
         // shared operands come from LDS with matching split k slots.
