@@ -175,3 +175,15 @@ def test_forward_varlen_validates_before_launch(lib, gdn):
     # no tokens and no final state: nothing to do
     assert _fwd_varlen(lib, _problem(gdn, B=1, T=0), q=None, k=None, v=None, beta=None,
                        g=None, o=None) == 0
+
+
+def test_streams_beyond_32bit_offsets_rejected(lib, gdn):
+    # one (batch, head) stream of q addressed with 32-bit byte offsets: T*H*K*2
+    # bytes must stay below 4 GiB; 2^20 tokens of 16 heads of 128 reach it
+    pr = _problem(gdn, B=1, T=1 << 20, H=16, K=128, V=128)
+    assert _fwd(lib, pr) == 3
+    assert _fwd_states(lib, pr) == 3
+    assert _fwd_varlen(lib, pr) == 3
+    # one token fewer fits
+    ok = _problem(gdn, B=1, T=(1 << 20) - 1, H=16, K=128, V=128)
+    assert lib.gdn_workspace_bytes(ctypes.byref(ok)) == 0
