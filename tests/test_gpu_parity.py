@@ -296,3 +296,102 @@ def test_workload_full_size_sampled(name):
     run_case("full_" + name, w.B, w.T, w.H, w.K, w.V, w.chunk, w.io, w.gate, w.gate_bias,
              w.h0, w.seed, o_dtypes=[w.io] if w.io == "fp32" else ["bf16", "fp32"],
              heads=heads)
+
+
+# ---------------------------------------------------------------------------
+# invariants and closed forms checked on the GPU itself
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("gate,io,K,V,C", [("head", "bf16", 128, 128, 64), ("key", "bf16", 128, 64, 64),
+                                           ("head", "bf16", 64, 64, 32), ("key", "fp32", 64, 64, 32)])
+def test_beta_zero_state_is_pure_decay(gate, io, K, V, C):
+    """beta = 0: nothing is written into the state, so h_t = exp(G_t) h0 with
+    G_t the running sum of the gate (per key row for the per-key gate) and
+    o_t = h_t^T q_t; a closed form in fp64, independent of the oracle."""
+    B, T, H = 1, 2 * C + 17, 2
+    inp = make_inputs(B, T, H, K, V, io=io, gate=gate, gate_bias=3.0, h0=True, seed=21)
+    inp["beta"] = torch.zeros_like(inp["beta"])
+    d = _cuda(inp)
+    o, hT = gdn.forward(d["q"], d["k"], d["v"], d["beta"], d["g"], C, d["h0"],
+                        o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    G = np.cumsum(inp["g"].numpy().astype(np.float64), axis=1)         # [B,T,H(,K)]
+    h0 = inp["h0"].numpy().astype(np.float64)                           # [B,H,K,V]
+    q = inp["q"].float().numpy().astype(np.float64)                     # [B,T,H,K]
+    if gate == "key":
+        o_ref = np.einsum("bthk,bthk,bhkv->bthv", q, np.exp(G), h0)
+        h_ref = np.exp(G[:, -1])[..., None] * h0
+    else:
+        o_ref = np.exp(G)[..., None] * np.einsum("bthk,bhkv->bthv", q, h0)
+        h_ref = np.exp(G[:, -1])[..., None, None] * h0
+    ro, rh = oracle.rel_err(_np(o), o_ref), oracle.rel_err(_np(hT), h_ref)
+    _record("beta0_%s_%s" % (gate, io), o_rel=ro, hT_rel=rh)
+    assert ro <= TOL[io] and rh <= TOL[io]
+
+
+@pytest.mark.parametrize("C", [32, 64])
+def test_plain_deltanet_with_orthonormal_keys_is_linear_attention(C):
+    """g = 0, beta = 1, orthonormal keys and h0 = 0: every token writes v_t
+    along a fresh direction, so S_T = sum_s v_s k_s^T and
+    o_t = sum_{s <= t} (k_s . q_t) v_s (linear attention).  The keys are
+    rows of a 64 x 64 Hadamard matrix times 1/8, exact in bf16 and fp16."""
+    T, K, V, H = 64, 64, 64, 2
+    Hd = np.array([[1.0]])
+    while Hd.shape[0] < K:
+        Hd = np.block([[Hd, Hd], [Hd, -Hd]])
+    gen = np.random.default_rng(5)
+    keys = np.stack([Hd[gen.permutation(K)[:T]] / 8.0 for _ in range(H)], axis=1)   # [T,H,K]
+    inp = make_inputs(1, T, H, K, V, io="bf16", gate="head", seed=22)
+    inp["k"] = torch.from_numpy(keys[None].astype(np.float32)).to(torch.bfloat16).contiguous()
+    inp["g"] = torch.zeros_like(inp["g"])
+    inp["beta"] = torch.ones_like(inp["beta"])
+    d = _cuda(inp)
+    o, hT = gdn.forward(d["q"], d["k"], d["v"], d["beta"], d["g"], C, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    q = inp["q"].float().numpy().astype(np.float64)[0]                # [T,H,K]
+    k = inp["k"].float().numpy().astype(np.float64)[0]
+    v = inp["v"].float().numpy().astype(np.float64)[0]
+    scores = np.tril(np.einsum("thk,shk->hts", q, k))                 # [H,T,S], s <= t
+    o_ref = np.einsum("hts,shv->thv", scores, v)[None]
+    h_ref = np.einsum("shk,shv->hkv", k, v)[None]
+    ro, rh = oracle.rel_err(_np(o), o_ref), oracle.rel_err(_np(hT), h_ref)
+    _record("linear_attention_C%d" % C, o_rel=ro, hT_rel=rh)
+    assert ro <= TOL["bf16"] and rh <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("gate", ["head", "key"])
+def test_prepare_residuals(gate):
+    """gdn_prepare's own outputs satisfy the equations that define them, with
+    A built in fp64 from the inputs: (I + A) w = diag(beta e^gcum) k and
+    (I + A) u = diag(beta) v per chunk (no oracle involved)."""
+    B, T, H, K, V, C = 1, 2 * 64 + 11, 2, 128, 128, 64
+    inp = make_inputs(B, T, H, K, V, io="bf16", gate=gate, gate_bias=2.5, seed=23)
+    d = _cuda(inp)
+    w, u, gc = gdn.prepare(d["k"], d["v"], d["beta"], d["g"], C)
+    torch.cuda.synchronize()
+    k = inp["k"].float().numpy().astype(np.float64)[0]
+    v = inp["v"].float().numpy().astype(np.float64)[0]
+    beta = inp["beta"].numpy().astype(np.float64)[0]
+    g = inp["g"].numpy().astype(np.float64)[0]
+    w, u = _np(w)[0].astype(np.float64), _np(u)[0].astype(np.float64)
+    worst = 0.0
+    for hh in range(H):
+        for s in range(0, T, C):
+            e = min(s + C, T)
+            kc, vc, bc = k[s:e, hh], v[s:e, hh], beta[s:e, hh]
+            gam = np.cumsum(g[s:e, hh], axis=0)
+            if gate == "key":
+                A = np.einsum("rd,sd,rsd->rs", kc, kc, np.exp(gam[:, None, :] - gam[None, :, :]))
+                rhs_w = bc[:, None] * np.exp(gam) * kc
+            else:
+                A = (kc @ kc.T) * np.exp(gam[:, None] - gam[None, :])
+                rhs_w = (bc * np.exp(gam))[:, None] * kc
+            A = np.tril(bc[:, None] * A, -1)
+            I = np.eye(e - s)
+            rw = (I + A) @ w[s:e, hh] - rhs_w
+            ru = (I + A) @ u[s:e, hh] - bc[:, None] * vc
+            worst = max(worst, np.abs(rw).max() / np.sqrt(np.mean(rhs_w ** 2)),
+                        np.abs(ru).max() / np.sqrt(np.mean((bc[:, None] * vc) ** 2)))
+    _record("prepare_residual_%s" % gate, residual=worst)
+    assert worst <= TOL["bf16"]
+
