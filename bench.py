@@ -74,12 +74,13 @@ def forward_flops(w):
 
 def kernel_name(w, o_dtype, states=False):
     """Template instance of the kernel that gdn_forward (or, with states,
-    gdn_forward_states) launches: the pipelined kernel for a scalar gate with
-    bf16 io, else the four-wave one."""
+    gdn_forward_states) launches: with bf16 io the pipelined kernel of the
+    scalar or the per-key gate, with fp32 io the four-wave one."""
     io = {"bf16": "bf16_t", "fp32": "float"}
     st = ", true" if states else ""
-    if w.gate == "head" and w.io == "bf16":
-        return "forward_pipe_kernel<%d, %d, %s%s>" % (w.chunk, w.K, io[o_dtype], st)
+    if w.io == "bf16":
+        name = "forward_pipe_kernel" if w.gate == "head" else "forward_pipe_kda_kernel"
+        return "%s<%d, %d, %s%s>" % (name, w.chunk, w.K, io[o_dtype], st)
     return "forward_kernel<%d, %d, %s, %s, %s%s>" % (w.chunk, w.K, io[w.io], io[o_dtype],
                                                      "true" if w.gate == "key" else "false", st)
 

@@ -26,15 +26,19 @@ gdn_status run_forward(FwdParams &fp, int grid, hipStream_t s) {
     }
 }
 
-// Scalar gate with bf16 io runs the pipelined kernel (prepare and re-scan on
-// separate waves); the per-key gate and fp32 io run the four-wave kernel.
+// bf16 io runs the pipelined kernels (prepare and re-scan on separate waves),
+// one for the scalar gate and one for the per-key gate; fp32 io runs the
+// four-wave kernel (as does bf16 io with GDN_FORWARD_FOUR_WAVE=1).
 template <int C, int K, typename IO, typename OT, bool ST, bool VL>
 gdn_status forward_gate(const gdn_problem *pr, FwdParams &fp, int grid, hipStream_t s) {
-    if (pr->gate == GDN_GATE_KEY) return run_forward<C, K, IO, OT, true, ST, VL>(fp, grid, s);
+    const bool key = pr->gate == GDN_GATE_KEY;
     if constexpr (sizeof(IO) == 2) {
-        if (!pipe_disabled()) return enqueue_forward_pipe(C, K, sizeof(OT) == 4, fp, grid, s);
+        if (!pipe_disabled())
+            return key ? enqueue_forward_pipe_kda(C, K, sizeof(OT) == 4, fp, grid, s)
+                       : enqueue_forward_pipe(C, K, sizeof(OT) == 4, fp, grid, s);
     }
-    return run_forward<C, K, IO, OT, false, ST, VL>(fp, grid, s);
+    return key ? run_forward<C, K, IO, OT, true, ST, VL>(fp, grid, s)
+               : run_forward<C, K, IO, OT, false, ST, VL>(fp, grid, s);
 }
 
 template <int C, int K, bool ST, bool VL>

@@ -1,0 +1,31 @@
+// libgdn: dispatch of the pipelined forward kernel for the per-key gate
+// (gdn_forward_pipe_kda.h), plain, saving states (ST) or over packed
+// sequences (VL).
+#include "gdn_forward_pipe_kda.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+namespace {
+template <int C, int K, bool ST, bool VL>
+const void *kda_fn(bool o_f32) {
+    return o_f32 ? (const void *)&forward_pipe_kda_kernel<C, K, float, ST, VL>
+                 : (const void *)&forward_pipe_kda_kernel<C, K, bf16_t, ST, VL>;
+}
+
+template <int C, int K>
+const void *kda_mode(bool o_f32, const FwdParams &fp) {
+    if (fp.hck) return kda_fn<C, K, true, false>(o_f32);
+    if (fp.cu) return kda_fn<C, K, false, true>(o_f32);
+    return kda_fn<C, K, false, false>(o_f32);
+}
+}  // namespace
+
+gdn_status enqueue_forward_pipe_kda(int C, int K, bool o_f32, FwdParams &fp, int grid,
+                                    hipStream_t s) {
+    const void *fn = C == 32 ? (K == 64 ? kda_mode<32, 64>(o_f32, fp) : kda_mode<32, 128>(o_f32, fp))
+                             : (K == 64 ? kda_mode<64, 64>(o_f32, fp) : kda_mode<64, 128>(o_f32, fp));
+    return launch_kernel(fn, grid, &fp, s, kPipeThreads);
+}
+
+}  // namespace gdn

@@ -39,6 +39,9 @@ gdn_status enqueue_forward_pipe_varlen_c64(int K, bool o_f32, FwdParams &fp, int
 gdn_status enqueue_forward_pipe(int C, int K, bool o_f32, FwdParams &fp, int grid,
                                 hipStream_t s);
 gdn_status enqueue_forward_pipe_c32k128(bool o_f32, FwdParams &fp, int grid, hipStream_t s);
+// The pipelined kernel for the per-key gate (plain, ST or VL by fp.hck / fp.cu).
+gdn_status enqueue_forward_pipe_kda(int C, int K, bool o_f32, FwdParams &fp, int grid,
+                                    hipStream_t s);
 // Chunk 32, saving the chunk-start states and the per-token deltas.
 gdn_status enqueue_forward_pipe_c32_states(int K, bool o_f32, FwdParams &fp, int grid,
                                            hipStream_t s);
