@@ -252,17 +252,21 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
         float4v rg[NR];
         u32x4 rv[NVV];
         float b_pre = 0.f;
-        auto issue_loads = [&](int n) {
+        // The loads of chunk n come in pieces, each issued as soon as the
+        // registers it fills are free: the CU's memory pipeline takes about a
+        // cycle per 64 bytes, and 72 KB per chunk issued at once would stall
+        // the issuing waves for most of that time.
+        auto load_v_beta = [&](int n) {
             const uint32_t t0 = (uint32_t)(n * C);
 #pragma unroll
             for (int j = 0; j < NVV; ++j) rv[j] = bload128(rv_, vv_off[j], t0 * rsV * SIO);
-#pragma unroll
-            for (int i = 0; i < NR; ++i) {
-                rg[i] = __builtin_bit_cast(float4v, bload128(rg_, g_off, (t0 + i) * rsK * 4));
-                rq[i] = bload64(rq_, qk_off, (t0 + i) * rsK * SIO);
-                rk[i] = bload64(rk_, qk_off, (t0 + i) * rsK * SIO);
-            }
             if (pt < C) b_pre = __uint_as_float(bload32(rb_, (uint32_t)pt * (uint32_t)H * 4, t0 * (uint32_t)H * 4));
+        };
+        auto load_row = [&](int n, int i) {
+            const uint32_t t0 = (uint32_t)(n * C);
+            rg[i] = __builtin_bit_cast(float4v, bload128(rg_, g_off, (t0 + i) * rsK * 4));
+            rq[i] = bload64(rq_, qk_off, (t0 + i) * rsK * SIO);
+            rk[i] = bload64(rk_, qk_off, (t0 + i) * rsK * SIO);
         };
         unsigned sync_target = 0;
 
@@ -277,6 +281,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
 #pragma unroll
             for (int j = 0; j < NVV; ++j) *(u32x4 *)(Vs + vv_lds[j]) = rv[j];
             if (pt < C) bet[pt] = b_pre;
+            if (n + 1 < nt) load_v_beta(n + 1);
             float4v run = {0, 0, 0, 0};
 #pragma unroll
             for (int i = 0; i < NR; ++i) { run += rg[i]; rg[i] = run; }
@@ -322,9 +327,9 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
                 *(half4 *)(Qs + qk_lds[i]) = hq;
                 *(half4 *)(Ks + qk_lds[i]) = hk;
                 *(half4 *)(Hs + qk_lds[i]) = hh;
+                if (n + 1 < nt) load_row(n + 1, i);
             }
             prep_arrive(sync_ctr, sync_target);
-            if (n + 1 < nt) issue_loads(n + 1);
             // every prepare wave's operand rows (and beta) are in
             wait_counter(sync_ctr, sync_target);
 
@@ -477,7 +482,9 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
         };
 
         if (nt > 0) {
-            issue_loads(0);
+            load_v_beta(0);
+#pragma unroll
+            for (int i = 0; i < NR; ++i) load_row(0, i);
             prepare(0);
         }
         wg_barrier();                       // chunk 0 prepared
