@@ -167,5 +167,9 @@ __device__ __forceinline__ int acc_row(int r) { return 4 * (lane_id() >> 4) + r;
 __device__ __forceinline__ int acc_col() { return lane_id() & 15; }
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
+// 2^x on the transcendental unit (v_exp_f32), for arguments already scaled
+// by log2(e) (one multiply shared by e^d and e^-d).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float kLog2e = 1.4426950408889634f;
 
 }  // namespace gdn

@@ -312,11 +312,11 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
             // ---- operands q~, k~, k^ (fp16) of this thread's rows
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
-                const float4v d = rg[i] + off - gm;
+                const float4v d = (rg[i] + off - gm) * kLog2e;
                 half4 hq, hk, hh;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float up = fast_exp(d[e]), dn = fast_exp(-d[e]);
+                    const float up = fast_exp2(d[e]), dn = fast_exp2(-d[e]);
                     const uint32_t wq = rq[i][e >> 1], wk = rk[i][e >> 1];
                     const float xq = __uint_as_float((e & 1) ? (wq & 0xffff0000u) : (wq << 16));
                     const float xk = __uint_as_float((e & 1) ? (wk & 0xffff0000u) : (wk << 16));
