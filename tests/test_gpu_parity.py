@@ -395,3 +395,16 @@ def test_prepare_residuals(gate):
     _record("prepare_residual_%s" % gate, residual=worst)
     assert worst <= TOL["bf16"]
 
+
+
+# ---------------------------------------------------------------------------
+# the four-wave kernel with bf16 io (GDN_FORWARD_FOUR_WAVE=1): the fallback
+# schedule for both gates stays parity-green too
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("gate,K,V,C", [("head", 128, 128, 64), ("key", 128, 128, 64),
+                                        ("key", 64, 128, 32), ("head", 64, 64, 32)])
+def test_four_wave_kernel_bf16(gate, K, V, C, monkeypatch):
+    monkeypatch.setenv("GDN_FORWARD_FOUR_WAVE", "1")
+    run_case("four_wave", 2, 3 * C + 21, 2, K, V, C, "bf16", gate, 3.0 if gate == "key" else 2.0,
+             True, seed=31 + K + C, o_dtypes=["fp32", "bf16"])
