@@ -408,3 +408,41 @@ def test_four_wave_kernel_bf16(gate, K, V, C, monkeypatch):
     monkeypatch.setenv("GDN_FORWARD_FOUR_WAVE", "1")
     run_case("four_wave", 2, 3 * C + 21, 2, K, V, C, "bf16", gate, 3.0 if gate == "key" else 2.0,
              True, seed=31 + K + C, o_dtypes=["fp32", "bf16"])
+
+
+# ---------------------------------------------------------------------------
+# the largest stream the 32-bit buffer offsets allow
+# ---------------------------------------------------------------------------
+
+def test_forward_at_the_32bit_stream_limit():
+    """One (batch, head) stream of q spans T*H*K*2 bytes of address range;
+    the library accepts up to just below 4 GiB.  T = 2^20 - 64 tokens of 32
+    heads of K = V = 64 come within 8 KiB of it; two heads are checked against
+    the oracle over the whole sequence.  Inputs are drawn on the GPU from a
+    seeded generator (the same distributions as the workloads), then the two
+    heads' slices are copied back for the oracle."""
+    d = _dev()
+    B, T, H, K, V, C = 1, (1 << 20) - 64, 32, 64, 64, 64
+    assert T * H * K * 2 < (1 << 32) and (T + 64) * H * K * 2 >= (1 << 32)
+    gen = torch.Generator(device=d).manual_seed(41)
+    q = torch.randn(B, T, H, K, device=d, generator=gen)
+    q = (q / q.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    k = torch.randn(B, T, H, K, device=d, generator=gen)
+    k = (k / k.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    v = torch.randn(B, T, H, V, device=d, generator=gen).to(torch.bfloat16)
+    beta = torch.sigmoid(torch.randn(B, T, H, device=d, generator=gen))
+    g = torch.nn.functional.logsigmoid(torch.randn(B, T, H, device=d, generator=gen) + 2.0)
+    # (o in bf16: an fp32 o stream would pass 4 GiB and is refused)
+    o, hT = gdn.forward(q, k, v, beta, g, C)
+    torch.cuda.synchronize()
+    for hh in (0, H - 1):
+        sl = lambda x: x[:, :, hh:hh + 1].contiguous().float().cpu().numpy()
+        o_ref, h_ref = oracle.token_recurrence(sl(q), sl(k), sl(v), sl(beta), sl(g))
+        og = o[:, :, hh:hh + 1].float().cpu().numpy()
+        hg = hT[:, hh:hh + 1].cpu().numpy()
+        ro = check_o(og, o_ref, "bf16", "limit head %d" % hh, "bf16")
+        rh = oracle.rel_err(hg, h_ref)
+        _record("limit_T%d_head%d" % (T, hh), o_rel=ro, hT_rel=rh)
+        assert rh <= TOL["bf16"]
+    del q, k, v, o
+    torch.cuda.empty_cache()
