@@ -74,6 +74,13 @@ def test_every_dispatched_kernel_is_present(disassembly):
     for kernel in ("forward_pipe_kernelILi64ELi128ENS_6bf16_t", "forward_pipe_kernelILi64ELi128Ef",
                    "forward_pipe_kernelILi32ELi64ENS_6bf16_t", "forward_pipe_kernelILi32ELi128ENS_6bf16_t",
                    "forward_kernelILi64ELi128ENS_6bf16_tES1_Lb1", "forward_kernelILi64ELi64EffLb0",
+                   "forward_pipe_kda_kernelILi64ELi128ENS_6bf16_t",
+                   "forward_pipe_kda_kernelILi32ELi64ENS_6bf16_t",
+                   # instances that save states (ST) and read packed sequences (VL)
+                   "forward_pipe_kernelILi64ELi128ENS_6bf16_tELb1ELb0",
+                   "forward_pipe_kernelILi64ELi128ENS_6bf16_tELb0ELb1",
+                   "forward_pipe_kda_kernelILi64ELi128ENS_6bf16_tELb1ELb0",
+                   "forward_pipe_kda_kernelILi64ELi128ENS_6bf16_tELb0ELb1",
                    "prepare_kernel", "scan_kernel"):
         assert kernel in demangled, kernel
 
