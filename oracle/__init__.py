@@ -9,7 +9,8 @@ These functions mirror the library entry points:
 * ``token_recurrence`` -- the plain definition (C, fp64, one token at a time),
   the reference for ``gdn_forward``.  See ``gdn_oracle.c`` for the recurrence.
   ``token_states`` also records the per-chunk start states and the per-token
-  state deltas, the reference for ``gdn_forward_states``.
+  state deltas, the reference for ``gdn_forward_states``; ``rescan_dq`` forms
+  dq's chunk-start-state term from them, the reference for ``gdn_rescan_dq``.
 * ``chunk_prepare`` -- the per-chunk WY factors (gate cumsum, the strictly lower
   decayed Gram matrix, its unit-triangular inverse, then w and u), the
   reference for ``gdn_prepare``.  Steps follow the TileOPs "Reuse P as beta
@@ -151,6 +152,27 @@ def token_states(q, k, v, beta, g, chunk, h0=None, heads=None, nthreads=None):
     [n,T,V].
     """
     return _recurrence(q, k, v, beta, g, h0, heads, nthreads, True, True, int(chunk))
+
+
+def rescan_dq(hck, do, chunk):
+    """The chunk-start-state term of dq that the backward's re-scan forms
+    (the KDA re-scan page, bwd_scan.py module docstring: DQ = do h_c^T, raw:
+    no gate and no scale, those are applied by the later stage): for token t
+    of chunk c, dq[t] = h_c do_t, with h_c (K x V) the state at the chunk's
+    start, the checkpoints of ``token_states``.
+
+    hck [B,NT,H,K,V], do [B,T,H,V] -> [B,T,H,K] fp64.
+    """
+    hck = np.asarray(hck, np.float64)
+    do = np.asarray(do, np.float64)
+    B, T, H, V = do.shape
+    K = hck.shape[3]
+    dq = np.zeros((B, T, H, K), np.float64)
+    for c in range(hck.shape[1]):
+        s, e = c * chunk, min(c * chunk + chunk, T)
+        # [B,H,K,V] x [B,t,H,V] -> [B,t,H,K]
+        dq[:, s:e] = np.einsum("bhkv,bthv->bthk", hck[:, c], do[:, s:e])
+    return dq
 
 
 # --------------------------------------------------------------------------

@@ -559,3 +559,46 @@ def test_planted_mistakes_are_caught(oracle_mod, name, tmp_path):
     assert not _pins_pass(mod), "planted mistake %r was not caught" % name
     # the unmutated oracle passes the same subset
     assert _pins_pass(oracle_mod)
+
+
+@pytest.mark.parametrize("per_key", [False, True])
+def test_rescan_dq_with_state_deltas_is_the_autograd_dq(oracle_mod, per_key):
+    """dq of L = sum_t o_t . do_t by autograd of a plain fp64 torch loop
+    equals, token by token, the chunk-start term rescan_dq (raw) under the
+    gate decay plus the in-chunk writes:
+        dq_t = e^{G_t} (h_c do_t) + sum_{s <= t in chunk} e^{G_t - G_s} k_s (vnew_s . do_t)
+    with G the chunk-local cumsum (per key column for the per-key gate)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(401)
+    T, K, V, C = 19, 5, 3, 6
+    q, k, v, beta, g, h0 = _small_case(rng, T, K, V, per_key)
+    do = rng.standard_normal((1, T, 1, V)).astype(np.float32)
+    _, _, hck, vnew = oracle_mod.token_states(q, k, v, beta, g, C, h0, nthreads=1)
+    dq_raw = oracle_mod.rescan_dq(hck, do, C)
+
+    f64 = lambda x: torch.tensor(np.asarray(x, np.float64))
+    qt = f64(q[0, :, 0]).requires_grad_(True)
+    kt, vt, bt, gt = f64(k[0, :, 0]), f64(v[0, :, 0]), f64(beta[0, :, 0]), f64(g[0, :, 0])
+    S = f64(h0[0, 0]).T.clone()                                  # S = h^T, V x K
+    loss = 0.0
+    for t in range(T):
+        a = torch.exp(gt[t])
+        S = S * a                                                 # per key column (or scalar)
+        e = vt[t] - S @ kt[t]
+        S = S + bt[t] * torch.outer(e, kt[t])
+        loss = loss + (S @ qt[t]) @ f64(do[0, t, 0])
+    loss.backward()
+    dq = qt.grad.numpy()
+
+    gg = g[0, :, 0].astype(np.float64)
+    if not per_key:
+        gg = gg[:, None] * np.ones((1, K))
+    kk = k[0, :, 0].astype(np.float64)
+    dd = do[0, :, 0].astype(np.float64)
+    for t in range(T):
+        s0 = (t // C) * C
+        G = np.cumsum(gg[s0:t + 1], axis=0)                       # G[j] = sum up to s0 + j
+        x = np.exp(G[-1]) * dq_raw[0, t, 0]
+        for s in range(s0, t + 1):
+            x += np.exp(G[-1] - G[s - s0]) * kk[s] * (vnew[0, s, 0] @ dd[t])
+        np.testing.assert_allclose(x, dq[t], rtol=1e-9, atol=1e-11)
