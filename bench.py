@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--o-dtype", default=None, choices=[None, "bf16", "fp32"])
     ap.add_argument("--states", action="store_true",
                     help="time gdn_forward_states (also saves chunk-start states and v')")
+    ap.add_argument("--rescan", action="store_true",
+                    help="time gdn_rescan_dq (the backward's re-scan: states, v', dq; no o)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
@@ -53,10 +55,14 @@ def io_bytes(dt):
     return {"bf16": 2, "fp32": 4}[dt]
 
 
-def forward_bytes(w, o_dtype, states=False):
+def forward_bytes(w, o_dtype, states=False, rescan=False):
     B, T, H, K, V = w.B, w.T, w.H, w.K, w.V
     per_tok = (io_bytes(w.io) * 2 * K + io_bytes(w.io) * V + io_bytes(o_dtype) * V
                + 4 + 4 * (K if w.gate == "key" else 1))
+    if rescan:
+        # no o; dO read (io dtype), dq accumulated (fp32, read and written)
+        per_tok += io_bytes(w.io) * V - io_bytes(o_dtype) * V + 8 * K
+        states = True
     state = 4 * K * V * B * H * (2 if w.h0 else 1)
     saved = 0
     if states:
@@ -72,12 +78,12 @@ def forward_flops(w):
     return 2.0 * mac * w.B * w.T * w.H
 
 
-def kernel_name(w, o_dtype, states=False):
+def kernel_name(w, o_dtype, states=False, rescan=False):
     """Template instance of the kernel that gdn_forward (or, with states,
     gdn_forward_states) launches: with bf16 io the pipelined kernel of the
     scalar or the per-key gate, with fp32 io the four-wave one."""
     io = {"bf16": "bf16_t", "fp32": "float"}
-    st = ", true" if states else ""
+    st = ", true, false, true" if rescan else (", true" if states else "")
     if w.io == "bf16":
         name = "forward_pipe_kernel" if w.gate == "head" else "forward_pipe_kda_kernel"
         return "%s<%d, %d, %s%s>" % (name, w.chunk, w.K, io[o_dtype], st)
@@ -158,7 +164,20 @@ def main():
                                    w.gate == "key", tdt)
     ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8) if ws_bytes else None
 
-    if args.states:
+    if args.rescan:
+        nt = (w.T + w.chunk - 1) // w.chunk
+        hck = torch.empty(w.B, nt, w.H, w.K, w.V, device=dev, dtype=tdt)
+        vnew = torch.empty(w.B, w.T, w.H, w.V, device=dev, dtype=tdt)
+        gen = torch.Generator().manual_seed(w.seed + 1000)
+        dout = torch.randn(w.B, w.T, w.H, w.V, generator=gen).to(d["q"].dtype).to(dev)
+        dq = torch.zeros(w.B, w.T, w.H, w.K, device=dev, dtype=torch.float32)
+
+        def step():
+            # (dq accumulates over the steps; the zeroing is the caller's and
+            # not part of the timed re-scan)
+            gdn.rescan_dq(d["q"], d["k"], d["v"], d["beta"], d["g"], dout, w.chunk, d["h0"],
+                          o_dtype=tdt, hT=hT, hck=hck, vnew=vnew, dq=dq)
+    elif args.states:
         nt = (w.T + w.chunk - 1) // w.chunk
         hck = torch.empty(w.B, nt, w.H, w.K, w.V, device=dev, dtype=tdt)
         vnew = torch.empty(w.B, w.T, w.H, w.V, device=dev, dtype=tdt)
@@ -205,13 +224,13 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     ms_launch = sum(a.elapsed_time(b) for a, b in evs) / n_k
-    fbytes, fflops = forward_bytes(w, o_dtype, args.states), forward_flops(w)
+    fbytes, fflops = forward_bytes(w, o_dtype, args.states, args.rescan), forward_flops(w)
     achieved = fbytes / (ms_launch * 1e-3) / 1e9
     mfma_peak = MFMA_PEAK_TFLOPS["f16" if w.io == "bf16" else "f32"]
-    roofline = {"kernel": kernel_name(w, o_dtype, args.states), "bound": "hbm",
+    roofline = {"kernel": kernel_name(w, o_dtype, args.states, args.rescan), "bound": "hbm",
                 "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(w, o_dtype, args.states),
+                "traffic": None if args.rescan else measured_traffic(w, o_dtype, args.states),
                 "ms_per_launch": round(ms_launch, 5),
                 "algorithmic_bytes_per_launch": fbytes,
                 "algorithmic_flops_per_launch": fflops,
@@ -230,7 +249,8 @@ def main():
         "dtype": "f16" if w.io == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "K": w.K, "V": w.V,
                    "chunk": w.chunk, "io": w.io, "o_dtype": o_dtype, "gate": w.gate,
-                   "h0": w.h0, "states": bool(args.states), "parallelism": "single-gpu"},
+                   "h0": w.h0, "states": bool(args.states), "rescan": bool(args.rescan),
+                   "parallelism": "single-gpu"},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -14,6 +14,8 @@ Entry points (same names as the C ABI):
                                                   -> (o, hT, hck, vnew)
     forward_varlen(q, k, v, beta, g, cu_seqlens, chunk, h0=None)
                                                   -> (o, hT [N,H,K,V])
+    rescan_dq(q, k, v, beta, g, do, chunk, h0=None)
+                                                  -> (hT, hck, vnew, dq)
 Layouts: q, k [B,T,H,K]; v [B,T,H,V]; beta [B,T,H]; g [B,T,H] or [B,T,H,K];
 h0/hT [B,H,K,V] fp32.  q, k, v are bf16 or fp32 (same dtype); o is the io
 dtype unless ``o_dtype`` says otherwise.
@@ -24,7 +26,8 @@ import ctypes
 import os
 import threading
 
-__all__ = ["prepare", "scan", "forward", "forward_states", "forward_varlen", "workspace_bytes",
+__all__ = ["prepare", "scan", "forward", "forward_states", "forward_varlen", "rescan_dq",
+           "workspace_bytes",
            "load_library",
            "GdnError", "LIB_PATH", "STATUS"]
 
@@ -39,8 +42,9 @@ STATUS = {
     6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP",
 }
 EXPORTS = ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_forward_states",
-           "gdn_forward_varlen", "gdn_workspace_bytes", "gdn_status_str", "gdn_abi_version"]
-ABI_VERSION = 3
+           "gdn_forward_varlen", "gdn_rescan_dq", "gdn_workspace_bytes", "gdn_status_str",
+           "gdn_abi_version"]
+ABI_VERSION = 4
 
 
 class GdnError(RuntimeError):
@@ -80,8 +84,9 @@ def load_library(path: str | None = None):
         lib.gdn_forward.argtypes = [pp] + [vp] * 9 + [sz, vp]
         lib.gdn_forward_states.argtypes = [pp] + [vp] * 11
         lib.gdn_forward_varlen.argtypes = [pp, vp, ctypes.c_int64] + [vp] * 9
+        lib.gdn_rescan_dq.argtypes = [pp] + [vp] * 12
         for f in (lib.gdn_prepare, lib.gdn_scan, lib.gdn_forward, lib.gdn_forward_states,
-                  lib.gdn_forward_varlen):
+                  lib.gdn_forward_varlen, lib.gdn_rescan_dq):
             f.restype = ctypes.c_int
         lib.gdn_workspace_bytes.argtypes = [pp]
         lib.gdn_workspace_bytes.restype = sz
@@ -340,3 +345,49 @@ def forward_varlen(q, k, v, beta, g, cu_seqlens, chunk, h0=None, *, o_dtype=None
                                 _ptr(o), _ptr(hT), _stream(stream))
     _check("gdn_forward_varlen", rc)
     return o, hT
+
+
+def rescan_dq(q, k, v, beta, g, do, chunk, h0=None, *, o_dtype=None, hT=None, hck=None,
+              vnew=None, dq=None, output_final_state=True, stream=None):
+    """The backward's forward re-scan for the scalar gate with bf16 io:
+    returns (hT or None, hck [B,NT,H,K,V], vnew [B,T,H,V], dq [B,T,H,K] fp32)
+    with dq[t] = h_c do_t (raw, the chunk-start-state term).  A given dq is
+    accumulated into; a new one starts from zero."""
+    torch = _torch()
+    lib = load_library()
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    _gate_kind(g, B, T, H, K)
+    _need(q, "q")
+    _need(k, "k", q.dtype, (B, T, H, K))
+    _need(v, "v", q.dtype, (B, T, H, V))
+    _need(do, "do", q.dtype, (B, T, H, V))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    _need(g, "g", torch.float32, (B, T, H))
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (B, H, K, V))
+    od = o_dtype or q.dtype
+    nt = (T + int(chunk) - 1) // int(chunk) if chunk > 0 else 0
+    if hck is None:
+        hck = torch.empty(B, nt, H, K, V, device=q.device, dtype=od)
+    if vnew is None:
+        vnew = torch.empty(B, T, H, V, device=q.device, dtype=od)
+    if dq is None:
+        dq = torch.zeros(B, T, H, K, device=q.device, dtype=torch.float32)
+    _need(hck, "hck", od, (B, nt, H, K, V))
+    _need(vnew, "vnew", od, (B, T, H, V))
+    _need(dq, "dq", torch.float32, (B, T, H, K))
+    if hT is None and output_final_state:
+        hT = torch.empty(B, H, K, V, device=q.device, dtype=torch.float32)
+    if hT is not None:
+        _need(hT, "hT", torch.float32, (B, H, K, V))
+    pr = _problem(q, v, chunk, False, od)
+    if T == 0:
+        rc = lib.gdn_rescan_dq(ctypes.byref(pr), None, None, None, None, None, _ptr(h0), None,
+                               _ptr(hT), None, None, None, _stream(stream))
+    else:
+        rc = lib.gdn_rescan_dq(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                               _ptr(h0), _ptr(do), _ptr(hT), _ptr(hck), _ptr(vnew), _ptr(dq),
+                               _stream(stream))
+    _check("gdn_rescan_dq", rc)
+    return hT, hck, vnew, dq

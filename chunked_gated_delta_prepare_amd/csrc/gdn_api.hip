@@ -229,6 +229,26 @@ gdn_status gdn_forward_states(const gdn_problem *problem, const void *q, const v
                            (hipStream_t)stream);
 }
 
+gdn_status gdn_rescan_dq(const gdn_problem *problem, const void *q, const void *k,
+                         const void *v, const float *beta, const float *g, const float *h0,
+                         const void *dout, float *hT, void *hck, void *vnew, float *dq,
+                         void *stream) {
+    gdn_status st = check_problem(problem);
+    if (st != GDN_OK) return st;
+    if (problem->gate != GDN_GATE_HEAD || problem->io_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (problem->T == 0) {
+        st = check_ptrs({}, {h0, hT, hck, vnew, dq, dout});
+        if (st != GDN_OK) return st;
+        if (!hT) return GDN_OK;
+        return enqueue_forward(problem, q, k, v, beta, g, h0, nullptr, hT, nullptr, nullptr,
+                               nullptr, 0, (hipStream_t)stream);
+    }
+    st = check_ptrs({q, k, v, beta, g, dout, hck, vnew, dq}, {h0, hT});
+    if (st != GDN_OK) return st;
+    return enqueue_forward(problem, q, k, v, beta, g, h0, nullptr, hT, hck, vnew, nullptr, 0,
+                           (hipStream_t)stream, dout, dq);
+}
+
 gdn_status gdn_forward_varlen(const gdn_problem *problem, const int32_t *cu_seqlens,
                               int64_t n_seqs, const void *q, const void *k, const void *v,
                               const float *beta, const float *g, const float *h0, void *o,

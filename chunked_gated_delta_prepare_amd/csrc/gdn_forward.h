@@ -52,6 +52,10 @@ struct FwdParams {
     // packed sequences: NULL, or B + 1 token offsets (int32) into a
     // [1, T, H, .] layout, sequence b being tokens [cu[b], cu[b+1])
     const int *cu;
+    // backward re-scan: dO [B, T, H, V] (io dtype) in, dq's chunk-start-state
+    // term [B, T, H, K] (fp32, accumulated into) out; both NULL otherwise
+    const void *dout;
+    float *dq;
     int B, T, H, V;
     int nvt;        // V / 64
     int swizzle;

@@ -22,11 +22,13 @@ static bool fits_32bit_streams(const gdn_problem *pr) {
 gdn_status enqueue_forward(const gdn_problem *pr, const void *q, const void *k,
                            const void *v, const float *beta, const float *g,
                            const float *h0, void *o, float *hT, void *hck, void *vnew,
-                           const int32_t *cu, int64_t n_seqs, hipStream_t s) {
+                           const int32_t *cu, int64_t n_seqs, hipStream_t s,
+                           const void *dout, float *dq) {
     if (!fits_32bit_streams(pr)) return GDN_ERR_UNSUPPORTED;
     FwdParams fp;
     fp.q = q; fp.k = k; fp.v = v; fp.beta = beta; fp.g = g; fp.h0 = h0;
     fp.o = o; fp.hT = hT; fp.hck = hck; fp.vnew = vnew; fp.cu = cu;
+    fp.dout = dout; fp.dq = dq;
     // packed sequences: one stream per sequence over the [1, T, H, .] tensors
     const int64_t streams = cu ? n_seqs : pr->B;
     fp.B = (int)streams; fp.T = (int)pr->T; fp.H = (int)pr->H; fp.V = (int)pr->V;

@@ -295,7 +295,10 @@ struct PipeLayout {
     static_assert(kSync % 8 == 0, "the two sync counters are read as one 8-byte word");
 };
 
-template <int C, int K, typename OT, bool ST = false, bool VL = false>
+// DQ: the backward's re-scan (the KDA re-scan page's kernel): the chunk-start
+// states and v' as with ST, plus dq's chunk-start-state term
+// DQ = dO h_c^T (raw) accumulated into p.dq, and no o.
+template <int C, int K, typename OT, bool ST = false, bool VL = false, bool DQ = false>
 __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams p) {
     typedef PipeLayout<C, K> L;
     typedef Mma<_Float16> M;
@@ -305,8 +308,13 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
     static_assert(L::kBytes <= kLdsBytesMax, "LDS budget");
     static_assert(NB == 2 || NB == 4, "chunk 32 or 64");
     static_assert(K == 64 || K == 128, "key dim 64 or 128");
+    static_assert(!DQ || ST, "the re-scan also saves the states");
+    static_assert(L::kBytes + (DQ ? 4 * K * 64 : 0) <= kLdsBytesMax, "LDS budget with the re-scan");
 
     __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
+    // DQ: h_c as bf16 high and low parts, [K][64] (key row, tile column),
+    // 16-byte chunks XOR-swizzled by row (swz<64>)
+    __shared__ __attribute__((aligned(16))) uint16_t hq_lds[DQ ? 2 * K * 64 : 8];
     _Float16 *Qb = (_Float16 *)(smem + L::kQ);
     _Float16 *Kb = (_Float16 *)(smem + L::kK);
     _Float16 *Tmbb = (_Float16 *)(smem + L::kTmb);
@@ -337,6 +345,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
     if (tid == 0) {
         sync_ctr[0] = 0u;                   // prepare waves' barrier
         sync_ctr[1] = 0u;                   // chunks whose row factors are written
+        sync_ctr[2] = 0u;                   // chain waves' barrier (DQ)
     }
     wg_barrier();
 
@@ -355,6 +364,11 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
         const uint32_t prow = (uint32_t)(g4 + 2 * (l & 1));
         const uint32_t vn_off = (prow * rsV + (vcol & ~1)) * SO;
         const uint32_t hck_off = (prow * V + (vcol & ~1)) * SO;
+        // DQ: dO rows as bf16 A fragments, lane (q, i): row i of a 16-token
+        // block, columns 8q .. 8q+7 of a 32-column half of the tile
+        const rsrc_t rdo_ = make_rsrc(DQ ? (const IO *)p.dout + row0 * V : nullptr, DQ ? (uint32_t)T * rsV * SIO : 0u);
+        const uint32_t do_off = ((uint32_t)(l & 15) * rsV + vt * 64 + 8 * (l >> 4)) * SIO;
+        unsigned chain_target = 0;
         float4v hacc[NKB];
         if (p.h0) {
 #pragma unroll
@@ -400,6 +414,62 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                 if (c + 2 < nt) gload(c + 2);
             }
             const float el = eg[2 * C];
+            if constexpr (DQ) {
+                // h_c into LDS as bf16 high and low parts (RNE), then each
+                // wave forms DQ for its K/4 key rows over the tile's 64
+                // value columns: DQ[t][key] = sum_v dO[t][v] h_c[key][v], two
+                // bf16 MFMAs per step (the split keeps h_c to ~16 bits;
+                // bf16 keeps any dO magnitude in range)
+                uint16_t *Hhi = hq_lds, *Hlo = hq_lds + K * 64;
+#pragma unroll
+                for (int i = 0; i < NKB; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = 16 * i + g4 + r, col = 16 * wv + (l & 15);
+                        const uint16_t hb = f32_to_bf16_bits(hacc[i][r]);
+                        Hhi[swz<64>(row, col)] = hb;
+                        Hlo[swz<64>(row, col)] = f32_to_bf16_bits(hacc[i][r] - __uint_as_float((uint32_t)hb << 16));
+                    }
+                prep_barrier(sync_ctr + 2, chain_target);
+                constexpr int NKW = K / 64;                  // 16-row key tiles per wave
+                float4v dq[NB][NKW];
+#pragma unroll
+                for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+                    for (int nt = 0; nt < NKW; ++nt) dq[cb][nt] = float4v{0, 0, 0, 0};
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    bf16x8 bh[NKW], bl[NKW];
+#pragma unroll
+                    for (int nt = 0; nt < NKW; ++nt) {
+                        const int row = (K / 4) * wv + 16 * nt + (l & 15), c0 = 32 * s + 8 * (l >> 4);
+                        bh[nt] = *(const bf16x8 *)(Hhi + swz<64>(row, c0));
+                        bl[nt] = *(const bf16x8 *)(Hlo + swz<64>(row, c0));
+                    }
+#pragma unroll
+                    for (int cb = 0; cb < NB; ++cb) {
+                        const bf16x8 a = __builtin_bit_cast(bf16x8, bload128(rdo_, do_off + 32 * s * SIO, (t0 + 16 * cb) * rsV * SIO));
+#pragma unroll
+                        for (int nt = 0; nt < NKW; ++nt) {
+                            dq[cb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[nt], dq[cb][nt], 0, 0, 0);
+                            dq[cb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[nt], dq[cb][nt], 0, 0, 0);
+                        }
+                    }
+                }
+                // accumulate into dq (the V tiles of a head add up there)
+#pragma unroll
+                for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = (int)t0 + 16 * cb + g4 + r;
+                        if (t < T) {
+#pragma unroll
+                            for (int nt = 0; nt < NKW; ++nt)
+                                unsafeAtomicAdd(p.dq + (row0 + (int64_t)t * H) * K + (K / 4) * wv + 16 * nt + (l & 15),
+                                                dq[cb][nt][r]);
+                        }
+                    }
+            }
 
             float4v eg4[NB], egl4[NB];
 #pragma unroll
@@ -458,13 +528,15 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
             half8 df[C / 32];
 #pragma unroll
             for (int s = 0; s < C / 32; ++s) df[s] = fragB_acc(da[2 * s], da[2 * s + 1], _Float16{});
+            if constexpr (!DQ) {
 #pragma unroll
-            for (int cb = 0; cb < NB; ++cb) {
-                float4v oa = eg[16 * cb + (l & 15)] * ya[cb];
+                for (int cb = 0; cb < NB; ++cb) {
+                    float4v oa = eg[16 * cb + (l & 15)] * ya[cb];
 #pragma unroll
-                for (int s = 0; s < C / 32; ++s)
-                    if (32 * s < 16 * (cb + 1)) M::mma(oa, df[s], frag_sw<C>(Ps, 16 * cb, 32 * s));
-                store4<OT>(oa, ro_, o_off, (t0 + 16 * cb) * rsV * SO);
+                    for (int s = 0; s < C / 32; ++s)
+                        if (32 * s < 16 * (cb + 1)) M::mma(oa, df[s], frag_sw<C>(Ps, 16 * cb, 32 * s));
+                    store4<OT>(oa, ro_, o_off, (t0 + 16 * cb) * rsV * SO);
+                }
             }
             if constexpr (ST) {
                 // v' of this chunk's tokens (dropped past token T by the range)

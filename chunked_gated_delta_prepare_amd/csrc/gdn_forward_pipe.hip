@@ -19,6 +19,7 @@ gdn_status pipe_o(bool o_f32, FwdParams &fp, int grid, hipStream_t s) {
 
 gdn_status enqueue_forward_pipe(int C, int K, bool o_f32, FwdParams &fp, int grid,
                                 hipStream_t s) {
+    if (fp.dq) return enqueue_forward_pipe_dq(C, K, o_f32, fp, grid, s);
     if (fp.cu) return C == 32 ? enqueue_forward_pipe_varlen_c32(K, o_f32, fp, grid, s)
                               : enqueue_forward_pipe_varlen_c64(K, o_f32, fp, grid, s);
     const bool st = fp.hck != nullptr;

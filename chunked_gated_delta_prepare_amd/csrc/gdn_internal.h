@@ -19,7 +19,8 @@ gdn_status launch_kernel(const void *fn, int grid, void *params, hipStream_t s,
 gdn_status enqueue_forward(const gdn_problem *pr, const void *q, const void *k,
                            const void *v, const float *beta, const float *g,
                            const float *h0, void *o, float *hT, void *hck, void *vnew,
-                           const int32_t *cu, int64_t n_seqs, hipStream_t s);
+                           const int32_t *cu, int64_t n_seqs, hipStream_t s,
+                           const void *dout = nullptr, float *dq = nullptr);
 
 struct FwdParams;
 // Dispatch a forward problem whose FwdParams carry hck and vnew.
@@ -42,6 +43,9 @@ gdn_status enqueue_forward_pipe_c32k128(bool o_f32, FwdParams &fp, int grid, hip
 // The pipelined kernel for the per-key gate (plain, ST or VL by fp.hck / fp.cu).
 gdn_status enqueue_forward_pipe_kda(int C, int K, bool o_f32, FwdParams &fp, int grid,
                                     hipStream_t s);
+// The scalar-gate pipelined kernel as the backward's re-scan (fp.dq set).
+gdn_status enqueue_forward_pipe_dq(int C, int K, bool o_f32, FwdParams &fp, int grid,
+                                   hipStream_t s);
 // Chunk 32, saving the chunk-start states and the per-token deltas.
 gdn_status enqueue_forward_pipe_c32_states(int K, bool o_f32, FwdParams &fp, int grid,
                                            hipStream_t s);

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -161,6 +161,27 @@ gdn_status gdn_forward_states(const gdn_problem *problem, const void *q, const v
                               const void *v, const float *beta, const float *g,
                               const float *h0, void *o, float *hT, void *hck, void *vnew,
                               void *stream);
+
+/*
+ * gdn_rescan_dq -- the backward pass's forward re-scan (kernel_fun KDA re-scan
+ * page, bwd_scan.py: its CuTe kernel re-runs the state recurrence to save
+ * the h checkpoints and v_new and, fused in, forms dq's only dependence on
+ * the state, DQ = dO h_c^T, raw: no gate and no scale).  Here for the scalar
+ * gate (Gated DeltaNet) with bf16 io:
+ *   hck, vnew  as in gdn_forward_states (problem->o_dtype);
+ *   dq [B,T,H,K] fp32: dq[t] += h_c dO_t for token t of chunk c, h_c the
+ *              state at the chunk's start (K x V), dO [B,T,H,V] in the io
+ *              dtype.  dq is accumulated into (the V tiles of a head add up
+ *              there, in an order that does not change the sum for V <= 128),
+ *              so the caller zeroes it first.
+ * No o is produced (q is still read).  hT, h0 as in gdn_forward.  Other
+ * gates or dtypes return GDN_ERR_UNSUPPORTED.  With T = 0 only hT is
+ * written.  Pointers as in gdn_forward_states; dq must not alias any input.
+ */
+gdn_status gdn_rescan_dq(const gdn_problem *problem, const void *q, const void *k,
+                         const void *v, const float *beta, const float *g, const float *h0,
+                         const void *dout, float *hT, void *hck, void *vnew, float *dq,
+                         void *stream);
 
 /*
  * gdn_forward_varlen -- gdn_forward over packed sequences of different

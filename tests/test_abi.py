@@ -36,7 +36,8 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     assert _declared_functions() == sorted(
         ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_forward_states",
-         "gdn_forward_varlen", "gdn_workspace_bytes", "gdn_status_str", "gdn_abi_version"])
+         "gdn_forward_varlen", "gdn_rescan_dq", "gdn_workspace_bytes", "gdn_status_str",
+         "gdn_abi_version"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -187,3 +188,19 @@ def test_streams_beyond_32bit_offsets_rejected(lib, gdn):
     # one token fewer fits
     ok = _problem(gdn, B=1, T=(1 << 20) - 1, H=16, K=128, V=128)
     assert lib.gdn_workspace_bytes(ctypes.byref(ok)) == 0
+
+
+def _rescan(lib, pr, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, h0=None, do=FAKE, hT=None,
+            hck=FAKE, vnew=FAKE, dq=FAKE):
+    return lib.gdn_rescan_dq(ctypes.byref(pr), q, k, v, beta, g, h0, do, hT, hck, vnew, dq, None)
+
+
+def test_rescan_dq_validates_before_launch(lib, gdn):
+    pr = _problem(gdn)
+    for name in ("q", "k", "v", "beta", "g", "do", "hck", "vnew", "dq"):
+        assert _rescan(lib, pr, **{name: None}) == 1, name
+    assert _rescan(lib, pr, dq=MISALIGNED) == 4
+    assert _rescan(lib, _problem(gdn, gate=1)) == 3           # scalar gate only
+    assert _rescan(lib, _problem(gdn, io=0, o=0)) == 3        # bf16 io only
+    assert _rescan(lib, _problem(gdn, T=0), q=None, k=None, v=None, beta=None, g=None, do=None,
+                   hck=None, vnew=None, dq=None) == 0
