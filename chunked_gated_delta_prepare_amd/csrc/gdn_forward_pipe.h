@@ -421,6 +421,15 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                 // bf16 MFMAs per step (the split keeps h_c to ~16 bits;
                 // bf16 keeps any dO magnitude in range)
                 uint16_t *Hhi = hq_lds, *Hlo = hq_lds + K * 64;
+                // this chunk's dO fragments first: their latency then runs
+                // under the LDS writes and the barrier below
+                bf16x8 dof[2][NB];
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int cb = 0; cb < NB; ++cb)
+                        dof[s][cb] = __builtin_bit_cast(bf16x8, bload128(rdo_, do_off + 32 * s * SIO,
+                                                                         (t0 + 16 * cb) * rsV * SIO));
 #pragma unroll
                 for (int i = 0; i < NKB; ++i)
 #pragma unroll
@@ -448,11 +457,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                     }
 #pragma unroll
                     for (int cb = 0; cb < NB; ++cb) {
-                        const bf16x8 a = __builtin_bit_cast(bf16x8, bload128(rdo_, do_off + 32 * s * SIO, (t0 + 16 * cb) * rsV * SIO));
 #pragma unroll
                         for (int nt = 0; nt < NKW; ++nt) {
-                            dq[cb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[nt], dq[cb][nt], 0, 0, 0);
-                            dq[cb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[nt], dq[cb][nt], 0, 0, 0);
+                            dq[cb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dof[s][cb], bh[nt], dq[cb][nt], 0, 0, 0);
+                            dq[cb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dof[s][cb], bl[nt], dq[cb][nt], 0, 0, 0);
                         }
                     }
                 }

@@ -1,6 +1,6 @@
 // libgdn: the scalar-gate pipelined kernel as the backward's re-scan (the
 // DQ instances: chunk-start states, v' and dq's chunk-start-state term),
-// built with the default machine scheduler.
+// built with the ILP machine scheduler.
 #include "gdn_forward_pipe.h"
 #include "gdn_internal.h"
 
