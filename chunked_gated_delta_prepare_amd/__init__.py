@@ -349,21 +349,22 @@ def forward_varlen(q, k, v, beta, g, cu_seqlens, chunk, h0=None, *, o_dtype=None
 
 def rescan_dq(q, k, v, beta, g, do, chunk, h0=None, *, o_dtype=None, hT=None, hck=None,
               vnew=None, dq=None, output_final_state=True, stream=None):
-    """The backward's forward re-scan for the scalar gate with bf16 io:
-    returns (hT or None, hck [B,NT,H,K,V], vnew [B,T,H,V], dq [B,T,H,K] fp32)
-    with dq[t] = h_c do_t (raw, the chunk-start-state term).  A given dq is
-    accumulated into; a new one starts from zero."""
+    """The backward's forward re-scan with bf16 io: returns (hT or None,
+    hck [B,NT,H,K,V], vnew [B,T,H,V], dq [B,T,H,K] fp32) with
+    dq[t] = h_c do_t (raw, the chunk-start-state term).  g is [B,T,H] (one
+    gate per head) or [B,T,H,K] (one per key dimension, chunk 64 only).  A
+    given dq is accumulated into; a new one starts from zero."""
     torch = _torch()
     lib = load_library()
     B, T, H, K = q.shape
     V = v.shape[-1]
-    _gate_kind(g, B, T, H, K)
+    per_key = _gate_kind(g, B, T, H, K)
     _need(q, "q")
     _need(k, "k", q.dtype, (B, T, H, K))
     _need(v, "v", q.dtype, (B, T, H, V))
     _need(do, "do", q.dtype, (B, T, H, V))
     _need(beta, "beta", torch.float32, (B, T, H))
-    _need(g, "g", torch.float32, (B, T, H))
+    _need(g, "g", torch.float32)
     if h0 is not None:
         _need(h0, "h0", torch.float32, (B, H, K, V))
     od = o_dtype or q.dtype
@@ -381,7 +382,7 @@ def rescan_dq(q, k, v, beta, g, do, chunk, h0=None, *, o_dtype=None, hT=None, hc
         hT = torch.empty(B, H, K, V, device=q.device, dtype=torch.float32)
     if hT is not None:
         _need(hT, "hT", torch.float32, (B, H, K, V))
-    pr = _problem(q, v, chunk, False, od)
+    pr = _problem(q, v, chunk, per_key, od)
     if T == 0:
         rc = lib.gdn_rescan_dq(ctypes.byref(pr), None, None, None, None, None, _ptr(h0), None,
                                _ptr(hT), None, None, None, _stream(stream))

@@ -37,6 +37,7 @@ gdn_status forward_gate(const gdn_problem *pr, FwdParams &fp, int grid, hipStrea
             return key ? enqueue_forward_pipe_kda(C, K, sizeof(OT) == 4, fp, grid, s)
                        : enqueue_forward_pipe(C, K, sizeof(OT) == 4, fp, grid, s);
     }
+    if (fp.dq) return GDN_ERR_UNSUPPORTED;   // the re-scan with dq is a pipelined kernel only
     return key ? run_forward<C, K, IO, OT, true, ST, VL>(fp, grid, s)
                : run_forward<C, K, IO, OT, false, ST, VL>(fp, grid, s);
 }

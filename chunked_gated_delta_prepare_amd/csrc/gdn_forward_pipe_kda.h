@@ -56,7 +56,12 @@ __device__ __forceinline__ u32x2 bload64(rsrc_t r, uint32_t voff, uint32_t soff)
     return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
 }
 
-template <int C, int K, typename OT, bool ST = false, bool VL = false>
+// DQ: the backward's re-scan (the KDA re-scan page's kernel): the chunk-start
+// states and v' as with ST, plus dq's chunk-start-state term
+// DQ = dO h_c^T (raw) accumulated into p.dq, and no o.  Chunk 64 only: the
+// state is staged in the q~ and k~ tiles of the slot the chain has just
+// finished with, which hold K x 64 bf16 at C = 64.
+template <int C, int K, typename OT, bool ST = false, bool VL = false, bool DQ = false>
 __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdParams p) {
     typedef PipeKdaLayout<C, K> L;
     typedef Mma<_Float16> M;
@@ -67,6 +72,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
     static_assert(L::kBytes <= kLdsBytesMax, "LDS budget");
     static_assert(NB == 2 || NB == 4, "chunk 32 or 64");
     static_assert(K == 64 || K == 128, "key dim 64 or 128");
+    static_assert(!DQ || (ST && C * K * 2 >= K * 64 * 2), "the re-scan saves states; chunk 64");
 
     __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
     _Float16 *Qb = (_Float16 *)(smem + L::kQ);
@@ -100,6 +106,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
     if (tid == 0) {
         sync_ctr[0] = 0u;                   // prepare waves' barrier
         sync_ctr[1] = 0u;
+        sync_ctr[2] = 0u;                   // chain waves' barrier (DQ)
     }
     wg_barrier();
 
@@ -126,6 +133,75 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
 #pragma unroll
             for (int i = 0; i < NKB; ++i) hacc[i] = float4v{0, 0, 0, 0};
         }
+        // DQ: dq[t] += h_c dO_t for the tokens of chunk n, with h_c in hacc:
+        // the state goes to LDS as bf16 high and low parts ([K][64], 16-byte
+        // chunks swizzled by row) in the q~ and k~ tiles of slot sl, free
+        // then; each wave forms DQ for K/4 key rows over the tile's 64 value
+        // columns with bf16 MFMAs (bf16 keeps any dO magnitude in range)
+        const rsrc_t rdo_ = make_rsrc(DQ ? (const IO *)p.dout + row0 * V : nullptr, DQ ? (uint32_t)T * rsV * SIO : 0u);
+        const uint32_t do_off = ((uint32_t)(l & 15) * rsV + vt * 64 + 8 * (l >> 4)) * SIO;
+        unsigned chain_target = 0;
+        auto rescan_dq = [&](int n, int sl) {
+            const uint32_t t0 = (uint32_t)(n * C);
+            uint16_t *Hhi = (uint16_t *)(Qb + sl * C * K), *Hlo = (uint16_t *)(Kb + sl * C * K);
+            bf16x8 dof[2][NB];
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int cb = 0; cb < NB; ++cb)
+                    dof[s][cb] = __builtin_bit_cast(bf16x8, bload128(rdo_, do_off + 32 * s * SIO,
+                                                                     (t0 + 16 * cb) * rsV * SIO));
+            prep_barrier(sync_ctr + 2, chain_target);        // every chain wave is past its reads
+#pragma unroll
+            for (int i = 0; i < NKB; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * i + g4 + r, col = 16 * wv + (l & 15);
+                    const uint16_t hb = f32_to_bf16_bits(hacc[i][r]);
+                    Hhi[swz<64>(row, col)] = hb;
+                    Hlo[swz<64>(row, col)] = f32_to_bf16_bits(hacc[i][r] - __uint_as_float((uint32_t)hb << 16));
+                }
+            prep_barrier(sync_ctr + 2, chain_target);
+            constexpr int NKW = K / 64;                      // 16-row key tiles per wave
+            float4v dq[NB][NKW];
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+                for (int nt = 0; nt < NKW; ++nt) dq[cb][nt] = float4v{0, 0, 0, 0};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                bf16x8 bh[NKW], bl[NKW];
+#pragma unroll
+                for (int nt = 0; nt < NKW; ++nt) {
+                    const int row = (K / 4) * wv + 16 * nt + (l & 15), c0 = 32 * s + 8 * (l >> 4);
+                    bh[nt] = *(const bf16x8 *)(Hhi + swz<64>(row, c0));
+                    bl[nt] = *(const bf16x8 *)(Hlo + swz<64>(row, c0));
+                }
+#pragma unroll
+                for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+                    for (int nt = 0; nt < NKW; ++nt) {
+                        dq[cb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dof[s][cb], bh[nt], dq[cb][nt], 0, 0, 0);
+                        dq[cb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dof[s][cb], bl[nt], dq[cb][nt], 0, 0, 0);
+                    }
+            }
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = (int)t0 + 16 * cb + g4 + r;
+                    if (t < T) {
+#pragma unroll
+                        for (int nt = 0; nt < NKW; ++nt)
+                            unsafeAtomicAdd(p.dq + (row0 + (int64_t)t * H) * K + (K / 4) * wv + 16 * nt + (l & 15),
+                                            dq[cb][nt][r]);
+                    }
+                }
+        };
+        // chunk 0's dq term from h0, staged in slot 1 (not written before the
+        // prepare of chunk 1, which starts after the next barrier)
+        if constexpr (DQ)
+            if (nt > 0) rescan_dq(0, 1);
         wg_barrier();                       // chunk 0 prepared
 
         for (int c = 0; c < nt; ++c) {
@@ -183,13 +259,15 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
             half8 df[C / 32];
 #pragma unroll
             for (int s = 0; s < C / 32; ++s) df[s] = fragB_acc(da[2 * s], da[2 * s + 1], _Float16{});
+            if constexpr (!DQ) {
 #pragma unroll
-            for (int cb = 0; cb < NB; ++cb) {
-                float4v oa = ya[cb];
+                for (int cb = 0; cb < NB; ++cb) {
+                    float4v oa = ya[cb];
 #pragma unroll
-                for (int s = 0; s < C / 32; ++s)
-                    if (32 * s < 16 * (cb + 1)) M::mma(oa, df[s], frag_sw<C>(Ps, 16 * cb, 32 * s));
-                store4<OT>(oa, ro_, o_off, (t0 + 16 * cb) * rsV * SO);
+                    for (int s = 0; s < C / 32; ++s)
+                        if (32 * s < 16 * (cb + 1)) M::mma(oa, df[s], frag_sw<C>(Ps, 16 * cb, 32 * s));
+                    store4<OT>(oa, ro_, o_off, (t0 + 16 * cb) * rsV * SO);
+                }
             }
             if constexpr (ST) {
 #pragma unroll
@@ -211,6 +289,11 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
                 hacc[i] = *(const float4v *)(flv + 16 * i + g4) * hacc[i] +
                           *(const float4v *)(fmv + 16 * i + g4) * acc;
             }
+            // the next chunk's dq term from its start state (now in hacc),
+            // staged in this chunk's q~ and k~ tiles: the chain is done with
+            // them, and the prepare writes this slot only after the barrier
+            if constexpr (DQ)
+                if (c + 1 < nt) rescan_dq(c + 1, slot);
             wg_barrier();
         }
         if (p.hT) {

@@ -1,20 +1,23 @@
 // libgdn: dispatch of the pipelined forward kernel for the per-key gate
-// (gdn_forward_pipe_kda.h), plain, saving states (ST) or over packed
-// sequences (VL).
+// (gdn_forward_pipe_kda.h), plain, saving states (ST), over packed
+// sequences (VL) or as the backward's re-scan (DQ, chunk 64).
 #include "gdn_forward_pipe_kda.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
 namespace {
-template <int C, int K, bool ST, bool VL>
+template <int C, int K, bool ST, bool VL, bool DQ = false>
 const void *kda_fn(bool o_f32) {
-    return o_f32 ? (const void *)&forward_pipe_kda_kernel<C, K, float, ST, VL>
-                 : (const void *)&forward_pipe_kda_kernel<C, K, bf16_t, ST, VL>;
+    return o_f32 ? (const void *)&forward_pipe_kda_kernel<C, K, float, ST, VL, DQ>
+                 : (const void *)&forward_pipe_kda_kernel<C, K, bf16_t, ST, VL, DQ>;
 }
 
 template <int C, int K>
 const void *kda_mode(bool o_f32, const FwdParams &fp) {
+    if constexpr (C == 64) {
+        if (fp.dq) return kda_fn<C, K, true, false, true>(o_f32);
+    }
     if (fp.hck) return kda_fn<C, K, true, false>(o_f32);
     if (fp.cu) return kda_fn<C, K, false, true>(o_f32);
     return kda_fn<C, K, false, false>(o_f32);

@@ -1,5 +1,5 @@
 """GPU parity of gdn_rescan_dq (the backward's forward re-scan, through the C
-ABI) against the fp64 oracle.
+ABI) against the fp64 oracle, for the scalar gate and the per-key gate.
 
 dq's chunk-start-state term dq[t] = h_c dO_t, the chunk-start states and v'
 are held to the forward's bar: max |x - x_ref| / rms(x_ref) <= 2e-2 with bf16
@@ -33,11 +33,11 @@ def _dout(B, T, H, V, seed):
     return torch.randn(B, T, H, V, generator=gen).to(torch.bfloat16).contiguous()
 
 
-def run_rescan(case, B, T, H, K, V, C, h0, seed, heads=None):
-    inp = make_inputs(B, T, H, K, V, io="bf16", gate="head", gate_bias=2.0, h0=h0, seed=seed)
+def run_rescan(case, B, T, H, K, V, C, h0, seed, heads=None, gate="head", bias=2.0):
+    inp = make_inputs(B, T, H, K, V, io="bf16", gate=gate, gate_bias=bias, h0=h0, seed=seed)
     do = _dout(B, T, H, V, seed + 1)
     d = {n: (None if t is None else t.to(_dev())) for n, t in inp.items()}
-    print("case", case, [B, T, H, K, V, C], flush=True)
+    print("case", case, [B, T, H, K, V, C], gate, flush=True)
     hT, hck, vnew, dq = gdn.rescan_dq(d["q"], d["k"], d["v"], d["beta"], d["g"], do.to(_dev()),
                                       C, d["h0"], o_dtype=torch.float32)
     torch.cuda.synchronize()
@@ -64,23 +64,31 @@ def run_rescan(case, B, T, H, K, V, C, h0, seed, heads=None):
 
 
 CASES = [
-    # B, T, H, K, V, chunk, h0
-    (2, 333, 2, 128, 128, 64, True),
-    (1, 200, 3, 64, 64, 32, False),
-    (1, 130, 2, 128, 64, 64, True),       # one V tile
-    (1, 97, 2, 64, 128, 32, True),        # dk != dv
-    (1, 1, 1, 128, 128, 64, True),        # a single token
+    # B, T, H, K, V, chunk, h0, gate
+    (2, 333, 2, 128, 128, 64, True, "head"),
+    (1, 200, 3, 64, 64, 32, False, "head"),
+    (1, 130, 2, 128, 64, 64, True, "head"),       # one V tile
+    (1, 97, 2, 64, 128, 32, True, "head"),        # dk != dv
+    (1, 1, 1, 128, 128, 64, True, "head"),        # a single token
+    (2, 300, 2, 128, 128, 64, True, "key"),
+    (1, 200, 3, 64, 64, 64, False, "key"),
+    (1, 130, 2, 128, 64, 64, True, "key"),        # one V tile, ragged tail
+    (1, 97, 2, 64, 128, 64, True, "key"),         # dk != dv
+    (1, 1, 1, 128, 128, 64, True, "key"),         # a single token
 ]
 
 
-@pytest.mark.parametrize("cfg", CASES, ids=lambda c: "B%dT%dH%dK%dV%dC%d" % c[:6])
+@pytest.mark.parametrize("cfg", CASES, ids=lambda c: "B%dT%dH%dK%dV%dC%d_%s" % (c[:6] + c[7:]))
 def test_rescan_dq_small(cfg):
-    B, T, H, K, V, C, h0 = cfg
-    run_rescan("rescan_small", B, T, H, K, V, C, h0, seed=T + K + 3)
+    B, T, H, K, V, C, h0, gate = cfg
+    run_rescan("rescan_small", B, T, H, K, V, C, h0, seed=T + K + 3, gate=gate,
+               bias=3.0 if gate == "key" else 2.0)
 
 
-def test_rescan_dq_accumulates_and_is_deterministic():
-    d, do, dq = run_rescan("rescan_acc", 1, 256, 2, 128, 128, 64, True, seed=77)
+@pytest.mark.parametrize("gate", ["head", "key"])
+def test_rescan_dq_accumulates_and_is_deterministic(gate):
+    d, do, dq = run_rescan("rescan_acc", 1, 256, 2, 128, 128, 64, True, seed=77, gate=gate,
+                           bias=3.0)
     do = do.to(_dev())
     base = torch.full_like(dq, 0.25)
     _, _, _, dq2 = gdn.rescan_dq(d["q"], d["k"], d["v"], d["beta"], d["g"], do, 64, d["h0"],
@@ -93,8 +101,19 @@ def test_rescan_dq_accumulates_and_is_deterministic():
     assert torch.allclose(dq2 - 0.25, dq, rtol=0, atol=1e-5)
 
 
-def test_rescan_dq_full_size_sampled():
-    w = WORKLOADS["gdn_t4k"]
+@pytest.mark.parametrize("name", ["gdn_t4k", "kda_t8k"])
+def test_rescan_dq_full_size_sampled(name):
+    w = WORKLOADS[name]
     pairs = w.B * w.H
-    run_rescan("rescan_full_gdn_t4k", w.B, w.T, w.H, w.K, w.V, w.chunk, w.h0, w.seed,
-               heads=[0, (7 * pairs) // 11, pairs - 1])
+    run_rescan("rescan_full_" + name, w.B, w.T, w.H, w.K, w.V, w.chunk, w.h0, w.seed,
+               heads=[0, (7 * pairs) // 11, pairs - 1], gate=w.gate, bias=w.gate_bias)
+
+
+def test_rescan_dq_key_gate_needs_chunk_64():
+    d = _dev()
+    q = torch.zeros(1, 64, 1, 64, device=d, dtype=torch.bfloat16)
+    beta = torch.zeros(1, 64, 1, device=d)
+    g = torch.zeros(1, 64, 1, 64, device=d)
+    with pytest.raises(gdn.GdnError) as e:
+        gdn.rescan_dq(q, q, q, beta, g, q, 32)
+    assert e.value.status == 3                       # GDN_ERR_UNSUPPORTED
