@@ -204,3 +204,13 @@ def test_rescan_dq_validates_before_launch(lib, gdn):
     assert _rescan(lib, _problem(gdn, io=0, o=0)) == 3        # bf16 io only
     assert _rescan(lib, _problem(gdn, T=0), q=None, k=None, v=None, beta=None, g=None, do=None,
                    hck=None, vnew=None, dq=None) == 0
+
+
+def test_rescan_dq_is_not_routed_to_the_four_wave_kernel(lib, gdn, monkeypatch):
+    # with the pipelined kernels switched off for bf16 io, the re-scan has no
+    # kernel: it returns GDN_ERR_UNSUPPORTED before any launch instead of
+    # running a forward that leaves dq untouched
+    monkeypatch.setenv("GDN_FORWARD_FOUR_WAVE", "1")
+    assert _rescan(lib, _problem(gdn)) == 3
+    assert _rescan(lib, _problem(gdn, gate=1)) == 3
+

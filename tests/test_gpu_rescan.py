@@ -101,7 +101,7 @@ def test_rescan_dq_accumulates_and_is_deterministic(gate):
     assert torch.allclose(dq2 - 0.25, dq, rtol=0, atol=1e-5)
 
 
-@pytest.mark.parametrize("name", ["gdn_t4k", "kda_t8k"])
+@pytest.mark.parametrize("name", ["gdn_t4k", "gdn_c32_d64", "kda_t8k"])
 def test_rescan_dq_full_size_sampled(name):
     w = WORKLOADS[name]
     pairs = w.B * w.H
