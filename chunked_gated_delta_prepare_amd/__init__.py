@@ -42,9 +42,9 @@ STATUS = {
     6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP",
 }
 EXPORTS = ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_forward_states",
-           "gdn_forward_varlen", "gdn_rescan_dq", "gdn_workspace_bytes", "gdn_status_str",
-           "gdn_abi_version"]
-ABI_VERSION = 4
+           "gdn_forward_varlen", "gdn_rescan_dq", "gdn_chunk_dq", "gdn_workspace_bytes",
+           "gdn_status_str", "gdn_abi_version"]
+ABI_VERSION = 5
 
 
 class GdnError(RuntimeError):
@@ -85,8 +85,9 @@ def load_library(path: str | None = None):
         lib.gdn_forward_states.argtypes = [pp] + [vp] * 11
         lib.gdn_forward_varlen.argtypes = [pp, vp, ctypes.c_int64] + [vp] * 9
         lib.gdn_rescan_dq.argtypes = [pp] + [vp] * 12
+        lib.gdn_chunk_dq.argtypes = [pp] + [vp] * 4
         for f in (lib.gdn_prepare, lib.gdn_scan, lib.gdn_forward, lib.gdn_forward_states,
-                  lib.gdn_forward_varlen, lib.gdn_rescan_dq):
+                  lib.gdn_forward_varlen, lib.gdn_rescan_dq, lib.gdn_chunk_dq):
             f.restype = ctypes.c_int
         lib.gdn_workspace_bytes.argtypes = [pp]
         lib.gdn_workspace_bytes.restype = sz
@@ -345,6 +346,31 @@ def forward_varlen(q, k, v, beta, g, cu_seqlens, chunk, h0=None, *, o_dtype=None
                                 _ptr(o), _ptr(hT), _stream(stream))
     _check("gdn_forward_varlen", rc)
     return o, hT
+
+
+def chunk_dq(do, hck, chunk, *, dq=None, stream=None):
+    """dq's chunk-start-state term from saved states: dq[t] = h_c do_t (raw)
+    for token t of chunk c, with do [B,T,H,V] bf16 and hck [B,NT,H,K,V] bf16
+    or fp32 as forward_states returns it.  Returns dq [B,T,H,K] fp32,
+    written (a given dq is overwritten, not accumulated into)."""
+    torch = _torch()
+    lib = load_library()
+    B, T, H, V = do.shape
+    K = hck.shape[3]
+    nt = (T + int(chunk) - 1) // int(chunk) if chunk > 0 else 0
+    _need(do, "do", torch.bfloat16)
+    _need(hck, "hck", None, (B, nt, H, K, V))
+    if hck.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("hck must be bfloat16 or float32, got %s" % hck.dtype)
+    if dq is None:
+        dq = torch.empty(B, T, H, K, device=do.device, dtype=torch.float32)
+    _need(dq, "dq", torch.float32, (B, T, H, K))
+    pr = Problem(B, T, H, K, V, int(chunk), _dtype_code(do.dtype), _dtype_code(hck.dtype),
+                 GDN_GATE_HEAD)
+    rc = lib.gdn_chunk_dq(ctypes.byref(pr), _ptr(do) if T else None, _ptr(hck) if T else None,
+                          _ptr(dq) if T else None, _stream(stream))
+    _check("gdn_chunk_dq", rc)
+    return dq
 
 
 def rescan_dq(q, k, v, beta, g, do, chunk, h0=None, *, o_dtype=None, hT=None, hck=None,

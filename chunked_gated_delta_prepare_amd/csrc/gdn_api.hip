@@ -250,6 +250,20 @@ gdn_status gdn_rescan_dq(const gdn_problem *problem, const void *q, const void *
                            (hipStream_t)stream, dout, dq);
 }
 
+gdn_status gdn_chunk_dq(const gdn_problem *problem, const void *dout, const void *hck, float *dq,
+                        void *stream) {
+    gdn_status st = check_problem(problem);
+    if (st != GDN_OK) return st;
+    if (problem->io_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (problem->T == 0) return GDN_OK;
+    st = check_ptrs({dout, hck, dq}, {});
+    if (st != GDN_OK) return st;
+    // one chunk's token rows of dO and dq are addressed with 32-bit offsets
+    const int64_t row_bytes = problem->H * std::max(2 * problem->V, 4 * problem->K);
+    if ((int64_t)problem->chunk * row_bytes >= ((int64_t)1 << 32)) return GDN_ERR_UNSUPPORTED;
+    return enqueue_chunk_dq(problem, dout, hck, dq, (hipStream_t)stream);
+}
+
 gdn_status gdn_forward_varlen(const gdn_problem *problem, const int32_t *cu_seqlens,
                               int64_t n_seqs, const void *q, const void *k, const void *v,
                               const float *beta, const float *g, const float *h0, void *o,

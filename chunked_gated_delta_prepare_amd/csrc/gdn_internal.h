@@ -16,6 +16,10 @@ gdn_status launch_kernel(const void *fn, int grid, void *params, hipStream_t s,
 // hck and vnew are both NULL, or both set for the instance that also saves
 // the chunk-start states and the per-token deltas.  cu (n_seqs + 1 device
 // int32 offsets) selects packed sequences over a B = 1 problem, or is NULL.
+// Enqueue dq = dO h_c^T per chunk from saved states (validated problem, T > 0).
+gdn_status enqueue_chunk_dq(const gdn_problem *pr, const void *dout, const void *hck, float *dq,
+                            hipStream_t s);
+
 gdn_status enqueue_forward(const gdn_problem *pr, const void *q, const void *k,
                            const void *v, const float *beta, const float *g,
                            const float *h0, void *o, float *hT, void *hck, void *vnew,

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -184,6 +184,27 @@ gdn_status gdn_rescan_dq(const gdn_problem *problem, const void *q, const void *
                          const void *v, const float *beta, const float *g, const float *h0,
                          const void *dout, float *hT, void *hck, void *vnew, float *dq,
                          void *stream);
+
+/*
+ * gdn_chunk_dq -- dq's chunk-start-state term on its own, from states that
+ * gdn_forward_states saved: the DQ = dO h^T product that the kernel_fun KDA
+ * re-scan page fuses into its re-scan, whose own measurements found the
+ * fused form slower (its section on the dq fusion); gdn_rescan_dq is the
+ * fused form here.
+ *   dout [B,T,H,V] in the io dtype (bf16 only);
+ *   hck  [B,NT,H,K,V] in problem->o_dtype (bf16 or fp32), NT = ceil(T/chunk),
+ *        as gdn_forward_states writes it;
+ *   dq   [B,T,H,K] fp32, written (not accumulated): dq[t] = h_c dO_t for
+ *        token t of chunk c, raw (no gate, no scale; the same for either
+ *        gate).  fp32 states enter the product as bf16 high and low parts
+ *        (~16 bits), bf16 states exactly; fp32 accumulation.
+ * problem->gate is not used.  fp32 io returns GDN_ERR_UNSUPPORTED.  With
+ * T = 0 nothing is done and the pointers may be NULL; otherwise all three
+ * are required and 16-byte aligned, and dq must not alias the others.
+ * Needs no workspace; one kernel launch, deterministic.
+ */
+gdn_status gdn_chunk_dq(const gdn_problem *problem, const void *dout, const void *hck, float *dq,
+                        void *stream);
 
 /*
  * gdn_forward_varlen -- gdn_forward over packed sequences of different

@@ -36,8 +36,8 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     assert _declared_functions() == sorted(
         ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_forward_states",
-         "gdn_forward_varlen", "gdn_rescan_dq", "gdn_workspace_bytes", "gdn_status_str",
-         "gdn_abi_version"])
+         "gdn_forward_varlen", "gdn_rescan_dq", "gdn_chunk_dq", "gdn_workspace_bytes",
+         "gdn_status_str", "gdn_abi_version"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -214,3 +214,22 @@ def test_rescan_dq_is_not_routed_to_the_four_wave_kernel(lib, gdn, monkeypatch):
     assert _rescan(lib, _problem(gdn)) == 3
     assert _rescan(lib, _problem(gdn, gate=1)) == 3
 
+
+
+def _chunk_dq(lib, pr, do=FAKE, hck=FAKE, dq=FAKE):
+    return lib.gdn_chunk_dq(ctypes.byref(pr), do, hck, dq, None)
+
+
+def test_chunk_dq_validates_before_launch(lib, gdn):
+    pr = _problem(gdn)
+    for name in ("do", "hck", "dq"):
+        assert _chunk_dq(lib, pr, **{name: None}) == 1, name
+    assert _chunk_dq(lib, pr, dq=MISALIGNED) == 4
+    assert _chunk_dq(lib, pr, hck=MISALIGNED) == 4
+    assert _chunk_dq(lib, _problem(gdn, io=0, o=0)) == 3        # bf16 dO only
+    assert _chunk_dq(lib, _problem(gdn, K=96)) == 3
+    assert _chunk_dq(lib, _problem(gdn, chunk=16)) == 3
+    # a chunk's rows of 2^17 heads of fp32 dq pass 32-bit offsets
+    assert _chunk_dq(lib, _problem(gdn, B=1, T=64, H=1 << 17, K=128, V=128)) == 3
+    # no tokens: nothing to do, no buffers needed
+    assert _chunk_dq(lib, _problem(gdn, T=0), do=None, hck=None, dq=None) == 0

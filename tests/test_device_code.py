@@ -81,6 +81,10 @@ def test_every_dispatched_kernel_is_present(disassembly):
                    "forward_pipe_kernelILi64ELi128ENS_6bf16_tELb0ELb1",
                    "forward_pipe_kda_kernelILi64ELi128ENS_6bf16_tELb1ELb0",
                    "forward_pipe_kda_kernelILi64ELi128ENS_6bf16_tELb0ELb1",
+                   # the re-scan with dq (DQ) and dq from saved states
+                   "forward_pipe_kernelILi64ELi128ENS_6bf16_tELb1ELb0ELb1",
+                   "forward_pipe_kda_kernelILi64ELi128ENS_6bf16_tELb1ELb0ELb1",
+                   "chunk_dq_kernelILi64ELi128ELi128E", "chunk_dq_kernelILi32ELi64ELi64E",
                    "prepare_kernel", "scan_kernel"):
         assert kernel in demangled, kernel
 
