@@ -38,6 +38,8 @@ def parse():
                     help="time gdn_forward_states (also saves chunk-start states and v')")
     ap.add_argument("--rescan", action="store_true",
                     help="time gdn_rescan_dq (the backward's re-scan: states, v', dq; no o)")
+    ap.add_argument("--chunk-dq", action="store_true",
+                    help="time gdn_chunk_dq (dq's state term from saved states, on its own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
@@ -70,6 +72,13 @@ def forward_bytes(w, o_dtype, states=False, rescan=False):
         nt = (T + w.chunk - 1) // w.chunk
         saved = io_bytes(o_dtype) * (B * nt * H * K * V + B * T * H * V)
     return B * T * H * per_tok + state + saved
+
+
+def chunk_dq_bytes(w, o_dtype):
+    """dO read (io dtype), the saved states read (o dtype), dq written (fp32)."""
+    nt = (w.T + w.chunk - 1) // w.chunk
+    return (w.B * w.T * w.H * (io_bytes(w.io) * w.V + 4 * w.K)
+            + io_bytes(o_dtype) * w.B * nt * w.H * w.K * w.V)
 
 
 def forward_flops(w):
@@ -164,7 +173,18 @@ def main():
                                    w.gate == "key", tdt)
     ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8) if ws_bytes else None
 
-    if args.rescan:
+    if args.chunk_dq:
+        if w.io != "bf16":
+            sys.exit("bench: --chunk-dq takes bf16 workloads (gdn_chunk_dq reads bf16 dO)")
+        nt = (w.T + w.chunk - 1) // w.chunk
+        gen = torch.Generator().manual_seed(w.seed + 1000)
+        dout = torch.randn(w.B, w.T, w.H, w.V, generator=gen).to(d["q"].dtype).to(dev)
+        hck = (0.1 * torch.randn(w.B, nt, w.H, w.K, w.V, generator=gen)).to(tdt).to(dev)
+        dq = torch.empty(w.B, w.T, w.H, w.K, device=dev, dtype=torch.float32)
+
+        def step():
+            gdn.chunk_dq(dout, hck, w.chunk, dq=dq)
+    elif args.rescan:
         nt = (w.T + w.chunk - 1) // w.chunk
         hck = torch.empty(w.B, nt, w.H, w.K, w.V, device=dev, dtype=tdt)
         vnew = torch.empty(w.B, w.T, w.H, w.V, device=dev, dtype=tdt)
@@ -225,12 +245,18 @@ def main():
     torch.cuda.synchronize()
     ms_launch = sum(a.elapsed_time(b) for a, b in evs) / n_k
     fbytes, fflops = forward_bytes(w, o_dtype, args.states, args.rescan), forward_flops(w)
+    kname = kernel_name(w, o_dtype, args.states, args.rescan)
+    if args.chunk_dq:
+        fbytes, fflops = chunk_dq_bytes(w, o_dtype), 2.0 * w.B * w.T * w.H * w.K * w.V
+        kname = "chunk_dq_kernel<%d, %d, %d, %s>" % (w.chunk, w.K, w.V,
+                                                     {"bf16": "bf16_t", "fp32": "float"}[o_dtype])
     achieved = fbytes / (ms_launch * 1e-3) / 1e9
     mfma_peak = MFMA_PEAK_TFLOPS["f16" if w.io == "bf16" else "f32"]
-    roofline = {"kernel": kernel_name(w, o_dtype, args.states, args.rescan), "bound": "hbm",
+    roofline = {"kernel": kname, "bound": "hbm",
                 "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None if args.rescan else measured_traffic(w, o_dtype, args.states),
+                "traffic": (None if args.rescan or args.chunk_dq
+                            else measured_traffic(w, o_dtype, args.states)),
                 "ms_per_launch": round(ms_launch, 5),
                 "algorithmic_bytes_per_launch": fbytes,
                 "algorithmic_flops_per_launch": fflops,
@@ -250,6 +276,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "K": w.K, "V": w.V,
                    "chunk": w.chunk, "io": w.io, "o_dtype": o_dtype, "gate": w.gate,
                    "h0": w.h0, "states": bool(args.states), "rescan": bool(args.rescan),
+                   "chunk_dq": bool(args.chunk_dq),
                    "parallelism": "single-gpu"},
         "roofline": roofline,
         "cpu_baseline": cpu,
