@@ -10,7 +10,7 @@
 // formed transposed, DQ^T = h_c dO^T, so that both MFMA operands are rows
 // read straight from HBM (16 contiguous bytes per lane: a row of h_c and a
 // row of dO over 8 value columns) and each lane's result is 4 consecutive
-// keys of one token, stored as two 8-byte pieces.  Wave w takes key tiles
+// keys of one token, stored as 8-byte pieces (paired with the next lane's).  Wave w takes key tiles
 // [w K/64, (w + 1) K/64) and every token tile, so h_c is read once per
 // workgroup and dO (the smaller tile) once per wave, through the cache.
 // Tokens past T read zero and their stores are dropped by the buffer
@@ -83,6 +83,10 @@ __global__ __launch_bounds__(256) void chunk_dq_kernel(ChunkDqParams p) {
         for (int s = 0; s < NS; ++s)
             bo[n][s] = __builtin_bit_cast(bf16x8, bload128(rdo, ((uint32_t)(16 * n + (l & 15)) * HV +
                                                                  (uint32_t)h * V + 32 * s + col) * 2, 0));
+    // every load is in flight before the first product: left to itself the
+    // scheduler interleaves them with the MFMAs to save registers, which
+    // makes three or four memory round trips of one
+    __builtin_amdgcn_sched_barrier(0);
     float4v acc[MT][NTT];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
@@ -97,21 +101,28 @@ __global__ __launch_bounds__(256) void chunk_dq_kernel(ChunkDqParams p) {
 #pragma unroll
                 for (int q = 0; q < HFrag<HT>::kParts; ++q)
                     acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m][s].part[q], bo[n][s], acc[m][n], 0, 0, 0);
-    // lane (g, j): keys 16 (MT wv + m) + 4 g .. + 3 of token 16 n + j
+    // Lane (g, j) holds keys 16 (MT wv + m) + 4 g .. + 3 of token 16 n + j.
+    // Neighbouring lanes (tokens j, j ^ 1) swap halves, so that each 8-byte
+    // store of a lane pair fills 16 contiguous bytes of one token's row and
+    // an instruction writes whole 64-byte pieces of 8 rows: the even lane
+    // stores its keys +0, +1 of token j and the odd lane's of token j + 1,
+    // the odd lane the even lane's +2, +3 of token j and its own of j + 1.
+    const bool odd = l & 1;
+    const uint32_t tok_a = (uint32_t)(l & 14), half = 8 * (uint32_t)odd;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int n = 0; n < NTT; ++n) {
-            const uint32_t off = ((uint32_t)(16 * n + (l & 15)) * HK + (uint32_t)h * K +
-                                  16 * (MT * wv + m) + 4 * (l >> 4)) * 4;
-            __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(acc[m][n][0]), __float_as_uint(acc[m][n][1])},
-                                                  rdq, off, 0, 0);
-            // (kept as two 8-byte stores: the compiler would merge them into
-            // one 16-byte store, whose data registers it does not protect
-            // from a following write)
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(acc[m][n][2]), __float_as_uint(acc[m][n][3])},
-                                                  rdq, off + 8, 0, 0);
+            const float4v x = acc[m][n];
+            const float s0 = odd ? x[0] : x[2], s1 = odd ? x[1] : x[3];
+            const float r0 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s0), 0xB1, 0xf, 0xf, false));
+            const float r1 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s1), 0xB1, 0xf, 0xf, false));
+            const uint32_t off = ((uint32_t)(16 * n) + tok_a) * HK * 4 +
+                                 ((uint32_t)h * K + 16 * (MT * wv + m) + 4 * (l >> 4)) * 4 + half;
+            __builtin_amdgcn_raw_buffer_store_b64(
+                u32x2{__float_as_uint(odd ? r0 : x[0]), __float_as_uint(odd ? r1 : x[1])}, rdq, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(
+                u32x2{__float_as_uint(odd ? x[2] : r0), __float_as_uint(odd ? x[3] : r1)}, rdq, off + HK * 4, 0, 0);
         }
 }
 

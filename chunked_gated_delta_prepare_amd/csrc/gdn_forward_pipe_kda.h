@@ -393,10 +393,15 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
                 *(float4v *)(flv + kc) = e1;
                 *(float4v *)(fmv + kc) = e2;
             }
-            // ---- operands q~, k~, k^ (fp16) of this thread's rows
+            // ---- operands q~, k~, k^ (fp16) of this thread's rows; the
+            // exponent (gcum - gcum_gm) log2 e is one FMA per element on the
+            // in-segment cumsum, with the segment's offset folded in
+            const float4v dof = (off - gm) * kLog2e;
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
-                const float4v d = (rg[i] + off - gm) * kLog2e;
+                float4v d;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) d[e] = __builtin_fmaf(rg[i][e], kLog2e, dof[e]);
                 half4 hq, hk, hh;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
