@@ -306,8 +306,12 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
     } else {
         // =====================  prepare waves  ===========================
         // (unlike the scalar-gate kernel, these keep the default wave
-        // priority: raising it measured 2 % slower here)
+        // priority in the plain forward, where raising it measured 2 %
+        // slower, and in the re-scan, 3 % slower; with saved states the
+        // chain's store work competes for the SIMDs' issue slots, and a
+        // raised priority measured 7 % faster)
         const int pw = wv - 4, pt = tid - 256;
+        if constexpr (ST && !DQ) __builtin_amdgcn_s_setprio(3);
         const rsrc_t rq_ = make_rsrc((const IO *)p.q + row0 * K, (uint32_t)T * rsK * SIO);
         const rsrc_t rk_ = make_rsrc((const IO *)p.k + row0 * K, (uint32_t)T * rsK * SIO);
         const rsrc_t rv_ = make_rsrc((const IO *)p.v + row0 * V, (uint32_t)T * rsV * SIO);
