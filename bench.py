@@ -38,6 +38,9 @@ def parse():
                     help="time gdn_forward_states (also saves chunk-start states and v')")
     ap.add_argument("--rescan", action="store_true",
                     help="time gdn_rescan_dq (the backward's re-scan: states, v', dq; no o)")
+    ap.add_argument("--varlen", action="store_true",
+                    help="time gdn_forward_varlen on the workload's tokens packed as eight "
+                         "sequences of mixed lengths")
     ap.add_argument("--chunk-dq", action="store_true",
                     help="time gdn_chunk_dq (dq's state term from saved states, on its own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -173,7 +176,23 @@ def main():
                                    w.gate == "key", tdt)
     ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8) if ws_bytes else None
 
-    if args.chunk_dq:
+    n_seqs = 0
+    if args.varlen:
+        from chunked_gated_delta_prepare_amd.inputs import varlen_lengths
+        lens = varlen_lengths(w.B * w.T)
+        n_seqs = len(lens)
+        import itertools
+        cu = torch.tensor([0] + list(itertools.accumulate(lens)), dtype=torch.int32, device=dev)
+        flat = {n: d[n].reshape(1, w.B * w.T, *d[n].shape[2:]) for n in ("q", "k", "v", "beta", "g")}
+        gen = torch.Generator().manual_seed(w.seed + 2000)
+        h0v = (0.1 * torch.randn(n_seqs, w.H, w.K, w.V, generator=gen)).to(dev) if w.h0 else None
+        ov = torch.empty(1, w.B * w.T, w.H, w.V, device=dev, dtype=tdt)
+        hTv = torch.empty(n_seqs, w.H, w.K, w.V, device=dev, dtype=torch.float32)
+
+        def step():
+            gdn.forward_varlen(flat["q"], flat["k"], flat["v"], flat["beta"], flat["g"], cu, w.chunk,
+                               h0v, o_dtype=tdt, o=ov, hT=hTv)
+    elif args.chunk_dq:
         if w.io != "bf16":
             sys.exit("bench: --chunk-dq takes bf16 workloads (gdn_chunk_dq reads bf16 dO)")
         nt = (w.T + w.chunk - 1) // w.chunk
@@ -246,6 +265,10 @@ def main():
     ms_launch = sum(a.elapsed_time(b) for a, b in evs) / n_k
     fbytes, fflops = forward_bytes(w, o_dtype, args.states, args.rescan), forward_flops(w)
     kname = kernel_name(w, o_dtype, args.states, args.rescan)
+    if args.varlen:
+        # one state per sequence instead of per batch row; the VL instance
+        fbytes += 4 * w.K * w.V * w.H * (n_seqs - w.B) * (2 if w.h0 else 1)
+        kname = kname[:-1] + ", false, true>"
     if args.chunk_dq:
         fbytes, fflops = chunk_dq_bytes(w, o_dtype), 2.0 * w.B * w.T * w.H * w.K * w.V
         kname = "chunk_dq_kernel<%d, %d, %d, %s>" % (w.chunk, w.K, w.V,
@@ -255,7 +278,7 @@ def main():
     roofline = {"kernel": kname, "bound": "hbm",
                 "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": (None if args.rescan or args.chunk_dq
+                "traffic": (None if args.rescan or args.chunk_dq or args.varlen
                             else measured_traffic(w, o_dtype, args.states)),
                 "ms_per_launch": round(ms_launch, 5),
                 "algorithmic_bytes_per_launch": fbytes,
@@ -276,7 +299,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "K": w.K, "V": w.V,
                    "chunk": w.chunk, "io": w.io, "o_dtype": o_dtype, "gate": w.gate,
                    "h0": w.h0, "states": bool(args.states), "rescan": bool(args.rescan),
-                   "chunk_dq": bool(args.chunk_dq),
+                   "chunk_dq": bool(args.chunk_dq), "varlen_seqs": n_seqs or None,
                    "parallelism": "single-gpu"},
         "roofline": roofline,
         "cpu_baseline": cpu,

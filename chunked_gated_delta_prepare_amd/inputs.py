@@ -78,6 +78,20 @@ def make_inputs(B, T, H, K, V, *, io="bf16", gate="head", gate_bias=2.0,
             "g": g.contiguous(), "h0": hz}
 
 
+# Length mix for packed sequences: eight sequences whose lengths are these
+# shares of the total token count (at 16384 tokens exactly these lengths,
+# the longest 4096).
+VARLEN_MIX = (4096, 3000, 2500, 2000, 1596, 1200, 1000, 992)
+
+
+def varlen_lengths(total: int):
+    """Sequence lengths of the packed-sequence mix for `total` tokens."""
+    base = sum(VARLEN_MIX)
+    lens = [total * x // base for x in VARLEN_MIX]
+    lens[-1] += total - sum(lens)
+    return lens
+
+
 def workload_inputs(w: Workload, *, T=None, B=None, H=None):
     """Inputs for a named workload; T/B/H may be overridden to shrink it."""
     return make_inputs(B or w.B, T or w.T, H or w.H, w.K, w.V, io=w.io,
