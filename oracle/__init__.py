@@ -10,7 +10,9 @@ These functions mirror the library entry points:
   the reference for ``gdn_forward``.  See ``gdn_oracle.c`` for the recurrence.
   ``token_states`` also records the per-chunk start states and the per-token
   state deltas, the reference for ``gdn_forward_states``; ``rescan_dq`` forms
-  dq's chunk-start-state term from them, the reference for ``gdn_rescan_dq``.
+  dq's chunk-start-state term from them, the reference for ``gdn_rescan_dq``
+  and ``gdn_chunk_dq``.  ``token_backward`` differentiates the recurrence
+  (every input's gradient), the reference for a backward pass.
 * ``chunk_prepare`` -- the per-chunk WY factors (gate cumsum, the strictly lower
   decayed Gram matrix, its unit-triangular inverse, then w and u), the
   reference for ``gdn_prepare``.  Steps follow the TileOPs "Reuse P as beta
@@ -179,6 +181,41 @@ def rescan_dq(hck, do, chunk):
 # Chunk form.  Per (batch, head) and per chunk of C tokens (the last chunk may
 # be shorter).  Notation: gamma = chunk-local inclusive cumsum of g.
 # --------------------------------------------------------------------------
+
+def token_backward(q, k, v, beta, g, do, h0=None, dhT=None):
+    """Gradients of the forward pass by reverse-mode differentiation of the
+    token recurrence, the method's plain definition (decay, then the delta
+    correction, then o_t = S_t q_t; the same steps as ``token_recurrence``),
+    in fp64 with torch autograd on the CPU.  This is what the backward's WY
+    stage of the kernel_fun KDA re-scan page (its dq/dk/dv/dbeta/dg outputs)
+    computes by the chunk form.
+
+    For L = sum_t o_t . do_t + sum hT * dhT (dhT optional), returns
+    ``(dq, dk, dv, dbeta, dg, dh0)`` as float64 arrays in the inputs' layouts
+    (dh0 is None without h0).  A Python loop over tokens: small inputs only.
+    """
+    import torch
+    f64 = lambda x: torch.tensor(np.asarray(x, np.float64))
+    qt, kt, vt, bt, gt = (f64(x).requires_grad_(True) for x in (q, k, v, beta, g))
+    B, T, H, K = qt.shape
+    V = vt.shape[-1]
+    per_key = gt.dim() == 4
+    h0t = f64(h0).requires_grad_(True) if h0 is not None else None
+    S = h0t.transpose(-1, -2) if h0t is not None else torch.zeros(B, H, V, K, dtype=torch.float64)
+    dot = f64(do)
+    loss = torch.zeros((), dtype=torch.float64)
+    for t in range(T):
+        a = torch.exp(gt[:, t])
+        S = S * (a[:, :, None, :] if per_key else a[:, :, None, None])
+        e = vt[:, t] - torch.einsum("bhvk,bhk->bhv", S, kt[:, t])
+        S = S + bt[:, t, :, None, None] * e[..., :, None] * kt[:, t][..., None, :]
+        loss = loss + (torch.einsum("bhvk,bhk->bhv", S, qt[:, t]) * dot[:, t]).sum()
+    if dhT is not None:
+        loss = loss + (S.transpose(-1, -2) * f64(dhT)).sum()
+    loss.backward()
+    grads = [x.grad.numpy() for x in (qt, kt, vt, bt, gt)]
+    return tuple(grads) + (h0t.grad.numpy() if h0t is not None else None,)
+
 
 def _chunks(T, C):
     for s in range(0, T, C):

@@ -602,3 +602,74 @@ def test_rescan_dq_with_state_deltas_is_the_autograd_dq(oracle_mod, per_key):
         for s in range(s0, t + 1):
             x += np.exp(G[-1] - G[s - s0]) * kk[s] * (vnew[0, s, 0] @ dd[t])
         np.testing.assert_allclose(x, dq[t], rtol=1e-9, atol=1e-11)
+
+
+def _np_loss(q, k, v, beta, g, h0, do, dhT):
+    """L = sum_t o_t . do_t + sum hT * dhT by a plain numpy fp64 loop, written
+    apart from the oracle's (independent of its C and torch code)."""
+    q, k, v, beta, g, h0, do, dhT = (np.asarray(x, np.float64) for x in (q, k, v, beta, g, h0, do, dhT))
+    B, T, H, K = q.shape
+    L = 0.0
+    for b in range(B):
+        for h in range(H):
+            S = h0[b, h].T.copy()
+            for t in range(T):
+                S = S * np.exp(g[b, t, h])               # scalar, or per key column
+                e = v[b, t, h] - S @ k[b, t, h]
+                S = S + beta[b, t, h] * np.outer(e, k[b, t, h])
+                L += (S @ q[b, t, h]) @ do[b, t, h]
+            L += np.sum(S.T * dhT[b, h])
+    return L
+
+
+@pytest.mark.parametrize("per_key", [False, True])
+def test_token_backward_matches_finite_differences(oracle_mod, per_key):
+    """Every gradient of token_backward against central differences of an
+    independently written loss (step 1e-5 in fp64: error ~1e-10)."""
+    pytest.importorskip("torch")
+    rng = np.random.default_rng(503 + per_key)
+    B, T, H, K, V = 1, 6, 2, 3, 2
+    q = rng.standard_normal((B, T, H, K))
+    k = rng.standard_normal((B, T, H, K))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, V))
+    beta = rng.uniform(0.1, 0.9, (B, T, H))
+    g = -rng.uniform(0.05, 0.5, (B, T, H, K) if per_key else (B, T, H))
+    h0 = 0.3 * rng.standard_normal((B, H, K, V))
+    do = rng.standard_normal((B, T, H, V))
+    dhT = rng.standard_normal((B, H, K, V))
+    grads = oracle_mod.token_backward(q, k, v, beta, g, do, h0, dhT)
+    args = [q, k, v, beta, g, h0]
+    eps = 1e-5
+    for i, (x, gx) in enumerate(zip(args, grads)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            ap = list(args); ap[i] = xp
+            am = list(args); am[i] = xm
+            fd[idx] = (_np_loss(*ap, do, dhT) - _np_loss(*am, do, dhT)) / (2 * eps)
+        np.testing.assert_allclose(gx, fd, rtol=1e-6, atol=1e-8, err_msg="input %d" % i)
+
+
+def test_token_backward_forward_value_is_the_recurrence(oracle_mod):
+    """The loss token_backward differentiates is the C recurrence's: with
+    do = one-hot and no dhT, dq at that token is S_t^T e_j (row j of S_t),
+    and the C oracle's o_t = S_t q_t, so dq_t . q_t = o_t[j]."""
+    pytest.importorskip("torch")
+    rng = np.random.default_rng(509)
+    B, T, H, K, V = 1, 5, 1, 4, 3
+    q = rng.standard_normal((B, T, H, K)).astype(np.float32)
+    k = rng.standard_normal((B, T, H, K)).astype(np.float32)
+    v = rng.standard_normal((B, T, H, V)).astype(np.float32)
+    beta = rng.uniform(0.1, 0.9, (B, T, H)).astype(np.float32)
+    g = -rng.uniform(0.05, 0.5, (B, T, H)).astype(np.float32)
+    h0 = (0.3 * rng.standard_normal((B, H, K, V))).astype(np.float32)
+    o, _ = oracle_mod.token_recurrence(q, k, v, beta, g, h0)
+    for t in range(T):
+        for j in range(V):
+            do = np.zeros((B, T, H, V))
+            do[0, t, 0, j] = 1.0
+            dq = oracle_mod.token_backward(q, k, v, beta, g, do, h0)[0]
+            assert abs(dq[0, t, 0] @ q[0, t, 0].astype(np.float64) - o[0, t, 0, j]) < 1e-10
