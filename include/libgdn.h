@@ -133,6 +133,9 @@ gdn_status gdn_scan(const gdn_problem *problem, const void *q, const void *k,
  * gdn_prepare followed by gdn_scan up to rounding.  `workspace` must hold
  * gdn_workspace_bytes(problem) bytes (it may be NULL when that is 0); its
  * contents on entry do not matter.  hT may be NULL or alias h0.
+ * fp32 io with the per-key gate, K = 128 and chunk 64 needs more than 160
+ * KiB of LDS and returns GDN_ERR_LDS_BUDGET (chunk 32 runs it), as do the
+ * other forward entry points for that shape.
  */
 gdn_status gdn_forward(const gdn_problem *problem, const void *q, const void *k,
                        const void *v, const float *beta, const float *g,

@@ -233,3 +233,12 @@ def test_chunk_dq_validates_before_launch(lib, gdn):
     assert _chunk_dq(lib, _problem(gdn, B=1, T=64, H=1 << 17, K=128, V=128)) == 3
     # no tokens: nothing to do, no buffers needed
     assert _chunk_dq(lib, _problem(gdn, T=0), do=None, hck=None, dq=None) == 0
+
+
+def test_fp32_key_gate_k128_chunk64_reports_the_lds_budget(lib, gdn):
+    # the one listed shape the four-wave kernel cannot hold in 160 KiB of LDS:
+    # a status before any launch, for every forward entry point
+    pr = _problem(gdn, io=0, o=0, gate=1, K=128, V=128, chunk=64)
+    assert _fwd(lib, pr) == 5
+    assert _fwd_states(lib, pr) == 5
+    assert _fwd_varlen(lib, _problem(gdn, B=1, io=0, o=0, gate=1, K=128, V=128, chunk=64)) == 5
