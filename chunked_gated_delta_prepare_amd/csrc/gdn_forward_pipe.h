@@ -186,6 +186,31 @@ __device__ __forceinline__ void store4<float>(const float4v &x, rsrc_t r, uint32
     __builtin_amdgcn_raw_buffer_store_b64(u32x2{u[2], u[3]}, r, voff + 8, soff, 0);
 }
 
+// o^T tiles: lane (g, j) holds 4 consecutive columns of token j (voff is
+// that token's byte offset, row_bytes the token pitch).  bf16: one 8-byte
+// store.  fp32: the neighbouring lanes (tokens j, j ^ 1) swap halves by DPP
+// so that each lane pair fills 16 contiguous bytes of one token with its two
+// 8-byte stores (an instruction then writes 64-byte pieces of 8 rows instead
+// of 8-byte pieces of 16 rows with gaps between them).
+template <typename OT>
+__device__ __forceinline__ void store_o_rows(const float4v &x, rsrc_t r, uint32_t voff,
+                                             uint32_t row_bytes, uint32_t soff) {
+    if constexpr (sizeof(OT) == 2) {
+        store4<bf16_t>(x, r, voff, soff);
+    } else {
+        const bool odd = lane_id() & 1;
+        const float s0 = odd ? x[0] : x[2], s1 = odd ? x[1] : x[3];
+        const float r0 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s0), 0xB1, 0xf, 0xf, false));
+        const float r1 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s1), 0xB1, 0xf, 0xf, false));
+        // token j & ~1 at columns +2 odd, then token j | 1
+        const uint32_t va = odd ? voff - row_bytes + 8 : voff;
+        __builtin_amdgcn_raw_buffer_store_b64(
+            u32x2{__float_as_uint(odd ? r0 : x[0]), __float_as_uint(odd ? r1 : x[1])}, r, va, soff, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(
+            u32x2{__float_as_uint(odd ? x[2] : r0), __float_as_uint(odd ? x[3] : r1)}, r, va + row_bytes, soff, 0);
+    }
+}
+
 // Inclusive scan of a chunk's scalar gate (lane l holds g of row l) and
 // the row factors the chunk needs, written by one wave: e^gcum, e^(gl-gcum),
 // e^gl for the chain; beta, e^(gcum_block - gcum), e^(gcum - gcum_16J) for
@@ -543,7 +568,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
 #pragma unroll
                     for (int s = 0; s < C / 32; ++s)
                         if (32 * s < 16 * (cb + 1)) M::mma(oa, df[s], frag_sw<C>(Ps, 16 * cb, 32 * s));
-                    store4<OT>(oa, ro_, o_off, (t0 + 16 * cb) * rsV * SO);
+                    store_o_rows<OT>(oa, ro_, o_off, rsV * SO, (t0 + 16 * cb) * rsV * SO);
                 }
             }
             if constexpr (ST) {

@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
 #pragma unroll
                     for (int s = 0; s < C / 32; ++s)
                         if (32 * s < 16 * (cb + 1)) M::mma(oa, df[s], frag_sw<C>(Ps, 16 * cb, 32 * s));
-                    store4<OT>(oa, ro_, o_off, (t0 + 16 * cb) * rsV * SO);
+                    store_o_rows<OT>(oa, ro_, o_off, rsV * SO, (t0 + 16 * cb) * rsV * SO);
                 }
             }
             if constexpr (ST) {
