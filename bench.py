@@ -138,7 +138,7 @@ def measured_traffic(w, o_dtype, states=False):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+        print("bench.py: the benchmark runs on one GPU only; --gpus %d is not supported "
               "(batch/head and sequence sharding across GPUs is a design note, not built)"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
