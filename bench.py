@@ -4,10 +4,16 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one gdn_forward call over one batch of synthetic input already in
-HBM (q, k, v, beta, g, h0 -> o, hT).  Prints one JSON line: tokens/s, the
-roofline of the dominant kernel (algorithmic bytes or flops per launch over
-its average HIP-event-timed duration), and the fp64 CPU oracle timed on the
-host's cores on a bounded sample of the same workload.
+HBM (q, k, v, beta, g, h0 -> o, hT); by default the long-context workload
+gdn_t64k (1 x 65536 tokens, 64 heads, dk = dv = 128), the largest that the
+five workloads put on one GPU.  Each timed step is bracketed by its own HIP
+events on the library's stream; between steps (outside those brackets) a
+1 GiB buffer is written so that no input is still in the 256 MB Infinity
+Cache.  Prints one JSON line: tokens/s from the mean step time (with the
+median and minimum beside it), the roofline of the dominant kernel
+(algorithmic bytes per launch over its mean event-timed duration), a plain
+device copy's bandwidth measured in the same run, and the fp64 CPU oracle
+timed on the host's cores on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -24,14 +30,18 @@ if ROOT not in sys.path:
 METRIC = "tokens/sec of chunked GDN forward at 1 MI355X; % of bf16 MFMA roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
-DEFAULT_WORKLOAD = "gdn_t4k"
+DEFAULT_WORKLOAD = "gdn_t64k"
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="MiB written between timed steps to evict the Infinity Cache (0: none)")
+    ap.add_argument("--chunk", type=int, default=None,
+                    help="override the workload's chunk size (32 or 64)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--o-dtype", default=None, choices=[None, "bf16", "fp32"])
     ap.add_argument("--states", action="store_true",
@@ -163,6 +173,9 @@ def main():
         return
 
     w = WORKLOADS[args.workload]
+    if args.chunk:
+        import dataclasses
+        w = dataclasses.replace(w, chunk=args.chunk)
     o_dtype = args.o_dtype or w.io
     inp = workload_inputs(w)
     d = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
@@ -234,35 +247,39 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # ---- the timed region: exactly K steps, synchronised on both sides
+    # ---- the timed region: exactly K steps, each bracketed by its own
+    # events on the stream the library launches on; between steps, outside
+    # the brackets, a buffer larger than the Infinity Cache is written
     stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    flush = (torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev)
+             if args.flush_mib > 0 else None)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-    tokens = w.B * w.T
-    value = tokens / (ms_step * 1e-3)
-    print("bench: %d steps, %.4f ms/step (wall %.4f ms/step)"
-          % (args.steps, ms_step, wall * 1e3 / args.steps), file=sys.stderr, flush=True)
-
-    # ---- the dominant (and only) kernel: gdn_forward is one launch of the
-    # fused forward kernel.  Each launch is bracketed by its own events on
-    # the stream the library launches on, and the durations averaged.
-    n_k = max(5, args.steps)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n_k)]
     for a, b in evs:
+        if flush is not None:
+            flush.fill_(1)
         a.record(stream)
         step()
         b.record(stream)
     torch.cuda.synchronize()
-    ms_launch = sum(a.elapsed_time(b) for a, b in evs) / n_k
+    wall = time.perf_counter() - t0
+    times = sorted(a.elapsed_time(b) for a, b in evs)
+    ms_step = sum(times) / len(times)
+    ms_median = times[len(times) // 2] if len(times) % 2 else 0.5 * (
+        times[len(times) // 2 - 1] + times[len(times) // 2])
+    ms_min = times[0]
+    tokens = w.B * w.T
+    value = tokens / (ms_step * 1e-3)
+    print("bench: %d steps, mean %.4f ms, median %.4f, min %.4f (wall %.4f ms/step with flushes)"
+          % (args.steps, ms_step, ms_median, ms_min, wall * 1e3 / args.steps),
+          file=sys.stderr, flush=True)
+    del flush
+
+    # ---- the dominant (and only) kernel: a step is one launch of the fused
+    # forward kernel, so its mean event-timed duration is ms_step
+    ms_launch = ms_step
     fbytes, fflops = forward_bytes(w, o_dtype, args.states, args.rescan), forward_flops(w)
     kname = kernel_name(w, o_dtype, args.states, args.rescan)
     if args.varlen:
@@ -286,6 +303,9 @@ def main():
                 "mfma_frac": round(fflops / (ms_launch * 1e-3) / 1e12 / mfma_peak, 4),
                 "mfma_peak_tflops": mfma_peak}
 
+    # ---- what a plain device copy reaches on this GPU, for scale
+    copy_ref = copy_bandwidth(torch, dev)
+
     # ---- the oracle on the host's cores, on a bounded sample of the workload
     cpu = None
     if not args.no_cpu_baseline:
@@ -294,6 +314,8 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "ms_median": round(ms_median, 5), "ms_min": round(ms_min, 5),
+        "flush_between_steps_bytes": args.flush_mib << 20,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16" if w.io == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "K": w.K, "V": w.V,
@@ -302,9 +324,44 @@ def main():
                    "chunk_dq": bool(args.chunk_dq), "varlen_seqs": n_seqs or None,
                    "parallelism": "single-gpu"},
         "roofline": roofline,
+        "copy_ref": copy_ref,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def copy_bandwidth(torch, dev, mib=1024, reps=10):
+    """A plain device-to-device copy of `mib` MiB (torch's copy kernel), timed
+    with events: bytes read plus written per second, the practical ceiling a
+    streaming kernel can reach on this GPU."""
+    n = mib << 20
+    x = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        y.copy_(x)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    gbs = 2 * n / (ms * 1e-3) / 1e9
+    del x, y
+    return {"bytes_read": n, "bytes_written": n, "ms": round(ms, 4), "GB/s": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(w, inp, target_s):
@@ -314,7 +371,10 @@ def cpu_baseline(w, inp, target_s):
     wall time has been spent, and report the mean rate."""
     import oracle
 
-    nthreads = min(os.cpu_count() or 1, 16)
+    # one thread per (batch, head) sequence, on the cores this process may
+    # use, at most 16: a GPU host's CPU share per GPU
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    nthreads = max(1, min(avail, 16))
     q = inp["q"].float().numpy()
     k = inp["k"].float().numpy()
     v = inp["v"].float().numpy()
@@ -340,6 +400,7 @@ def cpu_baseline(w, inp, target_s):
     token_heads_per_s = n * w.T * len(times) / sum(times)
     return {"value": round(token_heads_per_s / w.H, 1), "unit": "tokens/s",
             "cores": min(nthreads, n), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(), "cpus_usable": avail,
             "sample": "%d of %d (batch, head) sequences of %d tokens, %d passes; fp64 token "
                       "recurrence in C, one thread per sequence; tokens/s = token-heads/s / H"
                       % (n, pairs, w.T, len(times)),

@@ -27,7 +27,7 @@ import os
 import threading
 
 __all__ = ["prepare", "scan", "forward", "forward_states", "forward_varlen", "rescan_dq",
-           "workspace_bytes",
+           "workspace_bytes", "wait_timeouts",
            "load_library",
            "GdnError", "LIB_PATH", "STATUS"]
 
@@ -43,8 +43,8 @@ STATUS = {
 }
 EXPORTS = ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_forward_states",
            "gdn_forward_varlen", "gdn_rescan_dq", "gdn_chunk_dq", "gdn_workspace_bytes",
-           "gdn_status_str", "gdn_abi_version"]
-ABI_VERSION = 5
+           "gdn_status_str", "gdn_abi_version", "gdn_wait_timeouts"]
+ABI_VERSION = 6
 
 
 class GdnError(RuntimeError):
@@ -95,6 +95,8 @@ def load_library(path: str | None = None):
         lib.gdn_status_str.restype = ctypes.c_char_p
         lib.gdn_abi_version.argtypes = []
         lib.gdn_abi_version.restype = ctypes.c_int
+        lib.gdn_wait_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]
+        lib.gdn_wait_timeouts.restype = ctypes.c_int
         if lib.gdn_abi_version() != ABI_VERSION:
             raise RuntimeError("libgdn ABI %d, binding expects %d"
                                % (lib.gdn_abi_version(), ABI_VERSION))
@@ -169,6 +171,16 @@ def workspace_bytes(B, T, H, K, V, chunk, io_dtype, gate_per_key=False, o_dtype=
     od = _dtype_code(o_dtype or io_dtype)
     pr = Problem(B, T, H, K, V, chunk, io, od, GDN_GATE_KEY if gate_per_key else GDN_GATE_HEAD)
     return int(load_library().gdn_workspace_bytes(ctypes.byref(pr)))
+
+
+def wait_timeouts(reset=False):
+    """Count of bounded LDS waits inside the bf16-io kernels that gave up on
+    the current device since the last reset (gdn_wait_timeouts; synchronous).
+    A launch during which it grew produced results that must not be trusted."""
+    lib = load_library()
+    n = ctypes.c_uint32(0)
+    _check("gdn_wait_timeouts", lib.gdn_wait_timeouts(ctypes.byref(n), 1 if reset else 0))
+    return int(n.value)
 
 
 def prepare(k, v, beta, g, chunk, *, w=None, u=None, gcum=None, stream=None):

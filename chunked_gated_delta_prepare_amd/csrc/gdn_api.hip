@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/libgdn.h"
 #include "gdn_internal.h"
@@ -143,6 +144,41 @@ gdn_status enqueue_scan(const gdn_problem *pr, const void *q, const void *k,
 }
 
 }  // namespace
+
+// The count of bounded LDS waits that gave up (see WaitCtl), one word per
+// device.  Its device address is looked up once per device, with that
+// device current, and kept: host code passes that address, never the
+// symbol's name, to the kernels.
+__device__ unsigned gdn_wait_timeout_word;
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_wait_mu;
+unsigned *g_wait_addr[kMaxDevices];
+bool g_wait_looked_up[kMaxDevices];
+}  // namespace
+
+unsigned *wait_count_ptr() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lk(g_wait_mu);
+    if (!g_wait_looked_up[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(gdn_wait_timeout_word)) != hipSuccess) p = nullptr;
+        g_wait_addr[dev] = (unsigned *)p;
+        g_wait_looked_up[dev] = true;
+    }
+    return g_wait_addr[dev];
+}
+
+void wait_params(unsigned &limit, unsigned &bias) {
+    // GDN_WAIT_FORCE_TIMEOUT=1 makes every bounded wait give up after a few
+    // polls (a test of the timeout path; results are then garbage)
+    const char *e = std::getenv("GDN_WAIT_FORCE_TIMEOUT");
+    const bool force = e && *e == '1';
+    limit = force ? 4u : (1u << 16);
+    bias = force ? (1u << 30) : 0u;
+}
 
 gdn_status launch_kernel(const void *fn, int grid, void *params, hipStream_t s, int threads) {
     if (grid <= 0) return GDN_OK;
@@ -284,6 +320,20 @@ gdn_status gdn_forward_varlen(const gdn_problem *problem, const int32_t *cu_seql
     }
     return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, nullptr, nullptr, cu_seqlens,
                            n_seqs, (hipStream_t)stream);
+}
+
+gdn_status gdn_wait_timeouts(uint32_t *count, int reset) {
+    if (!count) return GDN_ERR_NULL_ARG;
+    unsigned *p = wait_count_ptr();
+    if (!p) return GDN_ERR_HIP;
+    unsigned v = 0;
+    if (hipMemcpy(&v, p, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return GDN_ERR_HIP;
+    *count = v;
+    if (reset) {
+        const unsigned zero = 0;
+        if (hipMemcpy(p, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return GDN_ERR_HIP;
+    }
+    return GDN_OK;
 }
 
 const char *gdn_status_str(gdn_status status) {

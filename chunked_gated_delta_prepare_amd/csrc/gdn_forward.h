@@ -56,6 +56,12 @@ struct FwdParams {
     // term [B, T, H, K] (fp32, accumulated into) out; both NULL otherwise
     const void *dout;
     float *dq;
+    // bounded LDS waits of the pipelined kernels (see WaitCtl): a device word
+    // that counts waits that gave up (NULL: not counted), the poll limit, and
+    // a bias added to every wait target (0; a value no counter reaches makes
+    // every wait give up, which the host sets only to test this path)
+    unsigned *wait_count;
+    unsigned wait_limit, wait_bias;
     int B, T, H, V;
     int nvt;        // V / 64
     int swizzle;
@@ -221,8 +227,8 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
     float *Tmf = (float *)(smem + L::kTm);
     float *Gst = (float *)(smem + L::kGst);
     float *rowf = (float *)(smem + L::kRow);
-    // GDN row factors
-    float *eg = rowf + C, *egl = rowf + 2 * C, *bet = rowf + 3 * C;
+    // GDN row factors (gcv: gcum itself)
+    float *gcv = rowf, *eg = rowf + C, *egl = rowf + 2 * C, *bet = rowf + 3 * C;
     float *einv = rowf + 4 * C, *efac = rowf + 5 * C, *misc = rowf + 5 * C + NB * C;
     // KDA key factors (beta takes the first C slots)
     float *kbet = rowf, *gmv = rowf + C, *fsv = rowf + C + K, *flv = rowf + C + 2 * K;
@@ -419,17 +425,23 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
                     const float y = __shfl_up(x, d);
                     if (l >= d) x += y;
                 }
+                // Every factor a product uses is at most 1 for any g <= 0:
+                // off-diagonal Gram tiles (I > J) split e^(gcum_r - gcum_s)
+                // at the end of block J, einv[s] = e^(gend_J - gcum_s) and
+                // efac[J][r] = e^(gcum_r - gend_J); diagonal tiles take each
+                // entry's decay from gcum directly.
                 const float gl = __shfl(x, C - 1);
-                const float gref = __shfl(x, l & ~15);      // gcum at the start of l's block
+                const float gref = __shfl(x, l | 15);       // gcum at the end of l's block
                 float ef[NB];
 #pragma unroll
-                for (int J = 0; J < NB; ++J) ef[J] = __shfl(x, 16 * J);
+                for (int J = 0; J < NB; ++J) ef[J] = __shfl(x, 16 * J + 15);
                 if (l < C) {
+                    gcv[l] = x;
                     eg[l] = fast_exp(x);
                     egl[l] = fast_exp(gl - x);
                     einv[l] = fast_exp(gref - x);
 #pragma unroll
-                    for (int J = 0; J < NB; ++J) efac[J * C + l] = fast_exp(x - ef[J]);
+                    for (int J = 0; J < NB; ++J) efac[J * C + l] = fast_exp(fminf(x - ef[J], 0.f));
                 }
                 if (l == 0) misc[0] = fast_exp(gl);
             }
@@ -518,9 +530,14 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
                 const int r = 16 * I + acc_col(), s0 = 16 * J + g4;
                 float4v fac = {1.f, 1.f, 1.f, 1.f};
                 if constexpr (!KEYGATE) {
-                    const float fr = efac[J * C + r];
-                    const float4v fi = *(const float4v *)(einv + s0);
-                    fac = fi * fr;
+                    if (I == J) {
+                        const float gr = gcv[r];
+                        const float4v gs = *(const float4v *)(gcv + s0);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) fac[e] = fast_exp(fminf(gr - gs[e], 0.f));
+                    } else {
+                        fac = *(const float4v *)(einv + s0) * efac[J * C + r];
+                    }
                 }
                 if (isA) {
                     const float br = betp[r];

@@ -29,6 +29,8 @@ gdn_status enqueue_forward(const gdn_problem *pr, const void *q, const void *k,
     fp.q = q; fp.k = k; fp.v = v; fp.beta = beta; fp.g = g; fp.h0 = h0;
     fp.o = o; fp.hT = hT; fp.hck = hck; fp.vnew = vnew; fp.cu = cu;
     fp.dout = dout; fp.dq = dq;
+    fp.wait_count = wait_count_ptr();
+    wait_params(fp.wait_limit, fp.wait_bias);
     // packed sequences: one stream per sequence over the [1, T, H, .] tensors
     const int64_t streams = cu ? n_seqs : pr->B;
     fp.B = (int)streams; fp.T = (int)pr->T; fp.H = (int)pr->H; fp.V = (int)pr->V;

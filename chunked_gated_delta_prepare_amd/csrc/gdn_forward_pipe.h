@@ -116,20 +116,47 @@ __device__ __forceinline__ void wg_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Bounded LDS waits.  A wave polls an LDS counter (s_sleep between polls);
+// a normal wait ends after a few thousand cycles.  One that polls `limit`
+// times without its condition coming true gives up and the wave goes on, so
+// a stalled partner can never hang the kernel.  Each wave counts its
+// give-ups (`missed`, wave-uniform) and adds them, once, at its end, to
+// *count: a device word the host reads back (gdn_wait_timeouts) to learn
+// that the launch's results are not to be trusted.  `bias` is added to
+// every target: 0, or a value no counter reaches, with which every wait
+// gives up (only to test this path; every kernel still ends normally).
+struct WaitCtl {
+    unsigned *count;
+    unsigned limit, bias;
+    unsigned missed;
+};
+
+__device__ __forceinline__ void wait_report(const WaitCtl &wc) {
+    if (wc.missed && wc.count && lane_id() == 0)
+        __hip_atomic_fetch_add(wc.count, wc.missed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until an LDS counter reaches target.
+__device__ __forceinline__ void wait_counter(const unsigned *ctr, unsigned target, WaitCtl &wc) {
+    asm volatile("" ::: "memory");
+    const unsigned t = target + wc.bias;
+    for (unsigned it = 0;; ++it) {
+        const unsigned v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if ((unsigned)__builtin_amdgcn_readfirstlane((int)v) >= t) break;
+        if (it >= wc.limit) { ++wc.missed; break; }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+}
+
 // Barrier of the four prepare waves: an LDS arrival counter that only grows
-// (four arrivals per barrier).  The wait is bounded so that no error can
-// leave a wave spinning; a normal wait is a few thousand cycles.
-__device__ __forceinline__ void prep_barrier(unsigned *ctr, unsigned &target) {
+// (four arrivals per barrier), with a bounded wait.
+__device__ __forceinline__ void prep_barrier(unsigned *ctr, unsigned &target, WaitCtl &wc) {
     target += 4;
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     if (lane_id() == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    for (int it = 0; it < (1 << 16); ++it) {
-        const unsigned v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if ((unsigned)__builtin_amdgcn_readfirstlane((int)v) >= target) break;
-        __builtin_amdgcn_s_sleep(1);
-    }
-    asm volatile("" ::: "memory");
+    wait_counter(ctr, target, wc);
 }
 
 // The arrival half of prep_barrier, for a wave that has other work to issue
@@ -143,14 +170,16 @@ __device__ __forceinline__ void prep_arrive(unsigned *ctr, unsigned &target) {
 }
 
 // Wait until ctr[0] >= t0 and ctr[1] >= t1, both read by one 8-byte LDS load
-// per poll (bounded, like prep_barrier).
-__device__ __forceinline__ void wait_two(const unsigned *ctr, unsigned t0, unsigned t1) {
+// per poll (bounded like wait_counter).
+__device__ __forceinline__ void wait_two(const unsigned *ctr, unsigned t0, unsigned t1, WaitCtl &wc) {
     asm volatile("" ::: "memory");
-    for (int it = 0; it < (1 << 16); ++it) {
+    const unsigned u0 = t0 + wc.bias, u1 = t1 + wc.bias;
+    for (unsigned it = 0;; ++it) {
         const uint64_t v = __hip_atomic_load((const uint64_t *)ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         const unsigned a = (unsigned)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
         const unsigned b = (unsigned)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
-        if (a >= t0 && b >= t1) break;
+        if (a >= u0 && b >= u1) break;
+        if (it >= wc.limit) { ++wc.missed; break; }
         __builtin_amdgcn_s_sleep(1);
     }
     asm volatile("" ::: "memory");
@@ -213,13 +242,17 @@ __device__ __forceinline__ void store_o_rows(const float4v &x, rsrc_t r, uint32_
 
 // Inclusive scan of a chunk's scalar gate (lane l holds g of row l) and
 // the row factors the chunk needs, written by one wave: e^gcum, e^(gl-gcum),
-// e^gl for the chain; beta, e^(gcum_block - gcum), e^(gcum - gcum_16J) for
-// the Gram tiles.  (Within rows of 16 lanes by DPP shifts, then the row
-// totals.)
+// e^gl for the chain; beta, gcum itself, e^(gend_J - gcum) and
+// e^(gcum - gend_J) for the Gram tiles, where gend_J is gcum at the last row
+// of 16-row block J.  Every factor a product uses is at most 1 for any g <= 0:
+// an off-diagonal tile (I > J) splits its decay e^(gcum_r - gcum_s) at the
+// boundary after block J, which lies between r and s; a diagonal tile takes
+// the decay of each entry directly (gate_decay_diag).  (Within rows of 16
+// lanes by DPP shifts, then the row totals.)
 template <int C>
 __device__ __forceinline__ void gate_factors(float g_own, float b_own, float *eg, float *bet) {
     constexpr int NB = C / 16;
-    float *egl = eg + C, *einv = bet + C, *efac = bet + 2 * C;
+    float *egl = eg + C, *einv = bet + C, *efac = bet + 2 * C, *gcp = bet + (2 + NB) * C;
     const int l = lane_id();
     float x = l < C ? g_own : 0.f;
     x += dpp_row_shr<0x111>(x);
@@ -231,34 +264,38 @@ __device__ __forceinline__ void gate_factors(float g_own, float b_own, float *eg
     const float t2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
     const int rw = l >> 4;
     x += (rw >= 1 ? t0 : 0.f) + (rw >= 2 ? t1 : 0.f) + (rw >= 3 ? t2 : 0.f);
-    float gblk[NB];
+    float gend[NB];
 #pragma unroll
-    for (int J = 0; J < NB; ++J) gblk[J] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16 * J));
-    const float gl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), C - 1));
+    for (int J = 0; J < NB; ++J) gend[J] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16 * J + 15));
+    const float gl = gend[NB - 1];
     if (l < C) {
         eg[l] = fast_exp(x);
         egl[l] = fast_exp(gl - x);
         bet[l] = b_own;
-        float gref = gblk[0];
+        gcp[l] = x;
+        float gref = gend[0];
 #pragma unroll
         for (int J = 1; J < NB; ++J)
-            if ((l >> 4) == J) gref = gblk[J];
+            if ((l >> 4) == J) gref = gend[J];
         einv[l] = fast_exp(gref - x);
+        // (rows of block J and before get a growth factor here, which no
+        // product reads: efac[J] multiplies rows of later blocks only)
 #pragma unroll
-        for (int J = 0; J < NB; ++J) efac[J * C + l] = fast_exp(x - gblk[J]);
+        for (int J = 0; J < NB; ++J) efac[J * C + l] = fast_exp(fminf(x - gend[J], 0.f));
     }
     if (l == 0) eg[2 * C] = fast_exp(gl);
 }
 
-// Wait until an LDS counter reaches target (bounded, like prep_barrier).
-__device__ __forceinline__ void wait_counter(const unsigned *ctr, unsigned target) {
-    asm volatile("" ::: "memory");
-    for (int it = 0; it < (1 << 16); ++it) {
-        const unsigned v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if ((unsigned)__builtin_amdgcn_readfirstlane((int)v) >= target) break;
-        __builtin_amdgcn_s_sleep(1);
-    }
-    asm volatile("" ::: "memory");
+// The decays e^(gcum_r - gcum_s) of a diagonal Gram tile entry by entry, for
+// row r against the columns s0 .. s0+3 (1 where s > r: those entries are
+// masked out).
+__device__ __forceinline__ float4v gate_decay_diag(const float *gcp, int r, int s0) {
+    const float gr = gcp[r];
+    const float4v gs = *(const float4v *)(gcp + s0);
+    float4v f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = fast_exp(fminf(gr - gs[e], 0.f));
+    return f;
 }
 
 // Count one arrival on an LDS counter once this wave's LDS writes are done.
@@ -313,9 +350,10 @@ struct PipeLayout {
     // chain-side row factors per slot: e^gcum, e^(gl - gcum), e^gl
     static constexpr int kRowCN = 2 * C + 4;
     static constexpr int kRowC = kTr + NB * 512;         // [2][kRowCN]
-    // prepare-side row factors: beta, e^(gcum_block0 - gcum), e^(gcum - gcum_16J)
-    static constexpr int kRowP = kRowC + 2 * kRowCN * 4; // [C + C + NB C]
-    static constexpr int kSync = kRowP + (2 * C + NB * C) * 4;
+    // prepare-side row factors: beta, e^(gend_J(s) - gcum_s), e^(gcum - gend_J),
+    // gcum (gend_J: gcum at the last row of block J)
+    static constexpr int kRowP = kRowC + 2 * kRowCN * 4; // [C + C + NB C + C]
+    static constexpr int kSync = kRowP + (3 * C + NB * C) * 4;
     static constexpr int kBytes = kSync + 16;
     static_assert(kSync % 8 == 0, "the two sync counters are read as one 8-byte word");
 };
@@ -349,7 +387,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
     _Float16 *Tr = (_Float16 *)(smem + L::kTr);
     float *rowC = (float *)(smem + L::kRowC);
     float *bet = (float *)(smem + L::kRowP);
-    float *einv = bet + C, *efac = bet + 2 * C;
+    float *einv = bet + C, *efac = bet + 2 * C, *gcp = bet + (2 + NB) * C;
     unsigned *sync_ctr = (unsigned *)(smem + L::kSync);
 
     const int wv = wave_id(), l = lane_id(), tid = threadIdx.x;
@@ -361,6 +399,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
     const int nt = (T + C - 1) / C;
     const int64_t row0 = sr.row0;
     const uint32_t rsK = (uint32_t)(H * K), rsV = (uint32_t)(H * V);
+    WaitCtl wc{p.wait_count, p.wait_limit, p.wait_bias, 0u};
 
     // the operand tiles above the diagonal are read but stay zero
     for (int i = tid; i < 2 * C * C; i += kPipeThreads) {
@@ -464,7 +503,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                         Hhi[swz<64>(row, col)] = hb;
                         Hlo[swz<64>(row, col)] = f32_to_bf16_bits(hacc[i][r] - __uint_as_float((uint32_t)hb << 16));
                     }
-                prep_barrier(sync_ctr + 2, chain_target);
+                prep_barrier(sync_ctr + 2, chain_target, wc);
                 constexpr int NKW = K / 64;                  // 16-row key tiles per wave
                 float4v dq[NB][NKW];
 #pragma unroll
@@ -609,6 +648,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                 for (int r = 0; r < 4; ++r)
                     p.hT[((int64_t)pair * K + 16 * i + g4 + r) * V + vcol] = hacc[i][r];
         }
+        wait_report(wc);
     } else {
         // =====================  prepare waves  ===========================
         // The prepare is the longer of the two roles per chunk: its waves
@@ -684,16 +724,19 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
             prep_arrive(sync_ctr, sync_target);
             if (n + 1 < nt) issue_loads(n + 1);
             // every prepare wave's q/k rows and chunk n's row factors are in
-            wait_two(sync_ctr, sync_target, (unsigned)(n + 1));
+            wait_two(sync_ctr, sync_target, (unsigned)(n + 1), wc);
 
             // ---- Gram tiles.  Tile (I, J) of a P or A block, with its decay
-            // e^(gcum_r - gcum_s) = efac[J][r] einv[s] (and beta_r for A), in
-            // row layout (lane (g, n): row 16 I + n, columns 16 J + 4g + e)
-            // or col layout (rows 16 I + 4g + e, column 16 J + n).
+            // e^(gcum_r - gcum_s) (and beta_r for A): off the diagonal
+            // efac[J][r] einv[s], split at the end of block J; on it entry by
+            // entry.  Row layout (lane (g, n): row 16 I + n, columns
+            // 16 J + 4g + e) or col layout (rows 16 I + 4g + e, column
+            // 16 J + n).
             auto fac_row = [&](int I, int J, bool isA, const float4v &acc) {
                 const int r = 16 * I + (l & 15), s0 = 16 * J + 4 * (l >> 4);
-                const float fr = efac[J * C + r] * (isA ? bet[r] : 1.f);
-                const float4v fs = *(const float4v *)(einv + s0);
+                const float fr = isA ? bet[r] : 1.f;
+                const float4v fs = I == J ? gate_decay_diag(gcp, r, s0)
+                                          : *(const float4v *)(einv + s0) * efac[J * C + r];
                 float4v a;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) a[e] = (isA ? s0 + e < r : s0 + e <= r) ? acc[e] * fs[e] * fr : 0.f;
@@ -829,7 +872,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
             if constexpr (NB == 4) {
                 // Mn_20, Mn_21, Mn_30, Mn_31 (prepare wave pw takes A block pw):
                 // T_22 and T_33 come from wave 1, the A blocks from waves 2, 3
-                prep_barrier(sync_ctr, sync_target);
+                prep_barrier(sync_ctr, sync_target, wc);
                 const int i = 2 + (pw >> 1);
                 put_mn(i, pw & 1, *(const half8 *)(Asp + pw * 512 + 8 * l), *(const half4 *)(Tr + i * 256 + 4 * l));
             }
@@ -844,6 +887,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
             if (c + 1 < nt) prepare(c + 1);
             wg_barrier();
         }
+        wait_report(wc);
     }
 }
 

@@ -25,8 +25,7 @@ gdn_status enqueue_forward_pipe(int C, int K, bool o_f32, FwdParams &fp, int gri
     const bool st = fp.hck != nullptr;
     if (C == 32) {
         if (st) return enqueue_forward_pipe_c32_states(K, o_f32, fp, grid, s);
-        return K == 64 ? pipe_o<32, 64, false>(o_f32, fp, grid, s)
-                       : enqueue_forward_pipe_c32k128(o_f32, fp, grid, s);
+        return enqueue_forward_pipe_c32(K, o_f32, fp, grid, s);
     }
     if (st) return K == 64 ? pipe_o<64, 64, true>(o_f32, fp, grid, s)
                            : pipe_o<64, 128, true>(o_f32, fp, grid, s);

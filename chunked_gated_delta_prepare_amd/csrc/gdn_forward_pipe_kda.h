@@ -97,6 +97,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
     const int nt = (T + C - 1) / C;
     const int64_t row0 = sr.row0;
     const uint32_t rsK = (uint32_t)(H * K), rsV = (uint32_t)(H * V);
+    WaitCtl wc{p.wait_count, p.wait_limit, p.wait_bias, 0u};
 
     // the operand tiles above the diagonal are read but stay zero
     for (int i = tid; i < 2 * C * C; i += kPipeThreads) {
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
                 for (int cb = 0; cb < NB; ++cb)
                     dof[s][cb] = __builtin_bit_cast(bf16x8, bload128(rdo_, do_off + 32 * s * SIO,
                                                                      (t0 + 16 * cb) * rsV * SIO));
-            prep_barrier(sync_ctr + 2, chain_target);        // every chain wave is past its reads
+            prep_barrier(sync_ctr + 2, chain_target, wc);        // every chain wave is past its reads
 #pragma unroll
             for (int i = 0; i < NKB; ++i)
 #pragma unroll
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
                     Hhi[swz<64>(row, col)] = hb;
                     Hlo[swz<64>(row, col)] = f32_to_bf16_bits(hacc[i][r] - __uint_as_float((uint32_t)hb << 16));
                 }
-            prep_barrier(sync_ctr + 2, chain_target);
+            prep_barrier(sync_ctr + 2, chain_target, wc);
             constexpr int NKW = K / 64;                      // 16-row key tiles per wave
             float4v dq[NB][NKW];
 #pragma unroll
@@ -303,6 +304,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
                 for (int r = 0; r < 4; ++r)
                     p.hT[((int64_t)pair * K + 16 * i + g4 + r) * V + vcol] = hacc[i][r];
         }
+        wait_report(wc);
     } else {
         // =====================  prepare waves  ===========================
         // (unlike the scalar-gate kernel, these keep the default wave
@@ -374,7 +376,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
 #pragma unroll
             for (int i = 0; i < NR; ++i) { run += rg[i]; rg[i] = run; }
             *(float4v *)(segt + seg * K + kc) = run;
-            prep_barrier(sync_ctr, sync_target);
+            prep_barrier(sync_ctr, sync_target, wc);
             // segment offsets in segment order; gcum at the middle row (the
             // end of segment C/2/NR - 1) and at the last row
             float4v off = {0, 0, 0, 0}, gm = {0, 0, 0, 0}, gl = {0, 0, 0, 0};
@@ -424,7 +426,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
             }
             prep_arrive(sync_ctr, sync_target);
             // every prepare wave's operand rows (and beta) are in
-            wait_counter(sync_ctr, sync_target);
+            wait_counter(sync_ctr, sync_target, wc);
 
             // ---- Gram tiles.  A = diag(beta) k~ k^^T and P = q~ k^^T need no
             // decay factor; A tiles get beta of their rows and the strict
@@ -568,7 +570,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
             if constexpr (NB == 4) {
                 // Mn_20, Mn_21, Mn_30, Mn_31 (prepare wave pw takes A block pw):
                 // T_22 and T_33 come from wave 1, the A blocks from waves 2, 3
-                prep_barrier(sync_ctr, sync_target);
+                prep_barrier(sync_ctr, sync_target, wc);
                 const int i = 2 + (pw >> 1);
                 put_mn(i, pw & 1, *(const half8 *)(Asp + pw * 512 + 8 * l), *(const half4 *)(Tr + i * 256 + 4 * l));
             }
@@ -585,6 +587,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
             if (c + 1 < nt) prepare(c + 1);
             wg_barrier();
         }
+        wait_report(wc);
     }
 }
 

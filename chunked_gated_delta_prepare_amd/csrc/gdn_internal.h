@@ -7,6 +7,12 @@
 
 namespace gdn {
 
+// Device address of this device's count of bounded LDS waits that gave up
+// (NULL if it cannot be looked up), and the poll limit and target bias the
+// pipelined kernels take (normal: 2^16 polls, bias 0).
+unsigned *wait_count_ptr();
+void wait_params(unsigned &limit, unsigned &bias);
+
 // Launch a kernel with one by-value parameter struct (256 threads per block
 // unless stated).
 gdn_status launch_kernel(const void *fn, int grid, void *params, hipStream_t s,
@@ -43,7 +49,7 @@ gdn_status enqueue_forward_pipe_varlen_c64(int K, bool o_f32, FwdParams &fp, int
 // key dim K and fp32 (else bf16) output.
 gdn_status enqueue_forward_pipe(int C, int K, bool o_f32, FwdParams &fp, int grid,
                                 hipStream_t s);
-gdn_status enqueue_forward_pipe_c32k128(bool o_f32, FwdParams &fp, int grid, hipStream_t s);
+gdn_status enqueue_forward_pipe_c32(int K, bool o_f32, FwdParams &fp, int grid, hipStream_t s);
 // The pipelined kernel for the per-key gate (plain, ST or VL by fp.hck / fp.cu).
 gdn_status enqueue_forward_pipe_kda(int C, int K, bool o_f32, FwdParams &fp, int grid,
                                     hipStream_t s);

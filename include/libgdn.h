@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -231,6 +231,25 @@ gdn_status gdn_forward_varlen(const gdn_problem *problem, const int32_t *cu_seql
                               int64_t n_seqs, const void *q, const void *k, const void *v,
                               const float *beta, const float *g, const float *h0, void *o,
                               float *hT, void *stream);
+
+/*
+ * gdn_wait_timeouts -- diagnostics of the bf16-io kernels' internal waits.
+ * Inside a workgroup, the waves that prepare a chunk and the waves that scan
+ * the previous one hand tiles over through LDS counters.  Every such wait is
+ * bounded (2^16 polls, a few milliseconds): a wait that runs out lets the
+ * wave go on instead of hanging the GPU, and adds one to a per-device count.
+ * A launch during which the count grew has results that must not be
+ * trusted.  This call stores the current device's count in *count and, if
+ * `reset` is nonzero, sets it back to zero.  Unlike every other entry point
+ * it is synchronous: it copies from device memory with hipMemcpy, so it
+ * waits for the device's outstanding work.  Returns GDN_ERR_NULL_ARG for a
+ * NULL count and GDN_ERR_HIP if the device word cannot be read.
+ * (Setting the environment variable GDN_WAIT_FORCE_TIMEOUT=1 before a
+ * launch makes every such wait give up after a few polls: a test of this
+ * path only; the results of that launch are garbage, and every kernel still
+ * ends normally.)
+ */
+gdn_status gdn_wait_timeouts(uint32_t *count, int reset);
 
 /* Workspace gdn_forward needs for this problem (0 if none); 0 on bad args. */
 size_t gdn_workspace_bytes(const gdn_problem *problem);

@@ -37,7 +37,7 @@ def test_header_declares_the_boundary():
     assert _declared_functions() == sorted(
         ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_forward_states",
          "gdn_forward_varlen", "gdn_rescan_dq", "gdn_chunk_dq", "gdn_workspace_bytes",
-         "gdn_status_str", "gdn_abi_version"])
+         "gdn_status_str", "gdn_abi_version", "gdn_wait_timeouts"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -242,3 +242,8 @@ def test_fp32_key_gate_k128_chunk64_reports_the_lds_budget(lib, gdn):
     assert _fwd(lib, pr) == 5
     assert _fwd_states(lib, pr) == 5
     assert _fwd_varlen(lib, _problem(gdn, B=1, io=0, o=0, gate=1, K=128, V=128, chunk=64)) == 5
+
+
+def test_wait_timeouts_rejects_null(lib, gdn):
+    # validated before the device word is touched: no GPU needed
+    assert lib.gdn_wait_timeouts(None, 0) == 1
