@@ -182,8 +182,9 @@ def main():
     tdt = {"bf16": torch.bfloat16, "fp32": torch.float32}[o_dtype]
     o = torch.empty(w.B, w.T, w.H, w.V, device=dev, dtype=tdt)
     hT = torch.empty(w.B, w.H, w.K, w.V, device=dev, dtype=torch.float32)
-    # the fused forward needs no workspace (gdn_workspace_bytes is 0); a
-    # nonzero size would be allocated here, outside the timed region
+    # the scalar gate's fused forward needs no workspace; the per-key gate's
+    # Gram stage writes its triangular factors into one, allocated here,
+    # outside the timed region
     ws_bytes = gdn.workspace_bytes(w.B, w.T, w.H, w.K, w.V, w.chunk,
                                    {"bf16": torch.bfloat16, "fp32": torch.float32}[w.io],
                                    w.gate == "key", tdt)
@@ -277,8 +278,11 @@ def main():
           file=sys.stderr, flush=True)
     del flush
 
-    # ---- the dominant (and only) kernel: a step is one launch of the fused
-    # forward kernel, so its mean event-timed duration is ms_step
+    # ---- the dominant kernel.  Scalar gate: a step is one launch of the
+    # fused forward kernel, so its mean event-timed duration is ms_step.  Per-
+    # key gate: a step is the Gram launch then the re-scan launch on one
+    # stream; the events bracket both, so the figure is that of the pair
+    # (the kernel trace splits it)
     ms_launch = ms_step
     fbytes, fflops = forward_bytes(w, o_dtype, args.states, args.rescan), forward_flops(w)
     kname = kernel_name(w, o_dtype, args.states, args.rescan)
@@ -290,6 +294,12 @@ def main():
         fbytes, fflops = chunk_dq_bytes(w, o_dtype), 2.0 * w.B * w.T * w.H * w.K * w.V
         kname = "chunk_dq_kernel<%d, %d, %d, %s>" % (w.chunk, w.K, w.V,
                                                      {"bf16": "bf16_t", "fp32": "float"}[o_dtype])
+    launches = 1
+    if w.gate == "key" and not args.chunk_dq:
+        launches = 2
+        kname = "kda_gram_kernel<%d, %d, %s%s> + %s" % (
+            w.chunk, w.K, {"bf16": "bf16_t", "fp32": "float"}[w.io],
+            ", true" if args.varlen else ", false", kname)
     achieved = fbytes / (ms_launch * 1e-3) / 1e9
     mfma_peak = MFMA_PEAK_TFLOPS["f16" if w.io == "bf16" else "f32"]
     roofline = {"kernel": kname, "bound": "hbm",
@@ -297,7 +307,7 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": (None if args.rescan or args.chunk_dq or args.varlen
                             else measured_traffic(w, o_dtype, args.states)),
-                "ms_per_launch": round(ms_launch, 5),
+                "ms_per_launch": round(ms_launch, 5), "launches_per_step": launches,
                 "algorithmic_bytes_per_launch": fbytes,
                 "algorithmic_flops_per_launch": fflops,
                 "mfma_frac": round(fflops / (ms_launch * 1e-3) / 1e12 / mfma_peak, 4),

@@ -43,8 +43,9 @@ STATUS = {
 }
 EXPORTS = ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_forward_states",
            "gdn_forward_varlen", "gdn_rescan_dq", "gdn_chunk_dq", "gdn_workspace_bytes",
-           "gdn_status_str", "gdn_abi_version", "gdn_wait_timeouts"]
-ABI_VERSION = 6
+           "gdn_workspace_bytes_varlen", "gdn_status_str", "gdn_abi_version",
+           "gdn_wait_timeouts"]
+ABI_VERSION = 7
 
 
 class GdnError(RuntimeError):
@@ -82,15 +83,17 @@ def load_library(path: str | None = None):
         lib.gdn_prepare.argtypes = [pp] + [vp] * 8
         lib.gdn_scan.argtypes = [pp] + [vp] * 9
         lib.gdn_forward.argtypes = [pp] + [vp] * 9 + [sz, vp]
-        lib.gdn_forward_states.argtypes = [pp] + [vp] * 11
-        lib.gdn_forward_varlen.argtypes = [pp, vp, ctypes.c_int64] + [vp] * 9
-        lib.gdn_rescan_dq.argtypes = [pp] + [vp] * 12
+        lib.gdn_forward_states.argtypes = [pp] + [vp] * 11 + [sz, vp]
+        lib.gdn_forward_varlen.argtypes = [pp, vp, ctypes.c_int64] + [vp] * 9 + [sz, vp]
+        lib.gdn_rescan_dq.argtypes = [pp] + [vp] * 12 + [sz, vp]
         lib.gdn_chunk_dq.argtypes = [pp] + [vp] * 4
         for f in (lib.gdn_prepare, lib.gdn_scan, lib.gdn_forward, lib.gdn_forward_states,
                   lib.gdn_forward_varlen, lib.gdn_rescan_dq, lib.gdn_chunk_dq):
             f.restype = ctypes.c_int
         lib.gdn_workspace_bytes.argtypes = [pp]
         lib.gdn_workspace_bytes.restype = sz
+        lib.gdn_workspace_bytes_varlen.argtypes = [pp, ctypes.c_int64]
+        lib.gdn_workspace_bytes_varlen.restype = sz
         lib.gdn_status_str.argtypes = [ctypes.c_int]
         lib.gdn_status_str.restype = ctypes.c_char_p
         lib.gdn_abi_version.argtypes = []
@@ -241,6 +244,18 @@ def scan(q, k, w, u, gcum, chunk, h0=None, *, o_dtype=None, o=None, hT=None,
     return o, hT
 
 
+def _workspace(lib, pr, device, workspace, n_seqs=0):
+    """The workspace the call needs (gdn_workspace_bytes), allocated with
+    torch when the caller passes none; returns (tensor or None, bytes)."""
+    torch = _torch()
+    need = int(lib.gdn_workspace_bytes_varlen(ctypes.byref(pr), ctypes.c_int64(n_seqs)) if n_seqs
+               else lib.gdn_workspace_bytes(ctypes.byref(pr)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=device, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return workspace, ctypes.c_size_t(ws_bytes)
+
+
 def forward(q, k, v, beta, g, chunk, h0=None, *, o_dtype=None, o=None, hT=None,
             output_final_state=True, workspace=None, stream=None):
     """Whole forward pass: returns (o [B,T,H,V], hT [B,H,K,V] fp32 or None)."""
@@ -265,19 +280,15 @@ def forward(q, k, v, beta, g, chunk, h0=None, *, o_dtype=None, o=None, hT=None,
     if hT is not None:
         _need(hT, "hT", torch.float32, (B, H, K, V))
     pr = _problem(q, v, chunk, per_key, od)
-    need = int(lib.gdn_workspace_bytes(ctypes.byref(pr)))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _workspace(lib, pr, q.device, workspace)
     rc = lib.gdn_forward(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
-                         _ptr(h0), _ptr(o), _ptr(hT), _ptr(workspace),
-                         ctypes.c_size_t(ws_bytes), _stream(stream))
+                         _ptr(h0), _ptr(o), _ptr(hT), _ptr(workspace), ws_bytes, _stream(stream))
     _check("gdn_forward", rc)
     return o, hT
 
 
 def forward_states(q, k, v, beta, g, chunk, h0=None, *, o_dtype=None, o=None, hT=None,
-                   hck=None, vnew=None, output_final_state=True, stream=None):
+                   hck=None, vnew=None, output_final_state=True, workspace=None, stream=None):
     """Forward pass that also saves the chunk-start states and the per-token
     deltas: returns (o, hT or None, hck [B,NT,H,K,V], vnew [B,T,H,V]), with
     hck and vnew in the o dtype and NT = ceil(T / chunk)."""
@@ -311,17 +322,19 @@ def forward_states(q, k, v, beta, g, chunk, h0=None, *, o_dtype=None, o=None, hT
     pr = _problem(q, v, chunk, per_key, od)
     if T == 0:
         rc = lib.gdn_forward_states(ctypes.byref(pr), None, None, None, None, None,
-                                    _ptr(h0), None, _ptr(hT), None, None, _stream(stream))
+                                    _ptr(h0), None, _ptr(hT), None, None, None,
+                                    ctypes.c_size_t(0), _stream(stream))
     else:
+        workspace, ws_bytes = _workspace(lib, pr, q.device, workspace)
         rc = lib.gdn_forward_states(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
                                     _ptr(g), _ptr(h0), _ptr(o), _ptr(hT), _ptr(hck),
-                                    _ptr(vnew), _stream(stream))
+                                    _ptr(vnew), _ptr(workspace), ws_bytes, _stream(stream))
     _check("gdn_forward_states", rc)
     return o, hT, hck, vnew
 
 
 def forward_varlen(q, k, v, beta, g, cu_seqlens, chunk, h0=None, *, o_dtype=None, o=None,
-                   hT=None, output_final_state=True, stream=None):
+                   hT=None, output_final_state=True, workspace=None, stream=None):
     """Forward pass over packed sequences: q, k [1,T,H,K], v [1,T,H,V], beta
     [1,T,H], g [1,T,H] or [1,T,H,K]; cu_seqlens an int32 device tensor of
     N + 1 token offsets; h0 [N,H,K,V] fp32 or None.  Returns (o [1,T,H,V],
@@ -353,9 +366,10 @@ def forward_varlen(q, k, v, beta, g, cu_seqlens, chunk, h0=None, *, o_dtype=None
     if hT is not None:
         _need(hT, "hT", torch.float32, (N, H, K, V))
     pr = _problem(q, v, chunk, per_key, od)
+    workspace, ws_bytes = _workspace(lib, pr, q.device, workspace, n_seqs=N)
     rc = lib.gdn_forward_varlen(ctypes.byref(pr), _ptr(cu_seqlens), ctypes.c_int64(N),
                                 _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0),
-                                _ptr(o), _ptr(hT), _stream(stream))
+                                _ptr(o), _ptr(hT), _ptr(workspace), ws_bytes, _stream(stream))
     _check("gdn_forward_varlen", rc)
     return o, hT
 
@@ -386,7 +400,7 @@ def chunk_dq(do, hck, chunk, *, dq=None, stream=None):
 
 
 def rescan_dq(q, k, v, beta, g, do, chunk, h0=None, *, o_dtype=None, hT=None, hck=None,
-              vnew=None, dq=None, output_final_state=True, stream=None):
+              vnew=None, dq=None, output_final_state=True, workspace=None, stream=None):
     """The backward's forward re-scan with bf16 io: returns (hT or None,
     hck [B,NT,H,K,V], vnew [B,T,H,V], dq [B,T,H,K] fp32) with
     dq[t] = h_c do_t (raw, the chunk-start-state term).  g is [B,T,H] (one
@@ -423,10 +437,12 @@ def rescan_dq(q, k, v, beta, g, do, chunk, h0=None, *, o_dtype=None, hT=None, hc
     pr = _problem(q, v, chunk, per_key, od)
     if T == 0:
         rc = lib.gdn_rescan_dq(ctypes.byref(pr), None, None, None, None, None, _ptr(h0), None,
-                               _ptr(hT), None, None, None, _stream(stream))
+                               _ptr(hT), None, None, None, None, ctypes.c_size_t(0),
+                               _stream(stream))
     else:
+        workspace, ws_bytes = _workspace(lib, pr, q.device, workspace)
         rc = lib.gdn_rescan_dq(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
                                _ptr(h0), _ptr(do), _ptr(hT), _ptr(hck), _ptr(vnew), _ptr(dq),
-                               _stream(stream))
+                               _ptr(workspace), ws_bytes, _stream(stream))
     _check("gdn_rescan_dq", rc)
     return hT, hck, vnew, dq

@@ -47,6 +47,7 @@ UNITS = {
     "gdn_forward_pipe_kda.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
     "gdn_forward_pipe_dq.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
     "gdn_chunk_dq.hip": [],
+    "gdn_kda_gram.hip": [],
 }
 
 

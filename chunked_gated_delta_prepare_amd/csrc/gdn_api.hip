@@ -50,6 +50,15 @@ gdn_status check_ptrs(std::initializer_list<const void *> required,
     return GDN_OK;
 }
 
+// The workspace a forward entry point needs, checked before any launch.
+gdn_status check_workspace(const gdn_problem *pr, int64_t n_seqs, const void *ws, size_t ws_bytes) {
+    const int64_t need = kda_workspace_bytes(pr, n_seqs);
+    if (need == 0) return GDN_OK;
+    if (!ws || ws_bytes < (size_t)need) return GDN_ERR_WORKSPACE;
+    if (!aligned16(ws)) return GDN_ERR_ALIGNMENT;
+    return GDN_OK;
+}
+
 gdn_status launch(const void *fn, int grid, void *params, size_t psize, hipStream_t s) {
     (void)psize;
     return launch_kernel(fn, grid, params, s);
@@ -221,16 +230,19 @@ gdn_status gdn_scan(const gdn_problem *problem, const void *q, const void *k,
 }
 
 size_t gdn_workspace_bytes(const gdn_problem *problem) {
-    (void)problem;
-    return 0;        // the fused kernel keeps every intermediate on chip
+    if (check_problem(problem) != GDN_OK) return 0;
+    return (size_t)kda_workspace_bytes(problem, 0);
+}
+
+size_t gdn_workspace_bytes_varlen(const gdn_problem *problem, int64_t n_seqs) {
+    if (check_problem(problem) != GDN_OK || n_seqs < 1) return 0;
+    return (size_t)kda_workspace_bytes(problem, n_seqs);
 }
 
 gdn_status gdn_forward(const gdn_problem *problem, const void *q, const void *k,
                        const void *v, const float *beta, const float *g,
                        const float *h0, void *o, float *hT, void *workspace,
                        size_t workspace_bytes, void *stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     gdn_status st = check_problem(problem);
     if (st != GDN_OK) return st;
     if (problem->T == 0) {
@@ -240,15 +252,17 @@ gdn_status gdn_forward(const gdn_problem *problem, const void *q, const void *k,
     } else {
         st = check_ptrs({q, k, v, beta, g, o}, {h0, hT});
         if (st != GDN_OK) return st;
+        st = check_workspace(problem, 0, workspace, workspace_bytes);
+        if (st != GDN_OK) return st;
     }
     return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, nullptr, nullptr, nullptr, 0,
-                           (hipStream_t)stream);
+                           workspace, (hipStream_t)stream);
 }
 
 gdn_status gdn_forward_states(const gdn_problem *problem, const void *q, const void *k,
                               const void *v, const float *beta, const float *g,
                               const float *h0, void *o, float *hT, void *hck, void *vnew,
-                              void *stream) {
+                              void *workspace, size_t workspace_bytes, void *stream) {
     gdn_status st = check_problem(problem);
     if (st != GDN_OK) return st;
     if (problem->T == 0) {
@@ -257,18 +271,20 @@ gdn_status gdn_forward_states(const gdn_problem *problem, const void *q, const v
         if (st != GDN_OK) return st;
         if (!hT) return GDN_OK;
         return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, nullptr, nullptr, nullptr,
-                               0, (hipStream_t)stream);
+                               0, nullptr, (hipStream_t)stream);
     }
     st = check_ptrs({q, k, v, beta, g, o, hck, vnew}, {h0, hT});
     if (st != GDN_OK) return st;
-    return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, hck, vnew, nullptr, 0,
+    st = check_workspace(problem, 0, workspace, workspace_bytes);
+    if (st != GDN_OK) return st;
+    return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, hck, vnew, nullptr, 0, workspace,
                            (hipStream_t)stream);
 }
 
 gdn_status gdn_rescan_dq(const gdn_problem *problem, const void *q, const void *k,
                          const void *v, const float *beta, const float *g, const float *h0,
                          const void *dout, float *hT, void *hck, void *vnew, float *dq,
-                         void *stream) {
+                         void *workspace, size_t workspace_bytes, void *stream) {
     gdn_status st = check_problem(problem);
     if (st != GDN_OK) return st;
     if (problem->io_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
@@ -278,12 +294,14 @@ gdn_status gdn_rescan_dq(const gdn_problem *problem, const void *q, const void *
         if (st != GDN_OK) return st;
         if (!hT) return GDN_OK;
         return enqueue_forward(problem, q, k, v, beta, g, h0, nullptr, hT, nullptr, nullptr,
-                               nullptr, 0, (hipStream_t)stream);
+                               nullptr, 0, nullptr, (hipStream_t)stream);
     }
     st = check_ptrs({q, k, v, beta, g, dout, hck, vnew, dq}, {h0, hT});
     if (st != GDN_OK) return st;
+    st = check_workspace(problem, 0, workspace, workspace_bytes);
+    if (st != GDN_OK) return st;
     return enqueue_forward(problem, q, k, v, beta, g, h0, nullptr, hT, hck, vnew, nullptr, 0,
-                           (hipStream_t)stream, dout, dq);
+                           workspace, (hipStream_t)stream, dout, dq);
 }
 
 gdn_status gdn_chunk_dq(const gdn_problem *problem, const void *dout, const void *hck, float *dq,
@@ -303,7 +321,7 @@ gdn_status gdn_chunk_dq(const gdn_problem *problem, const void *dout, const void
 gdn_status gdn_forward_varlen(const gdn_problem *problem, const int32_t *cu_seqlens,
                               int64_t n_seqs, const void *q, const void *k, const void *v,
                               const float *beta, const float *g, const float *h0, void *o,
-                              float *hT, void *stream) {
+                              float *hT, void *workspace, size_t workspace_bytes, void *stream) {
     gdn_status st = check_problem(problem);
     if (st != GDN_OK) return st;
     if (problem->B != 1 || n_seqs < 1 || n_seqs * problem->H > (1 << 24)) return GDN_ERR_BAD_SHAPE;
@@ -317,9 +335,11 @@ gdn_status gdn_forward_varlen(const gdn_problem *problem, const int32_t *cu_seql
     } else {
         st = check_ptrs({q, k, v, beta, g, o}, {h0, hT});
         if (st != GDN_OK) return st;
+        st = check_workspace(problem, n_seqs, workspace, workspace_bytes);
+        if (st != GDN_OK) return st;
     }
     return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, nullptr, nullptr, cu_seqlens,
-                           n_seqs, (hipStream_t)stream);
+                           n_seqs, workspace, (hipStream_t)stream);
 }
 
 gdn_status gdn_wait_timeouts(uint32_t *count, int reset) {

@@ -11,9 +11,11 @@
 //                                   w or u: the KDA re-scan page's v')
 //   o     e^gcum * (q h) + P v'   P = tril_incl(q k^T * decay)
 //   h    <- e^gl h + (k * e^(gl - gcum))^T v'             (gl = last gcum)
-// For the per-key gate (KDA) every exponent is per key dimension; the decays
-// move into the operands around a reference row gm in the middle of the
-// chunk: q e^(g-gm), k e^(g-gm), k e^(gm-g), and h scaled by e^gm.
+// For the per-key gate (KDA) every exponent is per key dimension: the decays
+// move into the operands, q e^gcum and k e^gcum (for X and Y) and
+// k e^(gl - gcum) (for the state update), all decays, and the chunk's A, its
+// inverse by blocks and P (whose decays no row factor alone can carry)
+// come from kda_gram_kernel through the workspace.
 //
 // Work split.  The state update is the serial chain; each wave owns 16 of the
 // tile's 64 value columns (its slice of h, v', o), so the chain is wave-local
@@ -62,10 +64,19 @@ struct FwdParams {
     // every wait give up, which the host sets only to test this path)
     unsigned *wait_count;
     unsigned wait_limit, wait_bias;
+    // per-key gate: the workspace kda_gram_kernel filled, a slot of Tmb and P
+    // ([2][C][C], operand type) per (chunk, head), chunks of stream b from
+    // slot b * nt (fixed length) or after those of the sequences before b
+    const void *ws;
     int B, T, H, V;
     int nvt;        // V / 64
     int swizzle;
 };
+
+// Workspace slot of one (chunk, head) for the per-key gate: Tmb then P,
+// [C][C] each, in the operand type.
+template <int C>
+constexpr int64_t kda_slot_elems() { return 2 * (int64_t)C * C; }
 
 // The tokens of stream b: batch row b, [0, T) of a [B, T, H, .] layout, or
 // with VL (cu set) the packed sequence b, tokens [cu[b], cu[b+1]) of a
@@ -113,18 +124,22 @@ struct FwdLayout {
     static constexpr int kSk = kSq + (kStage ? C * K * 2 : 0);
     static constexpr int kVs = kSk + (kStage ? C * K * 2 : 0);
     static constexpr int kScr = kVs + (kStage ? 2 * C * LDV * 2 : 0);
-    // scratch: fp32 A and Tm of the inverse; for KDA the fp32 gcum rows
-    // [C][K] in phase 0, before the Gram needs the space
+    // scratch: GDN, fp32 A and Tm of the inverse; KDA, the fp32 gcum rows
+    // [C][K] of phase 0 (the KDA chunk's A, inverse and P come from the
+    // workspace).  Where that would not fit, the gcum rows share the Tmb / P
+    // tiles, which phase 0 fills only after the operands are built.
     static constexpr int kA = kScr;
     static constexpr int kTm = kA + C * LDA * 4;
-    static constexpr int kGst = kScr;
-    static constexpr int kScrBytes0 = 2 * C * LDA * 4;
-    static constexpr int kScrBytes = (KEYGATE && C * K * 4 > kScrBytes0) ? C * K * 4 : kScrBytes0;
+    static constexpr int kRowN = KEYGATE ? (C + 2 * K + (kThreads * 4 / K) * K) : (5 * C + NB * C + 4);
+    static constexpr int kGBytes = C * K * 4;
+    static constexpr bool kAliasG = KEYGATE && kScr + kGBytes + kRowN * 4 > kLdsBytesMax &&
+                                    2 * C * LDC * E >= kGBytes;
+    static constexpr int kGst = kAliasG ? kTmb : kScr;
+    static constexpr int kScrBytes = KEYGATE ? (kAliasG ? 0 : kGBytes) : 2 * C * LDA * 4;
     // per-row / per-key fp32 factors
     static constexpr int kRow = kScr + kScrBytes;
     // KDA cumsum segments: a thread holds 4 key columns of C / NSEG rows
     static constexpr int NSEG = kThreads * 4 / K;
-    static constexpr int kRowN = KEYGATE ? (C + 5 * K + NSEG * K) : (5 * C + NB * C + 4);
     static constexpr int kBytes = kRow + kRowN * 4;
 };
 
@@ -215,9 +230,9 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
     static_assert(NB == 2 || NB == 4, "chunk 32 or 64");
 
     __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
-    OpT *Qs = (OpT *)(smem + L::kQ);      // GDN q; KDA q e^(g - gm)
-    OpT *Ks = (OpT *)(smem + L::kK);      // GDN k; KDA k e^(g - gm)
-    OpT *Ki = KEYGATE ? (OpT *)(smem + L::kKi) : Ks;   // KDA k e^(gm - g)
+    OpT *Qs = (OpT *)(smem + L::kQ);      // GDN q; KDA q e^gcum
+    OpT *Ks = (OpT *)(smem + L::kK);      // GDN k; KDA k e^gcum
+    OpT *Ki = KEYGATE ? (OpT *)(smem + L::kKi) : Ks;   // KDA k e^(gl - gcum)
     OpT *Tmb = (OpT *)(smem + L::kTmb);
     OpT *Ps = (OpT *)(smem + L::kP);
     uint16_t *Sq = (uint16_t *)(smem + L::kSq);
@@ -231,8 +246,7 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
     float *gcv = rowf, *eg = rowf + C, *egl = rowf + 2 * C, *bet = rowf + 3 * C;
     float *einv = rowf + 4 * C, *efac = rowf + 5 * C, *misc = rowf + 5 * C + NB * C;
     // KDA key factors (beta takes the first C slots)
-    float *kbet = rowf, *gmv = rowf + C, *fsv = rowf + C + K, *flv = rowf + C + 2 * K;
-    float *fmv = rowf + C + 3 * K, *glv = rowf + C + 4 * K, *segt = rowf + C + 5 * K;
+    float *kbet = rowf, *flv = rowf + C, *glv = rowf + C + K, *segt = rowf + C + 2 * K;
     float *betp = KEYGATE ? kbet : bet;
 
     const int wv = wave_id(), l = lane_id(), tid = threadIdx.x;
@@ -245,6 +259,20 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
     const int T = sr.T, H = p.H, V = p.V;
     const int vcol = vt * 64 + 16 * wv + acc_col();          // this lane's value column
     const int nt = (T + C - 1) / C;
+    // per-key gate: this stream's first workspace slot (chunk n: slot0 + n)
+    int slot0 = 0;
+    if constexpr (KEYGATE) {
+        if constexpr (VL) {
+            for (int m = 0; m < b; ++m) {
+                const int c0 = __builtin_amdgcn_readfirstlane(p.cu[m]);
+                const int c1 = __builtin_amdgcn_readfirstlane(p.cu[m + 1]);
+                const int bos = min(max(c0, 0), p.T), eos = min(max(c1, bos), p.T);
+                slot0 += (eos - bos + C - 1) / C;
+            }
+        } else {
+            slot0 = b * nt;
+        }
+    }
 
     // ---- buffer descriptors: each covers this (b, h) stream up to token T
     const int64_t row0 = sr.row0;
@@ -430,7 +458,10 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
                 // at the end of block J, einv[s] = e^(gend_J - gcum_s) and
                 // efac[J][r] = e^(gcum_r - gend_J); diagonal tiles take each
                 // entry's decay from gcum directly.
-                const float gl = __shfl(x, C - 1);
+                // gl: gcum at the chunk's last token (not a padded row's,
+                // which the scan sums in another order), so that token's
+                // e^(gl - gcum) is exactly 1
+                const float gl = __shfl(x, min(C, T - (int)t0) - 1);
                 const float gref = __shfl(x, l | 15);       // gcum at the end of l's block
                 float ef[NB];
 #pragma unroll
@@ -456,26 +487,21 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
             for (int i = 0; i < NR; ++i) { run += gk4[i]; gk4[i] = run; }
             *(float4v *)(segt + kseg * K + kcol) = run;
             __syncthreads();
-            float4v off = {0, 0, 0, 0};
+            // (gl, the chunk total, sums the segment totals in the same
+            // order as the offsets, so it equals gcum at the last token)
+            float4v off = {0, 0, 0, 0}, gtot = {0, 0, 0, 0};
 #pragma unroll
-            for (int sgi = 0; sgi < L::NSEG; ++sgi)
-                if (sgi < kseg) off += *(const float4v *)(segt + sgi * K + kcol);
-            constexpr int MROW = C / 2 - 1;
-#pragma unroll
-            for (int i = 0; i < NR; ++i) {
-                const int row = kseg * NR + i;
-                const float4v gg = gk4[i] + off;
-                *(float4v *)(Gst + row * K + kcol) = gg;
-                if (row == MROW) *(float4v *)(gmv + kcol) = gg;
-                if (row == C - 1) *(float4v *)(glv + kcol) = gg;
+            for (int sgi = 0; sgi < L::NSEG; ++sgi) {
+                const float4v t = *(const float4v *)(segt + sgi * K + kcol);
+                if (sgi < kseg) off += t;
+                gtot += t;
             }
+#pragma unroll
+            for (int i = 0; i < NR; ++i)
+                *(float4v *)(Gst + (kseg * NR + i) * K + kcol) = off + gk4[i];
+            if (kseg == 0) *(float4v *)(glv + kcol) = gtot;
             __syncthreads();
-            if (tid < K) {
-                const float gm = gmv[tid], gl = glv[tid];
-                fsv[tid] = fast_exp(gm);
-                flv[tid] = fast_exp(gl);
-                fmv[tid] = fast_exp(gl - gm);
-            }
+            if (tid < K) flv[tid] = fast_exp(glv[tid]);
 #pragma unroll
             for (int j = 0; j < NVEC; ++j) {
                 const int i = tid + kThreads * j, row = i / (K / 8), col = 8 * (i % (K / 8));
@@ -490,10 +516,11 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
                     unpack_raw8(rq[j], xq);
                     unpack_raw8(rk[j], xk);
                 }
+                // qd = q e^gcum, kd = k e^gcum, kg = k e^(gl - gcum): decays
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float d = Gst[row * K + col + e] - gmv[col + e];
-                    const float up = fast_exp(d), dn = fast_exp(-d);
+                    const float gr = Gst[row * K + col + e];
+                    const float up = fast_exp(gr), dn = fast_exp(glv[col + e] - gr);
                     a[e] = xq[e] * up;
                     bq[e] = xk[e] * up;
                     bk[e] = xk[e] * dn;
@@ -514,6 +541,19 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
             if constexpr (!L::kStage)
                 if (c + 1 < nt) load_chunk(c + 1, kLdAll);
             __syncthreads();
+            // this chunk's Tmb and P, formed by kda_gram_kernel, from the
+            // workspace (their tiles may have held the gcum rows until the
+            // barrier above)
+            {
+                const OpT *src = (const OpT *)p.ws + ((int64_t)(slot0 + c) * H + h) * kda_slot_elems<C>();
+                constexpr int PER = 16 / L::E;
+                for (int i = tid; i < 2 * C * C / PER; i += kThreads) {
+                    const int e0 = i * PER, tile = e0 / (C * C), rc = e0 % (C * C);
+                    const u32x4 w = *(const u32x4 *)(src + e0);
+                    *(u32x4 *)((tile ? Ps : Tmb) + (rc / C) * LDC + rc % C) = w;
+                }
+            }
+            __syncthreads();
         }
 
         // ================= phase 1: Gram, diagonal inverses, first solve block
@@ -525,7 +565,8 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
         // Tile (I, J) is computed transposed (rows s of block J against rows
         // r of block I), so lane (l/16, j) ends up with row r = 16 I + j and
         // four consecutive columns s = 16 J + 4 (l/16) + e: one vector store.
-        {
+        // (The per-key gate has its A, inverse and P from the workspace.)
+        if constexpr (!KEYGATE) {
             auto gram_put = [&](int I, int J, bool isA, const float4v &acc) {
                 const int r = 16 * I + acc_col(), s0 = 16 * J + g4;
                 float4v fac = {1.f, 1.f, 1.f, 1.f};
@@ -648,7 +689,7 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
         // ================= phase 2: remaining solve blocks (C = 64) ==========
         if constexpr (L::kStage && kLdP2 != 0)
             if (c + 1 < nt) load_chunk(c + 1, kLdP2);
-        if constexpr (NB == 4) {
+        if constexpr (NB == 4 && !KEYGATE) {
             // Mn_20, Mn_21, Mn_30, Mn_31: T_22 and T_33 from the pair waves,
             // the A blocks from the tile waves
             solve_block<LDA, LDC, OpT>(Af, Tmf, Tmb, 2 + (wv >> 1), wv & 1);
@@ -679,18 +720,10 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
                 }
                 el = misc[0];
             }
-            // h as B fragments over the key dimension (KDA: rows scaled by
-            // e^gm, the reference of the q and k operands)
+            // h as B fragments over the key dimension
             typename M::frag hf[K / 32];
 #pragma unroll
-            for (int s = 0; s < K / 32; ++s) {
-                float4v lo = hacc[2 * s], hi = hacc[2 * s + 1];
-                if constexpr (KEYGATE) {
-                    lo = lo * *(const float4v *)(fsv + 32 * s + g4);
-                    hi = hi * *(const float4v *)(fsv + 32 * s + 16 + g4);
-                }
-                hf[s] = fragB_acc(lo, hi, OpT{});
-            }
+            for (int s = 0; s < K / 32; ++s) hf[s] = fragB_acc(hacc[2 * s], hacc[2 * s + 1], OpT{});
             // X = k h, Y = q h for this wave's 16 columns
             float4v xa[NB], ya[NB];
 #pragma unroll
@@ -775,16 +808,14 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
                         M::mma(hacc[i], fragAT_split(Ks, LDK, 16 * i, 32 * s), df[s]);
                 }
             } else {
-                // h = e^gl h + e^(gl - gm) (k e^(gm - g))^T v'
+                // h = e^gl h + (k e^(gl - gcum))^T v', the decay row-wise
 #pragma unroll
                 for (int i = 0; i < NKB; ++i) {
                     float4v acc = {0, 0, 0, 0};
 #pragma unroll
                     for (int s = 0; s < C / 32; ++s)
                         M::mma(acc, fragAT_split(Ki, LDK, 16 * i, 32 * s), df[s]);
-                    const float4v fl = *(const float4v *)(flv + 16 * i + g4);
-                    const float4v fm = *(const float4v *)(fmv + 16 * i + g4);
-                    hacc[i] = fl * hacc[i] + fm * acc;
+                    hacc[i] = *(const float4v *)(flv + 16 * i + g4) * hacc[i] + acc;
                 }
             }
         }

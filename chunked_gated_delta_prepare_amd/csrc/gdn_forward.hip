@@ -16,19 +16,31 @@ static bool fits_32bit_streams(const gdn_problem *pr) {
     const int64_t gdim = pr->gate == GDN_GATE_KEY ? pr->K : 1;
     const int64_t worst = std::max({th * pr->K * sio, th * pr->V * sio, th * pr->V * so,
                                     th * gdim * 4});
-    return worst < ((int64_t)1 << 32);
+    // per-key gate: one stream's workspace slots for all heads
+    const int64_t nt = (pr->T + pr->chunk - 1) / pr->chunk;
+    const int64_t ws = pr->gate == GDN_GATE_KEY ? nt * pr->H * 2 * (int64_t)pr->chunk * pr->chunk * sio : 0;
+    return worst < ((int64_t)1 << 32) && ws < ((int64_t)1 << 32);
 }
 
 gdn_status enqueue_forward(const gdn_problem *pr, const void *q, const void *k,
                            const void *v, const float *beta, const float *g,
                            const float *h0, void *o, float *hT, void *hck, void *vnew,
-                           const int32_t *cu, int64_t n_seqs, hipStream_t s,
+                           const int32_t *cu, int64_t n_seqs, void *ws, hipStream_t s,
                            const void *dout, float *dq) {
     if (!fits_32bit_streams(pr)) return GDN_ERR_UNSUPPORTED;
+    // the re-scan with dq is a pipelined kernel only (bf16 io): refused
+    // before anything is enqueued
+    if (dq && (pr->io_dtype != GDN_BF16 || pipe_disabled())) return GDN_ERR_UNSUPPORTED;
+    // per-key gate: the chunks' exact Gram products and triangular factors
+    // first, all chunks at once, into the workspace the re-scan reads
+    if (pr->gate == GDN_GATE_KEY && pr->T > 0) {
+        const gdn_status st = enqueue_kda_gram(pr, q, k, beta, g, ws, cu, n_seqs, s);
+        if (st != GDN_OK) return st;
+    }
     FwdParams fp;
     fp.q = q; fp.k = k; fp.v = v; fp.beta = beta; fp.g = g; fp.h0 = h0;
     fp.o = o; fp.hT = hT; fp.hck = hck; fp.vnew = vnew; fp.cu = cu;
-    fp.dout = dout; fp.dq = dq;
+    fp.dout = dout; fp.dq = dq; fp.ws = ws;
     fp.wait_count = wait_count_ptr();
     wait_params(fp.wait_limit, fp.wait_bias);
     // packed sequences: one stream per sequence over the [1, T, H, .] tensors

@@ -249,8 +249,12 @@ __device__ __forceinline__ void store_o_rows(const float4v &x, rsrc_t r, uint32_
 // boundary after block J, which lies between r and s; a diagonal tile takes
 // the decay of each entry directly (gate_decay_diag).  (Within rows of 16
 // lanes by DPP shifts, then the row totals.)
+// nvalid is the chunk's number of tokens (C except in a short last chunk):
+// gl is gcum at its last token, so that e^(gl - gcum) of that token is
+// exactly 1 (the padded rows' gcum, summed in another order by the scan,
+// can differ from it by an ulp of |gcum|).
 template <int C>
-__device__ __forceinline__ void gate_factors(float g_own, float b_own, float *eg, float *bet) {
+__device__ __forceinline__ void gate_factors(float g_own, float b_own, float *eg, float *bet, int nvalid) {
     constexpr int NB = C / 16;
     float *egl = eg + C, *einv = bet + C, *efac = bet + 2 * C, *gcp = bet + (2 + NB) * C;
     const int l = lane_id();
@@ -267,7 +271,7 @@ __device__ __forceinline__ void gate_factors(float g_own, float b_own, float *eg
     float gend[NB];
 #pragma unroll
     for (int J = 0; J < NB; ++J) gend[J] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16 * J + 15));
-    const float gl = gend[NB - 1];
+    const float gl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), nvalid - 1));
     if (l < C) {
         eg[l] = fast_exp(x);
         egl[l] = fast_exp(gl - x);
@@ -458,7 +462,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
         };
         if (wv == 0 && nt > 0) {
             gload(0);
-            gate_factors<C>(g_nx, b_nx, rowC, bet);
+            gate_factors<C>(g_nx, b_nx, rowC, bet, min(C, T));
             signal_counter(sync_ctr + 1);
             if (nt > 1) gload(1);
         }
@@ -473,7 +477,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
             const float *eg = rowC + slot * L::kRowCN, *egl = eg + C;
             const uint32_t t0 = (uint32_t)(c * C);
             if (wv == 0 && c + 1 < nt) {
-                gate_factors<C>(g_nx, b_nx, rowC + (slot ^ 1) * L::kRowCN, bet);
+                gate_factors<C>(g_nx, b_nx, rowC + (slot ^ 1) * L::kRowCN, bet, min(C, T - (c + 1) * C));
                 signal_counter(sync_ctr + 1);
                 if (c + 2 < nt) gload(c + 2);
             }

@@ -1,55 +1,53 @@
 // gdn_forward for the per-key gate (Kimi-Delta-Attention), pipelined over
 // chunks like forward_pipe_kernel (gdn_forward_pipe.h), bf16 io.
 //
-// The per-chunk algebra is the four-wave kernel's KDA form (gdn_forward.h):
-// the decays move into the operands around the chunk's middle row gm,
-//     q~ = q e^(gcum - gcum_gm),  k~ = k e^(gcum - gcum_gm),
-//     k^ = k e^(gcum_gm - gcum)                      (per key column),
-// so that A = strict_lower(diag(beta) k~ k^^T), P = tril_incl(q~ k^^T), and
-// the re-scan of the kernel-fun KDA re-scan page becomes
-//     X = k~ (e^gcum_gm h),  Y = q~ (e^gcum_gm h),  R' = v - X,
-//     v' = (I + A)^-1 diag(beta) R'   (by blocks of 16 tokens, as there),
-//     o = Y + P v',  h <- e^gl h + e^(gl - gcum_gm) (k^^T v')   (row-wise).
+// The chunk's decayed Gram products, its triangular solve blocks and P come
+// from kda_gram_kernel (gdn_kda_gram.h), which forms them for every chunk in
+// parallel with every decay factor at most 1, and leaves them in a workspace
+// slot per (chunk, head).  This kernel is the inter-chunk re-scan of the
+// kernel-fun KDA re-scan page with every operand referenced to the chunk's
+// ends, so that every factor is a decay:
+//     qd = q e^gcum,  kd = k e^gcum,  kg = k e^(gl - gcum)   (per key column;
+//                                                           gl: the last row)
+//     X = kd h,  Y = qd h,  R' = v - X,
+//     v' = (I + A)^-1 diag(beta) R'   (by blocks of 16 tokens from Tmb),
+//     o = Y + P v',  h <- e^gl h + kg^T v'   (row-wise by the key vector).
 // The schedule is forward_pipe_kernel's: chain waves 0..3 run the re-scan of
 // chunk c with h in MFMA accumulators while prepare waves 4..7 build chunk
-// c+1.  What the prepare adds for the per-key gate: the chunk-local cumsum of
-// the C x K gate (each thread holds four key columns of C/NSEG rows in
-// registers; the segment totals meet in LDS), the per-key factors e^gcum_gm,
-// e^gl and e^(gl - gcum_gm) for the chain, and the third operand tile k^.
-// The prepare waves also load beta themselves, so chain wave 0 has no gate
-// work and the prepare waits for nothing but its own barriers.
+// c+1: the chunk-local cumsum of the C x K gate (each thread holds four key
+// columns of C/NSEG rows in registers; the segment totals meet in LDS), the
+// three fp16 operand tiles, the per-key e^gl, and the chunk's Tmb and P
+// copied from the workspace into the LDS layout the chain reads.
 #pragma once
 
 #include "gdn_forward_pipe.h"
+#include "gdn_kda_gram.h"
 
 namespace gdn {
 
 template <int C, int K>
 struct PipeKdaLayout {
     static constexpr int NB = C / 16;
-    static constexpr int NASP = NB == 4 ? 4 : 0;         // A blocks (2,0) (2,1) (3,0) (3,1)
     static constexpr int kQK = C * K * 2;                // one fp16 C x K tile
     static constexpr int kCC = C * C * 2;                // one fp16 C x C tile
     static constexpr int kVT = C * 64 * 2;               // one bf16 v tile
-    static constexpr int kQ = 0;                         // [2] q~
-    static constexpr int kK = kQ + 2 * kQK;              // [2] k~
-    static constexpr int kH = kK + 2 * kQK;              // [2] k^
+    static constexpr int kQ = 0;                         // [2] qd
+    static constexpr int kK = kQ + 2 * kQK;              // [2] kd
+    static constexpr int kH = kK + 2 * kQK;              // [2] kg
     static constexpr int kTmb = kH + 2 * kQK;            // [2] solve blocks (Tb, Mn)
     static constexpr int kP = kTmb + 2 * kCC;            // [2] P
     static constexpr int kV = kP + 2 * kCC;              // [2] raw v tiles
-    static constexpr int kAsp = kV + 2 * kVT;            // [NASP][64][8] split A blocks
-    static constexpr int kTr = kAsp + NASP * 1024;       // [NB][64][4] fp16 T_bb
-    // per-key factors per slot: e^gcum_gm, e^gl, e^(gl - gcum_gm)
-    static constexpr int kKf = kTr + NB * 512;           // [2][3K] fp32
-    static constexpr int kBet = kKf + 2 * 3 * K * 4;     // [C] beta of the prepared chunk
+    static constexpr int kKf = kV + 2 * kVT;             // [2][K] e^gl per key
     // gate cumsum segments: a prepare thread holds 4 key columns of NR rows
     static constexpr int NSEG = 256 * 4 / K;
     static constexpr int NR = C / NSEG;
-    static constexpr int kSeg = kBet + C * 4;            // [NSEG][K] segment totals
+    static constexpr int kSeg = kKf + 2 * K * 4;         // [NSEG][K] segment totals
     static constexpr int kSync = kSeg + NSEG * K * 4;
     static constexpr int kBytes = kSync + 16;
     static_assert(NR >= 1 && NSEG * NR == C, "gate segments tile the chunk");
-    static_assert((C / 2) % NR == 0, "the middle row ends a segment");
+    // workspace pieces per chunk: Tmb and P, 16 bytes each
+    static constexpr int NWS = 2 * C * C * 2 / 16 / 256;
+    static_assert(NWS >= 1 && NWS * 16 * 256 == 2 * C * C * 2, "workspace pieces per thread");
 };
 
 __device__ __forceinline__ u32x2 bload64(rsrc_t r, uint32_t voff, uint32_t soff) {
@@ -81,10 +79,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
     _Float16 *Tmbb = (_Float16 *)(smem + L::kTmb);
     _Float16 *Pb = (_Float16 *)(smem + L::kP);
     uint16_t *Vb = (uint16_t *)(smem + L::kV);
-    _Float16 *Asp = (_Float16 *)(smem + L::kAsp);
-    _Float16 *Tr = (_Float16 *)(smem + L::kTr);
     float *Kf = (float *)(smem + L::kKf);
-    float *bet = (float *)(smem + L::kBet);
     float *segt = (float *)(smem + L::kSeg);
     unsigned *sync_ctr = (unsigned *)(smem + L::kSync);
 
@@ -99,11 +94,6 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
     const uint32_t rsK = (uint32_t)(H * K), rsV = (uint32_t)(H * V);
     WaitCtl wc{p.wait_count, p.wait_limit, p.wait_bias, 0u};
 
-    // the operand tiles above the diagonal are read but stay zero
-    for (int i = tid; i < 2 * C * C; i += kPipeThreads) {
-        Tmbb[i] = (_Float16)0.f;
-        Pb[i] = (_Float16)0.f;
-    }
     if (tid == 0) {
         sync_ctr[0] = 0u;                   // prepare waves' barrier
         sync_ctr[1] = 0u;
@@ -136,7 +126,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
         }
         // DQ: dq[t] += h_c dO_t for the tokens of chunk n, with h_c in hacc:
         // the state goes to LDS as bf16 high and low parts ([K][64], 16-byte
-        // chunks swizzled by row) in the q~ and k~ tiles of slot sl, free
+        // chunks swizzled by row) in the qd and kd tiles of slot sl, free
         // then; each wave forms DQ for K/4 key rows over the tile's 64 value
         // columns with bf16 MFMAs (bf16 keeps any dO magnitude in range)
         const rsrc_t rdo_ = make_rsrc(DQ ? (const IO *)p.dout + row0 * V : nullptr, DQ ? (uint32_t)T * rsV * SIO : 0u);
@@ -210,16 +200,14 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
             const _Float16 *Qs = Qb + slot * C * K, *Ks = Kb + slot * C * K, *Hs = Hb + slot * C * K;
             const _Float16 *Tmb = Tmbb + slot * C * C, *Ps = Pb + slot * C * C;
             const uint16_t *Vs = Vb + slot * C * 64;
-            const float *fsv = Kf + slot * 3 * K, *flv = fsv + K, *fmv = fsv + 2 * K;
+            const float *flv = Kf + slot * K;
             const uint32_t t0 = (uint32_t)(c * C);
 
-            // h as B fragments over the key dimension, rows scaled by e^gcum_gm
+            // h as B fragments over the key dimension
             half8 hf[K / 32];
 #pragma unroll
-            for (int s = 0; s < K / 32; ++s)
-                hf[s] = fragB_acc(hacc[2 * s] * *(const float4v *)(fsv + 32 * s + g4),
-                                  hacc[2 * s + 1] * *(const float4v *)(fsv + 32 * s + 16 + g4), _Float16{});
-            // X = k~ h', Y^T = h'^T q~^T for this wave's 16 columns
+            for (int s = 0; s < K / 32; ++s) hf[s] = fragB_acc(hacc[2 * s], hacc[2 * s + 1], _Float16{});
+            // X = kd h, Y^T = h^T qd^T for this wave's 16 columns
             float4v xa[NB], ya[NB];
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb) {
@@ -231,7 +219,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
                     M::mma(ya[cb], hf[s], frag_sw<K>(Qs, 16 * cb, 32 * s));
                 }
             }
-            // R' = v - X (the decay is inside X)
+            // R' = v - X (the decay is inside kd)
             float4v rr[NB];
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb) {
@@ -280,18 +268,17 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
 #pragma unroll
                 for (int i = 0; i < NKB; ++i) store_acc_pairs<OT>(hacc[i], rh, hck_off, V * SO, 16 * i * V * SO);
             }
-            // h <- e^gl h + e^(gl - gcum_gm) (k^^T v'), row-wise
+            // h <- e^gl h + kg^T v', the decay row-wise by the key vector
 #pragma unroll
             for (int i = 0; i < NKB; ++i) {
                 float4v acc = {0, 0, 0, 0};
 #pragma unroll
                 for (int s = 0; s < C / 32; ++s)
                     M::mma(acc, fragAT_split_p<K>(Hs, 16 * i, 32 * s), df[s]);
-                hacc[i] = *(const float4v *)(flv + 16 * i + g4) * hacc[i] +
-                          *(const float4v *)(fmv + 16 * i + g4) * acc;
+                hacc[i] = *(const float4v *)(flv + 16 * i + g4) * hacc[i] + acc;
             }
             // the next chunk's dq term from its start state (now in hacc),
-            // staged in this chunk's q~ and k~ tiles: the chain is done with
+            // staged in this chunk's qd and kd tiles: the chain is done with
             // them, and the prepare writes this slot only after the barrier
             if constexpr (DQ)
                 if (c + 1 < nt) rescan_dq(c + 1, slot);
@@ -308,17 +295,31 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
     } else {
         // =====================  prepare waves  ===========================
         // (unlike the scalar-gate kernel, these keep the default wave
-        // priority in the plain forward, where raising it measured 2 %
-        // slower, and in the re-scan, 3 % slower; with saved states the
-        // chain's store work competes for the SIMDs' issue slots, and a
+        // priority in the plain forward and the re-scan; with saved states
+        // the chain's store work competes for the SIMDs' issue slots, and a
         // raised priority measured 7 % faster)
-        const int pw = wv - 4, pt = tid - 256;
+        const int pt = tid - 256;
         if constexpr (ST && !DQ) __builtin_amdgcn_s_setprio(3);
         const rsrc_t rq_ = make_rsrc((const IO *)p.q + row0 * K, (uint32_t)T * rsK * SIO);
         const rsrc_t rk_ = make_rsrc((const IO *)p.k + row0 * K, (uint32_t)T * rsK * SIO);
         const rsrc_t rv_ = make_rsrc((const IO *)p.v + row0 * V, (uint32_t)T * rsV * SIO);
         const rsrc_t rg_ = make_rsrc(p.g + row0 * K, (uint32_t)T * rsK * 4);
-        const rsrc_t rb_ = make_rsrc(p.beta + row0, (uint32_t)T * (uint32_t)H * 4);
+        // this stream's workspace slots (see slot_chunk): chunk n of stream b
+        // is slot slot0 + n, each slot H heads of Tmb and P
+        int slot0 = 0;
+        if constexpr (VL) {
+            for (int m = 0; m < b; ++m) {
+                const int c0 = __builtin_amdgcn_readfirstlane(p.cu[m]);
+                const int c1 = __builtin_amdgcn_readfirstlane(p.cu[m + 1]);
+                const int bos = min(max(c0, 0), p.T), eos = min(max(c1, bos), p.T);
+                slot0 += (eos - bos + C - 1) / C;
+            }
+        } else {
+            slot0 = b * nt;
+        }
+        constexpr uint32_t kSlotBytes = (uint32_t)(kda_slot_elems<C>() * 2);
+        const rsrc_t rw_ = make_rsrc((const char *)p.ws + ((int64_t)slot0 * H + h) * kSlotBytes,
+                                     (uint32_t)nt * (uint32_t)H * kSlotBytes);
 
         // thread (seg, cg): rows seg NR .. +NR-1, key columns 4 cg .. 4 cg + 3
         const int cg = pt % (K / 4), seg = pt / (K / 4), kc = 4 * cg;
@@ -337,20 +338,33 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
             vv_off[j] = ((uint32_t)row * rsV + vt * 64 + 8 * ch) * SIO;
             vv_lds[j] = swz<64>(row, 8 * ch);
         }
+        // Tmb and P: 16-byte pieces of 8 columns, placed in the swizzled,
+        // column-permuted layout of the chain's operand tiles
+        constexpr int NWS = L::NWS;
+        int ws_lds[NWS][2];
+#pragma unroll
+        for (int j = 0; j < NWS; ++j) {
+            const int e0 = 8 * (pt + 256 * j), tile = e0 / (C * C), rc = e0 % (C * C);
+            const int row = rc / C, col = rc % C;
+            const int base = tile ? (L::kP - L::kTmb) / 2 : 0;      // in halves from Tmb slot 0
+            ws_lds[j][0] = base + swz<C>(row, pcol(col));
+            ws_lds[j][1] = base + swz<C>(row, pcol(col + 4));
+        }
 
         u32x2 rq[NR], rk[NR];
         float4v rg[NR];
-        u32x4 rv[NVV];
-        float b_pre = 0.f;
+        u32x4 rv[NVV], rw[NWS];
         // The loads of chunk n come in pieces, each issued as soon as the
         // registers it fills are free: the CU's memory pipeline takes about a
-        // cycle per 64 bytes, and 72 KB per chunk issued at once would stall
+        // cycle per 64 bytes, and a chunk's loads issued at once would stall
         // the issuing waves for most of that time.
-        auto load_v_beta = [&](int n) {
+        auto load_v_ws = [&](int n) {
             const uint32_t t0 = (uint32_t)(n * C);
 #pragma unroll
             for (int j = 0; j < NVV; ++j) rv[j] = bload128(rv_, vv_off[j], t0 * rsV * SIO);
-            if (pt < C) b_pre = __uint_as_float(bload32(rb_, (uint32_t)pt * (uint32_t)H * 4, t0 * (uint32_t)H * 4));
+#pragma unroll
+            for (int j = 0; j < NWS; ++j)
+                rw[j] = bload128(rw_, (uint32_t)(16 * (pt + 256 * j)), (uint32_t)n * (uint32_t)H * kSlotBytes);
         };
         auto load_row = [&](int n, int i) {
             const uint32_t t0 = (uint32_t)(n * C);
@@ -363,55 +377,49 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
         auto prepare = [&](int n) {
             const int slot = n & 1;
             _Float16 *Qs = Qb + slot * C * K, *Ks = Kb + slot * C * K, *Hs = Hb + slot * C * K;
-            _Float16 *Tmb = Tmbb + slot * C * C, *Ps = Pb + slot * C * C;
+            _Float16 *Tmb = Tmbb + slot * C * C;
             uint16_t *Vs = Vb + slot * C * 64;
-            float *fsv = Kf + slot * 3 * K, *flv = fsv + K, *fmv = fsv + 2 * K;
+            float *flv = Kf + slot * K;
 
-            // ---- raw v, beta, and the gate cumsum of this thread's rows
+            // ---- raw v, Tmb and P, then the next chunk's v and workspace loads
 #pragma unroll
             for (int j = 0; j < NVV; ++j) *(u32x4 *)(Vs + vv_lds[j]) = rv[j];
-            if (pt < C) bet[pt] = b_pre;
-            if (n + 1 < nt) load_v_beta(n + 1);
+#pragma unroll
+            for (int j = 0; j < NWS; ++j) {
+                *(u32x2 *)(Tmb + ws_lds[j][0]) = u32x2{rw[j][0], rw[j][1]};
+                *(u32x2 *)(Tmb + ws_lds[j][1]) = u32x2{rw[j][2], rw[j][3]};
+            }
+            if (n + 1 < nt) load_v_ws(n + 1);
+            // ---- the gate cumsum of this thread's rows; segment totals meet
+            // in LDS and are summed in segment order (gl: the chunk total,
+            // equal to gcum at the last token summed the same way)
             float4v run = {0, 0, 0, 0};
 #pragma unroll
             for (int i = 0; i < NR; ++i) { run += rg[i]; rg[i] = run; }
             *(float4v *)(segt + seg * K + kc) = run;
             prep_barrier(sync_ctr, sync_target, wc);
-            // segment offsets in segment order; gcum at the middle row (the
-            // end of segment C/2/NR - 1) and at the last row
-            float4v off = {0, 0, 0, 0}, gm = {0, 0, 0, 0}, gl = {0, 0, 0, 0};
+            float4v off = {0, 0, 0, 0}, gl = {0, 0, 0, 0};
 #pragma unroll
-            for (int s = 0; s < NSEG; ++s) {
-                const float4v t = *(const float4v *)(segt + s * K + kc);
-                if (s < seg) off += t;
-                if (s < C / 2 / NR) gm += t;
+            for (int m = 0; m < NSEG; ++m) {
+                const float4v t = *(const float4v *)(segt + m * K + kc);
+                if (m < seg) off += t;
                 gl += t;
             }
             if (seg == 0) {
-                float4v e0, e1, e2;
+                float4v e1;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    e0[e] = fast_exp(gm[e]);
-                    e1[e] = fast_exp(gl[e]);
-                    e2[e] = fast_exp(gl[e] - gm[e]);
-                }
-                *(float4v *)(fsv + kc) = e0;
+                for (int e = 0; e < 4; ++e) e1[e] = fast_exp(gl[e]);
                 *(float4v *)(flv + kc) = e1;
-                *(float4v *)(fmv + kc) = e2;
             }
-            // ---- operands q~, k~, k^ (fp16) of this thread's rows; the
-            // exponent (gcum - gcum_gm) log2 e is one FMA per element on the
-            // in-segment cumsum, with the segment's offset folded in
-            const float4v dof = (off - gm) * kLog2e;
+            // ---- operands qd, kd, kg (fp16) of this thread's rows; both
+            // exponents are <= 0 for any gate g <= 0
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
-                float4v d;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) d[e] = __builtin_fmaf(rg[i][e], kLog2e, dof[e]);
+                const float4v gr = off + rg[i];
                 half4 hq, hk, hh;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float up = fast_exp2(d[e]), dn = fast_exp2(-d[e]);
+                    const float up = fast_exp2(gr[e] * kLog2e), dn = fast_exp2((gl[e] - gr[e]) * kLog2e);
                     const uint32_t wq = rq[i][e >> 1], wk = rk[i][e >> 1];
                     const float xq = __uint_as_float((e & 1) ? (wq & 0xffff0000u) : (wq << 16));
                     const float xk = __uint_as_float((e & 1) ? (wk & 0xffff0000u) : (wk << 16));
@@ -424,160 +432,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
                 *(half4 *)(Hs + qk_lds[i]) = hh;
                 if (n + 1 < nt) load_row(n + 1, i);
             }
-            prep_arrive(sync_ctr, sync_target);
-            // every prepare wave's operand rows (and beta) are in
-            wait_counter(sync_ctr, sync_target, wc);
-
-            // ---- Gram tiles.  A = diag(beta) k~ k^^T and P = q~ k^^T need no
-            // decay factor; A tiles get beta of their rows and the strict
-            // mask, P tiles the inclusive one.
-            auto fac_row = [&](int I, int J, bool isA, const float4v &acc) {
-                const int r = 16 * I + (l & 15), s0 = 16 * J + 4 * (l >> 4);
-                const float fr = isA ? bet[r] : 1.f;
-                float4v a;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) a[e] = (isA ? s0 + e < r : s0 + e <= r) ? acc[e] * fr : 0.f;
-                return a;
-            };
-            auto fac_col = [&](int I, int J, const float4v &acc) {      // A blocks only
-                const int r0 = 16 * I + 4 * (l >> 4), s = 16 * J + (l & 15);
-                const float4v fr = *(const float4v *)(bet + r0);
-                float4v a;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) a[e] = s < r0 + e ? acc[e] * fr[e] : 0.f;
-                return a;
-            };
-            auto put_p = [&](int I, int J, const float4v &acc) {
-                const float4v a = fac_row(I, J, false, acc);
-                half4 hv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) hv[e] = (_Float16)a[e];
-                *(half4 *)(Ps + swz<C>(16 * I + (l & 15), pcol(16 * J + 4 * (l >> 4)))) = hv;
-            };
-            // Two tiles at once.  mma(x, frag of rows X, frag of rows Y) forms
-            // X Y^T in col layout: with k^ rows of block J first, P tiles come
-            // out in row layout; A tiles (k~ rows of block I first) in col
-            // layout.
-            auto gram_two = [&](int I0, int J0, bool a0, int I1, int J1, bool a1, bool two, int sl0, int sl1) {
-                half8 fa0[K / 32], fb0[K / 32], fa1[K / 32], fb1[K / 32];
-#pragma unroll
-                for (int k = 0; k < K / 32; ++k) {
-                    fa0[k] = frag_sw<K>(Hs, 16 * J0, 32 * k);
-                    fb0[k] = frag_sw<K>(a0 ? Ks : Qs, 16 * I0, 32 * k);
-                    if (two) {
-                        fa1[k] = frag_sw<K>(Hs, 16 * J1, 32 * k);
-                        fb1[k] = frag_sw<K>(a1 ? Ks : Qs, 16 * I1, 32 * k);
-                    }
-                }
-                float4v acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-#pragma unroll
-                for (int k = 0; k < K / 32; ++k) {
-                    if (a0) M::mma(acc0, fb0[k], fa0[k]); else M::mma(acc0, fa0[k], fb0[k]);
-                    if (two) {
-                        if (a1) M::mma(acc1, fb1[k], fa1[k]); else M::mma(acc1, fa1[k], fb1[k]);
-                    }
-                }
-                auto put = [&](int I, int J, bool isA, int sl, const float4v &acc) {
-                    if (isA)
-                        *(half8 *)(Asp + sl * 512 + 8 * l) = split_hi_lo(fac_col(I, J, acc));
-                    else
-                        put_p(I, J, acc);
-                };
-                put(I0, J0, a0, sl0, acc0);
-                if (two) put(I1, J1, a1, sl1, acc1);
-            };
-            auto put_mn = [&](int i, int j, const half8 &a_split, const half4 &t) {
-                *(half4 *)(Tmb + swz<C>(16 * i + (l & 15), pcol(16 * j + 4 * (l >> 4)))) = solve_block(a_split, t);
-            };
-            if (pw < NB / 2) {
-                // the diagonal pair (pb, pb+1): A_pb,pb, A_pb+1,pb+1 (row
-                // layout, for the inverse) and A_pb+1,pb (col layout, for its
-                // solve block), kept in registers
-                const int pb = 2 * pw;
-                half8 f0[K / 32], f1[K / 32], g0[K / 32], g1[K / 32], q0[K / 32], q1[K / 32];
-#pragma unroll
-                for (int k = 0; k < K / 32; ++k) {
-                    f0[k] = frag_sw<K>(Hs, 16 * pb, 32 * k);
-                    f1[k] = frag_sw<K>(Hs, 16 * (pb + 1), 32 * k);
-                    g0[k] = frag_sw<K>(Ks, 16 * pb, 32 * k);
-                    g1[k] = frag_sw<K>(Ks, 16 * (pb + 1), 32 * k);
-                }
-                if constexpr (NB == 4) {
-#pragma unroll
-                    for (int k = 0; k < K / 32; ++k) {
-                        q0[k] = frag_sw<K>(Qs, 16 * pb, 32 * k);
-                        q1[k] = frag_sw<K>(Qs, 16 * (pb + 1), 32 * k);
-                    }
-                }
-                float4v a00 = {0, 0, 0, 0}, a11 = {0, 0, 0, 0}, a10 = {0, 0, 0, 0};
-#pragma unroll
-                for (int k = 0; k < K / 32; ++k) {
-                    M::mma(a00, f0[k], g0[k]);
-                    M::mma(a11, f1[k], g1[k]);
-                    M::mma(a10, g1[k], f0[k]);
-                }
-                const float4v ad[2] = {fac_row(pb, pb, true, a00), fac_row(pb + 1, pb + 1, true, a11)};
-                const half8 a10s = split_hi_lo(fac_col(pb + 1, pb, a10));
-                float4v tr[2];
-                diag_inverse_mfma(ad, tr);
-                if constexpr (NB == 4) {
-                    // the P tiles of the same 2 x 2 block (their MFMAs fill
-                    // the gaps of the inverse's dependent chain)
-                    float4v p00 = {0, 0, 0, 0}, p10 = {0, 0, 0, 0}, p11 = {0, 0, 0, 0};
-#pragma unroll
-                    for (int k = 0; k < K / 32; ++k) {
-                        M::mma(p00, f0[k], q0[k]);
-                        M::mma(p10, f0[k], q1[k]);
-                        M::mma(p11, f1[k], q1[k]);
-                    }
-                    put_p(pb, pb, p00);
-                    put_p(pb + 1, pb, p10);
-                    put_p(pb + 1, pb + 1, p11);
-                }
-                // Tb = T scaled by beta of its columns, and T itself (fp16, row
-                // layout) for the other waves' solve blocks
-                half4 t16[2];
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int row = 16 * (pb + e) + (l & 15), c4 = 16 * (pb + e) + 4 * (l >> 4);
-                    const float4v t = tr[e] * *(const float4v *)(bet + c4);
-                    half4 hv;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        hv[q] = (_Float16)t[q];
-                        t16[e][q] = (_Float16)tr[e][q];
-                    }
-                    *(half4 *)(Tmb + swz<C>(row, pcol(c4))) = hv;
-                    *(half4 *)(Tr + (pb + e) * 256 + 4 * l) = t16[e];
-                }
-                put_mn(pb + 1, pb, a10s, t16[1]);
-            }
-            if constexpr (NB == 4) {
-                // prepare wave 2 + J: the A and P tiles (2, J) and (3, J), with
-                // the A tiles in slots 2 (I - 2) + J
-                if (pw >= 2) {
-                    const int J = pw - 2;
-                    gram_two(2, J, true, 3, J, true, true, J, 2 + J);
-                    gram_two(2, J, false, 3, J, false, true, 0, 0);
-                }
-            } else {
-                // prepare waves 1..3: one P tile each
-                if (pw >= 1) {
-                    const int t = pw - 1, I = t == 0 ? 0 : 1, J = t == 2 ? 1 : 0;
-                    gram_two(I, J, false, 0, 0, false, false, 0, 0);
-                }
-            }
-            if constexpr (NB == 4) {
-                // Mn_20, Mn_21, Mn_30, Mn_31 (prepare wave pw takes A block pw):
-                // T_22 and T_33 come from wave 1, the A blocks from waves 2, 3
-                prep_barrier(sync_ctr, sync_target, wc);
-                const int i = 2 + (pw >> 1);
-                put_mn(i, pw & 1, *(const half8 *)(Asp + pw * 512 + 8 * l), *(const half4 *)(Tr + i * 256 + 4 * l));
-            }
         };
 
         if (nt > 0) {
-            load_v_beta(0);
+            load_v_ws(0);
 #pragma unroll
             for (int i = 0; i < NR; ++i) load_row(0, i);
             prepare(0);

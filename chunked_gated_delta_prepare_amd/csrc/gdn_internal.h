@@ -29,8 +29,17 @@ gdn_status enqueue_chunk_dq(const gdn_problem *pr, const void *dout, const void 
 gdn_status enqueue_forward(const gdn_problem *pr, const void *q, const void *k,
                            const void *v, const float *beta, const float *g,
                            const float *h0, void *o, float *hT, void *hck, void *vnew,
-                           const int32_t *cu, int64_t n_seqs, hipStream_t s,
+                           const int32_t *cu, int64_t n_seqs, void *ws, hipStream_t s,
                            const void *dout = nullptr, float *dq = nullptr);
+
+// Per-key gate: the workspace the forward entry points need (kda_gram_kernel's
+// Tmb and P per chunk and head; 0 for the scalar gate or T = 0), for a
+// fixed-length batch (n_seqs = 0) or n_seqs packed sequences; and the launch
+// of kda_gram_kernel into it.
+int64_t kda_workspace_bytes(const gdn_problem *pr, int64_t n_seqs);
+gdn_status enqueue_kda_gram(const gdn_problem *pr, const void *q, const void *k,
+                            const float *beta, const float *g, void *ws, const int32_t *cu,
+                            int64_t n_seqs, hipStream_t s);
 
 struct FwdParams;
 // Dispatch a forward problem whose FwdParams carry hck and vnew.

@@ -17,6 +17,7 @@
 
 #include "gdn_chunk_io.h"
 #include "gdn_inverse.h"
+#include "gdn_key_gram.h"
 #include "gdn_scan.h"
 
 namespace gdn {
@@ -38,9 +39,8 @@ struct PrepLayout {
     static constexpr int LDC = C + Mma<OpT>::kPad;
     static constexpr int LDA = C + 4;                        // fp32 C x C pitch
     static constexpr int E = sizeof(OpT);
-    static constexpr int kKs = 0;                            // [C][LDK] k (KDA: k e^(g-ref))
-    static constexpr int kKm = kKs + C * LDK * E;            // [C][LDK] KDA: k e^(ref-g)
-    static constexpr int kKbT = kKm + (KEYGATE ? C * LDK * E : 0);  // [K][LDC] (beta e^g k)^T
+    static constexpr int kKs = 0;                            // [C][LDK] k (KDA: exact_key_gram's scratch)
+    static constexpr int kKbT = kKs + C * LDK * E;           // [K][LDC] (beta e^g k)^T
     static constexpr int kVbT = kKbT + K * LDC * E;          // [64][LDC] (beta v)^T, one V tile
     static constexpr int kScr = kVbT + 64 * LDC * E;         // shared scratch region
     static constexpr int kA = kScr;                          // fp32 [C][LDA] A
@@ -50,7 +50,11 @@ struct PrepLayout {
                                          ? 2 * C * LDA * 4 : C * K * 4;
     static constexpr int kGam = kScr + kScrBytes;            // GDN: fp32 gcum[C]
     static constexpr int kBeta = kGam + C * 4;               // fp32 beta[C]
-    static constexpr int kBytes = kBeta + C * 4;
+    // KDA: the gate scan's segment totals and segment-end gcum
+    static constexpr int NSEG = kThreads * 4 / K;
+    static constexpr int kSegt = kBeta + C * 4;
+    static constexpr int kGend = kSegt + (KEYGATE ? NSEG * K * 4 : 0);
+    static constexpr int kBytes = kGend + (KEYGATE ? NSEG * K * 4 : 0);
 };
 
 // Fragment of an fp32 A operand converted to the operand type.
@@ -95,7 +99,6 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepParams p) {
 
     __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
     OpT *Ks = (OpT *)(smem + L::kKs);
-    OpT *Km = KEYGATE ? (OpT *)(smem + L::kKm) : Ks;
     OpT *KbT = (OpT *)(smem + L::kKbT);
     OpT *VbT = (OpT *)(smem + L::kVbT);
     float *Af = (float *)(smem + L::kA);
@@ -103,6 +106,8 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepParams p) {
     float *Gr = (float *)(smem + L::kGrows);
     float *gam = (float *)(smem + L::kGam);
     float *bet = (float *)(smem + L::kBeta);
+    float *segt = (float *)(smem + L::kSegt);
+    float *gend = (float *)(smem + L::kGend);
 
     const int pair = blockIdx.x / p.nt, c = blockIdx.x % p.nt;
     const int b = pair / p.H, h = pair - b * p.H;
@@ -123,23 +128,35 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepParams p) {
         if (vt < nvt) rv[vt].load((const IO *)p.v + row0 * V + 64 * vt, rsV, nvalid);
     if (tid < C) bet[tid] = tid < nvalid ? p.beta[(row0 + (int64_t)tid * H)] : 0.f;
 
+    // KDA: the gate, k in exact_key_gram's row order; gcum out and, for the
+    // operands below, into Gr
+    constexpr int NRK = KEYGATE ? KeyRows<C, K>::NR : 1;
+    float4v gamK[NRK], kvK[NRK];
     if constexpr (KEYGATE) {
-        ChunkRows<float, C, K> rg;
-        rg.load(p.g + row0 * K, rsG, nvalid);
+        const uint32_t rk32 = (uint32_t)rsK;
+        const rsrc_t rgs = make_rsrc(p.g + row0 * K, (uint32_t)nvalid * rk32 * 4);
+        const rsrc_t rks = make_rsrc((const IO *)p.k + row0 * K, (uint32_t)nvalid * rk32 * sizeof(IO));
+        load_key_rows<C, K, IO>(rgs, rks, rks, rk32, 0, segt, gend, gamK, kvK, kvK);
+        const int sg = tid / (K / 4), kc = 4 * (tid % (K / 4));
+        // gcum out through a range-clamped resource (rows past nvalid fall
+        // outside the range and are dropped).  A lane pair holds 8 adjacent
+        // columns of one row; it swaps halves so that each lane issues two
+        // 8-byte stores 16 bytes apart, which the compiler cannot fuse into
+        // one 16-byte store.
+        const rsrc_t rgo = make_rsrc(p.gcum + row0 * K, (uint32_t)nvalid * rk32 * 4);
+        const bool odd = tid & 1;
 #pragma unroll
-        for (int j = 0; j < ChunkRows<float, C, K>::kVec; ++j) {
-            float x[8];
-            rg.get(j, x);
-            put8(Gr + ChunkRows<float, C, K>::row(j) * K + ChunkRows<float, C, K>::col(j), x);
-        }
-        __syncthreads();
-        if (tid < K) {
-            float s = 0.f;
-            for (int r = 0; r < C; ++r) {
-                s += Gr[r * K + tid];
-                Gr[r * K + tid] = s;
-                if (r < nvalid) p.gcum[(row0 + (int64_t)r * H) * K + tid] = s;
-            }
+        for (int i = 0; i < NRK; ++i) {
+            const int r = sg * NRK + i;
+            *(float4v *)(Gr + r * K + kc) = gamK[i];
+            const float s0 = odd ? gamK[i][0] : gamK[i][2], s1 = odd ? gamK[i][1] : gamK[i][3];
+            const uint32_t r0 = __builtin_amdgcn_update_dpp(0, __float_as_uint(s0), 0xB1, 0xf, 0xf, false);
+            const uint32_t r1 = __builtin_amdgcn_update_dpp(0, __float_as_uint(s1), 0xB1, 0xf, 0xf, false);
+            const uint32_t off = ((uint32_t)r * rk32 + (uint32_t)kc) * 4;
+            const u32x2 a = odd ? u32x2{r0, r1} : u32x2{__float_as_uint(gamK[i][0]), __float_as_uint(gamK[i][1])};
+            const u32x2 b = odd ? u32x2{__float_as_uint(gamK[i][2]), __float_as_uint(gamK[i][3])} : u32x2{r0, r1};
+            __builtin_amdgcn_raw_buffer_store_b64(a, rgo, odd ? off - 8 : off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(b, rgo, odd ? off + 8 : off + 16, 0, 0);
         }
     } else {
         if (wv == 0) {
@@ -157,32 +174,20 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepParams p) {
     }
     __syncthreads();
 
-    // ---- S1: operands.  Ks (and Km), KbT = (beta e^gcum k)^T
+    // ---- S1: operands.  Ks (the scalar gate), KbT = (beta e^gcum k)^T
     {
-        float gref[8];
-        const int refrow = (nvalid - 1) / 2;
-        if constexpr (KEYGATE) {
-            const int col = ChunkRows<IO, C, K>::col(0);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) gref[e] = Gr[refrow * K + col + e];
-        }
 #pragma unroll
         for (int j = 0; j < ChunkRows<IO, C, K>::kVec; ++j) {
             const int row = ChunkRows<IO, C, K>::row(j), col = ChunkRows<IO, C, K>::col(j);
             const bool ok = row < nvalid;
-            float x[8], kp[8], km[8], kb[8];
+            float x[8], kb[8];
             rk.get(j, x);
             const float br = bet[row];
             if constexpr (KEYGATE) {
+                // (A comes from exact_key_gram below)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float gg = Gr[row * K + col + e];
-                    kp[e] = ok ? x[e] * fast_exp(gg - gref[e]) : 0.f;
-                    km[e] = ok ? x[e] * fast_exp(gref[e] - gg) : 0.f;
-                    kb[e] = ok ? br * x[e] * fast_exp(gg) : 0.f;
-                }
-                put8(Ks + row * LDK + col, kp);
-                put8(Km + row * LDK + col, km);
+                for (int e = 0; e < 8; ++e)
+                    kb[e] = ok ? br * x[e] * fast_exp(Gr[row * K + col + e]) : 0.f;
             } else {
                 const float sc = br * fast_exp(gam[row]);
 #pragma unroll
@@ -195,8 +200,10 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepParams p) {
     __syncthreads();   // Gr (KDA gate rows) is dead from here: the region is A / Tm
 
     // ---- S2: A = strictly lower beta * (k k^T * decay); clear Tm
+    if constexpr (KEYGATE)
+        exact_key_gram<C, K, OpT, true, false>(gamK, kvK, kvK, gend, bet, Ks, Ks, Af, Af);
     for (int i = tid; i < C * LDA; i += kThreads) Tm[i] = 0.f;
-    constexpr int NP = NCB * (NCB + 1) / 2;
+    constexpr int NP = KEYGATE ? 0 : NCB * (NCB + 1) / 2;
 #pragma unroll
     for (int idx = 0; idx < NP; ++idx) {
         if (idx % kWaves != wv) continue;
@@ -204,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(PrepParams p) {
         while ((I + 1) * (I + 2) / 2 <= idx) ++I;
         const int J = idx - I * (I + 1) / 2;                 // J <= I
         float4v acc = {0, 0, 0, 0};
-        mma_tile<OpT, K>(acc, Ks + 16 * I * LDK, LDK, Km + 16 * J * LDK, LDK);
+        mma_tile<OpT, K>(acc, Ks + 16 * I * LDK, LDK, Ks + 16 * J * LDK, LDK);
         const int cp = 16 * J + acc_col();                  // column s
 #pragma unroll
         for (int r = 0; r < 4; ++r) {

@@ -13,6 +13,7 @@
 #pragma once
 
 #include "gdn_chunk_io.h"
+#include "gdn_key_gram.h"
 
 namespace gdn {
 
@@ -51,8 +52,8 @@ struct ScanLayout {
     static constexpr int LDC = C + Mma<OpT>::kPad;
     static constexpr int E = sizeof(OpT);
     static constexpr int kQ = 0;                              // [C][LDK] q (KDA: q e^g)
-    static constexpr int kK = kQ + C * LDK * E;               // [C][LDK] k (KDA: k e^(ref-g))
-    static constexpr int kQr = kK + C * LDK * E;              // [C][LDK] KDA: q e^(g-ref)
+    static constexpr int kK = kQ + C * LDK * E;               // [C][LDK] k (KDA: scratch)
+    static constexpr int kQr = kK + C * LDK * E;              // [C][LDK] KDA: scratch
     static constexpr int kW = kQr + (KEYGATE ? C * LDK * E : 0);   // [C][LDK] w
     static constexpr int kKT = kW + C * LDK * E;              // [K][LDC] k^T (KDA: kg^T)
     static constexpr int kHT = kKT + K * LDC * E;             // [BV][LDK] h^T
@@ -61,7 +62,13 @@ struct ScanLayout {
     static constexpr int kDS = kDT + BV * LDC * E;            // [BV][LDC] GDN: (v' e^(gl-g))^T
     static constexpr int kGam = kDS + (KEYGATE ? 0 : BV * LDC * E);  // fp32 gates
     static constexpr int kGamN = KEYGATE ? K : C;             // KDA: gcum_last[K]; GDN: gcum[C]
-    static constexpr int kBytes = kGam + kGamN * 4;
+    // KDA: P in fp32 from exact_key_gram (whose operand scratch is the k and
+    // q tiles kK, kQr), the segment totals and segment-end gcum it reads
+    static constexpr int LDA = C + 4;
+    static constexpr int kPf = kGam + kGamN * 4;
+    static constexpr int NSEG = kThreads * 4 / K;
+    static constexpr int kGend = kPf + (KEYGATE ? C * LDA * 4 : 0);
+    static constexpr int kBytes = kGend + (KEYGATE ? NSEG * K * 4 : 0);
 };
 
 template <int C, int K, int BV, typename IO, typename OT, bool KEYGATE>
@@ -86,6 +93,8 @@ __global__ __launch_bounds__(kThreads, 1) void scan_kernel(ScanParams p) {
     OpT *DT = (OpT *)(smem + L::kDT);
     OpT *DS = KEYGATE ? DT : (OpT *)(smem + L::kDS);
     float *gam = (float *)(smem + L::kGam);
+    float *Pf = (float *)(smem + L::kPf);
+    float *gend = (float *)(smem + L::kGend);
 
     int pair, vt;
     map_block(blockIdx.x, p.nvt, p.swizzle, pair, vt);
@@ -123,7 +132,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_kernel(ScanParams p) {
     ChunkRows<float, C, K> rw;
     ChunkRows<float, C, K> rg;      // KDA gate rows
     float g_own = 0.f;              // GDN: gcum of row tid (tid < C)
-    float gl_own[8], gr_own[8];     // KDA: gcum of the chunk's last / middle row
+    float gl_own[8];                // KDA: gcum of the chunk's last row
     float4v ureg[NZW];
 
     auto load_chunk = [&](int c) {
@@ -136,9 +145,8 @@ __global__ __launch_bounds__(kThreads, 1) void scan_kernel(ScanParams p) {
             // every vector of this thread sits in the same column group
             const int col = ChunkRows<float, C, K>::col(0);
             const float *gl = gb + (t0 + nvalid - 1) * rsG + col;
-            const float *gr = gb + (t0 + (nvalid - 1) / 2) * rsG + col;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { gl_own[e] = gl[e]; gr_own[e] = gr[e]; }
+            for (int e = 0; e < 8; ++e) gl_own[e] = gl[e];
         } else {
             if (tid < C) g_own = gb[(t0 + min(tid, nvalid - 1)) * rsG];
         }
@@ -160,29 +168,27 @@ __global__ __launch_bounds__(kThreads, 1) void scan_kernel(ScanParams p) {
         // ---- S1: registers -> LDS operands
         if constexpr (KEYGATE) {
             const int col = ChunkRows<float, C, K>::col(0);
-            float glast[8], gref[8];
+            float glast[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { glast[e] = gl_own[e]; gref[e] = gr_own[e]; }
+            for (int e = 0; e < 8; ++e) glast[e] = gl_own[e];
             if (tid < K / 8) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) gam[col + e] = glast[e];
             }
+            // q e^gcum and k e^(gl - gcum): decays (P comes from
+            // exact_key_gram below)
 #pragma unroll
             for (int j = 0; j < ChunkRows<IO, C, K>::kVec; ++j) {
                 const int row = ChunkRows<IO, C, K>::row(j);
                 const bool ok = row < nvalid;
-                float xq[8], xk[8], xw[8], xg[8], a[8], bq[8], bk[8], kg[8];
+                float xq[8], xk[8], xw[8], xg[8], a[8], kg[8];
                 rq.get(j, xq); rk.get(j, xk); rw.get(j, xw); rg.get(j, xg);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     a[e] = ok ? xq[e] * fast_exp(xg[e]) : 0.f;
-                    bq[e] = ok ? xq[e] * fast_exp(xg[e] - gref[e]) : 0.f;
-                    bk[e] = ok ? xk[e] * fast_exp(gref[e] - xg[e]) : 0.f;
                     kg[e] = ok ? xk[e] * fast_exp(glast[e] - xg[e]) : 0.f;
                 }
                 put8(Qs + row * LDK + col, a);
-                put8(Qr + row * LDK + col, bq);
-                put8(Ks + row * LDK + col, bk);
                 put8(Ws + row * LDK + col, xw);
                 put8_col(KT + col * LDC + row, LDC, kg);
             }
@@ -208,10 +214,29 @@ __global__ __launch_bounds__(kThreads, 1) void scan_kernel(ScanParams p) {
         if (c + 1 < nt) load_chunk(c + 1);
         __syncthreads();
 
-        // ---- S2: P = masked decayed q k^T;  Z = w h, Y = q h;  v' = u - Z
+        if constexpr (KEYGATE) {
+            // P with every decay split at a row between its two tokens: the
+            // chunk's gcum, k and q in exact_key_gram's row order (from L2:
+            // the ChunkRows copies above have another layout), the k and q
+            // tiles as its operand scratch, P in fp32, then into Ps
+            constexpr int NR = KeyRows<C, K>::NR;
+            const uint32_t rsk = (uint32_t)rsK;
+            const rsrc_t rgc = make_rsrc(gb, (uint32_t)T * rsk * 4);
+            const rsrc_t rkc = make_rsrc(kb, (uint32_t)T * rsk * sizeof(IO));
+            const rsrc_t rqc = make_rsrc(qb, (uint32_t)T * rsk * sizeof(IO));
+            float4v gS[NR], kS[NR], qS[NR];
+            load_key_rows<C, K, IO, true>(rgc, rkc, rqc, rsk, (uint32_t)t0, nullptr, gend, gS, kS, qS);
+            exact_key_gram<C, K, OpT, false, true>(gS, kS, qS, gend, gend, Ks, Qr, Pf, Pf);
+            for (int i = tid; i < C * C; i += kThreads)
+                Ps[(i / C) * LDC + i % C] = Mma<OpT>::cvt(Pf[(i / C) * L::LDA + i % C]);
+            __syncthreads();
+        }
+
+        // ---- S2: P = masked decayed q k^T (the scalar gate);  Z = w h,
+        // Y = q h;  v' = u - Z
         float gl = 0.f;
         if constexpr (!KEYGATE) gl = gam[nvalid - 1];
-        constexpr int NP = NCB * (NCB + 1) / 2;
+        constexpr int NP = KEYGATE ? 0 : NCB * (NCB + 1) / 2;
 #pragma unroll
         for (int idx = 0; idx < NP; ++idx) {
             if (idx % kWaves != wv) continue;
@@ -219,8 +244,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_kernel(ScanParams p) {
             while ((J + 1) * (J + 2) / 2 <= idx) ++J;
             const int I = idx - J * (J + 1) / 2;            // I <= J
             float4v acc = {0, 0, 0, 0};
-            mma_tile<OpT, K>(acc, Ks + 16 * I * LDK, LDK,
-                             (KEYGATE ? Qr : Qs) + 16 * J * LDK, LDK);
+            mma_tile<OpT, K>(acc, Ks + 16 * I * LDK, LDK, Qs + 16 * J * LDK, LDK);
             // acc[r] = P[c = 16J + col][c' = 16I + row(r)]
             const int cc = 16 * J + acc_col();
 #pragma unroll

@@ -34,9 +34,13 @@
  * bf16 io, matrix-core operands are fp16 (raw bf16 inputs convert exactly for
  * magnitudes in [2^-14, 65504]; derived operands are rounded once); with
  * fp32 io they are fp32.  Inputs and the state must keep |x| < 65504 with
- * bf16 io.  For the per-key gate, the chunk-local gate sums are referenced to
- * the middle of the chunk, so |gcum[r] - gcum[mid]| must stay below ~11 for
- * full accuracy with bf16 io.
+ * bf16 io.  Any gate g <= 0 is supported, however strong: every decay
+ * factor that enters an operand or a product is a decay (at most 1), for
+ * both gates -- within a chunk each pair's decay e^(gcum_r - gcum_s) is
+ * split at a row between r and s (the per-key gate by halving the chunk,
+ * see gdn_forward), and operands are referenced to the chunk's start or end.
+ * A factor that underflows only drops contributions below the operands'
+ * precision.
  *
  * Ownership and execution: the caller allocates every buffer (device
  * memory) and owns it; the library never allocates, frees or synchronises.
@@ -64,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 6
+#define GDN_ABI_VERSION 7
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -130,12 +134,21 @@ gdn_status gdn_scan(const gdn_problem *problem, const void *q, const void *k,
 /*
  * gdn_forward -- the whole forward pass: o and the final state from q, k, v,
  * beta, g and an optional h0 (NULL = zero state).  Results equal
- * gdn_prepare followed by gdn_scan up to rounding.  `workspace` must hold
- * gdn_workspace_bytes(problem) bytes (it may be NULL when that is 0); its
- * contents on entry do not matter.  hT may be NULL or alias h0.
- * fp32 io with the per-key gate, K = 128 and chunk 64 needs more than 160
- * KiB of LDS and returns GDN_ERR_LDS_BUDGET (chunk 32 runs it), as do the
- * other forward entry points for that shape.
+ * gdn_prepare followed by gdn_scan up to rounding.  hT may be NULL or alias
+ * h0.
+ * Workspace: `workspace` must hold gdn_workspace_bytes(problem) bytes of
+ * device memory, 16-byte aligned (it may be NULL when that is 0: the scalar
+ * gate, or T = 0); its contents on entry do not matter, and it is free again
+ * once the call's work on `stream` is done.  Otherwise GDN_ERR_WORKSPACE
+ * (missing or too small) or GDN_ERR_ALIGNMENT before any launch.
+ * For the per-key gate the call is two launches: a kernel over every chunk at
+ * once forms each chunk's decayed Gram products (A, and P of the read-out)
+ * with every pair's decay split at a row between the two tokens, found by
+ * halving the chunk (TileOPs fused-prepare page: A_g and its inverse), and
+ * the 16-token blocks of (I + A)^-1; it leaves them in the workspace,
+ * 2 chunk^2 values per (chunk, head) in the operand type (fp16 for bf16 io,
+ * fp32 for fp32 io); the re-scan then reads them (kernel-fun KDA re-scan
+ * page's per-chunk algebra).
  */
 gdn_status gdn_forward(const gdn_problem *problem, const void *q, const void *k,
                        const void *v, const float *beta, const float *g,
@@ -158,12 +171,12 @@ gdn_status gdn_forward(const gdn_problem *problem, const void *q, const void *k,
  * nearest even).  o, hT and every other argument are as in gdn_forward;
  * hck and vnew must be non-NULL and 16-byte aligned when T > 0 (with T = 0
  * nothing is written to them and they may be NULL).  hck, vnew and o must
- * not alias each other or any input.  Needs no workspace.
+ * not alias each other or any input.  Workspace as in gdn_forward.
  */
 gdn_status gdn_forward_states(const gdn_problem *problem, const void *q, const void *k,
                               const void *v, const float *beta, const float *g,
                               const float *h0, void *o, float *hT, void *hck, void *vnew,
-                              void *stream);
+                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * gdn_rescan_dq -- the backward pass's forward re-scan (kernel_fun KDA re-scan
@@ -182,11 +195,12 @@ gdn_status gdn_forward_states(const gdn_problem *problem, const void *q, const v
  * dtypes, or the per-key gate at chunk 32, return GDN_ERR_UNSUPPORTED.
  * With T = 0 only hT is
  * written.  Pointers as in gdn_forward_states; dq must not alias any input.
+ * Workspace as in gdn_forward.
  */
 gdn_status gdn_rescan_dq(const gdn_problem *problem, const void *q, const void *k,
                          const void *v, const float *beta, const float *g, const float *h0,
                          const void *dout, float *hT, void *hck, void *vnew, float *dq,
-                         void *stream);
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * gdn_chunk_dq -- dq's chunk-start-state term on its own, from states that
@@ -225,12 +239,13 @@ gdn_status gdn_chunk_dq(const gdn_problem *problem, const void *dout, const void
  *   sequence; h0 NULL means zero states, hT NULL means not written.
  * The state never crosses from one sequence into the next; results equal
  * separate gdn_forward calls per sequence.  Returns GDN_ERR_BAD_SHAPE if
- * problem->B != 1 or n_seqs < 1.  Needs no workspace.
+ * problem->B != 1 or n_seqs < 1.  Workspace as in gdn_forward, of
+ * gdn_workspace_bytes_varlen(problem, n_seqs) bytes.
  */
 gdn_status gdn_forward_varlen(const gdn_problem *problem, const int32_t *cu_seqlens,
                               int64_t n_seqs, const void *q, const void *k, const void *v,
                               const float *beta, const float *g, const float *h0, void *o,
-                              float *hT, void *stream);
+                              float *hT, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * gdn_wait_timeouts -- diagnostics of the bf16-io kernels' internal waits.
@@ -251,8 +266,15 @@ gdn_status gdn_forward_varlen(const gdn_problem *problem, const int32_t *cu_seql
  */
 gdn_status gdn_wait_timeouts(uint32_t *count, int reset);
 
-/* Workspace gdn_forward needs for this problem (0 if none); 0 on bad args. */
+/* Workspace gdn_forward, gdn_forward_states and gdn_rescan_dq need for this
+ * problem: 0 for the scalar gate or T = 0; for the per-key gate
+ * B * ceil(T / chunk) * H * 2 * chunk^2 values of the operand type (fp16 for
+ * bf16 io, fp32 for fp32 io).  0 on bad arguments. */
 size_t gdn_workspace_bytes(const gdn_problem *problem);
+
+/* The same for gdn_forward_varlen over n_seqs packed sequences (the per-key
+ * gate: (ceil(T / chunk) + n_seqs) * H * 2 * chunk^2 values). */
+size_t gdn_workspace_bytes_varlen(const gdn_problem *problem, int64_t n_seqs);
 
 /* Static, human-readable name of a status code. */
 const char *gdn_status_str(gdn_status status);

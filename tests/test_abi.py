@@ -37,7 +37,8 @@ def test_header_declares_the_boundary():
     assert _declared_functions() == sorted(
         ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_forward_states",
          "gdn_forward_varlen", "gdn_rescan_dq", "gdn_chunk_dq", "gdn_workspace_bytes",
-         "gdn_status_str", "gdn_abi_version", "gdn_wait_timeouts"])
+         "gdn_workspace_bytes_varlen", "gdn_status_str", "gdn_abi_version",
+         "gdn_wait_timeouts"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -114,11 +115,41 @@ def test_alignment_rejected(lib, gdn):
     assert _fwd(lib, pr, hT=MISALIGNED) == 4
 
 
-def test_forward_needs_no_workspace(lib, gdn):
-    # the fused forward keeps every intermediate on chip
-    for gate in (0, 1):
-        pr = _problem(gdn, B=2, T=100, H=3, K=64, V=128, gate=gate)
+def test_workspace_sizes(lib, gdn):
+    # the scalar gate keeps every intermediate on chip; the per-key gate's
+    # kernel over all chunks leaves Tmb and P per (chunk, head) in the
+    # workspace: B * ceil(T/C) * H * 2 * C^2 values of the operand type
+    for io, e in ((1, 2), (0, 4)):
+        pr = _problem(gdn, B=2, T=100, H=3, K=64, V=128, gate=0, io=io, o=io)
         assert lib.gdn_workspace_bytes(ctypes.byref(pr)) == 0
+        assert lib.gdn_workspace_bytes_varlen(ctypes.byref(pr), ctypes.c_int64(4)) == 0
+        pr = _problem(gdn, B=2, T=100, H=3, K=64, V=128, gate=1, io=io, o=io)
+        assert lib.gdn_workspace_bytes(ctypes.byref(pr)) == 2 * 2 * 3 * 2 * 64 * 64 * e
+        pr1 = _problem(gdn, B=1, T=100, H=3, K=64, V=128, gate=1, io=io, o=io)
+        assert lib.gdn_workspace_bytes_varlen(ctypes.byref(pr1), ctypes.c_int64(4)) == \
+            (2 + 4) * 3 * 2 * 64 * 64 * e
+        assert lib.gdn_workspace_bytes_varlen(ctypes.byref(pr1), ctypes.c_int64(0)) == 0
+    # T = 0: nothing to form
+    assert lib.gdn_workspace_bytes(ctypes.byref(_problem(gdn, T=0, gate=1))) == 0
+
+
+def test_key_gate_workspace_checked_before_launch(lib, gdn):
+    pr = _problem(gdn, B=1, T=200, H=2, K=128, V=128, gate=1)
+    need = lib.gdn_workspace_bytes(ctypes.byref(pr))
+    assert need > 0
+    assert _fwd(lib, pr, ws=None, ws_bytes=0) == 6
+    assert _fwd(lib, pr, ws_bytes=need - 1) == 6
+    assert _fwd(lib, pr, ws=MISALIGNED, ws_bytes=need) == 4
+    assert _fwd_states(lib, pr, ws=None, ws_bytes=0) == 6
+    assert _rescan(lib, pr, ws_bytes=need - 16) == 6
+    pv = _problem(gdn, B=1, T=200, H=2, K=128, V=128, gate=1)
+    needv = lib.gdn_workspace_bytes_varlen(ctypes.byref(pv), ctypes.c_int64(2))
+    assert _fwd_varlen(lib, pv, ws_bytes=needv - 1) == 6
+    # fp32 io at K = 128, chunk 64 (the four-wave kernel without its own
+    # Gram tiles) now fits; it asks for its workspace like any other shape
+    p32 = _problem(gdn, io=0, o=0, gate=1, K=128, V=128, chunk=64)
+    assert _fwd(lib, p32, ws=None, ws_bytes=0) == 6
+    assert _fwd_states(lib, p32, ws=None, ws_bytes=0) == 6
 
 
 def test_lds_budget_reported_before_launch(lib, gdn):
@@ -132,9 +163,9 @@ def test_lds_budget_reported_before_launch(lib, gdn):
 
 
 def _fwd_states(lib, pr, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, h0=None, o=FAKE,
-                hT=None, hck=FAKE, vnew=FAKE):
+                hT=None, hck=FAKE, vnew=FAKE, ws=FAKE, ws_bytes=1 << 40):
     return lib.gdn_forward_states(ctypes.byref(pr), q, k, v, beta, g, h0, o, hT, hck,
-                                  vnew, None)
+                                  vnew, ws, ctypes.c_size_t(ws_bytes), None)
 
 
 def test_forward_states_validates_before_launch(lib, gdn):
@@ -146,7 +177,7 @@ def test_forward_states_validates_before_launch(lib, gdn):
     bad = _problem(gdn, K=96)
     assert _fwd_states(lib, bad) == 3
     assert lib.gdn_forward_states(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
-                                  FAKE, FAKE, None) == 1
+                                  FAKE, FAKE, FAKE, ctypes.c_size_t(0), None) == 1
 
 
 def test_forward_states_empty_sequence_needs_no_buffers(lib, gdn):
@@ -157,9 +188,9 @@ def test_forward_states_empty_sequence_needs_no_buffers(lib, gdn):
 
 
 def _fwd_varlen(lib, pr, cu=FAKE, n=2, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, h0=None,
-                o=FAKE, hT=None):
+                o=FAKE, hT=None, ws=FAKE, ws_bytes=1 << 40):
     return lib.gdn_forward_varlen(ctypes.byref(pr), cu, ctypes.c_int64(n), q, k, v, beta, g,
-                                  h0, o, hT, None)
+                                  h0, o, hT, ws, ctypes.c_size_t(ws_bytes), None)
 
 
 def test_forward_varlen_validates_before_launch(lib, gdn):
@@ -191,8 +222,9 @@ def test_streams_beyond_32bit_offsets_rejected(lib, gdn):
 
 
 def _rescan(lib, pr, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, h0=None, do=FAKE, hT=None,
-            hck=FAKE, vnew=FAKE, dq=FAKE):
-    return lib.gdn_rescan_dq(ctypes.byref(pr), q, k, v, beta, g, h0, do, hT, hck, vnew, dq, None)
+            hck=FAKE, vnew=FAKE, dq=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return lib.gdn_rescan_dq(ctypes.byref(pr), q, k, v, beta, g, h0, do, hT, hck, vnew, dq,
+                             ws, ctypes.c_size_t(ws_bytes), None)
 
 
 def test_rescan_dq_validates_before_launch(lib, gdn):
@@ -233,15 +265,6 @@ def test_chunk_dq_validates_before_launch(lib, gdn):
     assert _chunk_dq(lib, _problem(gdn, B=1, T=64, H=1 << 17, K=128, V=128)) == 3
     # no tokens: nothing to do, no buffers needed
     assert _chunk_dq(lib, _problem(gdn, T=0), do=None, hck=None, dq=None) == 0
-
-
-def test_fp32_key_gate_k128_chunk64_reports_the_lds_budget(lib, gdn):
-    # the one listed shape the four-wave kernel cannot hold in 160 KiB of LDS:
-    # a status before any launch, for every forward entry point
-    pr = _problem(gdn, io=0, o=0, gate=1, K=128, V=128, chunk=64)
-    assert _fwd(lib, pr) == 5
-    assert _fwd_states(lib, pr) == 5
-    assert _fwd_varlen(lib, _problem(gdn, B=1, io=0, o=0, gate=1, K=128, V=128, chunk=64)) == 5
 
 
 def test_wait_timeouts_rejects_null(lib, gdn):

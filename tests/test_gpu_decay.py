@@ -89,3 +89,86 @@ def test_scalar_gate_strong_decay_prepare_scan(recipe, C):
         xv = _np(x)
         assert np.isfinite(xv).all(), "%s not finite" % name
         assert oracle.rel_err(xv, ref) <= TOL["bf16"], name
+
+
+KEY_CASES = [
+    # K, V, C, io, recipe
+    (128, 128, 64, "bf16", "b1"),
+    (128, 128, 64, "bf16", "b0"),
+    (128, 128, 64, "bf16", "bm2"),
+    (128, 128, 64, "bf16", "pin20"),
+    (128, 128, 64, "bf16", "reset"),
+    (128, 128, 32, "bf16", "b0"),
+    (128, 64, 32, "bf16", "pin20"),
+    (64, 64, 32, "bf16", "bm2"),
+    (64, 128, 64, "bf16", "reset"),
+    (128, 128, 64, "fp32", "bm2"),
+    (128, 128, 64, "fp32", "pin20"),
+    (64, 64, 32, "fp32", "reset"),
+    (64, 64, 64, "fp32", "b0"),
+]
+
+
+@pytest.mark.parametrize("K,V,C,io,recipe", KEY_CASES, ids=lambda c: str(c))
+def test_key_gate_strong_decay(K, V, C, io, recipe):
+    _forward_case("decay_key_%s" % recipe, 2, 2 * C + 21, 2, K, V, C, io, "key", recipe,
+                  seed=61 + K + C, o_dtypes=["fp32"] if io == "fp32" else ["fp32", "bf16"])
+
+
+@pytest.mark.parametrize("recipe", ["bm2", "pin20"])
+@pytest.mark.parametrize("C", [32, 64])
+def test_key_gate_strong_decay_prepare_scan(recipe, C):
+    """The two-stage path with the per-key gate: gdn_prepare's w, u against
+    the fp64 chunk form, gdn_scan on them against the token recurrence."""
+    B, T, H, K, V = 1, 2 * C + 9, 2, 64, 64
+    inp = strong_inputs(B, T, H, K, V, "key", recipe, seed=63 + C, io="bf16", h0=True)
+    d = {n: (None if x is None else x.to(_dev())) for n, x in inp.items()}
+    w, u, gc = gdn.prepare(d["k"], d["v"], d["beta"], d["g"], C)
+    o, hT = gdn.scan(d["q"], d["k"], w, u, gc, C, d["h0"], o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    gr, wr, ur = oracle.chunk_prepare(inp["k"].float().numpy(), inp["v"].float().numpy(),
+                                      inp["beta"].numpy(), inp["g"].numpy(), C)
+    o_ref, h_ref = _ref(inp)
+    for name, x, ref in (("gcum", gc, gr), ("w", w, wr), ("u", u, ur), ("o", o, o_ref),
+                         ("hT", hT, h_ref)):
+        xv = _np(x)
+        assert np.isfinite(xv).all(), "%s not finite" % name
+        err = oracle.rel_err(xv, ref)
+        _record("decay_key_prepare_scan_%s" % recipe, C=C, name=name, rel=err)
+        assert err <= (1e-5 if name == "gcum" else TOL["bf16"]), (name, err)
+
+
+@pytest.mark.parametrize("recipe", ["b0", "pin20"])
+def test_key_gate_strong_decay_states_and_varlen(recipe):
+    """The per-key gate's other forward entry points at strong gates: saved
+    states against the oracle's, packed sequences against per-sequence runs
+    of the oracle."""
+    B, T, H, K, V, C = 1, 150, 2, 128, 128, 64
+    inp = strong_inputs(B, T, H, K, V, "key", recipe, seed=71, io="bf16", h0=True)
+    d = {n: (None if x is None else x.to(_dev())) for n, x in inp.items()}
+    f = lambda x: None if x is None else x.float().numpy()
+    o, hT, hck, vnew = gdn.forward_states(d["q"], d["k"], d["v"], d["beta"], d["g"], C, d["h0"],
+                                          o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, h_ref, hck_ref, vn_ref = oracle.token_states(
+        f(inp["q"]), f(inp["k"]), f(inp["v"]), f(inp["beta"]), f(inp["g"]), C, f(inp["h0"]))
+    for name, x, ref in (("o", o, o_ref), ("hT", hT, h_ref), ("hck", hck, hck_ref),
+                         ("vnew", vnew, vn_ref)):
+        xv = _np(x)
+        assert np.isfinite(xv).all(), name
+        assert oracle.rel_err(xv, ref) <= TOL["bf16"], (name, oracle.rel_err(xv, ref))
+    # packed: the stream cut into sequences of 70 and 80 tokens, own states
+    lens = [70, 80]
+    cu = torch.tensor([0, 70, 150], dtype=torch.int32, device=_dev())
+    h0v = (0.1 * torch.randn(2, H, K, V, generator=torch.Generator().manual_seed(5))).to(_dev())
+    ov, hTv = gdn.forward_varlen(d["q"], d["k"], d["v"], d["beta"], d["g"], cu, C, h0v,
+                                 o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    s0 = 0
+    for n, L in enumerate(lens):
+        sl = lambda x: f(x)[:, s0:s0 + L]
+        o_r, h_r = oracle.token_recurrence(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]),
+                                           sl(inp["beta"]), sl(inp["g"]), f(h0v)[n:n + 1])
+        assert oracle.rel_err(_np(ov)[:, s0:s0 + L], o_r) <= TOL["bf16"]
+        assert oracle.rel_err(_np(hTv)[n:n + 1], h_r) <= TOL["bf16"]
+        s0 += L
