@@ -160,8 +160,8 @@ def test_key_gate_strong_decay_states_and_varlen(recipe):
     # packed: the stream cut into sequences of 70 and 80 tokens, own states
     lens = [70, 80]
     cu = torch.tensor([0, 70, 150], dtype=torch.int32, device=_dev())
-    h0v = (0.1 * torch.randn(2, H, K, V, generator=torch.Generator().manual_seed(5))).to(_dev())
-    ov, hTv = gdn.forward_varlen(d["q"], d["k"], d["v"], d["beta"], d["g"], cu, C, h0v,
+    h0v = 0.1 * torch.randn(2, H, K, V, generator=torch.Generator().manual_seed(5))
+    ov, hTv = gdn.forward_varlen(d["q"], d["k"], d["v"], d["beta"], d["g"], cu, C, h0v.to(_dev()),
                                  o_dtype=torch.float32)
     torch.cuda.synchronize()
     s0 = 0
