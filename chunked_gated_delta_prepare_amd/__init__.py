@@ -44,7 +44,8 @@ STATUS = {
 EXPORTS = ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_forward_states",
            "gdn_forward_varlen", "gdn_rescan_dq", "gdn_chunk_dq", "gdn_workspace_bytes",
            "gdn_workspace_bytes_varlen", "gdn_status_str", "gdn_abi_version",
-           "gdn_wait_timeouts"]
+           "gdn_wait_timeouts", "gdn_forward_noalloc"]
+NOALLOC_SCRATCH_BYTES = 32 << 20
 ABI_VERSION = 7
 
 
@@ -87,8 +88,10 @@ def load_library(path: str | None = None):
         lib.gdn_forward_varlen.argtypes = [pp, vp, ctypes.c_int64] + [vp] * 9 + [sz, vp]
         lib.gdn_rescan_dq.argtypes = [pp] + [vp] * 12 + [sz, vp]
         lib.gdn_chunk_dq.argtypes = [pp] + [vp] * 4
+        lib.gdn_forward_noalloc.argtypes = [pp] + [vp] * 9
         for f in (lib.gdn_prepare, lib.gdn_scan, lib.gdn_forward, lib.gdn_forward_states,
-                  lib.gdn_forward_varlen, lib.gdn_rescan_dq, lib.gdn_chunk_dq):
+                  lib.gdn_forward_varlen, lib.gdn_rescan_dq, lib.gdn_chunk_dq,
+                  lib.gdn_forward_noalloc):
             f.restype = ctypes.c_int
         lib.gdn_workspace_bytes.argtypes = [pp]
         lib.gdn_workspace_bytes.restype = sz
@@ -259,6 +262,24 @@ def _workspace(lib, pr, device, workspace, n_seqs=0):
 def forward(q, k, v, beta, g, chunk, h0=None, *, o_dtype=None, o=None, hT=None,
             output_final_state=True, workspace=None, stream=None):
     """Whole forward pass: returns (o [B,T,H,V], hT [B,H,K,V] fp32 or None)."""
+    return _forward(q, k, v, beta, g, chunk, h0, o_dtype, o, hT, output_final_state,
+                    workspace, stream, noalloc=False)
+
+
+def forward_noalloc(q, k, v, beta, g, chunk, h0=None, *, o=None, hT=None, stream=None):
+    """gdn_forward_noalloc: the forward pass with the per-key gate's workspace
+    taken from the library's static device scratch (at most
+    NOALLOC_SCRATCH_BYTES) instead of an allocation.  The library call itself
+    allocates nothing; o and hT, which the caller must pass, are written in
+    place and returned."""
+    if o is None:
+        raise ValueError("forward_noalloc writes into a caller-provided o")
+    return _forward(q, k, v, beta, g, chunk, h0, o.dtype, o, hT, hT is not None, None, stream,
+                    noalloc=True)
+
+
+def _forward(q, k, v, beta, g, chunk, h0, o_dtype, o, hT, output_final_state, workspace,
+             stream, noalloc):
     torch = _torch()
     lib = load_library()
     B, T, H, K = q.shape
@@ -280,6 +301,11 @@ def forward(q, k, v, beta, g, chunk, h0=None, *, o_dtype=None, o=None, hT=None,
     if hT is not None:
         _need(hT, "hT", torch.float32, (B, H, K, V))
     pr = _problem(q, v, chunk, per_key, od)
+    if noalloc:
+        rc = lib.gdn_forward_noalloc(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                     _ptr(g), _ptr(h0), _ptr(o), _ptr(hT), _stream(stream))
+        _check("gdn_forward_noalloc", rc)
+        return o, hT
     workspace, ws_bytes = _workspace(lib, pr, q.device, workspace)
     rc = lib.gdn_forward(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
                          _ptr(h0), _ptr(o), _ptr(hT), _ptr(workspace), ws_bytes, _stream(stream))

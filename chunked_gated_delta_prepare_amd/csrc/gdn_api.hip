@@ -180,6 +180,37 @@ unsigned *wait_count_ptr() {
     return g_wait_addr[dev];
 }
 
+// Device memory for gdn_forward_noalloc: the per-key gate's Gram workspace
+// lives in this file-scope array instead of caller memory.  Each device
+// that loads the library holds its own copy until the process ends; its
+// address is looked up once per device, with that device current, and only
+// that address (never the array's name, which on the host is a stand-in)
+// is handed to kernels.  Every no-alloc call on a device shares the array:
+// the Gram kernel writes every slot the re-scan reads before the re-scan
+// starts (same stream), so nothing needs clearing, but calls that overlap
+// in time on one device (other streams, other threads) race.
+constexpr size_t kNoAllocScratchBytes = GDN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+std::mutex g_scr_mu;
+void *g_scr_addr[kMaxDevices];
+bool g_scr_looked_up[kMaxDevices];
+}  // namespace
+
+void *scratch_ptr() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lk(g_scr_mu);
+    if (!g_scr_looked_up[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress((void **)&ptr, HIP_SYMBOL(scratch)) != hipSuccess) ptr = nullptr;
+        g_scr_addr[dev] = ptr;
+        g_scr_looked_up[dev] = true;
+    }
+    return g_scr_addr[dev];
+}
+
 void wait_params(unsigned &limit, unsigned &bias) {
     // GDN_WAIT_FORCE_TIMEOUT=1 makes every bounded wait give up after a few
     // polls (a test of the timeout path; results are then garbage)
@@ -257,6 +288,31 @@ gdn_status gdn_forward(const gdn_problem *problem, const void *q, const void *k,
     }
     return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, nullptr, nullptr, nullptr, 0,
                            workspace, (hipStream_t)stream);
+}
+
+gdn_status gdn_forward_noalloc(const gdn_problem *problem, const void *q, const void *k,
+                               const void *v, const float *beta, const float *g,
+                               const float *h0, void *o, float *hT, void *stream) {
+    gdn_status st = check_problem(problem);
+    if (st != GDN_OK) return st;
+    if (problem->T == 0) {
+        st = check_ptrs({}, {h0, hT});
+        if (st != GDN_OK) return st;
+        if (!hT) return GDN_OK;
+        return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, nullptr, nullptr, nullptr,
+                               0, nullptr, (hipStream_t)stream);
+    }
+    st = check_ptrs({q, k, v, beta, g, o}, {h0, hT});
+    if (st != GDN_OK) return st;
+    const int64_t need = kda_workspace_bytes(problem, 0);
+    if (need > (int64_t)kNoAllocScratchBytes) return GDN_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (need > 0) {
+        ws = scratch_ptr();
+        if (!ws) return GDN_ERR_HIP;
+    }
+    return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, nullptr, nullptr, nullptr, 0, ws,
+                           (hipStream_t)stream);
 }
 
 gdn_status gdn_forward_states(const gdn_problem *problem, const void *q, const void *k,

@@ -266,6 +266,28 @@ gdn_status gdn_forward_varlen(const gdn_problem *problem, const int32_t *cu_seql
  */
 gdn_status gdn_wait_timeouts(uint32_t *count, int reset);
 
+/*
+ * gdn_forward_noalloc -- gdn_forward for callers that cannot allocate device
+ * memory (code under stream capture into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and launches as
+ * gdn_forward, without the workspace: the per-key gate's Gram workspace is
+ * taken from a static device array of GDN_NOALLOC_SCRATCH_BYTES bytes that
+ * the library holds on each device it runs on until the process ends.  The
+ * call allocates nothing and frees nothing.  Returns GDN_ERR_WORKSPACE,
+ * before anything is enqueued, when gdn_workspace_bytes(problem) exceeds
+ * that size (the scalar gate needs none and is never refused for it), and
+ * GDN_ERR_HIP if the array's device address cannot be looked up (done once
+ * per device, on the first call that needs it, with the current device).
+ * All calls on one device share the array: calls that may run at the same
+ * time on one device (different streams or host threads without ordering
+ * between them) race and corrupt each other's results; calls ordered on one
+ * stream are safe.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+gdn_status gdn_forward_noalloc(const gdn_problem *problem, const void *q, const void *k,
+                               const void *v, const float *beta, const float *g,
+                               const float *h0, void *o, float *hT, void *stream);
+
 /* Workspace gdn_forward, gdn_forward_states and gdn_rescan_dq need for this
  * problem: 0 for the scalar gate or T = 0; for the per-key gate
  * B * ceil(T / chunk) * H * 2 * chunk^2 values of the operand type (fp16 for

@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
         ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_forward_states",
          "gdn_forward_varlen", "gdn_rescan_dq", "gdn_chunk_dq", "gdn_workspace_bytes",
          "gdn_workspace_bytes_varlen", "gdn_status_str", "gdn_abi_version",
-         "gdn_wait_timeouts"])
+         "gdn_wait_timeouts", "gdn_forward_noalloc"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -150,6 +150,22 @@ def test_key_gate_workspace_checked_before_launch(lib, gdn):
     p32 = _problem(gdn, io=0, o=0, gate=1, K=128, V=128, chunk=64)
     assert _fwd(lib, p32, ws=None, ws_bytes=0) == 6
     assert _fwd_states(lib, p32, ws=None, ws_bytes=0) == 6
+
+
+def test_noalloc_refuses_oversize_before_launch(lib, gdn):
+    # the static scratch holds GDN_NOALLOC_SCRATCH_BYTES; a per-key problem
+    # that needs more is refused before the device is touched
+    C = 64
+    per = 2 * C * C * 2                                  # bf16 io: fp16 Tmb and P
+    nt = gdn.NOALLOC_SCRATCH_BYTES // per
+    fits = _problem(gdn, B=1, T=nt * C, H=1, K=128, V=128, gate=1, chunk=C)
+    assert lib.gdn_workspace_bytes(ctypes.byref(fits)) == gdn.NOALLOC_SCRATCH_BYTES
+    over = _problem(gdn, B=1, T=nt * C + 1, H=1, K=128, V=128, gate=1, chunk=C)
+    st = lib.gdn_forward_noalloc(ctypes.byref(over), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                 None, None)
+    assert st == 6
+    assert lib.gdn_forward_noalloc(ctypes.byref(over), None, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                   None, None) == 1
 
 
 def test_lds_budget_reported_before_launch(lib, gdn):
