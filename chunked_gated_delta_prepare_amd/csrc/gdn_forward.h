@@ -73,10 +73,26 @@ struct FwdParams {
     int swizzle;
 };
 
-// Workspace slot of one (chunk, head) for the per-key gate: Tmb then P,
-// [C][C] each, in the operand type.
+// Workspace slot of one (chunk, head) for the per-key gate.  It starts with
+// Tmb then P, [C][C] row-major each in the operand type (kda_slot_elems
+// elements).  With bf16 io (fp16 operands) the pipelined re-scan's operand
+// tiles follow: qd = q e^gcum, kd = k e^gcum and kg = k e^(gl - gcum), [C][K]
+// fp16 each, laid out as that kernel's LDS tiles (16-byte chunks swizzled by
+// row, 4-column groups permuted: swz, pcol), then e^gl [K] fp32.
 template <int C>
 constexpr int64_t kda_slot_elems() { return 2 * (int64_t)C * C; }
+template <int C, int K>
+struct KdaSlotOps {
+    static constexpr int kQd = 2 * C * C * 2;
+    static constexpr int kKd = kQd + C * K * 2;
+    static constexpr int kKg = kKd + C * K * 2;
+    static constexpr int kFl = kKg + C * K * 2;
+    static constexpr int kBytes = kFl + K * 4;
+};
+template <int C, int K, typename IO>
+constexpr int64_t kda_slot_bytes() {
+    return sizeof(IO) == 4 ? kda_slot_elems<C>() * 4 : (int64_t)KdaSlotOps<C, K>::kBytes;
+}
 
 // The tokens of stream b: batch row b, [0, T) of a [B, T, H, .] layout, or
 // with VL (cu set) the packed sequence b, tokens [cu[b], cu[b+1]) of a
@@ -545,7 +561,8 @@ __global__ __launch_bounds__(kThreads, 1) void forward_kernel(FwdParams p) {
             // workspace (their tiles may have held the gcum rows until the
             // barrier above)
             {
-                const OpT *src = (const OpT *)p.ws + ((int64_t)(slot0 + c) * H + h) * kda_slot_elems<C>();
+                const OpT *src = (const OpT *)((const char *)p.ws +
+                                               ((int64_t)(slot0 + c) * H + h) * kda_slot_bytes<C, K, IO>());
                 constexpr int PER = 16 / L::E;
                 for (int i = tid; i < 2 * C * C / PER; i += kThreads) {
                     const int e0 = i * PER, tile = e0 / (C * C), rc = e0 % (C * C);

@@ -18,7 +18,7 @@ static bool fits_32bit_streams(const gdn_problem *pr) {
                                     th * gdim * 4});
     // per-key gate: one stream's workspace slots for all heads
     const int64_t nt = (pr->T + pr->chunk - 1) / pr->chunk;
-    const int64_t ws = pr->gate == GDN_GATE_KEY ? nt * pr->H * 2 * (int64_t)pr->chunk * pr->chunk * sio : 0;
+    const int64_t ws = pr->gate == GDN_GATE_KEY ? nt * pr->H * kda_slot_bytes_host(pr) : 0;
     return worst < ((int64_t)1 << 32) && ws < ((int64_t)1 << 32);
 }
 

@@ -149,10 +149,11 @@ __device__ __forceinline__ void wait_counter(const unsigned *ctr, unsigned targe
     asm volatile("" ::: "memory");
 }
 
-// Barrier of the four prepare waves: an LDS arrival counter that only grows
-// (four arrivals per barrier), with a bounded wait.
+// Barrier of N waves (the four prepare waves by default): an LDS arrival
+// counter that only grows (N arrivals per barrier), with a bounded wait.
+template <unsigned N = 4>
 __device__ __forceinline__ void prep_barrier(unsigned *ctr, unsigned &target, WaitCtl &wc) {
-    target += 4;
+    target += N;
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     if (lane_id() == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);

@@ -1,23 +1,22 @@
 // gdn_forward for the per-key gate (Kimi-Delta-Attention), pipelined over
 // chunks like forward_pipe_kernel (gdn_forward_pipe.h), bf16 io.
 //
-// The chunk's decayed Gram products, its triangular solve blocks and P come
-// from kda_gram_kernel (gdn_kda_gram.h), which forms them for every chunk in
-// parallel with every decay factor at most 1, and leaves them in a workspace
-// slot per (chunk, head).  This kernel is the inter-chunk re-scan of the
-// kernel-fun KDA re-scan page with every operand referenced to the chunk's
-// ends, so that every factor is a decay:
+// kda_gram_kernel (gdn_kda_gram.h) forms, for every chunk in parallel and
+// with every decay factor at most 1, the chunk's triangular solve blocks, P,
+// and this kernel's operands, and leaves them in a workspace slot per
+// (chunk, head).  This kernel is the inter-chunk re-scan of the kernel-fun
+// KDA re-scan page with every operand referenced to the chunk's ends, so
+// that every factor is a decay:
 //     qd = q e^gcum,  kd = k e^gcum,  kg = k e^(gl - gcum)   (per key column;
 //                                                           gl: the last row)
 //     X = kd h,  Y = qd h,  R' = v - X,
 //     v' = (I + A)^-1 diag(beta) R'   (by blocks of 16 tokens from Tmb),
 //     o = Y + P v',  h <- e^gl h + kg^T v'   (row-wise by the key vector).
 // The schedule is forward_pipe_kernel's: chain waves 0..3 run the re-scan of
-// chunk c with h in MFMA accumulators while prepare waves 4..7 build chunk
-// c+1: the chunk-local cumsum of the C x K gate (each thread holds four key
-// columns of C/NSEG rows in registers; the segment totals meet in LDS), the
-// three fp16 operand tiles, the per-key e^gl, and the chunk's Tmb and P
-// copied from the workspace into the LDS layout the chain reads.
+// chunk c with h in MFMA accumulators while prepare waves 4..7 copy chunk
+// c+1's slot (the operand tiles, already in the chain's LDS layout; Tmb and
+// P into that layout; e^gl) and its raw v tile into LDS, and issue the loads
+// of chunk c+2.
 #pragma once
 
 #include "gdn_forward_pipe.h"
@@ -25,7 +24,13 @@
 
 namespace gdn {
 
-template <int C, int K>
+// Prepare waves of the per-key kernel: four, one per SIMD.
+template <int C, int K, bool DQ>
+constexpr int kda_prep_waves() { return 4; }
+template <int C, int K, bool DQ>
+constexpr int kda_threads() { return 256 + 64 * kda_prep_waves<C, K, DQ>(); }
+
+template <int C, int K, int NPT = 256>
 struct PipeKdaLayout {
     static constexpr int NB = C / 16;
     static constexpr int kQK = C * K * 2;                // one fp16 C x K tile
@@ -38,20 +43,35 @@ struct PipeKdaLayout {
     static constexpr int kP = kTmb + 2 * kCC;            // [2] P
     static constexpr int kV = kP + 2 * kCC;              // [2] raw v tiles
     static constexpr int kKf = kV + 2 * kVT;             // [2][K] e^gl per key
-    // gate cumsum segments: a prepare thread holds 4 key columns of NR rows
-    static constexpr int NSEG = 256 * 4 / K;
-    static constexpr int NR = C / NSEG;
-    static constexpr int kSeg = kKf + 2 * K * 4;         // [NSEG][K] segment totals
-    static constexpr int kSync = kSeg + NSEG * K * 4;
+    static constexpr int kSync = kKf + 2 * K * 4;
     static constexpr int kBytes = kSync + 16;
-    static_assert(NR >= 1 && NSEG * NR == C, "gate segments tile the chunk");
     // workspace pieces per chunk: Tmb and P, 16 bytes each
-    static constexpr int NWS = 2 * C * C * 2 / 16 / 256;
-    static_assert(NWS >= 1 && NWS * 16 * 256 == 2 * C * C * 2, "workspace pieces per thread");
+    static constexpr int NWS = 2 * C * C * 2 / 16 / NPT;
+    static_assert(NWS >= 1 && NWS * 16 * NPT == 2 * C * C * 2, "workspace pieces per thread");
 };
 
 __device__ __forceinline__ u32x2 bload64(rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+}
+
+// The raw v tile and the workspace slot of chunk n into registers (see the
+// prepare waves of forward_pipe_kda_kernel): v pieces at vv_off plus n
+// times v_chunk bytes; the slot's Tmb and P pieces, operand pieces and e^gl
+// at n times slot_stride.
+template <int NVV, int NWS, int NOP, int NPT>
+__device__ __forceinline__ void kda_slot_load(rsrc_t rv_, rsrc_t rw_, const uint32_t (&vv_off)[NVV],
+                                              int pt, bool fl_thread, uint32_t v_chunk,
+                                              uint32_t slot_stride, int k_ops, int k_fl, int n,
+                                              u32x4 (&rv)[NVV], u32x4 (&rw)[NWS], u32x4 (&ro)[NOP],
+                                              u32x4 &rf) {
+    const uint32_t sv = (uint32_t)n * v_chunk, so = (uint32_t)n * slot_stride;
+#pragma unroll
+    for (int j = 0; j < NVV; ++j) rv[j] = bload128(rv_, vv_off[j], sv);
+#pragma unroll
+    for (int j = 0; j < NWS; ++j) rw[j] = bload128(rw_, (uint32_t)(16 * (pt + NPT * j)), so);
+#pragma unroll
+    for (int j = 0; j < NOP; ++j) ro[j] = bload128(rw_, (uint32_t)(k_ops + 16 * (pt + NPT * j)), so);
+    if (fl_thread) rf = bload128(rw_, (uint32_t)(k_fl + 16 * pt), so);
 }
 
 // DQ: the backward's re-scan (the KDA re-scan page's kernel): the chunk-start
@@ -60,13 +80,13 @@ __device__ __forceinline__ u32x2 bload64(rsrc_t r, uint32_t voff, uint32_t soff)
 // state is staged in the q~ and k~ tiles of the slot the chain has just
 // finished with, which hold K x 64 bf16 at C = 64.
 template <int C, int K, typename OT, bool ST = false, bool VL = false, bool DQ = false>
-__global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdParams p) {
-    typedef PipeKdaLayout<C, K> L;
+__global__ __launch_bounds__((kda_threads<C, K, DQ>()), 1) void forward_pipe_kda_kernel(FwdParams p) {
+    constexpr int NPW = kda_prep_waves<C, K, DQ>(), NPT = 64 * NPW;
+    typedef PipeKdaLayout<C, K, NPT> L;
     typedef Mma<_Float16> M;
     typedef bf16_t IO;
     constexpr int NB = C / 16, NKB = K / 16;
     constexpr int SIO = 2, SO = sizeof(OT);
-    constexpr int NSEG = L::NSEG, NR = L::NR;
     static_assert(L::kBytes <= kLdsBytesMax, "LDS budget");
     static_assert(NB == 2 || NB == 4, "chunk 32 or 64");
     static_assert(K == 64 || K == 128, "key dim 64 or 128");
@@ -80,7 +100,6 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
     _Float16 *Pb = (_Float16 *)(smem + L::kP);
     uint16_t *Vb = (uint16_t *)(smem + L::kV);
     float *Kf = (float *)(smem + L::kKf);
-    float *segt = (float *)(smem + L::kSeg);
     unsigned *sync_ctr = (unsigned *)(smem + L::kSync);
 
     const int wv = wave_id(), l = lane_id(), tid = threadIdx.x;
@@ -91,7 +110,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
     const int T = sr.T, H = p.H, V = p.V;
     const int nt = (T + C - 1) / C;
     const int64_t row0 = sr.row0;
-    const uint32_t rsK = (uint32_t)(H * K), rsV = (uint32_t)(H * V);
+    const uint32_t rsV = (uint32_t)(H * V);
     WaitCtl wc{p.wait_count, p.wait_limit, p.wait_bias, 0u};
 
     if (tid == 0) {
@@ -300,12 +319,9 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
         // raised priority measured 7 % faster)
         const int pt = tid - 256;
         if constexpr (ST && !DQ) __builtin_amdgcn_s_setprio(3);
-        const rsrc_t rq_ = make_rsrc((const IO *)p.q + row0 * K, (uint32_t)T * rsK * SIO);
-        const rsrc_t rk_ = make_rsrc((const IO *)p.k + row0 * K, (uint32_t)T * rsK * SIO);
         const rsrc_t rv_ = make_rsrc((const IO *)p.v + row0 * V, (uint32_t)T * rsV * SIO);
-        const rsrc_t rg_ = make_rsrc(p.g + row0 * K, (uint32_t)T * rsK * 4);
         // this stream's workspace slots (see slot_chunk): chunk n of stream b
-        // is slot slot0 + n, each slot H heads of Tmb and P
+        // is slot slot0 + n, each slot H heads of KdaSlotOps
         int slot0 = 0;
         if constexpr (VL) {
             for (int m = 0; m < b; ++m) {
@@ -317,133 +333,74 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kda_kernel(FwdPa
         } else {
             slot0 = b * nt;
         }
-        constexpr uint32_t kSlotBytes = (uint32_t)(kda_slot_elems<C>() * 2);
+        typedef KdaSlotOps<C, K> SO;
+        constexpr uint32_t kSlotBytes = (uint32_t)SO::kBytes;
         const rsrc_t rw_ = make_rsrc((const char *)p.ws + ((int64_t)slot0 * H + h) * kSlotBytes,
                                      (uint32_t)nt * (uint32_t)H * kSlotBytes);
 
-        // thread (seg, cg): rows seg NR .. +NR-1, key columns 4 cg .. 4 cg + 3
-        const int cg = pt % (K / 4), seg = pt / (K / 4), kc = 4 * cg;
-        const uint32_t qk_off = ((uint32_t)(seg * NR) * rsK + kc) * SIO;
-        const uint32_t g_off = ((uint32_t)(seg * NR) * rsK + kc) * 4;
-        int qk_lds[NR];
-#pragma unroll
-        for (int i = 0; i < NR; ++i) qk_lds[i] = swz<K>(seg * NR + i, pcol(kc));
-        constexpr int NVV = C * 64 / 8 / 256;            // v vectors per thread
+        constexpr int NVV = C * 64 / 8 / NPT;            // v vectors per thread
         static_assert(NVV >= 1, "tile smaller than the prepare waves");
         uint32_t vv_off[NVV];
         int vv_lds[NVV];
 #pragma unroll
         for (int j = 0; j < NVV; ++j) {
-            const int i = pt + 256 * j, row = i / 8, ch = i % 8;
+            const int i = pt + NPT * j, row = i / 8, ch = i % 8;
             vv_off[j] = ((uint32_t)row * rsV + vt * 64 + 8 * ch) * SIO;
             vv_lds[j] = swz<64>(row, 8 * ch);
         }
-        // Tmb and P: 16-byte pieces of 8 columns, placed in the swizzled,
-        // column-permuted layout of the chain's operand tiles
+        // Tmb and P (row-major in the slot): 16-byte pieces of 8 columns,
+        // placed in the swizzled, column-permuted layout of the chain's tiles
         constexpr int NWS = L::NWS;
         int ws_lds[NWS][2];
 #pragma unroll
         for (int j = 0; j < NWS; ++j) {
-            const int e0 = 8 * (pt + 256 * j), tile = e0 / (C * C), rc = e0 % (C * C);
+            const int e0 = 8 * (pt + NPT * j), tile = e0 / (C * C), rc = e0 % (C * C);
             const int row = rc / C, col = rc % C;
             const int base = tile ? (L::kP - L::kTmb) / 2 : 0;      // in halves from Tmb slot 0
             ws_lds[j][0] = base + swz<C>(row, pcol(col));
             ws_lds[j][1] = base + swz<C>(row, pcol(col + 4));
         }
+        // the operand tiles qd, kd, kg, already in the tiles' layout: 16-byte
+        // pieces copied as they are, NOP per thread (piece j of thread pt is
+        // byte 16 (pt + NPT j) of the three tiles, tile (pt + NPT j) / (C K / 8))
+        constexpr int NOP = 3 * C * K * 2 / 16 / NPT;
+        static_assert(NOP * 16 * NPT == 3 * C * K * 2, "operand pieces per thread");
+        constexpr int PPT = C * K * 2 / 16;              // pieces per tile
+        const bool fl_thread = pt < K / 4;                // e^gl: 16 bytes each
 
-        u32x2 rq[NR], rk[NR];
-        float4v rg[NR];
-        u32x4 rv[NVV], rw[NWS];
-        // The loads of chunk n come in pieces, each issued as soon as the
-        // registers it fills are free: the CU's memory pipeline takes about a
-        // cycle per 64 bytes, and a chunk's loads issued at once would stall
-        // the issuing waves for most of that time.
-        auto load_v_ws = [&](int n) {
-            const uint32_t t0 = (uint32_t)(n * C);
+        u32x4 rv[NVV], rw[NWS], ro[NOP], rf = {0, 0, 0, 0};
+        // The loads of chunk n + 1 are issued right after chunk n's pieces are
+        // in LDS, so they have the chain's whole period to arrive.
+        for (int c = -1; c < nt; ++c) {
+            const int n = c + 1;
+            if (n < nt) {
+                if (n == 0)
+                    kda_slot_load<NVV, NWS, NOP, NPT>(rv_, rw_, vv_off, pt, fl_thread, rsV * SIO * (uint32_t)C,
+                                                      (uint32_t)H * kSlotBytes, SO::kQd, SO::kFl, 0, rv, rw, ro, rf);
+                const int slot = n & 1;
+                _Float16 *Tmb = Tmbb + slot * C * C;
+                uint16_t *Vs = Vb + slot * C * 64;
 #pragma unroll
-            for (int j = 0; j < NVV; ++j) rv[j] = bload128(rv_, vv_off[j], t0 * rsV * SIO);
+                for (int j = 0; j < NVV; ++j) *(u32x4 *)(Vs + vv_lds[j]) = rv[j];
 #pragma unroll
-            for (int j = 0; j < NWS; ++j)
-                rw[j] = bload128(rw_, (uint32_t)(16 * (pt + 256 * j)), (uint32_t)n * (uint32_t)H * kSlotBytes);
-        };
-        auto load_row = [&](int n, int i) {
-            const uint32_t t0 = (uint32_t)(n * C);
-            rg[i] = __builtin_bit_cast(float4v, bload128(rg_, g_off, (t0 + i) * rsK * 4));
-            rq[i] = bload64(rq_, qk_off, (t0 + i) * rsK * SIO);
-            rk[i] = bload64(rk_, qk_off, (t0 + i) * rsK * SIO);
-        };
-        unsigned sync_target = 0;
-
-        auto prepare = [&](int n) {
-            const int slot = n & 1;
-            _Float16 *Qs = Qb + slot * C * K, *Ks = Kb + slot * C * K, *Hs = Hb + slot * C * K;
-            _Float16 *Tmb = Tmbb + slot * C * C;
-            uint16_t *Vs = Vb + slot * C * 64;
-            float *flv = Kf + slot * K;
-
-            // ---- raw v, Tmb and P, then the next chunk's v and workspace loads
-#pragma unroll
-            for (int j = 0; j < NVV; ++j) *(u32x4 *)(Vs + vv_lds[j]) = rv[j];
-#pragma unroll
-            for (int j = 0; j < NWS; ++j) {
-                *(u32x2 *)(Tmb + ws_lds[j][0]) = u32x2{rw[j][0], rw[j][1]};
-                *(u32x2 *)(Tmb + ws_lds[j][1]) = u32x2{rw[j][2], rw[j][3]};
-            }
-            if (n + 1 < nt) load_v_ws(n + 1);
-            // ---- the gate cumsum of this thread's rows; segment totals meet
-            // in LDS and are summed in segment order (gl: the chunk total,
-            // equal to gcum at the last token summed the same way)
-            float4v run = {0, 0, 0, 0};
-#pragma unroll
-            for (int i = 0; i < NR; ++i) { run += rg[i]; rg[i] = run; }
-            *(float4v *)(segt + seg * K + kc) = run;
-            prep_barrier(sync_ctr, sync_target, wc);
-            float4v off = {0, 0, 0, 0}, gl = {0, 0, 0, 0};
-#pragma unroll
-            for (int m = 0; m < NSEG; ++m) {
-                const float4v t = *(const float4v *)(segt + m * K + kc);
-                if (m < seg) off += t;
-                gl += t;
-            }
-            if (seg == 0) {
-                float4v e1;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) e1[e] = fast_exp(gl[e]);
-                *(float4v *)(flv + kc) = e1;
-            }
-            // ---- operands qd, kd, kg (fp16) of this thread's rows; both
-            // exponents are <= 0 for any gate g <= 0
-#pragma unroll
-            for (int i = 0; i < NR; ++i) {
-                const float4v gr = off + rg[i];
-                half4 hq, hk, hh;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float up = fast_exp2(gr[e] * kLog2e), dn = fast_exp2((gl[e] - gr[e]) * kLog2e);
-                    const uint32_t wq = rq[i][e >> 1], wk = rk[i][e >> 1];
-                    const float xq = __uint_as_float((e & 1) ? (wq & 0xffff0000u) : (wq << 16));
-                    const float xk = __uint_as_float((e & 1) ? (wk & 0xffff0000u) : (wk << 16));
-                    hq[e] = (_Float16)(xq * up);
-                    hk[e] = (_Float16)(xk * up);
-                    hh[e] = (_Float16)(xk * dn);
+                for (int j = 0; j < NWS; ++j) {
+                    *(u32x2 *)(Tmb + ws_lds[j][0]) = u32x2{rw[j][0], rw[j][1]};
+                    *(u32x2 *)(Tmb + ws_lds[j][1]) = u32x2{rw[j][2], rw[j][3]};
                 }
-                *(half4 *)(Qs + qk_lds[i]) = hq;
-                *(half4 *)(Ks + qk_lds[i]) = hk;
-                *(half4 *)(Hs + qk_lds[i]) = hh;
-                if (n + 1 < nt) load_row(n + 1, i);
-            }
-        };
-
-        if (nt > 0) {
-            load_v_ws(0);
+                // the qd, kd and kg tiles follow each other in LDS, each with
+                // its two slots: tile t of slot s starts (2 t + s) C K halves
+                // after qd's slot 0
 #pragma unroll
-            for (int i = 0; i < NR; ++i) load_row(0, i);
-            prepare(0);
-        }
-        wg_barrier();                       // chunk 0 prepared
-        for (int c = 0; c < nt; ++c) {
-            if (c + 1 < nt) prepare(c + 1);
-            wg_barrier();
+                for (int j = 0; j < NOP; ++j) {
+                    const int q = pt + NPT * j, tile = q / PPT;
+                    *(u32x4 *)(Qb + tile * 2 * C * K + slot * C * K + 8 * (q - tile * PPT)) = ro[j];
+                }
+                if (fl_thread) *(u32x4 *)(Kf + slot * K + 4 * pt) = rf;
+                if (n + 1 < nt)
+                    kda_slot_load<NVV, NWS, NOP, NPT>(rv_, rw_, vv_off, pt, fl_thread, rsV * SIO * (uint32_t)C,
+                                                      (uint32_t)H * kSlotBytes, SO::kQd, SO::kFl, n + 1, rv, rw, ro, rf);
+            }
+            wg_barrier();                   // c < 0: chunk 0 prepared; else end of chunk c
         }
         wait_report(wc);
     }

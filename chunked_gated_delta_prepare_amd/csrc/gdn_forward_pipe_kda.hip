@@ -14,9 +14,13 @@ const void *kda_fn(bool o_f32) {
 }
 
 template <int C, int K>
-const void *kda_mode(bool o_f32, const FwdParams &fp) {
+const void *kda_mode(bool o_f32, const FwdParams &fp, int &threads) {
+    threads = kda_threads<C, K, false>();
     if constexpr (C == 64) {
-        if (fp.dq) return kda_fn<C, K, true, false, true>(o_f32);
+        if (fp.dq) {
+            threads = kda_threads<C, K, true>();
+            return kda_fn<C, K, true, false, true>(o_f32);
+        }
     }
     if (fp.hck) return kda_fn<C, K, true, false>(o_f32);
     if (fp.cu) return kda_fn<C, K, false, true>(o_f32);
@@ -26,9 +30,10 @@ const void *kda_mode(bool o_f32, const FwdParams &fp) {
 
 gdn_status enqueue_forward_pipe_kda(int C, int K, bool o_f32, FwdParams &fp, int grid,
                                     hipStream_t s) {
-    const void *fn = C == 32 ? (K == 64 ? kda_mode<32, 64>(o_f32, fp) : kda_mode<32, 128>(o_f32, fp))
-                             : (K == 64 ? kda_mode<64, 64>(o_f32, fp) : kda_mode<64, 128>(o_f32, fp));
-    return launch_kernel(fn, grid, &fp, s, kPipeThreads);
+    int threads = 0;
+    const void *fn = C == 32 ? (K == 64 ? kda_mode<32, 64>(o_f32, fp, threads) : kda_mode<32, 128>(o_f32, fp, threads))
+                             : (K == 64 ? kda_mode<64, 64>(o_f32, fp, threads) : kda_mode<64, 128>(o_f32, fp, threads));
+    return launch_kernel(fn, grid, &fp, s, threads);
 }
 
 }  // namespace gdn

@@ -37,6 +37,8 @@ gdn_status enqueue_forward(const gdn_problem *pr, const void *q, const void *k,
 // fixed-length batch (n_seqs = 0) or n_seqs packed sequences; and the launch
 // of kda_gram_kernel into it.
 int64_t kda_workspace_bytes(const gdn_problem *pr, int64_t n_seqs);
+// bytes of one (chunk, head) slot of that workspace (kda_slot_bytes)
+int64_t kda_slot_bytes_host(const gdn_problem *pr);
 gdn_status enqueue_kda_gram(const gdn_problem *pr, const void *q, const void *k,
                             const float *beta, const float *g, void *ws, const int32_t *cu,
                             int64_t n_seqs, hipStream_t s);

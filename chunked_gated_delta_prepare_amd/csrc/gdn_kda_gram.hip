@@ -8,10 +8,10 @@ namespace gdn {
 
 namespace {
 template <int C, int K, typename IO>
-gdn_status gram_vl(GramParams &gp, bool vl, int grid, hipStream_t s) {
+gdn_status gram_vl(GramParams &gp, bool vl, int items, hipStream_t s) {
     const void *fn = vl ? (const void *)&kda_gram_kernel<C, K, IO, true>
                         : (const void *)&kda_gram_kernel<C, K, IO, false>;
-    return launch_kernel(fn, grid, &gp, s);
+    return launch_kernel(fn, items, &gp, s);
 }
 
 template <int C, typename IO>
@@ -25,12 +25,16 @@ gdn_status gram_c(const gdn_problem *pr, GramParams &gp, bool vl, int grid, hipS
 }
 }  // namespace
 
+int64_t kda_slot_bytes_host(const gdn_problem *pr) {
+    const int64_t C = pr->chunk, K = pr->K;
+    return pr->io_dtype == GDN_F32 ? 2 * C * C * 4 : 2 * C * C * 2 + 3 * C * K * 2 + K * 4;
+}
+
 int64_t kda_workspace_bytes(const gdn_problem *pr, int64_t n_seqs) {
     if (pr->gate != GDN_GATE_KEY || pr->T == 0) return 0;
     const int64_t nt = (pr->T + pr->chunk - 1) / pr->chunk;
     const int64_t slots = n_seqs > 0 ? nt + n_seqs : pr->B * nt;
-    const int64_t e = pr->io_dtype == GDN_F32 ? 4 : 2;
-    return slots * pr->H * 2 * (int64_t)pr->chunk * pr->chunk * e;
+    return slots * pr->H * kda_slot_bytes_host(pr);
 }
 
 gdn_status enqueue_kda_gram(const gdn_problem *pr, const void *q, const void *k,
@@ -43,6 +47,7 @@ gdn_status enqueue_kda_gram(const gdn_problem *pr, const void *q, const void *k,
     gp.H = (int)pr->H;
     gp.nt = (int)((pr->T + pr->chunk - 1) / pr->chunk);
     const int64_t slots = cu ? gp.nt + n_seqs : (int64_t)gp.B * gp.nt;
+    if (slots * pr->H > ((int64_t)1 << 30)) return GDN_ERR_UNSUPPORTED;
     const int grid = (int)(slots * pr->H);
     return pr->io_dtype == GDN_F32 ? gram_c<float>(pr, gp, cu != nullptr, grid, s)
                                    : gram_c<bf16_t>(pr, gp, cu != nullptr, grid, s);

@@ -145,9 +145,11 @@ gdn_status gdn_scan(const gdn_problem *problem, const void *q, const void *k,
  * once forms each chunk's decayed Gram products (A, and P of the read-out)
  * with every pair's decay split at a row between the two tokens, found by
  * halving the chunk (TileOPs fused-prepare page: A_g and its inverse), and
- * the 16-token blocks of (I + A)^-1; it leaves them in the workspace,
- * 2 chunk^2 values per (chunk, head) in the operand type (fp16 for bf16 io,
- * fp32 for fp32 io); the re-scan then reads them (kernel-fun KDA re-scan
+ * the 16-token blocks of (I + A)^-1; with bf16 io also the re-scan's
+ * operands q e^gcum, k e^gcum and k e^(gl - gcum), all decays referenced to
+ * the chunk's ends.  Every factor is a product of per-token decays e^g <= 1.
+ * It leaves them in the workspace, one slot per (chunk, head) (see
+ * gdn_workspace_bytes); the re-scan then reads them (kernel-fun KDA re-scan
  * page's per-chunk algebra).
  */
 gdn_status gdn_forward(const gdn_problem *problem, const void *q, const void *k,
@@ -289,13 +291,15 @@ gdn_status gdn_forward_noalloc(const gdn_problem *problem, const void *q, const 
                                const float *h0, void *o, float *hT, void *stream);
 
 /* Workspace gdn_forward, gdn_forward_states and gdn_rescan_dq need for this
- * problem: 0 for the scalar gate or T = 0; for the per-key gate
- * B * ceil(T / chunk) * H * 2 * chunk^2 values of the operand type (fp16 for
- * bf16 io, fp32 for fp32 io).  0 on bad arguments. */
+ * problem: 0 for the scalar gate or T = 0; for the per-key gate one slot per
+ * (chunk, head), B * ceil(T / chunk) * H slots of 2 * chunk^2 * 4 bytes (fp32
+ * io: the solve tile and P) or 2 * chunk^2 * 2 + 3 * chunk * K * 2 + 4 * K
+ * bytes (bf16 io: the same in fp16, the re-scan's three fp16 operand tiles
+ * and the chunk's per-key decay).  0 on bad arguments. */
 size_t gdn_workspace_bytes(const gdn_problem *problem);
 
 /* The same for gdn_forward_varlen over n_seqs packed sequences (the per-key
- * gate: (ceil(T / chunk) + n_seqs) * H * 2 * chunk^2 values). */
+ * gate: (ceil(T / chunk) + n_seqs) * H slots). */
 size_t gdn_workspace_bytes_varlen(const gdn_problem *problem, int64_t n_seqs);
 
 /* Static, human-readable name of a status code. */

@@ -117,17 +117,18 @@ def test_alignment_rejected(lib, gdn):
 
 def test_workspace_sizes(lib, gdn):
     # the scalar gate keeps every intermediate on chip; the per-key gate's
-    # kernel over all chunks leaves Tmb and P per (chunk, head) in the
-    # workspace: B * ceil(T/C) * H * 2 * C^2 values of the operand type
-    for io, e in ((1, 2), (0, 4)):
+    # kernel over all chunks leaves a slot per (chunk, head) in the
+    # workspace: Tmb and P ([C][C] each, operand type) and, with bf16 io, the
+    # re-scan's operand tiles ([C][K] fp16, three) and e^gl ([K] fp32)
+    for io, slot in ((1, 2 * 64 * 64 * 2 + 3 * 64 * 64 * 2 + 64 * 4), (0, 2 * 64 * 64 * 4)):
         pr = _problem(gdn, B=2, T=100, H=3, K=64, V=128, gate=0, io=io, o=io)
         assert lib.gdn_workspace_bytes(ctypes.byref(pr)) == 0
         assert lib.gdn_workspace_bytes_varlen(ctypes.byref(pr), ctypes.c_int64(4)) == 0
         pr = _problem(gdn, B=2, T=100, H=3, K=64, V=128, gate=1, io=io, o=io)
-        assert lib.gdn_workspace_bytes(ctypes.byref(pr)) == 2 * 2 * 3 * 2 * 64 * 64 * e
+        assert lib.gdn_workspace_bytes(ctypes.byref(pr)) == 2 * 2 * 3 * slot
         pr1 = _problem(gdn, B=1, T=100, H=3, K=64, V=128, gate=1, io=io, o=io)
         assert lib.gdn_workspace_bytes_varlen(ctypes.byref(pr1), ctypes.c_int64(4)) == \
-            (2 + 4) * 3 * 2 * 64 * 64 * e
+            (2 + 4) * 3 * slot
         assert lib.gdn_workspace_bytes_varlen(ctypes.byref(pr1), ctypes.c_int64(0)) == 0
     # T = 0: nothing to form
     assert lib.gdn_workspace_bytes(ctypes.byref(_problem(gdn, T=0, gate=1))) == 0
@@ -155,12 +156,13 @@ def test_key_gate_workspace_checked_before_launch(lib, gdn):
 def test_noalloc_refuses_oversize_before_launch(lib, gdn):
     # the static scratch holds GDN_NOALLOC_SCRATCH_BYTES; a per-key problem
     # that needs more is refused before the device is touched
-    C = 64
-    per = 2 * C * C * 2                                  # bf16 io: fp16 Tmb and P
+    C, K = 64, 128
+    per = 2 * C * C * 2 + 3 * C * K * 2 + K * 4          # bf16 io slot bytes
     nt = gdn.NOALLOC_SCRATCH_BYTES // per
-    fits = _problem(gdn, B=1, T=nt * C, H=1, K=128, V=128, gate=1, chunk=C)
-    assert lib.gdn_workspace_bytes(ctypes.byref(fits)) == gdn.NOALLOC_SCRATCH_BYTES
-    over = _problem(gdn, B=1, T=nt * C + 1, H=1, K=128, V=128, gate=1, chunk=C)
+    fits = _problem(gdn, B=1, T=nt * C, H=1, K=K, V=128, gate=1, chunk=C)
+    assert lib.gdn_workspace_bytes(ctypes.byref(fits)) == nt * per <= gdn.NOALLOC_SCRATCH_BYTES
+    over = _problem(gdn, B=1, T=nt * C + 1, H=1, K=K, V=128, gate=1, chunk=C)
+    assert lib.gdn_workspace_bytes(ctypes.byref(over)) > gdn.NOALLOC_SCRATCH_BYTES
     st = lib.gdn_forward_noalloc(ctypes.byref(over), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
                                  None, None)
     assert st == 6

@@ -40,7 +40,7 @@ def _run_pair(B, T, H, K, V, C, io, gate, seed):
 @pytest.mark.parametrize("io,C,K", [("bf16", 64, 128), ("bf16", 32, 64), ("fp32", 64, 128)])
 def test_noalloc_matches_forward_twice(io, C, K):
     # first call: a scratch need close to the array's size
-    need_per_chunk_head = 2 * C * C * (4 if io == "fp32" else 2)
+    need_per_chunk_head = 2 * C * C * 4 if io == "fp32" else 2 * C * C * 2 + 3 * C * K * 2 + K * 4
     nt = (gdn.NOALLOC_SCRATCH_BYTES // need_per_chunk_head) // 8 - 3   # H = 8, B = 1
     _run_pair(1, nt * C - 5, 8, K, K, C, io, "key", seed=90)
     # second call, smaller, also against the oracle
@@ -59,7 +59,7 @@ def test_noalloc_scalar_gate_needs_no_scratch():
 def test_noalloc_refuses_oversize_before_launch():
     dev = torch.device("cuda:0")
     C, K = 64, 128
-    nt = gdn.NOALLOC_SCRATCH_BYTES // (2 * C * C * 2) + 1           # one chunk-head too many
+    nt = gdn.NOALLOC_SCRATCH_BYTES // (2 * C * C * 2 + 3 * C * K * 2 + K * 4) + 1   # one too many
     B, T, H = 1, nt * C, 1
     inp = make_inputs(B, T, H, K, K, io="bf16", gate="key", gate_bias=3.0, h0=False, seed=93)
     d = {n: (None if x is None else x.to(dev)) for n, x in inp.items()}
