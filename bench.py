@@ -132,7 +132,9 @@ def measured_traffic(w, o_dtype, states=False):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
     this kernel and workload (FETCH_SIZE and WRITE_SIZE, each scaled by what
     the counter reads for a plain copy of known size), or None when there is
-    none or it was taken on different sources."""
+    none or it was taken on different sources.  For the per-key gate the
+    figure covers the step's two launches (the Gram kernel and the re-scan),
+    like the step's achieved figure."""
     short = kernel_name(w, o_dtype).split("<")[0]
     path = os.path.join(ROOT, "profiles", "%s.%s.%s%s.traffic.json"
                         % (short, w.name, o_dtype, ".states" if states else ""))
