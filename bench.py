@@ -53,6 +53,9 @@ def parse():
                          "sequences of mixed lengths")
     ap.add_argument("--chunk-dq", action="store_true",
                     help="time gdn_chunk_dq (dq's state term from saved states, on its own)")
+    ap.add_argument("--split", type=float, default=None,
+                    help="run gdn_forward_split with the cut at this fraction of T (rounded to "
+                         "whole chunks): the scalar gate's two-segment forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
@@ -232,6 +235,20 @@ def main():
             # not part of the timed re-scan)
             gdn.rescan_dq(d["q"], d["k"], d["v"], d["beta"], d["g"], dout, w.chunk, d["h0"],
                           o_dtype=tdt, hT=hT, hck=hck, vnew=vnew, dq=dq)
+    elif args.split is not None:
+        if w.gate != "head" or w.io != "bf16" or w.chunk != 64:
+            sys.exit("bench: --split takes scalar-gate bf16 workloads at chunk 64")
+        t_split = int(round(w.T * args.split / w.chunk)) * w.chunk
+        t_split = min(max(t_split, w.chunk), (w.T - 1) // w.chunk * w.chunk)
+        pr = gdn.Problem(w.B, w.T, w.H, w.K, w.V, w.chunk, gdn.GDN_BF16,
+                         {"bf16": gdn.GDN_BF16, "fp32": gdn.GDN_F32}[o_dtype], gdn.GDN_GATE_HEAD)
+        import ctypes
+        ws_split = torch.empty(int(gdn.load_library().gdn_workspace_bytes_split(
+            ctypes.byref(pr), ctypes.c_int64(t_split))), device=dev, dtype=torch.uint8)
+
+        def step():
+            gdn.forward_split(d["q"], d["k"], d["v"], d["beta"], d["g"], w.chunk, t_split, d["h0"],
+                              o_dtype=tdt, o=o, hT=hT, workspace=ws_split)
     elif args.states:
         nt = (w.T + w.chunk - 1) // w.chunk
         hck = torch.empty(w.B, nt, w.H, w.K, w.V, device=dev, dtype=tdt)
@@ -297,6 +314,10 @@ def main():
         kname = "chunk_dq_kernel<%d, %d, %d, %s>" % (w.chunk, w.K, w.V,
                                                      {"bf16": "bf16_t", "fp32": "float"}[o_dtype])
     launches = 1
+    if args.split is not None:
+        launches = 3
+        kname = ("forward_pipe_kernel<%d, %d, %s, false, false, false, true> + split_out_kernel "
+                 "+ split_state_kernel" % (w.chunk, w.K, {"bf16": "bf16_t", "fp32": "float"}[o_dtype]))
     if w.gate == "key" and not args.chunk_dq:
         launches = 2
         kname = "kda_gram_kernel<%d, %d, %s%s> + %s" % (
@@ -307,7 +328,7 @@ def main():
     roofline = {"kernel": kname, "bound": "hbm",
                 "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": (None if args.rescan or args.chunk_dq or args.varlen
+                "traffic": (None if args.rescan or args.chunk_dq or args.varlen or args.split is not None
                             else measured_traffic(w, o_dtype, args.states)),
                 "ms_per_launch": round(ms_launch, 5), "launches_per_step": launches,
                 "algorithmic_bytes_per_launch": fbytes,
@@ -334,6 +355,7 @@ def main():
                    "chunk": w.chunk, "io": w.io, "o_dtype": o_dtype, "gate": w.gate,
                    "h0": w.h0, "states": bool(args.states), "rescan": bool(args.rescan),
                    "chunk_dq": bool(args.chunk_dq), "varlen_seqs": n_seqs or None,
+                   "split_at": (t_split if args.split is not None else None),
                    "parallelism": "single-gpu"},
         "roofline": roofline,
         "copy_ref": copy_ref,

@@ -44,9 +44,10 @@ STATUS = {
 EXPORTS = ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_forward_states",
            "gdn_forward_varlen", "gdn_rescan_dq", "gdn_chunk_dq", "gdn_workspace_bytes",
            "gdn_workspace_bytes_varlen", "gdn_status_str", "gdn_abi_version",
-           "gdn_wait_timeouts", "gdn_forward_noalloc"]
+           "gdn_wait_timeouts", "gdn_forward_noalloc", "gdn_forward_split",
+           "gdn_workspace_bytes_split"]
 NOALLOC_SCRATCH_BYTES = 32 << 20
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 
 class GdnError(RuntimeError):
@@ -89,9 +90,12 @@ def load_library(path: str | None = None):
         lib.gdn_rescan_dq.argtypes = [pp] + [vp] * 12 + [sz, vp]
         lib.gdn_chunk_dq.argtypes = [pp] + [vp] * 4
         lib.gdn_forward_noalloc.argtypes = [pp] + [vp] * 9
+        lib.gdn_forward_split.argtypes = [pp, ctypes.c_int64] + [vp] * 9 + [sz, vp]
+        lib.gdn_workspace_bytes_split.argtypes = [pp, ctypes.c_int64]
+        lib.gdn_workspace_bytes_split.restype = sz
         for f in (lib.gdn_prepare, lib.gdn_scan, lib.gdn_forward, lib.gdn_forward_states,
                   lib.gdn_forward_varlen, lib.gdn_rescan_dq, lib.gdn_chunk_dq,
-                  lib.gdn_forward_noalloc):
+                  lib.gdn_forward_noalloc, lib.gdn_forward_split):
             f.restype = ctypes.c_int
         lib.gdn_workspace_bytes.argtypes = [pp]
         lib.gdn_workspace_bytes.restype = sz
@@ -310,6 +314,44 @@ def _forward(q, k, v, beta, g, chunk, h0, o_dtype, o, hT, output_final_state, wo
     rc = lib.gdn_forward(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
                          _ptr(h0), _ptr(o), _ptr(hT), _ptr(workspace), ws_bytes, _stream(stream))
     _check("gdn_forward", rc)
+    return o, hT
+
+
+def forward_split(q, k, v, beta, g, chunk, t_split, h0=None, *, o_dtype=None, o=None, hT=None,
+                  output_final_state=True, workspace=None, stream=None):
+    """gdn_forward_split: the scalar-gate forward (bf16 io, chunk 64) with each
+    stream cut at token t_split into two segments that run at the same time;
+    returns (o, hT or None) like forward."""
+    torch = _torch()
+    lib = load_library()
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if _gate_kind(g, B, T, H, K):
+        raise GdnError("gdn_forward_split", 3, "the split forward takes the scalar gate only")
+    _need(q, "q")
+    _need(k, "k", q.dtype, (B, T, H, K))
+    _need(v, "v", q.dtype, (B, T, H, V))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    _need(g, "g", torch.float32, (B, T, H))
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (B, H, K, V))
+    od = o_dtype or q.dtype
+    if o is None:
+        o = torch.empty(B, T, H, V, device=q.device, dtype=od)
+    _need(o, "o", od, (B, T, H, V))
+    if hT is None and output_final_state:
+        hT = torch.empty(B, H, K, V, device=q.device, dtype=torch.float32)
+    if hT is not None:
+        _need(hT, "hT", torch.float32, (B, H, K, V))
+    pr = _problem(q, v, chunk, False, od)
+    need = int(lib.gdn_workspace_bytes_split(ctypes.byref(pr), ctypes.c_int64(t_split)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.gdn_forward_split(ctypes.byref(pr), ctypes.c_int64(t_split), _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(beta), _ptr(g), _ptr(h0), _ptr(o), _ptr(hT), _ptr(workspace),
+                               ctypes.c_size_t(ws_bytes), _stream(stream))
+    _check("gdn_forward_split", rc)
     return o, hT
 
 

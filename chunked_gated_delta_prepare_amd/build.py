@@ -48,6 +48,8 @@ UNITS = {
     "gdn_forward_pipe_dq.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
     "gdn_chunk_dq.hip": [],
     "gdn_kda_gram.hip": [],
+    "gdn_forward_pipe_split.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "gdn_split.hip": [],
 }
 
 

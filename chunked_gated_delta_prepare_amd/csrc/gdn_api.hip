@@ -315,6 +315,39 @@ gdn_status gdn_forward_noalloc(const gdn_problem *problem, const void *q, const 
                            (hipStream_t)stream);
 }
 
+// The split forward's own conditions: scalar gate, bf16 io, chunk 64, a cut
+// at a chunk boundary strictly inside the sequence.
+static gdn_status check_split(const gdn_problem *pr, int64_t t_split) {
+    if (pr->gate != GDN_GATE_HEAD || pr->io_dtype != GDN_BF16 || pr->chunk != 64)
+        return GDN_ERR_UNSUPPORTED;
+    if (t_split <= 0 || t_split >= pr->T || t_split % pr->chunk != 0) return GDN_ERR_BAD_SHAPE;
+    const int64_t th = pr->T * pr->H;
+    if (th * std::max(pr->K, pr->V) * 4 >= ((int64_t)1 << 32)) return GDN_ERR_UNSUPPORTED;
+    if (pr->B * pr->H * (pr->V / 64 + pr->V / 64 + pr->K / 64) >= ((int64_t)1 << 31))
+        return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+size_t gdn_workspace_bytes_split(const gdn_problem *problem, int64_t t_split) {
+    if (check_problem(problem) != GDN_OK || check_split(problem, t_split) != GDN_OK) return 0;
+    return (size_t)split_workspace_bytes(problem, t_split);
+}
+
+gdn_status gdn_forward_split(const gdn_problem *problem, int64_t t_split, const void *q,
+                             const void *k, const void *v, const float *beta, const float *g,
+                             const float *h0, void *o, float *hT, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    gdn_status st = check_problem(problem);
+    if (st != GDN_OK) return st;
+    st = check_split(problem, t_split);
+    if (st != GDN_OK) return st;
+    st = check_ptrs({q, k, v, beta, g, o, workspace}, {h0, hT});
+    if (st != GDN_OK) return st;
+    if (workspace_bytes < (size_t)split_workspace_bytes(problem, t_split)) return GDN_ERR_WORKSPACE;
+    return enqueue_forward_split(problem, t_split, q, k, v, beta, g, h0, o, hT, workspace,
+                                 (hipStream_t)stream);
+}
+
 gdn_status gdn_forward_states(const gdn_problem *problem, const void *q, const void *k,
                               const void *v, const float *beta, const float *g,
                               const float *h0, void *o, float *hT, void *hck, void *vnew,

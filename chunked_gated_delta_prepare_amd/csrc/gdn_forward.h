@@ -71,6 +71,16 @@ struct FwdParams {
     int B, T, H, V;
     int nvt;        // V / 64
     int swizzle;
+    // sequence split (SP instances of forward_pipe_kernel): each stream is cut
+    // at token sp_t; the first sp_g0 workgroups run the first segment from h0
+    // (end state to sp_h0out [B, H, K, V]); the rest run the second segment
+    // twice in one pass over its chunks, as nvt ordinary V tiles from a zero
+    // state (o into o, end state to sp_N [B, H, K, V]) and K / 64 identity
+    // tiles with v = 0 and h0 = I (o into sp_oI [B, T - sp_t, H, K], end state
+    // to sp_M [B, H, K, K])
+    int sp_t, sp_g0;
+    void *sp_oI;
+    float *sp_h0out, *sp_N, *sp_M;
 };
 
 // Workspace slot of one (chunk, head) for the per-key gate.  It starts with

@@ -366,7 +366,11 @@ struct PipeLayout {
 // DQ: the backward's re-scan (the KDA re-scan page's kernel): the chunk-start
 // states and v' as with ST, plus dq's chunk-start-state term
 // DQ = dO h_c^T (raw) accumulated into p.dq, and no o.
-template <int C, int K, typename OT, bool ST = false, bool VL = false, bool DQ = false>
+// SP: the sequence-split instance (see FwdParams): the stream's first
+// segment, or its second one as ordinary tiles from a zero state and as
+// identity tiles (v = 0, h0 = I), whose outputs are the second segment's
+// correction basis (gdn_forward_split).
+template <int C, int K, typename OT, bool ST = false, bool VL = false, bool DQ = false, bool SP = false>
 __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams p) {
     typedef PipeLayout<C, K> L;
     typedef Mma<_Float16> M;
@@ -396,10 +400,21 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
     unsigned *sync_ctr = (unsigned *)(smem + L::kSync);
 
     const int wv = wave_id(), l = lane_id(), tid = threadIdx.x;
-    int pair, vt;
-    map_block(blockIdx.x, p.nvt, p.swizzle, pair, vt);
+    int pair, vt, seg = 0;
+    bool ident = false;             // SP: an identity tile of the second segment
+    if (SP && (int)blockIdx.x >= p.sp_g0) {
+        seg = 1;
+        map_block((int)blockIdx.x - p.sp_g0, p.nvt + K / 64, p.swizzle, pair, vt);
+        ident = vt >= p.nvt;
+    } else {
+        map_block(blockIdx.x, p.nvt, p.swizzle, pair, vt);
+    }
     const int b = pair / p.H, h = pair - b * p.H;
-    const StreamRange sr = stream_range<VL>(p, b, h);
+    StreamRange sr = stream_range<VL>(p, b, h);
+    if constexpr (SP) {
+        sr.T = seg ? p.T - p.sp_t : p.sp_t;
+        sr.row0 = ((int64_t)b * p.T + (seg ? p.sp_t : 0)) * p.H + h;
+    }
     const int T = sr.T, H = p.H, V = p.V;
     const int nt = (T + C - 1) / C;
     const int64_t row0 = sr.row0;
@@ -420,11 +435,15 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
 
     if (wv < 4) {
         // =====================  chain waves  =============================
-        const rsrc_t ro_ = make_rsrc((OT *)p.o + row0 * V, (uint32_t)T * rsV * SO);
+        // (SP identity tiles: o rows K wide in sp_oI, columns from 64 (vt - nvt))
+        const uint32_t rsO = ident ? rsK : rsV;
+        const int ocol = (ident ? vt - p.nvt : vt) * 64;
+        const rsrc_t ro_ = ident ? make_rsrc((OT *)p.sp_oI + ((int64_t)b * T * H + h) * K, (uint32_t)T * rsK * SO)
+                                 : make_rsrc((OT *)p.o + row0 * V, (uint32_t)T * rsV * SO);
         const int g4 = 4 * (l >> 4);
         const int vcol = vt * 64 + 16 * wv + acc_col();
         // o^T tiles: token (l % 16) of a 16-token block, columns 4 (l / 16) .. +3
-        const uint32_t o_off = ((uint32_t)(l & 15) * rsV + vt * 64 + 16 * wv + g4) * SO;
+        const uint32_t o_off = ((uint32_t)(l & 15) * rsO + ocol + 16 * wv + g4) * SO;
         // saved states: v' and h leave the accumulators as column pairs
         // (store_acc_pairs): this lane's first row 4 (l / 16) + 2 (l & 1)
         // of a 16-row block (tokens for v', key rows for h), columns
@@ -439,7 +458,13 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
         const uint32_t do_off = ((uint32_t)(l & 15) * rsV + vt * 64 + 8 * (l >> 4)) * SIO;
         unsigned chain_target = 0;
         float4v hacc[NKB];
-        if (p.h0) {
+        if (ident) {
+            // h0 = I: this lane's column ocol + 16 wv + (l % 16) of the K x K identity
+#pragma unroll
+            for (int i = 0; i < NKB; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) hacc[i][r] = (16 * i + g4 + r == ocol + 16 * wv + acc_col()) ? 1.f : 0.f;
+        } else if (p.h0 && seg == 0) {
 #pragma unroll
             for (int i = 0; i < NKB; ++i)
 #pragma unroll
@@ -612,7 +637,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
 #pragma unroll
                     for (int s = 0; s < C / 32; ++s)
                         if (32 * s < 16 * (cb + 1)) M::mma(oa, df[s], frag_sw<C>(Ps, 16 * cb, 32 * s));
-                    store_o_rows<OT>(oa, ro_, o_off, rsV * SO, (t0 + 16 * cb) * rsV * SO);
+                    store_o_rows<OT>(oa, ro_, o_off, rsO * SO, (t0 + 16 * cb) * rsO * SO);
                 }
             }
             if constexpr (ST) {
@@ -646,12 +671,21 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
             asm volatile("" : "+v"(g_nx), "+v"(b_nx));
             wg_barrier();
         }
-        if (p.hT) {
+        // (SP: the first segment's end state, or the second's zero-state
+        // end N or its transfer M, K wide)
+        float *hTp = p.hT;
+        int hcols = V, hcol = vcol;
+        if constexpr (SP) {
+            hTp = seg == 0 ? p.sp_h0out : (ident ? p.sp_M : p.sp_N);
+            hcols = ident ? K : V;
+            hcol = ident ? ocol + 16 * wv + acc_col() : vcol;
+        }
+        if (hTp) {
 #pragma unroll
             for (int i = 0; i < NKB; ++i)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    p.hT[((int64_t)pair * K + 16 * i + g4 + r) * V + vcol] = hacc[i][r];
+                    hTp[((int64_t)pair * K + 16 * i + g4 + r) * hcols + hcol] = hacc[i][r];
         }
         wait_report(wc);
     } else {
@@ -665,7 +699,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
         const int pw = wv - 4, pt = tid - 256;
         const rsrc_t rq_ = make_rsrc((const IO *)p.q + row0 * K, (uint32_t)T * rsK * SIO);
         const rsrc_t rk_ = make_rsrc((const IO *)p.k + row0 * K, (uint32_t)T * rsK * SIO);
-        const rsrc_t rv_ = make_rsrc((const IO *)p.v + row0 * V, (uint32_t)T * rsV * SIO);
+        // (SP identity tiles read v = 0: an empty range)
+        const rsrc_t rv_ = make_rsrc((const IO *)p.v + row0 * V, ident ? 0u : (uint32_t)T * rsV * SIO);
 
         constexpr int NVEC = C * K / 8 / 256;            // q/k vectors per thread
         constexpr int NVV = C * 64 / 8 / 256;            // v vectors per thread

@@ -39,6 +39,12 @@ gdn_status enqueue_forward(const gdn_problem *pr, const void *q, const void *k,
 int64_t kda_workspace_bytes(const gdn_problem *pr, int64_t n_seqs);
 // bytes of one (chunk, head) slot of that workspace (kda_slot_bytes)
 int64_t kda_slot_bytes_host(const gdn_problem *pr);
+
+// gdn_forward_split (gdn_split.hip): its workspace and its launches
+int64_t split_workspace_bytes(const gdn_problem *pr, int64_t t_split);
+gdn_status enqueue_forward_split(const gdn_problem *pr, int64_t t_split, const void *q, const void *k,
+                                 const void *v, const float *beta, const float *g, const float *h0,
+                                 void *o, float *hT, void *ws, hipStream_t s);
 gdn_status enqueue_kda_gram(const gdn_problem *pr, const void *q, const void *k,
                             const float *beta, const float *g, void *ws, const int32_t *cu,
                             int64_t n_seqs, hipStream_t s);
@@ -61,6 +67,8 @@ gdn_status enqueue_forward_pipe_varlen_c64(int K, bool o_f32, FwdParams &fp, int
 gdn_status enqueue_forward_pipe(int C, int K, bool o_f32, FwdParams &fp, int grid,
                                 hipStream_t s);
 gdn_status enqueue_forward_pipe_c32(int K, bool o_f32, FwdParams &fp, int grid, hipStream_t s);
+// the sequence-split (SP) instances, chunk 64 (gdn_forward_pipe_split.hip)
+gdn_status enqueue_forward_pipe_split(int K, bool o_f32, FwdParams &fp, int grid, hipStream_t s);
 // The pipelined kernel for the per-key gate (plain, ST or VL by fp.hck / fp.cu).
 gdn_status enqueue_forward_pipe_kda(int C, int K, bool o_f32, FwdParams &fp, int grid,
                                     hipStream_t s);

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 7
+#define GDN_ABI_VERSION 8
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -267,6 +267,37 @@ gdn_status gdn_forward_varlen(const gdn_problem *problem, const int32_t *cu_seql
  * ends normally.)
  */
 gdn_status gdn_wait_timeouts(uint32_t *count, int reset);
+
+/*
+ * gdn_forward_split -- gdn_forward for the scalar gate (bf16 io, chunk 64)
+ * with every stream cut at token t_split (a multiple of 64, 0 < t_split < T)
+ * into two segments that run at the same time.  The recurrence is affine in
+ * the state: from a start state h_in a segment ends in N + M h_in and
+ * outputs o0_t + h_in^T oI_t, where N and o0 come from a zero start and M
+ * and oI (a K-vector per token) from the identity start with v = 0 (the
+ * chunk-parallel form of the scan the kernel-fun KDA re-scan page runs
+ * serially).  One launch runs the first segment from h0 beside the second
+ * segment's zero-start and identity-start passes; two small launches then
+ * add h_in^T oI_t to the second segment's outputs and form hT = N + M h_in.
+ * With one workgroup per compute unit the two segments fill the device
+ * together when the first holds about twice the second's chunks.  Results
+ * equal gdn_forward's up to rounding (the o of the second segment is
+ * rounded to the o dtype twice when that is bf16).  Arguments as in
+ * gdn_forward; hT may be NULL but not alias h0.  Workspace:
+ * gdn_workspace_bytes_split(problem, t_split) bytes, 16-byte aligned.
+ * GDN_ERR_UNSUPPORTED for the per-key gate, fp32 io or chunk 32;
+ * GDN_ERR_BAD_SHAPE for a t_split outside those bounds.
+ */
+gdn_status gdn_forward_split(const gdn_problem *problem, int64_t t_split, const void *q,
+                             const void *k, const void *v, const float *beta, const float *g,
+                             const float *h0, void *o, float *hT, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/* Workspace gdn_forward_split needs: B H K V 4 (the first segment's end
+ * state) + B H K V 4 (N) + B H K K 4 (M) + B H K V 4 (that end state
+ * transposed in two bf16 parts) + B (T - t_split) H K times the o dtype's
+ * size (oI).  0 on bad or unsupported arguments. */
+size_t gdn_workspace_bytes_split(const gdn_problem *problem, int64_t t_split);
 
 /*
  * gdn_forward_noalloc -- gdn_forward for callers that cannot allocate device

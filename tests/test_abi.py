@@ -38,7 +38,8 @@ def test_header_declares_the_boundary():
         ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_forward_states",
          "gdn_forward_varlen", "gdn_rescan_dq", "gdn_chunk_dq", "gdn_workspace_bytes",
          "gdn_workspace_bytes_varlen", "gdn_status_str", "gdn_abi_version",
-         "gdn_wait_timeouts", "gdn_forward_noalloc"])
+         "gdn_wait_timeouts", "gdn_forward_noalloc", "gdn_forward_split",
+         "gdn_workspace_bytes_split"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -168,6 +169,27 @@ def test_noalloc_refuses_oversize_before_launch(lib, gdn):
     assert st == 6
     assert lib.gdn_forward_noalloc(ctypes.byref(over), None, FAKE, FAKE, FAKE, FAKE, None, FAKE,
                                    None, None) == 1
+
+
+def _split(lib, pr, t_split, ws=FAKE, ws_bytes=1 << 40, h0=None, hT=None):
+    return lib.gdn_forward_split(ctypes.byref(pr), ctypes.c_int64(t_split), FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, h0, FAKE, hT, ws, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_split_forward_checks(lib, gdn):
+    pr = _problem(gdn, B=2, T=300, H=4, K=128, V=64, chunk=64)
+    need = lib.gdn_workspace_bytes_split(ctypes.byref(pr), ctypes.c_int64(192))
+    assert need == 2 * 4 * 128 * 64 * 4 * 3 + 2 * 4 * 128 * 128 * 4 + 2 * (300 - 192) * 4 * 128 * 2
+    assert _split(lib, pr, 192, ws=None, ws_bytes=0) == 1
+    assert _split(lib, pr, 192, ws_bytes=need - 1) == 6
+    for bad in (0, 300, 100, -64, 320):
+        assert _split(lib, pr, bad) == 2, bad
+        assert lib.gdn_workspace_bytes_split(ctypes.byref(pr), ctypes.c_int64(bad)) == 0
+    # scalar gate, bf16 io and chunk 64 only
+    assert _split(lib, _problem(gdn, T=300, gate=1), 128) == 3
+    assert _split(lib, _problem(gdn, T=300, io=0, o=0), 128) == 3
+    assert _split(lib, _problem(gdn, T=300, chunk=32), 128) == 3
+    assert _split(lib, pr, 192, h0=MISALIGNED) == 4
 
 
 def test_lds_budget_reported_before_launch(lib, gdn):
