@@ -12,7 +12,10 @@ These functions mirror the library entry points:
   state deltas, the reference for ``gdn_forward_states``; ``rescan_dq`` forms
   dq's chunk-start-state term from them, the reference for ``gdn_rescan_dq``
   and ``gdn_chunk_dq``.  ``token_backward`` differentiates the recurrence
-  (every input's gradient), the reference for a backward pass.
+  (every input's gradient), the reference for ``gdn_backward``;
+  ``chunk_backward`` reaches the same gradients by the chunk form (a reverse
+  scan of the state's gradient, then per-chunk products) and also returns
+  that scan's intermediates.
 * ``chunk_prepare`` -- the per-chunk WY factors (gate cumsum, the strictly lower
   decayed Gram matrix, its unit-triangular inverse, then w and u), the
   reference for ``gdn_prepare``.  Steps follow the TileOPs "Reuse P as beta
@@ -335,6 +338,118 @@ def chunk_forward(q, k, v, beta, g, chunk, h0=None, states=False):
     """chunk_prepare followed by chunk_scan."""
     gcum, w, u = chunk_prepare(k, v, beta, g, chunk)
     return chunk_scan(q, k, w, u, gcum, chunk, h0, states)
+
+
+def chunk_backward(q, k, v, beta, g, do, chunk, h0=None, dhT=None):
+    """Gradients of the forward pass in the chunk form, fp64: the reverse
+    state-gradient scan and the per-chunk gradient stage that the backward's
+    WY stage computes (the kernel_fun KDA re-scan page, module docstring: the
+    re-scan's h checkpoints and v' feed the later stage, which forms dq, dk,
+    dv, dbeta and dg).  The same loss as ``token_backward``:
+    L = sum_t o_t . do_t + sum hT * dhT.
+
+    Per chunk, with gamma the chunk-local inclusive cumsum of g (per key
+    column; a scalar gate is every column alike), b = exp(gamma),
+    c = exp(gamma_last - gamma), E_rsd = exp(gamma_rd - gamma_sd), start
+    state h and v' = D from the forward:
+      A_rs = beta_r sum_d k_rd k_sd E_rsd (s < r),  T = (I + A)^-1
+      P_rs = sum_d q_rd k_sd E_rsd (s <= r)
+      R = diag(beta) (V - (K * b) h),  D = T R
+      o = (Q * b) h + P D,  h' = diag(exp(gamma_last)) h + (K * c)^T D
+    Reverse, from dh' (the gradient of the chunk-end state):
+      dD = P^T dO + (K * c) dh',  dR = T^T dD
+      dh = diag(exp(gamma_last)) dh' + (Q * b)^T dO - (K * b * beta)^T dR
+    and the chunk's gradients from dP = tril_incl(dO D^T),
+    dA = -strict_tril(dR D^T), Z = dO h^T, Y = dR h^T, W = D dh'^T (each
+    term differentiates one factor above; dg is the reverse cumsum of the
+    gradient of gamma, the last row also taking gamma_last's).
+
+    Returns ``(dq, dk, dv, dbeta, dg, dh0, extra)`` with dh0 None without h0
+    and ``extra`` a dict of the intermediates: ``dR`` [B,T,H,V] and ``dhe``
+    [B,NT,H,K,V], the gradient of each chunk's end state (dhT for the last).
+    """
+    q, k, v, do = (np.asarray(x, np.float64) for x in (q, k, v, do))
+    beta = np.asarray(beta, np.float64)
+    g = np.asarray(g, np.float64)
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    per_key = g.ndim == 4
+    NT = (T + chunk - 1) // chunk
+    dq, dk = np.zeros_like(q), np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dbeta = np.zeros_like(beta)
+    dg = np.zeros_like(g)
+    dh0 = np.zeros((B, H, K, V)) if h0 is not None else None
+    dR_all = np.zeros((B, T, H, V))
+    dhe = np.zeros((B, NT, H, K, V))
+    spans = list(_chunks(T, chunk))
+    for b in range(B):
+        for hh in range(H):
+            # forward: chunk-start states and each chunk's factors
+            S = np.zeros((K, V)) if h0 is None else np.array(h0[b, hh], np.float64)
+            saved = []
+            for s, e in spans:
+                n = e - s
+                qc, kc, vc = q[b, s:e, hh], k[b, s:e, hh], v[b, s:e, hh]
+                bc = beta[b, s:e, hh]
+                gc = g[b, s:e, hh]
+                gam = np.cumsum(gc if per_key else np.repeat(gc[:, None], K, 1), axis=0)   # [n,K]
+                E = np.exp(gam[:, None, :] - gam[None, :, :])                          # [n,n,K]
+                lower = np.tril(np.ones((n, n)), -1)
+                A = lower * bc[:, None] * np.einsum("rd,sd,rsd->rs", kc, kc, E)
+                P = np.tril(np.einsum("rd,sd,rsd->rs", qc, kc, E))
+                Tm = np.linalg.inv(np.eye(n) + A)
+                bq = np.exp(gam)
+                cq = np.exp(gam[-1][None, :] - gam)
+                R = bc[:, None] * (vc - (kc * bq) @ S)
+                D = Tm @ R
+                saved.append((S, gam, E, A, P, Tm, D))
+                S = np.exp(gam[-1])[:, None] * S + (kc * cq).T @ D
+            # reverse
+            dH = np.zeros((K, V)) if dhT is None else np.array(dhT[b, hh], np.float64)
+            for ci in range(len(spans) - 1, -1, -1):
+                s, e = spans[ci]
+                n = e - s
+                Sc, gam, E, A, P, Tm, D = saved[ci]
+                qc, kc, vc = q[b, s:e, hh], k[b, s:e, hh], v[b, s:e, hh]
+                bc = beta[b, s:e, hh]
+                doc = do[b, s:e, hh]
+                bq = np.exp(gam)
+                cq = np.exp(gam[-1][None, :] - gam)
+                gl = np.exp(gam[-1])
+                dhe[b, ci, hh] = dH
+                dD = P.T @ doc + (kc * cq) @ dH
+                dR = Tm.T @ dD
+                dP = np.tril(doc @ D.T)
+                dA = -np.tril(dR @ D.T, -1)
+                Z = doc @ Sc.T
+                Y = dR @ Sc.T
+                W = D @ dH.T
+                # dq, dk through P and A (per key column d)
+                tP = np.einsum("rs,rd,sd,rsd->rsd", dP, qc, kc, E)
+                tA = np.einsum("rs,r,rd,sd,rsd->rsd", dA, bc, kc, kc, E)
+                dqc = bq * Z + np.einsum("rs,sd,rsd->rd", dP, kc, E)
+                dkc = (np.einsum("rs,rd,rsd->sd", dP, qc, E)
+                       + np.einsum("rs,r,sd,rsd->rd", dA, bc, kc, E)
+                       + np.einsum("rs,r,rd,rsd->sd", dA, bc, kc, E)
+                       - bc[:, None] * bq * Y + cq * W)
+                dvc = bc[:, None] * dR
+                dbc = (np.einsum("rv,rv->r", dR, vc) - np.einsum("rd,rd,rd->r", bq, kc, Y)
+                       + np.einsum("rs,rd,sd,rsd->r", dA, kc, kc, E))
+                dgam = (bq * qc * Z - bc[:, None] * bq * kc * Y
+                        + tP.sum(1) - tP.sum(0) + tA.sum(1) - tA.sum(0) - cq * kc * W)
+                dgam[-1] += (cq * kc * W).sum(0) + gl * np.einsum("dv,dv->d", Sc, dH)
+                dgc = np.cumsum(dgam[::-1], axis=0)[::-1]
+                dq[b, s:e, hh] = dqc
+                dk[b, s:e, hh] = dkc
+                dv[b, s:e, hh] = dvc
+                dbeta[b, s:e, hh] = dbc
+                dg[b, s:e, hh] = dgc if per_key else dgc.sum(1)
+                dR_all[b, s:e, hh] = dR
+                dH = gl[:, None] * dH + (qc * bq).T @ doc - (kc * bq * bc[:, None]).T @ dR
+            if dh0 is not None:
+                dh0[b, hh] = dH
+    return dq, dk, dv, dbeta, dg, dh0, {"dR": dR_all, "dhe": dhe}
 
 
 def rel_err(x, ref):
