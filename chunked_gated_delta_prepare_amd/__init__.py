@@ -45,9 +45,9 @@ EXPORTS = ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_forward_states",
            "gdn_forward_varlen", "gdn_rescan_dq", "gdn_chunk_dq", "gdn_workspace_bytes",
            "gdn_workspace_bytes_varlen", "gdn_status_str", "gdn_abi_version",
            "gdn_wait_timeouts", "gdn_forward_noalloc", "gdn_forward_split",
-           "gdn_workspace_bytes_split"]
+           "gdn_workspace_bytes_split", "gdn_backward", "gdn_workspace_bytes_backward"]
 NOALLOC_SCRATCH_BYTES = 32 << 20
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 
 class GdnError(RuntimeError):
@@ -93,9 +93,12 @@ def load_library(path: str | None = None):
         lib.gdn_forward_split.argtypes = [pp, ctypes.c_int64] + [vp] * 9 + [sz, vp]
         lib.gdn_workspace_bytes_split.argtypes = [pp, ctypes.c_int64]
         lib.gdn_workspace_bytes_split.restype = sz
+        lib.gdn_backward.argtypes = [pp] + [vp] * 16 + [sz, vp]
+        lib.gdn_workspace_bytes_backward.argtypes = [pp]
+        lib.gdn_workspace_bytes_backward.restype = sz
         for f in (lib.gdn_prepare, lib.gdn_scan, lib.gdn_forward, lib.gdn_forward_states,
                   lib.gdn_forward_varlen, lib.gdn_rescan_dq, lib.gdn_chunk_dq,
-                  lib.gdn_forward_noalloc, lib.gdn_forward_split):
+                  lib.gdn_forward_noalloc, lib.gdn_forward_split, lib.gdn_backward):
             f.restype = ctypes.c_int
         lib.gdn_workspace_bytes.argtypes = [pp]
         lib.gdn_workspace_bytes.restype = sz
@@ -514,3 +517,56 @@ def rescan_dq(q, k, v, beta, g, do, chunk, h0=None, *, o_dtype=None, hT=None, hc
                                _ptr(workspace), ws_bytes, _stream(stream))
     _check("gdn_rescan_dq", rc)
     return hT, hck, vnew, dq
+
+
+def backward(q, k, v, beta, g, do, chunk, hck, vnew, dhT=None, *, want_dh0=True, dq=None, dk=None,
+             dv=None, dbeta=None, dg=None, dh0=None, workspace=None, stream=None):
+    """Gradients of the forward (scalar gate, bf16 io) for the loss
+    sum_t o_t . do_t + sum hT * dhT, from the bf16 hck and vnew that
+    forward_states (or rescan_dq) saved for the same inputs and chunk.
+    Returns (dq, dk, dv, dbeta, dg, dh0 or None), fp32.  The workspace
+    (gdn_workspace_bytes_backward bytes) is allocated when not given; after
+    the call it holds v's gradient before the beta factor [B,T,H,V] and the
+    gradient of every chunk's end state [B,NT,H,K,V], both fp32."""
+    torch = _torch()
+    lib = load_library()
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if _gate_kind(g, B, T, H, K):
+        raise ValueError("backward: the per-key gate is not supported")
+    nt = (T + int(chunk) - 1) // int(chunk) if chunk > 0 else 0
+    for t, name, dt, shp in ((q, "q", torch.bfloat16, None), (k, "k", torch.bfloat16, (B, T, H, K)),
+                             (v, "v", torch.bfloat16, (B, T, H, V)),
+                             (do, "do", torch.bfloat16, (B, T, H, V)),
+                             (beta, "beta", torch.float32, (B, T, H)), (g, "g", torch.float32, (B, T, H)),
+                             (hck, "hck", torch.bfloat16, (B, nt, H, K, V)),
+                             (vnew, "vnew", torch.bfloat16, (B, T, H, V))):
+        _need(t, name, dt, shp)
+    if dhT is not None:
+        _need(dhT, "dhT", torch.float32, (B, H, K, V))
+    dev = q.device
+    f32 = dict(device=dev, dtype=torch.float32)
+    dq = torch.empty(B, T, H, K, **f32) if dq is None else dq
+    dk = torch.empty(B, T, H, K, **f32) if dk is None else dk
+    dv = torch.empty(B, T, H, V, **f32) if dv is None else dv
+    dbeta = torch.empty(B, T, H, **f32) if dbeta is None else dbeta
+    dg = torch.empty(B, T, H, **f32) if dg is None else dg
+    if dh0 is None and want_dh0:
+        dh0 = torch.empty(B, H, K, V, **f32)
+    for t, name, shp in ((dq, "dq", (B, T, H, K)), (dk, "dk", (B, T, H, K)), (dv, "dv", (B, T, H, V)),
+                         (dbeta, "dbeta", (B, T, H)), (dg, "dg", (B, T, H))):
+        _need(t, name, torch.float32, shp)
+    if dh0 is not None:
+        _need(dh0, "dh0", torch.float32, (B, H, K, V))
+    pr = _problem(q, v, chunk, False, torch.bfloat16)
+    need = int(lib.gdn_workspace_bytes_backward(ctypes.byref(pr)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=dev, dtype=torch.uint8)
+    _need(workspace, "workspace")
+    rc = lib.gdn_backward(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(do),
+                          _ptr(dhT), _ptr(hck), _ptr(vnew), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta),
+                          _ptr(dg), _ptr(dh0), _ptr(workspace),
+                          ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                          _stream(stream))
+    _check("gdn_backward", rc)
+    return dq, dk, dv, dbeta, dg, dh0

@@ -50,6 +50,7 @@ UNITS = {
     "gdn_kda_gram.hip": [],
     "gdn_forward_pipe_split.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
     "gdn_split.hip": [],
+    "gdn_backward.hip": [],
 }
 
 

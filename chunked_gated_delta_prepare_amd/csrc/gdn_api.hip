@@ -431,6 +431,41 @@ gdn_status gdn_forward_varlen(const gdn_problem *problem, const int32_t *cu_seql
                            n_seqs, workspace, (hipStream_t)stream);
 }
 
+size_t gdn_workspace_bytes_backward(const gdn_problem *problem) {
+    if (check_problem(problem) != GDN_OK) return 0;
+    return (size_t)backward_workspace_bytes(problem);
+}
+
+gdn_status gdn_backward(const gdn_problem *problem, const void *q, const void *k, const void *v,
+                        const float *beta, const float *g, const void *dout, const float *dhT,
+                        const void *hck, const void *vnew, float *dq, float *dk, float *dv,
+                        float *dbeta, float *dg, float *dh0, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    gdn_status st = check_problem(problem);
+    if (st != GDN_OK) return st;
+    if (problem->gate != GDN_GATE_HEAD || problem->io_dtype != GDN_BF16 ||
+        problem->o_dtype != GDN_BF16)
+        return GDN_ERR_UNSUPPORTED;
+    // per-stream 32-bit byte offsets: fp32 [T, H, K | V] rows and one head's K x V block
+    const int64_t row_bytes = problem->H * 4 * std::max(problem->K, problem->V);
+    if (problem->T * row_bytes >= ((int64_t)1 << 32)) return GDN_ERR_UNSUPPORTED;
+    if (problem->T == 0) {
+        // no tokens: dh0 = dhT (or zero)
+        st = check_ptrs({}, {dhT, dh0});
+        if (st != GDN_OK) return st;
+        if (!dh0) return GDN_OK;
+        return enqueue_backward(problem, q, k, v, beta, g, dout, dhT, hck, vnew, dq, dk, dv, dbeta,
+                                dg, dh0, nullptr, (hipStream_t)stream);
+    }
+    st = check_ptrs({q, k, v, beta, g, dout, hck, vnew, dq, dk, dv, dbeta, dg}, {dhT, dh0});
+    if (st != GDN_OK) return st;
+    const int64_t need = backward_workspace_bytes(problem);
+    if (!workspace || workspace_bytes < (size_t)need) return GDN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return GDN_ERR_ALIGNMENT;
+    return enqueue_backward(problem, q, k, v, beta, g, dout, dhT, hck, vnew, dq, dk, dv, dbeta, dg,
+                            dh0, workspace, (hipStream_t)stream);
+}
+
 gdn_status gdn_wait_timeouts(uint32_t *count, int reset) {
     if (!count) return GDN_ERR_NULL_ARG;
     unsigned *p = wait_count_ptr();

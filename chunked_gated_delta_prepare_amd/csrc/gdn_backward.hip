@@ -1,0 +1,51 @@
+// libgdn: gdn_backward dispatch -- the reverse scan of the state's gradient,
+// then the per-chunk gradients (kernels in gdn_backward.h).
+#include "gdn_backward.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+template <int C, int K, int V>
+gdn_status launch_backward(BwdParams &bp, hipStream_t s) {
+    const int gscan = bp.B * bp.H * bp.nvt;
+    gdn_status st = launch_kernel((const void *)&bwd_dh_kernel<C, K>, gscan, &bp, s, 256);
+    if (st != GDN_OK || bp.NT == 0) return st;
+    return launch_kernel((const void *)&bwd_grad_kernel<C, K, V>, bp.B * bp.H * bp.NT, &bp, s, 256);
+}
+
+template <int C, int K>
+gdn_status backward_v(const gdn_problem *pr, BwdParams &bp, hipStream_t s) {
+    return pr->V == 64 ? launch_backward<C, K, 64>(bp, s) : launch_backward<C, K, 128>(bp, s);
+}
+
+template <int C>
+gdn_status backward_k(const gdn_problem *pr, BwdParams &bp, hipStream_t s) {
+    return pr->K == 64 ? backward_v<C, 64>(pr, bp, s) : backward_v<C, 128>(pr, bp, s);
+}
+
+}  // namespace
+
+int64_t backward_workspace_bytes(const gdn_problem *pr) {
+    const int64_t nt = (pr->T + pr->chunk - 1) / pr->chunk;
+    return pr->B * pr->T * pr->H * pr->V * 4 + pr->B * nt * pr->H * pr->K * pr->V * 4;
+}
+
+gdn_status enqueue_backward(const gdn_problem *pr, const void *q, const void *k, const void *v,
+                            const float *beta, const float *g, const void *dout, const float *dhT,
+                            const void *hck, const void *vnew, float *dq, float *dk, float *dv,
+                            float *dbeta, float *dg, float *dh0, void *ws, hipStream_t s) {
+    BwdParams bp;
+    bp.q = q; bp.k = k; bp.v = v; bp.dout = dout; bp.beta = beta; bp.g = g; bp.dhT = dhT;
+    bp.hck = hck; bp.vnew = vnew;
+    bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dbeta = dbeta; bp.dg = dg; bp.dh0 = dh0;
+    bp.B = (int)pr->B; bp.T = (int)pr->T; bp.H = (int)pr->H; bp.V = (int)pr->V;
+    bp.nvt = (int)(pr->V / 64);
+    bp.NT = (int)((pr->T + pr->chunk - 1) / pr->chunk);
+    bp.dR = (float *)ws;
+    bp.dhe = ws ? (float *)ws + pr->B * pr->T * pr->H * pr->V : nullptr;
+    bp.swizzle = ((int64_t)bp.B * bp.H * bp.nvt) % 8 == 0 ? 1 : 0;
+    return pr->chunk == 32 ? backward_k<32>(pr, bp, s) : backward_k<64>(pr, bp, s);
+}
+
+}  // namespace gdn

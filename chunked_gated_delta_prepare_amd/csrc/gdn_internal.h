@@ -49,6 +49,13 @@ gdn_status enqueue_kda_gram(const gdn_problem *pr, const void *q, const void *k,
                             const float *beta, const float *g, void *ws, const int32_t *cu,
                             int64_t n_seqs, hipStream_t s);
 
+// gdn_backward (gdn_backward.hip): its workspace and its two launches
+int64_t backward_workspace_bytes(const gdn_problem *pr);
+gdn_status enqueue_backward(const gdn_problem *pr, const void *q, const void *k, const void *v,
+                            const float *beta, const float *g, const void *dout, const float *dhT,
+                            const void *hck, const void *vnew, float *dq, float *dk, float *dv,
+                            float *dbeta, float *dg, float *dh0, void *ws, hipStream_t s);
+
 struct FwdParams;
 // Dispatch a forward problem whose FwdParams carry hck and vnew.
 gdn_status enqueue_forward_states(const gdn_problem *pr, FwdParams &fp, int grid, hipStream_t s);

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 8
+#define GDN_ABI_VERSION 9
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -203,6 +203,42 @@ gdn_status gdn_rescan_dq(const gdn_problem *problem, const void *q, const void *
                          const void *v, const float *beta, const float *g, const float *h0,
                          const void *dout, float *hT, void *hck, void *vnew, float *dq,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_backward -- the gradients of gdn_forward's outputs with respect to
+ * every input, for the scalar gate (Gated DeltaNet) with bf16 io, from what
+ * gdn_forward_states (or gdn_rescan_dq) saved: the kernel_fun KDA re-scan
+ * page has its re-scan keep the h checkpoints and v_new for the backward's
+ * later stage (bwd_scan.py module docstring); this is that stage, with the
+ * state's gradient carried backwards through the chunks.  For the loss
+ * L = sum_t o_t . dO_t + sum hT * dhT:
+ *   dout [B,T,H,V] bf16   dO
+ *   dhT  [B,H,K,V] fp32   the final state's gradient, or NULL (zero)
+ *   hck, vnew             bf16, as gdn_forward_states writes them for the
+ *                         same inputs and chunk (problem->o_dtype must be
+ *                         GDN_BF16: they are read in that dtype)
+ *   dq, dk [B,T,H,K], dv [B,T,H,V], dbeta, dg [B,T,H]   fp32, written in full
+ *   dh0  [B,H,K,V] fp32   h0's gradient, or NULL (not written)
+ * Two launches on the stream: the reverse scan (one workgroup per (batch,
+ * head, 64-wide V tile), serial over chunks) writes dR (v's gradient before
+ * the beta factor) and the gradient of every chunk's end state into the
+ * workspace, and dv and dh0; then one workgroup per (chunk, head) forms dq,
+ * dk, dbeta and dg.  Workspace: gdn_workspace_bytes_backward(problem)
+ * bytes, 16-byte aligned: dR [B,T,H,V] fp32, then the chunk-end gradients
+ * [B,NT,H,K,V] fp32.  Results are deterministic (no atomics).  Outputs must
+ * not alias inputs or each other.  With T = 0 only dh0 is written (= dhT or
+ * zero).  GDN_ERR_UNSUPPORTED for the per-key gate, fp32 io, an fp32
+ * o_dtype, or a stream whose fp32 rows exceed 4 GiB.
+ */
+gdn_status gdn_backward(const gdn_problem *problem, const void *q, const void *k, const void *v,
+                        const float *beta, const float *g, const void *dout, const float *dhT,
+                        const void *hck, const void *vnew, float *dq, float *dk, float *dv,
+                        float *dbeta, float *dg, float *dh0, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* Workspace gdn_backward needs: B T H V 4 + B NT H K V 4 bytes (NT =
+ * ceil(T / chunk)); 0 on bad arguments. */
+size_t gdn_workspace_bytes_backward(const gdn_problem *problem);
 
 /*
  * gdn_chunk_dq -- dq's chunk-start-state term on its own, from states that

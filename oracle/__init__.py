@@ -340,7 +340,7 @@ def chunk_forward(q, k, v, beta, g, chunk, h0=None, states=False):
     return chunk_scan(q, k, w, u, gcum, chunk, h0, states)
 
 
-def chunk_backward(q, k, v, beta, g, do, chunk, h0=None, dhT=None):
+def chunk_backward(q, k, v, beta, g, do, chunk, h0=None, dhT=None, hck=None, vnew=None):
     """Gradients of the forward pass in the chunk form, fp64: the reverse
     state-gradient scan and the per-chunk gradient stage that the backward's
     WY stage computes (the kernel_fun KDA re-scan page, module docstring: the
@@ -363,6 +363,11 @@ def chunk_backward(q, k, v, beta, g, do, chunk, h0=None, dhT=None):
     dA = -strict_tril(dR D^T), Z = dO h^T, Y = dR h^T, W = D dh'^T (each
     term differentiates one factor above; dg is the reverse cumsum of the
     gradient of gamma, the last row also taking gamma_last's).
+
+    With ``hck`` [B,NT,H,K,V] and ``vnew`` [B,T,H,V] (the forward's saved
+    chunk-start states and deltas, as token_states returns them, possibly
+    rounded) the per-chunk gradients take h and D from them, as a backward
+    that is handed saved states does; the reverse scan needs neither.
 
     Returns ``(dq, dk, dv, dbeta, dg, dh0, extra)`` with dh0 None without h0
     and ``extra`` a dict of the intermediates: ``dR`` [B,T,H,V] and ``dhe``
@@ -403,7 +408,9 @@ def chunk_backward(q, k, v, beta, g, do, chunk, h0=None, dhT=None):
                 cq = np.exp(gam[-1][None, :] - gam)
                 R = bc[:, None] * (vc - (kc * bq) @ S)
                 D = Tm @ R
-                saved.append((S, gam, E, A, P, Tm, D))
+                ci = s // chunk
+                saved.append((S if hck is None else np.asarray(hck[b, ci, hh], np.float64), gam, E, A, P, Tm,
+                              D if vnew is None else np.asarray(vnew[b, s:e, hh], np.float64)))
                 S = np.exp(gam[-1])[:, None] * S + (kc * cq).T @ D
             # reverse
             dH = np.zeros((K, V)) if dhT is None else np.array(dhT[b, hh], np.float64)

@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
          "gdn_forward_varlen", "gdn_rescan_dq", "gdn_chunk_dq", "gdn_workspace_bytes",
          "gdn_workspace_bytes_varlen", "gdn_status_str", "gdn_abi_version",
          "gdn_wait_timeouts", "gdn_forward_noalloc", "gdn_forward_split",
-         "gdn_workspace_bytes_split"])
+         "gdn_workspace_bytes_split", "gdn_backward", "gdn_workspace_bytes_backward"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -190,6 +190,35 @@ def test_split_forward_checks(lib, gdn):
     assert _split(lib, _problem(gdn, T=300, io=0, o=0), 128) == 3
     assert _split(lib, _problem(gdn, T=300, chunk=32), 128) == 3
     assert _split(lib, pr, 192, h0=MISALIGNED) == 4
+
+
+def _bwd(lib, pr, ws=FAKE, ws_bytes=1 << 40, **kw):
+    names = ("q", "k", "v", "beta", "g", "dout", "dhT", "hck", "vnew", "dq", "dk", "dv", "dbeta",
+             "dg", "dh0")
+    args = [kw.get(n, None if n in ("dhT", "dh0") else FAKE) for n in names]
+    return lib.gdn_backward(ctypes.byref(pr), *args, ws, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_backward_checks(lib, gdn):
+    pr = _problem(gdn, B=2, T=300, H=4, K=128, V=64, chunk=64)
+    need = lib.gdn_workspace_bytes_backward(ctypes.byref(pr))
+    assert need == 2 * 300 * 4 * 64 * 4 + 2 * 5 * 4 * 128 * 64 * 4
+    assert _bwd(lib, pr, ws=None, ws_bytes=0) == 6
+    assert _bwd(lib, pr, ws_bytes=need - 1) == 6
+    assert _bwd(lib, pr, ws=MISALIGNED) == 4
+    for name in ("q", "k", "v", "beta", "g", "dout", "hck", "vnew", "dq", "dk", "dv", "dbeta", "dg"):
+        assert _bwd(lib, pr, **{name: None}) == 1, name
+        assert _bwd(lib, pr, **{name: MISALIGNED}) == 4, name
+    for name in ("dhT", "dh0"):
+        assert _bwd(lib, pr, **{name: MISALIGNED}) == 4, name
+    # scalar gate, bf16 io, bf16 saved states only
+    assert _bwd(lib, _problem(gdn, T=300, gate=1)) == 3
+    assert _bwd(lib, _problem(gdn, T=300, io=0, o=0)) == 3
+    assert _bwd(lib, _problem(gdn, T=300, o=0)) == 3
+    assert _bwd(lib, _problem(gdn, K=96)) == 3
+    assert lib.gdn_workspace_bytes_backward(None) == 0
+    # an fp32 row of a stream past 4 GiB
+    assert _bwd(lib, _problem(gdn, T=1 << 22, H=512, K=128, V=128)) == 3
 
 
 def test_lds_budget_reported_before_launch(lib, gdn):

@@ -104,3 +104,26 @@ def test_chunk_backward_intermediates(oracle_mod, per_key):
         np.testing.assert_allclose(dhe[:, c], ref[5], rtol=1e-7, atol=1e-9, err_msg="chunk %d" % c)
     dv = oracle_mod.chunk_backward(q, k, v, beta, g, do, C, h0, dhT)[2]
     np.testing.assert_allclose(dv, beta[..., None] * dR, rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("per_key", [False, True])
+def test_chunk_backward_with_the_exact_saved_states(oracle_mod, per_key):
+    """Handed the exact chunk-start states and deltas (token_states), the
+    chunk backward gives token_backward's gradients; handed rounded ones it
+    moves by about the rounding."""
+    rng = np.random.default_rng(731 + per_key)
+    T, C = 14, 4
+    q, k, v, beta, g, h0, do, dhT = _case(rng, 1, T, 2, 4, 3, per_key)
+    f = lambda x: x.astype(np.float32).astype(np.float64)
+    q, k, v, beta, g, h0 = (f(x) for x in (q, k, v, beta, g, h0))
+    _, _, hck, vnew = oracle_mod.token_states(q.astype(np.float32), k.astype(np.float32),
+                                              v.astype(np.float32), beta.astype(np.float32),
+                                              g.astype(np.float32), C, h0.astype(np.float32))
+    ref = oracle_mod.token_backward(q, k, v, beta, g, do, h0, dhT)
+    got = oracle_mod.chunk_backward(q, k, v, beta, g, do, C, h0, dhT, hck=hck, vnew=vnew)
+    for name, x, r in zip(NAMES, got[:6], ref):
+        np.testing.assert_allclose(x, r, rtol=1e-9, atol=1e-11, err_msg=name)
+    rnd = oracle_mod.chunk_backward(q, k, v, beta, g, do, C, h0, dhT, hck=hck.astype(np.float16),
+                                    vnew=vnew.astype(np.float16))
+    moved = max(oracle_mod.rel_err(x, r) for x, r in zip(rnd[:2], ref[:2]))
+    assert 1e-5 < moved < 1e-2
