@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--split", type=float, default=None,
                     help="run gdn_forward_split with the cut at this fraction of T (rounded to "
                          "whole chunks): the scalar gate's two-segment forward")
+    ap.add_argument("--backward", action="store_true",
+                    help="time gdn_backward (the scalar gate's gradients from saved bf16 states; "
+                         "the states come from one untimed gdn_forward_states call)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
@@ -95,6 +98,25 @@ def chunk_dq_bytes(w, o_dtype):
     nt = (w.T + w.chunk - 1) // w.chunk
     return (w.B * w.T * w.H * (io_bytes(w.io) * w.V + 4 * w.K)
             + io_bytes(o_dtype) * w.B * nt * w.H * w.K * w.V)
+
+
+def backward_bytes(w):
+    """Inputs q, k, v, dO (io dtype), beta, g, dhT and the saved bf16 states
+    (hck, vnew) read once; dq, dk, dv, dbeta, dg, dh0 (fp32) written once."""
+    B, T, H, K, V = w.B, w.T, w.H, w.K, w.V
+    nt = (T + w.chunk - 1) // w.chunk
+    per_tok = io_bytes(w.io) * (2 * K + 2 * V) + 8 + 2 * V + 4 * (2 * K + V) + 8
+    return B * T * H * per_tok + 2 * B * nt * H * K * V + 8 * B * H * K * V
+
+
+def backward_flops(w):
+    """Per token-head: the reverse scan's Gram halves, inverse, P^T dO, the
+    state products and T^T dD (C K + C V + C^2/6 + 3 K V multiply-adds), the
+    gradient stage's Gram halves again, dO D^T and dR D^T halves, the three
+    state products and F K, F^T Q, G K halves (1.5 C K + C V + 3 K V)."""
+    C, K, V = w.chunk, w.K, w.V
+    mac = 2.5 * C * K + 2 * C * V + C * C / 6.0 + 6 * K * V
+    return 2.0 * mac * w.B * w.T * w.H
 
 
 def forward_flops(w):
@@ -249,6 +271,28 @@ def main():
         def step():
             gdn.forward_split(d["q"], d["k"], d["v"], d["beta"], d["g"], w.chunk, t_split, d["h0"],
                               o_dtype=tdt, o=o, hT=hT, workspace=ws_split)
+    elif args.backward:
+        if w.gate != "head" or w.io != "bf16":
+            sys.exit("bench: --backward takes scalar-gate bf16 workloads")
+        tdt = torch.bfloat16
+        o_dtype = "bf16"
+        gen = torch.Generator().manual_seed(w.seed + 3000)
+        dout = torch.randn(w.B, w.T, w.H, w.V, generator=gen).to(torch.bfloat16).to(dev)
+        dhT = torch.randn(w.B, w.H, w.K, w.V, generator=gen).to(dev)
+        _, _, hck, vnew = gdn.forward_states(d["q"], d["k"], d["v"], d["beta"], d["g"], w.chunk,
+                                             d["h0"], o_dtype=tdt)
+        f32 = dict(device=dev, dtype=torch.float32)
+        grads = dict(dq=torch.empty(w.B, w.T, w.H, w.K, **f32), dk=torch.empty(w.B, w.T, w.H, w.K, **f32),
+                     dv=torch.empty(w.B, w.T, w.H, w.V, **f32), dbeta=torch.empty(w.B, w.T, w.H, **f32),
+                     dg=torch.empty(w.B, w.T, w.H, **f32), dh0=torch.empty(w.B, w.H, w.K, w.V, **f32))
+        pr = gdn.Problem(w.B, w.T, w.H, w.K, w.V, w.chunk, gdn.GDN_BF16, gdn.GDN_BF16, gdn.GDN_GATE_HEAD)
+        import ctypes
+        ws_b = torch.empty(int(gdn.load_library().gdn_workspace_bytes_backward(ctypes.byref(pr))),
+                           device=dev, dtype=torch.uint8)
+
+        def step():
+            gdn.backward(d["q"], d["k"], d["v"], d["beta"], d["g"], dout, w.chunk, hck, vnew, dhT,
+                         workspace=ws_b, **grads)
     elif args.states:
         nt = (w.T + w.chunk - 1) // w.chunk
         hck = torch.empty(w.B, nt, w.H, w.K, w.V, device=dev, dtype=tdt)
@@ -314,6 +358,10 @@ def main():
         kname = "chunk_dq_kernel<%d, %d, %d, %s>" % (w.chunk, w.K, w.V,
                                                      {"bf16": "bf16_t", "fp32": "float"}[o_dtype])
     launches = 1
+    if args.backward:
+        fbytes, fflops = backward_bytes(w), backward_flops(w)
+        launches = 2
+        kname = "bwd_dh_kernel<%d, %d> + bwd_grad_kernel<%d, %d, %d>" % (w.chunk, w.K, w.chunk, w.K, w.V)
     if args.split is not None:
         launches = 3
         kname = ("forward_pipe_kernel<%d, %d, %s, false, false, false, true> + split_out_kernel "
@@ -329,6 +377,7 @@ def main():
                 "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": (None if args.rescan or args.chunk_dq or args.varlen or args.split is not None
+                            or args.backward
                             else measured_traffic(w, o_dtype, args.states)),
                 "ms_per_launch": round(ms_launch, 5), "launches_per_step": launches,
                 "algorithmic_bytes_per_launch": fbytes,
@@ -345,7 +394,8 @@ def main():
         cpu = cpu_baseline(w, inp, args.cpu_seconds)
 
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": (METRIC.replace("forward", "backward") if args.backward else METRIC),
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "ms_median": round(ms_median, 5), "ms_min": round(ms_min, 5),
         "flush_between_steps_bytes": args.flush_mib << 20,
@@ -356,6 +406,7 @@ def main():
                    "h0": w.h0, "states": bool(args.states), "rescan": bool(args.rescan),
                    "chunk_dq": bool(args.chunk_dq), "varlen_seqs": n_seqs or None,
                    "split_at": (t_split if args.split is not None else None),
+                   "backward": bool(args.backward),
                    "parallelism": "single-gpu"},
         "roofline": roofline,
         "copy_ref": copy_ref,

@@ -48,6 +48,7 @@ struct BwdParams {
     float *dq, *dk, *dv, *dbeta, *dg, *dh0;   // dh0 may be NULL
     float *dR;                      // workspace [B, T, H, V]
     float *dhe;                     // workspace [B, NT, H, K, V]: chunk-end gradients
+    void *prep;                     // workspace: the reverse scan's per-chunk slots (BwdSlot)
     int B, T, H, V, nvt, NT;
     int swizzle;
 };
@@ -85,8 +86,164 @@ __device__ __forceinline__ void acc_frag_split(const float4v &a, const float4v &
     fh = __builtin_bit_cast(bf16x8, h);
     fl = __builtin_bit_cast(bf16x8, lo);
 }
+// A workgroup barrier that orders LDS only: this wave's LDS operations
+// complete, then s_barrier.  Global loads in flight (the next phase's
+// operands) stay in flight; no wave of these kernels reads global memory
+// that another wave of the workgroup writes.
+__device__ __forceinline__ void bwd_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ uint16_t half_of(const u32x4 &x, int e) {
     return (uint16_t)(x[e >> 1] >> (16 * (e & 1)));
+}
+
+// ---------------------------------------------------------------------------
+// Per-chunk factors of the reverse scan, formed for every (chunk, head) at
+// once by bwd_prep_kernel before the serial scan reads them: P^T and T^T
+// (C x C, bf16 high and low parts, row-major, pitch C) and the row factors
+// b = e^gamma, c = e^(gamma_last - gamma), beta b, beta (fp32 [C]) and
+// e^gamma_last.  Slot of chunk c of stream (b, h): (b * NT + c) * H + h.
+// ---------------------------------------------------------------------------
+template <int C> struct BwdSlot {
+    static constexpr int kPTh = 0, kPTl = kPTh + C * C * 2, kTTh = kPTl + C * C * 2,
+                         kTTl = kTTh + C * C * 2;
+    static constexpr int kVec = kTTl + C * C * 2;      // b, c, beta b, beta [C], e^gamma_last, pad
+    static constexpr int kBytes = kVec + (4 * C + 4) * 4;
+    static_assert(kBytes % 16 == 0, "slot pieces");
+};
+
+template <int C, int K> struct BwdPrepLayout {
+    static constexpr int LK = K + 8, LC = C + 8, LF = C + 4;
+    static constexpr int kQr = 0;                          // q [C][LK]
+    static constexpr int kKr = kQr + C * LK * 2;           // k [C][LK]
+    static constexpr int kAf = kKr + C * LK * 2;           // A fp32 [C][LF]
+    static constexpr int kTf = kAf + C * LF * 4;           // T fp32 [C][LF]
+    static constexpr int kPl = kTf + C * LF * 4;           // P^T h, l, T^T h, l [4][C][LC]
+    static constexpr int kVec = kPl + 4 * C * LC * 2;      // gamma, b, c, beta b, beta [C], gl
+    static constexpr int kBytes = kVec + (5 * C + 4) * 4;
+    static_assert(kBytes <= kLdsBytesMax, "LDS budget");
+};
+
+// The reverse scan's per-chunk factors, one workgroup per (chunk, head):
+// gate cumsum, the lower tiles of k k^T (-> A) and q k^T (-> P), the
+// inverse T = (I + A)^-1 in fp32, then P^T, T^T and the row factors into the
+// chunk's slot.  Rows past T load as zero (an identity step).
+template <int C, int K>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
+    typedef BwdPrepLayout<C, K> L;
+    typedef BwdSlot<C> SL;
+    constexpr int LK = L::LK, LC = L::LC, LF = L::LF;
+    constexpr int NB = C / 16, KS = K / 32, NLT = NB * (NB + 1) / 2;
+    __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
+    uint16_t *Qr = (uint16_t *)(smem + L::kQr), *Kr = (uint16_t *)(smem + L::kKr);
+    float *Af = (float *)(smem + L::kAf), *Tf = (float *)(smem + L::kTf);
+    uint16_t *Pl = (uint16_t *)(smem + L::kPl);          // planes: P^T h, P^T l, T^T h, T^T l
+    float *gam = (float *)(smem + L::kVec), *bv = gam + C, *cv = bv + C, *bbv = cv + C, *betv = bbv + C,
+          *glp = betv + C;
+
+    const int tid = threadIdx.x, wv = wave_id(), l = lane_id(), g = l >> 4, n = l & 15;
+    const int NT = p.NT, T = p.T;
+    const int c = blockIdx.x % NT, bh = blockIdx.x / NT, b = bh / p.H, h = bh % p.H;
+    const int t0 = c * C;
+    const uint32_t H = p.H, rsK = H * K;
+    const int64_t row0 = (int64_t)b * T * H + h;
+    const rsrc_t rq = make_rsrc((const bf16_t *)p.q + row0 * K, (uint32_t)T * rsK * 2);
+    const rsrc_t rk = make_rsrc((const bf16_t *)p.k + row0 * K, (uint32_t)T * rsK * 2);
+#pragma unroll
+    for (int pc = tid; pc < C * K / 8; pc += 256) {
+        const int row = pc / (K / 8), c8 = pc % (K / 8);
+        const uint32_t off = (row * rsK + 8 * c8) * 2;
+        *(u32x4 *)(Qr + row * LK + 8 * c8) = bload128(rq, off, t0 * rsK * 2);
+        *(u32x4 *)(Kr + row * LK + 8 * c8) = bload128(rk, off, t0 * rsK * 2);
+    }
+    for (int i = tid; i < C * LF; i += 256) Tf[i] = 0.f;
+    if (wv == 0) {
+        const rsrc_t rg = make_rsrc(p.g + row0, (uint32_t)T * H * 4);
+        const rsrc_t rb = make_rsrc(p.beta + row0, (uint32_t)T * H * 4);
+        float x = l < C ? __uint_as_float(bload32(rg, l * H * 4, t0 * H * 4)) : 0.f;
+        const float bt = l < C ? __uint_as_float(bload32(rb, l * H * 4, t0 * H * 4)) : 0.f;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float y = __shfl_up(x, o);
+            if (l >= o) x += y;
+        }
+        const float xl = __shfl(x, C - 1);
+        if (l < C) {
+            const float e = __expf(x);
+            gam[l] = x;
+            bv[l] = e;
+            cv[l] = __expf(xl - x);
+            bbv[l] = bt * e;
+            betv[l] = bt;
+        }
+        if (l == 0) *glp = __expf(xl);
+    }
+    __syncthreads();
+    // Gram tiles: A (fp32) and P^T (bf16 parts)
+#pragma unroll 1
+    for (int t = wv; t < 2 * NLT; t += 4) {
+        const bool isP = t >= NLT;
+        int tt = isP ? t - NLT : t, i = 0;
+        while (tt > i) {
+            tt -= i + 1;
+            ++i;
+        }
+        const int j = tt;
+        float4v acc = {0, 0, 0, 0};
+        const uint16_t *Aop = isP ? Qr : Kr;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            mfma_bf(acc, lds_frag(Aop, LK, 16 * i, 32 * s), lds_frag(Kr, LK, 16 * j, 32 * s));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int R = 16 * i + 4 * g + e, S = 16 * j + n;
+            const float d = __expf(fminf(gam[R] - gam[S], 0.f));
+            if (!isP) {
+                Af[R * LF + S] = S < R ? betv[R] * acc[e] * d : 0.f;
+            } else {
+                uint16_t hh, ll;
+                bf_split(S <= R ? acc[e] * d : 0.f, hh, ll);
+                Pl[S * LC + R] = hh;
+                Pl[C * LC + S * LC + R] = ll;
+                if (i != j) {                        // P^T is zero below its diagonal
+                    Pl[R * LC + S] = 0;
+                    Pl[C * LC + R * LC + S] = 0;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    tri_inverse<C, LF>(Af, Tf);
+    for (int idx = tid; idx < C * C; idx += 256) {
+        const int s = idx / C, r = idx % C;
+        uint16_t hh, ll;
+        bf_split(Tf[s * LF + r], hh, ll);
+        Pl[2 * C * LC + r * LC + s] = hh;
+        Pl[3 * C * LC + r * LC + s] = ll;
+    }
+    __syncthreads();
+    // out: the four planes row by row (8-byte pieces, consecutive lanes on
+    // consecutive pieces), then the vectors
+    char *slot = (char *)p.prep + (((int64_t)b * NT + c) * H + h) * SL::kBytes;
+    const rsrc_t rsl = make_rsrc(slot, (uint32_t)SL::kBytes);
+#pragma unroll
+    for (int pc = tid; pc < C * C; pc += 256) {
+        const int pl = pc / (C * C / 4), rem = pc % (C * C / 4), row = rem / (C / 4), c4 = rem % (C / 4);
+        const u32x2 x = *(const u32x2 *)(Pl + pl * C * LC + row * LC + 4 * c4);
+        __builtin_amdgcn_raw_buffer_store_b64(x, rsl, (pl * C * C + row * C + 4 * c4) * 2, 0, 0);
+    }
+    float *sv = (float *)(slot + SL::kVec);
+    if (tid < C) {
+        sv[tid] = bv[tid];
+        sv[C + tid] = cv[tid];
+        sv[2 * C + tid] = bbv[tid];
+        sv[3 * C + tid] = betv[tid];
+    }
+    if (tid == 0) sv[4 * C] = *glp;
 }
 
 // ---------------------------------------------------------------------------
@@ -94,84 +251,84 @@ __device__ __forceinline__ uint16_t half_of(const u32x4 &x, int e) {
 // bytes so that the 16 rows of a fragment load fall in distinct banks).
 // ---------------------------------------------------------------------------
 template <int C, int K> struct BwdScanLayout {
-    static constexpr int LK = K + 8, LC = C + 8, LF = C + 4;
+    static constexpr int LK = K + 8, LC = C + 8, LD = 64 + 8;
     static constexpr int kQr = 0;                          // q   [C][LK]
     static constexpr int kKr = kQr + C * LK * 2;           // k   [C][LK]
-    static constexpr int kQT = kKr + C * LK * 2;           // q^T [K][LC]
-    static constexpr int kKT = kQT + K * LC * 2;           // k^T [K][LC]
-    static constexpr int kDoT = kKT + K * LC * 2;          // dO^T of the V tile [64][LC]
-    static constexpr int kPT = kDoT + 64 * LC * 2;         // P^T high, low [2][C][LC]
+    static constexpr int kDo = kKr + C * LK * 2;           // dO of the V tile [C][LD]
+    static constexpr int kPT = kDo + C * LD * 2;           // P^T high, low [2][C][LC]
     static constexpr int kTT = kPT + 2 * C * LC * 2;       // T^T high, low [2][C][LC]
-    static constexpr int kAf = kTT + 2 * C * LC * 2;       // A  fp32 [C][LF]
-    static constexpr int kTf = kAf + C * LF * 4;           // T  fp32 [C][LF]
-    static constexpr int kVec = kTf + C * LF * 4;          // gamma, b, c, beta [C]; e^gamma_last
+    static constexpr int kVec = kTT + 2 * C * LC * 2;      // b, c, beta b, beta [C]; e^gamma_last
     static constexpr int kBytes = kVec + (4 * C + 4) * 4;
     static_assert(kBytes <= kLdsBytesMax, "LDS budget");
 };
 
-// One chunk's q, k (C x K) and dO tile (C x 64) as 16-byte pieces, piece j of
-// this thread covering row (tid + 256 j) % C, columns 8 ((tid + 256 j) / C) ..
-// +7, so that the 64 lanes of a wave take 64 rows of one column group (their
-// transposed LDS writes then fall in distinct banks); plus g and beta of row
-// tid.  Rows at or past T read as zero.
+// Transposed fragments of a row-major bf16 block S [k][m] in LDS (pitch ld,
+// in elements), read with ds_read_b64_tr_b16 (the f16 helpers move 16-bit
+// values and serve bf16 bits alike): lane (g, i) gets S[k0 + 8g + e][m0 + i]
+// (standard k slots), or S[k0 + 4g + e][m0 + i] and S[k0 + 16 + 4g + e][m0 + i]
+// (split k slots), e = 0 ..
+__device__ __forceinline__ bf16x8 lds_frag_T(const uint16_t *S, int ld, int m0, int k0) {
+    return __builtin_bit_cast(bf16x8, frag_T((const _Float16 *)S, ld, m0, k0));
+}
+__device__ __forceinline__ bf16x8 lds_frag_T_split(const uint16_t *S, int ld, int m0, int k0) {
+    return __builtin_bit_cast(bf16x8, fragAT_split((const _Float16 *)S, ld, m0, k0));
+}
+
+// One chunk's q, k (C x K), dO tile (C x 64) and slot (the four planes and
+// the row factors) as 16-byte pieces, row-major over the workgroup (piece j
+// of a thread covers row (tid + 256 j) / (width / 8), columns
+// 8 ((tid + 256 j) % (width / 8)) .. +7).  Rows at or past T read as zero.
 template <int C, int K> struct BwdChunkRegs {
     static constexpr int NQK = C * K / 8 / 256;
     static constexpr int NDO = C * 64 / 8 / 256;
-    static_assert(NQK >= 1 && NDO >= 1, "tile too small");
-    u32x4 q[NQK], k[NQK], d[NDO];
-    float g, beta;
+    static constexpr int NPL = 4 * C * C / 8 / 256;       // plane pieces
+    static constexpr int NVP = (4 * C + 4) / 4;           // vector pieces (threads < NVP)
+    static_assert(NQK >= 1 && NDO >= 1 && NPL >= 1 && NVP <= 256, "tile too small");
+    u32x4 q[NQK], k[NQK], d[NDO], pl[NPL], vec;
 };
 
 template <int C, int K>
 __device__ __forceinline__ void bwd_load_chunk(BwdChunkRegs<C, K> &r, rsrc_t rq, rsrc_t rk, rsrc_t rdo,
-                                               rsrc_t rg, rsrc_t rb, int t0, uint32_t H, uint32_t rsK,
-                                               uint32_t rsV, int vt) {
+                                               rsrc_t rsl, int t0, uint32_t rsK, uint32_t rsV, int vt) {
+    typedef BwdChunkRegs<C, K> R;
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int j = 0; j < BwdChunkRegs<C, K>::NQK; ++j) {
-        const int pc = tid + 256 * j, row = pc % C, c8 = pc / C;
+    for (int j = 0; j < R::NQK; ++j) {
+        const int pc = tid + 256 * j, row = pc / (K / 8), c8 = pc % (K / 8);
         const uint32_t off = (row * rsK + 8 * c8) * 2;
         r.q[j] = bload128(rq, off, t0 * rsK * 2);
         r.k[j] = bload128(rk, off, t0 * rsK * 2);
     }
 #pragma unroll
-    for (int j = 0; j < BwdChunkRegs<C, K>::NDO; ++j) {
-        const int pc = tid + 256 * j, row = pc % C, c8 = pc / C;
+    for (int j = 0; j < R::NDO; ++j) {
+        const int pc = tid + 256 * j, row = pc / 8, c8 = pc % 8;
         r.d[j] = bload128(rdo, (row * rsV + 64 * vt + 8 * c8) * 2, t0 * rsV * 2);
     }
-    r.g = 0.f;
-    r.beta = 0.f;
-    if (tid < C) {
-        r.g = __uint_as_float(bload32(rg, tid * H * 4, t0 * H * 4));
-        r.beta = __uint_as_float(bload32(rb, tid * H * 4, t0 * H * 4));
-    }
+#pragma unroll
+    for (int j = 0; j < R::NPL; ++j) r.pl[j] = bload128(rsl, (tid + 256 * j) * 16, 0);
+    r.vec = bload128(rsl, BwdSlot<C>::kVec + (tid < R::NVP ? tid : 0) * 16, 0);
 }
 
 // The state's gradient, backwards over the chunks: one workgroup per (batch,
 // head, 64-wide V tile); wave w owns value columns 16 w .. 16 w + 15 of the
 // tile, so the chain (dh' -> dD -> dR -> dh) is wave-local.  Per chunk:
-//   phase L  the chunk's q, k, dO tile into LDS (row and transposed forms),
-//            the previous chunk's loads issued
-//   phase 1  gate cumsum and row factors (wave 0)
-//   phase 2  Gram tiles: A into fp32 LDS, P^T as bf16 high and low parts
-//   phase 3  T = (I + A)^-1 (fp32), T^T as bf16 parts
+//   phase L  the chunk's q, k, dO tile and its slot (P^T, T^T, the row
+//            factors) into LDS; the previous chunk's loads issued
 //   phase 4  off the chain: P^T dO and (diag(b) Q)^T dO for the wave's columns
 //   phase 5  the chain; stores dh' (the chunk-end gradient), dR and dv
-// Rows past T load as zero: g = 0, beta = 0, k = q = dO = 0, an identity step
-// whose outputs the buffer ranges drop.
+// Rows past T load as zero: an identity step whose outputs the buffer ranges
+// drop.
 template <int C, int K>
 __global__ __launch_bounds__(256, 1) void bwd_dh_kernel(BwdParams p) {
     typedef BwdScanLayout<C, K> L;
-    constexpr int LK = L::LK, LC = L::LC, LF = L::LF;
+    typedef BwdChunkRegs<C, K> CR;
+    constexpr int LK = L::LK, LC = L::LC, LD = L::LD;
     constexpr int NB = C / 16, NS = C / 32, KT16 = K / 16, KS = K / 32;
-    constexpr int NQK = BwdChunkRegs<C, K>::NQK, NDO = BwdChunkRegs<C, K>::NDO;
     __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
     uint16_t *Qr = (uint16_t *)(smem + L::kQr), *Kr = (uint16_t *)(smem + L::kKr);
-    uint16_t *QT = (uint16_t *)(smem + L::kQT), *KT = (uint16_t *)(smem + L::kKT);
-    uint16_t *DoT = (uint16_t *)(smem + L::kDoT);
+    uint16_t *Do = (uint16_t *)(smem + L::kDo);
     uint16_t *PT = (uint16_t *)(smem + L::kPT), *TT = (uint16_t *)(smem + L::kTT);
-    float *Af = (float *)(smem + L::kAf), *Tf = (float *)(smem + L::kTf);
-    float *gam = (float *)(smem + L::kVec), *bv = gam + C, *cv = bv + C, *betv = cv + C, *glp = betv + C;
+    float *bv = (float *)(smem + L::kVec), *cv = bv + C, *bbv = cv + C, *glp = bbv + 2 * C;
 
     const int tid = threadIdx.x, wv = wave_id(), l = lane_id(), g = l >> 4, n = l & 15;
     int bid = blockIdx.x;
@@ -183,17 +340,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dh_kernel(BwdParams p) {
     const rsrc_t rq = make_rsrc((const bf16_t *)p.q + row0 * K, (uint32_t)T * rsK * 2);
     const rsrc_t rk = make_rsrc((const bf16_t *)p.k + row0 * K, (uint32_t)T * rsK * 2);
     const rsrc_t rdo = make_rsrc((const bf16_t *)p.dout + row0 * V, (uint32_t)T * rsV * 2);
-    const rsrc_t rg = make_rsrc(p.g + row0, (uint32_t)T * H * 4);
-    const rsrc_t rb = make_rsrc(p.beta + row0, (uint32_t)T * H * 4);
     const rsrc_t rdR = make_rsrc(p.dR + row0 * V, (uint32_t)T * rsV * 4);
-    const rsrc_t rdv = make_rsrc(p.dv + row0 * V, (uint32_t)T * rsV * 4);
     const int col = 64 * vt + 16 * wv;                       // the wave's first value column
     // this lane's (row 4g + 2 (n & 1), column n & ~1) of a 16 x 16 tile
     const uint32_t pr_row = 4 * g + 2 * (n & 1), pr_col = col + (n & ~1);
-
-    // entries never written below stay zero: P^T below its diagonal, T above
-    for (int i = tid; i < 2 * C * LC / 2; i += 256) ((uint32_t *)PT)[i] = 0u;
-    for (int i = tid; i < C * LF; i += 256) Tf[i] = 0.f;
+    auto slot_rsrc = [&](int c) {
+        return make_rsrc((const char *)p.prep + (((int64_t)b * NT + c) * H + h) * BwdSlot<C>::kBytes,
+                         (uint32_t)BwdSlot<C>::kBytes);
+    };
 
     // the state's gradient at the end of the last chunk: dhT or zero
     float4v dh[KT16];
@@ -204,96 +358,51 @@ __global__ __launch_bounds__(256, 1) void bwd_dh_kernel(BwdParams p) {
             dh[kt][e] = p.dhT ? p.dhT[((int64_t)b * H + h) * K * V + (16 * kt + 4 * g + e) * V + col + n] : 0.f;
     }
 
-    BwdChunkRegs<C, K> cr;
-    if (NT > 0) bwd_load_chunk<C, K>(cr, rq, rk, rdo, rg, rb, (NT - 1) * C, H, rsK, rsV, vt);
+    // a chunk's dh' and dR are stored one iteration late, after the next
+    // chunk's loads have been issued: a wait for those loads then never has
+    // to wait for these stores as well (the wait counter covers both, in
+    // issue order), and the stores have a whole chunk to drain
+    float4v dhs[KT16], rrs[NB];
+    int cs = -1;
+    auto store_stash = [&](int cc) {
+        float *he = p.dhe + (((int64_t)b * NT + cc) * H + h) * K * V;
+        const rsrc_t rhe = make_rsrc(he, (uint32_t)(K * V * 4));
+#pragma unroll
+        for (int kt = 0; kt < KT16; ++kt)
+            store_acc_pairs<float>(dhs[kt], rhe, (pr_row * V + pr_col) * 4, V * 4, 16 * kt * V * 4);
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            store_acc_pairs<float>(rrs[i], rdR, (pr_row * rsV + pr_col) * 4, rsV * 4, (cc * C + 16 * i) * rsV * 4);
+    };
+
+    CR cr;
+    if (NT > 0) bwd_load_chunk<C, K>(cr, rq, rk, rdo, slot_rsrc(NT - 1), (NT - 1) * C, rsK, rsV, vt);
 #pragma unroll 1
     for (int c = NT - 1; c >= 0; --c) {
         const int t0 = c * C;
-        __syncthreads();
+        bwd_barrier();
         // phase L
 #pragma unroll
-        for (int j = 0; j < NQK; ++j) {
-            const int pc = tid + 256 * j, row = pc % C, c8 = pc / C;
+        for (int j = 0; j < CR::NQK; ++j) {
+            const int pc = tid + 256 * j, row = pc / (K / 8), c8 = pc % (K / 8);
             *(u32x4 *)(Qr + row * LK + 8 * c8) = cr.q[j];
             *(u32x4 *)(Kr + row * LK + 8 * c8) = cr.k[j];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                QT[(8 * c8 + e) * LC + row] = half_of(cr.q[j], e);
-                KT[(8 * c8 + e) * LC + row] = half_of(cr.k[j], e);
-            }
         }
 #pragma unroll
-        for (int j = 0; j < NDO; ++j) {
-            const int pc = tid + 256 * j, row = pc % C, c8 = pc / C;
+        for (int j = 0; j < CR::NDO; ++j) {
+            const int pc = tid + 256 * j, row = pc / 8, c8 = pc % 8;
+            *(u32x4 *)(Do + row * LD + 8 * c8) = cr.d[j];
+        }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) DoT[(8 * c8 + e) * LC + row] = half_of(cr.d[j], e);
+        for (int j = 0; j < CR::NPL; ++j) {
+            const int pc = tid + 256 * j, pl = pc / (C * C / 8), rem = pc % (C * C / 8);
+            const int row = rem / (C / 8), c8 = rem % (C / 8);
+            *(u32x4 *)(PT + pl * C * LC + row * LC + 8 * c8) = cr.pl[j];   // PT, TT planes are adjacent
         }
-        if (tid < C) {
-            gam[tid] = cr.g;
-            betv[tid] = cr.beta;
-        }
-        if (c > 0) bwd_load_chunk<C, K>(cr, rq, rk, rdo, rg, rb, t0 - C, H, rsK, rsV, vt);
-        __syncthreads();
-        // phase 1
-        if (wv == 0) {
-            float x = l < C ? gam[l] : 0.f;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const float y = __shfl_up(x, o);
-                if (l >= o) x += y;
-            }
-            const float xl = __shfl(x, C - 1);
-            if (l < C) {
-                gam[l] = x;
-                bv[l] = __expf(x);
-                cv[l] = __expf(xl - x);
-            }
-            if (l == 0) *glp = __expf(xl);
-        }
-        __syncthreads();
-        // phase 2: the lower tiles (i >= j) of k k^T (-> A) and q k^T (-> P^T)
-        {
-            constexpr int NLT = NB * (NB + 1) / 2;
-#pragma unroll 1
-            for (int t = wv; t < 2 * NLT; t += 4) {
-                const bool isP = t >= NLT;
-                int tt = isP ? t - NLT : t, i = 0;
-                while (tt > i) {
-                    tt -= i + 1;
-                    ++i;
-                }
-                const int j = tt;
-                float4v acc = {0, 0, 0, 0};
-                const uint16_t *Aop = isP ? Qr : Kr;
-#pragma unroll
-                for (int s = 0; s < KS; ++s)
-                    mfma_bf(acc, lds_frag(Aop, LK, 16 * i, 32 * s), lds_frag(Kr, LK, 16 * j, 32 * s));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int R = 16 * i + 4 * g + e, S = 16 * j + n;
-                    const float d = __expf(fminf(gam[R] - gam[S], 0.f));
-                    if (!isP) {
-                        Af[R * LF + S] = S < R ? betv[R] * acc[e] * d : 0.f;
-                    } else {
-                        uint16_t hh, ll;
-                        bf_split(S <= R ? acc[e] * d : 0.f, hh, ll);
-                        PT[S * LC + R] = hh;
-                        PT[C * LC + S * LC + R] = ll;
-                    }
-                }
-            }
-        }
-        __syncthreads();
-        // phase 3
-        tri_inverse<C, LF>(Af, Tf);
-        for (int idx = tid; idx < C * C; idx += 256) {
-            const int s = idx / C, r = idx % C;
-            uint16_t hh, ll;
-            bf_split(Tf[s * LF + r], hh, ll);
-            TT[r * LC + s] = hh;
-            TT[C * LC + r * LC + s] = ll;
-        }
-        __syncthreads();
+        if (tid < CR::NVP) *(u32x4 *)(bv + 4 * tid) = cr.vec;
+        if (c > 0) bwd_load_chunk<C, K>(cr, rq, rk, rdo, slot_rsrc(c - 1), t0 - C, rsK, rsV, vt);
+        if (cs >= 0) store_stash(cs);
+        bwd_barrier();
         // phase 4: P^T dO (tokens x the wave's columns) and (diag(b) Q)^T dO
         // (keys x the wave's columns)
         float4v pd[NB], qd[KT16];
@@ -302,7 +411,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dh_kernel(BwdParams p) {
 #pragma unroll
             for (int st = 0; st < NS; ++st) {
                 const int s0 = 32 * st + 8 * g;
-                const u32x4 raw = *(const u32x4 *)(DoT + (16 * wv + n) * LC + s0);
+                const u32x4 raw = __builtin_bit_cast(u32x4, lds_frag_T(Do, LD, 16 * wv, 32 * st));
                 uint16_t hh[8], ll[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
@@ -316,7 +425,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dh_kernel(BwdParams p) {
 #pragma unroll
                 for (int st = 0; st < NS; ++st) {
                     if (32 * st + 31 < 16 * i) continue;      // P^T is zero below its diagonal
-                    const bf16x8 bdo = lds_frag(DoT, LC, 16 * wv, 32 * st);
+                    const bf16x8 bdo = lds_frag_T(Do, LD, 16 * wv, 32 * st);
                     mfma_bf(pd[i], lds_frag(PT, LC, 16 * i, 32 * st), bdo);
                     mfma_bf(pd[i], lds_frag(PT + C * LC, LC, 16 * i, 32 * st), bdo);
                 }
@@ -326,20 +435,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dh_kernel(BwdParams p) {
                 qd[kt] = float4v{0, 0, 0, 0};
 #pragma unroll
                 for (int st = 0; st < NS; ++st) {
-                    const bf16x8 a = lds_frag(QT, LC, 16 * kt, 32 * st);
+                    const bf16x8 a = lds_frag_T(Qr, LK, 16 * kt, 32 * st);
                     mfma_bf(qd[kt], a, bq_h[st]);
                     mfma_bf(qd[kt], a, bq_l[st]);
                 }
             }
         }
         // phase 5: the chain.  dh' is this chunk's end gradient.
-        {
-            float *he = p.dhe + (((int64_t)b * NT + c) * H + h) * K * V;
-            const rsrc_t rhe = make_rsrc(he, (uint32_t)(K * V * 4));
 #pragma unroll
-            for (int kt = 0; kt < KT16; ++kt)
-                store_acc_pairs<float>(dh[kt], rhe, (pr_row * V + pr_col) * 4, V * 4, 16 * kt * V * 4);
-        }
+        for (int kt = 0; kt < KT16; ++kt) dhs[kt] = dh[kt];
         float4v rr[NB];
         {
             bf16x8 bh[KS], bl[KS];
@@ -376,14 +480,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dh_kernel(BwdParams p) {
             }
         }
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const uint32_t voff = (pr_row * rsV + pr_col) * 4, soff = (t0 + 16 * i) * rsV * 4;
-            store_acc_pairs<float>(rr[i], rdR, voff, rsV * 4, soff);
-            float4v x;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = betv[16 * i + 4 * g + e] * rr[i][e];
-            store_acc_pairs<float>(x, rdv, voff, rsV * 4, soff);
-        }
+        for (int i = 0; i < NB; ++i) rrs[i] = rr[i];
+        cs = c;
         {
             bf16x8 uh[NS], ul[NS];
 #pragma unroll
@@ -392,8 +490,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dh_kernel(BwdParams p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r0 = 32 * st + 4 * g + e, r1 = r0 + 16;
-                    x0[e] = -betv[r0] * bv[r0] * rr[2 * st][e];
-                    x1[e] = -betv[r1] * bv[r1] * rr[2 * st + 1][e];
+                    x0[e] = -bbv[r0] * rr[2 * st][e];
+                    x1[e] = -bbv[r1] * rr[2 * st + 1][e];
                 }
                 acc_frag_split(x0, x1, uh[st], ul[st]);
             }
@@ -403,7 +501,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dh_kernel(BwdParams p) {
                 float4v acc = gl * dh[kt] + qd[kt];
 #pragma unroll
                 for (int st = 0; st < NS; ++st) {
-                    const bf16x8 a = lds_frag_split(KT, LC, 16 * kt, 32 * st);
+                    const bf16x8 a = lds_frag_T_split(Kr, LK, 16 * kt, 32 * st);
                     mfma_bf(acc, a, uh[st]);
                     mfma_bf(acc, a, ul[st]);
                 }
@@ -411,6 +509,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dh_kernel(BwdParams p) {
             }
         }
     }
+    if (cs >= 0) store_stash(cs);
     if (p.dh0) {
         const rsrc_t rh0 = make_rsrc(p.dh0 + ((int64_t)b * H + h) * K * V, (uint32_t)(K * V * 4));
 #pragma unroll
@@ -451,54 +550,88 @@ template <int C, int K, int V> struct BwdGradLayout {
     static_assert(kBytes <= kLdsBytesMax, "LDS budget");
 };
 
-// rows x X bf16 block of a token-major tensor (row pitch rs elements) into
-// LDS [rows][LD], 16 bytes per piece, row-major over the workgroup.
-template <int ROWS, int X, int LD>
-__device__ __forceinline__ void bwd_rows_to_lds(uint16_t *dst, rsrc_t r, uint32_t rs, uint32_t soff) {
-    constexpr int PPR = X / 8, NP = ROWS * PPR;
+// rows x X bf16 block of a token-major tensor (row pitch rs elements) as
+// 16-byte pieces in registers, row-major over the workgroup (piece j of a
+// thread: row (tid + 256 j) / (X / 8), columns 8 ((tid + 256 j) % (X / 8))).
+template <int ROWS, int X> struct RowsBf {
+    static constexpr int PPR = X / 8, NP = ROWS * PPR / 256;
+    static_assert(NP >= 1 && ROWS * PPR % 256 == 0, "pieces");
+    u32x4 v[NP];
+    __device__ void load(rsrc_t r, uint32_t rs, uint32_t soff) {
 #pragma unroll
-    for (int pc = threadIdx.x; pc < NP; pc += 256) {
-        const int row = pc / PPR, c8 = pc % PPR;
-        *(u32x4 *)(dst + row * LD + 8 * c8) = bload128(r, (row * rs + 8 * c8) * 2, soff);
-    }
-}
-
-// rows x X fp32 block (row pitch rs elements) into LDS as bf16 high and low
-// planes [2][rows][LD], 16 bytes per piece.  With rv (bf16, same layout and
-// pitch rvs) also each row's dot product of the two, reduced over the row's
-// pieces (consecutive lanes) and added into acc[row] by the row's first lane.
-template <int ROWS, int X, int LD, bool DOT>
-__device__ __forceinline__ void bwd_split_to_lds(uint16_t *dst, rsrc_t r, uint32_t rs, uint32_t soff,
-                                                 rsrc_t rv, uint32_t rvs, uint32_t vsoff, float *acc) {
-    constexpr int PPR = X / 4, NP = ROWS * PPR;
-    static_assert(PPR <= 64 && (PPR & (PPR - 1)) == 0, "pieces per row");
-#pragma unroll
-    for (int pc = threadIdx.x; pc < NP; pc += 256) {
-        const int row = pc / PPR, c4 = pc % PPR;
-        const u32x4 x = bload128(r, (row * rs + 4 * c4) * 4, soff);
-        uint16_t hh[4], ll[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) bf_split(__uint_as_float(x[e]), hh[e], ll[e]);
-        *(u32x2 *)(dst + row * LD + 4 * c4) = __builtin_bit_cast(u32x2, hh);
-        *(u32x2 *)(dst + ROWS * LD + row * LD + 4 * c4) = __builtin_bit_cast(u32x2, ll);
-        if constexpr (DOT) {
-            const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rv, (row * rvs + 4 * c4) * 2, vsoff, 0);
-            float d = __uint_as_float(x[0]) * __uint_as_float(w[0] << 16) +
-                      __uint_as_float(x[1]) * __uint_as_float(w[0] & 0xffff0000u) +
-                      __uint_as_float(x[2]) * __uint_as_float(w[1] << 16) +
-                      __uint_as_float(x[3]) * __uint_as_float(w[1] & 0xffff0000u);
-#pragma unroll
-            for (int o = PPR / 2; o >= 1; o >>= 1) d += __shfl_xor(d, o);
-            if (c4 == 0) acc[row] += d;
+        for (int j = 0; j < NP; ++j) {
+            const int pc = threadIdx.x + 256 * j, row = pc / PPR, c8 = pc % PPR;
+            v[j] = bload128(r, (row * rs + 8 * c8) * 2, soff);
         }
     }
+    template <int LD> __device__ void put(uint16_t *dst) const {
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int pc = threadIdx.x + 256 * j, row = pc / PPR, c8 = pc % PPR;
+            *(u32x4 *)(dst + row * LD + 8 * c8) = v[j];
+        }
+    }
+};
+
+// rows x X fp32 block as 16-byte pieces (four values; piece j of a thread:
+// row (tid + 256 j) / (X / 4), columns 4 ((tid + 256 j) % (X / 4)) .. +3),
+// put into LDS as bf16 high and low planes [2][ROWS][LD].
+template <int ROWS, int X> struct RowsF32 {
+    static constexpr int PPR = X / 4, NP = ROWS * PPR / 256;
+    static_assert(NP >= 1 && ROWS * PPR % 256 == 0 && PPR <= 32, "pieces");
+    u32x4 v[NP];
+    __device__ static int row(int j) { return (threadIdx.x + 256 * j) / PPR; }
+    __device__ static int c4(int j) { return (threadIdx.x + 256 * j) % PPR; }
+    __device__ void load(rsrc_t r, uint32_t rs, uint32_t soff) {
+#pragma unroll
+        for (int j = 0; j < NP; ++j) v[j] = bload128(r, (row(j) * rs + 4 * c4(j)) * 4, soff);
+    }
+    template <int LD> __device__ void put_split(uint16_t *dst) const {
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            uint16_t hh[4], ll[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bf_split(__uint_as_float(v[j][e]), hh[e], ll[e]);
+            *(u32x2 *)(dst + row(j) * LD + 4 * c4(j)) = __builtin_bit_cast(u32x2, hh);
+            *(u32x2 *)(dst + ROWS * LD + row(j) * LD + 4 * c4(j)) = __builtin_bit_cast(u32x2, ll);
+        }
+    }
+};
+
+// Dot product of four fp32 values with four bf16 values (8 bytes).
+__device__ __forceinline__ float dot4_bf(const u32x4 &x, const u32x2 &w) {
+    return __uint_as_float(x[0]) * __uint_as_float(w[0] << 16) +
+           __uint_as_float(x[1]) * __uint_as_float(w[0] & 0xffff0000u) +
+           __uint_as_float(x[2]) * __uint_as_float(w[1] << 16) +
+           __uint_as_float(x[3]) * __uint_as_float(w[1] & 0xffff0000u);
 }
 
-// Sum over the 16 lanes of a lane group (the columns of an accumulator tile).
+template <int CTRL> __device__ __forceinline__ float dpp_t(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+// Sum over the 16 lanes of a row (the columns of an accumulator tile), on
+// DPP: quad swaps, then the half-row and row mirrors; every lane gets the
+// sum, in an order that does not depend on scheduling.
 __device__ __forceinline__ float sum16(float x) {
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    x += dpp_t<0xB1>(x);
+    x += dpp_t<0x4E>(x);
+    x += dpp_t<0x141>(x);
+    x += dpp_t<0x140>(x);
     return x;
+}
+
+
+// Store four consecutive fp32 values of a row (16 bytes at byte offset off,
+// a multiple of 32 for the even lane of a lane pair, the odd lane's piece
+// following it) as 8-byte stores: lanes l and l ^ 1 swap halves, so that
+// each lane's two stores lie 16 bytes apart.
+__device__ __forceinline__ void store_row4_pairs(const float4v &x, rsrc_t r, uint32_t off_even, bool odd) {
+    const float s0 = odd ? x[0] : x[2], s1 = odd ? x[1] : x[3];
+    const float r0 = dpp_t<0xB1>(s0), r1 = dpp_t<0xB1>(s1);
+    const u32x2 a = odd ? u32x2{__float_as_uint(r0), __float_as_uint(r1)} : u32x2{__float_as_uint(x[0]), __float_as_uint(x[1])};
+    const u32x2 b = odd ? u32x2{__float_as_uint(x[2]), __float_as_uint(x[3])} : u32x2{__float_as_uint(r0), __float_as_uint(r1)};
+    __builtin_amdgcn_raw_buffer_store_b64(a, r, off_even + (odd ? 8 : 0), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(b, r, off_even + (odd ? 24 : 16), 0, 0);
 }
 
 template <int C, int K, int V>
@@ -533,7 +666,18 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
     const rsrc_t rh = make_rsrc((const bf16_t *)p.hck + kv, (uint32_t)(K * V * 2));
     const rsrc_t rdh = make_rsrc(p.dhe + kv, (uint32_t)(K * V * 4));
 
-    // q, k (row and transposed forms); g, beta; per-row partial sums cleared
+    // q, k (row and transposed forms) straight into LDS; dO, D, dR and v into
+    // registers (kept until their phases); g, beta; per-row sums cleared
+    RowsBf<C, V> r_do, r_D;
+    RowsF32<C, V> r_dR;
+    r_do.load(rdo, rsV, t0 * rsV * 2);
+    r_D.load(rD, rsV, t0 * rsV * 2);
+    r_dR.load(rdR, rsV, t0 * rsV * 4);
+    u32x2 r_v[RowsF32<C, V>::NP];
+#pragma unroll
+    for (int j = 0; j < RowsF32<C, V>::NP; ++j)
+        r_v[j] = __builtin_amdgcn_raw_buffer_load_b64(rv, (RowsF32<C, V>::row(j) * rsV + 4 * RowsF32<C, V>::c4(j)) * 2,
+                                                      t0 * rsV * 2, 0);
     {
         constexpr int NP = C * K / 8;
 #pragma unroll
@@ -551,10 +695,13 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
         }
         for (int i = tid; i < 12 * C + 4; i += 256) pg[i] = 0.f;
         uint16_t *X = (uint16_t *)(smem + L::kX);
-        bwd_rows_to_lds<C, V, LV>(X + (L::kA_do - L::kX) / 2, rdo, rsV, t0 * rsV * 2);
-        bwd_rows_to_lds<C, V, LV>(X + (L::kA_d - L::kX) / 2, rD, rsV, t0 * rsV * 2);
-        bwd_split_to_lds<C, V, LV, false>(X + (L::kA_r - L::kX) / 2, rdR, rsV, t0 * rsV * 4, rdR, 0, 0, nullptr);
+        r_do.template put<LV>(X + (L::kA_do - L::kX) / 2);
+        r_D.template put<LV>(X + (L::kA_d - L::kX) / 2);
+        r_dR.template put_split<LV>(X + (L::kA_r - L::kX) / 2);
     }
+    // phase B's h, in flight through phase A
+    RowsBf<K, V> r_h;
+    r_h.load(rh, V, 0);
     if (wv == 0) {
         float x = l < C ? __uint_as_float(bload32(rg, l * H * 4, t0 * H * 4)) : 0.f;
         const float bt = l < C ? __uint_as_float(bload32(rb, l * H * 4, t0 * H * 4)) : 0.f;
@@ -571,7 +718,7 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
             betv[l] = bt;
         }
     }
-    __syncthreads();
+    bwd_barrier();
 
     // phase A: lower C x C tiles of this wave
     float4v Fv[MT], Gv[MT];
@@ -635,11 +782,11 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
             if (g == 0) pg[wv * C + 16 * j + n] -= cs;
         }
     }
-    __syncthreads();
+    bwd_barrier();
     // phase A2: F, F^T, G + G^T as bf16 parts
     uint16_t *Fp = (uint16_t *)(smem + L::kF), *FTp = (uint16_t *)(smem + L::kFT), *Gp = (uint16_t *)(smem + L::kGs);
-    for (int i = tid; i < 6 * C * LC / 2; i += 256) ((uint32_t *)Fp)[i] = 0u;
-    __syncthreads();
+    for (int i = tid; i < 6 * C * LC / 8; i += 256) ((u32x4 *)Fp)[i] = u32x4{0u, 0u, 0u, 0u};
+    bwd_barrier();
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
         const int t = wv + 4 * m;
@@ -670,7 +817,7 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
             }
         }
     }
-    __syncthreads();
+    bwd_barrier();
     // phase A3: dq = F K, dk = F^T Q + (G + G^T) K for this wave's key columns
     float4v dq[NB][CT], dk[NB][CT];
 #pragma unroll
@@ -697,16 +844,37 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
             dq[i][ct] = aq;
             dk[i][ct] = ak;
         }
-    __syncthreads();
-    // phase B: Z = dO h^T, Y = dR h^T; with v . dR into beta's row sums
+    bwd_barrier();
+    // phase B: Z = dO h^T, Y = dR h^T.  Its operands come from registers;
+    // v . dR goes into beta's row sums (a row's pieces are consecutive lanes)
+    // and dv = beta dR out; phase C's operands are issued.
+    RowsF32<K, V> r_dh;
+    u32x2 r_hh[RowsF32<K, V>::NP];
     {
+        typedef RowsF32<C, V> RF;
         uint16_t *X = (uint16_t *)(smem + L::kX);
-        bwd_rows_to_lds<C, V, LV>(X + (L::kB_do - L::kX) / 2, rdo, rsV, t0 * rsV * 2);
-        bwd_split_to_lds<C, V, LV, true>(X + (L::kB_r - L::kX) / 2, rdR, rsV, t0 * rsV * 4, rv, rsV,
-                                         t0 * rsV * 2, pb + wv * C);
-        bwd_rows_to_lds<K, V, LV>(X + (L::kB_h - L::kX) / 2, rh, V, 0);
+        r_do.template put<LV>(X + (L::kB_do - L::kX) / 2);
+        r_dR.template put_split<LV>(X + (L::kB_r - L::kX) / 2);
+        r_h.template put<LV>(X + (L::kB_h - L::kX) / 2);
+        const rsrc_t rdv = make_rsrc(p.dv + row0 * V, (uint32_t)T * rsV * 4);
+#pragma unroll
+        for (int j = 0; j < RF::NP; ++j) {
+            const int row = RF::row(j), c4 = RF::c4(j);
+            float d = sum16(dot4_bf(r_dR.v[j], r_v[j]));
+            if (RF::PPR == 32) d += __shfl_xor(d, 16);
+            if (c4 == 0) pb[wv * C + row] += d;
+            const float bt = betv[row];
+            const float4v x = {bt * __uint_as_float(r_dR.v[j][0]), bt * __uint_as_float(r_dR.v[j][1]),
+                               bt * __uint_as_float(r_dR.v[j][2]), bt * __uint_as_float(r_dR.v[j][3])};
+            store_row4_pairs(x, rdv, ((t0 + row) * rsV + 4 * (c4 & ~1)) * 4, c4 & 1);
+        }
+        r_dh.load(rdh, V, 0);
+#pragma unroll
+        for (int j = 0; j < RowsF32<K, V>::NP; ++j)
+            r_hh[j] = __builtin_amdgcn_raw_buffer_load_b64(
+                rh, (RowsF32<K, V>::row(j) * V + 4 * RowsF32<K, V>::c4(j)) * 2, 0, 0);
     }
-    __syncthreads();
+    bwd_barrier();
     {
         const uint16_t *Do = (const uint16_t *)(smem + L::kB_do), *Hm = (const uint16_t *)(smem + L::kB_h);
         const uint16_t *Rh = (const uint16_t *)(smem + L::kB_r), *Rl = Rh + C * LV;
@@ -748,34 +916,21 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
             }
         }
     }
-    __syncthreads();
+    bwd_barrier();
     // phase C: W = D dh'^T; with <h, dh'>
     {
         uint16_t *X = (uint16_t *)(smem + L::kX);
-        bwd_rows_to_lds<C, V, LV>(X + (L::kC_d - L::kX) / 2, rD, rsV, t0 * rsV * 2);
+        r_D.template put<LV>(X + (L::kC_d - L::kX) / 2);
+        r_dh.template put_split<LV>(X + (L::kC_dh - L::kX) / 2);
         float hdp = 0.f;
-        constexpr int PPR = V / 4, NP = K * PPR;
-        uint16_t *dst = X + (L::kC_dh - L::kX) / 2;
 #pragma unroll
-        for (int pc = tid; pc < NP; pc += 256) {
-            const int row = pc / PPR, c4 = pc % PPR;
-            const u32x4 x = bload128(rdh, (row * V + 4 * c4) * 4, 0);
-            const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rh, (row * V + 4 * c4) * 2, 0, 0);
-            uint16_t hh[4], ll[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) bf_split(__uint_as_float(x[e]), hh[e], ll[e]);
-            *(u32x2 *)(dst + row * LV + 4 * c4) = __builtin_bit_cast(u32x2, hh);
-            *(u32x2 *)(dst + K * LV + row * LV + 4 * c4) = __builtin_bit_cast(u32x2, ll);
-            hdp += __uint_as_float(x[0]) * __uint_as_float(w[0] << 16) +
-                   __uint_as_float(x[1]) * __uint_as_float(w[0] & 0xffff0000u) +
-                   __uint_as_float(x[2]) * __uint_as_float(w[1] << 16) +
-                   __uint_as_float(x[3]) * __uint_as_float(w[1] & 0xffff0000u);
-        }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) hdp += __shfl_xor(hdp, o);
+        for (int j = 0; j < RowsF32<K, V>::NP; ++j) hdp += dot4_bf(r_dh.v[j], r_hh[j]);
+        hdp = sum16(hdp);
+        hdp += __shfl_xor(hdp, 16);
+        hdp += __shfl_xor(hdp, 32);
         if (l == 0) hd[wv] = hdp;
     }
-    __syncthreads();
+    bwd_barrier();
     {
         const uint16_t *Dm = (const uint16_t *)(smem + L::kC_d);
         const uint16_t *Hh = (const uint16_t *)(smem + L::kC_dh), *Hl = Hh + K * LV;
@@ -822,7 +977,7 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
                 store_acc_pairs<float>(dk[i][ct], rdk, voff, rsK * 4, soff);
             }
     }
-    __syncthreads();
+    bwd_barrier();
     // the gate's and beta's gradients: per-row sums in a fixed order, the
     // last row's extra terms, then the reverse cumsum within the chunk
     if (wv == 0) {

@@ -8,8 +8,12 @@ namespace {
 
 template <int C, int K, int V>
 gdn_status launch_backward(BwdParams &bp, hipStream_t s) {
-    const int gscan = bp.B * bp.H * bp.nvt;
-    gdn_status st = launch_kernel((const void *)&bwd_dh_kernel<C, K>, gscan, &bp, s, 256);
+    gdn_status st;
+    if (bp.NT > 0) {
+        st = launch_kernel((const void *)&bwd_prep_kernel<C, K>, bp.B * bp.H * bp.NT, &bp, s, 256);
+        if (st != GDN_OK) return st;
+    }
+    st = launch_kernel((const void *)&bwd_dh_kernel<C, K>, bp.B * bp.H * bp.nvt, &bp, s, 256);
     if (st != GDN_OK || bp.NT == 0) return st;
     return launch_kernel((const void *)&bwd_grad_kernel<C, K, V>, bp.B * bp.H * bp.NT, &bp, s, 256);
 }
@@ -26,9 +30,14 @@ gdn_status backward_k(const gdn_problem *pr, BwdParams &bp, hipStream_t s) {
 
 }  // namespace
 
+static int64_t slot_bytes(int64_t chunk) {
+    return chunk == 32 ? BwdSlot<32>::kBytes : BwdSlot<64>::kBytes;
+}
+
 int64_t backward_workspace_bytes(const gdn_problem *pr) {
     const int64_t nt = (pr->T + pr->chunk - 1) / pr->chunk;
-    return pr->B * pr->T * pr->H * pr->V * 4 + pr->B * nt * pr->H * pr->K * pr->V * 4;
+    return pr->B * pr->T * pr->H * pr->V * 4 + pr->B * nt * pr->H * pr->K * pr->V * 4 +
+           pr->B * nt * pr->H * slot_bytes(pr->chunk);
 }
 
 gdn_status enqueue_backward(const gdn_problem *pr, const void *q, const void *k, const void *v,
@@ -44,6 +53,7 @@ gdn_status enqueue_backward(const gdn_problem *pr, const void *q, const void *k,
     bp.NT = (int)((pr->T + pr->chunk - 1) / pr->chunk);
     bp.dR = (float *)ws;
     bp.dhe = ws ? (float *)ws + pr->B * pr->T * pr->H * pr->V : nullptr;
+    bp.prep = ws ? (void *)(bp.dhe + pr->B * bp.NT * pr->H * pr->K * pr->V) : nullptr;
     bp.swizzle = ((int64_t)bp.B * bp.H * bp.nvt) % 8 == 0 ? 1 : 0;
     return pr->chunk == 32 ? backward_k<32>(pr, bp, s) : backward_k<64>(pr, bp, s);
 }

@@ -219,13 +219,16 @@ gdn_status gdn_rescan_dq(const gdn_problem *problem, const void *q, const void *
  *                         GDN_BF16: they are read in that dtype)
  *   dq, dk [B,T,H,K], dv [B,T,H,V], dbeta, dg [B,T,H]   fp32, written in full
  *   dh0  [B,H,K,V] fp32   h0's gradient, or NULL (not written)
- * Two launches on the stream: the reverse scan (one workgroup per (batch,
- * head, 64-wide V tile), serial over chunks) writes dR (v's gradient before
- * the beta factor) and the gradient of every chunk's end state into the
+ * Three launches on the stream: one workgroup per (chunk, head) forms each
+ * chunk's factors of the reverse scan (the decayed Gram products, T^T and
+ * P^T, the row factors); the reverse scan (one workgroup per (batch, head,
+ * 64-wide V tile), serial over chunks) writes dR (v's gradient before the
+ * beta factor) and the gradient of every chunk's end state into the
  * workspace, and dv and dh0; then one workgroup per (chunk, head) forms dq,
  * dk, dbeta and dg.  Workspace: gdn_workspace_bytes_backward(problem)
  * bytes, 16-byte aligned: dR [B,T,H,V] fp32, then the chunk-end gradients
- * [B,NT,H,K,V] fp32.  Results are deterministic (no atomics).  Outputs must
+ * [B,NT,H,K,V] fp32, then the per-chunk factors.  Results are
+ * deterministic (no atomics).  Outputs must
  * not alias inputs or each other.  With T = 0 only dh0 is written (= dhT or
  * zero).  GDN_ERR_UNSUPPORTED for the per-key gate, fp32 io, an fp32
  * o_dtype, or a stream whose fp32 rows exceed 4 GiB.
@@ -237,7 +240,8 @@ gdn_status gdn_backward(const gdn_problem *problem, const void *q, const void *k
                         size_t workspace_bytes, void *stream);
 
 /* Workspace gdn_backward needs: B T H V 4 + B NT H K V 4 bytes (NT =
- * ceil(T / chunk)); 0 on bad arguments. */
+ * ceil(T / chunk)) + B NT H slot bytes, a slot being 8 C^2 + 16 C + 16
+ * bytes; 0 on bad arguments. */
 size_t gdn_workspace_bytes_backward(const gdn_problem *problem);
 
 /*

@@ -202,7 +202,7 @@ def _bwd(lib, pr, ws=FAKE, ws_bytes=1 << 40, **kw):
 def test_backward_checks(lib, gdn):
     pr = _problem(gdn, B=2, T=300, H=4, K=128, V=64, chunk=64)
     need = lib.gdn_workspace_bytes_backward(ctypes.byref(pr))
-    assert need == 2 * 300 * 4 * 64 * 4 + 2 * 5 * 4 * 128 * 64 * 4
+    assert need == 2 * 300 * 4 * 64 * 4 + 2 * 5 * 4 * 128 * 64 * 4 + 2 * 5 * 4 * (8 * 64 * 64 + 16 * 64 + 16)
     assert _bwd(lib, pr, ws=None, ws_bytes=0) == 6
     assert _bwd(lib, pr, ws_bytes=need - 1) == 6
     assert _bwd(lib, pr, ws=MISALIGNED) == 4
