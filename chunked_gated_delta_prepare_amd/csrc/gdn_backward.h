@@ -118,14 +118,14 @@ template <int C> struct BwdSlot {
 
 template <int C, int K> struct BwdPrepLayout {
     static constexpr int LK = K + 8, LC = C + 8, LF = C + 4;
-    static constexpr int kQr = 0;                          // q [C][LK]
-    static constexpr int kKr = kQr + C * LK * 2;           // k [C][LK]
-    static constexpr int kAf = kKr + C * LK * 2;           // A fp32 [C][LF]
-    static constexpr int kTf = kAf + C * LF * 4;           // T fp32 [C][LF]
-    static constexpr int kPl = kTf + C * LF * 4;           // P^T h, l, T^T h, l [4][C][LC]
+    static constexpr int cmax(int a, int b) { return a > b ? a : b; }
+    // q, k [C][LK] for the Gram products; afterwards A, T fp32 [C][LF] there
+    static constexpr int kQr = 0, kKr = kQr + C * LK * 2;
+    static constexpr int kAf = 0, kTf = kAf + C * LF * 4;
+    static constexpr int kPl = cmax(2 * C * LK * 2, 2 * C * LF * 4);   // P^T h, l, T^T h, l [4][C][LC]
     static constexpr int kVec = kPl + 4 * C * LC * 2;      // gamma, b, c, beta b, beta [C], gl
     static constexpr int kBytes = kVec + (5 * C + 4) * 4;
-    static_assert(kBytes <= kLdsBytesMax, "LDS budget");
+    static_assert(2 * kBytes <= kLdsBytesMax, "two workgroups per CU");
 };
 
 // The reverse scan's per-chunk factors, one workgroup per (chunk, head):
@@ -133,11 +133,12 @@ template <int C, int K> struct BwdPrepLayout {
 // inverse T = (I + A)^-1 in fp32, then P^T, T^T and the row factors into the
 // chunk's slot.  Rows past T load as zero (an identity step).
 template <int C, int K>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 2) void bwd_prep_kernel(BwdParams p) {
     typedef BwdPrepLayout<C, K> L;
     typedef BwdSlot<C> SL;
     constexpr int LK = L::LK, LC = L::LC, LF = L::LF;
     constexpr int NB = C / 16, KS = K / 32, NLT = NB * (NB + 1) / 2;
+    constexpr int MTP = (2 * NLT + 3) / 4;         // Gram tiles per wave (at most)
     __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
     uint16_t *Qr = (uint16_t *)(smem + L::kQr), *Kr = (uint16_t *)(smem + L::kKr);
     float *Af = (float *)(smem + L::kAf), *Tf = (float *)(smem + L::kTf);
@@ -160,7 +161,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
         *(u32x4 *)(Qr + row * LK + 8 * c8) = bload128(rq, off, t0 * rsK * 2);
         *(u32x4 *)(Kr + row * LK + 8 * c8) = bload128(rk, off, t0 * rsK * 2);
     }
-    for (int i = tid; i < C * LF; i += 256) Tf[i] = 0.f;
     if (wv == 0) {
         const rsrc_t rg = make_rsrc(p.g + row0, (uint32_t)T * H * 4);
         const rsrc_t rb = make_rsrc(p.beta + row0, (uint32_t)T * H * 4);
@@ -183,9 +183,14 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
         if (l == 0) *glp = __expf(xl);
     }
     __syncthreads();
-    // Gram tiles: A (fp32) and P^T (bf16 parts)
-#pragma unroll 1
-    for (int t = wv; t < 2 * NLT; t += 4) {
+    // Gram tiles (k k^T for A, q k^T for P) into registers; then, with q and
+    // k no longer read, A (fp32) and T's zeros over them, and P^T (bf16 parts)
+    float4v gacc[MTP];
+#pragma unroll
+    for (int m = 0; m < MTP; ++m) {
+        const int t = wv + 4 * m;
+        gacc[m] = float4v{0, 0, 0, 0};
+        if (t >= 2 * NLT) continue;
         const bool isP = t >= NLT;
         int tt = isP ? t - NLT : t, i = 0;
         while (tt > i) {
@@ -193,11 +198,25 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
             ++i;
         }
         const int j = tt;
-        float4v acc = {0, 0, 0, 0};
         const uint16_t *Aop = isP ? Qr : Kr;
 #pragma unroll
         for (int s = 0; s < KS; ++s)
-            mfma_bf(acc, lds_frag(Aop, LK, 16 * i, 32 * s), lds_frag(Kr, LK, 16 * j, 32 * s));
+            mfma_bf(gacc[m], lds_frag(Aop, LK, 16 * i, 32 * s), lds_frag(Kr, LK, 16 * j, 32 * s));
+    }
+    __syncthreads();
+    for (int i = tid; i < C * LF; i += 256) Tf[i] = 0.f;
+#pragma unroll
+    for (int m = 0; m < MTP; ++m) {
+        const int t = wv + 4 * m;
+        if (t >= 2 * NLT) continue;
+        const bool isP = t >= NLT;
+        int tt = isP ? t - NLT : t, i = 0;
+        while (tt > i) {
+            tt -= i + 1;
+            ++i;
+        }
+        const int j = tt;
+        const float4v acc = gacc[m];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int R = 16 * i + 4 * g + e, S = 16 * j + n;
@@ -519,9 +538,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dh_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// bwd_grad_kernel: one workgroup per (chunk, head).  LDS holds q and k in
-// row and transposed form for the whole chunk, and one region that the
-// phases reuse:
+// bwd_grad_kernel: one workgroup per (chunk, head).  LDS holds q and k
+// (row-major; transposed fragments come from ds_read_b64_tr_b16) for the
+// whole chunk, and one region that the phases reuse:
 //   A   dO, D, dR (bf16 parts)  -> the C x C tiles: k k^T, q k^T, dO D^T, dR D^T
 //   A2  F, F^T, G + G^T (bf16 parts)                -> F K, F^T Q, (G + G^T) K
 //   B   dO, dR (bf16 parts), h                       -> Z = dO h^T, Y = dR h^T
@@ -535,9 +554,7 @@ template <int C, int K, int V> struct BwdGradLayout {
     static constexpr int LK = K + 8, LC = C + 8, LV = V + 8;
     static constexpr int kQr = 0;
     static constexpr int kKr = kQr + C * LK * 2;
-    static constexpr int kQT = kKr + C * LK * 2;
-    static constexpr int kKT = kQT + K * LC * 2;
-    static constexpr int kX = kKT + K * LC * 2;
+    static constexpr int kX = kKr + C * LK * 2;
     static constexpr int kA_do = kX, kA_d = kA_do + C * LV * 2, kA_r = kA_d + C * LV * 2;
     static constexpr int kF = kX, kFT = kF + 2 * C * LC * 2, kGs = kFT + 2 * C * LC * 2;
     static constexpr int kB_do = kX, kB_r = kB_do + C * LV * 2, kB_h = kB_r + 2 * C * LV * 2;
@@ -644,7 +661,6 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
     static_assert(K % 64 == 0, "key tiles");
     __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
     uint16_t *Qr = (uint16_t *)(smem + L::kQr), *Kr = (uint16_t *)(smem + L::kKr);
-    uint16_t *QT = (uint16_t *)(smem + L::kQT), *KT = (uint16_t *)(smem + L::kKT);
     float *gam = (float *)(smem + L::kVec), *bv = gam + C, *cv = bv + C, *betv = cv + C;
     float *pg = betv + C, *pb = pg + 4 * C, *pkw = pb + 4 * C, *hd = pkw + 4 * C;
 
@@ -666,8 +682,11 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
     const rsrc_t rh = make_rsrc((const bf16_t *)p.hck + kv, (uint32_t)(K * V * 2));
     const rsrc_t rdh = make_rsrc(p.dhe + kv, (uint32_t)(K * V * 4));
 
-    // q, k (row and transposed forms) straight into LDS; dO, D, dR and v into
-    // registers (kept until their phases); g, beta; per-row sums cleared
+    // q, k into LDS; dO, D, dR and v into registers (kept until their
+    // phases); g, beta; per-row sums cleared
+    RowsBf<C, K> r_q, r_k;
+    r_q.load(rq, rsK, t0 * rsK * 2);
+    r_k.load(rk, rsK, t0 * rsK * 2);
     RowsBf<C, V> r_do, r_D;
     RowsF32<C, V> r_dR;
     r_do.load(rdo, rsV, t0 * rsV * 2);
@@ -679,20 +698,8 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
         r_v[j] = __builtin_amdgcn_raw_buffer_load_b64(rv, (RowsF32<C, V>::row(j) * rsV + 4 * RowsF32<C, V>::c4(j)) * 2,
                                                       t0 * rsV * 2, 0);
     {
-        constexpr int NP = C * K / 8;
-#pragma unroll
-        for (int pc = tid; pc < NP; pc += 256) {
-            const int row = pc % C, c8 = pc / C;
-            const uint32_t off = (row * rsK + 8 * c8) * 2;
-            const u32x4 xq = bload128(rq, off, t0 * rsK * 2), xk = bload128(rk, off, t0 * rsK * 2);
-            *(u32x4 *)(Qr + row * LK + 8 * c8) = xq;
-            *(u32x4 *)(Kr + row * LK + 8 * c8) = xk;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                QT[(8 * c8 + e) * LC + row] = half_of(xq, e);
-                KT[(8 * c8 + e) * LC + row] = half_of(xk, e);
-            }
-        }
+        r_q.template put<LK>(Qr);
+        r_k.template put<LK>(Kr);
         for (int i = tid; i < 12 * C + 4; i += 256) pg[i] = 0.f;
         uint16_t *X = (uint16_t *)(smem + L::kX);
         r_do.template put<LV>(X + (L::kA_do - L::kX) / 2);
@@ -828,13 +835,13 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
             float4v aq = {0, 0, 0, 0}, ak = {0, 0, 0, 0};
 #pragma unroll
             for (int st = 0; st < NS; ++st) {
-                const bf16x8 kb = lds_frag(KT, LC, kc, 32 * st);
+                const bf16x8 kb = lds_frag_T(Kr, LK, kc, 32 * st);
                 if (32 * st <= 16 * i + 15) {        // F is zero right of its diagonal
                     mfma_bf(aq, lds_frag(Fp, LC, 16 * i, 32 * st), kb);
                     mfma_bf(aq, lds_frag(Fp + C * LC, LC, 16 * i, 32 * st), kb);
                 }
                 if (32 * st + 31 >= 16 * i) {        // F^T is zero left of its diagonal
-                    const bf16x8 qb = lds_frag(QT, LC, kc, 32 * st);
+                    const bf16x8 qb = lds_frag_T(Qr, LK, kc, 32 * st);
                     mfma_bf(ak, lds_frag(FTp, LC, 16 * i, 32 * st), qb);
                     mfma_bf(ak, lds_frag(FTp + C * LC, LC, 16 * i, 32 * st), qb);
                 }
