@@ -6,9 +6,10 @@
 //   A  = strictly lower  beta_r (k_r . k_s) e^(gamma_r - gamma_s),  T = (I + A)^-1
 //   P  = lower (incl.)   (q_r . k_s) e^(gamma_r - gamma_s)
 //   o  = diag(b) Q h + P D,   h' = e^gamma_last h + (diag(c) K)^T D
-// The state's gradient runs backwards through the chunks (bwd_dh_kernel,
-// serial per (batch, head, 64-wide V tile), the same chain as the forward's
-// scan run in reverse):
+// Three launches.  bwd_prep_kernel forms every chunk's P^T, T^T and row
+// factors at once (one workgroup per (chunk, head)).  Then the state's
+// gradient runs backwards through the chunks (bwd_dh_kernel, serial per
+// (batch, head, 64-wide V tile), the forward's chain run in reverse):
 //   dD = P^T dO + diag(c) K dh'                         (dh': the chunk-end gradient)
 //   dR = T^T dD                                         (v's gradient is diag(beta) dR)
 //   dh = e^gamma_last dh' + (diag(b) Q)^T dO - K^T diag(beta b) dR
