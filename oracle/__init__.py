@@ -399,7 +399,10 @@ def chunk_backward(q, k, v, beta, g, do, chunk, h0=None, dhT=None, hck=None, vne
                 bc = beta[b, s:e, hh]
                 gc = g[b, s:e, hh]
                 gam = np.cumsum(gc if per_key else np.repeat(gc[:, None], K, 1), axis=0)   # [n,K]
-                E = np.exp(gam[:, None, :] - gam[None, :, :])                          # [n,n,K]
+                # E_rsd for s <= r (exponent <= 0); the entries s > r are only ever
+                # multiplied by masked-out zeros, so their exponent is clipped at 0
+                # to keep inf * 0 out of the masks under strong decays
+                E = np.exp(np.minimum(gam[:, None, :] - gam[None, :, :], 0.0))         # [n,n,K]
                 lower = np.tril(np.ones((n, n)), -1)
                 A = lower * bc[:, None] * np.einsum("rd,sd,rsd->rs", kc, kc, E)
                 P = np.tril(np.einsum("rd,sd,rsd->rs", qc, kc, E))
