@@ -521,24 +521,25 @@ def rescan_dq(q, k, v, beta, g, do, chunk, h0=None, *, o_dtype=None, hT=None, hc
 
 def backward(q, k, v, beta, g, do, chunk, hck, vnew, dhT=None, *, want_dh0=True, dq=None, dk=None,
              dv=None, dbeta=None, dg=None, dh0=None, workspace=None, stream=None):
-    """Gradients of the forward (scalar gate, bf16 io) for the loss
-    sum_t o_t . do_t + sum hT * dhT, from the bf16 hck and vnew that
-    forward_states (or rescan_dq) saved for the same inputs and chunk.
-    Returns (dq, dk, dv, dbeta, dg, dh0 or None), fp32.  The workspace
+    """Gradients of the forward (bf16 io; g [B,T,H] one gate per head or
+    [B,T,H,K] one per key dimension) for the loss sum_t o_t . do_t +
+    sum hT * dhT, from the bf16 hck and vnew that forward_states (or
+    rescan_dq) saved for the same inputs and chunk.  Returns (dq, dk, dv,
+    dbeta, dg, dh0 or None), fp32, dg in g's shape.  The workspace
     (gdn_workspace_bytes_backward bytes) is allocated when not given; after
-    the call it holds v's gradient before the beta factor [B,T,H,V] and the
-    gradient of every chunk's end state [B,NT,H,K,V], both fp32."""
+    the call it starts with v's gradient before the beta factor [B,T,H,V]
+    and the gradient of every chunk's end state [B,NT,H,K,V], both fp32."""
     torch = _torch()
     lib = load_library()
     B, T, H, K = q.shape
     V = v.shape[-1]
-    if _gate_kind(g, B, T, H, K):
-        raise ValueError("backward: the per-key gate is not supported")
+    per_key = _gate_kind(g, B, T, H, K)
+    gshape = (B, T, H, K) if per_key else (B, T, H)
     nt = (T + int(chunk) - 1) // int(chunk) if chunk > 0 else 0
     for t, name, dt, shp in ((q, "q", torch.bfloat16, None), (k, "k", torch.bfloat16, (B, T, H, K)),
                              (v, "v", torch.bfloat16, (B, T, H, V)),
                              (do, "do", torch.bfloat16, (B, T, H, V)),
-                             (beta, "beta", torch.float32, (B, T, H)), (g, "g", torch.float32, (B, T, H)),
+                             (beta, "beta", torch.float32, (B, T, H)), (g, "g", torch.float32, gshape),
                              (hck, "hck", torch.bfloat16, (B, nt, H, K, V)),
                              (vnew, "vnew", torch.bfloat16, (B, T, H, V))):
         _need(t, name, dt, shp)
@@ -550,15 +551,15 @@ def backward(q, k, v, beta, g, do, chunk, hck, vnew, dhT=None, *, want_dh0=True,
     dk = torch.empty(B, T, H, K, **f32) if dk is None else dk
     dv = torch.empty(B, T, H, V, **f32) if dv is None else dv
     dbeta = torch.empty(B, T, H, **f32) if dbeta is None else dbeta
-    dg = torch.empty(B, T, H, **f32) if dg is None else dg
+    dg = torch.empty(*gshape, **f32) if dg is None else dg
     if dh0 is None and want_dh0:
         dh0 = torch.empty(B, H, K, V, **f32)
     for t, name, shp in ((dq, "dq", (B, T, H, K)), (dk, "dk", (B, T, H, K)), (dv, "dv", (B, T, H, V)),
-                         (dbeta, "dbeta", (B, T, H)), (dg, "dg", (B, T, H))):
+                         (dbeta, "dbeta", (B, T, H)), (dg, "dg", gshape)):
         _need(t, name, torch.float32, shp)
     if dh0 is not None:
         _need(dh0, "dh0", torch.float32, (B, H, K, V))
-    pr = _problem(q, v, chunk, False, torch.bfloat16)
+    pr = _problem(q, v, chunk, per_key, torch.bfloat16)
     need = int(lib.gdn_workspace_bytes_backward(ctypes.byref(pr)))
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=dev, dtype=torch.uint8)

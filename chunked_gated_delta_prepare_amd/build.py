@@ -51,6 +51,7 @@ UNITS = {
     "gdn_forward_pipe_split.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
     "gdn_split.hip": [],
     "gdn_backward.hip": [],
+    "gdn_backward_kda.hip": [],
 }
 
 

@@ -443,9 +443,7 @@ gdn_status gdn_backward(const gdn_problem *problem, const void *q, const void *k
                         size_t workspace_bytes, void *stream) {
     gdn_status st = check_problem(problem);
     if (st != GDN_OK) return st;
-    if (problem->gate != GDN_GATE_HEAD || problem->io_dtype != GDN_BF16 ||
-        problem->o_dtype != GDN_BF16)
-        return GDN_ERR_UNSUPPORTED;
+    if (problem->io_dtype != GDN_BF16 || problem->o_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
     // per-stream 32-bit byte offsets: fp32 [T, H, K | V] rows and one head's K x V block
     const int64_t row_bytes = problem->H * 4 * std::max(problem->K, problem->V);
     if (problem->T * row_bytes >= ((int64_t)1 << 32)) return GDN_ERR_UNSUPPORTED;

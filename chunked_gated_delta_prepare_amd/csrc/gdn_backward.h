@@ -50,6 +50,7 @@ struct BwdParams {
     float *dR;                      // workspace [B, T, H, V]
     float *dhe;                     // workspace [B, NT, H, K, V]: chunk-end gradients
     void *prep;                     // workspace: the reverse scan's per-chunk slots (BwdSlot)
+    float *dpa;                     // workspace, per-key gate: dP, dA [B, NT, H][2][C][C]
     int B, T, H, V, nvt, NT;
     int swizzle;
 };

@@ -30,14 +30,17 @@ gdn_status backward_k(const gdn_problem *pr, BwdParams &bp, hipStream_t s) {
 
 }  // namespace
 
-static int64_t slot_bytes(int64_t chunk) {
-    return chunk == 32 ? BwdSlot<32>::kBytes : BwdSlot<64>::kBytes;
+static int64_t slot_bytes(const gdn_problem *pr) {
+    if (pr->gate == GDN_GATE_KEY) return backward_kda_slot_bytes(pr->chunk, pr->K);
+    return pr->chunk == 32 ? BwdSlot<32>::kBytes : BwdSlot<64>::kBytes;
 }
 
 int64_t backward_workspace_bytes(const gdn_problem *pr) {
     const int64_t nt = (pr->T + pr->chunk - 1) / pr->chunk;
-    return pr->B * pr->T * pr->H * pr->V * 4 + pr->B * nt * pr->H * pr->K * pr->V * 4 +
-           pr->B * nt * pr->H * slot_bytes(pr->chunk);
+    int64_t bytes = pr->B * pr->T * pr->H * pr->V * 4 + pr->B * nt * pr->H * pr->K * pr->V * 4 +
+                    pr->B * nt * pr->H * slot_bytes(pr);
+    if (pr->gate == GDN_GATE_KEY) bytes += pr->B * nt * pr->H * 2 * pr->chunk * pr->chunk * 4;
+    return bytes;
 }
 
 gdn_status enqueue_backward(const gdn_problem *pr, const void *q, const void *k, const void *v,
@@ -54,7 +57,9 @@ gdn_status enqueue_backward(const gdn_problem *pr, const void *q, const void *k,
     bp.dR = (float *)ws;
     bp.dhe = ws ? (float *)ws + pr->B * pr->T * pr->H * pr->V : nullptr;
     bp.prep = ws ? (void *)(bp.dhe + pr->B * bp.NT * pr->H * pr->K * pr->V) : nullptr;
+    bp.dpa = ws ? (float *)((char *)bp.prep + pr->B * bp.NT * pr->H * slot_bytes(pr)) : nullptr;
     bp.swizzle = ((int64_t)bp.B * bp.H * bp.nvt) % 8 == 0 ? 1 : 0;
+    if (pr->gate == GDN_GATE_KEY) return enqueue_backward_kda(pr, bp, s);
     return pr->chunk == 32 ? backward_k<32>(pr, bp, s) : backward_k<64>(pr, bp, s);
 }
 

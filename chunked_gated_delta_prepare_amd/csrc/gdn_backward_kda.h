@@ -1,0 +1,929 @@
+// gdn_backward kernels for the per-key gate (Kimi-Delta-Attention): the same
+// chunk algebra as gdn_backward.h with every decay per key column d.  With
+// Gamma = log2(e) * gamma (the chunk-local inclusive cumsum of g, per key):
+//   E_rsd = 2^(Gamma_rd - Gamma_sd),  b_rd = 2^Gamma_rd,
+//   c_rd = 2^(Gamma_Ld - Gamma_rd),   gl_d = 2^Gamma_Ld  (L the chunk's last row)
+//   A_rs = beta_r sum_d k_rd k_sd E_rsd (s < r),  P_rs = sum_d q_rd k_sd E_rsd (s <= r)
+// The reverse scan: dD = P^T dO + (K * c) dh', dR = T^T dD,
+//   dh = diag(gl) dh' + (Q * b)^T dO - (K * b)^T diag(beta) dR.
+// The gradients, with dP = lower(dO D^T), dA = -strictly lower(dR D^T),
+// Z = dO h^T, Y = dR h^T, W = D dh'^T and the four decay-weighted sums
+//   U1_rd = sum_{s<=r} dP_rs k_sd E_rsd,   U3_rd = sum_{s<r} dA_rs k_sd E_rsd,
+//   U2_sd = sum_{r>=s} dP_rs q_rd E_rsd,   U4_sd = sum_{r>s} dA_rs beta_r k_rd E_rsd:
+//   dq = b * Z + U1,   dk = -beta b * Y + c * W + U2 + beta U3 + U4,
+//   dbeta_r = dR_r . v_r - sum_d b_rd k_rd Y_rd + sum_d k_rd U3_rd,
+//   dgamma_rd = b q Z - beta b k Y - c k W + q U1 - k U2 + beta k U3 - k U4,
+//   the last row also taking sum_s c_sd k_sd W_sd + gl_d <h_d, dh'_d>,
+//   dg the reverse cumsum of dgamma over each chunk's rows, per key.
+// Every exponent is a difference Gamma_r - Gamma_s with s <= r, so every
+// factor is at most 1.  Four launches: the per-chunk factors
+// (bwd_prep_kda_kernel), the reverse scan (bwd_dh_kda_kernel), the matrix
+// products of the gradients (bwd_grad_kda_kernel) and the decay-weighted
+// sums (bwd_dec_kda_kernel).
+#pragma once
+
+#include "gdn_backward.h"
+
+namespace gdn {
+
+// A chunk's slot: P^T, T^T (bf16 high and low parts, [C][C] each), Gamma
+// [C][K] fp32, beta [C], gl [K].
+template <int C, int K> struct BwdSlotK {
+    static constexpr int kGam = 8 * C * C;
+    static constexpr int kBeta = kGam + C * K * 4;
+    static constexpr int kGl = kBeta + C * 4;
+    static constexpr int kBytes = kGl + K * 4;
+    static_assert(kBytes % 16 == 0, "slot pieces");
+};
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bfv(const u32x4 &x, int e) {
+    return (e & 1) ? bf_hi(x[e >> 1]) : bf_lo(x[e >> 1]);
+}
+
+// Column-wise inclusive cumsum of a [C][ld] fp32 LDS block over its C rows,
+// for columns 0 .. X-1, scaled by `scale`; all 256 threads, in 256 / X
+// segments of rows (X = 64 or 128).  Ends with a barrier.
+template <int C, int X>
+__device__ __forceinline__ void col_cumsum(float *G, int ld, float scale) {
+    constexpr int SEG = 256 / X, RPS = C / SEG;
+    const int d = threadIdx.x % X, sg = threadIdx.x / X;
+    float acc = 0.f;
+    for (int r = sg * RPS; r < (sg + 1) * RPS; ++r) {
+        acc += G[r * ld + d];
+        G[r * ld + d] = acc;
+    }
+    bwd_barrier();
+    float off = 0.f;
+    for (int s = 0; s < sg; ++s) off += G[((s + 1) * RPS - 1) * ld + d];
+    bwd_barrier();
+    for (int r = sg * RPS; r < (sg + 1) * RPS; ++r) G[r * ld + d] = (G[r * ld + d] + off) * scale;
+    bwd_barrier();
+}
+
+// Reverse (suffix) cumsum over the C rows of each column, in place.
+template <int C, int X>
+__device__ __forceinline__ void col_revsum(float *G, int ld) {
+    constexpr int SEG = 256 / X, RPS = C / SEG;
+    const int d = threadIdx.x % X, sg = threadIdx.x / X;
+    float acc = 0.f;
+    for (int r = (sg + 1) * RPS - 1; r >= sg * RPS; --r) {
+        acc += G[r * ld + d];
+        G[r * ld + d] = acc;
+    }
+    bwd_barrier();
+    float off = 0.f;
+    for (int s = sg + 1; s < SEG; ++s) off += G[(s * RPS) * ld + d];
+    bwd_barrier();
+    for (int r = sg * RPS; r < (sg + 1) * RPS; ++r) G[r * ld + d] += off;
+    bwd_barrier();
+}
+
+// ---------------------------------------------------------------------------
+// bwd_prep_kda_kernel: one workgroup per (chunk, head).  A and P with the
+// per-key decays: an off-diagonal 16-row block pair (I > J) splits every
+// pair's decay at m, the last row of block J, so both operands are decayed
+// toward m (q_I, k_I by 2^(Gamma_I - Gamma_m), k_J by 2^(Gamma_m - Gamma_J),
+// factors <= 1) and the product runs on the matrix cores (bf16 high and low
+// parts); a diagonal block is summed entry by entry over d with the exact
+// factor.  Then T = (I + A)^-1 (fp32) and the slot.
+// ---------------------------------------------------------------------------
+template <int C, int K> struct BwdPrepKLayout {
+    static constexpr int LK = K + 8, LC = C + 8, LF = C + 4, LG = K + 4;
+    static constexpr int cmax(int a, int b) { return a > b ? a : b; }
+    static constexpr int kQr = 0, kKr = kQr + C * LK * 2;    // q, k; later A, T fp32 [C][LF]
+    static constexpr int kAf = 0, kTf = kAf + C * LF * 4;
+    static constexpr int kGm = cmax(2 * C * LK * 2, 2 * C * LF * 4);   // Gamma [C][LG]
+    static constexpr int kPl = kGm + C * LG * 4;             // P^T h, l, T^T h, l [4][C][LC]
+    static constexpr int kVec = kPl + 4 * C * LC * 2;        // beta [C]
+    static constexpr int kBytes = kVec + C * 4;
+    static_assert(kBytes <= kLdsBytesMax, "LDS budget");
+};
+
+// Eight decayed values of row `row` of S (bf16 [.][LK]) at columns d0 .. +7,
+// times 2^(G[row][d] - G[mrow][d]) (sign +1) or 2^(G[mrow][d] - G[row][d])
+// (sign -1), as bf16 high and low parts.
+template <int LK, int LG>
+__device__ __forceinline__ void decayed8(const uint16_t *S, const float *G, int row, int mrow, int d0, float sign,
+                                         bf16x8 &fh, bf16x8 &fl) {
+    const u32x4 raw = *(const u32x4 *)(S + row * LK + d0);
+    const float4v g0 = *(const float4v *)(G + row * LG + d0), g1 = *(const float4v *)(G + row * LG + d0 + 4);
+    const float4v m0 = *(const float4v *)(G + mrow * LG + d0), m1 = *(const float4v *)(G + mrow * LG + d0 + 4);
+    uint16_t hh[8], ll[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float gr = e < 4 ? g0[e] : g1[e - 4], gm = e < 4 ? m0[e] : m1[e - 4];
+        bf_split(bfv(raw, e) * fast_exp2(sign * (gr - gm)), hh[e], ll[e]);
+    }
+    fh = __builtin_bit_cast(bf16x8, hh);
+    fl = __builtin_bit_cast(bf16x8, ll);
+}
+
+template <int C, int K>
+__global__ __launch_bounds__(256, 1) void bwd_prep_kda_kernel(BwdParams p) {
+    typedef BwdPrepKLayout<C, K> L;
+    typedef BwdSlotK<C, K> SL;
+    constexpr int LK = L::LK, LC = L::LC, LF = L::LF, LG = L::LG;
+    constexpr int NB = C / 16, KS = K / 32, NOD = NB * (NB - 1) / 2;
+    constexpr int NIT = 2 * NOD + NB, MTP = (NIT + 3) / 4;
+    __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
+    uint16_t *Qr = (uint16_t *)(smem + L::kQr), *Kr = (uint16_t *)(smem + L::kKr);
+    float *Af = (float *)(smem + L::kAf), *Tf = (float *)(smem + L::kTf);
+    float *Gm = (float *)(smem + L::kGm);
+    uint16_t *Pl = (uint16_t *)(smem + L::kPl);
+    float *betv = (float *)(smem + L::kVec);
+
+    const int tid = threadIdx.x, wv = wave_id(), l = lane_id(), g = l >> 4, n = l & 15;
+    const int NT = p.NT, T = p.T;
+    const int c = blockIdx.x % NT, bh = blockIdx.x / NT, b = bh / p.H, h = bh % p.H;
+    const int t0 = c * C;
+    const uint32_t H = p.H, rsK = H * K;
+    const int64_t row0 = (int64_t)b * T * H + h;
+    const rsrc_t rq = make_rsrc((const bf16_t *)p.q + row0 * K, (uint32_t)T * rsK * 2);
+    const rsrc_t rk = make_rsrc((const bf16_t *)p.k + row0 * K, (uint32_t)T * rsK * 2);
+    const rsrc_t rg = make_rsrc(p.g + row0 * K, (uint32_t)T * rsK * 4);
+    const rsrc_t rb = make_rsrc(p.beta + row0, (uint32_t)T * H * 4);
+#pragma unroll
+    for (int pc = tid; pc < C * K / 8; pc += 256) {
+        const int row = pc / (K / 8), c8 = pc % (K / 8);
+        const uint32_t off = (row * rsK + 8 * c8) * 2;
+        *(u32x4 *)(Qr + row * LK + 8 * c8) = bload128(rq, off, t0 * rsK * 2);
+        *(u32x4 *)(Kr + row * LK + 8 * c8) = bload128(rk, off, t0 * rsK * 2);
+    }
+#pragma unroll
+    for (int pc = tid; pc < C * K / 4; pc += 256) {
+        const int row = pc / (K / 4), c4 = pc % (K / 4);
+        *(u32x4 *)(Gm + row * LG + 4 * c4) = bload128(rg, (row * rsK + 4 * c4) * 4, t0 * rsK * 4);
+    }
+    if (tid < C) betv[tid] = __uint_as_float(bload32(rb, tid * H * 4, t0 * H * 4));
+    bwd_barrier();
+    col_cumsum<C, K>(Gm, LG, kLog2e);
+
+    // Gram items: off-diagonal block pairs of A (k k), of P (q k), then the
+    // diagonal blocks (A and P together)
+    float4v ga[MTP], gb[MTP];
+#pragma unroll
+    for (int m = 0; m < MTP; ++m) {
+        const int t = wv + 4 * m;
+        ga[m] = float4v{0, 0, 0, 0};
+        gb[m] = float4v{0, 0, 0, 0};
+        if (t >= NIT) continue;
+        if (t < 2 * NOD) {
+            const bool isP = t >= NOD;
+            int tt = isP ? t - NOD : t, i = 1;
+            while (tt >= i) {
+                tt -= i;
+                ++i;
+            }
+            const int j = tt, mrow = 16 * j + 15;
+            const uint16_t *X = isP ? Qr : Kr;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                bf16x8 ah, al, bh, bl;
+                decayed8<LK, LG>(X, Gm, 16 * i + n, mrow, 32 * s + 8 * g, 1.f, ah, al);
+                decayed8<LK, LG>(Kr, Gm, 16 * j + n, mrow, 32 * s + 8 * g, -1.f, bh, bl);
+                mfma_bf(ga[m], ah, bh);
+                mfma_bf(ga[m], ah, bl);
+                mfma_bf(ga[m], al, bh);
+            }
+        } else {
+            const int i = t - 2 * NOD, S = 16 * i + n;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int R = 16 * i + 4 * g + e;
+                if (S > R) continue;
+                float sa = 0.f, sp = 0.f;
+                for (int d = 0; d < K; d += 4) {
+                    const u32x2 ks = *(const u32x2 *)(Kr + S * LK + d), kr = *(const u32x2 *)(Kr + R * LK + d);
+                    const u32x2 qr = *(const u32x2 *)(Qr + R * LK + d);
+                    const float4v gr = *(const float4v *)(Gm + R * LG + d), gs = *(const float4v *)(Gm + S * LG + d);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const float E = fast_exp2(gr[u] - gs[u]);
+                        const float kv = (u & 1) ? bf_hi(ks[u >> 1]) : bf_lo(ks[u >> 1]);
+                        const float kk = (u & 1) ? bf_hi(kr[u >> 1]) : bf_lo(kr[u >> 1]);
+                        const float qq = (u & 1) ? bf_hi(qr[u >> 1]) : bf_lo(qr[u >> 1]);
+                        sa += kk * kv * E;
+                        sp += qq * kv * E;
+                    }
+                }
+                ga[m][e] = sa;
+                gb[m][e] = sp;
+            }
+        }
+    }
+    bwd_barrier();
+    for (int i = tid; i < C * LF; i += 256) Tf[i] = 0.f;
+#pragma unroll
+    for (int m = 0; m < MTP; ++m) {
+        const int t = wv + 4 * m;
+        if (t >= NIT) continue;
+        if (t < 2 * NOD) {
+            const bool isP = t >= NOD;
+            int tt = isP ? t - NOD : t, i = 1;
+            while (tt >= i) {
+                tt -= i;
+                ++i;
+            }
+            const int j = tt;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int R = 16 * i + 4 * g + e, S = 16 * j + n;
+                if (!isP) {
+                    Af[R * LF + S] = betv[R] * ga[m][e];
+                } else {
+                    uint16_t hh, ll;
+                    bf_split(ga[m][e], hh, ll);
+                    Pl[S * LC + R] = hh;
+                    Pl[C * LC + S * LC + R] = ll;
+                    Pl[R * LC + S] = 0;                  // P^T is zero below its diagonal
+                    Pl[C * LC + R * LC + S] = 0;
+                }
+            }
+        } else {
+            const int i = t - 2 * NOD, S = 16 * i + n;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int R = 16 * i + 4 * g + e;
+                Af[R * LF + S] = S < R ? betv[R] * ga[m][e] : 0.f;
+                uint16_t hh, ll;
+                bf_split(S <= R ? gb[m][e] : 0.f, hh, ll);
+                Pl[S * LC + R] = hh;
+                Pl[C * LC + S * LC + R] = ll;
+            }
+        }
+    }
+    __syncthreads();
+    tri_inverse<C, LF>(Af, Tf);
+    for (int idx = tid; idx < C * C; idx += 256) {
+        const int s = idx / C, r = idx % C;
+        uint16_t hh, ll;
+        bf_split(Tf[s * LF + r], hh, ll);
+        Pl[2 * C * LC + r * LC + s] = hh;
+        Pl[3 * C * LC + r * LC + s] = ll;
+    }
+    __syncthreads();
+    char *slot = (char *)p.prep + (((int64_t)b * NT + c) * H + h) * SL::kBytes;
+    const rsrc_t rsl = make_rsrc(slot, (uint32_t)SL::kBytes);
+#pragma unroll
+    for (int pc = tid; pc < C * C; pc += 256) {
+        const int pl = pc / (C * C / 4), rem = pc % (C * C / 4), row = rem / (C / 4), c4 = rem % (C / 4);
+        const u32x2 x = *(const u32x2 *)(Pl + pl * C * LC + row * LC + 4 * c4);
+        __builtin_amdgcn_raw_buffer_store_b64(x, rsl, (pl * C * C + row * C + 4 * c4) * 2, 0, 0);
+    }
+#pragma unroll
+    for (int pc = tid; pc < C * K / 2; pc += 256) {
+        const int row = pc / (K / 2), c2 = pc % (K / 2);
+        const u32x2 x = *(const u32x2 *)(Gm + row * LG + 2 * c2);
+        __builtin_amdgcn_raw_buffer_store_b64(x, rsl, SL::kGam + (row * K + 2 * c2) * 4, 0, 0);
+    }
+    if (tid < C) bstore32(__float_as_uint(betv[tid]), rsl, SL::kBeta + tid * 4, 0);
+    for (int d = tid; d < K; d += 256)
+        bstore32(__float_as_uint(fast_exp2(Gm[(C - 1) * LG + d])), rsl, SL::kGl + d * 4, 0);
+}
+
+// ---------------------------------------------------------------------------
+// bwd_dh_kda_kernel: the reverse scan with per-key decays, one workgroup per
+// (batch, head, 64-wide V tile), as bwd_dh_kernel: the decayed operands
+// (k * c, q * b, k * b) are formed from q, k and Gamma as the fragments are
+// read.
+// ---------------------------------------------------------------------------
+template <int C, int K> struct BwdScanKLayout {
+    static constexpr int LK = K + 8, LC = C + 8, LD = 64 + 8, LG = K + 4;
+    static constexpr int kQr = 0, kKr = kQr + C * LK * 2;
+    static constexpr int kDo = kKr + C * LK * 2;
+    static constexpr int kPT = kDo + C * LD * 2;
+    static constexpr int kTT = kPT + 2 * C * LC * 2;
+    static constexpr int kGm = kTT + 2 * C * LC * 2;       // Gamma [C][LG]
+    static constexpr int kVec = kGm + C * LG * 4;          // beta [C], gl [K]
+    static constexpr int kBytes = kVec + (C + K) * 4;
+    static_assert(kBytes <= kLdsBytesMax, "LDS budget");
+};
+
+template <int C, int K> struct BwdChunkRegsK {
+    static constexpr int NQK = C * K / 8 / 256;
+    static constexpr int NDO = C * 64 / 8 / 256;
+    static constexpr int NPL = 4 * C * C / 8 / 256;
+    static constexpr int NGM = C * K / 4 / 256;
+    static constexpr int NVP = (C + K) / 4;
+    static_assert(NQK >= 1 && NDO >= 1 && NPL >= 1 && NGM >= 1 && NVP <= 256, "tile too small");
+    u32x4 q[NQK], k[NQK], d[NDO], pl[NPL], gm[NGM], vec;
+};
+
+template <int C, int K>
+__device__ __forceinline__ void bwd_load_chunk_kda(BwdChunkRegsK<C, K> &r, rsrc_t rq, rsrc_t rk, rsrc_t rdo,
+                                                   rsrc_t rsl, int t0, uint32_t rsK, uint32_t rsV, int vt) {
+    typedef BwdChunkRegsK<C, K> R;
+    typedef BwdSlotK<C, K> SL;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < R::NQK; ++j) {
+        const int pc = tid + 256 * j, row = pc / (K / 8), c8 = pc % (K / 8);
+        const uint32_t off = (row * rsK + 8 * c8) * 2;
+        r.q[j] = bload128(rq, off, t0 * rsK * 2);
+        r.k[j] = bload128(rk, off, t0 * rsK * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < R::NDO; ++j) {
+        const int pc = tid + 256 * j, row = pc / 8, c8 = pc % 8;
+        r.d[j] = bload128(rdo, (row * rsV + 64 * vt + 8 * c8) * 2, t0 * rsV * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < R::NPL; ++j) r.pl[j] = bload128(rsl, (tid + 256 * j) * 16, 0);
+#pragma unroll
+    for (int j = 0; j < R::NGM; ++j) r.gm[j] = bload128(rsl, SL::kGam + (tid + 256 * j) * 16, 0);
+    r.vec = bload128(rsl, SL::kBeta + (tid < R::NVP ? tid : 0) * 16, 0);
+}
+
+template <int C, int K>
+__global__ __launch_bounds__(256, 1) void bwd_dh_kda_kernel(BwdParams p) {
+    typedef BwdScanKLayout<C, K> L;
+    typedef BwdChunkRegsK<C, K> CR;
+    typedef BwdSlotK<C, K> SL;
+    constexpr int LK = L::LK, LC = L::LC, LD = L::LD, LG = L::LG;
+    constexpr int NB = C / 16, NS = C / 32, KT16 = K / 16, KS = K / 32;
+    __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
+    uint16_t *Qr = (uint16_t *)(smem + L::kQr), *Kr = (uint16_t *)(smem + L::kKr);
+    uint16_t *Do = (uint16_t *)(smem + L::kDo);
+    uint16_t *PT = (uint16_t *)(smem + L::kPT), *TT = (uint16_t *)(smem + L::kTT);
+    float *Gm = (float *)(smem + L::kGm);
+    float *betv = (float *)(smem + L::kVec), *glv = betv + C;
+
+    const int tid = threadIdx.x, wv = wave_id(), l = lane_id(), g = l >> 4, n = l & 15;
+    int bid = blockIdx.x;
+    if (p.swizzle) bid = (bid % 8) * (gridDim.x / 8) + bid / 8;
+    const int vt = bid % p.nvt, bh = bid / p.nvt, b = bh / p.H, h = bh % p.H;
+    const int T = p.T, NT = p.NT, V = p.V;
+    const uint32_t H = p.H, rsK = H * K, rsV = H * V;
+    const int64_t row0 = (int64_t)b * T * H + h;
+    const rsrc_t rq = make_rsrc((const bf16_t *)p.q + row0 * K, (uint32_t)T * rsK * 2);
+    const rsrc_t rk = make_rsrc((const bf16_t *)p.k + row0 * K, (uint32_t)T * rsK * 2);
+    const rsrc_t rdo = make_rsrc((const bf16_t *)p.dout + row0 * V, (uint32_t)T * rsV * 2);
+    const rsrc_t rdR = make_rsrc(p.dR + row0 * V, (uint32_t)T * rsV * 4);
+    const int col = 64 * vt + 16 * wv;
+    const uint32_t pr_row = 4 * g + 2 * (n & 1), pr_col = col + (n & ~1);
+    auto slot_rsrc = [&](int cc) {
+        return make_rsrc((const char *)p.prep + (((int64_t)b * NT + cc) * H + h) * SL::kBytes,
+                         (uint32_t)SL::kBytes);
+    };
+
+    float4v dh[KT16];
+#pragma unroll
+    for (int kt = 0; kt < KT16; ++kt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            dh[kt][e] = p.dhT ? p.dhT[((int64_t)b * H + h) * K * V + (16 * kt + 4 * g + e) * V + col + n] : 0.f;
+    }
+    float4v dhs[KT16], rrs[NB];
+    int cs = -1;
+    auto store_stash = [&](int cc) {
+        float *he = p.dhe + (((int64_t)b * NT + cc) * H + h) * K * V;
+        const rsrc_t rhe = make_rsrc(he, (uint32_t)(K * V * 4));
+#pragma unroll
+        for (int kt = 0; kt < KT16; ++kt)
+            store_acc_pairs<float>(dhs[kt], rhe, (pr_row * V + pr_col) * 4, V * 4, 16 * kt * V * 4);
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            store_acc_pairs<float>(rrs[i], rdR, (pr_row * rsV + pr_col) * 4, rsV * 4, (cc * C + 16 * i) * rsV * 4);
+    };
+
+    CR cr;
+    if (NT > 0) bwd_load_chunk_kda<C, K>(cr, rq, rk, rdo, slot_rsrc(NT - 1), (NT - 1) * C, rsK, rsV, vt);
+#pragma unroll 1
+    for (int c = NT - 1; c >= 0; --c) {
+        const int t0 = c * C;
+        bwd_barrier();
+#pragma unroll
+        for (int j = 0; j < CR::NQK; ++j) {
+            const int pc = tid + 256 * j, row = pc / (K / 8), c8 = pc % (K / 8);
+            *(u32x4 *)(Qr + row * LK + 8 * c8) = cr.q[j];
+            *(u32x4 *)(Kr + row * LK + 8 * c8) = cr.k[j];
+        }
+#pragma unroll
+        for (int j = 0; j < CR::NDO; ++j) {
+            const int pc = tid + 256 * j, row = pc / 8, c8 = pc % 8;
+            *(u32x4 *)(Do + row * LD + 8 * c8) = cr.d[j];
+        }
+#pragma unroll
+        for (int j = 0; j < CR::NPL; ++j) {
+            const int pc = tid + 256 * j, pl = pc / (C * C / 8), rem = pc % (C * C / 8);
+            const int row = rem / (C / 8), c8 = rem % (C / 8);
+            *(u32x4 *)(PT + pl * C * LC + row * LC + 8 * c8) = cr.pl[j];
+        }
+#pragma unroll
+        for (int j = 0; j < CR::NGM; ++j) {
+            const int pc = tid + 256 * j, row = pc / (K / 4), c4 = pc % (K / 4);
+            *(u32x4 *)(Gm + row * LG + 4 * c4) = cr.gm[j];
+        }
+        if (tid < CR::NVP) *(u32x4 *)(betv + 4 * tid) = cr.vec;
+        if (c > 0) bwd_load_chunk_kda<C, K>(cr, rq, rk, rdo, slot_rsrc(c - 1), t0 - C, rsK, rsV, vt);
+        if (cs >= 0) store_stash(cs);
+        bwd_barrier();
+        // P^T dO, and (Q * b)^T dO with the decay on the q operand
+        float4v pd[NB], qd[KT16];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            pd[i] = float4v{0, 0, 0, 0};
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                if (32 * st + 31 < 16 * i) continue;
+                const bf16x8 bdo = lds_frag_T(Do, LD, 16 * wv, 32 * st);
+                mfma_bf(pd[i], lds_frag(PT, LC, 16 * i, 32 * st), bdo);
+                mfma_bf(pd[i], lds_frag(PT + C * LC, LC, 16 * i, 32 * st), bdo);
+            }
+        }
+#pragma unroll
+        for (int kt = 0; kt < KT16; ++kt) {
+            qd[kt] = float4v{0, 0, 0, 0};
+            const int key = 16 * kt + n;
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                const u32x4 raw = __builtin_bit_cast(u32x4, lds_frag_T(Qr, LK, 16 * kt, 32 * st));
+                uint16_t hh[8], ll[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    bf_split(bfv(raw, e) * fast_exp2(Gm[(32 * st + 8 * g + e) * LG + key]), hh[e], ll[e]);
+                const bf16x8 bdo = lds_frag_T(Do, LD, 16 * wv, 32 * st);
+                mfma_bf(qd[kt], __builtin_bit_cast(bf16x8, hh), bdo);
+                mfma_bf(qd[kt], __builtin_bit_cast(bf16x8, ll), bdo);
+            }
+        }
+        // the chain
+#pragma unroll
+        for (int kt = 0; kt < KT16; ++kt) dhs[kt] = dh[kt];
+        float4v rr[NB];
+        {
+            bf16x8 bh[KS], bl[KS];
+#pragma unroll
+            for (int s = 0; s < KS; ++s) acc_frag_split(dh[2 * s], dh[2 * s + 1], bh[s], bl[s]);
+            float4v dd[NB];
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                dd[i] = pd[i];
+                const int r = 16 * i + n;
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    // (k * c) row r at the split slots 32 s + 4 g + e and + 16
+                    const u32x4 raw = __builtin_bit_cast(u32x4, lds_frag_split(Kr, LK, 16 * i, 32 * s));
+                    const int d0 = 32 * s + 4 * g;
+                    const float4v ga0 = *(const float4v *)(Gm + r * LG + d0), ga1 = *(const float4v *)(Gm + r * LG + d0 + 16);
+                    const float4v gl0 = *(const float4v *)(Gm + (C - 1) * LG + d0),
+                                  gl1 = *(const float4v *)(Gm + (C - 1) * LG + d0 + 16);
+                    uint16_t hh[8], ll[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float gr = e < 4 ? ga0[e] : ga1[e - 4], gq = e < 4 ? gl0[e] : gl1[e - 4];
+                        bf_split(bfv(raw, e) * fast_exp2(gq - gr), hh[e], ll[e]);
+                    }
+                    const bf16x8 ah = __builtin_bit_cast(bf16x8, hh), al = __builtin_bit_cast(bf16x8, ll);
+                    mfma_bf(dd[i], ah, bh[s]);
+                    mfma_bf(dd[i], ah, bl[s]);
+                    mfma_bf(dd[i], al, bh[s]);
+                }
+            }
+            bf16x8 xh[NS], xl[NS];
+#pragma unroll
+            for (int st = 0; st < NS; ++st) acc_frag_split(dd[2 * st], dd[2 * st + 1], xh[st], xl[st]);
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                rr[i] = float4v{0, 0, 0, 0};
+#pragma unroll
+                for (int st = 0; st < NS; ++st) {
+                    if (32 * st + 31 < 16 * i) continue;
+                    const bf16x8 ah = lds_frag_split(TT, LC, 16 * i, 32 * st);
+                    const bf16x8 al = lds_frag_split(TT + C * LC, LC, 16 * i, 32 * st);
+                    mfma_bf(rr[i], ah, xh[st]);
+                    mfma_bf(rr[i], ah, xl[st]);
+                    mfma_bf(rr[i], al, xh[st]);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) rrs[i] = rr[i];
+        cs = c;
+        {
+            bf16x8 uh[NS], ul[NS];
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                float4v x0, x1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r0 = 32 * st + 4 * g + e, r1 = r0 + 16;
+                    x0[e] = -betv[r0] * rr[2 * st][e];
+                    x1[e] = -betv[r1] * rr[2 * st + 1][e];
+                }
+                acc_frag_split(x0, x1, uh[st], ul[st]);
+            }
+#pragma unroll
+            for (int kt = 0; kt < KT16; ++kt) {
+                float4v acc = qd[kt];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] += glv[16 * kt + 4 * g + e] * dh[kt][e];
+                const int key = 16 * kt + n;
+#pragma unroll
+                for (int st = 0; st < NS; ++st) {
+                    // (k * b)^T at split slots: rows 32 st + 4 g + e and + 16
+                    const u32x4 raw = __builtin_bit_cast(u32x4, lds_frag_T_split(Kr, LK, 16 * kt, 32 * st));
+                    uint16_t hh[8], ll[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int s = 32 * st + 4 * g + (e & 3) + (e >= 4 ? 16 : 0);
+                        bf_split(bfv(raw, e) * fast_exp2(Gm[s * LG + key]), hh[e], ll[e]);
+                    }
+                    const bf16x8 ah = __builtin_bit_cast(bf16x8, hh), al = __builtin_bit_cast(bf16x8, ll);
+                    mfma_bf(acc, ah, uh[st]);
+                    mfma_bf(acc, ah, ul[st]);
+                    mfma_bf(acc, al, uh[st]);
+                }
+                dh[kt] = acc;
+            }
+        }
+    }
+    if (cs >= 0) store_stash(cs);
+    if (p.dh0) {
+        const rsrc_t rh0 = make_rsrc(p.dh0 + ((int64_t)b * H + h) * K * V, (uint32_t)(K * V * 4));
+#pragma unroll
+        for (int kt = 0; kt < KT16; ++kt)
+            store_acc_pairs<float>(dh[kt], rh0, (pr_row * V + pr_col) * 4, V * 4, 16 * kt * V * 4);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_grad_kda_kernel: one workgroup per (chunk, head), the matrix products of
+// the per-key gradients, laid out as bwd_grad_kernel: dP and dA (C x C, lower
+// entries, fp32) into the workspace; dq = b * Z and dk = -beta b * Y + c * W
+// into dq, dk; the element terms of dgamma (with the last row's extra
+// terms) into dg; beta's row sums into dbeta; dv = beta dR.  The
+// decay-weighted sums are added by bwd_dec_kda_kernel.
+// ---------------------------------------------------------------------------
+template <int C, int K, int V> struct BwdGradKLayout {
+    typedef BwdGradLayout<C, K, V> B;
+    static constexpr int LK = B::LK, LC = B::LC, LV = B::LV, LG = K + 4;
+    static constexpr int kQr = B::kQr, kKr = B::kKr, kX = B::kX;
+    static constexpr int kA_do = B::kA_do, kA_d = B::kA_d, kA_r = B::kA_r;
+    static constexpr int kB_do = B::kB_do, kB_r = B::kB_r, kB_h = B::kB_h;
+    static constexpr int kC_d = B::kC_d, kC_dh = B::kC_dh;
+    static constexpr int kGm = kX + B::kXBytes;                // Gamma [C][LG]
+    static constexpr int kVec = kGm + C * LG * 4;              // beta [C], pb [4][C], hdk [K]
+    static constexpr int kBytes = kVec + (5 * C + K) * 4;
+    static_assert(kBytes <= kLdsBytesMax, "LDS budget");
+};
+
+template <int C, int K, int V>
+__global__ __launch_bounds__(256, 1) void bwd_grad_kda_kernel(BwdParams p) {
+    typedef BwdGradKLayout<C, K, V> L;
+    typedef BwdSlotK<C, K> SL;
+    constexpr int LK = L::LK, LV = L::LV, LG = L::LG;
+    constexpr int NB = C / 16, VS = V / 32, NLT = NB * (NB + 1) / 2;
+    constexpr int MT = (NLT + 3) / 4;
+    constexpr int CT = K / 64;
+    static_assert(K % 64 == 0, "key tiles");
+    __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
+    uint16_t *Qr = (uint16_t *)(smem + L::kQr), *Kr = (uint16_t *)(smem + L::kKr);
+    float *Gm = (float *)(smem + L::kGm);
+    float *betv = (float *)(smem + L::kVec), *pb = betv + C, *hdk = pb + 4 * C;
+
+    const int tid = threadIdx.x, wv = wave_id(), l = lane_id(), g = l >> 4, n = l & 15;
+    const int NT = p.NT, T = p.T;
+    const int c = blockIdx.x % NT, bh = blockIdx.x / NT, b = bh / p.H, h = bh % p.H;
+    const int t0 = c * C;
+    const uint32_t H = p.H, rsK = H * K, rsV = H * V;
+    const int64_t row0 = (int64_t)b * T * H + h;
+    const int64_t ch = ((int64_t)b * NT + c) * H + h;
+    const rsrc_t rq = make_rsrc((const bf16_t *)p.q + row0 * K, (uint32_t)T * rsK * 2);
+    const rsrc_t rk = make_rsrc((const bf16_t *)p.k + row0 * K, (uint32_t)T * rsK * 2);
+    const rsrc_t rv = make_rsrc((const bf16_t *)p.v + row0 * V, (uint32_t)T * rsV * 2);
+    const rsrc_t rdo = make_rsrc((const bf16_t *)p.dout + row0 * V, (uint32_t)T * rsV * 2);
+    const rsrc_t rD = make_rsrc((const bf16_t *)p.vnew + row0 * V, (uint32_t)T * rsV * 2);
+    const rsrc_t rdR = make_rsrc(p.dR + row0 * V, (uint32_t)T * rsV * 4);
+    const rsrc_t rb = make_rsrc(p.beta + row0, (uint32_t)T * H * 4);
+    const rsrc_t rsl = make_rsrc((const char *)p.prep + ch * SL::kBytes, (uint32_t)SL::kBytes);
+    const int64_t kv = ch * K * V;
+    const rsrc_t rh = make_rsrc((const bf16_t *)p.hck + kv, (uint32_t)(K * V * 2));
+    const rsrc_t rdh = make_rsrc(p.dhe + kv, (uint32_t)(K * V * 4));
+
+    RowsBf<C, K> r_q, r_k;
+    r_q.load(rq, rsK, t0 * rsK * 2);
+    r_k.load(rk, rsK, t0 * rsK * 2);
+    RowsBf<C, V> r_do, r_D;
+    RowsF32<C, V> r_dR;
+    r_do.load(rdo, rsV, t0 * rsV * 2);
+    r_D.load(rD, rsV, t0 * rsV * 2);
+    r_dR.load(rdR, rsV, t0 * rsV * 4);
+    u32x2 r_v[RowsF32<C, V>::NP];
+#pragma unroll
+    for (int j = 0; j < RowsF32<C, V>::NP; ++j)
+        r_v[j] = __builtin_amdgcn_raw_buffer_load_b64(rv, (RowsF32<C, V>::row(j) * rsV + 4 * RowsF32<C, V>::c4(j)) * 2,
+                                                      t0 * rsV * 2, 0);
+    {
+        r_q.template put<LK>(Qr);
+        r_k.template put<LK>(Kr);
+#pragma unroll
+        for (int pc = tid; pc < C * K / 4; pc += 256) {
+            const int row = pc / (K / 4), c4 = pc % (K / 4);
+            *(u32x4 *)(Gm + row * LG + 4 * c4) = bload128(rsl, SL::kGam + (row * K + 4 * c4) * 4, 0);
+        }
+        if (tid < C) betv[tid] = __uint_as_float(bload32(rb, tid * H * 4, t0 * H * 4));
+        for (int i = tid; i < 4 * C + K; i += 256) pb[i] = 0.f;
+        uint16_t *X = (uint16_t *)(smem + L::kX);
+        r_do.template put<LV>(X + (L::kA_do - L::kX) / 2);
+        r_D.template put<LV>(X + (L::kA_d - L::kX) / 2);
+        r_dR.template put_split<LV>(X + (L::kA_r - L::kX) / 2);
+    }
+    RowsBf<K, V> r_h;
+    r_h.load(rh, V, 0);
+    bwd_barrier();
+
+    // phase A: dP, dA (lower tiles of this wave) into the workspace
+    {
+        const uint16_t *Do = (const uint16_t *)(smem + L::kA_do), *Dm = (const uint16_t *)(smem + L::kA_d);
+        const uint16_t *Rh = (const uint16_t *)(smem + L::kA_r), *Rl = Rh + C * LV;
+        const rsrc_t rpa = make_rsrc(p.dpa + ch * 2 * C * C, (uint32_t)(2 * C * C * 4));
+        const uint32_t pr_row = 4 * g + 2 * (n & 1);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int t = wv + 4 * m;
+            if (t >= NLT) continue;
+            int tt = t, i = 0;
+            while (tt > i) {
+                tt -= i + 1;
+                ++i;
+            }
+            const int j = tt;
+            float4v dp = {0, 0, 0, 0}, da = {0, 0, 0, 0};
+#pragma unroll
+            for (int s = 0; s < VS; ++s) {
+                const bf16x8 db = lds_frag(Dm, LV, 16 * j, 32 * s);
+                mfma_bf(dp, lds_frag(Do, LV, 16 * i, 32 * s), db);
+                mfma_bf(da, lds_frag(Rh, LV, 16 * i, 32 * s), db);
+                mfma_bf(da, lds_frag(Rl, LV, 16 * i, 32 * s), db);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int R = 16 * i + 4 * g + e, S = 16 * j + n;
+                dp[e] = S <= R ? dp[e] : 0.f;
+                da[e] = S < R ? -da[e] : 0.f;
+            }
+            const uint32_t voff = (pr_row * C + 16 * j + (n & ~1)) * 4;
+            store_acc_pairs<float>(dp, rpa, voff, C * 4, 16 * i * C * 4);
+            store_acc_pairs<float>(da, rpa, voff, C * 4, (C * C + 16 * i * C) * 4);
+        }
+    }
+    bwd_barrier();
+    // phase B: Z, Y; v . dR and dv as in bwd_grad_kernel
+    RowsF32<K, V> r_dh;
+    u32x2 r_hh[RowsF32<K, V>::NP];
+    {
+        typedef RowsF32<C, V> RF;
+        uint16_t *X = (uint16_t *)(smem + L::kX);
+        r_do.template put<LV>(X + (L::kB_do - L::kX) / 2);
+        r_dR.template put_split<LV>(X + (L::kB_r - L::kX) / 2);
+        r_h.template put<LV>(X + (L::kB_h - L::kX) / 2);
+        const rsrc_t rdv = make_rsrc(p.dv + row0 * V, (uint32_t)T * rsV * 4);
+#pragma unroll
+        for (int j = 0; j < RF::NP; ++j) {
+            const int row = RF::row(j), c4 = RF::c4(j);
+            float d = sum16(dot4_bf(r_dR.v[j], r_v[j]));
+            if (RF::PPR == 32) d += __shfl_xor(d, 16);
+            if (c4 == 0) pb[wv * C + row] += d;
+            const float bt = betv[row];
+            const float4v x = {bt * __uint_as_float(r_dR.v[j][0]), bt * __uint_as_float(r_dR.v[j][1]),
+                               bt * __uint_as_float(r_dR.v[j][2]), bt * __uint_as_float(r_dR.v[j][3])};
+            store_row4_pairs(x, rdv, ((t0 + row) * rsV + 4 * (c4 & ~1)) * 4, c4 & 1);
+        }
+        r_dh.load(rdh, V, 0);
+#pragma unroll
+        for (int j = 0; j < RowsF32<K, V>::NP; ++j)
+            r_hh[j] = __builtin_amdgcn_raw_buffer_load_b64(
+                rh, (RowsF32<K, V>::row(j) * V + 4 * RowsF32<K, V>::c4(j)) * 2, 0, 0);
+    }
+    bwd_barrier();
+    float4v dq[NB][CT], dk[NB][CT], dg[NB][CT];
+    {
+        const uint16_t *Do = (const uint16_t *)(smem + L::kB_do), *Hm = (const uint16_t *)(smem + L::kB_h);
+        const uint16_t *Rh = (const uint16_t *)(smem + L::kB_r), *Rl = Rh + C * LV;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            float bky[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const int kc = 16 * (CT * wv + ct);
+                float4v z = {0, 0, 0, 0}, y = {0, 0, 0, 0};
+#pragma unroll
+                for (int s = 0; s < VS; ++s) {
+                    const bf16x8 hb = lds_frag(Hm, LV, kc, 32 * s);
+                    mfma_bf(z, lds_frag(Do, LV, 16 * i, 32 * s), hb);
+                    mfma_bf(y, lds_frag(Rh, LV, 16 * i, 32 * s), hb);
+                    mfma_bf(y, lds_frag(Rl, LV, 16 * i, 32 * s), hb);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int R = 16 * i + 4 * g + e, key = kc + n;
+                    const float bb = fast_exp2(Gm[R * LG + key]);
+                    const float qv = __uint_as_float((uint32_t)Qr[R * LK + key] << 16);
+                    const float kv = __uint_as_float((uint32_t)Kr[R * LK + key] << 16);
+                    dq[i][ct][e] = bb * z[e];
+                    dk[i][ct][e] = -betv[R] * bb * y[e];
+                    dg[i][ct][e] = bb * (qv * z[e] - betv[R] * kv * y[e]);
+                    bky[e] += bb * kv * y[e];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bky[e] = sum16(bky[e]);
+            if (n == 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pb[wv * C + 16 * i + 4 * g + e] -= bky[e];
+            }
+        }
+    }
+    bwd_barrier();
+    // phase C: W; <h_d, dh'_d> per key row
+    {
+        typedef RowsF32<K, V> RK;
+        uint16_t *X = (uint16_t *)(smem + L::kX);
+        r_D.template put<LV>(X + (L::kC_d - L::kX) / 2);
+        r_dh.template put_split<LV>(X + (L::kC_dh - L::kX) / 2);
+#pragma unroll
+        for (int j = 0; j < RK::NP; ++j) {
+            float d = sum16(dot4_bf(r_dh.v[j], r_hh[j]));
+            if (RK::PPR == 32) d += __shfl_xor(d, 16);
+            if (RK::c4(j) == 0) hdk[RK::row(j)] = d;
+        }
+    }
+    bwd_barrier();
+    {
+        const uint16_t *Dm = (const uint16_t *)(smem + L::kC_d);
+        const uint16_t *Hh = (const uint16_t *)(smem + L::kC_dh), *Hl = Hh + K * LV;
+        float cks[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) cks[ct] = 0.f;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const int kc = 16 * (CT * wv + ct);
+                float4v w = {0, 0, 0, 0};
+#pragma unroll
+                for (int s = 0; s < VS; ++s) {
+                    const bf16x8 a = lds_frag(Dm, LV, 16 * i, 32 * s);
+                    mfma_bf(w, a, lds_frag(Hh, LV, kc, 32 * s));
+                    mfma_bf(w, a, lds_frag(Hl, LV, kc, 32 * s));
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int R = 16 * i + 4 * g + e, key = kc + n;
+                    const float cc = fast_exp2(Gm[(C - 1) * LG + key] - Gm[R * LG + key]);
+                    const float kv = __uint_as_float((uint32_t)Kr[R * LK + key] << 16);
+                    dk[i][ct][e] += cc * w[e];
+                    dg[i][ct][e] -= cc * kv * w[e];
+                    cks[ct] += cc * kv * w[e];
+                }
+            }
+        }
+        // gamma_last's terms, sum_s c k W over the column and gl <h_d, dh'_d>,
+        // go to the chunk's last valid row: the padded rows after it (g = 0)
+        // share its gamma, and dg is the reverse cumsum over the rows
+        const int nv = T - t0 < C ? T - t0 : C;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            float x = cks[ct];
+            x += __shfl_xor(x, 16);
+            x += __shfl_xor(x, 32);
+            const int key = 16 * (CT * wv + ct) + n;
+            const float extra = x + fast_exp2(Gm[(C - 1) * LG + key]) * hdk[key];
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (16 * i + 4 * g + e == nv - 1) dg[i][ct][e] += extra;
+        }
+    }
+    {
+        const rsrc_t rdq = make_rsrc(p.dq + row0 * K, (uint32_t)T * rsK * 4);
+        const rsrc_t rdk = make_rsrc(p.dk + row0 * K, (uint32_t)T * rsK * 4);
+        const rsrc_t rdg = make_rsrc(p.dg + row0 * K, (uint32_t)T * rsK * 4);
+        const uint32_t pr_row = 4 * g + 2 * (n & 1);
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const uint32_t voff = (pr_row * rsK + 16 * (CT * wv + ct) + (n & ~1)) * 4;
+                const uint32_t soff = (t0 + 16 * i) * rsK * 4;
+                store_acc_pairs<float>(dq[i][ct], rdq, voff, rsK * 4, soff);
+                store_acc_pairs<float>(dk[i][ct], rdk, voff, rsK * 4, soff);
+                store_acc_pairs<float>(dg[i][ct], rdg, voff, rsK * 4, soff);
+            }
+    }
+    bwd_barrier();
+    if (wv == 0 && l < C) {
+        const float db = pb[l] + pb[C + l] + pb[2 * C + l] + pb[3 * C + l];
+        const rsrc_t rdb = make_rsrc(p.dbeta + row0, (uint32_t)T * H * 4);
+        bstore32(__float_as_uint(db), rdb, l * H * 4, t0 * H * 4);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_dec_kda_kernel: one workgroup per (chunk, head), the four
+// decay-weighted sums, entry by entry with the exact factor: thread (d, x)
+// for key column d and rows x, a row's partner rows in a loop.  Adds them to
+// dq, dk and dbeta, completes dgamma and writes dg = its reverse cumsum over
+// the chunk's rows, per key column.
+// ---------------------------------------------------------------------------
+template <int C, int K> struct BwdDecLayout {
+    static constexpr int kPa = 0;                           // dP, dA fp32 [2][C][C]
+    static constexpr int kQ = kPa + 2 * C * C * 4;          // q, k bf16 [2][C][K]
+    static constexpr int kGm = kQ + 2 * C * K * 2;          // Gamma fp32 [C][K]
+    static constexpr int kGd = kGm + C * K * 4;             // dgamma fp32 [C][K]
+    static constexpr int kVec = kGd + C * K * 4;            // beta [C], pbk [4][C]
+    static constexpr int kBytes = kVec + 5 * C * 4;
+    static_assert(kBytes <= kLdsBytesMax, "LDS budget");
+};
+
+template <int C, int K>
+__global__ __launch_bounds__(256, 1) void bwd_dec_kda_kernel(BwdParams p) {
+    typedef BwdDecLayout<C, K> L;
+    typedef BwdSlotK<C, K> SL;
+    constexpr int SEG = 256 / K;
+    __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
+    float *dP = (float *)(smem + L::kPa), *dA = dP + C * C;
+    uint16_t *Qs = (uint16_t *)(smem + L::kQ), *Ks = Qs + C * K;
+    float *Gm = (float *)(smem + L::kGm), *Gd = (float *)(smem + L::kGd);
+    float *betv = (float *)(smem + L::kVec), *pbk = betv + C;
+
+    const int tid = threadIdx.x, wv = wave_id(), l = lane_id();
+    const int NT = p.NT, T = p.T;
+    const int c = blockIdx.x % NT, bh = blockIdx.x / NT, b = bh / p.H, h = bh % p.H;
+    const int t0 = c * C;
+    const uint32_t H = p.H, rsK = H * K;
+    const int64_t row0 = (int64_t)b * T * H + h;
+    const int64_t ch = ((int64_t)b * NT + c) * H + h;
+    const rsrc_t rq = make_rsrc((const bf16_t *)p.q + row0 * K, (uint32_t)T * rsK * 2);
+    const rsrc_t rk = make_rsrc((const bf16_t *)p.k + row0 * K, (uint32_t)T * rsK * 2);
+    const rsrc_t rb = make_rsrc(p.beta + row0, (uint32_t)T * H * 4);
+    const rsrc_t rsl = make_rsrc((const char *)p.prep + ch * SL::kBytes, (uint32_t)SL::kBytes);
+    const rsrc_t rpa = make_rsrc(p.dpa + ch * 2 * C * C, (uint32_t)(2 * C * C * 4));
+    const rsrc_t rdq = make_rsrc(p.dq + row0 * K, (uint32_t)T * rsK * 4);
+    const rsrc_t rdk = make_rsrc(p.dk + row0 * K, (uint32_t)T * rsK * 4);
+    const rsrc_t rdg = make_rsrc(p.dg + row0 * K, (uint32_t)T * rsK * 4);
+    const rsrc_t rdb = make_rsrc(p.dbeta + row0, (uint32_t)T * H * 4);
+
+#pragma unroll
+    for (int pc = tid; pc < 2 * C * C / 4; pc += 256) *(u32x4 *)(dP + 4 * pc) = bload128(rpa, 16 * pc, 0);
+#pragma unroll
+    for (int pc = tid; pc < C * K / 8; pc += 256) {
+        const int row = pc / (K / 8), c8 = pc % (K / 8);
+        const uint32_t off = (row * rsK + 8 * c8) * 2;
+        *(u32x4 *)(Qs + row * K + 8 * c8) = bload128(rq, off, t0 * rsK * 2);
+        *(u32x4 *)(Ks + row * K + 8 * c8) = bload128(rk, off, t0 * rsK * 2);
+    }
+#pragma unroll
+    for (int pc = tid; pc < C * K / 4; pc += 256) *(u32x4 *)(Gm + 4 * pc) = bload128(rsl, SL::kGam + 16 * pc, 0);
+    if (tid < C) betv[tid] = __uint_as_float(bload32(rb, tid * H * 4, t0 * H * 4));
+    for (int i = tid; i < 4 * C; i += 256) pbk[i] = 0.f;
+    bwd_barrier();
+
+    const int d = tid % K, sg = tid / K;
+    auto ldk = [&](const uint16_t *S, int r) { return __uint_as_float((uint32_t)S[r * K + d] << 16); };
+#pragma unroll 1
+    for (int x = sg; x < C; x += SEG) {
+        const float gx = Gm[x * K + d];
+        float u1 = 0.f, u3 = 0.f, u2 = 0.f, u4 = 0.f;
+#pragma unroll 4
+        for (int s = 0; s <= x; ++s) {
+            const float ks = ldk(Ks, s) * fast_exp2(gx - Gm[s * K + d]);
+            u1 += dP[x * C + s] * ks;
+            u3 += dA[x * C + s] * ks;              // dA's diagonal is zero
+        }
+#pragma unroll 4
+        for (int r = x; r < C; ++r) {
+            const float E = fast_exp2(Gm[r * K + d] - gx);
+            u2 += dP[r * C + x] * ldk(Qs, r) * E;
+            u4 += dA[r * C + x] * betv[r] * ldk(Ks, r) * E;
+        }
+        const float qx = ldk(Qs, x), kx = ldk(Ks, x), bx = betv[x];
+        const uint32_t off = (x * rsK + d) * 4, soff = t0 * rsK * 4;
+        const float dq0 = __uint_as_float(bload32(rdq, off, soff));
+        const float dk0 = __uint_as_float(bload32(rdk, off, soff));
+        const float dg0 = __uint_as_float(bload32(rdg, off, soff));
+        bstore32(__float_as_uint(dq0 + u1), rdq, off, soff);
+        bstore32(__float_as_uint(dk0 + u2 + bx * u3 + u4), rdk, off, soff);
+        Gd[x * K + d] = dg0 + qx * u1 - kx * u2 + bx * kx * u3 - kx * u4;
+        float t = kx * u3;
+        t = sum16(t);
+        t += __shfl_xor(t, 16);
+        t += __shfl_xor(t, 32);
+        if (l == 0) pbk[wv * C + x] = t;
+    }
+    bwd_barrier();
+    col_revsum<C, K>(Gd, K);
+#pragma unroll 1
+    for (int x = sg; x < C; x += SEG) bstore32(__float_as_uint(Gd[x * K + d]), rdg, (x * rsK + d) * 4, t0 * rsK * 4);
+    if (tid < C) {
+        const float db0 = __uint_as_float(bload32(rdb, tid * H * 4, t0 * H * 4));
+        bstore32(__float_as_uint(db0 + pbk[tid] + pbk[C + tid] + pbk[2 * C + tid] + pbk[3 * C + tid]), rdb,
+                 tid * H * 4, t0 * H * 4);
+    }
+}
+
+}  // namespace gdn

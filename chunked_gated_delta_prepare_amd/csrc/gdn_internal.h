@@ -56,6 +56,11 @@ gdn_status enqueue_backward(const gdn_problem *pr, const void *q, const void *k,
                             const void *hck, const void *vnew, float *dq, float *dk, float *dv,
                             float *dbeta, float *dg, float *dh0, void *ws, hipStream_t s);
 
+struct BwdParams;
+// the per-key gate's backward (gdn_backward_kda.hip): slot size and launches
+int64_t backward_kda_slot_bytes(int64_t chunk, int64_t K);
+gdn_status enqueue_backward_kda(const gdn_problem *pr, BwdParams &bp, hipStream_t s);
+
 struct FwdParams;
 // Dispatch a forward problem whose FwdParams carry hck and vnew.
 gdn_status enqueue_forward_states(const gdn_problem *pr, FwdParams &fp, int grid, hipStream_t s);

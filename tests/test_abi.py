@@ -211,8 +211,13 @@ def test_backward_checks(lib, gdn):
         assert _bwd(lib, pr, **{name: MISALIGNED}) == 4, name
     for name in ("dhT", "dh0"):
         assert _bwd(lib, pr, **{name: MISALIGNED}) == 4, name
-    # scalar gate, bf16 io, bf16 saved states only
-    assert _bwd(lib, _problem(gdn, T=300, gate=1)) == 3
+    # the per-key gate's workspace also holds Gamma per key in its slots and
+    # dP, dA per (chunk, head)
+    prk = _problem(gdn, B=2, T=300, H=4, K=128, V=64, chunk=64, gate=1)
+    slot = 8 * 64 * 64 + 64 * 128 * 4 + 64 * 4 + 128 * 4
+    assert lib.gdn_workspace_bytes_backward(ctypes.byref(prk)) == (
+        2 * 300 * 4 * 64 * 4 + 2 * 5 * 4 * 128 * 64 * 4 + 2 * 5 * 4 * slot + 2 * 5 * 4 * 2 * 64 * 64 * 4)
+    # bf16 io and bf16 saved states only
     assert _bwd(lib, _problem(gdn, T=300, io=0, o=0)) == 3
     assert _bwd(lib, _problem(gdn, T=300, o=0)) == 3
     assert _bwd(lib, _problem(gdn, K=96)) == 3

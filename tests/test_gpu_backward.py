@@ -1,6 +1,9 @@
 """GPU parity of gdn_backward (the scalar gate's gradients, through the C ABI)
 against the fp64 oracle.
 
+Both gates: one gate per head (Gated DeltaNet) and one per key dimension
+(KDA), the latter with the decay-weighted sums of its own kernels.
+
 gdn_backward takes the forward's saved chunk-start states and deltas (hck,
 vnew) in bf16, as inputs.  Their rounding alone moves dq and dk by 1-3e-2
 (max |x - ref| / rms(ref)) against the exact gradients, which the oracle
@@ -39,8 +42,12 @@ def _np(t):
     return t.detach().float().cpu().numpy()
 
 
-def _grads_inputs(B, T, H, K, V, h0, dhT, seed, bias=2.0):
-    inp = make_inputs(B, T, H, K, V, io="bf16", gate="head", gate_bias=bias, h0=h0, seed=seed)
+def _grads_inputs(B, T, H, K, V, h0, dhT, seed, bias=2.0, gate="head", recipe=None):
+    if recipe is not None:
+        from test_decay_model import strong_inputs
+        inp = strong_inputs(B, T, H, K, V, gate, recipe, seed, io="bf16", h0=h0)
+    else:
+        inp = make_inputs(B, T, H, K, V, io="bf16", gate=gate, gate_bias=bias, h0=h0, seed=seed)
     gen = torch.Generator().manual_seed(seed + 7)
     do = torch.randn(B, T, H, V, generator=gen).to(torch.bfloat16).contiguous()
     dh = torch.randn(B, H, K, V, generator=gen).contiguous() if dhT else None
@@ -194,6 +201,81 @@ def test_backward_full_size_sampled_heads(name):
     for b, h in heads:
         one = {n: (None if t is None else (t[b:b + 1, h:h + 1] if n == "h0" else t[b:b + 1, :, h:h + 1]))
                for n, t in inp.items()}
+        ref = _oracle_grads(one, do[b:b + 1, :, h:h + 1], dh[b:b + 1, h:h + 1], C,
+                            hck[b:b + 1, :, h:h + 1], vnew[b:b + 1, :, h:h + 1])
+        for nm, x, r in zip(NAMES, got, ref[:6]):
+            xs = x[b:b + 1, h:h + 1] if nm == "dh0" else x[b:b + 1, :, h:h + 1]
+            err = oracle.rel_err(xs, r)
+            print("  head (%d, %d) %s rel err %.3e" % (b, h, nm, err), flush=True)
+            assert err <= TOL, (nm, b, h, err)
+
+
+KEY_CASES = [
+    # B, T, H, K, V, C, h0, dhT, recipe (None: logsigmoid(N(0,1) + 3))
+    (1, 150, 2, 64, 64, 64, True, True, None),
+    (1, 97, 2, 128, 128, 64, True, True, None),
+    (2, 100, 2, 128, 64, 32, False, True, None),
+    (1, 128, 2, 64, 128, 32, True, False, None),
+    (1, 130, 2, 128, 128, 64, True, True, "pin20"),
+    (1, 100, 2, 64, 64, 32, True, True, "bm2"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(KEY_CASES)))
+def test_backward_key_gate_matches_oracle(case):
+    B, T, H, K, V, C, h0, dhT, recipe = KEY_CASES[case]
+    print("backward key case", KEY_CASES[case], flush=True)
+    inp, do, dh = _grads_inputs(B, T, H, K, V, h0, dhT, seed=960 + case, bias=3.0, gate="key", recipe=recipe)
+    hck, vnew = _oracle_states(inp, C)
+    got = _gpu_backward(inp, do, dh, C, hck, vnew)
+    ref = _oracle_grads(inp, do, dh, C, hck, vnew)
+    for name, x, r in zip(NAMES, got, ref[:6]):
+        xv = _np(x)
+        assert np.isfinite(xv).all(), name
+        err = oracle.rel_err(xv, r)
+        print("  %s rel err %.3e" % (name, err), flush=True)
+        assert err <= TOL, (name, err)
+
+
+def test_backward_key_gate_intermediates_and_end_to_end():
+    import ctypes
+    B, T, H, K, V, C = 1, 200, 2, 128, 128, 64
+    inp, do, dh = _grads_inputs(B, T, H, K, V, True, True, seed=981, bias=3.0, gate="key")
+    pr = gdn.Problem(B, T, H, K, V, C, gdn.GDN_BF16, gdn.GDN_BF16, gdn.GDN_GATE_KEY)
+    need = int(gdn.load_library().gdn_workspace_bytes_backward(ctypes.byref(pr)))
+    ws = torch.empty(need, device=_dev(), dtype=torch.uint8)
+    hck, vnew = _oracle_states(inp, C)
+    _gpu_backward(inp, do, dh, C, hck, vnew, workspace=ws)
+    nt = (T + C - 1) // C
+    wsf = ws.view(torch.float32)
+    dR = _np(wsf[:B * T * H * V].view(B, T, H, V))
+    dhe = _np(wsf[B * T * H * V:B * T * H * V + B * nt * H * K * V].view(B, nt, H, K, V))
+    ref = _oracle_grads(inp, do, dh, C, hck, vnew)[6]
+    assert oracle.rel_err(dR, ref["dR"]) <= TOL
+    assert oracle.rel_err(dhe, ref["dhe"]) <= TOL
+    # end to end: the GPU forward's states, against the exact gradients
+    hg, vg = _gpu_forward_states(inp, C)
+    got = _gpu_backward(inp, do, dh, C, hg, vg)
+    exact = oracle.token_backward(_f(inp["q"]), _f(inp["k"]), _f(inp["v"]), _f(inp["beta"]),
+                                  _f(inp["g"]), _f(do), _f(inp["h0"]), _f(dh))
+    rounded = _oracle_grads(inp, do, dh, C, hck, vnew)
+    for name, x, r, o in zip(NAMES, got, exact, rounded[:6]):
+        bar = TOL + oracle.rel_err(o, r)
+        err = oracle.rel_err(_np(x), r)
+        print("  end to end %s rel err %.3e (bar %.3e)" % (name, err, bar), flush=True)
+        assert err <= bar, (name, err, bar)
+
+
+def test_backward_key_gate_full_size_sampled_heads():
+    """kda_t8k's shape (2 x 8192 tokens, 32 heads, per-key gate), states from
+    the oracle for every head, two heads against chunk_backward."""
+    B, T, H, K, V, C = 2, 8192, 32, 128, 128, 64
+    print("backward key full size", flush=True)
+    inp, do, dh = _grads_inputs(B, T, H, K, V, False, True, seed=991, bias=3.0, gate="key")
+    hck, vnew = _oracle_states(inp, C)
+    got = [_np(x) for x in _gpu_backward(inp, do, dh, C, hck, vnew)]
+    for b, h in [(0, 5), (1, 30)]:
+        one = {n: (None if t is None else t[b:b + 1, :, h:h + 1]) for n, t in inp.items()}
         ref = _oracle_grads(one, do[b:b + 1, :, h:h + 1], dh[b:b + 1, h:h + 1], C,
                             hck[b:b + 1, :, h:h + 1], vnew[b:b + 1, :, h:h + 1])
         for nm, x, r in zip(NAMES, got, ref[:6]):
