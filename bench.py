@@ -102,10 +102,12 @@ def chunk_dq_bytes(w, o_dtype):
 
 def backward_bytes(w):
     """Inputs q, k, v, dO (io dtype), beta, g, dhT and the saved bf16 states
-    (hck, vnew) read once; dq, dk, dv, dbeta, dg, dh0 (fp32) written once."""
+    (hck, vnew) read once; dq, dk, dv, dbeta, dg, dh0 (fp32) written once
+    (g and dg per key for the per-key gate)."""
     B, T, H, K, V = w.B, w.T, w.H, w.K, w.V
     nt = (T + w.chunk - 1) // w.chunk
-    per_tok = io_bytes(w.io) * (2 * K + 2 * V) + 8 + 2 * V + 4 * (2 * K + V) + 8
+    gd = K if w.gate == "key" else 1
+    per_tok = io_bytes(w.io) * (2 * K + 2 * V) + 4 + 4 * gd + 2 * V + 4 * (2 * K + V) + 4 + 4 * gd
     return B * T * H * per_tok + 2 * B * nt * H * K * V + 8 * B * H * K * V
 
 
@@ -272,8 +274,8 @@ def main():
             gdn.forward_split(d["q"], d["k"], d["v"], d["beta"], d["g"], w.chunk, t_split, d["h0"],
                               o_dtype=tdt, o=o, hT=hT, workspace=ws_split)
     elif args.backward:
-        if w.gate != "head" or w.io != "bf16":
-            sys.exit("bench: --backward takes scalar-gate bf16 workloads")
+        if w.io != "bf16":
+            sys.exit("bench: --backward takes bf16 workloads")
         tdt = torch.bfloat16
         o_dtype = "bf16"
         gen = torch.Generator().manual_seed(w.seed + 3000)
@@ -282,10 +284,12 @@ def main():
         _, _, hck, vnew = gdn.forward_states(d["q"], d["k"], d["v"], d["beta"], d["g"], w.chunk,
                                              d["h0"], o_dtype=tdt)
         f32 = dict(device=dev, dtype=torch.float32)
+        gsh = (w.B, w.T, w.H, w.K) if w.gate == "key" else (w.B, w.T, w.H)
         grads = dict(dq=torch.empty(w.B, w.T, w.H, w.K, **f32), dk=torch.empty(w.B, w.T, w.H, w.K, **f32),
                      dv=torch.empty(w.B, w.T, w.H, w.V, **f32), dbeta=torch.empty(w.B, w.T, w.H, **f32),
-                     dg=torch.empty(w.B, w.T, w.H, **f32), dh0=torch.empty(w.B, w.H, w.K, w.V, **f32))
-        pr = gdn.Problem(w.B, w.T, w.H, w.K, w.V, w.chunk, gdn.GDN_BF16, gdn.GDN_BF16, gdn.GDN_GATE_HEAD)
+                     dg=torch.empty(*gsh, **f32), dh0=torch.empty(w.B, w.H, w.K, w.V, **f32))
+        pr = gdn.Problem(w.B, w.T, w.H, w.K, w.V, w.chunk, gdn.GDN_BF16, gdn.GDN_BF16,
+                         gdn.GDN_GATE_KEY if w.gate == "key" else gdn.GDN_GATE_HEAD)
         import ctypes
         ws_b = torch.empty(int(gdn.load_library().gdn_workspace_bytes_backward(ctypes.byref(pr))),
                            device=dev, dtype=torch.uint8)
@@ -360,13 +364,19 @@ def main():
     launches = 1
     if args.backward:
         fbytes, fflops = backward_bytes(w), backward_flops(w)
-        launches = 2
-        kname = "bwd_dh_kernel<%d, %d> + bwd_grad_kernel<%d, %d, %d>" % (w.chunk, w.K, w.chunk, w.K, w.V)
+        if w.gate == "key":
+            launches = 4
+            kname = ("bwd_prep_kda_kernel<%d, %d> + bwd_dh_kda_kernel<%d, %d> + bwd_grad_kda_kernel<%d, %d, %d> "
+                     "+ bwd_dec_kda_kernel<%d, %d>" % (w.chunk, w.K, w.chunk, w.K, w.chunk, w.K, w.V, w.chunk, w.K))
+        else:
+            launches = 3
+            kname = "bwd_prep_kernel<%d, %d> + bwd_dh_kernel<%d, %d> + bwd_grad_kernel<%d, %d, %d>" % (
+                w.chunk, w.K, w.chunk, w.K, w.chunk, w.K, w.V)
     if args.split is not None:
         launches = 3
         kname = ("forward_pipe_kernel<%d, %d, %s, false, false, false, true> + split_out_kernel "
                  "+ split_state_kernel" % (w.chunk, w.K, {"bf16": "bf16_t", "fp32": "float"}[o_dtype]))
-    if w.gate == "key" and not args.chunk_dq:
+    if w.gate == "key" and not args.chunk_dq and not args.backward:
         launches = 2
         kname = "kda_gram_kernel<%d, %d, %s%s> + %s" % (
             w.chunk, w.K, {"bf16": "bf16_t", "fp32": "float"}[w.io],

@@ -206,7 +206,8 @@ gdn_status gdn_rescan_dq(const gdn_problem *problem, const void *q, const void *
 
 /*
  * gdn_backward -- the gradients of gdn_forward's outputs with respect to
- * every input, for the scalar gate (Gated DeltaNet) with bf16 io, from what
+ * every input, for either gate (one per head, Gated DeltaNet; one per key
+ * dimension, KDA) with bf16 io, from what
  * gdn_forward_states (or gdn_rescan_dq) saved: the kernel_fun KDA re-scan
  * page has its re-scan keep the h checkpoints and v_new for the backward's
  * later stage (bwd_scan.py module docstring); this is that stage, with the
@@ -217,9 +218,10 @@ gdn_status gdn_rescan_dq(const gdn_problem *problem, const void *q, const void *
  *   hck, vnew             bf16, as gdn_forward_states writes them for the
  *                         same inputs and chunk (problem->o_dtype must be
  *                         GDN_BF16: they are read in that dtype)
- *   dq, dk [B,T,H,K], dv [B,T,H,V], dbeta, dg [B,T,H]   fp32, written in full
+ *   dq, dk [B,T,H,K], dv [B,T,H,V], dbeta [B,T,H], dg (g's shape: [B,T,H]
+ *        or [B,T,H,K])   fp32, written in full
  *   dh0  [B,H,K,V] fp32   h0's gradient, or NULL (not written)
- * Three launches on the stream: one workgroup per (chunk, head) forms each
+ * Scalar gate: three launches on the stream: one workgroup per (chunk, head) forms each
  * chunk's factors of the reverse scan (the decayed Gram products, T^T and
  * P^T, the row factors); the reverse scan (one workgroup per (batch, head,
  * 64-wide V tile), serial over chunks) writes dR (v's gradient before the
@@ -227,11 +229,14 @@ gdn_status gdn_rescan_dq(const gdn_problem *problem, const void *q, const void *
  * workspace, and dv and dh0; then one workgroup per (chunk, head) forms dq,
  * dk, dbeta and dg.  Workspace: gdn_workspace_bytes_backward(problem)
  * bytes, 16-byte aligned: dR [B,T,H,V] fp32, then the chunk-end gradients
- * [B,NT,H,K,V] fp32, then the per-chunk factors.  Results are
- * deterministic (no atomics).  Outputs must
+ * [B,NT,H,K,V] fp32, then the per-chunk factors.  The per-key gate adds a
+ * fourth launch for its decay-weighted sums (the decay of every pair of
+ * tokens is per key, inside the C x C x K sums), and its workspace also
+ * holds dP and dA per (chunk, head).  Results are deterministic (no
+ * atomics).  Outputs must
  * not alias inputs or each other.  With T = 0 only dh0 is written (= dhT or
- * zero).  GDN_ERR_UNSUPPORTED for the per-key gate, fp32 io, an fp32
- * o_dtype, or a stream whose fp32 rows exceed 4 GiB.
+ * zero).  GDN_ERR_UNSUPPORTED for fp32 io, an fp32 o_dtype, or a stream
+ * whose fp32 rows exceed 4 GiB.
  */
 gdn_status gdn_backward(const gdn_problem *problem, const void *q, const void *k, const void *v,
                         const float *beta, const float *g, const void *dout, const float *dhT,
@@ -241,7 +246,8 @@ gdn_status gdn_backward(const gdn_problem *problem, const void *q, const void *k
 
 /* Workspace gdn_backward needs: B T H V 4 + B NT H K V 4 bytes (NT =
  * ceil(T / chunk)) + B NT H slot bytes, a slot being 8 C^2 + 16 C + 16
- * bytes; 0 on bad arguments. */
+ * bytes (per-key gate: 8 C^2 + 4 C K + 4 C + 4 K, plus 8 C^2 more per
+ * (chunk, head) for dP and dA); 0 on bad arguments. */
 size_t gdn_workspace_bytes_backward(const gdn_problem *problem);
 
 /*
