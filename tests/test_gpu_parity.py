@@ -446,3 +446,60 @@ def test_forward_at_the_32bit_stream_limit():
         assert rh <= TOL["bf16"]
     del q, k, v, o
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# inputs off the unit sphere: the documented range of the fp16 operands
+# ---------------------------------------------------------------------------
+
+def _off_sphere(B, T, H, K, V, gate, seed):
+    """q unnormalised (N(0, 1.5^2) entries, up to ~7), every k of norm 1.3
+    with one dominant entry of magnitude ~1.23 (beyond 1), 2 % of the q and
+    k entries shrunk by 1e-6 (below fp16's smallest normal, 2^-14), v of
+    scale 3 and h0 of scale 1.  beta < 1 keeps beta |k|^2 < 1.69, so every
+    step's (I - beta k k^T) stays a contraction-or-reflection with spectrum
+    in (-0.69, 1]: the state stays bounded."""
+    inp = make_inputs(B, T, H, K, V, io="bf16", gate=gate, gate_bias=2.0 if gate == "head" else 3.0,
+                      h0=True, seed=seed)
+    gen = torch.Generator().manual_seed(seed + 1000)
+    q = 1.5 * torch.randn(B, T, H, K, generator=gen)
+    k = 0.03 * torch.randn(B, T, H, K, generator=gen)
+    j = torch.randint(0, K, (B, T, H, 1), generator=gen)
+    k.scatter_(-1, j, torch.where(torch.rand(B, T, H, 1, generator=gen) < 0.5, -1.0, 1.0))
+    k = 1.3 * k / k.norm(dim=-1, keepdim=True)
+    tq = torch.rand(B, T, H, K, generator=gen) < 0.02
+    tk = torch.rand(B, T, H, K, generator=gen) < 0.02
+    q = torch.where(tq, q * 1e-6, q)
+    k = torch.where(tk, k * 1e-6, k)
+    inp["q"] = q.to(torch.bfloat16).contiguous()
+    inp["k"] = k.to(torch.bfloat16).contiguous()
+    inp["v"] = (3.0 * inp["v"].float()).to(torch.bfloat16).contiguous()
+    inp["h0"] = 10.0 * inp["h0"]
+    return inp
+
+
+@pytest.mark.parametrize("gate,K,V,C", [("head", 128, 128, 64), ("head", 64, 64, 32),
+                                        ("key", 128, 128, 64), ("key", 64, 128, 32)])
+def test_inputs_off_the_unit_sphere(gate, K, V, C):
+    """The bf16 path converts q and k to fp16 operands; the header promises
+    exact conversion for magnitudes in [2^-14, 65504] and only rounding below.
+    Unnormalised q, keys with entries beyond 1 and entries below fp16's
+    normal range meet the same bar as the standard inputs."""
+    B, T, H = 2, 3 * C + 29, 2
+    inp = _off_sphere(B, T, H, K, V, gate, seed=61 + K + C)
+    qf, kf = inp["q"].float(), inp["k"].float()
+    assert qf.abs().max() > 4.0 and kf.abs().max() > 1.1
+    small = (kf != 0) & (kf.abs() < 2.0 ** -14)
+    assert small.any() and ((qf != 0) & (qf.abs() < 2.0 ** -14)).any()
+    d = _cuda(inp)
+    o_ref, h_ref = oracle.token_recurrence(qf.numpy(), kf.numpy(), inp["v"].float().numpy(),
+                                           inp["beta"].numpy(), inp["g"].numpy(), inp["h0"].numpy())
+    assert np.isfinite(o_ref).all() and np.abs(h_ref).max() < 1e3
+    for od, tdt in (("fp32", torch.float32), ("bf16", torch.bfloat16)):
+        o, hT = gdn.forward(d["q"], d["k"], d["v"], d["beta"], d["g"], C, d["h0"], o_dtype=tdt)
+        torch.cuda.synchronize()
+        case = "off_sphere_%s_K%dV%dC%d_%s" % (gate, K, V, C, od)
+        ro = check_o(_np(o), o_ref, "bf16", case, od)
+        rh = oracle.rel_err(_np(hT), h_ref)
+        _record(case, o_rel=ro, hT_rel=rh)
+        assert rh <= TOL["bf16"], "%s: hT rel err %.3e" % (case, rh)
