@@ -225,6 +225,20 @@ def _chunks(T, C):
         yield s, min(s + C, T)
 
 
+def _pair_decay(gam):
+    """exp(gam_r - gam_s) for every pair of rows of a chunk (gam [n] or
+    [n, K]), with the exponent of the pairs s > r set to 0: those entries are
+    always masked out (tril), and their growth factor would otherwise
+    overflow to inf under strong decays (inf * 0 is NaN inside a product).
+    The pairs s <= r are the plain exponential, for either sign of g."""
+    n = gam.shape[0]
+    d = gam[:, None] - gam[None, :]
+    keep = (np.arange(n)[:, None] >= np.arange(n)[None, :])
+    if d.ndim == 3:
+        keep = keep[:, :, None]
+    return np.exp(np.where(keep, d, 0.0))
+
+
 def chunk_prepare(k, v, beta, g, chunk):
     """WY factors per chunk, fp64.  Returns ``(gcum, w, u)``.
 
@@ -263,11 +277,11 @@ def chunk_prepare(k, v, beta, g, chunk):
                 gcum[b, s:e, h] = gam
                 if per_key:
                     # A[r,s] = beta_r sum_d k_rd k_sd exp(gam_rd - gam_sd)
-                    dec = np.exp(gam[:, None, :] - gam[None, :, :])   # [n,n,K]
+                    dec = _pair_decay(gam)                        # [n,n,K]
                     G = np.einsum("rd,sd,rsd->rs", kc, kc, dec)
                     ke = kc * np.exp(gam)
                 else:
-                    G = (kc @ kc.T) * np.exp(gam[:, None] - gam[None, :])
+                    G = (kc @ kc.T) * _pair_decay(gam)
                     ke = kc * np.exp(gam)[:, None]
                 A = np.tril(bc[:, None] * G, -1)
                 Tm = np.linalg.inv(np.eye(n) + A)
@@ -316,13 +330,13 @@ def chunk_scan(q, k, w, u, gcum, chunk, h0=None, states=False):
                     hck[b, s // chunk, hh] = S
                     vnew[b, s:e, hh] = vp
                 if per_key:
-                    dec = np.exp(gam[:, None, :] - gam[None, :, :])
+                    dec = _pair_decay(gam)
                     P = np.einsum("rd,sd,rsd->rs", qc, kc, dec)
                     qd = qc * np.exp(gam)
                     kg = kc * np.exp(gam[-1][None, :] - gam)
                     last = np.exp(gam[-1])[:, None]
                 else:
-                    P = (qc @ kc.T) * np.exp(gam[:, None] - gam[None, :])
+                    P = (qc @ kc.T) * _pair_decay(gam)
                     qd = qc * np.exp(gam)[:, None]
                     kg = kc * np.exp(gam[-1] - gam)[:, None]
                     last = np.exp(gam[-1])
@@ -399,10 +413,9 @@ def chunk_backward(q, k, v, beta, g, do, chunk, h0=None, dhT=None, hck=None, vne
                 bc = beta[b, s:e, hh]
                 gc = g[b, s:e, hh]
                 gam = np.cumsum(gc if per_key else np.repeat(gc[:, None], K, 1), axis=0)   # [n,K]
-                # E_rsd for s <= r (exponent <= 0); the entries s > r are only ever
-                # multiplied by masked-out zeros, so their exponent is clipped at 0
-                # to keep inf * 0 out of the masks under strong decays
-                E = np.exp(np.minimum(gam[:, None, :] - gam[None, :, :], 0.0))         # [n,n,K]
+                # E_rsd (the entries s > r are only ever multiplied by masked-out
+                # zeros; _pair_decay keeps them finite)
+                E = _pair_decay(gam)                                                  # [n,n,K]
                 lower = np.tril(np.ones((n, n)), -1)
                 A = lower * bc[:, None] * np.einsum("rd,sd,rsd->rs", kc, kc, E)
                 P = np.tril(np.einsum("rd,sd,rsd->rs", qc, kc, E))
