@@ -29,10 +29,14 @@ import threading
 __all__ = ["prepare", "scan", "forward", "forward_states", "forward_varlen", "rescan_dq",
            "workspace_bytes", "wait_timeouts",
            "load_library",
-           "GdnError", "LIB_PATH", "STATUS"]
+           "GdnError", "LIB_PATH", "POISON_LIB_PATH", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
+# the debug build (build.py, poison=True): the same entry points, with every
+# pipelined kernel filling its LDS stages with NaN once their last reader is
+# done, so that a read that runs ahead of its write shows up as NaN
+POISON_LIB_PATH = os.path.join(_HERE, "libgdn_poison.so")
 
 GDN_F32, GDN_BF16 = 0, 1
 GDN_GATE_HEAD, GDN_GATE_KEY = 0, 1
@@ -267,10 +271,12 @@ def _workspace(lib, pr, device, workspace, n_seqs=0):
 
 
 def forward(q, k, v, beta, g, chunk, h0=None, *, o_dtype=None, o=None, hT=None,
-            output_final_state=True, workspace=None, stream=None):
-    """Whole forward pass: returns (o [B,T,H,V], hT [B,H,K,V] fp32 or None)."""
+            output_final_state=True, workspace=None, stream=None, library=None):
+    """Whole forward pass: returns (o [B,T,H,V], hT [B,H,K,V] fp32 or None).
+    ``library``: a library from load_library(path) to call instead of
+    libgdn.so (the debug build at POISON_LIB_PATH)."""
     return _forward(q, k, v, beta, g, chunk, h0, o_dtype, o, hT, output_final_state,
-                    workspace, stream, noalloc=False)
+                    workspace, stream, noalloc=False, library=library)
 
 
 def forward_noalloc(q, k, v, beta, g, chunk, h0=None, *, o=None, hT=None, stream=None):
@@ -286,9 +292,9 @@ def forward_noalloc(q, k, v, beta, g, chunk, h0=None, *, o=None, hT=None, stream
 
 
 def _forward(q, k, v, beta, g, chunk, h0, o_dtype, o, hT, output_final_state, workspace,
-             stream, noalloc):
+             stream, noalloc, library=None):
     torch = _torch()
-    lib = load_library()
+    lib = library or load_library()
     B, T, H, K = q.shape
     V = v.shape[-1]
     per_key = _gate_kind(g, B, T, H, K)
@@ -359,12 +365,14 @@ def forward_split(q, k, v, beta, g, chunk, t_split, h0=None, *, o_dtype=None, o=
 
 
 def forward_states(q, k, v, beta, g, chunk, h0=None, *, o_dtype=None, o=None, hT=None,
-                   hck=None, vnew=None, output_final_state=True, workspace=None, stream=None):
+                   hck=None, vnew=None, output_final_state=True, workspace=None, stream=None,
+                   library=None):
     """Forward pass that also saves the chunk-start states and the per-token
     deltas: returns (o, hT or None, hck [B,NT,H,K,V], vnew [B,T,H,V]), with
-    hck and vnew in the o dtype and NT = ceil(T / chunk)."""
+    hck and vnew in the o dtype and NT = ceil(T / chunk).  ``library`` as
+    for forward."""
     torch = _torch()
-    lib = load_library()
+    lib = library or load_library()
     B, T, H, K = q.shape
     V = v.shape[-1]
     per_key = _gate_kind(g, B, T, H, K)
@@ -405,13 +413,13 @@ def forward_states(q, k, v, beta, g, chunk, h0=None, *, o_dtype=None, o=None, hT
 
 
 def forward_varlen(q, k, v, beta, g, cu_seqlens, chunk, h0=None, *, o_dtype=None, o=None,
-                   hT=None, output_final_state=True, workspace=None, stream=None):
+                   hT=None, output_final_state=True, workspace=None, stream=None, library=None):
     """Forward pass over packed sequences: q, k [1,T,H,K], v [1,T,H,V], beta
     [1,T,H], g [1,T,H] or [1,T,H,K]; cu_seqlens an int32 device tensor of
     N + 1 token offsets; h0 [N,H,K,V] fp32 or None.  Returns (o [1,T,H,V],
-    hT [N,H,K,V] or None)."""
+    hT [N,H,K,V] or None).  ``library`` as for forward."""
     torch = _torch()
-    lib = load_library()
+    lib = library or load_library()
     B, T, H, K = q.shape
     V = v.shape[-1]
     if B != 1:

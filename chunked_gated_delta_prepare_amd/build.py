@@ -16,6 +16,9 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
+# the debug build: every pipelined kernel fills its LDS stages with NaN once
+# their last reader is done (GDN_POISON_LDS); same ABI, same entry points
+POISON_LIB = os.path.join(HERE, "libgdn_poison.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -63,9 +66,12 @@ def _run(cmd, verbose):
     return bad, res.stdout + res.stderr
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every HIP source into libgdn.so; returns the library path."""
-    tag = ".tmp%d" % os.getpid()
+def build(verbose: bool = False, extra_flags=None, poison: bool = False) -> str:
+    """Compile every HIP source into libgdn.so (or, with poison, the debug
+    library libgdn_poison.so); returns the library path."""
+    tag = ".tmp%d%s" % (os.getpid(), "p" if poison else "")
+    out = POISON_LIB if poison else LIB
+    extra_flags = list(extra_flags or []) + (["-DGDN_POISON_LDS=1"] if poison else [])
     objs, jobs = [], []
     for unit, flags in UNITS.items():
         obj = os.path.join(CSRC, unit.replace(".hip", ".o") + tag)
@@ -79,7 +85,7 @@ def build(verbose: bool = False, extra_flags=None) -> str:
             if bad:
                 sys.stderr.write(log[-8000:])
                 raise RuntimeError("hipcc failed: %s" % " ".join(cmd[-3:]))
-        tmp = LIB + tag
+        tmp = out + tag
         bad, log = _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs,
                         verbose)
         if bad:
@@ -87,13 +93,20 @@ def build(verbose: bool = False, extra_flags=None) -> str:
             raise RuntimeError("hipcc failed linking libgdn.so")
         # every kernel symbol must resolve (RTLD_NOW fails on any missing one)
         ctypes.CDLL(tmp, mode=os.RTLD_NOW)
-        os.replace(tmp, LIB)
+        os.replace(tmp, out)
     finally:
-        for p in objs + [LIB + tag]:
+        for p in objs + [out + tag]:
             if os.path.exists(p):
                 os.remove(p)
-    return LIB
+    return out
+
+
+def build_all(verbose: bool = False) -> None:
+    """Both libraries: libgdn.so and the debug libgdn_poison.so."""
+    build(verbose=verbose)
+    build(verbose=verbose, poison=True)
 
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build(verbose=True, poison=True))

@@ -3,7 +3,10 @@
 // the caller's stream and returns; nothing allocates or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <cxxabi.h>
+
 #include <algorithm>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -14,6 +17,9 @@
 #include "gdn_scan.h"
 
 namespace gdn {
+
+bool tracing();      // GDN_TRACE (below, beside launch_kernel)
+
 namespace {
 
 constexpr int kBV = 64;            // V tile per scan workgroup
@@ -57,6 +63,24 @@ gdn_status check_workspace(const gdn_problem *pr, int64_t n_seqs, const void *ws
     if (!ws || ws_bytes < (size_t)need) return GDN_ERR_WORKSPACE;
     if (!aligned16(ws)) return GDN_ERR_ALIGNMENT;
     return GDN_OK;
+}
+
+// check_problem, and with GDN_TRACE the entry point and its problem
+gdn_status check_and_trace(const char *entry, const gdn_problem *pr) {
+    const gdn_status st = check_problem(pr);
+    if (tracing()) {
+        if (pr)
+            std::fprintf(stderr,
+                         "gdn_trace %s: B=%lld T=%lld H=%lld K=%lld V=%lld chunk=%d io=%s o=%s gate=%s"
+                         " V tiles=%lld status=%d\n",
+                         entry, (long long)pr->B, (long long)pr->T, (long long)pr->H, (long long)pr->K,
+                         (long long)pr->V, pr->chunk, pr->io_dtype == GDN_BF16 ? "bf16" : "fp32",
+                         pr->o_dtype == GDN_BF16 ? "bf16" : "fp32", pr->gate == GDN_GATE_KEY ? "key" : "head",
+                         (long long)((pr->V + kBV - 1) / kBV), (int)st);
+        else
+            std::fprintf(stderr, "gdn_trace %s: no problem\n", entry);
+    }
+    return st;
 }
 
 gdn_status launch(const void *fn, int grid, void *params, size_t psize, hipStream_t s) {
@@ -220,8 +244,34 @@ void wait_params(unsigned &limit, unsigned &bias) {
     bias = force ? (1u << 30) : 0u;
 }
 
+// GDN_TRACE (environment, read at every call; unset, empty or "0" is off)
+// prints each entry point's problem and each launch's plan to stderr: the
+// kernel instance, grid, workgroup size, static LDS bytes, registers per
+// lane and scratch bytes per lane as the runtime reports them.
+bool tracing() {
+    const char *e = std::getenv("GDN_TRACE");
+    return e && *e && std::strcmp(e, "0") != 0;
+}
+
+void trace_launch(const void *fn, int grid, int threads, hipStream_t s) {
+    hipFuncAttributes a;
+    std::memset(&a, 0, sizeof(a));
+    const bool have = hipFuncGetAttributes(&a, fn) == hipSuccess;
+    const char *raw = hipKernelNameRefByPtr(fn, s);
+    int dst = -1;
+    char *nice = raw ? abi::__cxa_demangle(raw, nullptr, nullptr, &dst) : nullptr;
+    std::fprintf(stderr, "gdn_trace   launch %s grid=%d block=%d", nice ? nice : (raw ? raw : "?"), grid,
+                 threads);
+    if (have)
+        std::fprintf(stderr, " lds=%zu regs=%d scratch=%zu\n", a.sharedSizeBytes, a.numRegs, a.localSizeBytes);
+    else
+        std::fprintf(stderr, " (attributes unavailable)\n");
+    std::free(nice);
+}
+
 gdn_status launch_kernel(const void *fn, int grid, void *params, hipStream_t s, int threads) {
     if (grid <= 0) return GDN_OK;
+    if (tracing()) trace_launch(fn, grid, threads, s);
     void *args[] = {params};
     hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, s);
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
@@ -236,7 +286,7 @@ extern "C" {
 gdn_status gdn_prepare(const gdn_problem *problem, const void *k, const void *v,
                        const float *beta, const float *g, float *w, float *u,
                        float *gcum, void *stream) {
-    gdn_status st = check_problem(problem);
+    gdn_status st = check_and_trace("gdn_prepare", problem);
     if (st != GDN_OK) return st;
     if (problem->T == 0) return GDN_OK;
     st = check_ptrs({k, v, beta, g, w, u, gcum}, {});
@@ -247,7 +297,7 @@ gdn_status gdn_prepare(const gdn_problem *problem, const void *k, const void *v,
 gdn_status gdn_scan(const gdn_problem *problem, const void *q, const void *k,
                     const float *w, const float *u, const float *gcum,
                     const float *h0, void *o, float *hT, void *stream) {
-    gdn_status st = check_problem(problem);
+    gdn_status st = check_and_trace("gdn_scan", problem);
     if (st != GDN_OK) return st;
     if (problem->T == 0) {
         st = check_ptrs({}, {h0, hT});
@@ -274,7 +324,7 @@ gdn_status gdn_forward(const gdn_problem *problem, const void *q, const void *k,
                        const void *v, const float *beta, const float *g,
                        const float *h0, void *o, float *hT, void *workspace,
                        size_t workspace_bytes, void *stream) {
-    gdn_status st = check_problem(problem);
+    gdn_status st = check_and_trace("gdn_forward", problem);
     if (st != GDN_OK) return st;
     if (problem->T == 0) {
         st = check_ptrs({}, {h0, hT});
@@ -293,7 +343,7 @@ gdn_status gdn_forward(const gdn_problem *problem, const void *q, const void *k,
 gdn_status gdn_forward_noalloc(const gdn_problem *problem, const void *q, const void *k,
                                const void *v, const float *beta, const float *g,
                                const float *h0, void *o, float *hT, void *stream) {
-    gdn_status st = check_problem(problem);
+    gdn_status st = check_and_trace("gdn_forward_noalloc", problem);
     if (st != GDN_OK) return st;
     if (problem->T == 0) {
         st = check_ptrs({}, {h0, hT});
@@ -337,7 +387,7 @@ gdn_status gdn_forward_split(const gdn_problem *problem, int64_t t_split, const 
                              const void *k, const void *v, const float *beta, const float *g,
                              const float *h0, void *o, float *hT, void *workspace,
                              size_t workspace_bytes, void *stream) {
-    gdn_status st = check_problem(problem);
+    gdn_status st = check_and_trace("gdn_forward_split", problem);
     if (st != GDN_OK) return st;
     st = check_split(problem, t_split);
     if (st != GDN_OK) return st;
@@ -352,7 +402,7 @@ gdn_status gdn_forward_states(const gdn_problem *problem, const void *q, const v
                               const void *v, const float *beta, const float *g,
                               const float *h0, void *o, float *hT, void *hck, void *vnew,
                               void *workspace, size_t workspace_bytes, void *stream) {
-    gdn_status st = check_problem(problem);
+    gdn_status st = check_and_trace("gdn_forward_states", problem);
     if (st != GDN_OK) return st;
     if (problem->T == 0) {
         // no chunk, so no checkpoint and no token: only hT = h0 (or zero)
@@ -374,7 +424,7 @@ gdn_status gdn_rescan_dq(const gdn_problem *problem, const void *q, const void *
                          const void *v, const float *beta, const float *g, const float *h0,
                          const void *dout, float *hT, void *hck, void *vnew, float *dq,
                          void *workspace, size_t workspace_bytes, void *stream) {
-    gdn_status st = check_problem(problem);
+    gdn_status st = check_and_trace("gdn_rescan_dq", problem);
     if (st != GDN_OK) return st;
     if (problem->io_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
     if (problem->gate == GDN_GATE_KEY && problem->chunk != 64) return GDN_ERR_UNSUPPORTED;
@@ -395,7 +445,7 @@ gdn_status gdn_rescan_dq(const gdn_problem *problem, const void *q, const void *
 
 gdn_status gdn_chunk_dq(const gdn_problem *problem, const void *dout, const void *hck, float *dq,
                         void *stream) {
-    gdn_status st = check_problem(problem);
+    gdn_status st = check_and_trace("gdn_chunk_dq", problem);
     if (st != GDN_OK) return st;
     if (problem->io_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
     if (problem->T == 0) return GDN_OK;
@@ -411,7 +461,7 @@ gdn_status gdn_forward_varlen(const gdn_problem *problem, const int32_t *cu_seql
                               int64_t n_seqs, const void *q, const void *k, const void *v,
                               const float *beta, const float *g, const float *h0, void *o,
                               float *hT, void *workspace, size_t workspace_bytes, void *stream) {
-    gdn_status st = check_problem(problem);
+    gdn_status st = check_and_trace("gdn_forward_varlen", problem);
     if (st != GDN_OK) return st;
     if (problem->B != 1 || n_seqs < 1 || n_seqs * problem->H > (1 << 24)) return GDN_ERR_BAD_SHAPE;
     if (!cu_seqlens) return GDN_ERR_NULL_ARG;
@@ -441,7 +491,7 @@ gdn_status gdn_backward(const gdn_problem *problem, const void *q, const void *k
                         const void *hck, const void *vnew, float *dq, float *dk, float *dv,
                         float *dbeta, float *dg, float *dh0, void *workspace,
                         size_t workspace_bytes, void *stream) {
-    gdn_status st = check_problem(problem);
+    gdn_status st = check_and_trace("gdn_backward", problem);
     if (st != GDN_OK) return st;
     if (problem->io_dtype != GDN_BF16 || problem->o_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
     // per-stream 32-bit byte offsets: fp32 [T, H, K | V] rows and one head's K x V block

@@ -69,6 +69,32 @@ __device__ __forceinline__ int pcol(int col) {
     return (col & ~31) | (slot << 2) | (col & 3);
 }
 
+// Debug builds (GDN_POISON_LDS=1, the library libgdn_poison.so) fill each LDS
+// stage of the pipelined kernels with NaN once its last reader is done with
+// it, so that a read which runs ahead of the write it should wait for gets
+// NaN instead of the previous chunk's values.  All-ones bits are a NaN in
+// fp16, bf16 and fp32 alike.  Production builds contain none of this code.
+#ifndef GDN_POISON_LDS
+#define GDN_POISON_LDS 0
+#endif
+constexpr bool kPoisonLds = GDN_POISON_LDS != 0;
+
+// bytes (a multiple of 16) from a 16-byte aligned p, by threads t of n
+__device__ __forceinline__ void poison_fill(const void *p, int bytes, int t, int n) {
+    for (int i = t; i < bytes / 16; i += n) ((u32x4 *)p)[i] = u32x4{~0u, ~0u, ~0u, ~0u};
+}
+
+// The 16 x 16 blocks (I, J <= I) of a swizzled, column-permuted C x C tile:
+// the blocks that the prepare rewrites every chunk (those above stay zero).
+template <int C>
+__device__ __forceinline__ void poison_lower(const _Float16 *S, int t, int n) {
+    constexpr int NB = C / 16;
+    for (int i = t; i < NB * NB * 64; i += n) {
+        const int blk = i / 64, I = blk / NB, J = blk % NB, r = (i % 64) / 4, cg = i % 4;
+        if (J <= I) *(u32x2 *)(S + swz<C>(16 * I + r, pcol(16 * J + 4 * cg))) = u32x2{~0u, ~0u};
+    }
+}
+
 // Lane (q, i): row r0 + i, stored columns k0 + 8q .. +7 (one 16-byte read).
 // On a permuted tile this is the split-slot A fragment of logical columns
 // k0 .. k0+31.
@@ -664,6 +690,17 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                 for (int s = 0; s < C / 32; ++s)
                     M::mma(hacc[i], fragAT_split_p<K>(Ks, 16 * i, 32 * s), df[s]);
             }
+            if constexpr (kPoisonLds) {
+                // every chain wave is past its reads of this slot, which the
+                // prepare rewrites for chunk c + 2
+                prep_barrier(sync_ctr + 2, chain_target, wc);
+                poison_fill(Qs, C * K * 2, tid, 256);
+                poison_fill(Ks, C * K * 2, tid, 256);
+                poison_fill(Vs, C * 64 * 2, tid, 256);
+                poison_fill(eg, L::kRowCN * 4, tid, 256);
+                poison_lower<C>(Tmb, tid, 256);
+                poison_lower<C>(Ps, tid, 256);
+            }
             // (chain wave 0 has the gate and beta of chunk c + 2 in flight:
             // they are taken into registers here, where the wait counts the
             // o stores issued since, so the next chunk's factor scan does not
@@ -915,6 +952,15 @@ __global__ __launch_bounds__(kPipeThreads, 1) void forward_pipe_kernel(FwdParams
                 prep_barrier(sync_ctr, sync_target, wc);
                 const int i = 2 + (pw >> 1);
                 put_mn(i, pw & 1, *(const half8 *)(Asp + pw * 512 + 8 * l), *(const half4 *)(Tr + i * 256 + 4 * l));
+            }
+            if constexpr (kPoisonLds) {
+                // every prepare wave is past its reads of the row factors
+                // (rewritten for chunk n + 1 by chain wave 0), the split A
+                // blocks and the fp16 T_bb
+                prep_barrier(sync_ctr, sync_target, wc);
+                poison_fill(bet, (3 + NB) * C * 4, pt, 256);
+                poison_fill(Asp, L::NASP * 1024, pt, 256);
+                poison_fill(Tr, NB * 512, pt, 256);
             }
         };
 

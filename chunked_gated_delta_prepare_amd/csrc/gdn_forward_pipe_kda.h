@@ -301,6 +301,18 @@ __global__ __launch_bounds__((kda_threads<C, K, DQ>()), 1) void forward_pipe_kda
             // them, and the prepare writes this slot only after the barrier
             if constexpr (DQ)
                 if (c + 1 < nt) rescan_dq(c + 1, slot);
+            if constexpr (kPoisonLds) {
+                // every chain wave is past its reads of this slot, which the
+                // prepare rewrites for chunk c + 2
+                prep_barrier(sync_ctr + 2, chain_target, wc);
+                poison_fill(Qs, C * K * 2, tid, 256);
+                poison_fill(Ks, C * K * 2, tid, 256);
+                poison_fill(Hs, C * K * 2, tid, 256);
+                poison_fill(Tmb, C * C * 2, tid, 256);
+                poison_fill(Ps, C * C * 2, tid, 256);
+                poison_fill(Vs, C * 64 * 2, tid, 256);
+                poison_fill(flv, K * 4, tid, 256);
+            }
             wg_barrier();
         }
         if (p.hT) {

@@ -47,6 +47,18 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), name
 
 
+def test_debug_build_exports_the_same_boundary(gdn):
+    """libgdn_poison.so (LDS stages filled with NaN on release) is a drop-in
+    for libgdn.so: same symbols, same ABI version."""
+    if not os.path.exists(gdn.POISON_LIB_PATH):
+        from chunked_gated_delta_prepare_amd import build
+        build.build(poison=True)
+    dbg = gdn.load_library(gdn.POISON_LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(dbg, name), name
+    assert dbg.gdn_abi_version() == gdn.ABI_VERSION
+
+
 def test_binding_exports_match_header(gdn):
     assert sorted(gdn.EXPORTS) == _declared_functions()
 

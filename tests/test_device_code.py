@@ -1,7 +1,7 @@
-"""Host-only checks of the gfx950 code objects inside libgdn.so (built here
-from this repository's sources): every kernel the dispatch can launch is
-present, no kernel uses scratch memory, and no vector-memory store writes
-more than 8 bytes per lane.
+"""Host-only checks of the gfx950 code objects inside libgdn.so and its debug
+build libgdn_poison.so (both built here from this repository's sources):
+every kernel the dispatch can launch is present, no kernel uses scratch
+memory, and no vector-memory store writes more than 8 bytes per lane.
 
 Scratch: a register array indexed with a run-time value is moved to
 per-lane scratch memory, which silently costs a large factor in speed; the
@@ -31,17 +31,19 @@ def _tool(name):
     return path
 
 
-@pytest.fixture(scope="module")
-def disassembly(tmp_path_factory):
+@pytest.fixture(scope="module", params=["libgdn", "libgdn_poison"])
+def disassembly(tmp_path_factory, request):
     import chunked_gated_delta_prepare_amd as gdn
-    if not os.path.exists(gdn.LIB_PATH):
+    poison = request.param == "libgdn_poison"
+    path = gdn.POISON_LIB_PATH if poison else gdn.LIB_PATH
+    if not os.path.exists(path):
         from chunked_gated_delta_prepare_amd import build
-        build.build()
+        build.build(poison=poison)
     objcopy, bundler, objdump, readelf = (_tool("llvm-objcopy"), _tool("clang-offload-bundler"),
                                           _tool("llvm-objdump"), _tool("llvm-readelf"))
     d = tmp_path_factory.mktemp("co")
     fat = d / "fatbin.bin"
-    subprocess.run([objcopy, "--dump-section", ".hip_fatbin=%s" % fat, gdn.LIB_PATH], check=True)
+    subprocess.run([objcopy, "--dump-section", ".hip_fatbin=%s" % fat, path], check=True)
     data = fat.read_bytes()
     # one offload bundle per translation unit, concatenated in the section
     starts = [m.start() for m in re.finditer(re.escape(MAGIC), data)]
