@@ -50,6 +50,17 @@
  * GDN_ERR_HIP; faults during execution surface at the caller's next
  * synchronisation.  No C++ exception crosses this interface.
  *
+ * Diagnostics: with the environment variable GDN_TRACE set (to anything but
+ * "" or "0"; read at every call) each entry point that takes a problem
+ * prints it and its validation status to stderr, and each kernel launch
+ * prints its plan: the kernel instance, grid, workgroup size, static LDS
+ * bytes, registers and scratch bytes per lane.  libgdn_poison.so, built
+ * beside libgdn.so from the same sources, exports this same interface; its
+ * pipelined kernels fill each LDS stage with NaN once its last reader is
+ * done with it, so that a read that overtakes the write it must wait for
+ * shows up as NaN.  With every wait in place it returns exactly libgdn.so's
+ * results, more slowly.
+ *
  * Requirements: all pointers 16-byte aligned; K, V in {64, 128}; chunk in
  * {32, 64}; B, H >= 1; T >= 0 (any T: a short last chunk is exact).  Shapes
  * outside this set return GDN_ERR_UNSUPPORTED; there is no fallback path.
