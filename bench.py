@@ -4,7 +4,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one gdn_forward call over one batch of synthetic input already in
-HBM (q, k, v, beta, g, h0 -> o, hT); by default the long-context workload
+HBM (q, k, v, beta, g, h0 -> o, hT), with the workspace gdn_workspace_bytes
+asks for (there gdn_forward cuts long streams in two where that fills idle
+compute units: gdn_forward_split_point); by default the long-context workload
 gdn_t64k (1 x 65536 tokens, 64 heads, dk = dv = 128), the largest that the
 five workloads put on one GPU.  Each timed step is bracketed by its own HIP
 events on the library's stream; between steps (outside those brackets) a
@@ -56,6 +58,9 @@ def parse():
     ap.add_argument("--split", type=float, default=None,
                     help="run gdn_forward_split with the cut at this fraction of T (rounded to "
                          "whole chunks): the scalar gate's two-segment forward")
+    ap.add_argument("--no-split", action="store_true",
+                    help="make gdn_forward run its single pass where it would split the "
+                         "sequence (GDN_FORWARD_NO_SPLIT=1)")
     ap.add_argument("--backward", action="store_true",
                     help="time gdn_backward (the scalar gate's gradients from saved bf16 states; "
                          "the states come from one untimed gdn_forward_states call)")
@@ -140,6 +145,14 @@ def kernel_name(w, o_dtype, states=False, rescan=False):
                                                      "true" if w.gate == "key" else "false", st)
 
 
+def split_kernel_names(w, o_dtype):
+    """The three launches of the scalar gate's sequence split (gdn_forward at a
+    nonzero gdn_forward_split_point, or gdn_forward_split)."""
+    ot = {"bf16": "bf16_t", "fp32": "float"}[o_dtype]
+    return ("forward_pipe_kernel<%d, %d, %s, false, false, false, true> + split_state_kernel<%d, %d> "
+            "+ split_out_kernel<%d, %d, %s>" % (w.chunk, w.K, ot, w.K, w.V, w.K, w.V, ot))
+
+
 def source_digest():
     """sha256 over the HIP sources and the public header: a traffic figure
     measured on other sources no longer describes this kernel."""
@@ -201,6 +214,8 @@ def main():
                           "launches": 5}))
         return
 
+    if args.no_split:
+        os.environ["GDN_FORWARD_NO_SPLIT"] = "1"
     w = WORKLOADS[args.workload]
     if args.chunk:
         import dataclasses
@@ -211,12 +226,13 @@ def main():
     tdt = {"bf16": torch.bfloat16, "fp32": torch.float32}[o_dtype]
     o = torch.empty(w.B, w.T, w.H, w.V, device=dev, dtype=tdt)
     hT = torch.empty(w.B, w.H, w.K, w.V, device=dev, dtype=torch.float32)
-    # the scalar gate's fused forward needs no workspace; the per-key gate's
-    # Gram stage writes its triangular factors into one, allocated here,
-    # outside the timed region
-    ws_bytes = gdn.workspace_bytes(w.B, w.T, w.H, w.K, w.V, w.chunk,
-                                   {"bf16": torch.bfloat16, "fp32": torch.float32}[w.io],
-                                   w.gate == "key", tdt)
+    # the per-key gate's Gram stage writes its triangular factors into a
+    # workspace, and the scalar gate's sequence split its segment states and
+    # correction basis; allocated here, outside the timed region
+    iot = {"bf16": torch.bfloat16, "fp32": torch.float32}[w.io]
+    ws_bytes = gdn.workspace_bytes(w.B, w.T, w.H, w.K, w.V, w.chunk, iot, w.gate == "key", tdt)
+    # where gdn_forward cuts the streams (0: one pass)
+    t_auto = gdn.forward_split_point(w.B, w.T, w.H, w.K, w.V, w.chunk, iot, w.gate == "key", tdt)
     ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8) if ws_bytes else None
 
     n_seqs = 0
@@ -346,10 +362,12 @@ def main():
     del flush
 
     # ---- the dominant kernel.  Scalar gate: a step is one launch of the
-    # fused forward kernel, so its mean event-timed duration is ms_step.  Per-
-    # key gate: a step is the Gram launch then the re-scan launch on one
-    # stream; the events bracket both, so the figure is that of the pair
-    # (the kernel trace splits it)
+    # fused forward kernel, so its mean event-timed duration is ms_step; where
+    # gdn_forward splits the sequence, the step is the split instance and its
+    # two combine launches.  Per-key gate: a step is the Gram launch then the
+    # re-scan launch on one stream.  The events bracket the whole step, so
+    # the figure is that of the step's launches together (the kernel trace
+    # splits it)
     ms_launch = ms_step
     fbytes, fflops = forward_bytes(w, o_dtype, args.states, args.rescan), forward_flops(w)
     kname = kernel_name(w, o_dtype, args.states, args.rescan)
@@ -372,10 +390,11 @@ def main():
             launches = 3
             kname = "bwd_prep_kernel<%d, %d> + bwd_dh_kernel<%d, %d> + bwd_grad_kernel<%d, %d, %d>" % (
                 w.chunk, w.K, w.chunk, w.K, w.chunk, w.K, w.V)
-    if args.split is not None:
+    plain = not (args.states or args.rescan or args.varlen or args.chunk_dq or args.backward
+                 or args.split is not None)
+    if args.split is not None or (plain and t_auto > 0):
         launches = 3
-        kname = ("forward_pipe_kernel<%d, %d, %s, false, false, false, true> + split_out_kernel "
-                 "+ split_state_kernel" % (w.chunk, w.K, {"bf16": "bf16_t", "fp32": "float"}[o_dtype]))
+        kname = split_kernel_names(w, o_dtype)
     if w.gate == "key" and not args.chunk_dq and not args.backward:
         launches = 2
         kname = "kda_gram_kernel<%d, %d, %s%s> + %s" % (
@@ -387,7 +406,7 @@ def main():
                 "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": (None if args.rescan or args.chunk_dq or args.varlen or args.split is not None
-                            or args.backward
+                            or args.backward or args.no_split
                             else measured_traffic(w, o_dtype, args.states)),
                 "ms_per_launch": round(ms_launch, 5), "launches_per_step": launches,
                 "algorithmic_bytes_per_launch": fbytes,
@@ -415,7 +434,7 @@ def main():
                    "chunk": w.chunk, "io": w.io, "o_dtype": o_dtype, "gate": w.gate,
                    "h0": w.h0, "states": bool(args.states), "rescan": bool(args.rescan),
                    "chunk_dq": bool(args.chunk_dq), "varlen_seqs": n_seqs or None,
-                   "split_at": (t_split if args.split is not None else None),
+                   "split_at": (t_split if args.split is not None else (t_auto if plain and t_auto else None)),
                    "backward": bool(args.backward),
                    "parallelism": "single-gpu"},
         "roofline": roofline,

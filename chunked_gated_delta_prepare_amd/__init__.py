@@ -49,9 +49,10 @@ EXPORTS = ["gdn_prepare", "gdn_scan", "gdn_forward", "gdn_forward_states",
            "gdn_forward_varlen", "gdn_rescan_dq", "gdn_chunk_dq", "gdn_workspace_bytes",
            "gdn_workspace_bytes_varlen", "gdn_status_str", "gdn_abi_version",
            "gdn_wait_timeouts", "gdn_forward_noalloc", "gdn_forward_split",
-           "gdn_workspace_bytes_split", "gdn_backward", "gdn_workspace_bytes_backward"]
+           "gdn_workspace_bytes_split", "gdn_backward", "gdn_workspace_bytes_backward",
+           "gdn_forward_split_point"]
 NOALLOC_SCRATCH_BYTES = 32 << 20
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 
 class GdnError(RuntimeError):
@@ -97,6 +98,8 @@ def load_library(path: str | None = None):
         lib.gdn_forward_split.argtypes = [pp, ctypes.c_int64] + [vp] * 9 + [sz, vp]
         lib.gdn_workspace_bytes_split.argtypes = [pp, ctypes.c_int64]
         lib.gdn_workspace_bytes_split.restype = sz
+        lib.gdn_forward_split_point.argtypes = [pp]
+        lib.gdn_forward_split_point.restype = ctypes.c_int64
         lib.gdn_backward.argtypes = [pp] + [vp] * 16 + [sz, vp]
         lib.gdn_workspace_bytes_backward.argtypes = [pp]
         lib.gdn_workspace_bytes_backward.restype = sz
@@ -190,6 +193,14 @@ def workspace_bytes(B, T, H, K, V, chunk, io_dtype, gate_per_key=False, o_dtype=
     return int(load_library().gdn_workspace_bytes(ctypes.byref(pr)))
 
 
+def forward_split_point(B, T, H, K, V, chunk, io_dtype, gate_per_key=False, o_dtype=None):
+    """gdn_forward_split_point: the token at which gdn_forward cuts each
+    stream into two segments run side by side, or 0 for a single pass."""
+    pr = Problem(B, T, H, K, V, int(chunk), _dtype_code(io_dtype), _dtype_code(o_dtype or io_dtype),
+                 GDN_GATE_KEY if gate_per_key else GDN_GATE_HEAD)
+    return int(load_library().gdn_forward_split_point(ctypes.byref(pr)))
+
+
 def wait_timeouts(reset=False):
     """Count of bounded LDS waits inside the bf16-io kernels that gave up on
     the current device since the last reset (gdn_wait_timeouts; synchronous).
@@ -258,12 +269,17 @@ def scan(q, k, w, u, gcum, chunk, h0=None, *, o_dtype=None, o=None, hT=None,
     return o, hT
 
 
-def _workspace(lib, pr, device, workspace, n_seqs=0):
+def _workspace(lib, pr, device, workspace, n_seqs=0, split=False):
     """The workspace the call needs (gdn_workspace_bytes), allocated with
-    torch when the caller passes none; returns (tensor or None, bytes)."""
+    torch when the caller passes none; returns (tensor or None, bytes).
+    For the scalar gate only gdn_forward uses one (its sequence split:
+    ``split``); the other entry points need none."""
     torch = _torch()
-    need = int(lib.gdn_workspace_bytes_varlen(ctypes.byref(pr), ctypes.c_int64(n_seqs)) if n_seqs
-               else lib.gdn_workspace_bytes(ctypes.byref(pr)))
+    if pr.gate == GDN_GATE_HEAD and not split:
+        need = 0
+    else:
+        need = int(lib.gdn_workspace_bytes_varlen(ctypes.byref(pr), ctypes.c_int64(n_seqs)) if n_seqs
+                   else lib.gdn_workspace_bytes(ctypes.byref(pr)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=device, dtype=torch.uint8)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -319,7 +335,7 @@ def _forward(q, k, v, beta, g, chunk, h0, o_dtype, o, hT, output_final_state, wo
                                      _ptr(g), _ptr(h0), _ptr(o), _ptr(hT), _stream(stream))
         _check("gdn_forward_noalloc", rc)
         return o, hT
-    workspace, ws_bytes = _workspace(lib, pr, q.device, workspace)
+    workspace, ws_bytes = _workspace(lib, pr, q.device, workspace, split=True)
     rc = lib.gdn_forward(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
                          _ptr(h0), _ptr(o), _ptr(hT), _ptr(workspace), ws_bytes, _stream(stream))
     _check("gdn_forward", rc)

@@ -83,6 +83,45 @@ gdn_status check_and_trace(const char *entry, const gdn_problem *pr) {
     return st;
 }
 
+// gdn_forward_split's extra conditions on a validated problem.
+gdn_status check_split(const gdn_problem *pr, int64_t t_split) {
+    if (pr->gate != GDN_GATE_HEAD || pr->io_dtype != GDN_BF16 || pr->chunk != 64)
+        return GDN_ERR_UNSUPPORTED;
+    if (t_split <= 0 || t_split >= pr->T || t_split % pr->chunk != 0) return GDN_ERR_BAD_SHAPE;
+    const int64_t th = pr->T * pr->H;
+    if (th * std::max(pr->K, pr->V) * 4 >= ((int64_t)1 << 32)) return GDN_ERR_UNSUPPORTED;
+    if (pr->B * pr->H * (pr->V / 64 + pr->V / 64 + pr->K / 64) >= ((int64_t)1 << 31))
+        return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+// Where gdn_forward cuts its streams (0: a single pass).  Each stream is
+// serial over its chunks, one workgroup per compute unit: the single pass
+// keeps F = B H V/64 units busy for all of T.  The split runs the first
+// segment's F workgroups beside the second segment's S = B H (V/64 + K/64)
+// (zero-start V tiles and identity-start K tiles) on the other kCUs - F
+// units, in R = ceil(S / (kCUs - F)) rounds of T - t_split each, so the two
+// segments end together at t_split = T R / (R + 1).  Measured on gdn-shaped
+// problems (B H from 8 to 64, K = V = 128), the split took 0.56-0.74 of the
+// single pass's time at R = 1 from 128 chunks up and 0.86-0.89 at R = 2 from
+// 256 chunks up, and was slower at R = 2 with 64 chunks (the combine
+// launches and the ramp cost about 40 us).  Scalar gate, bf16 io, chunk 64
+// only (the split's instances); GDN_FORWARD_NO_SPLIT=1 turns it off.
+constexpr int64_t kCUs = 256;          // compute units of a gfx950 device
+int64_t auto_split_point(const gdn_problem *pr) {
+    if (pr->gate != GDN_GATE_HEAD || pr->io_dtype != GDN_BF16 || pr->chunk != 64) return 0;
+    if (const char *e = std::getenv("GDN_FORWARD_NO_SPLIT"))
+        if (*e == '1') return 0;
+    const int64_t nc = (pr->T + pr->chunk - 1) / pr->chunk;
+    const int64_t F = pr->B * pr->H * (pr->V / 64), S = pr->B * pr->H * (pr->V / 64 + pr->K / 64);
+    if (F >= kCUs) return 0;
+    const int64_t R = (S + kCUs - F - 1) / (kCUs - F);
+    if (!((R == 1 && nc >= 128) || (R == 2 && nc >= 256))) return 0;
+    int64_t t = (pr->T * R / (R + 1) + pr->chunk / 2) / pr->chunk * pr->chunk;
+    t = std::min(std::max(t, (int64_t)pr->chunk), (nc - 1) * pr->chunk);
+    return check_split(pr, t) == GDN_OK ? t : 0;
+}
+
 gdn_status launch(const void *fn, int grid, void *params, size_t psize, hipStream_t s) {
     (void)psize;
     return launch_kernel(fn, grid, params, s);
@@ -312,7 +351,14 @@ gdn_status gdn_scan(const gdn_problem *problem, const void *q, const void *k,
 
 size_t gdn_workspace_bytes(const gdn_problem *problem) {
     if (check_problem(problem) != GDN_OK) return 0;
+    const int64_t t_split = auto_split_point(problem);
+    if (t_split > 0) return (size_t)split_workspace_bytes(problem, t_split);
     return (size_t)kda_workspace_bytes(problem, 0);
+}
+
+int64_t gdn_forward_split_point(const gdn_problem *problem) {
+    if (check_problem(problem) != GDN_OK) return 0;
+    return auto_split_point(problem);
 }
 
 size_t gdn_workspace_bytes_varlen(const gdn_problem *problem, int64_t n_seqs) {
@@ -335,6 +381,13 @@ gdn_status gdn_forward(const gdn_problem *problem, const void *q, const void *k,
         if (st != GDN_OK) return st;
         st = check_workspace(problem, 0, workspace, workspace_bytes);
         if (st != GDN_OK) return st;
+        // long streams on a partly idle device: the sequence split, when the
+        // workspace holds it (else the single pass)
+        const int64_t t_split = auto_split_point(problem);
+        if (t_split > 0 && workspace && aligned16(workspace) &&
+            workspace_bytes >= (size_t)split_workspace_bytes(problem, t_split))
+            return enqueue_forward_split(problem, t_split, q, k, v, beta, g, h0, o, hT, workspace,
+                                         (hipStream_t)stream);
     }
     return enqueue_forward(problem, q, k, v, beta, g, h0, o, hT, nullptr, nullptr, nullptr, 0,
                            workspace, (hipStream_t)stream);
@@ -367,17 +420,6 @@ gdn_status gdn_forward_noalloc(const gdn_problem *problem, const void *q, const 
 
 // The split forward's own conditions: scalar gate, bf16 io, chunk 64, a cut
 // at a chunk boundary strictly inside the sequence.
-static gdn_status check_split(const gdn_problem *pr, int64_t t_split) {
-    if (pr->gate != GDN_GATE_HEAD || pr->io_dtype != GDN_BF16 || pr->chunk != 64)
-        return GDN_ERR_UNSUPPORTED;
-    if (t_split <= 0 || t_split >= pr->T || t_split % pr->chunk != 0) return GDN_ERR_BAD_SHAPE;
-    const int64_t th = pr->T * pr->H;
-    if (th * std::max(pr->K, pr->V) * 4 >= ((int64_t)1 << 32)) return GDN_ERR_UNSUPPORTED;
-    if (pr->B * pr->H * (pr->V / 64 + pr->V / 64 + pr->K / 64) >= ((int64_t)1 << 31))
-        return GDN_ERR_UNSUPPORTED;
-    return GDN_OK;
-}
-
 size_t gdn_workspace_bytes_split(const gdn_problem *problem, int64_t t_split) {
     if (check_problem(problem) != GDN_OK || check_split(problem, t_split) != GDN_OK) return 0;
     return (size_t)split_workspace_bytes(problem, t_split);

@@ -64,8 +64,9 @@
  * Requirements: all pointers 16-byte aligned; K, V in {64, 128}; chunk in
  * {32, 64}; B, H >= 1; T >= 0 (any T: a short last chunk is exact).  Shapes
  * outside this set return GDN_ERR_UNSUPPORTED; there is no fallback path.
- * o must not alias any input; hT may alias h0 only in gdn_forward/gdn_scan
- * (each state tile is read completely before it is written).
+ * o must not alias any input; hT may alias h0 only in gdn_forward,
+ * gdn_forward_split and gdn_scan (each state tile is read completely before
+ * it is written).
  *
  * Thread safety: stateless; calls from several host threads are safe.
  */
@@ -79,7 +80,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 9
+#define GDN_ABI_VERSION 10
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -148,10 +149,16 @@ gdn_status gdn_scan(const gdn_problem *problem, const void *q, const void *k,
  * gdn_prepare followed by gdn_scan up to rounding.  hT may be NULL or alias
  * h0.
  * Workspace: `workspace` must hold gdn_workspace_bytes(problem) bytes of
- * device memory, 16-byte aligned (it may be NULL when that is 0: the scalar
- * gate, or T = 0); its contents on entry do not matter, and it is free again
+ * device memory, 16-byte aligned (it may be NULL when that is 0, or for the
+ * scalar gate); its contents on entry do not matter, and it is free again
  * once the call's work on `stream` is done.  Otherwise GDN_ERR_WORKSPACE
  * (missing or too small) or GDN_ERR_ALIGNMENT before any launch.
+ * Scalar gate: when gdn_forward_split_point(problem) is nonzero (long
+ * streams that leave compute units idle, bf16 io, chunk 64) and the
+ * workspace holds gdn_workspace_bytes(problem) bytes, the call runs
+ * gdn_forward_split at that point (three launches); with a smaller or no
+ * workspace it runs the single pass.  Either way the results agree up to
+ * rounding.
  * For the per-key gate the call is two launches: a kernel over every chunk at
  * once forms each chunk's decayed Gram products (A, and P of the read-out)
  * with every pair's decay split at a row between the two tokens, found by
@@ -167,6 +174,22 @@ gdn_status gdn_forward(const gdn_problem *problem, const void *q, const void *k,
                        const void *v, const float *beta, const float *g,
                        const float *h0, void *o, float *hT, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_forward_split_point -- where gdn_forward cuts each stream of this
+ * problem into two segments run side by side (see gdn_forward_split), or 0
+ * for a single pass.  Every (batch, head, 64-wide V tile) stream is serial
+ * over its chunks and takes one compute unit, so a problem with F = B H V/64
+ * streams leaves 256 - F units of a gfx950 device idle.  The split runs the
+ * second segment as S = B H (V/64 + K/64) streams (zero-start V tiles and
+ * identity-start K tiles) on those units in R = ceil(S / (256 - F)) rounds,
+ * and cuts at T R / (R + 1), rounded to a chunk, so both segments end
+ * together.  Nonzero for the scalar gate with bf16 io and chunk 64 when
+ * R = 1 and T spans at least 128 chunks, or R = 2 and at least 256 chunks
+ * (where it measured faster); 0 otherwise, for bad arguments, or with the
+ * environment variable GDN_FORWARD_NO_SPLIT=1.
+ */
+int64_t gdn_forward_split_point(const gdn_problem *problem);
 
 /*
  * gdn_forward_states -- gdn_forward that also saves what a backward pass
@@ -340,7 +363,8 @@ gdn_status gdn_wait_timeouts(uint32_t *count, int reset);
  * together when the first holds about twice the second's chunks.  Results
  * equal gdn_forward's up to rounding (the o of the second segment is
  * rounded to the o dtype twice when that is bf16).  Arguments as in
- * gdn_forward; hT may be NULL but not alias h0.  Workspace:
+ * gdn_forward; hT may be NULL or alias h0 (h0 is read by the first launch
+ * only, hT written by the last).  Workspace:
  * gdn_workspace_bytes_split(problem, t_split) bytes, 16-byte aligned.
  * GDN_ERR_UNSUPPORTED for the per-key gate, fp32 io or chunk 32;
  * GDN_ERR_BAD_SHAPE for a t_split outside those bounds.
@@ -359,13 +383,15 @@ size_t gdn_workspace_bytes_split(const gdn_problem *problem, int64_t t_split);
 /*
  * gdn_forward_noalloc -- gdn_forward for callers that cannot allocate device
  * memory (code under stream capture into a HIP graph, tight serving loops,
- * harnesses that forbid hipMalloc).  Same arguments, results and launches as
+ * harnesses that forbid hipMalloc).  Same arguments and results as
  * gdn_forward, without the workspace: the per-key gate's Gram workspace is
  * taken from a static device array of GDN_NOALLOC_SCRATCH_BYTES bytes that
  * the library holds on each device it runs on until the process ends.  The
- * call allocates nothing and frees nothing.  Returns GDN_ERR_WORKSPACE,
- * before anything is enqueued, when gdn_workspace_bytes(problem) exceeds
- * that size (the scalar gate needs none and is never refused for it), and
+ * scalar gate always runs the single pass here (never the sequence split,
+ * whose workspace grows with T).  The call allocates nothing and frees
+ * nothing.  Returns GDN_ERR_WORKSPACE, before anything is enqueued, when the
+ * per-key gate's workspace, gdn_workspace_bytes(problem), exceeds that size
+ * (the scalar gate uses none here and is never refused for it), and
  * GDN_ERR_HIP if the array's device address cannot be looked up (done once
  * per device, on the first call that needs it, with the current device).
  * All calls on one device share the array: calls that may run at the same
@@ -379,11 +405,14 @@ gdn_status gdn_forward_noalloc(const gdn_problem *problem, const void *q, const 
                                const float *h0, void *o, float *hT, void *stream);
 
 /* Workspace gdn_forward, gdn_forward_states and gdn_rescan_dq need for this
- * problem: 0 for the scalar gate or T = 0; for the per-key gate one slot per
- * (chunk, head), B * ceil(T / chunk) * H slots of 2 * chunk^2 * 4 bytes (fp32
- * io: the solve tile and P) or 2 * chunk^2 * 2 + 3 * chunk * K * 2 + 4 * K
- * bytes (bf16 io: the same in fp16, the re-scan's three fp16 operand tiles
- * and the chunk's per-key decay).  0 on bad arguments. */
+ * problem.  Per-key gate: one slot per (chunk, head), B * ceil(T / chunk) * H
+ * slots of 2 * chunk^2 * 4 bytes (fp32 io: the solve tile and P) or
+ * 2 * chunk^2 * 2 + 3 * chunk * K * 2 + 4 * K bytes (bf16 io: the same in
+ * fp16, the re-scan's three fp16 operand tiles and the chunk's per-key
+ * decay).  Scalar gate: gdn_workspace_bytes_split(problem, t) when
+ * t = gdn_forward_split_point(problem) is nonzero (what gdn_forward's split
+ * uses; gdn_forward_states and gdn_rescan_dq need none and ignore it), else
+ * 0.  0 for T = 0 and on bad arguments. */
 size_t gdn_workspace_bytes(const gdn_problem *problem);
 
 /* The same for gdn_forward_varlen over n_seqs packed sequences (the per-key

@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
          "gdn_forward_varlen", "gdn_rescan_dq", "gdn_chunk_dq", "gdn_workspace_bytes",
          "gdn_workspace_bytes_varlen", "gdn_status_str", "gdn_abi_version",
          "gdn_wait_timeouts", "gdn_forward_noalloc", "gdn_forward_split",
-         "gdn_workspace_bytes_split", "gdn_backward", "gdn_workspace_bytes_backward"])
+         "gdn_workspace_bytes_split", "gdn_backward", "gdn_workspace_bytes_backward",
+         "gdn_forward_split_point"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -356,3 +357,35 @@ def test_chunk_dq_validates_before_launch(lib, gdn):
 def test_wait_timeouts_rejects_null(lib, gdn):
     # validated before the device word is touched: no GPU needed
     assert lib.gdn_wait_timeouts(None, 0) == 1
+
+
+def test_forward_split_point(lib, gdn, monkeypatch):
+    """Where gdn_forward cuts its streams: F = B H V/64 single-pass streams
+    leave 256 - F compute units idle; the second segment's S = B H (V/64 +
+    K/64) streams run there in R = ceil(S / (256 - F)) rounds, so the cut is
+    T R / (R + 1) rounded to a chunk; only for the scalar gate, bf16 io,
+    chunk 64, and R = 1 from 128 chunks or R = 2 from 256 chunks."""
+    monkeypatch.delenv("GDN_FORWARD_NO_SPLIT", raising=False)
+    sp = lambda **kw: lib.gdn_forward_split_point(ctypes.byref(_problem(gdn, **kw)))
+    big = dict(B=1, T=65536, H=64, K=128, V=128)
+    # F = 128, S = 256: R = 2, 2/3 of 65536 = 43690.7 -> 683 chunks
+    assert sp(**big) == 683 * 64
+    assert sp(B=1, T=16384, H=64, K=128, V=128) == 171 * 64          # 10922.7 -> 171 chunks
+    assert sp(B=1, T=16384 - 64, H=64, K=128, V=128) == 0            # 255 chunks at R = 2
+    assert sp(B=1, T=8192, H=8, K=128, V=128) == 4096                # F = 16, S = 32: R = 1
+    assert sp(B=1, T=8192 - 64, H=8, K=128, V=128) == 0              # 127 chunks
+    assert sp(B=4, T=4096, H=16, K=128, V=128) == 0                  # 64 chunks
+    assert sp(B=1, T=65536, H=128, K=128, V=128) == 0                # F = 256: no idle unit
+    assert sp(B=1, T=65536, H=96, K=128, V=128) == 0                 # F = 192: R = 6
+    assert sp(B=1, T=65536, H=64, K=64, V=128) == 683 * 64           # S = 192: R = 2
+    assert sp(B=1, T=65536, H=64, K=128, V=64) == 32768              # F = 64, S = 192: R = 1, T / 2
+    assert sp(B=1, T=65537, H=8, K=128, V=128) == 32768              # a ragged last chunk
+    for kw in (dict(chunk=32), dict(io=0, o=0), dict(gate=1)):
+        assert sp(**big, **kw) == 0, kw
+    assert lib.gdn_forward_split_point(None) == 0
+    # the workspace gdn_forward asks for is the split's
+    pr = _problem(gdn, **big)
+    assert lib.gdn_workspace_bytes(ctypes.byref(pr)) == lib.gdn_workspace_bytes_split(
+        ctypes.byref(pr), ctypes.c_int64(683 * 64)) > 0
+    monkeypatch.setenv("GDN_FORWARD_NO_SPLIT", "1")
+    assert sp(**big) == 0 and lib.gdn_workspace_bytes(ctypes.byref(pr)) == 0
