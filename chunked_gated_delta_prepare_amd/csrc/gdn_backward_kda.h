@@ -62,10 +62,12 @@ __device__ __forceinline__ void col_cumsum(float *G, int ld, float scale) {
     bwd_barrier();
 }
 
-// Reverse (suffix) cumsum over the C rows of each column, in place.
-template <int C, int X>
+// Reverse (suffix) cumsum over the C rows of each column, in place, by the
+// workgroup's NTH threads in NTH / X segments of rows.
+template <int C, int X, int NTH = 256>
 __device__ __forceinline__ void col_revsum(float *G, int ld) {
-    constexpr int SEG = 256 / X, RPS = C / SEG;
+    constexpr int SEG = NTH / X, RPS = C / SEG;
+    static_assert(SEG >= 1 && RPS >= 1 && C % SEG == 0, "row segments");
     const int d = threadIdx.x % X, sg = threadIdx.x / X;
     float acc = 0.f;
     for (int r = (sg + 1) * RPS - 1; r >= sg * RPS; --r) {
@@ -830,21 +832,26 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kda_kernel(BwdParams p) {
 // dq, dk and dbeta, completes dgamma and writes dg = its reverse cumsum over
 // the chunk's rows, per key column.
 // ---------------------------------------------------------------------------
+// bwd_dec_kda_kernel's workgroup: sixteen waves, four per SIMD.  Its
+// entry-wise sums are vector-ALU bound at 66 registers; on kda-shaped
+// problems two waves per SIMD ran it 1.7x faster than one, four another 1.16x.
+constexpr int kDecThreads = 1024;
+
 template <int C, int K> struct BwdDecLayout {
     static constexpr int kPa = 0;                           // dP, dA fp32 [2][C][C]
     static constexpr int kQ = kPa + 2 * C * C * 4;          // q, k bf16 [2][C][K]
     static constexpr int kGm = kQ + 2 * C * K * 2;          // Gamma fp32 [C][K]
     static constexpr int kGd = kGm + C * K * 4;             // dgamma fp32 [C][K]
-    static constexpr int kVec = kGd + C * K * 4;            // beta [C], pbk [4][C]
-    static constexpr int kBytes = kVec + 5 * C * 4;
+    static constexpr int kVec = kGd + C * K * 4;            // beta [C], pbk [waves][C]
+    static constexpr int kBytes = kVec + (1 + kDecThreads / 64) * C * 4;
     static_assert(kBytes <= kLdsBytesMax, "LDS budget");
 };
 
 template <int C, int K>
-__global__ __launch_bounds__(256, 1) void bwd_dec_kda_kernel(BwdParams p) {
+__global__ __launch_bounds__(kDecThreads, 1) void bwd_dec_kda_kernel(BwdParams p) {
     typedef BwdDecLayout<C, K> L;
     typedef BwdSlotK<C, K> SL;
-    constexpr int SEG = 256 / K;
+    constexpr int NTH = kDecThreads, SEG = NTH / K;
     __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
     float *dP = (float *)(smem + L::kPa), *dA = dP + C * C;
     uint16_t *Qs = (uint16_t *)(smem + L::kQ), *Ks = Qs + C * K;
@@ -869,24 +876,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dec_kda_kernel(BwdParams p) {
     const rsrc_t rdb = make_rsrc(p.dbeta + row0, (uint32_t)T * H * 4);
 
 #pragma unroll
-    for (int pc = tid; pc < 2 * C * C / 4; pc += 256) *(u32x4 *)(dP + 4 * pc) = bload128(rpa, 16 * pc, 0);
+    for (int pc = tid; pc < 2 * C * C / 4; pc += NTH) *(u32x4 *)(dP + 4 * pc) = bload128(rpa, 16 * pc, 0);
 #pragma unroll
-    for (int pc = tid; pc < C * K / 8; pc += 256) {
+    for (int pc = tid; pc < C * K / 8; pc += NTH) {
         const int row = pc / (K / 8), c8 = pc % (K / 8);
         const uint32_t off = (row * rsK + 8 * c8) * 2;
         *(u32x4 *)(Qs + row * K + 8 * c8) = bload128(rq, off, t0 * rsK * 2);
         *(u32x4 *)(Ks + row * K + 8 * c8) = bload128(rk, off, t0 * rsK * 2);
     }
 #pragma unroll
-    for (int pc = tid; pc < C * K / 4; pc += 256) *(u32x4 *)(Gm + 4 * pc) = bload128(rsl, SL::kGam + 16 * pc, 0);
+    for (int pc = tid; pc < C * K / 4; pc += NTH) *(u32x4 *)(Gm + 4 * pc) = bload128(rsl, SL::kGam + 16 * pc, 0);
     if (tid < C) betv[tid] = __uint_as_float(bload32(rb, tid * H * 4, t0 * H * 4));
-    for (int i = tid; i < 4 * C; i += 256) pbk[i] = 0.f;
+    for (int i = tid; i < (NTH / 64) * C; i += NTH) pbk[i] = 0.f;
     bwd_barrier();
 
     const int d = tid % K, sg = tid / K;
     auto ldk = [&](const uint16_t *S, int r) { return __uint_as_float((uint32_t)S[r * K + d] << 16); };
 #pragma unroll 1
     for (int x = sg; x < C; x += SEG) {
+        // this row's earlier gradient terms, in flight through the sums
+        const uint32_t off = (x * rsK + d) * 4, soff = t0 * rsK * 4;
+        const float dq0 = __uint_as_float(bload32(rdq, off, soff));
+        const float dk0 = __uint_as_float(bload32(rdk, off, soff));
+        const float dg0 = __uint_as_float(bload32(rdg, off, soff));
         const float gx = Gm[x * K + d];
         float u1 = 0.f, u3 = 0.f, u2 = 0.f, u4 = 0.f;
 #pragma unroll 4
@@ -902,10 +914,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dec_kda_kernel(BwdParams p) {
             u4 += dA[r * C + x] * betv[r] * ldk(Ks, r) * E;
         }
         const float qx = ldk(Qs, x), kx = ldk(Ks, x), bx = betv[x];
-        const uint32_t off = (x * rsK + d) * 4, soff = t0 * rsK * 4;
-        const float dq0 = __uint_as_float(bload32(rdq, off, soff));
-        const float dk0 = __uint_as_float(bload32(rdk, off, soff));
-        const float dg0 = __uint_as_float(bload32(rdg, off, soff));
         bstore32(__float_as_uint(dq0 + u1), rdq, off, soff);
         bstore32(__float_as_uint(dk0 + u2 + bx * u3 + u4), rdk, off, soff);
         Gd[x * K + d] = dg0 + qx * u1 - kx * u2 + bx * kx * u3 - kx * u4;
@@ -916,13 +924,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dec_kda_kernel(BwdParams p) {
         if (l == 0) pbk[wv * C + x] = t;
     }
     bwd_barrier();
-    col_revsum<C, K>(Gd, K);
+    col_revsum<C, K, NTH>(Gd, K);
 #pragma unroll 1
     for (int x = sg; x < C; x += SEG) bstore32(__float_as_uint(Gd[x * K + d]), rdg, (x * rsK + d) * 4, t0 * rsK * 4);
     if (tid < C) {
-        const float db0 = __uint_as_float(bload32(rdb, tid * H * 4, t0 * H * 4));
-        bstore32(__float_as_uint(db0 + pbk[tid] + pbk[C + tid] + pbk[2 * C + tid] + pbk[3 * C + tid]), rdb,
-                 tid * H * 4, t0 * H * 4);
+        float db = __uint_as_float(bload32(rdb, tid * H * 4, t0 * H * 4));
+#pragma unroll
+        for (int w = 0; w < NTH / 64; ++w) db += pbk[w * C + tid];
+        bstore32(__float_as_uint(db), rdb, tid * H * 4, t0 * H * 4);
     }
 }
 

@@ -111,6 +111,7 @@ SMALL = [
     (1, 128, 1, 64, 64, 64, "fp32", "head", 2.0, False),      # the tiny fp32 workload
     (1, 200, 2, 64, 64, 64, "fp32", "head", 2.0, True),
     (2, 150, 2, 64, 64, 32, "fp32", "key", 3.0, True),
+    (1, 150, 2, 128, 128, 64, "fp32", "key", 3.0, True),     # the four-wave kernel's largest LDS
     (1, 97, 3, 128, 128, 32, "fp32", "head", 2.0, True),
     (2, 333, 4, 128, 128, 64, "bf16", "head", 2.0, True),
     (2, 256, 4, 64, 64, 32, "bf16", "head", 4.0, False),
