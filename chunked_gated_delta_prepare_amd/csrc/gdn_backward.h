@@ -858,7 +858,6 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
     // v . dR goes into beta's row sums (a row's pieces are consecutive lanes)
     // and dv = beta dR out; phase C's operands are issued.
     RowsF32<K, V> r_dh;
-    u32x2 r_hh[RowsF32<K, V>::NP];
     {
         typedef RowsF32<C, V> RF;
         uint16_t *X = (uint16_t *)(smem + L::kX);
@@ -878,10 +877,6 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
             store_row4_pairs(x, rdv, ((t0 + row) * rsV + 4 * (c4 & ~1)) * 4, c4 & 1);
         }
         r_dh.load(rdh, V, 0);
-#pragma unroll
-        for (int j = 0; j < RowsF32<K, V>::NP; ++j)
-            r_hh[j] = __builtin_amdgcn_raw_buffer_load_b64(
-                rh, (RowsF32<K, V>::row(j) * V + 4 * RowsF32<K, V>::c4(j)) * 2, 0, 0);
     }
     bwd_barrier();
     {
@@ -926,18 +921,25 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
         }
     }
     bwd_barrier();
-    // phase C: W = D dh'^T; with <h, dh'>
+    // phase C: <h, dh'> from phase B's state tile, still in LDS; then
+    // W = D dh'^T over the operands that replace it
     {
-        uint16_t *X = (uint16_t *)(smem + L::kX);
-        r_D.template put<LV>(X + (L::kC_d - L::kX) / 2);
-        r_dh.template put_split<LV>(X + (L::kC_dh - L::kX) / 2);
+        typedef RowsF32<K, V> RK;
+        const uint16_t *Hm = (const uint16_t *)(smem + L::kB_h);
         float hdp = 0.f;
 #pragma unroll
-        for (int j = 0; j < RowsF32<K, V>::NP; ++j) hdp += dot4_bf(r_dh.v[j], r_hh[j]);
+        for (int j = 0; j < RK::NP; ++j)
+            hdp += dot4_bf(r_dh.v[j], *(const u32x2 *)(Hm + RK::row(j) * LV + 4 * RK::c4(j)));
         hdp = sum16(hdp);
         hdp += __shfl_xor(hdp, 16);
         hdp += __shfl_xor(hdp, 32);
         if (l == 0) hd[wv] = hdp;
+    }
+    bwd_barrier();
+    {
+        uint16_t *X = (uint16_t *)(smem + L::kX);
+        r_D.template put<LV>(X + (L::kC_d - L::kX) / 2);
+        r_dh.template put_split<LV>(X + (L::kC_dh - L::kX) / 2);
     }
     bwd_barrier();
     {

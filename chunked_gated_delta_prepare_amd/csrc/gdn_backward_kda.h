@@ -675,7 +675,6 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kda_kernel(BwdParams p) {
     bwd_barrier();
     // phase B: Z, Y; v . dR and dv as in bwd_grad_kernel
     RowsF32<K, V> r_dh;
-    u32x2 r_hh[RowsF32<K, V>::NP];
     {
         typedef RowsF32<C, V> RF;
         uint16_t *X = (uint16_t *)(smem + L::kX);
@@ -695,10 +694,6 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kda_kernel(BwdParams p) {
             store_row4_pairs(x, rdv, ((t0 + row) * rsV + 4 * (c4 & ~1)) * 4, c4 & 1);
         }
         r_dh.load(rdh, V, 0);
-#pragma unroll
-        for (int j = 0; j < RowsF32<K, V>::NP; ++j)
-            r_hh[j] = __builtin_amdgcn_raw_buffer_load_b64(
-                rh, (RowsF32<K, V>::row(j) * V + 4 * RowsF32<K, V>::c4(j)) * 2, 0, 0);
     }
     bwd_barrier();
     float4v dq[NB][CT], dk[NB][CT], dg[NB][CT];
@@ -740,18 +735,23 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kda_kernel(BwdParams p) {
         }
     }
     bwd_barrier();
-    // phase C: W; <h_d, dh'_d> per key row
+    // phase C: <h_d, dh'_d> per key row from phase B's state tile, still in
+    // LDS; then W over the operands that replace it
     {
         typedef RowsF32<K, V> RK;
-        uint16_t *X = (uint16_t *)(smem + L::kX);
-        r_D.template put<LV>(X + (L::kC_d - L::kX) / 2);
-        r_dh.template put_split<LV>(X + (L::kC_dh - L::kX) / 2);
+        const uint16_t *Hm = (const uint16_t *)(smem + L::kB_h);
 #pragma unroll
         for (int j = 0; j < RK::NP; ++j) {
-            float d = sum16(dot4_bf(r_dh.v[j], r_hh[j]));
+            float d = sum16(dot4_bf(r_dh.v[j], *(const u32x2 *)(Hm + RK::row(j) * LV + 4 * RK::c4(j))));
             if (RK::PPR == 32) d += __shfl_xor(d, 16);
             if (RK::c4(j) == 0) hdk[RK::row(j)] = d;
         }
+    }
+    bwd_barrier();
+    {
+        uint16_t *X = (uint16_t *)(smem + L::kX);
+        r_D.template put<LV>(X + (L::kC_d - L::kX) / 2);
+        r_dh.template put_split<LV>(X + (L::kC_dh - L::kX) / 2);
     }
     bwd_barrier();
     {
