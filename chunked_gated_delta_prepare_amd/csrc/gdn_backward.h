@@ -552,7 +552,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dh_kernel(BwdParams p) {
 // gradients) go through per-wave LDS rows, added in a fixed order: the
 // results do not depend on scheduling.
 // ---------------------------------------------------------------------------
-template <int C, int K, int V> struct BwdGradLayout {
+template <int C, int K, int V, int NW = 4> struct BwdGradLayout {
     static constexpr int LK = K + 8, LC = C + 8, LV = V + 8;
     static constexpr int kQr = 0;
     static constexpr int kKr = kQr + C * LK * 2;
@@ -564,43 +564,44 @@ template <int C, int K, int V> struct BwdGradLayout {
     static constexpr int cmax(int a, int b) { return a > b ? a : b; }
     static constexpr int kXBytes = cmax(cmax(4 * C * LV * 2, 6 * C * LC * 2),
                                         cmax(3 * C * LV * 2 + K * LV * 2, C * LV * 2 + 2 * K * LV * 2));
-    static constexpr int kVec = kX + kXBytes;   // gamma, b, c, beta [C]; pg, pb, pkw [4][C]; hd [4]
-    static constexpr int kBytes = kVec + (16 * C + 4) * 4;
+    static constexpr int kVec = kX + kXBytes;   // gamma, b, c, beta [C]; pg, pb, pkw [NW][C]; hd [NW]
+    static constexpr int kBytes = kVec + (4 * C + 3 * NW * C + NW) * 4;
     static_assert(kBytes <= kLdsBytesMax, "LDS budget");
 };
 
 // rows x X bf16 block of a token-major tensor (row pitch rs elements) as
-// 16-byte pieces in registers, row-major over the workgroup (piece j of a
-// thread: row (tid + 256 j) / (X / 8), columns 8 ((tid + 256 j) % (X / 8))).
-template <int ROWS, int X> struct RowsBf {
-    static constexpr int PPR = X / 8, NP = ROWS * PPR / 256;
-    static_assert(NP >= 1 && ROWS * PPR % 256 == 0, "pieces");
+// 16-byte pieces in registers, row-major over the workgroup's NTH threads
+// (piece j of a thread: row (tid + NTH j) / (X / 8), columns
+// 8 ((tid + NTH j) % (X / 8))).
+template <int ROWS, int X, int NTH = 256> struct RowsBf {
+    static constexpr int PPR = X / 8, NP = ROWS * PPR / NTH;
+    static_assert(NP >= 1 && ROWS * PPR % NTH == 0, "pieces");
     u32x4 v[NP];
     __device__ void load(rsrc_t r, uint32_t rs, uint32_t soff) {
 #pragma unroll
         for (int j = 0; j < NP; ++j) {
-            const int pc = threadIdx.x + 256 * j, row = pc / PPR, c8 = pc % PPR;
+            const int pc = threadIdx.x + NTH * j, row = pc / PPR, c8 = pc % PPR;
             v[j] = bload128(r, (row * rs + 8 * c8) * 2, soff);
         }
     }
     template <int LD> __device__ void put(uint16_t *dst) const {
 #pragma unroll
         for (int j = 0; j < NP; ++j) {
-            const int pc = threadIdx.x + 256 * j, row = pc / PPR, c8 = pc % PPR;
+            const int pc = threadIdx.x + NTH * j, row = pc / PPR, c8 = pc % PPR;
             *(u32x4 *)(dst + row * LD + 8 * c8) = v[j];
         }
     }
 };
 
 // rows x X fp32 block as 16-byte pieces (four values; piece j of a thread:
-// row (tid + 256 j) / (X / 4), columns 4 ((tid + 256 j) % (X / 4)) .. +3),
+// row (tid + NTH j) / (X / 4), columns 4 ((tid + NTH j) % (X / 4)) .. +3),
 // put into LDS as bf16 high and low planes [2][ROWS][LD].
-template <int ROWS, int X> struct RowsF32 {
-    static constexpr int PPR = X / 4, NP = ROWS * PPR / 256;
-    static_assert(NP >= 1 && ROWS * PPR % 256 == 0 && PPR <= 32, "pieces");
+template <int ROWS, int X, int NTH = 256> struct RowsF32 {
+    static constexpr int PPR = X / 4, NP = ROWS * PPR / NTH;
+    static_assert(NP >= 1 && ROWS * PPR % NTH == 0 && PPR <= 32, "pieces");
     u32x4 v[NP];
-    __device__ static int row(int j) { return (threadIdx.x + 256 * j) / PPR; }
-    __device__ static int c4(int j) { return (threadIdx.x + 256 * j) % PPR; }
+    __device__ static int row(int j) { return (threadIdx.x + NTH * j) / PPR; }
+    __device__ static int c4(int j) { return (threadIdx.x + NTH * j) % PPR; }
     __device__ void load(rsrc_t r, uint32_t rs, uint32_t soff) {
 #pragma unroll
         for (int j = 0; j < NP; ++j) v[j] = bload128(r, (row(j) * rs + 4 * c4(j)) * 4, soff);
@@ -653,20 +654,27 @@ __device__ __forceinline__ void store_row4_pairs(const float4v &x, rsrc_t r, uin
     __builtin_amdgcn_raw_buffer_store_b64(b, r, off_even + (odd ? 24 : 16), 0, 0);
 }
 
-template <int C, int K, int V>
-__global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
-    typedef BwdGradLayout<C, K, V> L;
+// NW = 4 or 8 waves.  With eight (two per SIMD, for the larger tiles) the
+// key tiles are shared out as with four and each wave takes half of the
+// 16-row blocks: wave w has key group w % 4 and row half w / 4.
+template <int C, int K, int V, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void bwd_grad_kernel(BwdParams p) {
+    typedef BwdGradLayout<C, K, V, NW> L;
+    constexpr int NTH = 64 * NW, NRH = NW / 4;
     constexpr int LK = L::LK, LC = L::LC, LV = L::LV;
     constexpr int NB = C / 16, NS = C / 32, KS = K / 32, VS = V / 32, NLT = NB * (NB + 1) / 2;
-    constexpr int MT = (NLT + 3) / 4;           // lower C x C tiles per wave (at most)
+    constexpr int MT = (NLT + NW - 1) / NW;     // lower C x C tiles per wave (at most)
     constexpr int CT = K / 64;                  // 16-column key tiles per wave
+    constexpr int NBW = NB / NRH;               // 16-row blocks per wave
     static_assert(K % 64 == 0, "key tiles");
+    static_assert((NW == 4 || NW == 8) && NB % NRH == 0, "waves");
     __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
     uint16_t *Qr = (uint16_t *)(smem + L::kQr), *Kr = (uint16_t *)(smem + L::kKr);
     float *gam = (float *)(smem + L::kVec), *bv = gam + C, *cv = bv + C, *betv = cv + C;
-    float *pg = betv + C, *pb = pg + 4 * C, *pkw = pb + 4 * C, *hd = pkw + 4 * C;
+    float *pg = betv + C, *pb = pg + NW * C, *pkw = pb + NW * C, *hd = pkw + NW * C;
 
     const int tid = threadIdx.x, wv = wave_id(), l = lane_id(), g = l >> 4, n = l & 15;
+    const int kgrp = wv % 4, rhalf = wv / 4;
     const int NT = p.NT, T = p.T;
     const int c = blockIdx.x % NT, bh = blockIdx.x / NT, b = bh / p.H, h = bh % p.H;
     const int t0 = c * C;
@@ -686,30 +694,30 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
 
     // q, k into LDS; dO, D, dR and v into registers (kept until their
     // phases); g, beta; per-row sums cleared
-    RowsBf<C, K> r_q, r_k;
+    typedef RowsF32<C, V, NTH> RV;
+    RowsBf<C, K, NTH> r_q, r_k;
     r_q.load(rq, rsK, t0 * rsK * 2);
     r_k.load(rk, rsK, t0 * rsK * 2);
-    RowsBf<C, V> r_do, r_D;
-    RowsF32<C, V> r_dR;
+    RowsBf<C, V, NTH> r_do, r_D;
+    RV r_dR;
     r_do.load(rdo, rsV, t0 * rsV * 2);
     r_D.load(rD, rsV, t0 * rsV * 2);
     r_dR.load(rdR, rsV, t0 * rsV * 4);
-    u32x2 r_v[RowsF32<C, V>::NP];
+    u32x2 r_v[RV::NP];
 #pragma unroll
-    for (int j = 0; j < RowsF32<C, V>::NP; ++j)
-        r_v[j] = __builtin_amdgcn_raw_buffer_load_b64(rv, (RowsF32<C, V>::row(j) * rsV + 4 * RowsF32<C, V>::c4(j)) * 2,
-                                                      t0 * rsV * 2, 0);
+    for (int j = 0; j < RV::NP; ++j)
+        r_v[j] = __builtin_amdgcn_raw_buffer_load_b64(rv, (RV::row(j) * rsV + 4 * RV::c4(j)) * 2, t0 * rsV * 2, 0);
     {
         r_q.template put<LK>(Qr);
         r_k.template put<LK>(Kr);
-        for (int i = tid; i < 12 * C + 4; i += 256) pg[i] = 0.f;
+        for (int i = tid; i < 3 * NW * C + NW; i += NTH) pg[i] = 0.f;
         uint16_t *X = (uint16_t *)(smem + L::kX);
         r_do.template put<LV>(X + (L::kA_do - L::kX) / 2);
         r_D.template put<LV>(X + (L::kA_d - L::kX) / 2);
         r_dR.template put_split<LV>(X + (L::kA_r - L::kX) / 2);
     }
     // phase B's h, in flight through phase A
-    RowsBf<K, V> r_h;
+    RowsBf<K, V, NTH> r_h;
     r_h.load(rh, V, 0);
     if (wv == 0) {
         float x = l < C ? __uint_as_float(bload32(rg, l * H * 4, t0 * H * 4)) : 0.f;
@@ -736,7 +744,7 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
         const uint16_t *Rh = (const uint16_t *)(smem + L::kA_r), *Rl = Rh + C * LV;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            const int t = wv + 4 * m;
+            const int t = wv + NW * m;
             Fv[m] = float4v{0, 0, 0, 0};
             Gv[m] = float4v{0, 0, 0, 0};
             if (t >= NLT) continue;
@@ -794,11 +802,11 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
     bwd_barrier();
     // phase A2: F, F^T, G + G^T as bf16 parts
     uint16_t *Fp = (uint16_t *)(smem + L::kF), *FTp = (uint16_t *)(smem + L::kFT), *Gp = (uint16_t *)(smem + L::kGs);
-    for (int i = tid; i < 6 * C * LC / 8; i += 256) ((u32x4 *)Fp)[i] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = tid; i < 6 * C * LC / 8; i += NTH) ((u32x4 *)Fp)[i] = u32x4{0u, 0u, 0u, 0u};
     bwd_barrier();
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-        const int t = wv + 4 * m;
+        const int t = wv + NW * m;
         if (t >= NLT) continue;
         int tt = t, i = 0;
         while (tt > i) {
@@ -827,13 +835,14 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
         }
     }
     bwd_barrier();
-    // phase A3: dq = F K, dk = F^T Q + (G + G^T) K for this wave's key columns
-    float4v dq[NB][CT], dk[NB][CT];
+    // phase A3: dq = F K, dk = F^T Q + (G + G^T) K for this wave's key
+    // columns and row blocks
+    float4v dq[NBW][CT], dk[NBW][CT];
 #pragma unroll
-    for (int i = 0; i < NB; ++i)
+    for (int ib = 0; ib < NBW; ++ib)
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-            const int kc = 16 * (CT * wv + ct);
+            const int i = NBW * rhalf + ib, kc = 16 * (CT * kgrp + ct);
             float4v aq = {0, 0, 0, 0}, ak = {0, 0, 0, 0};
 #pragma unroll
             for (int st = 0; st < NS; ++st) {
@@ -850,16 +859,16 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
                 mfma_bf(ak, lds_frag(Gp, LC, 16 * i, 32 * st), kb);
                 mfma_bf(ak, lds_frag(Gp + C * LC, LC, 16 * i, 32 * st), kb);
             }
-            dq[i][ct] = aq;
-            dk[i][ct] = ak;
+            dq[ib][ct] = aq;
+            dk[ib][ct] = ak;
         }
     bwd_barrier();
     // phase B: Z = dO h^T, Y = dR h^T.  Its operands come from registers;
     // v . dR goes into beta's row sums (a row's pieces are consecutive lanes)
     // and dv = beta dR out; phase C's operands are issued.
-    RowsF32<K, V> r_dh;
+    RowsF32<K, V, NTH> r_dh;
     {
-        typedef RowsF32<C, V> RF;
+        typedef RV RF;
         uint16_t *X = (uint16_t *)(smem + L::kX);
         r_do.template put<LV>(X + (L::kB_do - L::kX) / 2);
         r_dR.template put_split<LV>(X + (L::kB_r - L::kX) / 2);
@@ -883,11 +892,12 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
         const uint16_t *Do = (const uint16_t *)(smem + L::kB_do), *Hm = (const uint16_t *)(smem + L::kB_h);
         const uint16_t *Rh = (const uint16_t *)(smem + L::kB_r), *Rl = Rh + C * LV;
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
+        for (int ib = 0; ib < NBW; ++ib) {
+            const int i = NBW * rhalf + ib;
             float qz[4] = {0, 0, 0, 0}, ky[4] = {0, 0, 0, 0};
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-                const int kc = 16 * (CT * wv + ct);
+                const int kc = 16 * (CT * kgrp + ct);
                 float4v z = {0, 0, 0, 0}, y = {0, 0, 0, 0};
 #pragma unroll
                 for (int s = 0; s < VS; ++s) {
@@ -899,8 +909,8 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int R = 16 * i + 4 * g + e, key = kc + n;
-                    dq[i][ct][e] += bv[R] * z[e];
-                    dk[i][ct][e] -= betv[R] * bv[R] * y[e];
+                    dq[ib][ct][e] += bv[R] * z[e];
+                    dk[ib][ct][e] -= betv[R] * bv[R] * y[e];
                     qz[e] += __uint_as_float((uint32_t)Qr[R * LK + key] << 16) * z[e];
                     ky[e] += __uint_as_float((uint32_t)Kr[R * LK + key] << 16) * y[e];
                 }
@@ -924,7 +934,7 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
     // phase C: <h, dh'> from phase B's state tile, still in LDS; then
     // W = D dh'^T over the operands that replace it
     {
-        typedef RowsF32<K, V> RK;
+        typedef RowsF32<K, V, NTH> RK;
         const uint16_t *Hm = (const uint16_t *)(smem + L::kB_h);
         float hdp = 0.f;
 #pragma unroll
@@ -946,11 +956,12 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
         const uint16_t *Dm = (const uint16_t *)(smem + L::kC_d);
         const uint16_t *Hh = (const uint16_t *)(smem + L::kC_dh), *Hl = Hh + K * LV;
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
+        for (int ib = 0; ib < NBW; ++ib) {
+            const int i = NBW * rhalf + ib;
             float kw[4] = {0, 0, 0, 0};
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-                const int kc = 16 * (CT * wv + ct);
+                const int kc = 16 * (CT * kgrp + ct);
                 float4v w = {0, 0, 0, 0};
 #pragma unroll
                 for (int s = 0; s < VS; ++s) {
@@ -961,7 +972,7 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int R = 16 * i + 4 * g + e, key = kc + n;
-                    dk[i][ct][e] += cv[R] * w[e];
+                    dk[ib][ct][e] += cv[R] * w[e];
                     kw[e] += __uint_as_float((uint32_t)Kr[R * LK + key] << 16) * w[e];
                 }
             }
@@ -979,13 +990,13 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
         const rsrc_t rdk = make_rsrc(p.dk + row0 * K, (uint32_t)T * rsK * 4);
         const uint32_t pr_row = 4 * g + 2 * (n & 1);
 #pragma unroll
-        for (int i = 0; i < NB; ++i)
+        for (int ib = 0; ib < NBW; ++ib)
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-                const uint32_t voff = (pr_row * rsK + 16 * (CT * wv + ct) + (n & ~1)) * 4;
-                const uint32_t soff = (t0 + 16 * i) * rsK * 4;
-                store_acc_pairs<float>(dq[i][ct], rdq, voff, rsK * 4, soff);
-                store_acc_pairs<float>(dk[i][ct], rdk, voff, rsK * 4, soff);
+                const uint32_t voff = (pr_row * rsK + 16 * (CT * kgrp + ct) + (n & ~1)) * 4;
+                const uint32_t soff = (t0 + 16 * (NBW * rhalf + ib)) * rsK * 4;
+                store_acc_pairs<float>(dq[ib][ct], rdq, voff, rsK * 4, soff);
+                store_acc_pairs<float>(dk[ib][ct], rdk, voff, rsK * 4, soff);
             }
     }
     bwd_barrier();
@@ -995,7 +1006,7 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
         float dgam = 0.f, db = 0.f, kw = 0.f;
         if (l < C) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
+            for (int w = 0; w < NW; ++w) {
                 dgam += pg[w * C + l];
                 db += pb[w * C + l];
                 kw += pkw[w * C + l];
@@ -1007,7 +1018,10 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kernel(BwdParams p) {
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
         const float gl = __expf(gam[C - 1]);
-        if (l == C - 1) dgam += tot + gl * (hd[0] + hd[1] + hd[2] + hd[3]);
+        float hds = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) hds += hd[w];
+        if (l == C - 1) dgam += tot + gl * hds;
         // suffix sum over lanes (lanes >= C hold zero)
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {

@@ -15,7 +15,10 @@ gdn_status launch_backward(BwdParams &bp, hipStream_t s) {
     }
     st = launch_kernel((const void *)&bwd_dh_kernel<C, K>, bp.B * bp.H * bp.nvt, &bp, s, 256);
     if (st != GDN_OK || bp.NT == 0) return st;
-    return launch_kernel((const void *)&bwd_grad_kernel<C, K, V>, bp.B * bp.H * bp.NT, &bp, s, 256);
+    // eight waves (two per SIMD) where the register pieces divide among 512
+    // threads: chunk 64
+    constexpr int NW = C == 64 ? 8 : 4;
+    return launch_kernel((const void *)&bwd_grad_kernel<C, K, V, NW>, bp.B * bp.H * bp.NT, &bp, s, 64 * NW);
 }
 
 template <int C, int K>
