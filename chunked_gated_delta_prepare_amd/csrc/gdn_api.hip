@@ -469,7 +469,6 @@ gdn_status gdn_rescan_dq(const gdn_problem *problem, const void *q, const void *
     gdn_status st = check_and_trace("gdn_rescan_dq", problem);
     if (st != GDN_OK) return st;
     if (problem->io_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
-    if (problem->gate == GDN_GATE_KEY && problem->chunk != 64) return GDN_ERR_UNSUPPORTED;
     if (problem->T == 0) {
         st = check_ptrs({}, {h0, hT, hck, vnew, dq, dout});
         if (st != GDN_OK) return st;

@@ -76,9 +76,10 @@ __device__ __forceinline__ void kda_slot_load(rsrc_t rv_, rsrc_t rw_, const uint
 
 // DQ: the backward's re-scan (the KDA re-scan page's kernel): the chunk-start
 // states and v' as with ST, plus dq's chunk-start-state term
-// DQ = dO h_c^T (raw) accumulated into p.dq, and no o.  Chunk 64 only: the
+// DQ = dO h_c^T (raw) accumulated into p.dq, and no o.  At chunk 64 the
 // state is staged in the q~ and k~ tiles of the slot the chain has just
-// finished with, which hold K x 64 bf16 at C = 64.
+// finished with, which hold K x 64 bf16 there; at chunk 32 they are too
+// small and it has an LDS array of its own (32 KB at K = 128).
 template <int C, int K, typename OT, bool ST = false, bool VL = false, bool DQ = false>
 __global__ __launch_bounds__((kda_threads<C, K, DQ>()), 1) void forward_pipe_kda_kernel(FwdParams p) {
     constexpr int NPW = kda_prep_waves<C, K, DQ>(), NPT = 64 * NPW;
@@ -90,9 +91,12 @@ __global__ __launch_bounds__((kda_threads<C, K, DQ>()), 1) void forward_pipe_kda
     static_assert(L::kBytes <= kLdsBytesMax, "LDS budget");
     static_assert(NB == 2 || NB == 4, "chunk 32 or 64");
     static_assert(K == 64 || K == 128, "key dim 64 or 128");
-    static_assert(!DQ || (ST && C * K * 2 >= K * 64 * 2), "the re-scan saves states; chunk 64");
+    static_assert(!DQ || ST, "the re-scan saves states");
+    constexpr bool kOwnStage = DQ && C * K * 2 < K * 64 * 2;    // chunk 32
+    static_assert(L::kBytes + (kOwnStage ? 4 * K * 64 : 0) <= kLdsBytesMax, "LDS budget with the re-scan");
 
     __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
+    __shared__ __attribute__((aligned(16))) uint16_t hq_own[kOwnStage ? 2 * K * 64 : 8];
     _Float16 *Qb = (_Float16 *)(smem + L::kQ);
     _Float16 *Kb = (_Float16 *)(smem + L::kK);
     _Float16 *Hb = (_Float16 *)(smem + L::kH);
@@ -146,14 +150,16 @@ __global__ __launch_bounds__((kda_threads<C, K, DQ>()), 1) void forward_pipe_kda
         // DQ: dq[t] += h_c dO_t for the tokens of chunk n, with h_c in hacc:
         // the state goes to LDS as bf16 high and low parts ([K][64], 16-byte
         // chunks swizzled by row) in the qd and kd tiles of slot sl, free
-        // then; each wave forms DQ for K/4 key rows over the tile's 64 value
-        // columns with bf16 MFMAs (bf16 keeps any dO magnitude in range)
+        // then (chunk 32: in hq_own); each wave forms DQ for K/4 key rows over
+        // the tile's 64 value columns with bf16 MFMAs (bf16 keeps any dO
+        // magnitude in range)
         const rsrc_t rdo_ = make_rsrc(DQ ? (const IO *)p.dout + row0 * V : nullptr, DQ ? (uint32_t)T * rsV * SIO : 0u);
         const uint32_t do_off = ((uint32_t)(l & 15) * rsV + vt * 64 + 8 * (l >> 4)) * SIO;
         unsigned chain_target = 0;
         auto rescan_dq = [&](int n, int sl) {
             const uint32_t t0 = (uint32_t)(n * C);
-            uint16_t *Hhi = (uint16_t *)(Qb + sl * C * K), *Hlo = (uint16_t *)(Kb + sl * C * K);
+            uint16_t *Hhi = kOwnStage ? hq_own : (uint16_t *)(Qb + sl * C * K);
+            uint16_t *Hlo = kOwnStage ? hq_own + K * 64 : (uint16_t *)(Kb + sl * C * K);
             bf16x8 dof[2][NB];
 #pragma unroll
             for (int s = 0; s < 2; ++s)

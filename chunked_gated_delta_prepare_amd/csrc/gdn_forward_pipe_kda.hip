@@ -1,6 +1,6 @@
 // libgdn: dispatch of the pipelined forward kernel for the per-key gate
 // (gdn_forward_pipe_kda.h), plain, saving states (ST), over packed
-// sequences (VL) or as the backward's re-scan (DQ, chunk 64).
+// sequences (VL) or as the backward's re-scan (DQ).
 #include "gdn_forward_pipe_kda.h"
 #include "gdn_internal.h"
 
@@ -16,11 +16,9 @@ const void *kda_fn(bool o_f32) {
 template <int C, int K>
 const void *kda_mode(bool o_f32, const FwdParams &fp, int &threads) {
     threads = kda_threads<C, K, false>();
-    if constexpr (C == 64) {
-        if (fp.dq) {
-            threads = kda_threads<C, K, true>();
-            return kda_fn<C, K, true, false, true>(o_f32);
-        }
+    if (fp.dq) {
+        threads = kda_threads<C, K, true>();
+        return kda_fn<C, K, true, false, true>(o_f32);
     }
     if (fp.hck) return kda_fn<C, K, true, false>(o_f32);
     if (fp.cu) return kda_fn<C, K, false, true>(o_f32);

@@ -219,16 +219,16 @@ gdn_status gdn_forward_states(const gdn_problem *problem, const void *q, const v
  * page, bwd_scan.py: its CuTe kernel re-runs the state recurrence to save
  * the h checkpoints and v_new and, fused in, forms dq's only dependence on
  * the state, DQ = dO h_c^T, raw: no gate and no scale).  Here with bf16 io,
- * for the scalar gate (Gated DeltaNet, chunk 32 or 64) and the per-key gate
- * (KDA, chunk 64):
+ * for the scalar gate (Gated DeltaNet) and the per-key gate (KDA), chunk 32
+ * or 64:
  *   hck, vnew  as in gdn_forward_states (problem->o_dtype);
  *   dq [B,T,H,K] fp32: dq[t] += h_c dO_t for token t of chunk c, h_c the
  *              state at the chunk's start (K x V), dO [B,T,H,V] in the io
  *              dtype.  dq is accumulated into (the V tiles of a head add up
  *              there, in an order that does not change the sum for V <= 128),
  *              so the caller zeroes it first.
- * No o is produced (q is still read).  hT, h0 as in gdn_forward.  Other
- * dtypes, or the per-key gate at chunk 32, return GDN_ERR_UNSUPPORTED.
+ * No o is produced (q is still read).  hT, h0 as in gdn_forward.  fp32 io
+ * returns GDN_ERR_UNSUPPORTED.
  * With T = 0 only hT is
  * written.  Pointers as in gdn_forward_states; dq must not alias any input.
  * Workspace as in gdn_forward.

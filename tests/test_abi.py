@@ -319,7 +319,6 @@ def test_rescan_dq_validates_before_launch(lib, gdn):
     for name in ("q", "k", "v", "beta", "g", "do", "hck", "vnew", "dq"):
         assert _rescan(lib, pr, **{name: None}) == 1, name
     assert _rescan(lib, pr, dq=MISALIGNED) == 4
-    assert _rescan(lib, _problem(gdn, gate=1, chunk=32)) == 3  # per-key gate: chunk 64 only
     assert _rescan(lib, _problem(gdn, io=0, o=0)) == 3        # bf16 io only
     assert _rescan(lib, _problem(gdn, T=0), q=None, k=None, v=None, beta=None, g=None, do=None,
                    hck=None, vnew=None, dq=None) == 0

@@ -75,6 +75,9 @@ CASES = [
     (1, 130, 2, 128, 64, 64, True, "key"),        # one V tile, ragged tail
     (1, 97, 2, 64, 128, 64, True, "key"),         # dk != dv
     (1, 1, 1, 128, 128, 64, True, "key"),         # a single token
+    (2, 200, 2, 128, 128, 32, True, "key"),       # chunk 32: the state staged on its own
+    (1, 111, 3, 64, 128, 32, False, "key"),
+    (1, 77, 2, 128, 64, 32, True, "key"),
 ]
 
 
@@ -107,13 +110,3 @@ def test_rescan_dq_full_size_sampled(name):
     pairs = w.B * w.H
     run_rescan("rescan_full_" + name, w.B, w.T, w.H, w.K, w.V, w.chunk, w.h0, w.seed,
                heads=[0, (7 * pairs) // 11, pairs - 1], gate=w.gate, bias=w.gate_bias)
-
-
-def test_rescan_dq_key_gate_needs_chunk_64():
-    d = _dev()
-    q = torch.zeros(1, 64, 1, 64, device=d, dtype=torch.bfloat16)
-    beta = torch.zeros(1, 64, 1, device=d)
-    g = torch.zeros(1, 64, 1, 64, device=d)
-    with pytest.raises(gdn.GdnError) as e:
-        gdn.rescan_dq(q, q, q, beta, g, q, 32)
-    assert e.value.status == 3                       # GDN_ERR_UNSUPPORTED
