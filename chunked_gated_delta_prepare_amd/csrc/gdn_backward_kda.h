@@ -371,14 +371,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dh_kda_kernel(BwdParams p) {
     };
 
     float4v dh[KT16];
+    if (p.dhT) {
+        // (one branch, then every load in flight together)
+        const float *src = p.dhT + ((int64_t)b * H + h) * K * V + col + n;
 #pragma unroll
-    for (int kt = 0; kt < KT16; ++kt) {
+        for (int kt = 0; kt < KT16; ++kt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            dh[kt][e] = p.dhT ? p.dhT[((int64_t)b * H + h) * K * V + (16 * kt + 4 * g + e) * V + col + n] : 0.f;
+            for (int e = 0; e < 4; ++e) dh[kt][e] = src[(16 * kt + 4 * g + e) * V];
+    } else {
+#pragma unroll
+        for (int kt = 0; kt < KT16; ++kt) dh[kt] = float4v{0, 0, 0, 0};
     }
+    // dh' and dR are stored as soon as the chain has them (see bwd_dh_kernel)
     float4v dhs[KT16], rrs[NB];
-    int cs = -1;
     auto store_stash = [&](int cc) {
         float *he = p.dhe + (((int64_t)b * NT + cc) * H + h) * K * V;
         const rsrc_t rhe = make_rsrc(he, (uint32_t)(K * V * 4));
@@ -420,7 +425,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dh_kda_kernel(BwdParams p) {
         }
         if (tid < CR::NVP) *(u32x4 *)(betv + 4 * tid) = cr.vec;
         if (c > 0) bwd_load_chunk_kda<C, K>(cr, rq, rk, rdo, slot_rsrc(c - 1), t0 - C, rsK, rsV, vt);
-        if (cs >= 0) store_stash(cs);
         bwd_barrier();
         // P^T dO, and (Q * b)^T dO with the decay on the q operand
         float4v pd[NB], qd[KT16];
@@ -503,7 +507,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dh_kda_kernel(BwdParams p) {
         }
 #pragma unroll
         for (int i = 0; i < NB; ++i) rrs[i] = rr[i];
-        cs = c;
+        store_stash(c);
         {
             bf16x8 uh[NS], ul[NS];
 #pragma unroll
@@ -542,7 +546,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dh_kda_kernel(BwdParams p) {
             }
         }
     }
-    if (cs >= 0) store_stash(cs);
     if (p.dh0) {
         const rsrc_t rh0 = make_rsrc(p.dh0 + ((int64_t)b * H + h) * K * V, (uint32_t)(K * V * 4));
 #pragma unroll
