@@ -829,39 +829,54 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_kda_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// bwd_dec_kda_kernel: one workgroup per (chunk, head), the four
-// decay-weighted sums, entry by entry with the exact factor: thread (d, x)
-// for key column d and rows x, a row's partner rows in a loop.  Adds them to
-// dq, dk and dbeta, completes dgamma and writes dg = its reverse cumsum over
-// the chunk's rows, per key column.
+// bwd_dec_kda_kernel: one workgroup per (chunk, head) forms the four
+// decay-weighted sums, adds them to dq, dk and dbeta, completes dgamma and
+// writes dg, its reverse cumsum over the chunk's rows, per key column.  The
+// sums go by 16-row blocks.  Item (X, t) is
+// row block X of the chunk and 16-column key tile t; lane (j, g) owns rows
+// 16 X + 4 g + e (e = 0..3) of key column 16 t + j, the layout of a 16 x 16
+// accumulator tile.  For those entries:
+//  - pairs with the partner in an earlier block (s < 16 X) on the matrix
+//    cores (fp32 16x16x4): with m = 16 X - 1, the last row before block X,
+//    E_rsd = 2^(Gamma_rd - Gamma_md) 2^(Gamma_md - Gamma_sd), both decays;
+//    U1 = dP_{X,<X} Kt and U3 = dA_{X,<X} Kt with Kt_sd = k_sd
+//    2^(Gamma_md - Gamma_sd), each row r then scaled by 2^(Gamma_rd - Gamma_md);
+//  - pairs with the partner in a later block (r > 16 X + 15): with
+//    m = 16 X + 15, U2 = dP^T Qt and U4 = dA^T Bt, Qt_rd = q_rd
+//    2^(Gamma_rd - Gamma_md), Bt_rd = beta_r k_rd 2^(Gamma_rd - Gamma_md),
+//    each row s then scaled by 2^(Gamma_md - Gamma_sd);
+//  - pairs inside block X entry by entry, E_rsd the running product of the
+//    per-token decays a_td = 2^(Gamma_td - Gamma_(t-1)d), t = s+1 .. r.
+// Every factor is at most 1.  Each lane then adds its entries to dq and dk,
+// completes their dgamma, and its row sums k U3 go to dbeta.
 // ---------------------------------------------------------------------------
-// bwd_dec_kda_kernel's workgroup: sixteen waves, four per SIMD.  Its
-// entry-wise sums are vector-ALU bound at 66 registers; on kda-shaped
-// problems two waves per SIMD ran it 1.7x faster than one, four another 1.16x.
-constexpr int kDecThreads = 1024;
-
 template <int C, int K> struct BwdDecLayout {
-    static constexpr int kPa = 0;                           // dP, dA fp32 [2][C][C]
-    static constexpr int kQ = kPa + 2 * C * C * 4;          // q, k bf16 [2][C][K]
+    static constexpr int LA = C + 4;                        // dP, dA row pitch (floats)
+    static constexpr int kPa = 0;                           // dP, dA fp32 [2][C][LA]
+    static constexpr int kQ = kPa + 2 * C * LA * 4;         // q, k bf16 [2][C][K]
     static constexpr int kGm = kQ + 2 * C * K * 2;          // Gamma fp32 [C][K]
     static constexpr int kGd = kGm + C * K * 4;             // dgamma fp32 [C][K]
-    static constexpr int kVec = kGd + C * K * 4;            // beta [C], pbk [waves][C]
-    static constexpr int kBytes = kVec + (1 + kDecThreads / 64) * C * 4;
+    static constexpr int kVec = kGd + C * K * 4;            // beta [C], pbk [NW][C]
+    static constexpr int NIT = (C / 16) * (K / 16);         // items
+    static constexpr int NW = NIT < 16 ? NIT : 16;          // waves
+    static constexpr int kBytes = kVec + (1 + NW) * C * 4;
     static_assert(kBytes <= kLdsBytesMax, "LDS budget");
+    static_assert(NIT % NW == 0, "items per wave");
 };
 
 template <int C, int K>
-__global__ __launch_bounds__(kDecThreads, 1) void bwd_dec_kda_kernel(BwdParams p) {
+__global__ __launch_bounds__((64 * BwdDecLayout<C, K>::NW), 1) void bwd_dec_kda_kernel(BwdParams p) {
     typedef BwdDecLayout<C, K> L;
     typedef BwdSlotK<C, K> SL;
-    constexpr int NTH = kDecThreads, SEG = NTH / K;
+    constexpr int NB = C / 16, KT = K / 16, NW = L::NW, NTH = 64 * NW, LA = L::LA, SEG = NTH / K;
+    constexpr int IPW = L::NIT / NW;
     __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
-    float *dP = (float *)(smem + L::kPa), *dA = dP + C * C;
+    float *dP = (float *)(smem + L::kPa), *dA = dP + C * LA;
     uint16_t *Qs = (uint16_t *)(smem + L::kQ), *Ks = Qs + C * K;
     float *Gm = (float *)(smem + L::kGm), *Gd = (float *)(smem + L::kGd);
     float *betv = (float *)(smem + L::kVec), *pbk = betv + C;
 
-    const int tid = threadIdx.x, wv = wave_id(), l = lane_id();
+    const int tid = threadIdx.x, wv = wave_id(), l = lane_id(), j = l & 15, g = l >> 4;
     const int NT = p.NT, T = p.T;
     const int c = blockIdx.x % NT, bh = blockIdx.x / NT, b = bh / p.H, h = bh % p.H;
     const int t0 = c * C;
@@ -878,62 +893,138 @@ __global__ __launch_bounds__(kDecThreads, 1) void bwd_dec_kda_kernel(BwdParams p
     const rsrc_t rdg = make_rsrc(p.dg + row0 * K, (uint32_t)T * rsK * 4);
     const rsrc_t rdb = make_rsrc(p.dbeta + row0, (uint32_t)T * H * 4);
 
-#pragma unroll
-    for (int pc = tid; pc < 2 * C * C / 4; pc += NTH) *(u32x4 *)(dP + 4 * pc) = bload128(rpa, 16 * pc, 0);
-#pragma unroll
+    // dP and dA (rows padded to LA floats: the row-major and the transposed
+    // operand reads spread over the banks), q, k, Gamma, beta
+    for (int pc = tid; pc < 2 * C * C / 4; pc += NTH) {
+        const int row = pc / (C / 4), c4 = pc % (C / 4);          // row of either plane
+        *(u32x4 *)(dP + row * LA + 4 * c4) = bload128(rpa, 16 * pc, 0);
+    }
     for (int pc = tid; pc < C * K / 8; pc += NTH) {
         const int row = pc / (K / 8), c8 = pc % (K / 8);
         const uint32_t off = (row * rsK + 8 * c8) * 2;
         *(u32x4 *)(Qs + row * K + 8 * c8) = bload128(rq, off, t0 * rsK * 2);
         *(u32x4 *)(Ks + row * K + 8 * c8) = bload128(rk, off, t0 * rsK * 2);
     }
-#pragma unroll
     for (int pc = tid; pc < C * K / 4; pc += NTH) *(u32x4 *)(Gm + 4 * pc) = bload128(rsl, SL::kGam + 16 * pc, 0);
     if (tid < C) betv[tid] = __uint_as_float(bload32(rb, tid * H * 4, t0 * H * 4));
-    for (int i = tid; i < (NTH / 64) * C; i += NTH) pbk[i] = 0.f;
+    for (int i = tid; i < NW * C; i += NTH) pbk[i] = 0.f;
     bwd_barrier();
 
-    const int d = tid % K, sg = tid / K;
-    auto ldk = [&](const uint16_t *S, int r) { return __uint_as_float((uint32_t)S[r * K + d] << 16); };
+    auto bfv16 = [&](const uint16_t *S, int r, int d) { return __uint_as_float((uint32_t)S[r * K + d] << 16); };
+    const uint32_t soff = t0 * rsK * 4;
 #pragma unroll 1
-    for (int x = sg; x < C; x += SEG) {
-        // this row's earlier gradient terms, in flight through the sums
-        const uint32_t off = (x * rsK + d) * 4, soff = t0 * rsK * 4;
-        const float dq0 = __uint_as_float(bload32(rdq, off, soff));
-        const float dk0 = __uint_as_float(bload32(rdk, off, soff));
-        const float dg0 = __uint_as_float(bload32(rdg, off, soff));
-        const float gx = Gm[x * K + d];
-        float u1 = 0.f, u3 = 0.f, u2 = 0.f, u4 = 0.f;
-#pragma unroll 4
-        for (int s = 0; s <= x; ++s) {
-            const float ks = ldk(Ks, s) * fast_exp2(gx - Gm[s * K + d]);
-            u1 += dP[x * C + s] * ks;
-            u3 += dA[x * C + s] * ks;              // dA's diagonal is zero
+    for (int it = 0; it < IPW; ++it) {
+        const int item = wv + NW * it, X = item / KT, d = 16 * (item % KT) + j, r0 = 16 * X + 4 * g;
+        // this lane's earlier gradient terms, in flight through the sums
+        float dq0[4], dk0[4], dg0[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t off = ((r0 + e) * rsK + d) * 4;
+            dq0[e] = __uint_as_float(bload32(rdq, off, soff));
+            dk0[e] = __uint_as_float(bload32(rdk, off, soff));
+            dg0[e] = __uint_as_float(bload32(rdg, off, soff));
         }
+        float u1[4] = {0, 0, 0, 0}, u2[4] = {0, 0, 0, 0}, u3[4] = {0, 0, 0, 0}, u4[4] = {0, 0, 0, 0};
+        if (X > 0) {
+            // partners in the earlier blocks; operand A lane (i = j, k = g)
+            // holds dP[16 X + j][4 st + g], B lane (j, g) Kt[4 st + g][d]
+            const float gm = Gm[(16 * X - 1) * K + d];
+            float4v a1 = {0, 0, 0, 0}, a3 = {0, 0, 0, 0};
 #pragma unroll 4
-        for (int r = x; r < C; ++r) {
-            const float E = fast_exp2(Gm[r * K + d] - gx);
-            u2 += dP[r * C + x] * ldk(Qs, r) * E;
-            u4 += dA[r * C + x] * betv[r] * ldk(Ks, r) * E;
+            for (int st = 0; st < 4 * X; ++st) {
+                const int s = 4 * st + g;
+                const float bk = bfv16(Ks, s, d) * fast_exp2(gm - Gm[s * K + d]);
+                a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(dP[(16 * X + j) * LA + s], bk, a1, 0, 0, 0);
+                a3 = __builtin_amdgcn_mfma_f32_16x16x4f32(dA[(16 * X + j) * LA + s], bk, a3, 0, 0, 0);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float sc = fast_exp2(Gm[(r0 + e) * K + d] - gm);
+                u1[e] = a1[e] * sc;
+                u3[e] = a3[e] * sc;
+            }
         }
-        const float qx = ldk(Qs, x), kx = ldk(Ks, x), bx = betv[x];
-        bstore32(__float_as_uint(dq0 + u1), rdq, off, soff);
-        bstore32(__float_as_uint(dk0 + u2 + bx * u3 + u4), rdk, off, soff);
-        Gd[x * K + d] = dg0 + qx * u1 - kx * u2 + bx * kx * u3 - kx * u4;
-        float t = kx * u3;
-        t = sum16(t);
-        t += __shfl_xor(t, 16);
-        t += __shfl_xor(t, 32);
-        if (l == 0) pbk[wv * C + x] = t;
+        if (X < NB - 1) {
+            // partners in the later blocks; A lane (i = j, k = g) holds
+            // dP[r][16 X + j] for r = 16 X + 16 + 4 st + g (the transpose)
+            const float gm = Gm[(16 * X + 15) * K + d];
+            float4v a2 = {0, 0, 0, 0}, a4 = {0, 0, 0, 0};
+#pragma unroll 4
+            for (int st = 0; st < 4 * (NB - 1 - X); ++st) {
+                const int r = 16 * X + 16 + 4 * st + g;
+                const float f = fast_exp2(Gm[r * K + d] - gm);
+                const float bq = bfv16(Qs, r, d) * f, bb = betv[r] * bfv16(Ks, r, d) * f;
+                a2 = __builtin_amdgcn_mfma_f32_16x16x4f32(dP[r * LA + 16 * X + j], bq, a2, 0, 0, 0);
+                a4 = __builtin_amdgcn_mfma_f32_16x16x4f32(dA[r * LA + 16 * X + j], bb, a4, 0, 0, 0);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float sc = fast_exp2(gm - Gm[(r0 + e) * K + d]);
+                u2[e] = a2[e] * sc;
+                u4[e] = a4[e] * sc;
+            }
+        }
+        // inside block X; a = a_{s+1, d} (a_{r d} in the second pass), the
+        // decay of one token step, shared by the four rows
+        float cur[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cur[e] = 0.f;
+        // U1, U3: s from the block's last row down; cur[e] = E_{r s} for
+        // r = r0 + e (1 at s = r, one more step decay per step down, 0 past r)
+#pragma unroll 2
+        for (int sl = 15; sl >= 0; --sl) {
+            const int s = 16 * X + sl;
+            const float ks = bfv16(Ks, s, d);
+            const float a = sl < 15 ? fast_exp2(Gm[(s + 1) * K + d] - Gm[s * K + d]) : 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rl = 4 * g + e;
+                cur[e] = sl == rl ? 1.f : (sl < rl ? cur[e] * a : 0.f);
+                const float w = ks * cur[e];
+                u1[e] += dP[(r0 + e) * LA + s] * w;
+                u3[e] += dA[(r0 + e) * LA + s] * w;
+            }
+        }
+        // U2, U4: r from the block's first row up; cur[e] = E_{r s} for
+        // s = r0 + e
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cur[e] = 0.f;
+#pragma unroll 2
+        for (int rl = 0; rl < 16; ++rl) {
+            const int r = 16 * X + rl;
+            const float qr = bfv16(Qs, r, d), bkr = betv[r] * bfv16(Ks, r, d);
+            const float a = rl > 0 ? fast_exp2(Gm[r * K + d] - Gm[(r - 1) * K + d]) : 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int sl = 4 * g + e;
+                cur[e] = rl == sl ? 1.f : (rl > sl ? cur[e] * a : 0.f);
+                u2[e] += dP[r * LA + r0 + e] * qr * cur[e];
+                u4[e] += dA[r * LA + r0 + e] * bkr * cur[e];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = r0 + e;
+            const float qv = bfv16(Qs, r, d), kv = bfv16(Ks, r, d), bx = betv[r];
+            const uint32_t off = (r * rsK + d) * 4;
+            bstore32(__float_as_uint(dq0[e] + u1[e]), rdq, off, soff);
+            bstore32(__float_as_uint(dk0[e] + u2[e] + bx * u3[e] + u4[e]), rdk, off, soff);
+            Gd[r * K + d] = dg0[e] + qv * u1[e] - kv * u2[e] + bx * kv * u3[e] - kv * u4[e];
+            const float t = sum16(kv * u3[e]);
+            if (j == 0) pbk[wv * C + r] += t;
+        }
     }
     bwd_barrier();
     col_revsum<C, K, NTH>(Gd, K);
+    {
+        const int d = tid % K, sg = tid / K;
 #pragma unroll 1
-    for (int x = sg; x < C; x += SEG) bstore32(__float_as_uint(Gd[x * K + d]), rdg, (x * rsK + d) * 4, t0 * rsK * 4);
+        for (int x = sg; x < C; x += SEG) bstore32(__float_as_uint(Gd[x * K + d]), rdg, (x * rsK + d) * 4, soff);
+    }
     if (tid < C) {
         float db = __uint_as_float(bload32(rdb, tid * H * 4, t0 * H * 4));
 #pragma unroll
-        for (int w = 0; w < NTH / 64; ++w) db += pbk[w * C + tid];
+        for (int w = 0; w < NW; ++w) db += pbk[w * C + tid];
         bstore32(__float_as_uint(db), rdb, tid * H * 4, t0 * H * 4);
     }
 }

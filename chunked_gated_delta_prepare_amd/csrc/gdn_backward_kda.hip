@@ -19,7 +19,7 @@ gdn_status launch_backward_kda(BwdParams &bp, hipStream_t s) {
     if (st != GDN_OK || bp.NT == 0) return st;
     st = launch_kernel((const void *)&bwd_grad_kda_kernel<C, K, V>, gch, &bp, s, 256);
     if (st != GDN_OK) return st;
-    return launch_kernel((const void *)&bwd_dec_kda_kernel<C, K>, gch, &bp, s, kDecThreads);
+    return launch_kernel((const void *)&bwd_dec_kda_kernel<C, K>, gch, &bp, s, 64 * BwdDecLayout<C, K>::NW);
 }
 
 template <int C, int K>
