@@ -39,28 +39,59 @@ struct SplitParams {
 namespace {
 
 // hT = N + M h_in (fp32; skipped when hT is NULL), and h_in^T as bf16 high
-// and low parts for split_out_kernel: one thread per (key row, value
-// column), 256 / V key rows per workgroup.
+// and low parts for split_out_kernel.  One workgroup per 16 key rows of one
+// (batch, head): thread (value column c, row group) holds 16 / (256 / V)
+// consecutive key rows of column c; M's 16 rows are staged in LDS and read
+// as broadcasts, h_in's rows stream from memory once per workgroup.
+constexpr int kStateRows = 16;
+
 template <int K, int V>
 __global__ __launch_bounds__(256) void split_state_kernel(SplitParams p) {
-    constexpr int RPW = 256 / V;
-    const int tid = threadIdx.x, c = tid % V;
-    const int bh = blockIdx.x / (K / RPW), kr = RPW * (blockIdx.x % (K / RPW)) + tid / V;
+    constexpr int RB = kStateRows, CG = 256 / V, RPT = RB / CG;
+    static_assert(RPT % 4 == 0, "rows per thread");
+    __shared__ float Ms[RB * K];
+    const int tid = threadIdx.x, c = tid % V, rg = tid / V;
+    const int bh = blockIdx.x / (K / RB), r0 = RB * (blockIdx.x % (K / RB)) + RPT * rg;
     const float *hin = p.hin + (int64_t)bh * K * V;
-    const float x = hin[kr * V + c];
-    const uint16_t hi = f32_to_bf16_bits(x);
-    const int64_t tpos = ((int64_t)bh * V + c) * K + kr, plane = (int64_t)p.B * p.H * V * K;
-    p.hinT[tpos] = hi;
-    p.hinT[plane + tpos] = f32_to_bf16_bits(x - __uint_as_float((uint32_t)hi << 16));
-    if (!p.hT) return;
-    const float *M = p.M + ((int64_t)bh * K + kr) * K;
-    float s0 = 0.f, s1 = 0.f;
-    for (int j = 0; j < K; j += 2) {
-        s0 += M[j] * hin[j * V + c];
-        s1 += M[j + 1] * hin[(j + 1) * V + c];
+    {
+        // this thread's RPT rows of column c, transposed: RPT consecutive
+        // bf16 of row c of h_in^T, stored four at a time
+        const int64_t tpos = ((int64_t)bh * V + c) * K + r0, plane = (int64_t)p.B * p.H * V * K;
+#pragma unroll
+        for (int e4 = 0; e4 < RPT; e4 += 4) {
+            uint32_t hw[2], lw[2];
+#pragma unroll
+            for (int e = 0; e < 4; e += 2) {
+                const float x0 = hin[(r0 + e4 + e) * V + c], x1 = hin[(r0 + e4 + e + 1) * V + c];
+                const uint16_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
+                const uint16_t l0 = f32_to_bf16_bits(x0 - __uint_as_float((uint32_t)h0 << 16));
+                const uint16_t l1 = f32_to_bf16_bits(x1 - __uint_as_float((uint32_t)h1 << 16));
+                hw[e / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                lw[e / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+            }
+            *(u32x2 *)(p.hinT + tpos + e4) = u32x2{hw[0], hw[1]};
+            *(u32x2 *)(p.hinT + plane + tpos + e4) = u32x2{lw[0], lw[1]};
+        }
     }
-    const int64_t at = ((int64_t)bh * K + kr) * V + c;
-    p.hT[at] = p.N[at] + (s0 + s1);
+    if (!p.hT) return;                       // uniform over the grid
+    const float *M = p.M + ((int64_t)bh * K + RB * (blockIdx.x % (K / RB))) * K;
+    for (int i = tid; i < RB * K; i += 256) Ms[i] = M[i];
+    __syncthreads();
+    float acc[RPT];
+#pragma unroll
+    for (int e = 0; e < RPT; ++e) acc[e] = 0.f;
+    const float *Mr = Ms + RPT * rg * K;
+#pragma unroll 8
+    for (int j = 0; j < K; ++j) {
+        const float x = hin[j * V + c];
+#pragma unroll
+        for (int e = 0; e < RPT; ++e) acc[e] += Mr[e * K + j] * x;
+    }
+#pragma unroll
+    for (int e = 0; e < RPT; ++e) {
+        const int64_t at = ((int64_t)bh * K + r0 + e) * V + c;
+        p.hT[at] = p.N[at] + acc[e];
+    }
 }
 
 // One 16-token tile's operands in registers: oI rows (the B operand, 16
@@ -99,7 +130,8 @@ __device__ __forceinline__ void load_out_tile(OutTile<K, V, OT> &t, rsrc_t rI, r
     }
 }
 
-// o_t += h_in^T oI_t for 256 tokens of one (batch, head) per workgroup.  The
+// o_t += h_in^T oI_t for 64 kOutTiles tokens of one (batch, head) per
+// workgroup (512 or 1024 measured no faster than 256).  The
 // product is formed transposed, (o^T)[v][t] = sum_k h_in[k][v] oI[t][k]:
 // h_in^T, as bf16 high and low parts (about 16 bits of h_in), is staged once
 // into LDS and gives the A operand; each wave then streams its own 16-token
@@ -108,10 +140,12 @@ __device__ __forceinline__ void load_out_tile(OutTile<K, V, OT> &t, rsrc_t rI, r
 // A lane's result is four consecutive value columns of one token.  LDS rows
 // hold 16-byte chunks, chunk c of row r at c ^ (r mod 8), so that the eight
 // lanes of a 128-byte read phase hit distinct banks.
+constexpr int kOutTiles = 4;  // 16-token tiles per wave
+
 template <int K, int V, typename OT>
 __global__ __launch_bounds__(256, 2) void split_out_kernel(SplitParams p) {
     constexpr bool F32 = sizeof(OT) == 4;
-    constexpr int NT = 4;                // tiles per wave
+    constexpr int NT = kOutTiles;
     constexpr int TB = 16 * 4 * NT;      // tokens per workgroup
     constexpr int MT = V / 16, NS = K / 32, CPR = K / 8;
     __shared__ __attribute__((aligned(16))) u32x4 At[2 * V * CPR];
@@ -212,11 +246,11 @@ gdn_status launch_split(const gdn_problem *pr, FwdParams &fp, SplitParams &sp, i
     gdn_status st = enqueue_forward_pipe_split(K, F32, fp, grid, s);
     if (st != GDN_OK) return st;
     const int V = (int)pr->V;
-    const int gst = (int)(pr->B * pr->H * (K / (256 / V)));
+    const int gst = (int)(pr->B * pr->H * (K / kStateRows));
     const void *fs = V == 64 ? (const void *)&split_state_kernel<K, 64> : (const void *)&split_state_kernel<K, 128>;
     st = launch_kernel(fs, gst, &sp, s, 256);
     if (st != GDN_OK) return st;
-    const int nblk = (sp.T1 + 255) / 256;
+    const int nblk = (sp.T1 + 64 * kOutTiles - 1) / (64 * kOutTiles);
     const int gout = (int)(pr->B * pr->H * nblk);
     const void *fo = V == 64 ? (const void *)&split_out_kernel<K, 64, OT> : (const void *)&split_out_kernel<K, 128, OT>;
     return launch_kernel(fo, gout, &sp, s, 256);
