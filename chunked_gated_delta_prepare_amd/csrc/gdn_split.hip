@@ -94,79 +94,78 @@ __global__ __launch_bounds__(256) void split_state_kernel(SplitParams p) {
     }
 }
 
-// One 16-token tile's operands in registers: oI rows (the B operand, 16
-// bytes per 32-key step; fp32 two of them) and the lane's o pieces (four
-// value columns per 16-row value tile).
-template <int K, int V, typename OT> struct OutTile {
-    static constexpr bool F32 = sizeof(OT) == 4;
-    static constexpr int NS = K / 32, MT = V / 16;
-    u32x4 b[F32 ? 2 * NS : NS];
-    u32x4 o[MT];                         // bf16: the first two dwords
+// o_t += h_in^T oI_t for the second segment's tokens, 512 tokens of one
+// (batch, head) per workgroup of eight waves.  The product is formed
+// transposed, (o^T)[v][t] = sum_k h_in[k][v] oI[t][k]: h_in^T, as bf16 high
+// and low parts (about 16 bits of h_in), is staged once into LDS and gives
+// the A operand; each wave streams 16-token tiles with the next tile's loads
+// in flight.  Every load and store covers whole rows of the head: oI rows
+// come in 16 bytes per lane and go to the wave's own LDS tile, from which the
+// B fragments are read (fp32 oI as bf16 high and low parts, a third
+// product); o rows come in 8 bytes per lane.  The product, in accumulator
+// layout, goes back through the same LDS tile as fp32 [token][v] rows, and
+// each lane adds its values to its o piece and stores it.  (A first version
+// that fed the fragments straight from memory touched 16 token rows with
+// every load and store: 291 against 229 us at 65536 tokens, 64 heads.)
+// LDS rows hold 16-byte chunks, chunk c of row r at c ^ (r mod 8), so that
+// the eight lanes of a 128-byte read phase hit distinct banks.
+constexpr int kRowWaves = 8, kRowTiles = 4;
+
+template <int K, int V, typename OT> struct OutRowsLayout {
+    static constexpr int CPR = K / 8;                      // 16-byte chunks per At row (bf16)
+    static constexpr int CPI = K * (int)sizeof(OT) / 16;   // 16-byte chunks per oI row
+    static constexpr int LCT = V + 4;                      // fp32 product row pitch (floats)
+    static constexpr int kAt = 2 * V * CPR * 16;           // h_in^T high, low parts
+    static constexpr int kTileB = 16 * CPI * 16;           // oI tile [16][K]
+    static constexpr int kTileC = 16 * LCT * 4;            // product fp32 [16][LCT]
+    static constexpr int kTile = kTileB > kTileC ? kTileB : kTileC;
+    static constexpr int kBytes = kAt + kRowWaves * kTile;
+    static_assert(kBytes <= 160 * 1024, "LDS budget");
 };
 
 template <int K, int V, typename OT>
-__device__ __forceinline__ void load_out_tile(OutTile<K, V, OT> &t, rsrc_t rI, rsrc_t ro, int row, int h,
-                                              int n, int g, uint32_t HK, uint32_t HV) {
-    constexpr int NS = K / 32, MT = V / 16;
-    const uint32_t ib = ((uint32_t)row * HK + (uint32_t)h * K + 8 * g) * sizeof(OT);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        if constexpr (sizeof(OT) == 4) {
-            t.b[2 * s] = bload128(rI, ib + 32 * s * 4, 0);
-            t.b[2 * s + 1] = bload128(rI, ib + 32 * s * 4 + 16, 0);
-        } else {
-            t.b[s] = bload128(rI, ib + 32 * s * 2, 0);
-        }
-    }
-    const uint32_t ob = ((uint32_t)row * HV + (uint32_t)h * V + 4 * g) * sizeof(OT);
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        if constexpr (sizeof(OT) == 4) {
-            t.o[m] = bload128(ro, ob + 16 * m * 4, 0);
-        } else {
-            const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(ro, ob + 16 * m * 2, 0, 0);
-            t.o[m] = u32x4{w[0], w[1], 0u, 0u};
-        }
-    }
-}
-
-// o_t += h_in^T oI_t for 64 kOutTiles tokens of one (batch, head) per
-// workgroup (512 or 1024 measured no faster than 256).  The
-// product is formed transposed, (o^T)[v][t] = sum_k h_in[k][v] oI[t][k]:
-// h_in^T, as bf16 high and low parts (about 16 bits of h_in), is staged once
-// into LDS and gives the A operand; each wave then streams its own 16-token
-// tiles of oI (the B operand: bf16, or fp32 as high and low parts) and o,
-// with the next tile's loads in flight while the current one is multiplied.
-// A lane's result is four consecutive value columns of one token.  LDS rows
-// hold 16-byte chunks, chunk c of row r at c ^ (r mod 8), so that the eight
-// lanes of a 128-byte read phase hit distinct banks.
-constexpr int kOutTiles = 4;  // 16-token tiles per wave
-
-template <int K, int V, typename OT>
-__global__ __launch_bounds__(256, 2) void split_out_kernel(SplitParams p) {
+__global__ __launch_bounds__(64 * kRowWaves, 1) void split_out_kernel(SplitParams p) {
+    typedef OutRowsLayout<K, V, OT> L;
     constexpr bool F32 = sizeof(OT) == 4;
-    constexpr int NT = kOutTiles;
-    constexpr int TB = 16 * 4 * NT;      // tokens per workgroup
-    constexpr int MT = V / 16, NS = K / 32, CPR = K / 8;
-    __shared__ __attribute__((aligned(16))) u32x4 At[2 * V * CPR];
+    constexpr int MT = V / 16, NS = K / 32, CPR = L::CPR, CPI = L::CPI, LCT = L::LCT;
+    constexpr int RI = 64 / CPI, NI = 16 / RI;     // oI: rows per load, loads per tile
+    constexpr int PV = F32 ? 2 : 4;                // o values per 8-byte piece
+    constexpr int RO = 64 * PV / V, NO = 16 / RO;  // o: rows per load (and store), loads per tile
+    constexpr int TB = 16 * kRowWaves * kRowTiles;
+    __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
+    u32x4 *At = (u32x4 *)smem;
     const int wv = wave_id(), l = lane_id(), tid = threadIdx.x;
+    u32x4 *Bt = (u32x4 *)(smem + L::kAt + wv * L::kTile);      // chunk c of row r at c ^ (r & 7)
+    float *Ct = (float *)(smem + L::kAt + wv * L::kTile);       // the same bytes, after the products
     const int nblk = (p.T1 + TB - 1) / TB;
     const int bid = blockIdx.x;
     const int h = bid % p.H, rest = bid / p.H, blk = rest % nblk, b = rest / nblk;
     const int t_first = TB * blk;
     const int rows = min(TB, p.T1 - t_first);
     const uint32_t HK = (uint32_t)p.H * K, HV = (uint32_t)p.H * V;
-    const rsrc_t rI = make_rsrc((const OT *)p.oI + ((int64_t)b * p.T1 + t_first) * HK, (uint32_t)rows * HK * sizeof(OT));
-    const rsrc_t ro = make_rsrc((OT *)p.o + ((int64_t)b * p.T + p.t0 + t_first) * HV, (uint32_t)rows * HV * sizeof(OT));
+    const rsrc_t rI = make_rsrc((const OT *)p.oI + ((int64_t)b * p.T1 + t_first) * HK, (uint32_t)(rows * HK * sizeof(OT)));
+    const rsrc_t ro = make_rsrc((OT *)p.o + ((int64_t)b * p.T + p.t0 + t_first) * HV, (uint32_t)(rows * HV * sizeof(OT)));
     const int n = l & 15, g = l >> 4;
+    const int ir = l / CPI, ic = l % CPI;            // oI: row ir of each RI, chunk ic
+    const int orow = l / (V / PV), oc = l % (V / PV); // o: row orow of each RO, columns PV oc .. +PV-1
 
-    OutTile<K, V, OT> cur, nxt;
-    load_out_tile<K, V, OT>(cur, rI, ro, 16 * wv + n, h, n, g, HK, HV);
+    u32x4 bI[NI], bIn[NI];
+    u32x2 vo[NO], von[NO];
+    auto load = [&](u32x4 *bi, u32x2 *vv, int r0) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            bi[i] = bload128(rI, ((uint32_t)(r0 + RI * i + ir) * HK + (uint32_t)h * K) * sizeof(OT) + 16 * ic, 0);
+#pragma unroll
+        for (int j = 0; j < NO; ++j)
+            vv[j] = __builtin_amdgcn_raw_buffer_load_b64(
+                ro, ((uint32_t)(r0 + RO * j + orow) * HV + (uint32_t)h * V + PV * oc) * sizeof(OT), 0, 0);
+    };
+    load(bI, vo, 16 * wv);
     {
         const int64_t bh = (int64_t)b * p.H + h, plane = (int64_t)p.B * p.H * V * K;
         const u32x4 *hi = (const u32x4 *)(p.hinT + bh * V * K), *lo = (const u32x4 *)(p.hinT + plane + bh * V * K);
 #pragma unroll
-        for (int i = tid; i < V * CPR; i += 256) {
+        for (int i = tid; i < V * CPR; i += 64 * kRowWaves) {
             const int r = i / CPR, c = i % CPR;
             At[r * CPR + (c ^ (r & 7))] = hi[i];
             At[(V + r) * CPR + (c ^ (r & 7))] = lo[i];
@@ -175,31 +174,42 @@ __global__ __launch_bounds__(256, 2) void split_out_kernel(SplitParams p) {
     __syncthreads();
 
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-        const int row = 16 * (wv + 4 * i) + n;
-        if (i + 1 < NT) load_out_tile<K, V, OT>(nxt, rI, ro, row + 64, h, n, g, HK, HV);
+    for (int it = 0; it < kRowTiles; ++it) {
+        const int r0 = 16 * (wv + kRowWaves * it);
+        if (it + 1 < kRowTiles) load(bIn, von, r0 + 16 * kRowWaves);
+        // this tile's oI rows into the wave's LDS tile (LDS operations of one
+        // wave take effect in issue order: no barrier inside the wave's tile)
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int r = RI * i + ir;
+            Bt[r * CPI + (ic ^ (r & 7))] = bI[i];
+        }
         float4v acc[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[m] = float4v{0, 0, 0, 0};
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
+        for (int st = 0; st < NS; ++st) {
+            // lane (n, g): oI[n][32 st + 8 g .. +7]
             bf16x8 bh, bl;
             if constexpr (F32) {
-                uint16_t x[8], y[8];
+                const u32x4 x0 = Bt[n * CPI + ((8 * st + 2 * g) ^ (n & 7))];
+                const u32x4 x1 = Bt[n * CPI + ((8 * st + 2 * g + 1) ^ (n & 7))];
+                uint16_t xh[8], xl[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float f = __uint_as_float(j < 4 ? cur.b[2 * s][j] : cur.b[2 * s + 1][j - 4]);
-                    x[j] = f32_to_bf16_bits(f);
-                    y[j] = f32_to_bf16_bits(f - __uint_as_float((uint32_t)x[j] << 16));
+                    const float f = __uint_as_float(j < 4 ? x0[j] : x1[j - 4]);
+                    xh[j] = f32_to_bf16_bits(f);
+                    xl[j] = f32_to_bf16_bits(f - __uint_as_float((uint32_t)xh[j] << 16));
                 }
-                bh = __builtin_bit_cast(bf16x8, x);
-                bl = __builtin_bit_cast(bf16x8, y);
+                bh = __builtin_bit_cast(bf16x8, xh);
+                bl = __builtin_bit_cast(bf16x8, xl);
             } else {
-                bh = __builtin_bit_cast(bf16x8, cur.b[s]);
+                bh = __builtin_bit_cast(bf16x8, Bt[n * CPI + ((4 * st + g) ^ (n & 7))]);
             }
+            const int c = (4 * st + g) ^ (n & 7);
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                const int r = 16 * m + n, c = (4 * s + g) ^ (n & 7);
+                const int r = 16 * m + n;
                 const bf16x8 ah = __builtin_bit_cast(bf16x8, At[r * CPR + c]);
                 const bf16x8 al = __builtin_bit_cast(bf16x8, At[(V + r) * CPR + c]);
                 acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[m], 0, 0, 0);
@@ -207,36 +217,37 @@ __global__ __launch_bounds__(256, 2) void split_out_kernel(SplitParams p) {
                 if constexpr (F32) acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[m], 0, 0, 0);
             }
         }
-        // lane (g, n): value columns 16 m + 4 g .. +3 of token row
+        // lane (n, g) holds token n, value columns 16 m + 4 g .. +3; the tile's
+        // bytes change type here (the barriers keep the compiler from moving
+        // accesses of one view across those of the other)
+        asm volatile("" ::: "memory");
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const uint32_t col = (uint32_t)h * V + 16 * m + 4 * g;
-            if constexpr (!F32) {
-                const u32x4 w = cur.o[m];
-                const float4v x = float4v{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
-                                          __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)} + acc[m];
-                const uint32_t lo = (uint32_t)f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
-                const uint32_t hi = (uint32_t)f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
-                __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, ro, ((uint32_t)row * HV + col) * 2, 0, 0);
+        for (int m = 0; m < MT; ++m) *(float4v *)(Ct + n * LCT + 16 * m + 4 * g) = acc[m];
+#pragma unroll
+        for (int j = 0; j < NO; ++j) {
+            const int r = RO * j + orow;
+            const uint32_t off = ((uint32_t)(r0 + r) * HV + (uint32_t)h * V + PV * oc) * sizeof(OT);
+            const u32x2 w = vo[j];
+            if constexpr (F32) {
+                const float *x = Ct + r * LCT + 2 * oc;
+                const float y0 = __uint_as_float(w[0]) + x[0], y1 = __uint_as_float(w[1]) + x[1];
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(y0), __float_as_uint(y1)}, ro, off, 0, 0);
             } else {
-                // lanes of neighbouring tokens swap halves, so that each
-                // lane stores two 8-byte pieces a row apart (never one wide
-                // store): the even lane columns +0, +1 of its token and the
-                // next, the odd lane columns +2, +3 of the previous token
-                // and its own
-                const float4v x = __builtin_bit_cast(float4v, cur.o[m]) + acc[m];
-                const bool odd = n & 1;
-                const float s0 = odd ? x[0] : x[2], s1 = odd ? x[1] : x[3];
-                const float r0 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s0), 0xB1, 0xf, 0xf, false));
-                const float r1 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s1), 0xB1, 0xf, 0xf, false));
-                const uint32_t oa = ((uint32_t)(row & ~1) * HV + col) * 4 + 8 * (uint32_t)odd;
-                __builtin_amdgcn_raw_buffer_store_b64(
-                    u32x2{__float_as_uint(odd ? r0 : x[0]), __float_as_uint(odd ? r1 : x[1])}, ro, oa, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b64(
-                    u32x2{__float_as_uint(odd ? x[2] : r0), __float_as_uint(odd ? x[3] : r1)}, ro, oa + HV * 4, 0, 0);
+                const float4v x = *(const float4v *)(Ct + r * LCT + 4 * oc);
+                const float y0 = __uint_as_float(w[0] << 16) + x[0], y1 = __uint_as_float(w[0] & 0xffff0000u) + x[1];
+                const float y2 = __uint_as_float(w[1] << 16) + x[2], y3 = __uint_as_float(w[1] & 0xffff0000u) + x[3];
+                const uint32_t lo = (uint32_t)f32_to_bf16_bits(y0) | ((uint32_t)f32_to_bf16_bits(y1) << 16);
+                const uint32_t hi = (uint32_t)f32_to_bf16_bits(y2) | ((uint32_t)f32_to_bf16_bits(y3) << 16);
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, ro, off, 0, 0);
             }
         }
-        if (i + 1 < NT) cur = nxt;
+        asm volatile("" ::: "memory");
+        if (it + 1 < kRowTiles) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) bI[i] = bIn[i];
+#pragma unroll
+            for (int j = 0; j < NO; ++j) vo[j] = von[j];
+        }
     }
 }
 
@@ -250,10 +261,10 @@ gdn_status launch_split(const gdn_problem *pr, FwdParams &fp, SplitParams &sp, i
     const void *fs = V == 64 ? (const void *)&split_state_kernel<K, 64> : (const void *)&split_state_kernel<K, 128>;
     st = launch_kernel(fs, gst, &sp, s, 256);
     if (st != GDN_OK) return st;
-    const int nblk = (sp.T1 + 64 * kOutTiles - 1) / (64 * kOutTiles);
-    const int gout = (int)(pr->B * pr->H * nblk);
+    constexpr int TB = 16 * kRowWaves * kRowTiles;
+    const int gout = (int)(pr->B * pr->H * ((sp.T1 + TB - 1) / TB));
     const void *fo = V == 64 ? (const void *)&split_out_kernel<K, 64, OT> : (const void *)&split_out_kernel<K, 128, OT>;
-    return launch_kernel(fo, gout, &sp, s, 256);
+    return launch_kernel(fo, gout, &sp, s, 64 * kRowWaves);
 }
 
 }  // namespace
